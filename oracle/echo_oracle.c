@@ -1,0 +1,377 @@
+/*
+ * echo_oracle.c -- plain, slow CPU oracle for the ECHO decode-step hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or
+ * load this file: only the test suite, the smoke check and the CPU-baseline leg
+ * of the benchmark use it.  It shares no header, table, constant or helper with
+ * the GPU library; every value it needs comes in through its own arguments.
+ *
+ * Sources (all statements are restated, not quoted):
+ *  [P1]  "ECHO: Efficient KV Cache Offloading with Lossless Prefetching for
+ *        Serving Native Sparse Attention LLMs (OSDI 2026)", review page on
+ *        awesome-system-papers: sections "Problem and motivation" (indexer
+ *        scores every past token, the top 2048 are kept), "Key observations"
+ *        (observation 2: EMA with smoothing 0.5 of the 2048th score),
+ *        "Core method / in-graph per-layer cache management" (free bitmap,
+ *        eviction priority, index buffer, two-way host/GPU maps, allocation
+ *        by parallel scan, free protects the selected tokens, eviction moves
+ *        no data, recall finds misses from the map; metadata 4*N_H + 13*N_G
+ *        bytes per layer), "Core method / decode" (EMA threshold prefetch
+ *        during scoring under a global counter whose cap grows with context;
+ *        exact top-k and recall of every missing selected token).
+ *  [P2]  "ECHO: Lossless KV Cache Offloading for Sparse Attention LLMs",
+ *        podcast show notes: prediction only decides when to move data; every
+ *        missed token is recalled; management state lives in fixed-size
+ *        integer tensors.  Source 8 of its list is the DeepSeek-V3.2-Exp
+ *        report, whose lightning indexer is
+ *        score(s) = sum_j w_j * ReLU(q_j . k_s).
+ *
+ * Readings where the pages are silent (each also listed in the design notes):
+ *  R1  The indexer K is OCP fp8 E4M3FN with scale 1; q is bf16; w is fp32.
+ *  R2  Scores are computed in fp64 and rounded once (nearest-even) to fp32;
+ *      -0 is replaced by +0.
+ *  R3  Top-k order is (score descending, token index ascending); the result
+ *      is reported in ascending token order; if ctx <= k every token is kept.
+ *  R4  EMA: theta = +inf means "no estimate yet"; the first k-th score seeds
+ *      it; afterwards theta <- alpha*s_k + (1-alpha)*theta in fp32 (two
+ *      products and one sum, each rounded).  Updated only when ctx >= k.
+ *  R5  Prefetch: candidates are tokens with score > theta that have no GPU
+ *      slot; request b takes at most cap_b = min(k, ceil(ctx_b/cap_div)) of
+ *      them, the first ones in token order, and the free slots
+ *      F[off_b + r] (F = ascending free list at step start,
+ *      off_b = sum of earlier caps).  Installed with priority t.
+ *  R6  Protect: a selected resident token gets priority t.  Misses are listed
+ *      in (request, token) order.
+ *  R7  Evict: E = occupied slots with priority < t, ordered by
+ *      (priority, slot).  n_evict = min(|E|, max(0, |M| + R - n_free)) with
+ *      R = sum of caps (reserve for the next step's prefetch).  If
+ *      n_free + |E| < |M| the step stops with a capacity error.
+ *  R8  Alloc: miss i takes the i-th slot of the ascending free list after
+ *      eviction, priority t; its latent row is copied from the host pool.
+ *  R9  t (the decode-step counter) advances by one after a successful step.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_OK 0
+#define ORC_ECAPACITY (-4)
+
+#define ORC_MODE_EMA 0
+#define ORC_MODE_NEG_INF 1
+#define ORC_MODE_POS_INF 2
+
+/* ---------------------------------------------------------------- formats */
+
+/* OCP fp8 E4M3FN: 1 sign, 4 exponent (bias 7), 3 mantissa bits; exponent 0
+ * holds subnormals m * 2^-9; 0x7F / 0xFF are NaN; there is no infinity.    */
+double orc_e4m3_value(uint8_t code) {
+  int sign = (code >> 7) & 1;
+  int e = (code >> 3) & 0xF;
+  int m = code & 0x7;
+  double v;
+  if (e == 0xF && m == 0x7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m, -9);
+  else
+    v = ldexp(1.0 + m / 8.0, e - 7);
+  return sign ? -v : v;
+}
+
+/* bfloat16 is the upper half of an IEEE binary32. */
+double orc_bf16_value(uint16_t code) {
+  uint32_t bits = (uint32_t)code << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+/* ------------------------------------------------------------ metadata */
+
+/* Per-layer management metadata (P1, in-graph cache management): one int32
+ * host->GPU entry per host token, and per GPU slot a free byte, an int32
+ * priority, an int32 index-buffer entry and an int32 GPU->host entry.     */
+int64_t orc_meta_bytes(int64_t n_host, int64_t n_gpu) {
+  int64_t per_host = 4;              /* h2g */
+  int64_t per_slot = 1 + 4 + 4 + 4;  /* free, prio, idxbuf, g2h */
+  return per_host * n_host + per_slot * n_gpu;
+}
+
+/* --------------------------------------------------------------- scores */
+
+/* One request: score[s] = sum_j w[j] * max(0, sum_d q[j][d] * K[s][d]),
+ * fp64 throughout, one rounding to fp32 at the end (R1, R2).
+ * q: bf16 codes [H][D]; w: fp32 [H]; krows: e4m3 codes [ctx][D].           */
+void orc_scores(int H, int D, const uint16_t *q, const float *w,
+                const uint8_t *krows, int64_t ctx, float *out) {
+  double *qd = (double *)malloc(sizeof(double) * (size_t)H * D);
+  double kval[256];
+  for (int c = 0; c < 256; ++c) kval[c] = orc_e4m3_value((uint8_t)c);
+  for (int64_t i = 0; i < (int64_t)H * D; ++i) qd[i] = orc_bf16_value(q[i]);
+#pragma omp parallel for schedule(static)
+  for (int64_t s = 0; s < ctx; ++s) {
+    const uint8_t *k = krows + s * D;
+    double r = 0.0;
+    for (int j = 0; j < H; ++j) {
+      double x = 0.0;
+      for (int d = 0; d < D; ++d) x += qd[(int64_t)j * D + d] * kval[k[d]];
+      double relu = x > 0.0 ? x : 0.0;
+      r += (double)w[j] * relu;
+    }
+    float f = (float)r;
+    if (f == 0.0f) f = 0.0f; /* -0 -> +0 */
+    out[s] = f;
+  }
+  free(qd);
+}
+
+/* ---------------------------------------------------------------- top-k */
+
+static const float *g_sort_scores; /* comparator context (single-threaded use) */
+
+static int cmp_score_desc_idx_asc(const void *a, const void *b) {
+  int32_t ia = *(const int32_t *)a, ib = *(const int32_t *)b;
+  float sa = g_sort_scores[ia], sb = g_sort_scores[ib];
+  if (sa > sb) return -1;
+  if (sa < sb) return 1;
+  return (ia > ib) - (ia < ib);
+}
+
+static int cmp_int_asc(const void *a, const void *b) {
+  int32_t ia = *(const int32_t *)a, ib = *(const int32_t *)b;
+  return (ia > ib) - (ia < ib);
+}
+
+/* R3: the min(k, n) tokens that come first under (score desc, index asc),
+ * written in ascending index order.  Returns how many were written; if
+ * kth_out is not NULL it receives the score of the last one in the
+ * (score desc, index asc) order, i.e. the k-th highest score.              */
+int orc_topk(const float *scores, int64_t n, int k, int32_t *sel, float *kth_out) {
+  int32_t *order = (int32_t *)malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1));
+  for (int64_t i = 0; i < n; ++i) order[i] = (int32_t)i;
+  g_sort_scores = scores;
+  qsort(order, (size_t)n, sizeof(int32_t), cmp_score_desc_idx_asc);
+  int m = (int)(n < k ? n : k);
+  if (kth_out) *kth_out = m > 0 ? scores[order[m - 1]] : NAN;
+  memcpy(sel, order, sizeof(int32_t) * (size_t)m);
+  qsort(sel, (size_t)m, sizeof(int32_t), cmp_int_asc);
+  free(order);
+  return m;
+}
+
+/* ------------------------------------------------------------------ EMA */
+
+/* R4: one EMA step in fp32.  theta == +inf means "no estimate yet".        */
+float orc_ema_update(float theta, float s_k, float alpha) {
+  if (isinf(theta) && theta > 0) return s_k;
+  float keep = 1.0f - alpha;
+  float a = alpha * s_k;
+  float b = keep * theta;
+  return a + b;
+}
+
+/* ------------------------------------------------------ the layer step */
+
+typedef struct {
+  int32_t H, D, k, latent;
+  int64_t n_host;
+  int32_t n_gpu;
+  int32_t cap_div;
+  float alpha;
+} orc_cfg;
+
+typedef struct {
+  int32_t *h2g;   /* [n_host], -1 = not on the GPU            */
+  int32_t *g2h;   /* [n_gpu],  -1 = free slot                 */
+  int32_t *prio;  /* [n_gpu],  step of last use, -1 = free    */
+  uint8_t *freef; /* [n_gpu],  1 = free                       */
+  float *theta;   /* [B],      EMA of the k-th score          */
+  int32_t t;      /* decode-step counter                      */
+  uint16_t *pool; /* [n_gpu][latent] bf16 codes, or NULL      */
+} orc_state;
+
+typedef struct {
+  float *scores;     /* [B][ctx_stride]                          */
+  int32_t *sel_tok;  /* [B][k]   selected tokens, ascending       */
+  int32_t *sel_slot; /* [B][k]   their GPU slots after the step   */
+  int32_t *n_sel;    /* [B]                                        */
+  float *kth;        /* [B]      k-th highest score (NaN if none)  */
+  int32_t *pf_tok;   /* [B][k]   prefetched tokens, in rank order  */
+  int32_t *pf_slot;  /* [B][k]                                     */
+  int32_t *n_pf;     /* [B]                                        */
+  int32_t *n_cand;   /* [B]      prefetch candidates (before cap)  */
+  int32_t *miss_tok; /* [B][k]   missed tokens, ascending          */
+  int32_t *n_miss;   /* [B]                                        */
+  int32_t *evicted;  /* [n_gpu]  evicted slots in eviction order   */
+  int32_t n_evict;
+  int32_t n_free_start; /* free slots at step start               */
+  int32_t status;
+} orc_out;
+
+static void install(const orc_cfg *c, orc_state *st, int64_t h, int32_t g,
+                    const uint16_t *host_kv) {
+  st->h2g[h] = g;
+  st->g2h[g] = (int32_t)h;
+  st->freef[g] = 0;
+  st->prio[g] = st->t;
+  if (st->pool && host_kv)
+    memcpy(st->pool + (int64_t)g * c->latent, host_kv + h * c->latent,
+           sizeof(uint16_t) * (size_t)c->latent);
+}
+
+static int64_t cap_of(const orc_cfg *c, int64_t ctx) {
+  int64_t cap = (ctx + c->cap_div - 1) / c->cap_div;
+  return cap < c->k ? cap : c->k;
+}
+
+static int cmp_prio_slot(const void *a, const void *b) {
+  const int64_t *x = (const int64_t *)a, *y = (const int64_t *)b;
+  return (*x > *y) - (*x < *y);
+}
+
+/* One decode step of one layer for a batch of B requests.
+ * q: bf16 [B][H][D]; w: fp32 [B][H]; kidx: e4m3 [n_host][D];
+ * host_kv: bf16 [n_host][latent] (may be NULL when st->pool is NULL);
+ * host_base/ctx: [B] (request b owns host ids host_base[b] + s, s < ctx[b]);
+ * ext_scores: NULL, or [B][ctx_stride] scores to use instead of computing. */
+int orc_layer_step(const orc_cfg *c, orc_state *st, int B,
+                   const int32_t *host_base, const int32_t *ctx,
+                   const uint16_t *q, const float *w, const uint8_t *kidx,
+                   const uint16_t *host_kv, int mode, const float *ext_scores,
+                   int64_t ctx_stride, orc_out *o) {
+  const int k = c->k;
+  const int32_t t = st->t;
+  o->status = ORC_OK;
+  o->n_evict = 0;
+
+  /* scores (P1 problem statement; R1, R2) */
+  for (int b = 0; b < B; ++b) {
+    float *sb = o->scores + (int64_t)b * ctx_stride;
+    if (ext_scores)
+      memcpy(sb, ext_scores + (int64_t)b * ctx_stride, sizeof(float) * (size_t)ctx[b]);
+    else
+      orc_scores(c->H, c->D, q + (int64_t)b * c->H * c->D, w + (int64_t)b * c->H,
+                 kidx + (int64_t)host_base[b] * c->D, ctx[b], sb);
+  }
+
+  /* prefetch during scoring (P1 decode; R5) */
+  int32_t *F = (int32_t *)malloc(sizeof(int32_t) * (size_t)(c->n_gpu > 0 ? c->n_gpu : 1));
+  int64_t nF = 0;
+  for (int32_t g = 0; g < c->n_gpu; ++g)
+    if (st->freef[g]) F[nF++] = g;
+  o->n_free_start = (int32_t)nF;
+  int64_t off = 0, reserve = 0;
+  for (int b = 0; b < B; ++b) {
+    int64_t cap = cap_of(c, ctx[b]);
+    reserve += cap;
+    float th = INFINITY;
+    int active = 0;
+    if (mode == ORC_MODE_EMA) {
+      th = st->theta[b];
+      active = !(isinf(th) && th > 0);
+    } else if (mode == ORC_MODE_NEG_INF) {
+      th = -INFINITY;
+      active = 1;
+    }
+    int32_t r = 0, ncand = 0;
+    if (active) {
+      const float *sb = o->scores + (int64_t)b * ctx_stride;
+      for (int64_t s = 0; s < ctx[b]; ++s) {
+        int64_t h = host_base[b] + s;
+        if (sb[s] > th && st->h2g[h] == -1) {
+          ++ncand;
+          if (r < cap && off + r < nF) {
+            int32_t g = F[off + r];
+            install(c, st, h, g, host_kv);
+            o->pf_tok[(int64_t)b * k + r] = (int32_t)s;
+            o->pf_slot[(int64_t)b * k + r] = g;
+            ++r;
+          }
+        }
+      }
+    }
+    o->n_pf[b] = r;
+    o->n_cand[b] = ncand;
+    off += cap;
+  }
+
+  /* exact top-k (P1 decode; R3) and EMA (P1 observation 2; R4) */
+  for (int b = 0; b < B; ++b) {
+    const float *sb = o->scores + (int64_t)b * ctx_stride;
+    float kth;
+    int m = orc_topk(sb, ctx[b], k, o->sel_tok + (int64_t)b * k, &kth);
+    o->n_sel[b] = m;
+    o->kth[b] = kth;
+    if (mode == ORC_MODE_EMA && ctx[b] >= k)
+      st->theta[b] = orc_ema_update(st->theta[b], kth, c->alpha);
+  }
+
+  /* protect the selected tokens and list the misses (P1 cache management; R6) */
+  int64_t n_miss_all = 0;
+  for (int b = 0; b < B; ++b) {
+    int32_t nm = 0;
+    for (int i = 0; i < o->n_sel[b]; ++i) {
+      int32_t s = o->sel_tok[(int64_t)b * k + i];
+      int64_t h = host_base[b] + s;
+      int32_t g = st->h2g[h];
+      o->sel_slot[(int64_t)b * k + i] = g;
+      if (g >= 0)
+        st->prio[g] = t;
+      else
+        o->miss_tok[(int64_t)b * k + nm++] = s;
+    }
+    o->n_miss[b] = nm;
+    n_miss_all += nm;
+  }
+
+  /* evict (P1 cache management; R7): no bytes move */
+  int64_t n_free = 0, nE = 0;
+  int64_t *E = (int64_t *)malloc(sizeof(int64_t) * (size_t)(c->n_gpu > 0 ? c->n_gpu : 1));
+  for (int32_t g = 0; g < c->n_gpu; ++g) {
+    if (st->freef[g])
+      ++n_free;
+    else if (st->prio[g] < t)
+      E[nE++] = ((int64_t)st->prio[g] << 32) | (int64_t)g; /* prio >= 0 here */
+  }
+  if (n_free + nE < n_miss_all) {
+    o->status = ORC_ECAPACITY;
+    free(E);
+    free(F);
+    return o->status;
+  }
+  qsort(E, (size_t)nE, sizeof(int64_t), cmp_prio_slot);
+  int64_t want = n_miss_all + reserve - n_free;
+  if (want < 0) want = 0;
+  int64_t n_evict = want < nE ? want : nE;
+  for (int64_t i = 0; i < n_evict; ++i) {
+    int32_t g = (int32_t)(E[i] & 0xFFFFFFFF);
+    st->h2g[st->g2h[g]] = -1;
+    st->g2h[g] = -1;
+    st->freef[g] = 1;
+    st->prio[g] = -1;
+    o->evicted[i] = g;
+  }
+  o->n_evict = (int32_t)n_evict;
+
+  /* allocate and recall (P1 cache management; R8) */
+  nF = 0;
+  for (int32_t g = 0; g < c->n_gpu; ++g)
+    if (st->freef[g]) F[nF++] = g;
+  int64_t i = 0;
+  for (int b = 0; b < B; ++b) {
+    for (int j = 0; j < o->n_miss[b]; ++j, ++i) {
+      int32_t s = o->miss_tok[(int64_t)b * k + j];
+      int64_t h = host_base[b] + s;
+      install(c, st, h, F[i], host_kv);
+    }
+    for (int j = 0; j < o->n_sel[b]; ++j) {
+      int64_t h = host_base[b] + o->sel_tok[(int64_t)b * k + j];
+      o->sel_slot[(int64_t)b * k + j] = st->h2g[h];
+    }
+  }
+  st->t = t + 1; /* R9 */
+  free(E);
+  free(F);
+  return ORC_OK;
+}

@@ -1,0 +1,193 @@
+"""ctypes wrapper around the CPU oracle (``echo_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the CPU-baseline
+leg of the benchmark use this module; the product path never imports it.  It
+shares no code with the GPU library.  Every function cites, in the C source, the
+passage of the ECHO review page it follows.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "echo_oracle.c")
+LIB = os.path.join(HERE, "libecho_oracle.so")
+
+MODE_EMA, MODE_NEG_INF, MODE_POS_INF = 0, 1, 2
+OK, ECAPACITY = 0, -4
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (plain C99 + OpenMP, no FMA contraction)."""
+    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        cmd = ["gcc", "-std=gnu99", "-O2", "-ffp-contract=off", "-fopenmp", "-fPIC",
+               "-shared", SRC, "-o", LIB + ".tmp", "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """Load the oracle.  ECHO_ORACLE_LIB may name another build of the same source (the
+    planted-mistake tests use it to check that the pins notice a wrong oracle)."""
+    global _lib
+    if _lib is None:
+        path = os.environ.get("ECHO_ORACLE_LIB") or build()
+        _lib = C.CDLL(path)
+        _lib.orc_e4m3_value.restype = C.c_double
+        _lib.orc_e4m3_value.argtypes = [C.c_uint8]
+        _lib.orc_bf16_value.restype = C.c_double
+        _lib.orc_bf16_value.argtypes = [C.c_uint16]
+        _lib.orc_meta_bytes.restype = C.c_int64
+        _lib.orc_meta_bytes.argtypes = [C.c_int64, C.c_int64]
+        _lib.orc_scores.restype = None
+        _lib.orc_scores.argtypes = [C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p,
+                                    C.c_int64, C.c_void_p]
+        _lib.orc_topk.restype = C.c_int
+        _lib.orc_topk.argtypes = [C.c_void_p, C.c_int64, C.c_int, C.c_void_p, C.c_void_p]
+        _lib.orc_ema_update.restype = C.c_float
+        _lib.orc_ema_update.argtypes = [C.c_float, C.c_float, C.c_float]
+        _lib.orc_layer_step.restype = C.c_int
+        _lib.orc_layer_step.argtypes = [C.POINTER(Cfg), C.POINTER(State), C.c_int,
+                                        C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                        C.c_void_p, C.c_void_p, C.c_int, C.c_void_p,
+                                        C.c_int64, C.POINTER(Out)]
+    return _lib
+
+
+class Cfg(C.Structure):
+    _fields_ = [("H", C.c_int32), ("D", C.c_int32), ("k", C.c_int32), ("latent", C.c_int32),
+                ("n_host", C.c_int64), ("n_gpu", C.c_int32), ("cap_div", C.c_int32),
+                ("alpha", C.c_float)]
+
+
+class State(C.Structure):
+    _fields_ = [("h2g", C.c_void_p), ("g2h", C.c_void_p), ("prio", C.c_void_p),
+                ("freef", C.c_void_p), ("theta", C.c_void_p), ("t", C.c_int32),
+                ("pool", C.c_void_p)]
+
+
+class Out(C.Structure):
+    _fields_ = [("scores", C.c_void_p), ("sel_tok", C.c_void_p), ("sel_slot", C.c_void_p),
+                ("n_sel", C.c_void_p), ("kth", C.c_void_p), ("pf_tok", C.c_void_p),
+                ("pf_slot", C.c_void_p), ("n_pf", C.c_void_p), ("n_cand", C.c_void_p),
+                ("miss_tok", C.c_void_p), ("n_miss", C.c_void_p), ("evicted", C.c_void_p),
+                ("n_evict", C.c_int32), ("n_free_start", C.c_int32), ("status", C.c_int32)]
+
+
+def _p(a: np.ndarray) -> int:
+    assert a.flags["C_CONTIGUOUS"], "oracle buffers must be contiguous"
+    return a.ctypes.data
+
+
+def e4m3_value(code: int) -> float:
+    return lib().orc_e4m3_value(int(code))
+
+
+def bf16_value(code: int) -> float:
+    return lib().orc_bf16_value(int(code))
+
+
+def meta_bytes(n_host: int, n_gpu: int) -> int:
+    return lib().orc_meta_bytes(int(n_host), int(n_gpu))
+
+
+def scores(q: np.ndarray, w: np.ndarray, krows: np.ndarray) -> np.ndarray:
+    """q: uint16 bf16 codes [H, D]; w: float32 [H]; krows: uint8 e4m3 [ctx, D]."""
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    krows = np.ascontiguousarray(krows, dtype=np.uint8)
+    H, D = q.shape
+    assert krows.ndim == 2 and krows.shape[1] == D and w.shape == (H,)
+    out = np.empty(krows.shape[0], np.float32)
+    lib().orc_scores(H, D, _p(q), _p(w), _p(krows), krows.shape[0], _p(out))
+    return out
+
+
+def topk(sc: np.ndarray, k: int) -> tuple[np.ndarray, float]:
+    sc = np.ascontiguousarray(sc, dtype=np.float32)
+    sel = np.empty(max(1, min(k, sc.size)), np.int32)
+    kth = np.zeros(1, np.float32)
+    m = lib().orc_topk(_p(sc), sc.size, int(k), _p(sel), _p(kth))
+    return sel[:m].copy(), float(kth[0])
+
+
+def ema_update(theta: float, s_k: float, alpha: float = 0.5) -> float:
+    return lib().orc_ema_update(theta, s_k, alpha)
+
+
+class OracleLayer:
+    """State of one layer (maps, priorities, free flags, EMA, pool) plus the step."""
+
+    def __init__(self, H, D, k, latent, n_host, n_gpu, max_batch, cap_div=128, alpha=0.5,
+                 keep_pool=True):
+        self.cfg = Cfg(H, D, k, latent, n_host, n_gpu, cap_div, alpha)
+        self.h2g = np.full(n_host, -1, np.int32)
+        self.g2h = np.full(n_gpu, -1, np.int32)
+        self.prio = np.full(n_gpu, -1, np.int32)
+        self.free = np.ones(n_gpu, np.uint8)
+        self.theta = np.full(max_batch, np.inf, np.float32)
+        self.pool = np.zeros((n_gpu, latent), np.uint16) if keep_pool else None
+        self.t = 0
+        self.max_batch = max_batch
+
+    def step(self, host_base, ctx, q, w, kidx, host_kv, mode=MODE_EMA, ext_scores=None):
+        """One decode step.  q: uint16 [B, H, D]; w: float32 [B, H]; kidx: uint8 [n_host, D];
+        host_kv: uint16 [n_host, latent] or None; ext_scores: float32 [B, >= max ctx] or None.
+        Returns a dict of outputs (numpy arrays, trimmed to their counts)."""
+        cfg = self.cfg
+        k = cfg.k
+        host_base = np.ascontiguousarray(host_base, np.int32)
+        ctx = np.ascontiguousarray(ctx, np.int32)
+        B = int(ctx.size)
+        stride = max(1, int(ctx.max()) if B else 1)
+        if ext_scores is not None:
+            ext_scores = np.ascontiguousarray(ext_scores, np.float32)
+            stride = ext_scores.shape[1]
+        q = np.ascontiguousarray(q, np.uint16)
+        w = np.ascontiguousarray(w, np.float32)
+        kidx = np.ascontiguousarray(kidx, np.uint8)
+        assert q.shape == (B, cfg.H, cfg.D) and w.shape == (B, cfg.H)
+        assert kidx.shape == (cfg.n_host, cfg.D)
+        if B:
+            assert int((host_base.astype(np.int64) + ctx).max()) <= cfg.n_host
+        if host_kv is not None:
+            host_kv = np.ascontiguousarray(host_kv, np.uint16)
+            assert host_kv.shape == (cfg.n_host, cfg.latent)
+        o = dict(scores=np.zeros((B, stride), np.float32),
+                 sel_tok=np.full((B, k), -1, np.int32), sel_slot=np.full((B, k), -1, np.int32),
+                 n_sel=np.zeros(B, np.int32), kth=np.zeros(B, np.float32),
+                 pf_tok=np.full((B, k), -1, np.int32), pf_slot=np.full((B, k), -1, np.int32),
+                 n_pf=np.zeros(B, np.int32), n_cand=np.zeros(B, np.int32),
+                 miss_tok=np.full((B, k), -1, np.int32), n_miss=np.zeros(B, np.int32),
+                 evicted=np.full(max(1, cfg.n_gpu), -1, np.int32))
+        out = Out(*[_p(o[n]) for n in ("scores", "sel_tok", "sel_slot", "n_sel", "kth", "pf_tok",
+                                        "pf_slot", "n_pf", "n_cand", "miss_tok", "n_miss",
+                                        "evicted")], 0, 0, 0)
+        theta = np.ascontiguousarray(self.theta)
+        st = State(_p(self.h2g), _p(self.g2h), _p(self.prio), _p(self.free), _p(theta), self.t,
+                   _p(self.pool) if self.pool is not None else None)
+        rc = lib().orc_layer_step(C.byref(cfg), C.byref(st), B, _p(host_base), _p(ctx), _p(q),
+                                  _p(w), _p(kidx),
+                                  _p(host_kv) if host_kv is not None else None, int(mode),
+                                  _p(ext_scores) if ext_scores is not None else None,
+                                  stride, C.byref(out))
+        self.theta = theta
+        self.t = st.t
+        o["status"] = rc
+        o["n_evict"] = out.n_evict
+        o["n_free_start"] = out.n_free_start
+        o["evicted"] = o["evicted"][: out.n_evict]
+        return o
+
+    def snapshot(self):
+        return dict(h2g=self.h2g.copy(), g2h=self.g2h.copy(), prio=self.prio.copy(),
+                    free=self.free.copy(), theta=self.theta.copy(), t=self.t,
+                    pool=None if self.pool is None else self.pool.copy())

@@ -1,0 +1,69 @@
+"""Workload shapes for the decode-step hot path.
+
+The four decode workloads mirror the settings the ECHO review page describes:
+80K-100K-token inputs on InfiniteBench ("Experiments and results"), a 20K-token
+ShareGPT trace for the k-th-score trajectory ("Key observations", observation
+2), host pool 2M / GPU pool 200K tokens ("In-graph per-layer cache management")
+and a GPU pool held at 110K ("Experiments and results").  Neither dataset is
+available; seeded random tensors of the same shapes stand in for them.
+
+"64K" means 65,536 tokens; "80K", "100K", "110K", "200K" and "2M" are decimal.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    cfg_id: int            # substream id for seeding
+    batch: int             # B requests
+    ctx_lo: int            # context length range (inclusive); lo == hi -> fixed
+    ctx_hi: int
+    layers: int            # L
+    heads: int             # indexer heads H
+    head_dim: int          # indexer dim D
+    top_k: int             # k
+    n_gpu: int             # GPU pool slots per layer
+    n_host: int            # host pool tokens
+    rho: float             # AR(1) coefficient of the query stream
+    steps: int             # decode steps
+    latent: int = 576      # MLA latent elements (bf16)
+    cap_div: int = 128     # prefetch cap = min(k, ceil(ctx / cap_div))
+    alpha: float = 0.5     # EMA smoothing
+    notes: str = field(default="", compare=False)
+
+    def contexts(self, seed: int = 0) -> np.ndarray:
+        if self.ctx_lo == self.ctx_hi:
+            return np.full(self.batch, self.ctx_lo, np.int32)
+        ss = np.random.SeedSequence(seed, spawn_key=(self.cfg_id, 0xC7C7))
+        rng = np.random.Generator(np.random.PCG64(ss))
+        return rng.integers(self.ctx_lo, self.ctx_hi + 1, size=self.batch).astype(np.int32)
+
+    def scaled(self, **kw) -> "Workload":
+        d = dict(self.__dict__)
+        d.update(kw)
+        return Workload(**d)
+
+
+WORKLOADS = {
+    # 1 request, 1 layer, ctx 4096, 4x32 indexer, k=256, 1024 GPU slots, 4096 host tokens
+    "tiny": Workload("tiny", 1, 1, 4096, 4096, 1, 4, 32, 256, 1024, 4096, 0.95, 8),
+    # batch 8 x 64K, 64x128, k=2048, 200K GPU slots, 2M host tokens
+    "single_layer": Workload("single_layer", 2, 8, 65536, 65536, 1, 64, 128, 2048, 200_000,
+                             2_000_000, 0.98, 64),
+    # batch 32, ctx U{80K..100K}, 61 layers, 110K GPU slots per layer.  32 x 90K on average
+    # exceeds a 2M host pool, so the host pool holds 3.2M tokens.
+    "capacity": Workload("capacity", 3, 32, 80_000, 100_000, 61, 64, 128, 2048, 110_000,
+                         3_200_000, 0.98, 32),
+    # batch 16 x 100K, rho 0.5 for low locality, 200K GPU slots, 2M host tokens
+    "low_locality": Workload("low_locality", 4, 16, 100_000, 100_000, 1, 64, 128, 2048,
+                             200_000, 2_000_000, 0.5, 32),
+}
+
+
+def get(name: str) -> Workload:
+    return WORKLOADS[name]

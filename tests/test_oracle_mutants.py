@@ -1,0 +1,80 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each case copies the oracle's C source, plants one plausible mistake (a dropped
+term, a wrong sign or index, a swapped operand, a reversed order), builds it on
+the CPU and runs the pin suite against that build in a subprocess; the suite
+must fail.  The real oracle is never modified.
+"""
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+from oracle import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MUTANTS = {
+    "relu_dropped": ("double relu = x > 0.0 ? x : 0.0;", "double relu = x;"),
+    "weight_dropped": ("r += (double)w[j] * relu;", "r += relu;"),
+    "q_transposed": ("qd[(int64_t)j * D + d]", "qd[(int64_t)d * H + j]"),
+    "e4m3_bias": ("ldexp(1.0 + m / 8.0, e - 7)", "ldexp(1.0 + m / 8.0, e - 8)"),
+    "e4m3_subnormal": ("ldexp((double)m, -9)", "ldexp((double)m, -10)"),
+    "fp32_accumulation": ("double x = 0.0;", "float x = 0.0f;"),
+    "topk_ascending": ("if (sa > sb) return -1;\n  if (sa < sb) return 1;",
+                       "if (sa > sb) return 1;\n  if (sa < sb) return -1;"),
+    "topk_tie_high_index": ("  return (ia > ib) - (ia < ib);\n}\n\nstatic int cmp_int_asc",
+                            "  return (ia < ib) - (ia > ib);\n}\n\nstatic int cmp_int_asc"),
+    "ema_no_seed": ("if (isinf(theta) && theta > 0) return s_k;", ""),
+    "ema_weights_swapped": ("float a = alpha * s_k;\n  float b = keep * theta;",
+                            "float a = alpha * theta;\n  float b = keep * s_k;"),
+    "threshold_not_strict": ("if (sb[s] > th && st->h2g[h] == -1)",
+                             "if (sb[s] >= th && st->h2g[h] == -1)"),
+    "cap_rounds_down": ("int64_t cap = (ctx + c->cap_div - 1) / c->cap_div;",
+                        "int64_t cap = ctx / c->cap_div;"),
+    "no_protect": ("      if (g >= 0)\n        st->prio[g] = t;\n      else",
+                   "      if (g >= 0)\n        ;\n      else"),
+    "evict_newest_first": ("return (*x > *y) - (*x < *y);", "return (*x < *y) - (*x > *y);"),
+    "no_reserve": ("int64_t want = n_miss_all + reserve - n_free;",
+                   "int64_t want = n_miss_all - n_free;"),
+    "alloc_descending": ("install(c, st, h, F[i], host_kv);",
+                         "install(c, st, h, F[nF - 1 - i], host_kv);"),
+    "prefetch_ignores_offset": ("int32_t g = F[off + r];", "int32_t g = F[r];"),
+    "metadata_idxbuf_dropped": ("int64_t per_slot = 1 + 4 + 4 + 4;",
+                                "int64_t per_slot = 1 + 4 + 4;"),
+}
+
+
+def _build(name, tmp):
+    src = open(O.SRC).read()
+    old, new = MUTANTS[name]
+    assert src.count(old) == 1, f"mutation site for {name} is not unique"
+    path_c = os.path.join(tmp, f"m_{name}.c")
+    path_so = os.path.join(tmp, f"m_{name}.so")
+    open(path_c, "w").write(src.replace(old, new))
+    subprocess.run(["gcc", "-std=gnu99", "-O2", "-ffp-contract=off", "-fopenmp", "-fPIC",
+                    "-shared", path_c, "-o", path_so, "-lm"], check=True)
+    return path_so
+
+
+def _run_pins(so):
+    env = dict(os.environ, ECHO_ORACLE_LIB=so)
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       env=env, cwd=ROOT, capture_output=True, text=True, timeout=300)
+    return r.returncode
+
+
+def test_every_planted_mistake_fails_a_pin(tmp_path):
+    names = sorted(MUTANTS)
+    sos = [_build(n, str(tmp_path)) for n in names]
+    with ThreadPoolExecutor(max_workers=6) as ex:
+        codes = list(ex.map(_run_pins, sos))
+    survivors = [n for n, c in zip(names, codes) if c == 0]
+    assert not survivors, f"pins did not notice: {survivors}"
+
+
+def test_unmutated_oracle_passes_the_pins():
+    assert _run_pins(O.build()) == 0

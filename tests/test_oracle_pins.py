@@ -1,0 +1,382 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test fixes one part of the oracle by an independent route: the library's
+own fp8/bf16 decoders, exact rational arithmetic, a brute-force sort, closed
+forms, the review page's worked metadata example, hand-derived state machines,
+and invariants that must hold after every step.  None of them re-types the
+oracle's C code.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------- formats
+
+def test_e4m3_decode_matches_torch_for_every_code():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float32).numpy().astype(np.float64)
+    got = np.array([O.e4m3_value(c) for c in range(256)])
+    assert np.array_equal(np.isnan(ref), np.isnan(got))
+    m = ~np.isnan(ref)
+    assert np.array_equal(ref[m], got[m])
+    # anchor points of the OCP E4M3FN format
+    assert O.e4m3_value(0x7E) == 448.0 and O.e4m3_value(0xFE) == -448.0
+    assert O.e4m3_value(0x01) == 2.0 ** -9 and O.e4m3_value(0x08) == 2.0 ** -6
+    assert O.e4m3_value(0x38) == 1.0 and np.isnan(O.e4m3_value(0x7F))
+
+
+def test_bf16_decode_matches_torch_for_every_code():
+    codes = torch.arange(65536, dtype=torch.int32).to(torch.int16)
+    ref = codes.view(torch.bfloat16).to(torch.float32).numpy().astype(np.float64)
+    lib = O.lib()
+    got = np.array([lib.orc_bf16_value(c) for c in range(65536)])
+    assert np.array_equal(np.isnan(ref), np.isnan(got))
+    m = ~np.isnan(ref)
+    assert np.array_equal(ref[m], got[m])
+
+
+# ------------------------------------------------------------------ scores
+
+def _f32_nearest_even(x: Fraction) -> np.float32:
+    """Exact round-to-nearest-even of a rational to binary32 (finite range)."""
+    f = np.float32(float(x))
+    cands = {f, np.nextafter(f, np.float32(np.inf)), np.nextafter(f, np.float32(-np.inf))}
+    best = None
+    for c in cands:
+        d = abs(Fraction(float(c)) - x)
+        key = (d, int(np.array(c, np.float32).view(np.uint32)) & 1)
+        if best is None or key < best[0]:
+            best = (key, c)
+    out = best[1]
+    return np.float32(0.0) if out == 0 else out
+
+
+def _rand_case(H, D, n, seed):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn((H, D), generator=g).to(torch.bfloat16)
+    w = torch.rand((H,), generator=g)
+    k = torch.randn((n, D), generator=g).to(torch.float8_e4m3fn)
+    return q, w, k
+
+
+@pytest.mark.parametrize("H,D,n,seed", [(4, 32, 48, 0), (8, 16, 40, 1), (3, 5, 64, 2)])
+def test_scores_equal_exact_rational_arithmetic(H, D, n, seed):
+    q, w, k = _rand_case(H, D, n, seed)
+    qf = [[Fraction(float(v)) for v in row] for row in q.float().tolist()]
+    wf = [Fraction(float(v)) for v in w.tolist()]
+    kf = [[Fraction(float(v)) for v in row] for row in k.float().tolist()]
+    got = O.scores(q.view(torch.int16).numpy().view(np.uint16), w.numpy(),
+                   k.view(torch.uint8).numpy())
+    for s in range(n):
+        exact = Fraction(0)
+        for j in range(H):
+            x = sum(qf[j][d] * kf[s][d] for d in range(D))
+            exact += wf[j] * (x if x > 0 else 0)
+        ref = _f32_nearest_even(exact)
+        assert got[s].view(np.uint32) == np.float32(ref).view(np.uint32), (s, got[s], ref)
+
+
+def _codes(q_vals, w_vals, k_vals):
+    q = torch.tensor(q_vals, dtype=torch.float32).to(torch.bfloat16)
+    k = torch.tensor(k_vals, dtype=torch.float32).to(torch.float8_e4m3fn)
+    return (q.view(torch.int16).numpy().view(np.uint16), np.array(w_vals, np.float32),
+            k.view(torch.uint8).numpy())
+
+
+def test_scores_closed_forms():
+    # one head, one dim: score = w * max(0, q*k)
+    q, w, k = _codes([[1.5]], [0.25], [[2.0], [-2.0], [0.0], [448.0]])
+    s = O.scores(q, w, k)
+    assert s.tolist() == [0.75, 0.0, 0.0, 168.0]
+    assert all(np.array(s, np.float32).view(np.uint32)[1:3] == 0)  # +0, never -0
+    # ReLU is per head, before the weighted sum: heads (+3, -3) give w0*3, not 0
+    q, w, k = _codes([[1.0, 1.0], [-1.0, -1.0]], [0.5, 0.75], [[1.0, 2.0]])
+    assert O.scores(q, w, k).tolist() == [1.5]
+    # a zero weight removes its head
+    q, w, k = _codes([[1.0], [2.0]], [0.0, 1.0], [[4.0]])
+    assert O.scores(q, w, k).tolist() == [8.0]
+
+
+def test_scores_homogeneity_and_token_independence():
+    q, w, k = _rand_case(6, 24, 50, 7)
+    qc = q.view(torch.int16).numpy().view(np.uint16)
+    kc = k.view(torch.uint8).numpy()
+    base = O.scores(qc, w.numpy(), kc)
+    q2 = (q.float() * 2).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.scores(q2, w.numpy(), kc), base * 2)      # relu(2x) = 2 relu(x)
+    assert np.array_equal(O.scores(qc, (w * 4).numpy(), kc), base * 4)
+    perm = np.random.default_rng(0).permutation(50)
+    assert np.array_equal(O.scores(qc, w.numpy(), kc[perm]), base[perm])
+
+
+# ------------------------------------------------------------------ top-k
+
+def _brute_topk(sc, k):
+    order = sorted(range(len(sc)), key=lambda i: (-float(sc[i]), i))[: min(k, len(sc))]
+    return sorted(order), (float(sc[order[-1]]) if order else None)
+
+
+@pytest.mark.parametrize("n,k,seed", [(0, 4, 0), (3, 8, 1), (8, 8, 2), (50, 7, 3),
+                                      (300, 64, 4), (1000, 256, 5)])
+def test_topk_equals_full_sort_with_ties(n, k, seed):
+    rng = np.random.default_rng(seed)
+    sc = rng.integers(0, 12, size=n).astype(np.float32)  # many ties
+    sel, kth = O.topk(sc, k)
+    ref, ref_kth = _brute_topk(sc, k)
+    assert sel.tolist() == ref
+    if ref:
+        assert kth == ref_kth
+        chosen = np.zeros(n, bool)
+        chosen[sel] = True
+        if (~chosen).any():
+            assert sc[chosen].min() >= sc[~chosen].max()
+
+
+def test_topk_lower_index_wins_ties():
+    sel, kth = O.topk(np.array([5, 1, 5, 5, 1], np.float32), 2)
+    assert sel.tolist() == [0, 2] and kth == 5.0
+
+
+# -------------------------------------------------------------------- EMA
+
+def test_ema_closed_form_at_half():
+    s0, s1, s2 = 96.0, 40.0, 7.0
+    th = O.ema_update(np.inf, s0)                    # first estimate seeds theta
+    assert th == s0
+    th = O.ema_update(th, s1)
+    assert th == (s0 + s1) / 2
+    th = O.ema_update(th, s2)
+    assert th == (s0 + s1) / 4 + s2 / 2
+
+
+def test_ema_is_fp32_and_weights_new_sample_by_alpha():
+    th, s = np.float32(3.1), np.float32(1.7)
+    a = np.float32(0.3)
+    ref = np.float32(np.float32(a * s) + np.float32(np.float32(1) - a) * th)
+    assert np.float32(O.ema_update(float(th), float(s), float(a))) == ref
+    assert O.ema_update(float("-inf"), 5.0) == float("-inf")
+
+
+# --------------------------------------------------------------- metadata
+
+def test_metadata_matches_pages_worked_example():
+    g = json.load(open(os.path.join(GOLDEN, "metadata_example.json")))
+    per_layer = O.meta_bytes(g["n_host"], g["n_gpu"])
+    assert per_layer == g["bytes_per_layer_exact"]
+    mb = g["mb"]
+    tol = g["approx_rel_tolerance"]
+    assert abs(per_layer / mb - g["approx_mb_per_layer"]) <= tol * g["approx_mb_per_layer"]
+    model = per_layer * g["layers"] / mb
+    assert abs(model - g["approx_mb_model"]) <= tol * g["approx_mb_model"]
+
+
+def test_metadata_is_sum_of_structures():
+    lay = O.OracleLayer(4, 8, 2, 4, n_host=1000, n_gpu=37, max_batch=1, keep_pool=False)
+    idxbuf_bytes = 4 * 37  # the index buffer is scratch that the GPU side keeps per layer
+    total = (lay.h2g.nbytes + lay.g2h.nbytes + lay.prio.nbytes + lay.free.nbytes + idxbuf_bytes)
+    assert total == O.meta_bytes(1000, 37)
+
+
+# ---------------------------------------------- hand-derived state machines
+
+def _ext(ctx, winners, stride=None):
+    """External scores: the listed tokens get descending high scores."""
+    sc = np.zeros((1, stride or ctx), np.float32)
+    for r, s in enumerate(winners):
+        sc[0, s] = 100.0 - r
+    return sc
+
+
+def _tiny_layer(n_host, n_gpu, k, cap_div, latent=2):
+    lay = O.OracleLayer(H=1, D=1, k=k, latent=latent, n_host=n_host, n_gpu=n_gpu, max_batch=1,
+                        cap_div=cap_div)
+    hostkv = (np.arange(n_host * latent, dtype=np.uint16) + 1).reshape(n_host, latent)
+    return lay, hostkv
+
+
+def _step(lay, hostkv, ctx, winners, mode):
+    q = np.zeros((1, 1, 1), np.uint16)
+    w = np.zeros((1, 1), np.float32)
+    kidx = np.zeros((lay.cfg.n_host, 1), np.uint8)
+    return lay.step([0], [ctx], q, w, kidx, hostkv, mode=mode, ext_scores=_ext(ctx, winners))
+
+
+def test_lru_eviction_with_reserve_by_hand():
+    # 8 host tokens, 4 slots, k=2, cap=min(2, ceil(8/8))=1 -> reserve R=1; no prefetch
+    lay, hk = _tiny_layer(8, 4, 2, 8)
+    P = O.MODE_POS_INF
+    o = _step(lay, hk, 8, [1, 5], P)      # t=0: both miss -> slots 0,1
+    assert o["sel_slot"][0].tolist() == [0, 1] and o["n_evict"] == 0
+    o = _step(lay, hk, 8, [2, 5], P)      # t=1: 5 hits (slot 1 -> prio 1); 2 -> slot 2
+    assert o["n_miss"].tolist() == [1] and o["sel_slot"][0].tolist() == [2, 1]
+    assert o["n_evict"] == 0              # 1 miss + R=1 - 2 free = 0
+    assert lay.prio.tolist() == [0, 1, 1, -1]
+    o = _step(lay, hk, 8, [3, 6], P)      # t=2: 2 misses, 1 free -> evict 2 (LRU)
+    assert o["evicted"].tolist() == [0, 1]   # (prio 0, slot 0) then (prio 1, slot 1)
+    assert o["sel_slot"][0].tolist() == [0, 1]
+    assert lay.h2g.tolist() == [-1, -1, 2, 0, -1, -1, 1, -1]
+    assert lay.g2h.tolist() == [3, 6, 2, -1]
+    o = _step(lay, hk, 8, [2, 3], P)      # t=3: all hit, nothing moves
+    assert o["n_miss"].tolist() == [0] and o["n_evict"] == 0
+    assert lay.prio.tolist() == [3, 2, 3, -1] and lay.t == 4
+    for h in range(8):                    # pool rows equal their host rows
+        if lay.h2g[h] >= 0:
+            assert np.array_equal(lay.pool[lay.h2g[h]], hk[h])
+
+
+def test_prefetch_cap_free_list_and_protection_by_hand():
+    # cap = min(2, ceil(8/4)) = 2; threshold -inf: every non-resident token is a candidate
+    lay, hk = _tiny_layer(8, 4, 2, 4)
+    N = O.MODE_NEG_INF
+    o = _step(lay, hk, 8, [1, 5], N)      # t=0: prefetch tokens 0,1 -> slots 0,1
+    assert o["pf_tok"][0, :2].tolist() == [0, 1] and o["pf_slot"][0, :2].tolist() == [0, 1]
+    assert o["n_cand"].tolist() == [8] and o["n_miss"].tolist() == [1]
+    assert o["sel_slot"][0].tolist() == [1, 2] and o["n_evict"] == 0
+    o = _step(lay, hk, 8, [0, 7], N)      # t=1: one free slot -> only token 2 prefetched
+    assert o["n_pf"].tolist() == [1] and o["pf_tok"][0, 0] == 2 and o["pf_slot"][0, 0] == 3
+    assert o["n_cand"].tolist() == [5]
+    # E = slots 1 (token 1) and 2 (token 5), both prio 0; the prefetched token 2 is protected
+    assert o["evicted"].tolist() == [1, 2]
+    assert o["sel_slot"][0].tolist() == [0, 1]
+    assert lay.h2g.tolist() == [0, -1, 3, -1, -1, -1, -1, 1]
+    assert lay.prio.tolist() == [1, 1, -1, 1]
+
+
+def test_prefetch_cap_rounds_up():
+    # ctx 7, cap_div 4 -> cap = min(k=4, ceil(7/4)=2) = 2
+    lay, hk = _tiny_layer(8, 8, 4, 4)
+    o = _step(lay, hk, 7, [0, 1, 2, 3], O.MODE_NEG_INF)
+    assert o["n_pf"].tolist() == [2] and o["pf_tok"][0, :2].tolist() == [0, 1]
+    assert o["n_cand"].tolist() == [7]
+
+
+def test_capacity_error_leaves_state_consistent():
+    lay, hk = _tiny_layer(8, 1, 2, 8)
+    o = _step(lay, hk, 8, [3, 4], O.MODE_POS_INF)
+    assert o["status"] == O.ECAPACITY and lay.t == 0
+    assert (lay.h2g == -1).all() and lay.free.tolist() == [1]
+
+
+def test_ema_threshold_drives_prefetch_by_hand():
+    lay, hk = _tiny_layer(8, 8, 2, 4)
+    E = O.MODE_EMA
+    sc0 = np.array([[1, 9, 3, 8, 2, 7, 0, 4]], np.float32)   # top-2: 9 (tok1), 8 (tok3)
+    q = np.zeros((1, 1, 1), np.uint16)
+    w = np.zeros((1, 1), np.float32)
+    kidx = np.zeros((8, 1), np.uint8)
+    o = lay.step([0], [8], q, w, kidx, hk, mode=E, ext_scores=sc0)
+    assert o["n_pf"].tolist() == [0]      # theta=+inf before the first k-th score
+    assert lay.theta[0] == 8.0 and o["kth"][0] == 8.0
+    sc1 = np.array([[1, 9, 3, 8, 2, 7.5, 8.5, 8]], np.float32)
+    o = lay.step([0], [8], q, w, kidx, hk, mode=E, ext_scores=sc1)
+    # candidates: score strictly above 8 and not resident -> token 6 (8.5) only; token 7
+    # sits exactly on the threshold and is not a candidate
+    assert o["n_cand"].tolist() == [1] and o["pf_tok"][0, 0] == 6
+    assert o["sel_tok"][0].tolist() == [1, 6] and o["n_miss"].tolist() == [0]
+    assert lay.theta[0] == np.float32(0.5 * 8.0 + 0.5 * 8.5)
+
+
+# ------------------------------------------ invariants and losslessness
+
+def _check_invariants(lay, o, ctx, host_base, hk):
+    h2g, g2h, prio, free = lay.h2g, lay.g2h, lay.prio, lay.free
+    res = np.nonzero(h2g >= 0)[0]
+    assert np.array_equal(g2h[h2g[res]], res)                         # mutual inverses
+    occ = np.nonzero(g2h >= 0)[0]
+    assert np.array_equal(h2g[g2h[occ]], occ)
+    assert np.array_equal(free == 1, g2h == -1) and np.array_equal(free == 1, prio == -1)
+    assert res.size + int(free.sum()) == g2h.size
+    assert (prio < lay.t).all()                                       # prio <= t_step
+    for b in range(len(ctx)):
+        sel = o["sel_tok"][b, : o["n_sel"][b]]
+        hs = host_base[b] + sel
+        assert (h2g[hs] >= 0).all()                                   # selected resident
+        assert np.array_equal(o["sel_slot"][b, : sel.size], h2g[hs])
+        assert (prio[h2g[hs]] == lay.t - 1).all()                     # touched this step
+        assert np.array_equal(lay.pool[h2g[hs]], hk[hs])              # bytes equal host
+    for h in res:
+        assert np.array_equal(lay.pool[h2g[h]], hk[h])
+
+
+def _small_workload(seed=0, B=2, ctx=(700, 513), H=4, D=32, k=64, n_gpu=400, steps=6,
+                    rho=0.9):
+    rng = np.random.default_rng(seed)
+    ctx = np.array(ctx, np.int32)
+    host_base = np.concatenate([[0], np.cumsum(ctx)[:-1]]).astype(np.int32)
+    n_host = int(ctx.sum()) + 17
+    kid = torch.from_numpy(rng.standard_normal((n_host, D)).astype(np.float32))
+    kidx = kid.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    hk = rng.integers(0, 65536, size=(n_host, 8)).astype(np.uint16)
+    w = rng.random((B, H)).astype(np.float32)
+    st = rng.standard_normal((B, H, D)).astype(np.float32)
+    qs = []
+    for _ in range(steps):
+        qs.append(torch.from_numpy(st).to(torch.bfloat16).view(torch.int16).numpy()
+                  .view(np.uint16))
+        st = rho * st + np.sqrt(1 - rho * rho) * rng.standard_normal(st.shape).astype(np.float32)
+    return dict(ctx=ctx, host_base=host_base, n_host=n_host, kidx=kidx, hk=hk, w=w, qs=qs,
+                H=H, D=D, k=k, n_gpu=n_gpu)
+
+
+def _run_modes(wk, mode):
+    lay = O.OracleLayer(wk["H"], wk["D"], wk["k"], 8, wk["n_host"], wk["n_gpu"],
+                        len(wk["ctx"]), cap_div=32)
+    outs = []
+    for q in wk["qs"]:
+        o = lay.step(wk["host_base"], wk["ctx"], q, wk["w"], wk["kidx"], wk["hk"], mode=mode)
+        assert o["status"] == O.OK
+        _check_invariants(lay, o, wk["ctx"], wk["host_base"], wk["hk"])
+        gathered = [lay.pool[o["sel_slot"][b, : o["n_sel"][b]]].copy()
+                    for b in range(len(wk["ctx"]))]
+        outs.append((o, gathered))
+    return lay, outs
+
+
+def test_lossless_across_threshold_modes_and_invariants():
+    wk = _small_workload()
+    runs = {m: _run_modes(wk, m) for m in (O.MODE_EMA, O.MODE_NEG_INF, O.MODE_POS_INF)}
+    base = runs[O.MODE_POS_INF][1]
+    for m in (O.MODE_EMA, O.MODE_NEG_INF):
+        for (o, g), (ob, gb) in zip(runs[m][1], base):
+            assert np.array_equal(o["sel_tok"], ob["sel_tok"])
+            for x, y in zip(g, gb):
+                assert np.array_equal(x, y)
+    # the modes really differ in what they move
+    pf = {m: sum(int(o["n_pf"].sum()) for o, _ in runs[m][1]) for m in runs}
+    assert pf[O.MODE_POS_INF] == 0 and pf[O.MODE_NEG_INF] > pf[O.MODE_EMA] > 0
+    miss = {m: sum(int(o["n_miss"].sum()) for o, _ in runs[m][1][1:]) for m in runs}
+    assert miss[O.MODE_EMA] < miss[O.MODE_POS_INF]
+
+
+def test_eviction_pressure_keeps_invariants():
+    # a pool barely larger than one step's selection forces eviction every step
+    wk = _small_workload(seed=3, n_gpu=2 * 64 + 2 * 22 + 5, rho=0.3, steps=8)
+    for m in (O.MODE_EMA, O.MODE_NEG_INF, O.MODE_POS_INF):
+        lay, outs = _run_modes(wk, m)
+        assert sum(o["n_evict"] for o, _ in outs) > 0
+
+
+def test_oracle_is_deterministic():
+    wk = _small_workload(seed=5, steps=3)
+    a = _run_modes(wk, O.MODE_EMA)[0].snapshot()
+    b = _run_modes(wk, O.MODE_EMA)[0].snapshot()
+    for key in a:
+        assert np.array_equal(a[key], b[key])
+
+
+def test_short_context_selects_everything_and_skips_ema():
+    wk = _small_workload(seed=6, ctx=(40, 64), steps=2)
+    lay, outs = _run_modes(wk, O.MODE_EMA)
+    o = outs[0][0]
+    assert o["n_sel"].tolist() == [40, 64]
+    assert o["sel_tok"][0, :40].tolist() == list(range(40))
+    assert np.isinf(lay.theta[0]) and lay.theta[1] == o["kth"][1]
