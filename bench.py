@@ -1,0 +1,324 @@
+"""Decode-step benchmark of the ECHO offload hot path on one MI355X.
+
+Default workload: capacity-constrained decode -- batch 32, contexts uniform in
+[80,000, 100,000], 61 layers run one after another in one hipGraph per decode
+step, indexer 64 heads x 128 (bf16 q, fp8-E4M3 K), top-k 2048, GPU pool 110,000
+slots per layer, host pool 3,200,000 tokens x 576 bf16, query AR(1) rho 0.98.
+A "step" is one decode step: every layer runs indexer + prefetch, exact top-k,
+protect/evict/alloc and recall for the whole batch.  The metric is layer-steps/s
+(layers x steps / elapsed).  Inputs are seeded synthetic tensors resident in HBM
+(and in pinned host memory for the host pool) before the timed region starts.
+
+Also reported: the indexer kernel's HBM roofline (algorithmic bytes: 128 B of K
+read + 4 B of score written per scored token), the recall host-link rate, the
+measured pinned host-link peaks, the GPU-cache hit rate and a CPU baseline of the
+oracle on a bounded sample of one layer-step.
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload capacity]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+BYTES_PER_SCORED_TOKEN = 128 + 4
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=16)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--workload", default="capacity")
+    p.add_argument("--layers", type=int, default=None, help="override the layer count")
+    p.add_argument("--host-pools", type=int, default=4,
+                   help="distinct pinned host pools; layers share them round-robin")
+    p.add_argument("--breakdown-steps", type=int, default=2)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-requests", type=int, default=8)
+    p.add_argument("--mode", default="ema", choices=["ema", "neg_inf", "pos_inf"])
+    p.add_argument("--seed", type=int, default=0)
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the decode hot "
+              "path shards by request, one independent copy per GPU, and this build measures "
+              "the single-GPU share.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from kv_cache_offload_fp8_amd import abi
+    from kv_cache_offload_fp8_amd import runtime as R
+    from synth import get
+    from synth import gen as G
+
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    wl = get(args.workload)
+    L = args.layers or wl.layers
+    mode = {"ema": abi.ECHO_THETA_EMA, "neg_inf": abi.ECHO_THETA_NEG_INF,
+            "pos_inf": abi.ECHO_THETA_POS_INF}[args.mode]
+    ctx = wl.contexts(args.seed)
+    base = G.host_layout(ctx)
+    B = int(ctx.size)
+    total_tok = int(ctx.sum())
+    q_ring = args.warmup + args.steps + args.breakdown_steps
+    dims = R.make_dims(wl.heads, wl.head_dim, wl.top_k, wl.n_host, wl.n_gpu, B, int(ctx.max()),
+                       wl.latent, wl.alpha, wl.cap_div, q_ring)
+    log(f"[bench] workload {wl.name}: B={B} ctx {ctx.min()}..{ctx.max()} (sum {total_tok}) "
+        f"L={L} n_gpu={wl.n_gpu} n_host={wl.n_host} q_ring={q_ring}")
+
+    # ---------------------------------------------------------------- setup
+    t0 = time.time()
+    npools = max(1, min(args.host_pools, L))
+    pools = []
+    for i in range(npools):
+        hp = R.HostPool(wl.n_host, wl.latent)
+        lat = G.gen_latents(wl, i, ctx, base, dev, args.seed,
+                            out=torch.empty((wl.n_host, wl.latent), dtype=torch.int16,
+                                            device=dev))
+        hp.tensor.copy_(lat)
+        del lat
+        pools.append(hp)
+    log(f"[bench] {npools} host pools of {wl.n_host * wl.latent * 2 / 1e9:.2f} GB ready "
+        f"({time.time() - t0:.1f}s)")
+    layers = []
+    for l in range(L):
+        kidx = G.gen_kidx(wl, l, ctx, base, dev, args.seed)
+        lay = R.Layer(dims, kidx, pools[l % npools], B, dev)
+        lay.q.copy_(G.gen_q(wl, l, B, q_ring, dev, args.seed))
+        lay.w.copy_(G.gen_w(wl, l, B, dev, args.seed))
+        lay.init()
+        layers.append(lay)
+    batch = R.Batch(base, ctx, dev)
+    ws = R.Workspace(dims, dev)
+    ws.reset()
+    torch.cuda.synchronize()
+    log(f"[bench] {L} layers ready ({time.time() - t0:.1f}s); meta/layer "
+        f"{layers[0].meta_bytes()} B = echo_meta_bytes {abi.echo_meta_bytes(wl.n_host, wl.n_gpu)}")
+
+    def one_step(stream):
+        for lay in layers:
+            R.check(abi.echo_layer_step(dims, lay.struct, batch.struct, ws.ws, mode, stream),
+                    "echo_layer_step")
+
+    # ------------------------------------------------------- graph capture
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    with torch.cuda.stream(cs):
+        with torch.cuda.graph(g, stream=cs):
+            one_step(cs.cuda_stream)
+    torch.cuda.synchronize()
+    log("[bench] captured one decode step "
+        f"({L} layers) in a graph; warmup {args.warmup}")
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    st = int(ws.status.item())
+    if st != 0:
+        raise SystemExit(f"device status after warmup: {abi.echo_status_string(st)}")
+
+    # -------------------------------------------------------- timed region
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    gpu_ms = ev0.elapsed_time(ev1)
+    elapsed = max(wall, gpu_ms / 1e3)
+    st = int(ws.status.item())
+    if st != 0:
+        raise SystemExit(f"device status after timed steps: {abi.echo_status_string(st)}")
+    ms_per_step = elapsed * 1e3 / args.steps
+    layer_steps_per_s = args.steps * L / elapsed
+    log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step, "
+        f"{layer_steps_per_s:.1f} layer-steps/s")
+
+    # ------------------------------------------- per-phase breakdown (eager)
+    s = torch.cuda.current_stream()
+    sh = s.cuda_stream
+    nph = 4
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nph + 1)]
+           for _ in range(args.breakdown_steps * L)]
+    miss_rows, sel_rows, pf_rows = [], [], []
+    i = 0
+    for _ in range(args.breakdown_steps):
+        for lay in layers:
+            e = evs[i]
+            e[0].record(s)
+            R.check(abi.echo_indexer_prefetch(dims, lay.struct, batch.struct, ws.ws, mode, sh),
+                    "indexer")
+            e[1].record(s)
+            R.check(abi.echo_topk(dims, ws.ws.scores, dims.max_ctx, batch.struct, ws.ws,
+                                  lay.struct.theta if mode == abi.ECHO_THETA_EMA else None, sh),
+                    "topk")
+            e[2].record(s)
+            R.check(abi.echo_cache_alloc_evict(dims, lay.struct, batch.struct, ws.ws, sh),
+                    "alloc_evict")
+            e[3].record(s)
+            R.check(abi.echo_recall(dims, lay.struct, ws.ws, sh), "recall")
+            e[4].record(s)
+            R.check(abi.echo_step_advance(lay.struct, ws.ws, sh), "advance")
+            c = ws.counters.clone()
+            miss_rows.append(c[abi.ECHO_CNT_MISS])
+            pf_rows.append(c[abi.ECHO_CNT_PREFETCH])
+            sel_rows.append(ws.n_sel[:B].sum())
+            i += 1
+    torch.cuda.synchronize()
+    st = int(ws.status.item())
+    if st != 0:
+        raise SystemExit(f"device status after breakdown: {abi.echo_status_string(st)}")
+    ph = np.array([[evs[j][p].elapsed_time(evs[j][p + 1]) for p in range(nph)]
+                   for j in range(len(evs))])  # ms
+    misses = np.array([int(x) for x in miss_rows])
+    prefetched = np.array([int(x) for x in pf_rows])
+    selected = np.array([int(x) for x in sel_rows])
+    idx_ms = float(ph[:, 0].mean())
+    idx_bytes = total_tok * BYTES_PER_SCORED_TOKEN
+    idx_gbps = idx_bytes / (idx_ms * 1e-3) / 1e9
+    row = wl.latent * 2
+    recall_ms = ph[:, 3]
+    recall_gbps = float((misses * row).sum() / (recall_ms.sum() * 1e-3) / 1e9)
+    hit = float(1.0 - misses.sum() / max(1, selected.sum()))
+    log(f"[bench] phases (ms, mean over {len(evs)} layer-steps): indexer {idx_ms:.4f} "
+        f"topk {ph[:, 1].mean():.4f} alloc/evict {ph[:, 2].mean():.4f} "
+        f"recall {recall_ms.mean():.4f}; hit rate {hit:.4f}; misses/layer-step "
+        f"{misses.mean():.0f}; prefetched/layer-step {prefetched.mean():.0f}")
+
+    # ------------------------------------------------------ host-link peaks
+    n_rows = min(wl.n_host, 65536)
+    big = pools[0]
+    dst = torch.empty((n_rows, wl.latent), dtype=torch.int16, device=dev)
+    src = big.tensor[:n_rows]
+    for _ in range(2):
+        dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src, non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    memcpy_gbps = 5 * n_rows * row / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    # zero-copy: echo_recall over a synthetic recall list of n_rows rows into layer 0's pool
+    nz = min(n_rows, B * wl.top_k, wl.n_gpu)
+    ws.recall_h[:nz] = torch.arange(nz, dtype=torch.int32, device=dev)
+    ws.recall_g[:nz] = torch.arange(nz, dtype=torch.int32, device=dev)
+    ws.counters[abi.ECHO_CNT_MISS] = nz
+    R.check(abi.echo_recall(dims, layers[0].struct, ws.ws, sh), "recall")
+    e0.record()
+    for _ in range(5):
+        R.check(abi.echo_recall(dims, layers[0].struct, ws.ws, sh), "recall")
+    e1.record()
+    torch.cuda.synchronize()
+    zc_gbps = 5 * nz * row / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    link_peak = max(memcpy_gbps, zc_gbps)
+    log(f"[bench] host link: hipMemcpy H2D {memcpy_gbps:.1f} GB/s, zero-copy recall kernel "
+        f"{zc_gbps:.1f} GB/s over {nz} rows")
+
+    # ------------------------------------------------------- CPU baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, ctx, base, layers[0], args, dims)
+
+    out = {
+        "metric": "decode layer-steps/s @100K ctx; indexer HBM GB/s % peak; recall host-link GB/s",
+        "value": round(layer_steps_per_s, 3),
+        "unit": "layer-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 x fp8->bf16 MFMA, fp32 accumulate; int32 management",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: batch {B}, ctx U[{wl.ctx_lo},{wl.ctx_hi}], "
+                               f"{L} layers in one hipGraph per step, indexer {wl.heads}x"
+                               f"{wl.head_dim}, top-k {wl.top_k}, GPU pool {wl.n_gpu}/layer, "
+                               f"host pool {wl.n_host} x {wl.latent} bf16, rho {wl.rho}",
+                   "global_batch": B, "seq_len": int(ctx.max()), "layers": L,
+                   "threshold_mode": args.mode},
+        "roofline": {"kernel": "echo_indexer_prefetch (k_begin + k_score)", "bound": "hbm",
+                     "achieved": round(idx_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(idx_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": idx_bytes, "avg_launch_ms": round(idx_ms, 5)},
+        "indexer_hbm_gbps": round(idx_gbps, 1),
+        "recall_host_link_gbps": round(recall_gbps, 2),
+        "recall_frac_of_link_peak": round(recall_gbps / link_peak, 4),
+        "host_link_peak_gbps": {"hipMemcpy_h2d": round(memcpy_gbps, 2),
+                                "zero_copy_recall_kernel": round(zc_gbps, 2)},
+        "phase_ms": {"indexer": round(idx_ms, 5), "topk": round(float(ph[:, 1].mean()), 5),
+                     "alloc_evict": round(float(ph[:, 2].mean()), 5),
+                     "recall": round(float(recall_ms.mean()), 5)},
+        "hit_rate": round(hit, 5),
+        "misses_per_layer_step": round(float(misses.mean()), 1),
+        "prefetched_per_layer_step": round(float(prefetched.mean()), 1),
+        "cpu_baseline": cpu,
+    }
+    for hp in pools:
+        hp.close()
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(wl, ctx, base, lay0, args, dims):
+    """The oracle, as it stands, on a bounded sample of layer 0's first decode step:
+    the first `--cpu-sample-requests` requests of the batch.  Scaled to layer-steps/s
+    by the share of scored tokens the sample covers."""
+    import torch
+
+    from oracle import oracle as O
+    from synth import gen as G
+
+    nb = max(1, min(args.cpu_sample_requests, ctx.size))
+    sctx = ctx[:nb].astype(np.int32)
+    sbase = G.host_layout(sctx)
+    n = int(sctx.sum())
+    kid = np.zeros((n, wl.head_dim), np.uint8)
+    kdev = lay0.kidx
+    for b in range(nb):
+        kid[sbase[b]:sbase[b] + sctx[b]] = kdev[int(base[b]):int(base[b]) + int(sctx[b])].cpu() \
+            .numpy()
+    q0 = lay0.q[0, :nb].contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+    w0 = lay0.w[:nb].cpu().numpy()
+    orc = O.OracleLayer(wl.heads, wl.head_dim, wl.top_k, wl.latent, n, wl.n_gpu, nb,
+                        wl.cap_div, wl.alpha, keep_pool=False)
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    t0 = time.perf_counter()
+    o = orc.step(sbase, sctx, q0, w0, kid, None, mode=O.MODE_EMA)
+    dt = time.perf_counter() - t0
+    assert o["status"] == O.OK
+    frac = n / float(ctx.sum())
+    per_layer_step = dt / frac
+    log(f"[bench] cpu oracle: {nb} requests ({n} tokens) in {dt:.2f}s on {threads} threads "
+        f"-> {per_layer_step:.1f}s per full layer-step")
+    return {"value": round(1.0 / per_layer_step, 6), "unit": "layer-steps/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"layer 0, first decode step, {nb} of {ctx.size} requests ({n} scored "
+                      f"tokens, {frac:.3%} of the layer-step's tokens); time scaled by tokens"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,239 @@
+/*
+ * echo.h -- C ABI of the MI355X (gfx950) decode-step hot path of ECHO's lossless
+ * KV-cache offloading for sparse-attention (DeepSeek Sparse Attention) models.
+ *
+ * Source: "ECHO: Efficient KV Cache Offloading with Lossless Prefetching for
+ * Serving Native Sparse Attention LLMs (OSDI 2026)", review page on
+ * awesome-system-papers (cited below as "the ECHO review"), and the podcast show
+ * notes "ECHO: Lossless KV Cache Offloading for Sparse Attention LLMs".  The
+ * pages give no API; the calls below follow their problem statement: every
+ * structure is a fixed-size preallocated device tensor, there is no per-layer
+ * CPU control, the whole step can be captured in one graph, and allocation,
+ * eviction and recall are separate operations (review, "Core method / in-graph
+ * per-layer cache management").
+ *
+ * Conventions shared by every call
+ *  - Every pointer inside the structs is a device address, except where a field
+ *    says otherwise.  `host_kv` is pinned, mapped host memory: its device-visible
+ *    address (with unified addressing, the host pointer returned by hipHostMalloc).
+ *  - The caller allocates and owns all memory.  The library never allocates,
+ *    frees or synchronizes; each call validates its arguments on the host, enqueues
+ *    kernels on `stream` and returns.  Every call can be captured in a hipGraph.
+ *  - Host-side return codes: ECHO_OK, or ECHO_EINVAL (bad argument or shape; nothing
+ *    was enqueued), ECHO_EUNSUPPORTED (a shape this build has no kernel for), or
+ *    ECHO_EHIP (a launch failed).
+ *  - Errors found on the device (capacity, bad device-side lengths, a stuck wait)
+ *    are written to `ws->status`: the first error wins and stays until
+ *    echo_ws_reset.  Once it is set, every later kernel of every call is a no-op,
+ *    and the metadata stays consistent (mutual maps, free flags, priorities).
+ *    Read it after your own synchronization.
+ *  - Token identities: request b of a batch owns host ids
+ *    host_base[b] .. host_base[b] + ctx_len[b] - 1; ranges of different requests
+ *    must not overlap (checked on the device).
+ */
+#ifndef ECHO_H
+#define ECHO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------ status codes */
+enum {
+  ECHO_OK = 0,
+  ECHO_EINVAL = -1,       /* argument or shape check failed                    */
+  ECHO_EHIP = -2,         /* a kernel launch failed                            */
+  ECHO_EUNSUPPORTED = -3, /* shape with no kernel in this build                */
+  ECHO_ECAPACITY = -4,    /* device: free + evictable slots < missed tokens    */
+  ECHO_ETIMEOUT = -5,     /* device: a cross-workgroup wait exceeded 1 s       */
+  ECHO_EDEVARG = -6       /* device: ctx_len/host_base out of range or overlap */
+};
+
+/* Prefetch threshold modes.  EMA: the threshold is the exponential moving
+ * average of past k-th scores (ECHO review, "Core method / decode"; smoothing
+ * from "Key observations", observation 2).  NEG_INF admits every non-resident
+ * token (up to the cap); POS_INF disables prefetch.  The selected set and the
+ * gathered KV do not depend on the mode: that is the losslessness property. */
+enum { ECHO_THETA_EMA = 0, ECHO_THETA_NEG_INF = 1, ECHO_THETA_POS_INF = 2 };
+
+/* Indices into echo_ws_t.counters (int32, written by the step's kernels). */
+enum {
+  ECHO_CNT_MISS = 0,      /* selected tokens that were not resident (all requests) */
+  ECHO_CNT_EVICT = 1,     /* slots evicted this step                               */
+  ECHO_CNT_FREE = 2,      /* free slots after prefetch, before eviction            */
+  ECHO_CNT_EVICTABLE = 3, /* occupied slots with priority < t                      */
+  ECHO_CNT_FREE_END = 4,  /* free slots after allocation                           */
+  ECHO_CNT_PREFETCH = 5,  /* tokens prefetched this step (all requests)            */
+  ECHO_NCOUNTERS = 16
+};
+
+/* Words of per-layer control state (echo_layer_t.ctl). */
+enum {
+  ECHO_CTL_STEP = 0,  /* decode-step counter t of this layer                        */
+  ECHO_CTL_NFREE = 1, /* length of the ascending free list kept in meta.idxbuf       */
+  ECHO_CTL_WORDS = 4
+};
+
+/* Shapes.  Supported by this build: 1 <= n_heads <= 64; head_dim in {32, 64, 96,
+ * 128}; 1 <= top_k <= 4096; latent_dim*2 a multiple of 16 bytes; n_host < 2^31;
+ * 1 <= n_gpu < 2^31; 1 <= max_batch <= 64; 1 <= max_ctx < 2^31; prefetch_cap_div
+ * >= 1; q_ring >= 1; 0 < ema_alpha <= 1. */
+typedef struct {
+  int32_t n_heads;          /* H: indexer heads                                     */
+  int32_t head_dim;         /* D: indexer dimension (bytes per fp8 K row)          */
+  int32_t top_k;            /* k: tokens selected per request (2048 in DSA)        */
+  int32_t latent_dim;       /* MLA latent elements per token (576 bf16)            */
+  int64_t n_host;           /* N_H: host pool tokens                               */
+  int32_t n_gpu;            /* N_G: GPU pool slots per layer                       */
+  int32_t max_batch;        /* largest batch any call will use                     */
+  int32_t max_ctx;          /* largest context any request will have               */
+  float ema_alpha;          /* EMA smoothing: theta <- a*s_k + (1-a)*theta (0.5)   */
+  int32_t prefetch_cap_div; /* per-request prefetch cap = min(k, ceil(ctx/div))    */
+  int32_t q_ring;           /* query slots in echo_layer_t.q, used as t mod q_ring */
+} echo_dims_t;
+
+/* Per-layer cache-management metadata (ECHO review, "Core method / in-graph
+ * per-layer cache management"): a free bitmap (one byte per slot), an eviction
+ * priority (the step of last use), an index buffer (the ascending free list) and
+ * the two maps.  Total 4*n_host + 13*n_gpu bytes (echo_meta_bytes). */
+typedef struct {
+  int32_t *h2g;        /* [n_host]  GPU slot of each host token, -1 if not resident */
+  int32_t *g2h;        /* [n_gpu]   host token held by each slot, -1 if free        */
+  int32_t *prio;       /* [n_gpu]   step of last use, -1 if free                    */
+  int32_t *idxbuf;     /* [n_gpu]   ascending free slots, first ctl[NFREE] valid     */
+  uint8_t *free_flags; /* [n_gpu]   1 = free                                         */
+} echo_layer_meta_t;
+
+/* One layer's tensors. */
+typedef struct {
+  echo_layer_meta_t meta;
+  const uint8_t *k_index;  /* [n_host][head_dim] indexer K, OCP fp8 E4M3FN, resident */
+  uint16_t *gpu_kv;        /* [n_gpu][latent_dim] bf16 GPU pool                      */
+  const uint16_t *host_kv; /* [n_host][latent_dim] bf16 host pool (mapped, pinned)   */
+  const uint16_t *q;       /* [q_ring][batch][n_heads][head_dim] bf16 queries        */
+  const float *w;          /* [batch][n_heads] fp32 head weights                     */
+  float *theta;            /* [max_batch] EMA threshold, +inf = no estimate yet       */
+  int32_t *ctl;            /* [ECHO_CTL_WORDS] step counter and free-list length      */
+} echo_layer_t;
+
+typedef struct {
+  int32_t batch;            /* B, host value, 0 <= B <= max_batch                  */
+  const int32_t *host_base; /* [B] device: first host id of each request           */
+  const int32_t *ctx_len;   /* [B] device: context length, 0 <= ctx <= max_ctx      */
+} echo_batch_t;
+
+/* Workspace: one caller-allocated device buffer carved by echo_ws_bind.  The
+ * named arrays are outputs of the step that the caller may read. */
+typedef struct {
+  float *scores;      /* [max_batch][max_ctx] indexer scores                        */
+  int32_t *sel_tok;   /* [max_batch][top_k] selected tokens, ascending              */
+  int32_t *sel_slot;  /* [max_batch][top_k] their GPU slots after the step           */
+  int32_t *n_sel;     /* [max_batch] min(top_k, ctx)                                */
+  float *kth;         /* [max_batch] k-th highest score of the step                 */
+  int32_t *pf_tok;    /* [max_batch][top_k] prefetched tokens, in rank order        */
+  int32_t *pf_slot;   /* [max_batch][top_k] their slots                             */
+  int32_t *n_pf;      /* [max_batch] prefetched tokens                              */
+  int32_t *n_cand;    /* [max_batch] prefetch candidates before the cap             */
+  int32_t *miss_tok;  /* [max_batch][top_k] selected tokens that were not resident   */
+  int32_t *n_miss;    /* [max_batch]                                                */
+  int32_t *recall_h;  /* [max_batch*top_k] recall list: host ids, (request, token)   */
+  int32_t *recall_g;  /* [max_batch*top_k] recall list: destination slots           */
+  int32_t *counters;  /* [ECHO_NCOUNTERS]                                           */
+  int32_t *status;    /* [1] sticky device status                                   */
+  uint8_t *internal;  /* scratch used between the step's kernels                    */
+  size_t internal_bytes;
+} echo_ws_t;
+
+/* ------------------------------------------------------------- sizing */
+
+/* Bytes of per-layer metadata: 4*n_host + 13*n_gpu (ECHO review, "Core method /
+ * in-graph per-layer cache management": about 10 MB per layer at 2M host and
+ * 200K GPU tokens).  Pure function; returns -1 for negative sizes. */
+int64_t echo_meta_bytes(int64_t n_host, int64_t n_gpu);
+
+/* Bytes of the workspace buffer for these dims (0 if dims are invalid). */
+size_t echo_ws_bytes(const echo_dims_t *dims);
+
+/* Carve `base` (device, `bytes` >= echo_ws_bytes, 256-byte aligned) into *ws.
+ * Host-only; returns ECHO_EINVAL on a bad argument. */
+int echo_ws_bind(const echo_dims_t *dims, void *base, size_t bytes, echo_ws_t *ws);
+
+/* ------------------------------------------------------------- init */
+
+/* Reset one layer: every slot free (free=1, prio=-1, g2h=-1), h2g=-1 for every
+ * host token, idxbuf = 0..n_gpu-1, theta = +inf for max_batch requests, step 0. */
+int echo_meta_init(const echo_dims_t *dims, const echo_layer_t *layer, hipStream_t stream);
+
+/* Clear the workspace (status, counters and internal scratch). */
+int echo_ws_reset(const echo_dims_t *dims, const echo_ws_t *ws, hipStream_t stream);
+
+/* ------------------------------------------------------ the hot path */
+
+/* Steps a0-a2: query prologue, lightning-indexer scoring
+ * score[b,s] = sum_j w[b,j] * max(0, q[b,j,:] . K[host_base[b]+s,:]) for s < ctx_len[b]
+ * (DeepSeek Sparse Attention's indexer, which the ECHO review's "Problem and
+ * motivation" names; fp8 K, bf16 q, fp32 accumulation), and, while scoring
+ * proceeds, EMA-threshold prefetch (ECHO review, "Core method / decode" and
+ * "Core method / prefetch inside the indexer pipeline"): tokens with
+ * score > theta that have no slot are taken in token order, at most
+ * min(top_k, ceil(ctx/prefetch_cap_div)) per request, into the free slots
+ * idxbuf[off_b + r] (off_b = sum of earlier requests' caps), with priority t,
+ * and their latent rows are read from the host pool.  Writes ws->scores,
+ * pf_tok/pf_slot/n_pf/n_cand and counters[PREFETCH]. */
+int echo_indexer_prefetch(const echo_dims_t *dims, const echo_layer_t *layer,
+                          const echo_batch_t *batch, const echo_ws_t *ws, int theta_mode,
+                          hipStream_t stream);
+
+/* Step a3: exact top-k per request of `scores` ([batch][score_stride] fp32,
+ * device; may be ws->scores or any caller buffer): the min(top_k, ctx) tokens
+ * that come first under (score descending, token ascending), written in
+ * ascending token order to ws->sel_tok, with ws->n_sel and ws->kth (ECHO review,
+ * "Core method / decode").  If `theta` is not NULL, requests with ctx >= top_k
+ * update their EMA threshold theta[b] (seeded by the first k-th score).
+ * Scores must be finite. */
+int echo_topk(const echo_dims_t *dims, const float *scores, int64_t score_stride,
+              const echo_batch_t *batch, const echo_ws_t *ws, float *theta,
+              hipStream_t stream);
+
+/* Steps a4-a6 for the tokens in ws->sel_tok (ECHO review, "Core method /
+ * in-graph per-layer cache management"): protect every resident selected token
+ * (priority t) and list the misses in (request, token) order; evict the
+ * n_evict = min(|E|, max(0, misses + R - free)) occupied slots with the lowest
+ * (priority, slot) among those with priority < t (R = sum of prefetch caps; no
+ * data moves); give miss i the i-th free slot in ascending order; rebuild the
+ * free list in idxbuf.  Writes sel_slot, miss_tok, n_miss, recall_h/recall_g
+ * and counters.  Sets ECHO_ECAPACITY if free + evictable < misses. */
+int echo_cache_alloc_evict(const echo_dims_t *dims, const echo_layer_t *layer,
+                           const echo_batch_t *batch, const echo_ws_t *ws, hipStream_t stream);
+
+/* Step a7: copy every row in the recall list from the host pool to the GPU pool
+ * (a kernel reading mapped host memory directly; ECHO review, "Core method /
+ * in-graph per-layer cache management"). */
+int echo_recall(const echo_dims_t *dims, const echo_layer_t *layer, const echo_ws_t *ws,
+                hipStream_t stream);
+
+/* Advance the layer's step counter t by one (skipped if ws->status is set). */
+int echo_step_advance(const echo_layer_t *layer, const echo_ws_t *ws, hipStream_t stream);
+
+/* Steps a0-a8 for one layer and one decode step, in order, on `stream`: indexer
+ * + prefetch, top-k with the EMA update (mode EMA only), protect/evict/alloc,
+ * recall, and the step-counter advance. */
+int echo_layer_step(const echo_dims_t *dims, const echo_layer_t *layer,
+                    const echo_batch_t *batch, const echo_ws_t *ws, int theta_mode,
+                    hipStream_t stream);
+
+/* ------------------------------------------------------------- diagnostics */
+
+/* Static string for a status code. */
+const char *echo_status_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ECHO_H */

@@ -1,0 +1,144 @@
+"""ctypes binding of the C ABI in include/echo.h -- argument marshalling only.
+
+Every function keeps the C name and returns the C status code; all work happens in
+the HIP kernels of libecho.so.  There is no fallback: if the library is missing or
+fails to load, the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libecho.so")
+
+ECHO_OK, ECHO_EINVAL, ECHO_EHIP, ECHO_EUNSUPPORTED = 0, -1, -2, -3
+ECHO_ECAPACITY, ECHO_ETIMEOUT, ECHO_EDEVARG = -4, -5, -6
+ECHO_THETA_EMA, ECHO_THETA_NEG_INF, ECHO_THETA_POS_INF = 0, 1, 2
+(ECHO_CNT_MISS, ECHO_CNT_EVICT, ECHO_CNT_FREE, ECHO_CNT_EVICTABLE, ECHO_CNT_FREE_END,
+ ECHO_CNT_PREFETCH) = range(6)
+ECHO_NCOUNTERS = 16
+ECHO_CTL_STEP, ECHO_CTL_NFREE, ECHO_CTL_WORDS = 0, 1, 4
+
+EXPORTS = ("echo_meta_bytes", "echo_ws_bytes", "echo_ws_bind", "echo_meta_init",
+           "echo_ws_reset", "echo_indexer_prefetch", "echo_topk", "echo_cache_alloc_evict",
+           "echo_recall", "echo_step_advance", "echo_layer_step", "echo_status_string")
+
+P = C.c_void_p
+
+
+class echo_dims_t(C.Structure):
+    _fields_ = [("n_heads", C.c_int32), ("head_dim", C.c_int32), ("top_k", C.c_int32),
+                ("latent_dim", C.c_int32), ("n_host", C.c_int64), ("n_gpu", C.c_int32),
+                ("max_batch", C.c_int32), ("max_ctx", C.c_int32), ("ema_alpha", C.c_float),
+                ("prefetch_cap_div", C.c_int32), ("q_ring", C.c_int32)]
+
+
+class echo_layer_meta_t(C.Structure):
+    _fields_ = [("h2g", P), ("g2h", P), ("prio", P), ("idxbuf", P), ("free_flags", P)]
+
+
+class echo_layer_t(C.Structure):
+    _fields_ = [("meta", echo_layer_meta_t), ("k_index", P), ("gpu_kv", P), ("host_kv", P),
+                ("q", P), ("w", P), ("theta", P), ("ctl", P)]
+
+
+class echo_batch_t(C.Structure):
+    _fields_ = [("batch", C.c_int32), ("host_base", P), ("ctx_len", P)]
+
+
+class echo_ws_t(C.Structure):
+    _fields_ = [("scores", P), ("sel_tok", P), ("sel_slot", P), ("n_sel", P), ("kth", P),
+                ("pf_tok", P), ("pf_slot", P), ("n_pf", P), ("n_cand", P), ("miss_tok", P),
+                ("n_miss", P), ("recall_h", P), ("recall_g", P), ("counters", P),
+                ("status", P), ("internal", P), ("internal_bytes", C.c_size_t)]
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """Load libecho.so (built by __graft_entry__.build / kv_cache_offload_fp8_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m kv_cache_offload_fp8_amd.build` (no CPU fallback)")
+        L = C.CDLL(LIB_PATH)
+        dp, lp, bp, wp = (C.POINTER(echo_dims_t), C.POINTER(echo_layer_t),
+                          C.POINTER(echo_batch_t), C.POINTER(echo_ws_t))
+        sigs = {
+            "echo_meta_bytes": (C.c_int64, [C.c_int64, C.c_int64]),
+            "echo_ws_bytes": (C.c_size_t, [dp]),
+            "echo_ws_bind": (C.c_int, [dp, P, C.c_size_t, wp]),
+            "echo_meta_init": (C.c_int, [dp, lp, P]),
+            "echo_ws_reset": (C.c_int, [dp, wp, P]),
+            "echo_indexer_prefetch": (C.c_int, [dp, lp, bp, wp, C.c_int, P]),
+            "echo_topk": (C.c_int, [dp, P, C.c_int64, bp, wp, P, P]),
+            "echo_cache_alloc_evict": (C.c_int, [dp, lp, bp, wp, P]),
+            "echo_recall": (C.c_int, [dp, lp, wp, P]),
+            "echo_step_advance": (C.c_int, [lp, wp, P]),
+            "echo_layer_step": (C.c_int, [dp, lp, bp, wp, C.c_int, P]),
+            "echo_status_string": (C.c_char_p, [C.c_int]),
+        }
+        for name, (res, args) in sigs.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _ref(x):
+    return None if x is None else C.byref(x)
+
+
+def echo_meta_bytes(n_host: int, n_gpu: int) -> int:
+    return lib().echo_meta_bytes(n_host, n_gpu)
+
+
+def echo_ws_bytes(dims: echo_dims_t) -> int:
+    return lib().echo_ws_bytes(C.byref(dims))
+
+
+def echo_ws_bind(dims, base: int, nbytes: int, ws: echo_ws_t) -> int:
+    return lib().echo_ws_bind(C.byref(dims), base, nbytes, C.byref(ws))
+
+
+def echo_meta_init(dims, layer, stream: int) -> int:
+    return lib().echo_meta_init(C.byref(dims), _ref(layer), stream)
+
+
+def echo_ws_reset(dims, ws, stream: int) -> int:
+    return lib().echo_ws_reset(C.byref(dims), _ref(ws), stream)
+
+
+def echo_indexer_prefetch(dims, layer, batch, ws, theta_mode: int, stream: int) -> int:
+    return lib().echo_indexer_prefetch(C.byref(dims), _ref(layer), _ref(batch), _ref(ws),
+                                       theta_mode, stream)
+
+
+def echo_topk(dims, scores: int, score_stride: int, batch, ws, theta, stream: int) -> int:
+    return lib().echo_topk(C.byref(dims), scores, score_stride, _ref(batch), _ref(ws), theta,
+                           stream)
+
+
+def echo_cache_alloc_evict(dims, layer, batch, ws, stream: int) -> int:
+    return lib().echo_cache_alloc_evict(C.byref(dims), _ref(layer), _ref(batch), _ref(ws), stream)
+
+
+def echo_recall(dims, layer, ws, stream: int) -> int:
+    return lib().echo_recall(C.byref(dims), _ref(layer), _ref(ws), stream)
+
+
+def echo_step_advance(layer, ws, stream: int) -> int:
+    return lib().echo_step_advance(_ref(layer), _ref(ws), stream)
+
+
+def echo_layer_step(dims, layer, batch, ws, theta_mode: int, stream: int) -> int:
+    return lib().echo_layer_step(C.byref(dims), _ref(layer), _ref(batch), _ref(ws), theta_mode,
+                                 stream)
+
+
+def echo_status_string(code: int) -> str:
+    return lib().echo_status_string(code).decode()

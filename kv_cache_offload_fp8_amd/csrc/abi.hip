@@ -1,0 +1,301 @@
+// C ABI entry points (include/echo.h): host-side validation and the launch
+// sequence of each call.  No entry point allocates, frees or synchronizes.
+#include <math.h>
+#include <string.h>
+
+#include "kernels.h"
+
+using namespace echo;
+
+namespace {
+
+int check_dims(const echo_dims_t *d) {
+  if (!d) return ECHO_EINVAL;
+  if (d->n_heads < 1 || d->head_dim < 1 || d->top_k < 1 || d->latent_dim < 1 || d->n_host < 1 ||
+      d->n_gpu < 1 || d->max_batch < 1 || d->max_ctx < 1 || d->prefetch_cap_div < 1 ||
+      d->q_ring < 1)
+    return ECHO_EINVAL;
+  if (!(d->ema_alpha > 0.0f && d->ema_alpha <= 1.0f)) return ECHO_EINVAL;
+  if (d->n_host >= (1LL << 31) || d->max_ctx > (1 << 30) || d->n_gpu > (1 << 30))
+    return ECHO_EINVAL;
+  if (d->n_heads > kHeadsPad || d->head_dim > kDimPad || d->head_dim % 32 != 0 ||
+      d->top_k > 4096 || d->max_batch > kMaxBatch || (d->latent_dim * 2) % 16 != 0)
+    return ECHO_EUNSUPPORTED;
+  return ECHO_OK;
+}
+
+struct PublicLayout {
+  int64_t scores, sel_tok, sel_slot, n_sel, kth, pf_tok, pf_slot, n_pf, n_cand, miss_tok, n_miss,
+      recall_h, recall_g, counters, status, internal, total, internal_bytes;
+};
+
+PublicLayout public_layout(const echo_dims_t &d) {
+  PublicLayout L;
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    int64_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  const int64_t B = d.max_batch, C = d.max_ctx, K = d.top_k;
+  L.scores = take(B * C * 4);
+  L.sel_tok = take(B * K * 4);
+  L.sel_slot = take(B * K * 4);
+  L.n_sel = take(B * 4);
+  L.kth = take(B * 4);
+  L.pf_tok = take(B * K * 4);
+  L.pf_slot = take(B * K * 4);
+  L.n_pf = take(B * 4);
+  L.n_cand = take(B * 4);
+  L.miss_tok = take(B * K * 4);
+  L.n_miss = take(B * 4);
+  L.recall_h = take(B * K * 4);
+  L.recall_g = take(B * K * 4);
+  L.counters = take(ECHO_NCOUNTERS * 4);
+  L.status = take(4);
+  L.internal_bytes = scratch_layout(d, nullptr, nullptr);
+  L.internal = take(L.internal_bytes);
+  L.total = off;
+  return L;
+}
+
+bool ws_ok(const echo_ws_t *ws) {
+  return ws && ws->scores && ws->sel_tok && ws->sel_slot && ws->n_sel && ws->kth && ws->pf_tok &&
+         ws->pf_slot && ws->n_pf && ws->n_cand && ws->miss_tok && ws->n_miss && ws->recall_h &&
+         ws->recall_g && ws->counters && ws->status && ws->internal;
+}
+
+bool batch_ok(const echo_dims_t &d, const echo_batch_t *b) {
+  if (!b || b->batch < 0 || b->batch > d.max_batch) return false;
+  if (b->batch > 0 && (!b->host_base || !b->ctx_len)) return false;
+  return true;
+}
+
+bool layer_ok(const echo_layer_t *l, bool need_theta) {
+  if (!l) return false;
+  const echo_layer_meta_t &m = l->meta;
+  if (!m.h2g || !m.g2h || !m.prio || !m.idxbuf || !m.free_flags) return false;
+  if (!l->k_index || !l->gpu_kv || !l->host_kv || !l->q || !l->w || !l->ctl) return false;
+  if (need_theta && !l->theta) return false;
+  return true;
+}
+
+StepArgs make_args(const echo_dims_t &d, const echo_layer_t *l, const echo_batch_t *bt,
+                   const echo_ws_t &ws, int mode) {
+  StepArgs a;
+  memset(&a, 0, sizeof a);
+  a.H = d.n_heads;
+  a.D = d.head_dim;
+  a.K = d.top_k;
+  a.latent = d.latent_dim;
+  a.n_gpu = d.n_gpu;
+  a.max_ctx = d.max_ctx;
+  a.q_ring = d.q_ring;
+  a.cap_div = d.prefetch_cap_div;
+  a.max_batch = d.max_batch;
+  a.n_host = d.n_host;
+  a.alpha = d.ema_alpha;
+  if (bt) {
+    a.B = bt->batch;
+    a.host_base = bt->host_base;
+    a.ctx_len = bt->ctx_len;
+  }
+  if (l) {
+    a.h2g = l->meta.h2g;
+    a.g2h = l->meta.g2h;
+    a.prio = l->meta.prio;
+    a.idxbuf = l->meta.idxbuf;
+    a.freef = l->meta.free_flags;
+    a.kidx = l->k_index;
+    a.gpu_kv = l->gpu_kv;
+    a.host_kv = l->host_kv;
+    a.q = l->q;
+    a.w = l->w;
+    a.theta = l->theta;
+    a.ctl = l->ctl;
+  }
+  a.scores_in = ws.scores;
+  a.score_stride = d.max_ctx;
+  a.theta_upd = nullptr;
+  a.mode = mode;
+  a.ws = ws;
+  scratch_layout(d, ws.internal, &a.sc);
+  return a;
+}
+
+#define LAUNCH(x)                           \
+  do {                                      \
+    if ((x) != hipSuccess) return ECHO_EHIP; \
+  } while (0)
+
+int run_indexer(const StepArgs &a, int extra_roles, hipStream_t s) {
+  LAUNCH(launch_begin(a, BEGIN_REQ | BEGIN_Q | BEGIN_CLR_INDEX | BEGIN_CLR_TOPK | extra_roles, s));
+  LAUNCH(launch_score(a, s));
+  return ECHO_OK;
+}
+
+int run_manage(const StepArgs &a, hipStream_t s) {
+  LAUNCH(launch_evict_hist(a, s));
+  LAUNCH(launch_evict_collect(a, s));
+  LAUNCH(launch_evict_resolve(a, s));
+  LAUNCH(launch_alloc(a, s));
+  return ECHO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t echo_meta_bytes(int64_t n_host, int64_t n_gpu) {
+  if (n_host < 0 || n_gpu < 0) return -1;
+  return 4 * n_host + (1 + 4 + 4 + 4) * n_gpu;  // h2g | free, prio, idxbuf, g2h
+}
+
+size_t echo_ws_bytes(const echo_dims_t *dims) {
+  if (check_dims(dims) != ECHO_OK) return 0;
+  return (size_t)public_layout(*dims).total;
+}
+
+int echo_ws_bind(const echo_dims_t *dims, void *base, size_t bytes, echo_ws_t *ws) {
+  int rc = check_dims(dims);
+  if (rc != ECHO_OK) return rc;
+  if (!base || !ws || ((uintptr_t)base & 255) != 0) return ECHO_EINVAL;
+  const PublicLayout L = public_layout(*dims);
+  if (bytes < (size_t)L.total) return ECHO_EINVAL;
+  uint8_t *p = (uint8_t *)base;
+  ws->scores = (float *)(p + L.scores);
+  ws->sel_tok = (int32_t *)(p + L.sel_tok);
+  ws->sel_slot = (int32_t *)(p + L.sel_slot);
+  ws->n_sel = (int32_t *)(p + L.n_sel);
+  ws->kth = (float *)(p + L.kth);
+  ws->pf_tok = (int32_t *)(p + L.pf_tok);
+  ws->pf_slot = (int32_t *)(p + L.pf_slot);
+  ws->n_pf = (int32_t *)(p + L.n_pf);
+  ws->n_cand = (int32_t *)(p + L.n_cand);
+  ws->miss_tok = (int32_t *)(p + L.miss_tok);
+  ws->n_miss = (int32_t *)(p + L.n_miss);
+  ws->recall_h = (int32_t *)(p + L.recall_h);
+  ws->recall_g = (int32_t *)(p + L.recall_g);
+  ws->counters = (int32_t *)(p + L.counters);
+  ws->status = (int32_t *)(p + L.status);
+  ws->internal = p + L.internal;
+  ws->internal_bytes = (size_t)L.internal_bytes;
+  return ECHO_OK;
+}
+
+int echo_meta_init(const echo_dims_t *dims, const echo_layer_t *layer, hipStream_t stream) {
+  int rc = check_dims(dims);
+  if (rc != ECHO_OK) return rc;
+  if (!layer || !layer->meta.h2g || !layer->meta.g2h || !layer->meta.prio || !layer->meta.idxbuf ||
+      !layer->meta.free_flags || !layer->theta || !layer->ctl)
+    return ECHO_EINVAL;
+  echo_ws_t none;
+  memset(&none, 0, sizeof none);
+  StepArgs a = make_args(*dims, layer, nullptr, none, ECHO_THETA_POS_INF);
+  LAUNCH(launch_meta_init(a, stream));
+  return ECHO_OK;
+}
+
+int echo_ws_reset(const echo_dims_t *dims, const echo_ws_t *ws, hipStream_t stream) {
+  int rc = check_dims(dims);
+  if (rc != ECHO_OK) return rc;
+  if (!ws_ok(ws)) return ECHO_EINVAL;
+  LAUNCH(launch_ws_reset(*ws, stream));
+  return ECHO_OK;
+}
+
+int echo_indexer_prefetch(const echo_dims_t *dims, const echo_layer_t *layer,
+                          const echo_batch_t *batch, const echo_ws_t *ws, int theta_mode,
+                          hipStream_t stream) {
+  int rc = check_dims(dims);
+  if (rc != ECHO_OK) return rc;
+  if (theta_mode < ECHO_THETA_EMA || theta_mode > ECHO_THETA_POS_INF) return ECHO_EINVAL;
+  if (!layer_ok(layer, theta_mode == ECHO_THETA_EMA) || !batch_ok(*dims, batch) || !ws_ok(ws))
+    return ECHO_EINVAL;
+  const StepArgs a = make_args(*dims, layer, batch, *ws, theta_mode);
+  return run_indexer(a, 0, stream);
+}
+
+int echo_topk(const echo_dims_t *dims, const float *scores, int64_t score_stride,
+              const echo_batch_t *batch, const echo_ws_t *ws, float *theta, hipStream_t stream) {
+  int rc = check_dims(dims);
+  if (rc != ECHO_OK) return rc;
+  if (!scores || score_stride < dims->max_ctx || !batch_ok(*dims, batch) || !ws_ok(ws))
+    return ECHO_EINVAL;
+  StepArgs a = make_args(*dims, nullptr, batch, *ws, ECHO_THETA_POS_INF);
+  a.scores_in = scores;
+  a.score_stride = score_stride;
+  a.theta_upd = theta;
+  LAUNCH(launch_begin(a, BEGIN_REQ | BEGIN_CLR_TOPK, stream));
+  LAUNCH(launch_topk_minmax(a, stream));
+  LAUNCH(launch_topk_hist(a, stream));
+  LAUNCH(launch_topk_collect(a, stream));
+  LAUNCH(launch_topk_resolve(a, false, stream));
+  return ECHO_OK;
+}
+
+int echo_cache_alloc_evict(const echo_dims_t *dims, const echo_layer_t *layer,
+                           const echo_batch_t *batch, const echo_ws_t *ws, hipStream_t stream) {
+  int rc = check_dims(dims);
+  if (rc != ECHO_OK) return rc;
+  if (!layer_ok(layer, false) || !batch_ok(*dims, batch) || !ws_ok(ws)) return ECHO_EINVAL;
+  const StepArgs a = make_args(*dims, layer, batch, *ws, ECHO_THETA_POS_INF);
+  LAUNCH(launch_begin(a, BEGIN_REQ | BEGIN_CLR_MANAGE, stream));
+  LAUNCH(launch_protect(a, stream));
+  return run_manage(a, stream);
+}
+
+int echo_recall(const echo_dims_t *dims, const echo_layer_t *layer, const echo_ws_t *ws,
+                hipStream_t stream) {
+  int rc = check_dims(dims);
+  if (rc != ECHO_OK) return rc;
+  if (!layer_ok(layer, false) || !ws_ok(ws)) return ECHO_EINVAL;
+  const StepArgs a = make_args(*dims, layer, nullptr, *ws, ECHO_THETA_POS_INF);
+  LAUNCH(launch_recall(a, false, stream));
+  return ECHO_OK;
+}
+
+int echo_step_advance(const echo_layer_t *layer, const echo_ws_t *ws, hipStream_t stream) {
+  if (!layer || !layer->ctl || !ws || !ws->status) return ECHO_EINVAL;
+  StepArgs a;
+  memset(&a, 0, sizeof a);
+  a.ctl = layer->ctl;
+  a.ws = *ws;
+  LAUNCH(launch_step_advance(a, stream));
+  return ECHO_OK;
+}
+
+int echo_layer_step(const echo_dims_t *dims, const echo_layer_t *layer, const echo_batch_t *batch,
+                    const echo_ws_t *ws, int theta_mode, hipStream_t stream) {
+  int rc = check_dims(dims);
+  if (rc != ECHO_OK) return rc;
+  if (theta_mode < ECHO_THETA_EMA || theta_mode > ECHO_THETA_POS_INF) return ECHO_EINVAL;
+  if (!layer_ok(layer, theta_mode == ECHO_THETA_EMA) || !batch_ok(*dims, batch) || !ws_ok(ws))
+    return ECHO_EINVAL;
+  StepArgs a = make_args(*dims, layer, batch, *ws, theta_mode);
+  a.theta_upd = theta_mode == ECHO_THETA_EMA ? layer->theta : nullptr;
+  rc = run_indexer(a, BEGIN_CLR_MANAGE, stream);
+  if (rc != ECHO_OK) return rc;
+  LAUNCH(launch_topk_hist(a, stream));
+  LAUNCH(launch_topk_collect(a, stream));
+  LAUNCH(launch_topk_resolve(a, true, stream));
+  rc = run_manage(a, stream);
+  if (rc != ECHO_OK) return rc;
+  LAUNCH(launch_recall(a, true, stream));
+  return ECHO_OK;
+}
+
+const char *echo_status_string(int code) {
+  switch (code) {
+    case ECHO_OK: return "ok";
+    case ECHO_EINVAL: return "invalid argument";
+    case ECHO_EHIP: return "kernel launch failed";
+    case ECHO_EUNSUPPORTED: return "unsupported shape";
+    case ECHO_ECAPACITY: return "GPU pool too small for the missed tokens";
+    case ECHO_ETIMEOUT: return "cross-workgroup wait timed out";
+    case ECHO_EDEVARG: return "device-side batch arguments out of range or overlapping";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,290 @@
+// Internal device primitives and the workspace layout shared by the kernels.
+// Nothing here is part of the public ABI (include/echo.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "echo.h"
+
+namespace echo {
+
+// ----------------------------------------------------------------- sizes
+constexpr int kWave = 64;
+constexpr int kHeadsPad = 64;     // indexer heads padded to 4 groups of 16 (MFMA rows)
+constexpr int kDimPad = 128;      // indexer dim padded to four 16x16x32 bf16 MFMA k-steps
+constexpr int kScoreTile = 256;   // tokens per scoring work item (4 waves x 64)
+constexpr int kBins = 4096;       // first-level histogram bins
+constexpr int kSelChunk = 8192;   // tokens per block in the top-k histogram/collect passes
+constexpr int kSlotTile = 4096;   // slots per block in the eviction and allocation passes
+constexpr int kMaxBatch = 64;
+constexpr long long kSpinLimit = 100000000LL;  // 1 s of the 100 MHz constant clock
+
+// internal counters (Scratch::misc)
+enum {
+  M_TICKET_SCORE = 0,
+  M_TICKET_ALLOC = 1,
+  M_TOTAL_TILES = 2,
+  M_RESERVE = 3,
+  M_NMISC = 16
+};
+
+// lookback state: flag in the high word, value in the low word
+constexpr uint64_t kFlagA = 1ull << 32;  // aggregate of this tile only
+constexpr uint64_t kFlagP = 2ull << 32;  // inclusive prefix
+
+struct ReqInfo {
+  int32_t ctx;     // context length (0 if the request's arguments were rejected)
+  int32_t base;    // first host id
+  int32_t cap;     // prefetch cap min(k, ceil(ctx/div))
+  int32_t off;     // sum of earlier caps: first free-list position of this request
+  int32_t tile0;   // first scoring work item of this request
+  int32_t ntiles;  // scoring work items of this request
+  int32_t active;  // prefetch enabled for this request in this step
+  float theta;     // prefetch threshold
+};
+
+// Carved internal scratch.  Every region starts 256-byte aligned.
+struct Scratch {
+  uint16_t *qbf;          // [max_batch][64][128] bf16 query, zero-padded
+  float *wsc;             // [max_batch][64] head weights, zero-padded
+  ReqInfo *req;           // [max_batch]
+  int32_t *misc;          // [M_NMISC]
+  uint64_t *tstate;       // [max_tiles] scoring look-back states
+  uint32_t *kmin, *kmax;  // [max_batch] key range per request
+  uint32_t *thist;        // [max_batch][kBins]
+  uint32_t *tcand_key;    // [max_batch][max_ctx]
+  int32_t *tcand_idx;     // [max_batch][max_ctx]
+  int32_t *tcand_n;       // [max_batch]
+  int32_t *tbelow;        // [max_batch]
+  int32_t *tbin;          // [max_batch]
+  uint32_t *tbits;        // [max_batch][bw] selection bitmap
+  int32_t *miss_i;        // [max_batch][top_k] position of each miss in sel_tok
+  uint32_t *ehist;        // [kBins]
+  uint32_t *ecand_key;    // [n_gpu]
+  int32_t *ecand_idx;     // [n_gpu]
+  int32_t *ecnt;          // [4]: candidates, below, boundary bin
+  uint64_t *astate;       // [alloc tiles] free-list look-back states
+  int32_t max_tiles, bw, atiles;
+};
+
+inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+
+// Lays out the internal scratch for `d`; with base == nullptr only measures it.
+inline int64_t scratch_layout(const echo_dims_t &d, uint8_t *base, Scratch *s) {
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) -> uint8_t * {
+    uint8_t *p = base ? base + off : nullptr;
+    off = align256(off + bytes);
+    return p;
+  };
+  const int64_t B = d.max_batch, C = d.max_ctx, K = d.top_k, G = d.n_gpu;
+  const int32_t max_tiles = (int32_t)(B * ((C + kScoreTile - 1) / kScoreTile));
+  const int32_t bw = (int32_t)((C + 63) / 64 * 2);  // whole 64-bit groups
+  const int32_t atiles = (int32_t)((G + kSlotTile - 1) / kSlotTile);
+  Scratch t;
+  t.qbf = (uint16_t *)take(B * kHeadsPad * kDimPad * 2);
+  t.wsc = (float *)take(B * kHeadsPad * 4);
+  t.req = (ReqInfo *)take(B * sizeof(ReqInfo));
+  t.misc = (int32_t *)take(M_NMISC * 4);
+  t.tstate = (uint64_t *)take((int64_t)max_tiles * 8);
+  t.kmin = (uint32_t *)take(B * 4);
+  t.kmax = (uint32_t *)take(B * 4);
+  t.thist = (uint32_t *)take(B * kBins * 4);
+  t.tcand_key = (uint32_t *)take(B * C * 4);
+  t.tcand_idx = (int32_t *)take(B * C * 4);
+  t.tcand_n = (int32_t *)take(B * 4);
+  t.tbelow = (int32_t *)take(B * 4);
+  t.tbin = (int32_t *)take(B * 4);
+  t.tbits = (uint32_t *)take(B * bw * 4);
+  t.miss_i = (int32_t *)take(B * K * 4);
+  t.ehist = (uint32_t *)take(kBins * 4);
+  t.ecand_key = (uint32_t *)take(G * 4);
+  t.ecand_idx = (int32_t *)take(G * 4);
+  t.ecnt = (int32_t *)take(16);
+  t.astate = (uint64_t *)take((int64_t)atiles * 8);
+  t.max_tiles = max_tiles;
+  t.bw = bw;
+  t.atiles = atiles;
+  if (s) *s = t;
+  return off;
+}
+
+// ------------------------------------------------------------- status
+__device__ inline bool failed(const int32_t *status) {
+  return __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+}
+__device__ inline void fail(int32_t *status, int code) {
+  int expected = 0;
+  __hip_atomic_compare_exchange_strong(status, &expected, code, __ATOMIC_RELAXED,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ------------------------------------------------------------- wave / block
+__device__ inline int lane_id() { return threadIdx.x & (kWave - 1); }
+__device__ inline uint64_t lanemask_lt() { return (1ull << lane_id()) - 1ull; }
+
+__device__ inline int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ inline uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o));
+  return v;
+}
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+  return v;
+}
+__device__ inline uint64_t wave_min_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint64_t x = __shfl_xor(v, o);
+    v = x < v ? x : v;
+  }
+  return v;
+}
+__device__ inline uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint64_t x = __shfl_xor(v, o);
+    v = x > v ? x : v;
+  }
+  return v;
+}
+__device__ inline int wave_incl_scan(int v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int x = __shfl_up(v, o);
+    if (l >= o) v += x;
+  }
+  return v;
+}
+
+// Exclusive block scan of one int per thread.  `sh` needs NT/64 + 1 ints of
+// shared memory.  Returns the exclusive prefix; *total receives the block sum.
+template <int NT>
+__device__ inline int block_excl_scan(int v, int *sh, int *total) {
+  constexpr int NW = NT / kWave;
+  const int l = lane_id(), w = threadIdx.x / kWave;
+  int incl = wave_incl_scan(v);
+  if (l == kWave - 1) sh[w] = incl;
+  __syncthreads();
+  if (w == 0) {
+    int x = l < NW ? sh[l] : 0;
+    int xs = wave_incl_scan(x);
+    if (l < NW) sh[l] = xs - x;
+    if (l == NW - 1) sh[NW] = xs;
+  }
+  __syncthreads();
+  int r = sh[w] + incl - v;
+  *total = sh[NW];
+  __syncthreads();
+  return r;
+}
+
+template <int NT>
+__device__ inline uint64_t block_min_u64(uint64_t v, uint64_t *sh) {
+  constexpr int NW = NT / kWave;
+  v = wave_min_u64(v);
+  if (lane_id() == 0) sh[threadIdx.x / kWave] = v;
+  __syncthreads();
+  uint64_t r = sh[0];
+  for (int i = 1; i < NW; ++i) r = sh[i] < r ? sh[i] : r;
+  __syncthreads();
+  return r;
+}
+template <int NT>
+__device__ inline uint64_t block_max_u64(uint64_t v, uint64_t *sh) {
+  constexpr int NW = NT / kWave;
+  v = wave_max_u64(v);
+  if (lane_id() == 0) sh[threadIdx.x / kWave] = v;
+  __syncthreads();
+  uint64_t r = sh[0];
+  for (int i = 1; i < NW; ++i) r = sh[i] > r ? sh[i] : r;
+  __syncthreads();
+  return r;
+}
+
+// ------------------------------------------------------ decoupled look-back
+// Called by one whole wave.  Work item `tau` of a segment that starts at item
+// `seg0` publishes its own count `c`, walks back over earlier items of the same
+// segment (aggregates until an inclusive prefix is found) and publishes its
+// inclusive prefix.  Returns the exclusive prefix of `tau`.  Items are handed
+// out by an atomic ticket, so every earlier item belongs to a running or
+// finished workgroup and the wait always ends; a 1 s guard turns a broken
+// invariant into ECHO_ETIMEOUT instead of a hang.
+__device__ inline int lookback(uint64_t *st, int tau, int seg0, int c, int32_t *status) {
+  const int l = lane_id();
+  if (tau == seg0) {
+    if (l == 0)
+      __hip_atomic_store(&st[tau], kFlagP | (uint32_t)c, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    return 0;
+  }
+  if (l == 0)
+    __hip_atomic_store(&st[tau], kFlagA | (uint32_t)c, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  int E = 0;
+  int j = tau - 1;
+  const uint64_t t0 = wall_clock64();
+  bool timed_out = false;
+  while (true) {
+    const int idx = j - l;
+    uint64_t v = idx >= seg0 ? __hip_atomic_load(&st[idx], __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT)
+                             : kFlagP;
+    while (!__all((v >> 32) != 0)) {
+      if ((v >> 32) == 0)
+        v = __hip_atomic_load(&st[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (__any((long long)(wall_clock64() - t0) > kSpinLimit)) {
+        timed_out = true;
+        break;
+      }
+    }
+    if (timed_out) break;
+    const uint64_t pm = __ballot((v >> 32) == 2);
+    const int val = (int)(uint32_t)v;
+    if (pm) {
+      const int first = __ffsll((unsigned long long)pm) - 1;
+      E += wave_sum(l <= first ? val : 0);
+      break;
+    }
+    E += wave_sum(val);
+    j -= kWave;
+  }
+  if (timed_out) {
+    if (l == 0) fail(status, ECHO_ETIMEOUT);
+  }
+  if (l == 0)
+    __hip_atomic_store(&st[tau], kFlagP | (uint32_t)(E + c), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  return E;
+}
+
+// ------------------------------------------------------------ key orders
+// Order-preserving map of a finite fp32 value to uint32 (-0 treated as +0).
+__device__ inline uint32_t f32_order(float f) {
+  uint32_t u = __float_as_uint(f == 0.0f ? 0.0f : f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ inline float f32_from_order(uint32_t o) {
+  uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
+  return __uint_as_float(u);
+}
+// Top-k keys ascend as scores descend.
+__device__ inline uint32_t topk_key(float score) { return ~f32_order(score); }
+__device__ inline float score_of_key(uint32_t key) { return f32_from_order(~key); }
+
+// Histogram shift so that (key - kmin) >> shift < kBins for every key <= kmax.
+__device__ inline int bin_shift(uint32_t kmin, uint32_t kmax) {
+  uint32_t range = kmax - kmin;
+  int bits = range ? 32 - __clz(range) : 0;
+  return bits > 12 ? bits - 12 : 0;
+}
+
+}  // namespace echo

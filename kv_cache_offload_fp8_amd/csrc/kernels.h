@@ -1,0 +1,62 @@
+// Kernel arguments and launcher declarations (internal).
+#pragma once
+
+#include "common.h"
+
+namespace echo {
+
+// Everything a step's kernels read, passed by value as one kernel argument.
+struct StepArgs {
+  // dims
+  int32_t H, D, K, latent, n_gpu, max_ctx, q_ring, cap_div, max_batch;
+  int64_t n_host;
+  float alpha;
+  // batch (B is a host value baked into the launch)
+  int32_t B;
+  const int32_t *host_base, *ctx_len;
+  // layer
+  int32_t *h2g, *g2h, *prio, *idxbuf;
+  uint8_t *freef;
+  const uint8_t *kidx;
+  uint16_t *gpu_kv;
+  const uint16_t *host_kv;
+  const uint16_t *q;
+  const float *w;
+  float *theta;   // prefetch threshold state (read by the prologue)
+  int32_t *ctl;
+  // scores read by the top-k passes
+  const float *scores_in;
+  int64_t score_stride;
+  float *theta_upd;  // EMA state to update in the top-k epilogue, or null
+  int32_t mode;
+  // workspace
+  echo_ws_t ws;
+  Scratch sc;
+};
+
+// begin-kernel roles
+enum {
+  BEGIN_REQ = 1,         // request table, tickets, reserve
+  BEGIN_Q = 2,           // fp8 hi/lo split of the query
+  BEGIN_CLR_INDEX = 4,   // look-back states, prefetch counters
+  BEGIN_CLR_TOPK = 8,    // histograms, candidate counts, key ranges
+  BEGIN_CLR_MANAGE = 16  // eviction histogram, candidate counts, allocation states
+};
+
+hipError_t launch_begin(const StepArgs &a, int roles, hipStream_t s);
+hipError_t launch_score(const StepArgs &a, hipStream_t s);
+hipError_t launch_topk_minmax(const StepArgs &a, hipStream_t s);
+hipError_t launch_topk_hist(const StepArgs &a, hipStream_t s);
+hipError_t launch_topk_collect(const StepArgs &a, hipStream_t s);
+hipError_t launch_topk_resolve(const StepArgs &a, bool protect, hipStream_t s);
+hipError_t launch_protect(const StepArgs &a, hipStream_t s);
+hipError_t launch_evict_hist(const StepArgs &a, hipStream_t s);
+hipError_t launch_evict_collect(const StepArgs &a, hipStream_t s);
+hipError_t launch_evict_resolve(const StepArgs &a, hipStream_t s);
+hipError_t launch_alloc(const StepArgs &a, hipStream_t s);
+hipError_t launch_recall(const StepArgs &a, bool advance, hipStream_t s);
+hipError_t launch_step_advance(const StepArgs &a, hipStream_t s);
+hipError_t launch_meta_init(const StepArgs &a, hipStream_t s);
+hipError_t launch_ws_reset(const echo_ws_t &ws, hipStream_t s);
+
+}  // namespace echo

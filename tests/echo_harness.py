@@ -1,0 +1,168 @@
+"""Shared test rig: one layer on the GPU through the C ABI, the oracle beside it.
+
+The GPU side runs echo_layer_step (or the individual calls); the oracle runs the
+same step on the same seeded inputs, fed the GPU's scores so that every later
+decision (prefetch, top-k, eviction, allocation) can be compared bit for bit.
+The GPU scores themselves are compared with the oracle's own fp64 scores within
+the score tolerance.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from kv_cache_offload_fp8_amd import abi
+from kv_cache_offload_fp8_amd import runtime as R
+from oracle import oracle as O
+from synth import make_inputs
+
+MODE_EMA, MODE_NEG_INF, MODE_POS_INF = abi.ECHO_THETA_EMA, abi.ECHO_THETA_NEG_INF, \
+    abi.ECHO_THETA_POS_INF
+assert (MODE_EMA, MODE_NEG_INF, MODE_POS_INF) == (O.MODE_EMA, O.MODE_NEG_INF, O.MODE_POS_INF)
+
+SCORE_RTOL = 2e-3      # relative score tolerance
+SCORE_ATOL_REL = 2.0 ** -20  # times sum_j |w_j| sum_d |q_jd k_d| (cancellation allowance)
+
+
+def score_tolerance(q_codes: np.ndarray, w: np.ndarray, krows: np.ndarray,
+                    ref: np.ndarray) -> np.ndarray:
+    """Per-token allowed |gpu - oracle|: 2e-3 relative plus an absolute term from the
+    magnitude of the summed terms (fp32 accumulation of exact products)."""
+    qf = np.abs(torch.from_numpy(q_codes.view(np.int16)).view(torch.bfloat16).float()
+                .numpy().astype(np.float64))
+    kf = np.abs(torch.from_numpy(krows).view(torch.float8_e4m3fn).float().numpy()
+                .astype(np.float64))
+    mag = (kf @ qf.T) @ np.abs(w.astype(np.float64))
+    return SCORE_RTOL * np.abs(ref.astype(np.float64)) + SCORE_ATOL_REL * mag
+
+
+def assert_scores_close(gpu: np.ndarray, q_codes, w, krows, ctx_note=""):
+    ref = O.scores(q_codes, w, krows)
+    tol = score_tolerance(q_codes, w, krows, ref)
+    err = np.abs(gpu.astype(np.float64) - ref.astype(np.float64))
+    bad = np.nonzero(err > tol)[0]
+    assert bad.size == 0, (f"{ctx_note}: {bad.size} scores out of tolerance, first at {bad[:5]}: "
+                           f"gpu={gpu[bad[:5]]} ref={ref[bad[:5]]}")
+    return ref
+
+
+class Rig:
+    def __init__(self, wl, steps, device="cuda", ctx=None, n_gpu=None, n_host=None, seed=0,
+                 keep_pool=True, max_ctx=None, layer=0, cap_div=None, top_k=None):
+        if n_gpu is not None or n_host is not None or cap_div is not None or top_k is not None:
+            wl = wl.scaled(n_gpu=n_gpu or wl.n_gpu, n_host=n_host or wl.n_host,
+                           cap_div=cap_div or wl.cap_div, top_k=top_k or wl.top_k)
+        self.wl = wl
+        self.inp = make_inputs(wl, layer=layer, device="cpu", seed=seed, steps=steps, ctx=ctx)
+        self.ctx = self.inp.ctx
+        self.base = self.inp.host_base
+        self.B = int(self.ctx.size)
+        self.steps = steps
+        mc = int(max_ctx or max(1, int(self.ctx.max()) if self.B else 1))
+        self.dims = R.make_dims(wl.heads, wl.head_dim, wl.top_k, wl.n_host, wl.n_gpu,
+                                max(1, self.B), mc, wl.latent, wl.alpha, wl.cap_div, steps)
+        self.host = R.HostPool(wl.n_host, wl.latent)
+        self.host.np[:] = self.inp.np_latents()
+        self.kidx = self.inp.kidx.to(device)
+        self.layer = R.Layer(self.dims, self.kidx, self.host, self.B, device)
+        if self.B:
+            self.layer.q.copy_(self.inp.q.to(device))
+            self.layer.w.copy_(self.inp.w.to(device))
+        self.layer.init()
+        self.batch = R.Batch(self.base, self.ctx, device)
+        self.ws = R.Workspace(self.dims, device)
+        self.ws.reset()
+        self.orc = O.OracleLayer(wl.heads, wl.head_dim, wl.top_k, wl.latent, wl.n_host, wl.n_gpu,
+                                 max(1, self.B), wl.cap_div, wl.alpha, keep_pool=keep_pool)
+        self.np_kidx = self.inp.np_kidx()
+        self.np_host = self.host.np
+        self.np_w = self.inp.np_w()
+        self.t = 0
+        self.history = []
+
+    # ------------------------------------------------------------ GPU calls
+    def gpu_step(self, mode):
+        R.check(abi.echo_layer_step(self.dims, self.layer.struct, self.batch.struct, self.ws.ws,
+                                    mode, R.stream_handle()), "echo_layer_step")
+
+    def gpu_scores(self) -> np.ndarray:
+        torch.cuda.current_stream().synchronize()
+        return self.ws.scores[: self.B].cpu().numpy()
+
+    # --------------------------------------------------------- comparison
+    def step_and_compare(self, mode, check_scores=True, check_pool=True, expect_status=0):
+        t = self.t
+        q_t = self.inp.np_q(t % self.steps)
+        self.gpu_step(mode)
+        out = self.ws.read(self.B)
+        sc = self.gpu_scores()
+        st = self.layer.state()
+        if check_scores:
+            for b in range(self.B):
+                n = int(self.ctx[b])
+                if n:
+                    h0 = int(self.base[b])
+                    assert_scores_close(sc[b, :n], q_t[b], self.np_w[b],
+                                        self.np_kidx[h0:h0 + n], f"step {t} request {b}")
+        o = self.orc.step(self.base, self.ctx, q_t, self.np_w, self.np_kidx, self.np_host,
+                          mode=mode, ext_scores=sc)
+        self.compare(out, st, o, t, check_pool)
+        assert out["status"] == expect_status, (f"step {t}: status {out['status']}",
+                                                abi.echo_status_string(int(out["status"])))
+        self.history.append((out, o))
+        if o["status"] == O.OK:
+            self.t += 1
+        return out, o
+
+    def compare(self, out, st, o, t, check_pool=True):
+        tag = f"step {t}"
+        assert out["status"] == o["status"], (tag, out["status"], o["status"])
+        B, k = self.B, self.wl.top_k
+        for b in range(B):
+            n = int(o["n_sel"][b])
+            assert out["n_sel"][b] == n, (tag, "n_sel", b, out["n_sel"][b], n)
+            assert np.array_equal(out["sel_tok"][b, :n], o["sel_tok"][b, :n]), (tag, "sel_tok", b)
+            assert np.array_equal(np.float32(out["kth"][b]).view(np.uint32),
+                                  np.float32(o["kth"][b]).view(np.uint32)) or \
+                (np.isnan(out["kth"][b]) and np.isnan(o["kth"][b])), (tag, "kth", b)
+            npf = int(o["n_pf"][b])
+            assert out["n_pf"][b] == npf, (tag, "n_pf", b, out["n_pf"][b], npf)
+            assert out["n_cand"][b] == o["n_cand"][b], (tag, "n_cand", b, "gpu", out["n_cand"],
+                                                         "oracle", o["n_cand"])
+            assert np.array_equal(out["pf_tok"][b, :npf], o["pf_tok"][b, :npf]), (tag, "pf_tok")
+            assert np.array_equal(out["pf_slot"][b, :npf], o["pf_slot"][b, :npf]), (tag, "pf_slot")
+            nm = int(o["n_miss"][b])
+            assert out["n_miss"][b] == nm, (tag, "n_miss", b, out["n_miss"][b], nm)
+            assert np.array_equal(out["miss_tok"][b, :nm], o["miss_tok"][b, :nm]), (tag, "miss")
+            if o["status"] == O.OK:
+                assert np.array_equal(out["sel_slot"][b, :n], o["sel_slot"][b, :n]), \
+                    (tag, "sel_slot", b)
+        assert np.array_equal(st["theta"][:B], self.orc.theta[:B]), (tag, "theta")
+        assert np.array_equal(st["h2g"], self.orc.h2g), (tag, "h2g")
+        assert np.array_equal(st["g2h"], self.orc.g2h), (tag, "g2h")
+        assert np.array_equal(st["prio"], self.orc.prio), (tag, "prio")
+        assert np.array_equal(st["free"], self.orc.free), (tag, "free")
+        assert st["t"] == self.orc.t, (tag, "t", st["t"], self.orc.t)
+        if o["status"] == O.OK:
+            assert out["counters"][abi.ECHO_CNT_EVICT] == o["n_evict"], (tag, "n_evict")
+            assert out["counters"][abi.ECHO_CNT_MISS] == int(o["n_miss"].sum())
+            # the index buffer holds the ascending free list
+            nfree = st["nfree"]
+            assert nfree == int(self.orc.free.sum()), (tag, "nfree")
+            assert np.array_equal(st["idxbuf"][:nfree], np.nonzero(self.orc.free)[0]), \
+                (tag, "idxbuf")
+        if check_pool and self.orc.pool is not None:
+            torch.cuda.current_stream().synchronize()
+            gp = self.layer.gpu_kv.cpu().numpy().view(np.uint16)
+            assert np.array_equal(gp, self.orc.pool), (tag, "pool bytes")
+
+    def hit_rates(self):
+        hr = []
+        for out, _ in self.history:
+            sel = int(out["n_sel"].sum())
+            hr.append(1.0 - int(out["n_miss"].sum()) / sel if sel else 1.0)
+        return hr
+
+    def close(self):
+        torch.cuda.synchronize()
+        self.host.close()

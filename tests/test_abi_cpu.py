@@ -1,0 +1,115 @@
+"""The C-ABI library loads, exports every declared symbol, and its host-side logic
+(sizes, workspace carving, argument checks) works without a GPU."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from kv_cache_offload_fp8_amd import abi
+from oracle import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib_or_skip():
+    if not os.path.exists(abi.LIB_PATH):
+        pytest.skip("libecho.so not built (run __graft_entry__.build())")
+    return abi.lib()
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "echo.h")).read()
+    return sorted(set(re.findall(r"^\S[^;(]*?\b(echo_\w+)\(", src, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = _lib_or_skip()
+    names = _declared()
+    assert len(names) >= 12
+    assert set(names) == set(abi.EXPORTS)
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def test_meta_bytes_matches_oracle_and_page_example():
+    _lib_or_skip()
+    for nh, ng in [(2_000_000, 200_000), (4096, 1024), (3_200_000, 110_000), (0, 0)]:
+        assert abi.echo_meta_bytes(nh, ng) == O.meta_bytes(nh, ng)
+    assert abi.echo_meta_bytes(2_000_000, 200_000) == 10_600_000
+    assert abi.echo_meta_bytes(-1, 5) == -1
+
+
+def _dims(**kw):
+    d = dict(n_heads=64, head_dim=128, top_k=2048, latent_dim=576, n_host=2_000_000,
+             n_gpu=200_000, max_batch=8, max_ctx=65536, ema_alpha=0.5, prefetch_cap_div=128,
+             q_ring=1)
+    d.update(kw)
+    return abi.echo_dims_t(**d)
+
+
+def test_workspace_size_and_bind():
+    _lib_or_skip()
+    d = _dims()
+    n = abi.echo_ws_bytes(d)
+    assert n > 8 * 65536 * 4  # at least the score buffer
+    ws = abi.echo_ws_t()
+    base = 1 << 40  # any 256-aligned address: bind only does arithmetic
+    assert abi.echo_ws_bind(d, base, n, ws) == abi.ECHO_OK
+    ptrs = [getattr(ws, f) for f, _ in abi.echo_ws_t._fields_ if f != "internal_bytes"]
+    assert all(base <= p < base + n for p in ptrs)
+    assert len(set(ptrs)) == len(ptrs)
+    assert all(p % 256 == 0 for p in ptrs)
+    assert ws.internal + ws.internal_bytes <= base + n
+    assert ws.scores == base
+    assert abi.echo_ws_bind(d, base, n - 1, ws) == abi.ECHO_EINVAL
+    assert abi.echo_ws_bind(d, base + 8, n, ws) == abi.ECHO_EINVAL
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_heads=0), abi.ECHO_EINVAL), (dict(top_k=0), abi.ECHO_EINVAL),
+    (dict(ema_alpha=0.0), abi.ECHO_EINVAL), (dict(ema_alpha=1.5), abi.ECHO_EINVAL),
+    (dict(n_host=1 << 31), abi.ECHO_EINVAL), (dict(q_ring=0), abi.ECHO_EINVAL),
+    (dict(n_heads=65), abi.ECHO_EUNSUPPORTED), (dict(head_dim=256), abi.ECHO_EUNSUPPORTED),
+    (dict(head_dim=48), abi.ECHO_EUNSUPPORTED), (dict(top_k=4097), abi.ECHO_EUNSUPPORTED),
+    (dict(max_batch=65), abi.ECHO_EUNSUPPORTED), (dict(latent_dim=575), abi.ECHO_EUNSUPPORTED),
+])
+def test_dims_are_checked(kw, code):
+    _lib_or_skip()
+    d = _dims(**kw)
+    assert abi.echo_ws_bytes(d) == 0
+    assert abi.echo_ws_bind(d, 1 << 40, 1 << 40, abi.echo_ws_t()) == code
+
+
+def test_null_arguments_are_rejected_before_any_launch():
+    _lib_or_skip()
+    d = _dims()
+    ws = abi.echo_ws_t()
+    layer = abi.echo_layer_t()
+    batch = abi.echo_batch_t(1, None, None)  # batch of one with null arrays
+    assert abi.echo_layer_step(d, layer, batch, ws, 0, 0) == abi.ECHO_EINVAL
+    assert abi.echo_layer_step(d, None, None, None, 0, 0) == abi.ECHO_EINVAL
+    assert abi.echo_indexer_prefetch(d, None, None, None, 0, 0) == abi.ECHO_EINVAL
+    assert abi.echo_layer_step(d, layer, batch, ws, 7, 0) == abi.ECHO_EINVAL
+    assert abi.echo_topk(d, None, 65536, batch, ws, None, 0) == abi.ECHO_EINVAL
+    assert abi.echo_cache_alloc_evict(d, None, batch, ws, 0) == abi.ECHO_EINVAL
+    assert abi.echo_recall(d, None, ws, 0) == abi.ECHO_EINVAL
+    assert abi.echo_step_advance(None, None, 0) == abi.ECHO_EINVAL
+    assert abi.echo_meta_init(d, None, 0) == abi.ECHO_EINVAL
+    assert abi.echo_ws_reset(d, None, 0) == abi.ECHO_EINVAL
+    too_big = abi.echo_batch_t(9, 1, 1)  # batch above max_batch
+    assert abi.echo_topk(d, 1, 65536, too_big, ws, None, 0) == abi.ECHO_EINVAL
+
+
+def test_status_strings():
+    _lib_or_skip()
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        s = abi.echo_status_string(code)
+        assert s and s != "unknown status"
+    assert abi.echo_status_string(42) == "unknown status"
+
+
+def test_binding_has_no_compute_fallback():
+    src = open(os.path.join(ROOT, "kv_cache_offload_fp8_amd", "abi.py")).read()
+    src += open(os.path.join(ROOT, "kv_cache_offload_fp8_amd", "runtime.py")).read()
+    assert "oracle" not in src

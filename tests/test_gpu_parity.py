@@ -1,0 +1,178 @@
+"""GPU path vs the oracle, through the C ABI, on seeded inputs.
+
+Scores: within 2e-3 relative (plus the cancellation allowance of
+echo_harness.score_tolerance) of the oracle's fp64 scores.  Everything decided
+from the scores -- prefetch lists, top-k, EMA state, misses, evictions, slot maps,
+priorities, free flags, the free list and the pool bytes -- bit-exact, with the
+oracle fed the GPU's scores.
+"""
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_offload_fp8_amd import abi
+from kv_cache_offload_fp8_amd import runtime as R
+from oracle import oracle as O
+from synth import get
+
+from . import echo_harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+@pytest.mark.parametrize("mode", [H.MODE_EMA, H.MODE_NEG_INF, H.MODE_POS_INF])
+def test_tiny_decode_bit_exact(mode):
+    _say(f"tiny decode, mode {mode}")
+    rig = H.Rig(get("tiny"), steps=8)
+    for _ in range(8):
+        rig.step_and_compare(mode)
+    rig.close()
+
+
+@pytest.mark.parametrize("mode", [H.MODE_EMA, H.MODE_NEG_INF])
+def test_full_indexer_shape_ragged_with_eviction(mode):
+    # 64 heads x 128, three ragged requests, k=256, a pool that forces eviction
+    wl = get("single_layer").scaled(rho=0.6, steps=6)
+    ctx = [3000, 1777, 2561]
+    _say(f"64x128 ragged {ctx}, mode {mode}")
+    # room for one step's selection plus two steps of prefetch (caps 47+28+41)
+    rig = H.Rig(wl, steps=6, ctx=ctx, n_gpu=3 * 256 + 2 * 120, n_host=8000, top_k=256,
+                cap_div=64)
+    for _ in range(6):
+        out, _ = rig.step_and_compare(mode)
+        assert out["status"] == 0
+    assert sum(int(o["n_evict"]) for _, o in rig.history) > 0
+    rig.close()
+
+
+def test_lossless_across_modes_on_gpu():
+    wl = get("tiny").scaled(rho=0.7)
+    outs = {}
+    for mode in (H.MODE_EMA, H.MODE_NEG_INF, H.MODE_POS_INF):
+        rig = H.Rig(wl, steps=6, n_gpu=600)
+        seq = []
+        for _ in range(6):
+            rig.gpu_step(mode)
+            o = rig.ws.read(rig.B)
+            assert o["status"] == 0
+            n = int(o["n_sel"][0])
+            sel = o["sel_tok"][0, :n].copy()
+            slots = torch.as_tensor(o["sel_slot"][0, :n].astype(np.int64), device="cuda")
+            gathered = rig.layer.gpu_kv[slots].cpu().numpy().view(np.uint16)
+            assert np.array_equal(gathered, rig.np_host[rig.base[0] + sel])
+            seq.append((sel, gathered))
+        outs[mode] = seq
+        rig.close()
+    for mode in (H.MODE_EMA, H.MODE_NEG_INF):
+        for (s1, g1), (s2, g2) in zip(outs[mode], outs[H.MODE_POS_INF]):
+            assert np.array_equal(s1, s2) and np.array_equal(g1, g2)
+
+
+def test_graph_replay_matches_eager():
+    wl = get("tiny")
+    eager = H.Rig(wl, steps=6)
+    graph = H.Rig(wl, steps=6)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            graph.gpu_step(H.MODE_EMA)
+    torch.cuda.synchronize()
+    # capture does not execute: both rigs are still at step 0
+    for t in range(6):
+        eager.gpu_step(H.MODE_EMA)
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = eager.layer.state(), graph.layer.state()
+        for key in ("h2g", "g2h", "prio", "free", "theta", "idxbuf"):
+            assert np.array_equal(a[key], b[key]), (t, key)
+        assert a["t"] == b["t"] == t + 1
+        oa, ob = eager.ws.read(eager.B), graph.ws.read(graph.B)
+        assert np.array_equal(oa["sel_tok"], ob["sel_tok"])
+        assert np.array_equal(eager.gpu_scores(), graph.gpu_scores())
+        assert torch.equal(eager.layer.gpu_kv, graph.layer.gpu_kv)
+    eager.close()
+    graph.close()
+
+
+@pytest.mark.parametrize("n,k", [(5000, 256), (256, 256), (100, 256), (257, 256), (9000, 2048)])
+def test_topk_external_scores_with_ties(n, k):
+    rng = np.random.default_rng(n + k)
+    B = 3
+    sc = rng.integers(0, 40, size=(B, n)).astype(np.float32)  # heavy ties
+    sc[1] = rng.standard_normal(n).astype(np.float32) * 100
+    sc[2, : n // 2] = 7.0
+    dims = R.make_dims(4, 32, k, 3 * n, 4096, B, n)
+    ws = R.Workspace(dims)
+    ws.reset()
+    batch = R.Batch(np.arange(B) * n, [n] * B)
+    dev = torch.from_numpy(sc).cuda()
+    theta = torch.full((B,), float("inf"), device="cuda")
+    R.check(abi.echo_topk(dims, dev.data_ptr(), n, batch.struct, ws.ws, theta.data_ptr(),
+                          R.stream_handle()), "echo_topk")
+    o = ws.read(B)
+    assert o["status"] == 0
+    for b in range(B):
+        sel, kth = O.topk(sc[b], k)
+        m = sel.size
+        assert o["n_sel"][b] == m
+        assert np.array_equal(o["sel_tok"][b, :m], sel), b
+        assert np.float32(o["kth"][b]) == np.float32(kth)
+        if n >= k:
+            assert theta[b].item() == np.float32(kth)
+
+
+def test_capacity_error_matches_oracle():
+    wl = get("tiny")
+    rig = H.Rig(wl, steps=2, n_gpu=200)  # k=256 misses > 200 slots
+    out, o = rig.step_and_compare(H.MODE_POS_INF, expect_status=abi.ECHO_ECAPACITY)
+    assert out["status"] == abi.ECHO_ECAPACITY == o["status"]
+    # the error is sticky: the next call changes nothing until the workspace is reset
+    before = rig.layer.state()
+    rig.gpu_step(H.MODE_POS_INF)
+    after = rig.layer.state()
+    for key in ("h2g", "g2h", "prio", "free"):
+        assert np.array_equal(before[key], after[key])
+    assert after["t"] == 0
+    rig.close()
+
+
+def test_device_side_batch_check():
+    wl = get("tiny").scaled(n_host=8192)
+    rig = H.Rig(wl, steps=1, ctx=[4096])
+    bad = R.Batch([0, 100], [4096, 50], "cuda")  # overlapping host ranges
+    dims = R.make_dims(wl.heads, wl.head_dim, wl.top_k, wl.n_host, wl.n_gpu, 2, 4096,
+                       q_ring=1)
+    ws = R.Workspace(dims)
+    ws.reset()
+    layer = R.Layer(dims, rig.kidx, rig.host, 2)
+    layer.init()
+    R.check(abi.echo_layer_step(dims, layer.struct, bad.struct, ws.ws, H.MODE_EMA,
+                                R.stream_handle()), "launch")
+    o = ws.read(2)
+    assert o["status"] == abi.ECHO_EDEVARG
+    st = layer.state()
+    assert st["t"] == 0 and (st["h2g"] == -1).all() and (st["free"] == 1).all()
+    rig.close()
+
+
+def test_context_edge_cases():
+    # an empty request, one shorter than k, one equal to k, one just above k
+    wl = get("tiny").scaled(n_host=4 * 1024)
+    ctx = [0, 100, 256, 257]
+    rig = H.Rig(wl, steps=4, ctx=ctx, n_gpu=1024)
+    for mode in (H.MODE_EMA, H.MODE_NEG_INF, H.MODE_EMA, H.MODE_EMA):
+        rig.step_and_compare(mode)
+    rig.close()
