@@ -51,6 +51,8 @@ def parse():
     p.add_argument("--cpu-sample-requests", type=int, default=8)
     p.add_argument("--mode", default="ema", choices=["ema", "neg_inf", "pos_inf"])
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--cap-div", type=int, default=None,
+                   help="override the prefetch cap divisor (cap = min(k, ceil(ctx/div)))")
     return p.parse_args()
 
 
@@ -72,6 +74,8 @@ def main():
     torch.cuda.set_device(0)
     dev = "cuda"
     wl = get(args.workload)
+    if args.cap_div:
+        wl = wl.scaled(cap_div=args.cap_div)
     L = args.layers or wl.layers
     mode = {"ema": abi.ECHO_THETA_EMA, "neg_inf": abi.ECHO_THETA_NEG_INF,
             "pos_inf": abi.ECHO_THETA_POS_INF}[args.mode]

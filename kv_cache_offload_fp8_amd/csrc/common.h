@@ -13,7 +13,7 @@ namespace echo {
 constexpr int kWave = 64;
 constexpr int kHeadsPad = 64;     // indexer heads padded to 4 groups of 16 (MFMA rows)
 constexpr int kDimPad = 128;      // indexer dim padded to four 16x16x32 bf16 MFMA k-steps
-constexpr int kScoreTile = 256;   // tokens per scoring work item (4 waves x 64)
+constexpr int kScoreTile = 1024;  // tokens per scoring work item (4 waves x 4 x 64)
 constexpr int kBins = 4096;       // first-level histogram bins
 constexpr int kSelChunk = 8192;   // tokens per block in the top-k histogram/collect passes
 constexpr int kSlotTile = 4096;   // slots per block in the eviction and allocation passes

@@ -175,10 +175,67 @@ hipError_t launch_begin(const StepArgs &a, int roles, hipStream_t s) {
 
 // ------------------------------------------------------------------ score
 
+constexpr int kChunks = kScoreTile / 256;  // 64-token chunks per wave per work item
+
+// K rows of one 64-token chunk for this lane: 4 MFMA sub-tiles of 16 tokens,
+// 32 bytes each (dims chunk .. chunk+31 of token s0 + 16u + row).
+__device__ inline void load_k_chunk(const StepArgs &a, const ReqInfo &r, int s0, int row,
+                                    int chunk, v8i (&kb)[4]) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int s = s0 + u * 16 + row;
+    v8i x = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (s < r.ctx && chunk < a.D) {
+      const v4i *p = (const v4i *)(a.kidx + ((int64_t)r.base + s) * a.D + chunk);
+      const v4i x0 = __builtin_nontemporal_load(p);
+      const v4i x1 = __builtin_nontemporal_load(p + 1);
+      x[0] = x0[0]; x[1] = x0[1]; x[2] = x0[2]; x[3] = x0[3];
+      x[4] = x1[0]; x[5] = x1[1]; x[6] = x1[2]; x[7] = x1[3];
+    }
+    kb[u] = x;
+  }
+}
+
+// Scores of one 64-token chunk: returns, in lane l, the score of token s0 + l.
+template <int HG>
+__device__ inline float score_chunk(const v8i (&kb)[4], const v8bf (&qa)[HG][4],
+                                    const float (&wr)[HG][4], int lane) {
+  float sc4[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    v8bf kf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int w0 = kb[u][2 * ks], w1 = kb[u][2 * ks + 1];
+      const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+      const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+      const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+      const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+      kf[ks] = (v8bf){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+    }
+    float v = 0.0f;
+#pragma unroll
+    for (int hg = 0; hg < HG; ++hg) {
+      v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[hg][ks], kf[ks], acc, 0, 0, 0);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) v += wr[hg][rr] * fmaxf(acc[rr], 0.0f);
+    }
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    sc4[u] = v;  // every lane with (lane & 15) == i holds the score of token 16u + i
+  }
+  const int sel = lane >> 4;
+  return sel == 0 ? sc4[0] : sel == 1 ? sc4[1] : sel == 2 ? sc4[2] : sc4[3];
+}
+
 template <int HG>
 __global__ __launch_bounds__(256) void k_score(StepArgs a) {
   __shared__ __align__(16) uint16_t s_q[HG * 16][kDimPad];
-  __shared__ int s_tau, s_b, s_E, s_nemit;
+  __shared__ ReqInfo s_req[kMaxBatch];
+  __shared__ int s_next, s_E, s_nemit;
   __shared__ int s_wcnt[4];
   __shared__ uint32_t s_kmin[4], s_kmax[4];
   __shared__ int32_t s_emit_h[kScoreTile], s_emit_g[kScoreTile];
@@ -196,26 +253,24 @@ __global__ __launch_bounds__(256) void k_score(StepArgs a) {
   const int nfree = a.ctl[ECHO_CTL_NFREE];
   const int cpr = a.latent * 2 / 16;  // 16-byte chunks per latent row
 
+  for (int i = tid; i < a.B; i += 256) s_req[i] = a.sc.req[i];
+  if (tid == 0) s_next = atomicAdd(&a.sc.misc[M_TICKET_SCORE], 1);
+  __syncthreads();
+
   int cur_b = -1;
   v8bf qa[HG][4];
   float wr[HG][4];
 
   for (;;) {
-    if (tid == 0) {
-      const int tau = atomicAdd(&a.sc.misc[M_TICKET_SCORE], 1);
-      int b = 0;
-      for (int i = 0; i < a.B; ++i) {
-        const ReqInfo &r = a.sc.req[i];
-        if (r.tile0 <= tau && tau < r.tile0 + r.ntiles) b = i;
-      }
-      s_tau = tau;
-      s_b = b;
-    }
-    __syncthreads();
-    const int tau = s_tau;
-    const int b = s_b;
-    if (tau >= total) break;
-    const ReqInfo r = a.sc.req[b];
+    const int tau = s_next;
+    if (tau >= total) break;  // uniform
+    __syncthreads();          // every thread has read s_next
+    // fetch the next work item now; its latency hides behind this one
+    if (tid == 0) s_next = atomicAdd(&a.sc.misc[M_TICKET_SCORE], 1);
+    int b = 0;
+    for (int i = 0; i < a.B; ++i)
+      if (s_req[i].tile0 <= tau && tau < s_req[i].tile0 + s_req[i].ntiles) b = i;
+    const ReqInfo r = s_req[b];
 
     if (b != cur_b) {  // stage this request's query, then keep it in registers
       const uint4 *src = (const uint4 *)(a.sc.qbf + (int64_t)b * kHeadsPad * kDimPad);
@@ -234,141 +289,127 @@ __global__ __launch_bounds__(256) void k_score(StepArgs a) {
       cur_b = b;
     }
 
-    // ---- stream this wave's 64 K rows (4 MFMA sub-tiles of 16 tokens)
-    const int s_wave = (tau - r.tile0) * kScoreTile + wid * 64;
-    v8i kb[4];
+    // ---- stream this wave's kChunks x 64 tokens, next chunk's loads in flight
+    const int s_wave = (tau - r.tile0) * kScoreTile + wid * (kScoreTile / 4);
+    float *out = a.ws.scores + (int64_t)b * a.max_ctx;
+    v8i kb[2][4];
+    load_k_chunk(a, r, s_wave, row, chunk, kb[0]);
+    uint64_t above[kChunks];
+    uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int s = s_wave + u * 16 + row;
-      v8i x = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (s < r.ctx && chunk < a.D) {
-        const v4i *p = (const v4i *)(a.kidx + ((int64_t)r.base + s) * a.D + chunk);
-        const v4i x0 = __builtin_nontemporal_load(p);
-        const v4i x1 = __builtin_nontemporal_load(p + 1);
-        x[0] = x0[0]; x[1] = x0[1]; x[2] = x0[2]; x[3] = x0[3];
-        x[4] = x1[0]; x[5] = x1[1]; x[6] = x1[2]; x[7] = x1[3];
-      }
-      kb[u] = x;
+    for (int c = 0; c < kChunks; ++c) {
+      if (c + 1 < kChunks) load_k_chunk(a, r, s_wave + (c + 1) * 64, row, chunk, kb[(c + 1) & 1]);
+      const float score = score_chunk<HG>(kb[c & 1], qa, wr, lane);
+      const int s = s_wave + c * 64 + lane;
+      const bool valid = s < r.ctx;
+      if (valid) out[s] = score;
+      const uint32_t key = topk_key(score);
+      kmn = valid ? min(kmn, key) : kmn;
+      kmx = valid ? max(kmx, key) : kmx;
+      above[c] = __ballot(r.active && valid && score > r.theta);
     }
+    kmn = wave_min_u32(kmn);
+    kmx = wave_max_u32(kmx);
 
-    // ---- widen K to bf16, heads x tokens on the bf16 MFMA, ReLU, weights, head sum
-    float sc4[4];
+    // ---- prefetch candidates: above the threshold and not resident
+    int wc = 0;
+    uint64_t cand[kChunks];
+    if (r.active) {
+      int g_of[kChunks];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      v8bf kf[4];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int w0 = kb[u][2 * ks], w1 = kb[u][2 * ks + 1];
-        const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
-        const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
-        const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
-        const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
-        kf[ks] = (v8bf){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+      for (int c = 0; c < kChunks; ++c) {  // one batch of map lookups per work item
+        g_of[c] = 0;
+        if ((above[c] >> lane) & 1ull)
+          g_of[c] = a.h2g[(int64_t)r.base + s_wave + c * 64 + lane];
       }
-      float v = 0.0f;
 #pragma unroll
-      for (int hg = 0; hg < HG; ++hg) {
-        v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[hg][ks], kf[ks], acc, 0, 0, 0);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) v += wr[hg][rr] * fmaxf(acc[rr], 0.0f);
+      for (int c = 0; c < kChunks; ++c) {
+        cand[c] = __ballot(((above[c] >> lane) & 1ull) && g_of[c] == -1);
+        wc += __popcll(cand[c]);
       }
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
-      sc4[u] = v;  // every lane with (lane & 15) == i holds the score of token 16u + i
     }
-    const int sel = lane >> 4;
-    const float score = sel == 0 ? sc4[0] : sel == 1 ? sc4[1] : sel == 2 ? sc4[2] : sc4[3];
-    const int s = s_wave + lane;  // lane l now owns token s_wave + l
-    const bool valid = s < r.ctx;
-    if (valid) a.ws.scores[(int64_t)b * a.max_ctx + s] = score;
-
-    const uint32_t key = topk_key(score);
-    const uint32_t kmn = wave_min_u32(valid ? key : 0xFFFFFFFFu);
-    const uint32_t kmx = wave_max_u32(valid ? key : 0u);
-    bool cand = false;
-    if (r.active && valid && score > r.theta) cand = a.h2g[(int64_t)r.base + s] == -1;
-    const uint64_t m = __ballot(cand);
     if (lane == 0) {
       s_kmin[wid] = kmn;
       s_kmax[wid] = kmx;
-      s_wcnt[wid] = __popcll(m);
+      s_wcnt[wid] = wc;
     }
     if (tid == 0) s_nemit = 0;
     __syncthreads();
     if (tid == 0) {
-      const uint32_t mn = min(min(s_kmin[0], s_kmin[1]), min(s_kmin[2], s_kmin[3]));
-      const uint32_t mx = max(max(s_kmax[0], s_kmax[1]), max(s_kmax[2], s_kmax[3]));
-      atomicMin(&a.sc.kmin[b], mn);
-      atomicMax(&a.sc.kmax[b], mx);
+      atomicMin(&a.sc.kmin[b], min(min(s_kmin[0], s_kmin[1]), min(s_kmin[2], s_kmin[3])));
+      atomicMax(&a.sc.kmax[b], max(max(s_kmax[0], s_kmax[1]), max(s_kmax[2], s_kmax[3])));
     }
 
     if (r.active) {  // uniform over the block
-      const int c = s_wcnt[0] + s_wcnt[1] + s_wcnt[2] + s_wcnt[3];
-      int woff = 0;
-      for (int i = 0; i < wid; ++i) woff += s_wcnt[i];
+      const int c_all = s_wcnt[0] + s_wcnt[1] + s_wcnt[2] + s_wcnt[3];
+      int base = 0;
+      for (int i = 0; i < wid; ++i) base += s_wcnt[i];
       if (wid == 0) {
-        const int E = lookback(a.sc.tstate, tau, r.tile0, c, status);
+        const int E = lookback(a.sc.tstate, tau, r.tile0, c_all, status);
         if (lane == 0) s_E = E;
       }
       __syncthreads();
-      const int E = s_E;
-      if (cand) {
-        const int rank = E + woff + __popcll(m & lanemask_lt());
-        if (rank < r.cap) {
-          const int j = r.off + rank;
-          const int g = (j < nfree && j < a.n_gpu) ? a.idxbuf[j] : -1;
-          if (g >= 0 && g < a.n_gpu) {
-            const int64_t h = (int64_t)r.base + s;
-            a.h2g[h] = g;
-            a.g2h[g] = (int32_t)h;
-            a.freef[g] = 0;
-            a.prio[g] = t;
-            a.ws.pf_tok[(int64_t)b * a.K + rank] = s;
-            a.ws.pf_slot[(int64_t)b * a.K + rank] = g;
-            const int e = atomicAdd(&s_nemit, 1);
-            s_emit_h[e] = (int32_t)h;
-            s_emit_g[e] = g;
+      base += s_E;
+#pragma unroll
+      for (int c = 0; c < kChunks; ++c) {
+        const uint64_t m = cand[c];
+        if ((m >> lane) & 1ull) {
+          const int rank = base + __popcll(m & lanemask_lt());
+          if (rank < r.cap) {
+            const int j = r.off + rank;
+            const int g = (j < nfree && j < a.n_gpu) ? a.idxbuf[j] : -1;
+            if (g >= 0 && g < a.n_gpu) {
+              const int s = s_wave + c * 64 + lane;
+              const int64_t h = (int64_t)r.base + s;
+              a.h2g[h] = g;
+              a.g2h[g] = (int32_t)h;
+              a.freef[g] = 0;
+              a.prio[g] = t;
+              a.ws.pf_tok[(int64_t)b * a.K + rank] = s;
+              a.ws.pf_slot[(int64_t)b * a.K + rank] = g;
+              const int e = atomicAdd(&s_nemit, 1);
+              s_emit_h[e] = (int32_t)h;
+              s_emit_g[e] = g;
+            }
           }
         }
+        base += __popcll(m);
       }
       __syncthreads();
       const int ne = s_nemit;
       if (ne > 0) {
-        // copy the emitted latent rows host -> GPU pool, two loads in flight per thread
+        // copy the emitted latent rows host -> GPU pool, four loads in flight per thread
         const uint4 *src = (const uint4 *)a.host_kv;
         uint4 *dst = (uint4 *)a.gpu_kv;
         const int nchunks = ne * cpr;
-        for (int i0 = tid; i0 < nchunks; i0 += 2 * 256) {
-          const int i1 = i0 + 256;
-          const int e0 = i0 / cpr, c0 = i0 - e0 * cpr;
-          const uint4 v0 = src[(int64_t)s_emit_h[e0] * cpr + c0];
-          uint4 v1 = v0;
-          int e1 = 0, c1 = 0;
-          if (i1 < nchunks) {
-            e1 = i1 / cpr;
-            c1 = i1 - e1 * cpr;
-            v1 = src[(int64_t)s_emit_h[e1] * cpr + c1];
-          }
-          dst[(int64_t)s_emit_g[e0] * cpr + c0] = v0;
-          if (i1 < nchunks) dst[(int64_t)s_emit_g[e1] * cpr + c1] = v1;
+        for (int i0 = tid; i0 < nchunks; i0 += 4 * 256) {
+          uint4 v0, v1, v2, v3;
+          int e0 = i0 / cpr, e1 = 0, e2 = 0, e3 = 0;
+          const int i1 = i0 + 256, i2 = i0 + 512, i3 = i0 + 768;
+          v0 = src[(int64_t)s_emit_h[e0] * cpr + (i0 - e0 * cpr)];
+          if (i1 < nchunks) { e1 = i1 / cpr; v1 = src[(int64_t)s_emit_h[e1] * cpr + (i1 - e1 * cpr)]; }
+          if (i2 < nchunks) { e2 = i2 / cpr; v2 = src[(int64_t)s_emit_h[e2] * cpr + (i2 - e2 * cpr)]; }
+          if (i3 < nchunks) { e3 = i3 / cpr; v3 = src[(int64_t)s_emit_h[e3] * cpr + (i3 - e3 * cpr)]; }
+          dst[(int64_t)s_emit_g[e0] * cpr + (i0 - e0 * cpr)] = v0;
+          if (i1 < nchunks) dst[(int64_t)s_emit_g[e1] * cpr + (i1 - e1 * cpr)] = v1;
+          if (i2 < nchunks) dst[(int64_t)s_emit_g[e2] * cpr + (i2 - e2 * cpr)] = v2;
+          if (i3 < nchunks) dst[(int64_t)s_emit_g[e3] * cpr + (i3 - e3 * cpr)] = v3;
         }
         if (tid == 0) {
           atomicAdd(&a.ws.n_pf[b], ne);
           atomicAdd(&a.ws.counters[ECHO_CNT_PREFETCH], ne);
         }
       }
-      if (tid == 0 && c > 0) atomicAdd(&a.ws.n_cand[b], c);
+      if (tid == 0 && c_all > 0) atomicAdd(&a.ws.n_cand[b], c_all);
     }
-    __syncthreads();
+    __syncthreads();  // s_next is written; LDS may be reused
   }
 }
 
 hipError_t launch_score(const StepArgs &a, hipStream_t s) {
   const int hg = (a.H + 15) / 16;
-  int grid = a.sc.max_tiles < 1024 ? a.sc.max_tiles : 1024;
+  // persistent grid: two workgroups per CU, work items handed out by ticket
+  int grid = a.sc.max_tiles < 512 ? a.sc.max_tiles : 512;
   if (grid < 1) grid = 1;
   switch (hg) {
     case 1: hipLaunchKernelGGL(k_score<1>, dim3(grid), dim3(256), 0, s, a); break;
