@@ -154,6 +154,7 @@ def main():
     st = int(ws.status.item())
     if st != 0:
         raise SystemExit(f"device status after timed steps: {abi.echo_status_string(st)}")
+    shortcut_last = int(ws.counters[abi.ECHO_CNT_SHORTCUT].item())
     ms_per_step = elapsed * 1e3 / args.steps
     layer_steps_per_s = args.steps * L / elapsed
     log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step, "
@@ -165,7 +166,7 @@ def main():
     nph = 4
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nph + 1)]
            for _ in range(args.breakdown_steps * L)]
-    miss_rows, sel_rows, pf_rows = [], [], []
+    miss_rows, sel_rows, pf_rows, sc_rows = [], [], [], []
     i = 0
     for _ in range(args.breakdown_steps):
         for lay in layers:
@@ -187,6 +188,7 @@ def main():
             c = ws.counters.clone()
             miss_rows.append(c[abi.ECHO_CNT_MISS])
             pf_rows.append(c[abi.ECHO_CNT_PREFETCH])
+            sc_rows.append(c[abi.ECHO_CNT_SHORTCUT])
             sel_rows.append(ws.n_sel[:B].sum())
             i += 1
     torch.cuda.synchronize()
@@ -278,6 +280,7 @@ def main():
                      "alloc_evict": round(float(ph[:, 2].mean()), 5),
                      "recall": round(float(recall_ms.mean()), 5)},
         "hit_rate": round(hit, 5),
+        "topk_shortcut_requests_last_layer": f"{shortcut_last}/{B}",
         "misses_per_layer_step": round(float(misses.mean()), 1),
         "prefetched_per_layer_step": round(float(prefetched.mean()), 1),
         "cpu_baseline": cpu,

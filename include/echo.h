@@ -69,6 +69,7 @@ enum {
   ECHO_CNT_EVICTABLE = 3, /* occupied slots with priority < t                      */
   ECHO_CNT_FREE_END = 4,  /* free slots after allocation                           */
   ECHO_CNT_PREFETCH = 5,  /* tokens prefetched this step (all requests)            */
+  ECHO_CNT_SHORTCUT = 6,  /* requests whose top-k came from the guard candidates   */
   ECHO_NCOUNTERS = 16
 };
 
@@ -118,6 +119,11 @@ typedef struct {
   const uint16_t *q;       /* [q_ring][batch][n_heads][head_dim] bf16 queries        */
   const float *w;          /* [batch][n_heads] fp32 head weights                     */
   float *theta;            /* [max_batch] EMA threshold, +inf = no estimate yet       */
+  float *guard;            /* [max_batch] last step's k-th score, +inf = none; may be
+                              NULL.  Only a shortcut for the exact top-k (tokens near or
+                              above it are collected while scoring, and if at least k
+                              are, the full-score passes are skipped); results never
+                              depend on it. */
   int32_t *ctl;            /* [ECHO_CTL_WORDS] step counter and free-list length      */
 } echo_layer_t;
 
@@ -166,7 +172,8 @@ int echo_ws_bind(const echo_dims_t *dims, void *base, size_t bytes, echo_ws_t *w
 /* ------------------------------------------------------------- init */
 
 /* Reset one layer: every slot free (free=1, prio=-1, g2h=-1), h2g=-1 for every
- * host token, idxbuf = 0..n_gpu-1, theta = +inf for max_batch requests, step 0. */
+ * host token, idxbuf = 0..n_gpu-1, theta = guard = +inf for max_batch requests,
+ * step 0. */
 int echo_meta_init(const echo_dims_t *dims, const echo_layer_t *layer, hipStream_t stream);
 
 /* Clear the workspace (status, counters and internal scratch). */

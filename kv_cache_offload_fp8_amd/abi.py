@@ -16,7 +16,7 @@ ECHO_OK, ECHO_EINVAL, ECHO_EHIP, ECHO_EUNSUPPORTED = 0, -1, -2, -3
 ECHO_ECAPACITY, ECHO_ETIMEOUT, ECHO_EDEVARG = -4, -5, -6
 ECHO_THETA_EMA, ECHO_THETA_NEG_INF, ECHO_THETA_POS_INF = 0, 1, 2
 (ECHO_CNT_MISS, ECHO_CNT_EVICT, ECHO_CNT_FREE, ECHO_CNT_EVICTABLE, ECHO_CNT_FREE_END,
- ECHO_CNT_PREFETCH) = range(6)
+ ECHO_CNT_PREFETCH, ECHO_CNT_SHORTCUT) = range(7)
 ECHO_NCOUNTERS = 16
 ECHO_CTL_STEP, ECHO_CTL_NFREE, ECHO_CTL_WORDS = 0, 1, 4
 
@@ -40,7 +40,7 @@ class echo_layer_meta_t(C.Structure):
 
 class echo_layer_t(C.Structure):
     _fields_ = [("meta", echo_layer_meta_t), ("k_index", P), ("gpu_kv", P), ("host_kv", P),
-                ("q", P), ("w", P), ("theta", P), ("ctl", P)]
+                ("q", P), ("w", P), ("theta", P), ("guard", P), ("ctl", P)]
 
 
 class echo_batch_t(C.Structure):

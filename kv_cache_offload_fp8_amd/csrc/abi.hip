@@ -112,11 +112,13 @@ StepArgs make_args(const echo_dims_t &d, const echo_layer_t *l, const echo_batch
     a.q = l->q;
     a.w = l->w;
     a.theta = l->theta;
+    a.guard = l->guard;
     a.ctl = l->ctl;
   }
   a.scores_in = ws.scores;
   a.score_stride = d.max_ctx;
   a.theta_upd = nullptr;
+  a.guard_upd = nullptr;
   a.mode = mode;
   a.ws = ws;
   scratch_layout(d, ws.internal, &a.sc);
@@ -274,8 +276,11 @@ int echo_layer_step(const echo_dims_t *dims, const echo_layer_t *layer, const ec
     return ECHO_EINVAL;
   StepArgs a = make_args(*dims, layer, batch, *ws, theta_mode);
   a.theta_upd = theta_mode == ECHO_THETA_EMA ? layer->theta : nullptr;
+  a.guard_upd = layer->guard;
   rc = run_indexer(a, BEGIN_CLR_MANAGE, stream);
   if (rc != ECHO_OK) return rc;
+  // the histogram passes only run for requests the selection guard did not cover
+  LAUNCH(launch_topk_minmax(a, stream));
   LAUNCH(launch_topk_hist(a, stream));
   LAUNCH(launch_topk_collect(a, stream));
   LAUNCH(launch_topk_resolve(a, true, stream));

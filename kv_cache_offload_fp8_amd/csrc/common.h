@@ -12,8 +12,12 @@ namespace echo {
 // ----------------------------------------------------------------- sizes
 constexpr int kWave = 64;
 constexpr int kHeadsPad = 64;     // indexer heads padded to 4 groups of 16 (MFMA rows)
-constexpr int kDimPad = 128;      // indexer dim padded to four 16x16x32 bf16 MFMA k-steps
-constexpr int kScoreTile = 1024;  // tokens per scoring work item (4 waves x 4 x 64)
+constexpr int kDimPad = 128;      // indexer dim padded to one 16x16x128 fp8 MFMA k-step
+constexpr int kScoreTile = 256;   // tokens per scoring work item (one wave, 4 x 64)
+constexpr int kGuardSlots = 32;   // selection-guard candidates kept per work item
+constexpr int kScoreWaves = 7;    // scoring waves per workgroup; the eighth copies rows
+constexpr int kRing = 1024;       // LDS ring of prefetched rows waiting for the copy wave
+constexpr uint32_t kGuardUlps = 1u << 18;  // selection guard margin: ~3% below last k-th score
 constexpr int kBins = 4096;       // first-level histogram bins
 constexpr int kSelChunk = 8192;   // tokens per block in the top-k histogram/collect passes
 constexpr int kSlotTile = 4096;   // slots per block in the eviction and allocation passes
@@ -42,15 +46,19 @@ struct ReqInfo {
   int32_t ntiles;  // scoring work items of this request
   int32_t active;  // prefetch enabled for this request in this step
   float theta;     // prefetch threshold
+  int32_t use_guard;   // collect selection candidates with key <= guard_key
+  uint32_t guard_key;  // top-k key of (last k-th score - margin), saturated
+  int32_t pad[6];
 };
 
 // Carved internal scratch.  Every region starts 256-byte aligned.
 struct Scratch {
-  uint16_t *qbf;          // [max_batch][64][128] bf16 query, zero-padded
-  float *wsc;             // [max_batch][64] head weights, zero-padded
+  uint8_t *qhi, *qlo;     // [max_batch][64][128] fp8 split of the scaled query, zero-padded
+  float *wsc;             // [max_batch][64] head weights / query scale, zero-padded
   ReqInfo *req;           // [max_batch]
   int32_t *misc;          // [M_NMISC]
   uint64_t *tstate;       // [max_tiles] scoring look-back states
+  int32_t *rq_next;       // [max_batch] next scoring work item of each request
   uint32_t *kmin, *kmax;  // [max_batch] key range per request
   uint32_t *thist;        // [max_batch][kBins]
   uint32_t *tcand_key;    // [max_batch][max_ctx]
@@ -59,13 +67,18 @@ struct Scratch {
   int32_t *tbelow;        // [max_batch]
   int32_t *tbin;          // [max_batch]
   uint32_t *tbits;        // [max_batch][bw] selection bitmap
+  uint32_t *gcand_key;    // [max_tiles][kGuardSlots] candidates above the selection guard
+  int32_t *gcand_idx;     // [max_tiles][kGuardSlots]
+  int32_t *gcand_cnt;     // [max_tiles] candidates found in each work item
+  int32_t *gcand_n;       // [max_batch] total per request (no-return atomics)
+  int32_t *gcand_ovf;     // [max_batch] nonzero if a work item overflowed its slots
   int32_t *miss_i;        // [max_batch][top_k] position of each miss in sel_tok
   uint32_t *ehist;        // [kBins]
   uint32_t *ecand_key;    // [n_gpu]
   int32_t *ecand_idx;     // [n_gpu]
   int32_t *ecnt;          // [4]: candidates, below, boundary bin
   uint64_t *astate;       // [alloc tiles] free-list look-back states
-  int32_t max_tiles, bw, atiles;
+  int32_t max_tiles, bw, atiles, cap_g;
 };
 
 inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
@@ -83,11 +96,13 @@ inline int64_t scratch_layout(const echo_dims_t &d, uint8_t *base, Scratch *s) {
   const int32_t bw = (int32_t)((C + 63) / 64 * 2);  // whole 64-bit groups
   const int32_t atiles = (int32_t)((G + kSlotTile - 1) / kSlotTile);
   Scratch t;
-  t.qbf = (uint16_t *)take(B * kHeadsPad * kDimPad * 2);
+  t.qhi = take(B * kHeadsPad * kDimPad);
+  t.qlo = take(B * kHeadsPad * kDimPad);
   t.wsc = (float *)take(B * kHeadsPad * 4);
   t.req = (ReqInfo *)take(B * sizeof(ReqInfo));
   t.misc = (int32_t *)take(M_NMISC * 4);
   t.tstate = (uint64_t *)take((int64_t)max_tiles * 8);
+  t.rq_next = (int32_t *)take(B * 4);
   t.kmin = (uint32_t *)take(B * 4);
   t.kmax = (uint32_t *)take(B * 4);
   t.thist = (uint32_t *)take(B * kBins * 4);
@@ -97,6 +112,12 @@ inline int64_t scratch_layout(const echo_dims_t &d, uint8_t *base, Scratch *s) {
   t.tbelow = (int32_t *)take(B * 4);
   t.tbin = (int32_t *)take(B * 4);
   t.tbits = (uint32_t *)take(B * bw * 4);
+  const int32_t cap_g = (int32_t)(C < 4 * K ? C : 4 * K);
+  t.gcand_key = (uint32_t *)take((int64_t)max_tiles * kGuardSlots * 4);
+  t.gcand_idx = (int32_t *)take((int64_t)max_tiles * kGuardSlots * 4);
+  t.gcand_cnt = (int32_t *)take((int64_t)max_tiles * 4);
+  t.gcand_n = (int32_t *)take(B * 4);
+  t.gcand_ovf = (int32_t *)take(B * 4);
   t.miss_i = (int32_t *)take(B * K * 4);
   t.ehist = (uint32_t *)take(kBins * 4);
   t.ecand_key = (uint32_t *)take(G * 4);
@@ -106,6 +127,7 @@ inline int64_t scratch_layout(const echo_dims_t &d, uint8_t *base, Scratch *s) {
   t.max_tiles = max_tiles;
   t.bw = bw;
   t.atiles = atiles;
+  t.cap_g = cap_g;
   if (s) *s = t;
   return off;
 }
@@ -285,6 +307,31 @@ __device__ inline int bin_shift(uint32_t kmin, uint32_t kmax) {
   uint32_t range = kmax - kmin;
   int bits = range ? 32 - __clz(range) : 0;
   return bits > 12 ? bits - 12 : 0;
+}
+
+// ------------------------------------------------------------ fp8 E4M3FN
+// Round-to-nearest-even encode of a finite float with |x| < 464 (the scaled
+// queries never need saturation).
+__device__ inline uint8_t e4m3_encode(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fabsf(x);
+  if (a == 0.0f) return (uint8_t)sign;
+  int E = (int)((__float_as_uint(a) >> 23) & 0xFF) - 127;
+  if (E < -6) {  // subnormal range: multiples of 2^-9 (m == 8 is the smallest normal)
+    const int m = (int)rintf(a * 512.0f);
+    return (uint8_t)(sign | (uint32_t)m);
+  }
+  int m = (int)rintf((ldexpf(a, -E) - 1.0f) * 8.0f);  // 0..8
+  if (m == 8) {
+    m = 0;
+    E += 1;
+  }
+  return (uint8_t)(sign | (uint32_t)((E + 7) << 3) | (uint32_t)m);
+}
+__device__ inline float e4m3_decode(uint8_t c) {
+  const int e = (c >> 3) & 0xF, m = c & 7;
+  const float v = e == 0 ? ldexpf((float)m, -9) : ldexpf(1.0f + m * 0.125f, e - 7);
+  return (c & 0x80) ? -v : v;
 }
 
 }  // namespace echo

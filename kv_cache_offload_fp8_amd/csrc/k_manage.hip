@@ -150,7 +150,10 @@ __global__ __launch_bounds__(256) void k_meta_init(StepArgs a) {
     a.idxbuf[i] = (int32_t)i;
     a.freef[i] = 1;
   }
-  for (int64_t i = i0; i < a.max_batch; i += step) a.theta[i] = __builtin_huge_valf();
+  for (int64_t i = i0; i < a.max_batch; i += step) {
+    a.theta[i] = __builtin_huge_valf();
+    if (a.guard) a.guard[i] = __builtin_huge_valf();
+  }
   if (i0 == 0) {
     a.ctl[ECHO_CTL_STEP] = 0;
     a.ctl[ECHO_CTL_NFREE] = a.n_gpu;

@@ -128,6 +128,13 @@ __device__ static inline bool composite_selected(uint32_t key, int32_t idx, uint
 
 // ------------------------------------------------------------------ top-k
 
+// True when request b's exact top-k lies among the candidates collected above the
+// selection guard while scoring: at least k were found and all of them fit the list.
+__device__ static inline bool guard_covers(const StepArgs &a, int b) {
+  if (!a.sc.req[b].use_guard) return false;
+  return a.sc.gcand_ovf[b] == 0 && a.sc.gcand_n[b] >= a.K;
+}
+
 // Key range per request, for callers that pass their own scores.
 __global__ __launch_bounds__(256) void k_topk_minmax(StepArgs a) {
   __shared__ uint32_t s_mn[4], s_mx[4];
@@ -135,7 +142,7 @@ __global__ __launch_bounds__(256) void k_topk_minmax(StepArgs a) {
   const int b = blockIdx.y;
   const int ctx = a.sc.req[b].ctx;
   const int c0 = blockIdx.x * kSelChunk;
-  if (c0 >= ctx) return;
+  if (c0 >= ctx || guard_covers(a, b)) return;
   const float *sc = a.scores_in + (int64_t)b * a.score_stride;
   uint32_t mn = 0xFFFFFFFFu, mx = 0;
   const int end = min(ctx, c0 + kSelChunk);
@@ -163,7 +170,7 @@ __global__ __launch_bounds__(256) void k_topk_hist(StepArgs a) {
   const int b = blockIdx.y;
   const int ctx = a.sc.req[b].ctx;
   const int c0 = blockIdx.x * kSelChunk;
-  if (ctx <= a.K || c0 >= ctx) return;
+  if (ctx <= a.K || c0 >= ctx || guard_covers(a, b)) return;
   for (int i = threadIdx.x; i < kBins; i += 256) h[i] = 0;
   __syncthreads();
   const uint32_t kmin = a.sc.kmin[b];
@@ -185,7 +192,7 @@ __global__ __launch_bounds__(256) void k_topk_collect(StepArgs a) {
   const int b = blockIdx.y;
   const int ctx = a.sc.req[b].ctx;
   const int c0 = blockIdx.x * kSelChunk;
-  if (ctx <= a.K || c0 >= ctx) return;
+  if (ctx <= a.K || c0 >= ctx || guard_covers(a, b)) return;
   find_boundary(a.sc.thist + (int64_t)b * kBins, a.K, &s_bin, &s_below, sh);
   const uint32_t bstar = (uint32_t)s_bin;
   if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -201,8 +208,8 @@ __global__ __launch_bounds__(256) void k_topk_collect(StepArgs a) {
   for (int s0 = c0 + w * kWave; s0 < end; s0 += 256) {
     const int s = s0 + l;
     const bool valid = s < end;
-    const uint32_t okey = valid ? topk_key(sc[s]) - kmin : 0u;
-    const uint32_t bin = okey >> shift;
+    const uint32_t key = valid ? topk_key(sc[s]) : 0u;
+    const uint32_t bin = (key - kmin) >> shift;
     const bool take = valid && bin < bstar;
     const bool cand = valid && bin == bstar;
     const uint64_t m = __ballot(take);
@@ -214,7 +221,7 @@ __global__ __launch_bounds__(256) void k_topk_collect(StepArgs a) {
       basepos = __shfl(basepos, 0);
       if (cand) {
         const int pos = basepos + __popcll(cm & lanemask_lt());
-        a.sc.tcand_key[(int64_t)b * a.max_ctx + pos] = okey;
+        a.sc.tcand_key[(int64_t)b * a.max_ctx + pos] = key;
         a.sc.tcand_idx[(int64_t)b * a.max_ctx + pos] = s;
       }
     }
@@ -275,15 +282,49 @@ __global__ __launch_bounds__(kResolveThreads) void k_topk_resolve(StepArgs a) {
     }
     kth = ctx > 0 ? score_of_key(a.sc.kmax[b]) : __builtin_nanf("");
   } else {
-    const uint32_t kmin = a.sc.kmin[b];
-    const int need = K - a.sc.tbelow[b];
-    const int c = a.sc.tcand_n[b];
-    const uint32_t *ckey = a.sc.tcand_key + (int64_t)b * a.max_ctx;
-    const int32_t *cidx = a.sc.tcand_idx + (int64_t)b * a.max_ctx;
+    uint32_t *bits = a.sc.tbits + (int64_t)b * a.sc.bw;
+    const int nwords = (ctx + 31) / 32;
+    const uint32_t *ckey;
+    const int32_t *cidx;
+    int c, need;
+    if (guard_covers(a, b)) {  // candidates collected while scoring; nothing marked yet
+      // gather the work items' fixed slots into one list
+      const ReqInfo r = a.sc.req[b];
+      uint32_t *dkey = a.sc.tcand_key + (int64_t)b * a.max_ctx;
+      int32_t *didx = a.sc.tcand_idx + (int64_t)b * a.max_ctx;
+      const int per = (r.ntiles + kResolveThreads - 1) / kResolveThreads;
+      const int t0 = min(r.ntiles, tid * per), t1 = min(r.ntiles, t0 + per);
+      int mine = 0;
+      for (int ti = t0; ti < t1; ++ti) mine += a.sc.gcand_cnt[r.tile0 + ti];
+      int tot;
+      int p = block_excl_scan<kResolveThreads>(mine, sh, &tot);
+      for (int ti = t0; ti < t1; ++ti) {
+        const int tau = r.tile0 + ti;
+        const int n = a.sc.gcand_cnt[tau];
+        for (int j = 0; j < n; ++j, ++p) {
+          dkey[p] = a.sc.gcand_key[(int64_t)tau * kGuardSlots + j];
+          didx[p] = a.sc.gcand_idx[(int64_t)tau * kGuardSlots + j];
+        }
+      }
+      __threadfence();
+      __syncthreads();
+      ckey = dkey;
+      cidx = didx;
+      c = tot;
+      need = K;
+      for (int wi = tid; wi < nwords; wi += kResolveThreads) bits[wi] = 0u;
+      if (tid == 0) atomicAdd(&a.ws.counters[ECHO_CNT_SHORTCUT], 1);
+    } else {  // histogram path: lower bins already marked, boundary bin listed
+      ckey = a.sc.tcand_key + (int64_t)b * a.max_ctx;
+      cidx = a.sc.tcand_idx + (int64_t)b * a.max_ctx;
+      c = a.sc.tcand_n[b];
+      need = K - a.sc.tbelow[b];
+    }
     uint64_t P;
     int pos;
     block_select(ckey, cidx, c, need, &P, &pos);
-    uint32_t *bits = a.sc.tbits + (int64_t)b * a.sc.bw;
+    __threadfence();
+    __syncthreads();
     uint64_t kmax_sel = 0;
     for (int i = tid; i < c; i += kResolveThreads) {
       const uint32_t k = ckey[i];
@@ -294,11 +335,10 @@ __global__ __launch_bounds__(kResolveThreads) void k_topk_resolve(StepArgs a) {
       }
     }
     kmax_sel = block_max_u64<kResolveThreads>(kmax_sel, shu);
-    kth = score_of_key((uint32_t)kmax_sel + kmin);
+    kth = score_of_key((uint32_t)kmax_sel);
     __threadfence();
     __syncthreads();
     // ordered extraction of the selection bitmap
-    const int nwords = (ctx + 31) / 32;
     const int per = (nwords + kResolveThreads - 1) / kResolveThreads;
     const int w0 = tid * per, w1 = min(nwords, w0 + per);
     int cnt = 0;
@@ -330,6 +370,7 @@ __global__ __launch_bounds__(kResolveThreads) void k_topk_resolve(StepArgs a) {
                                               : __fadd_rn(__fmul_rn(a.alpha, kth),
                                                           __fmul_rn(keep, th));
     }
+    if (a.guard_upd) a.guard_upd[b] = ctx > K ? kth : __builtin_huge_valf();
   }
   if (PROTECT) {
     __syncthreads();

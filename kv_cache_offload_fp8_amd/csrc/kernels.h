@@ -23,11 +23,13 @@ struct StepArgs {
   const uint16_t *q;
   const float *w;
   float *theta;   // prefetch threshold state (read by the prologue)
+  float *guard;   // last k-th score per request (selection guard), or null
   int32_t *ctl;
   // scores read by the top-k passes
   const float *scores_in;
   int64_t score_stride;
   float *theta_upd;  // EMA state to update in the top-k epilogue, or null
+  float *guard_upd;  // selection guard to refresh in the top-k epilogue, or null
   int32_t mode;
   // workspace
   echo_ws_t ws;

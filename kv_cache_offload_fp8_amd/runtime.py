@@ -178,6 +178,7 @@ class Layer:
                              dtype=torch.bfloat16, device=device)
         self.w = torch.zeros((max(1, batch), dims.n_heads), dtype=torch.float32, device=device)
         self.theta = torch.empty(dims.max_batch, dtype=torch.float32, device=device)
+        self.guard = torch.empty(dims.max_batch, dtype=torch.float32, device=device)
         self.ctl = torch.zeros(abi.ECHO_CTL_WORDS, dtype=torch.int32, device=device)
         self.kidx = kidx
         self.host = host
@@ -185,7 +186,7 @@ class Layer:
                                      _ptr(self.idxbuf), _ptr(self.free))
         self.struct = abi.echo_layer_t(meta, _ptr(kidx), _ptr(self.gpu_kv), host.dev_ptr,
                                        _ptr(self.q), _ptr(self.w), _ptr(self.theta),
-                                       _ptr(self.ctl))
+                                       _ptr(self.guard), _ptr(self.ctl))
 
     def meta_bytes(self) -> int:
         return sum(t.numel() * t.element_size()
