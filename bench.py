@@ -104,13 +104,20 @@ def main():
     log(f"[bench] {npools} host pools of {wl.n_host * wl.latent * 2 / 1e9:.2f} GB ready "
         f"({time.time() - t0:.1f}s)")
     layers = []
+    rows = torch.empty((wl.n_host, wl.head_dim), dtype=torch.uint8, device=dev)
+    rows0 = None  # layer 0's row-major K, for the CPU baseline
     for l in range(L):
-        kidx = G.gen_kidx(wl, l, ctx, base, dev, args.seed)
+        rows.zero_()
+        G.gen_kidx(wl, l, ctx, base, dev, args.seed, out=rows)
+        if l == 0:
+            rows0 = rows.clone()
+        kidx = R.pack_kidx(dims, rows, torch.empty_like(rows))
         lay = R.Layer(dims, kidx, pools[l % npools], B, dev)
         lay.q.copy_(G.gen_q(wl, l, B, q_ring, dev, args.seed))
         lay.w.copy_(G.gen_w(wl, l, B, dev, args.seed))
         lay.init()
         layers.append(lay)
+    del rows
     batch = R.Batch(base, ctx, dev)
     ws = R.Workspace(dims, dev)
     ws.reset()
@@ -212,6 +219,23 @@ def main():
         f"recall {recall_ms.mean():.4f}; hit rate {hit:.4f}; misses/layer-step "
         f"{misses.mean():.0f}; prefetched/layer-step {prefetched.mean():.0f}")
 
+    # ------------------------------------- indexer with prefetch off (scoring only)
+    # Threshold +inf: the same kernel scores every token but prefetches nothing and
+    # changes no cache state, so this isolates the HBM-bound scoring stream.
+    nso = min(L, 16)
+    so = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nso)]
+    for j in range(nso):
+        so[j][0].record(s)
+        R.check(abi.echo_indexer_prefetch(dims, layers[j].struct, batch.struct, ws.ws,
+                                          abi.ECHO_THETA_POS_INF, sh), "indexer")
+        so[j][1].record(s)
+    torch.cuda.synchronize()
+    so_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in so[1:]] or
+                          [so[0][0].elapsed_time(so[0][1])]))
+    so_gbps = total_tok * BYTES_PER_SCORED_TOKEN / (so_ms * 1e-3) / 1e9
+    log(f"[bench] indexer, prefetch off: {so_ms:.4f} ms = {so_gbps:.0f} GB/s "
+        f"({so_gbps / HBM_PEAK_GBPS:.1%} of HBM peak)")
+
     # ------------------------------------------------------ host-link peaks
     n_rows = min(wl.n_host, 65536)
     big = pools[0]
@@ -246,7 +270,7 @@ def main():
     # ------------------------------------------------------- CPU baseline
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, ctx, base, layers[0], args, dims)
+        cpu = cpu_baseline(wl, ctx, base, layers[0], rows0, args, dims)
 
     out = {
         "metric": "decode layer-steps/s @100K ctx; indexer HBM GB/s % peak; recall host-link GB/s",
@@ -259,7 +283,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 x fp8->bf16 MFMA, fp32 accumulate; int32 management",
+        "dtype": "fp8 MFMA (bf16 q split into two e4m3 terms) with fp32 accumulate; int32 "
+                 "management",
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: batch {B}, ctx U[{wl.ctx_lo},{wl.ctx_hi}], "
                                f"{L} layers in one hipGraph per step, indexer {wl.heads}x"
@@ -271,6 +296,10 @@ def main():
                      "achieved": round(idx_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(idx_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                      "bytes_per_launch": idx_bytes, "avg_launch_ms": round(idx_ms, 5)},
+        "indexer_scoring_only": {"kernel": "echo_indexer_prefetch (k_begin + k_score), "
+                                           "threshold +inf", "avg_launch_ms": round(so_ms, 5),
+                                 "achieved": round(so_gbps, 1), "peak": HBM_PEAK_GBPS,
+                                 "unit": "GB/s", "frac": round(so_gbps / HBM_PEAK_GBPS, 4)},
         "indexer_hbm_gbps": round(idx_gbps, 1),
         "recall_host_link_gbps": round(recall_gbps, 2),
         "recall_frac_of_link_peak": round(recall_gbps / link_peak, 4),
@@ -290,7 +319,7 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(wl, ctx, base, lay0, args, dims):
+def cpu_baseline(wl, ctx, base, lay0, rows0, args, dims):
     """The oracle, as it stands, on a bounded sample of layer 0's first decode step:
     the first `--cpu-sample-requests` requests of the batch.  Scaled to layer-steps/s
     by the share of scored tokens the sample covers."""
@@ -303,14 +332,15 @@ def cpu_baseline(wl, ctx, base, lay0, args, dims):
     sctx = ctx[:nb].astype(np.int32)
     sbase = G.host_layout(sctx)
     n = int(sctx.sum())
-    kid = np.zeros((n, wl.head_dim), np.uint8)
-    kdev = lay0.kidx
+    n_rows = (int(sbase[-1]) + int(sctx[-1]) + 15) // 16 * 16
+    kid = np.zeros((n_rows, wl.head_dim), np.uint8)
+    kdev = rows0
     for b in range(nb):
         kid[sbase[b]:sbase[b] + sctx[b]] = kdev[int(base[b]):int(base[b]) + int(sctx[b])].cpu() \
             .numpy()
     q0 = lay0.q[0, :nb].contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
     w0 = lay0.w[:nb].cpu().numpy()
-    orc = O.OracleLayer(wl.heads, wl.head_dim, wl.top_k, wl.latent, n, wl.n_gpu, nb,
+    orc = O.OracleLayer(wl.heads, wl.head_dim, wl.top_k, wl.latent, n_rows, wl.n_gpu, nb,
                         wl.cap_div, wl.alpha, keep_pool=False)
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
     t0 = time.perf_counter()

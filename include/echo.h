@@ -29,7 +29,11 @@
  *    Read it after your own synchronization.
  *  - Token identities: request b of a batch owns host ids
  *    host_base[b] .. host_base[b] + ctx_len[b] - 1; ranges of different requests
- *    must not overlap (checked on the device).
+ *    must not overlap, and every host_base is a multiple of 16 (both checked on
+ *    the device: ECHO_EDEVARG).
+ *  - The indexer K cache is kept in the tiled layout that the gfx950 fp8 MFMA
+ *    consumes (see echo_kindex_pack): host ids are grouped by 16, and group g
+ *    holds bytes [16*g*D, 16*(g+1)*D), D = head_dim.
  */
 #ifndef ECHO_H
 #define ECHO_H
@@ -81,7 +85,8 @@ enum {
 };
 
 /* Shapes.  Supported by this build: 1 <= n_heads <= 64; head_dim in {32, 64, 96,
- * 128}; 1 <= top_k <= 4096; latent_dim*2 a multiple of 16 bytes; n_host < 2^31;
+ * 128}; 1 <= top_k <= 4096; latent_dim*2 a multiple of 16 bytes; n_host < 2^31
+ * and a multiple of 16;
  * 1 <= n_gpu < 2^31; 1 <= max_batch <= 64; 1 <= max_ctx < 2^31; prefetch_cap_div
  * >= 1; q_ring >= 1; 0 < ema_alpha <= 1. */
 typedef struct {
@@ -113,7 +118,8 @@ typedef struct {
 /* One layer's tensors. */
 typedef struct {
   echo_layer_meta_t meta;
-  const uint8_t *k_index;  /* [n_host][head_dim] indexer K, OCP fp8 E4M3FN, resident */
+  const uint8_t *k_index;  /* n_host*head_dim bytes: indexer K, OCP fp8 E4M3FN, in the
+                              tiled layout of echo_kindex_pack, resident in HBM     */
   uint16_t *gpu_kv;        /* [n_gpu][latent_dim] bf16 GPU pool                      */
   const uint16_t *host_kv; /* [n_host][latent_dim] bf16 host pool (mapped, pinned)   */
   const uint16_t *q;       /* [q_ring][batch][n_heads][head_dim] bf16 queries        */
@@ -178,6 +184,20 @@ int echo_meta_init(const echo_dims_t *dims, const echo_layer_t *layer, hipStream
 
 /* Clear the workspace (status, counters and internal scratch). */
 int echo_ws_reset(const echo_dims_t *dims, const echo_ws_t *ws, hipStream_t stream);
+
+/* Write indexer K rows into the tiled layout the scoring kernel reads.
+ * `rows` is [n_rows][D] row-major fp8 (device), `tiled` receives the same
+ * n_rows*D bytes (device, may not alias `rows`), n_rows a multiple of 16.
+ * Byte d of host id h goes to
+ *     16*D*(h/16) + 8*D*((d%32)/16) + 256*(d/32) + 16*(h%16) + d%16,
+ * so that for every 16-token group one 16-byte load per lane, 64 lanes wide,
+ * reads 1 KB (for D = 128) of contiguous memory holding exactly the MFMA
+ * operand bytes of those lanes: lane c*16 + r gets dims 32c + 16j .. +15 of
+ * token r in load j (j = 0, 1).  The layout is a permutation inside each group
+ * of 16 rows; the scores do not depend on it.  Returns ECHO_EINVAL for a bad
+ * argument (nothing enqueued). */
+int echo_kindex_pack(const echo_dims_t *dims, const uint8_t *rows, uint8_t *tiled,
+                     int64_t n_rows, hipStream_t stream);
 
 /* ------------------------------------------------------ the hot path */
 

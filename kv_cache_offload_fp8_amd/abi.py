@@ -21,8 +21,9 @@ ECHO_NCOUNTERS = 16
 ECHO_CTL_STEP, ECHO_CTL_NFREE, ECHO_CTL_WORDS = 0, 1, 4
 
 EXPORTS = ("echo_meta_bytes", "echo_ws_bytes", "echo_ws_bind", "echo_meta_init",
-           "echo_ws_reset", "echo_indexer_prefetch", "echo_topk", "echo_cache_alloc_evict",
-           "echo_recall", "echo_step_advance", "echo_layer_step", "echo_status_string")
+           "echo_ws_reset", "echo_kindex_pack", "echo_indexer_prefetch", "echo_topk",
+           "echo_cache_alloc_evict", "echo_recall", "echo_step_advance", "echo_layer_step",
+           "echo_status_string")
 
 P = C.c_void_p
 
@@ -73,6 +74,7 @@ def lib() -> C.CDLL:
             "echo_ws_bind": (C.c_int, [dp, P, C.c_size_t, wp]),
             "echo_meta_init": (C.c_int, [dp, lp, P]),
             "echo_ws_reset": (C.c_int, [dp, wp, P]),
+            "echo_kindex_pack": (C.c_int, [dp, P, P, C.c_int64, P]),
             "echo_indexer_prefetch": (C.c_int, [dp, lp, bp, wp, C.c_int, P]),
             "echo_topk": (C.c_int, [dp, P, C.c_int64, bp, wp, P, P]),
             "echo_cache_alloc_evict": (C.c_int, [dp, lp, bp, wp, P]),
@@ -111,6 +113,10 @@ def echo_meta_init(dims, layer, stream: int) -> int:
 
 def echo_ws_reset(dims, ws, stream: int) -> int:
     return lib().echo_ws_reset(C.byref(dims), _ref(ws), stream)
+
+
+def echo_kindex_pack(dims, rows: int, tiled: int, n_rows: int, stream: int) -> int:
+    return lib().echo_kindex_pack(C.byref(dims), rows, tiled, n_rows, stream)
 
 
 def echo_indexer_prefetch(dims, layer, batch, ws, theta_mode: int, stream: int) -> int:

@@ -7,6 +7,34 @@
 
 using namespace echo;
 
+namespace echo {
+
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n < 1)
+      n = 1;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+int score_grid(const echo_dims_t &d) {
+  const int64_t max_tiles =
+      (int64_t)d.max_batch * (((int64_t)d.max_ctx + kScoreTile - 1) / kScoreTile);
+  int64_t g = (max_tiles + kScoreWaves - 1) / kScoreWaves;
+  const int cus = device_cus();
+  if (g > cus) g = cus;
+  if (g < 1) g = 1;
+  return (int)g;
+}
+
+}  // namespace echo
+
 namespace {
 
 int check_dims(const echo_dims_t *d) {
@@ -18,9 +46,18 @@ int check_dims(const echo_dims_t *d) {
   if (!(d->ema_alpha > 0.0f && d->ema_alpha <= 1.0f)) return ECHO_EINVAL;
   if (d->n_host >= (1LL << 31) || d->max_ctx > (1 << 30) || d->n_gpu > (1 << 30))
     return ECHO_EINVAL;
+  if (d->n_host % 16 != 0) return ECHO_EINVAL;
   if (d->n_heads > kHeadsPad || d->head_dim > kDimPad || d->head_dim % 32 != 0 ||
       d->top_k > 4096 || d->max_batch > kMaxBatch || (d->latent_dim * 2) % 16 != 0)
     return ECHO_EUNSUPPORTED;
+  return ECHO_OK;
+}
+
+// The management kernel keeps all of its workgroups (one per 4096 slots) resident
+// for its grid barrier: at most one per compute unit.
+int check_launch(const echo_dims_t *d) {
+  const int64_t atiles = ((int64_t)d->n_gpu + kSlotTile - 1) / kSlotTile;
+  if (atiles > device_cus()) return ECHO_EUNSUPPORTED;
   return ECHO_OK;
 }
 
@@ -120,6 +157,7 @@ StepArgs make_args(const echo_dims_t &d, const echo_layer_t *l, const echo_batch
   a.theta_upd = nullptr;
   a.guard_upd = nullptr;
   a.mode = mode;
+  a.score_waves = score_grid(d) * kScoreWaves;
   a.ws = ws;
   scratch_layout(d, ws.internal, &a.sc);
   return a;
@@ -133,14 +171,6 @@ StepArgs make_args(const echo_dims_t &d, const echo_layer_t *l, const echo_batch
 int run_indexer(const StepArgs &a, int extra_roles, hipStream_t s) {
   LAUNCH(launch_begin(a, BEGIN_REQ | BEGIN_Q | BEGIN_CLR_INDEX | BEGIN_CLR_TOPK | extra_roles, s));
   LAUNCH(launch_score(a, s));
-  return ECHO_OK;
-}
-
-int run_manage(const StepArgs &a, hipStream_t s) {
-  LAUNCH(launch_evict_hist(a, s));
-  LAUNCH(launch_evict_collect(a, s));
-  LAUNCH(launch_evict_resolve(a, s));
-  LAUNCH(launch_alloc(a, s));
   return ECHO_OK;
 }
 
@@ -229,10 +259,7 @@ int echo_topk(const echo_dims_t *dims, const float *scores, int64_t score_stride
   a.score_stride = score_stride;
   a.theta_upd = theta;
   LAUNCH(launch_begin(a, BEGIN_REQ | BEGIN_CLR_TOPK, stream));
-  LAUNCH(launch_topk_minmax(a, stream));
-  LAUNCH(launch_topk_hist(a, stream));
-  LAUNCH(launch_topk_collect(a, stream));
-  LAUNCH(launch_topk_resolve(a, false, stream));
+  LAUNCH(launch_topk(a, false, stream));
   return ECHO_OK;
 }
 
@@ -241,10 +268,13 @@ int echo_cache_alloc_evict(const echo_dims_t *dims, const echo_layer_t *layer,
   int rc = check_dims(dims);
   if (rc != ECHO_OK) return rc;
   if (!layer_ok(layer, false) || !batch_ok(*dims, batch) || !ws_ok(ws)) return ECHO_EINVAL;
+  rc = check_launch(dims);
+  if (rc != ECHO_OK) return rc;
   const StepArgs a = make_args(*dims, layer, batch, *ws, ECHO_THETA_POS_INF);
   LAUNCH(launch_begin(a, BEGIN_REQ | BEGIN_CLR_MANAGE, stream));
   LAUNCH(launch_protect(a, stream));
-  return run_manage(a, stream);
+  LAUNCH(launch_manage(a, false, false, stream));
+  return ECHO_OK;
 }
 
 int echo_recall(const echo_dims_t *dims, const echo_layer_t *layer, const echo_ws_t *ws,
@@ -253,7 +283,7 @@ int echo_recall(const echo_dims_t *dims, const echo_layer_t *layer, const echo_w
   if (rc != ECHO_OK) return rc;
   if (!layer_ok(layer, false) || !ws_ok(ws)) return ECHO_EINVAL;
   const StepArgs a = make_args(*dims, layer, nullptr, *ws, ECHO_THETA_POS_INF);
-  LAUNCH(launch_recall(a, false, stream));
+  LAUNCH(launch_recall(a, stream));
   return ECHO_OK;
 }
 
@@ -274,19 +304,29 @@ int echo_layer_step(const echo_dims_t *dims, const echo_layer_t *layer, const ec
   if (theta_mode < ECHO_THETA_EMA || theta_mode > ECHO_THETA_POS_INF) return ECHO_EINVAL;
   if (!layer_ok(layer, theta_mode == ECHO_THETA_EMA) || !batch_ok(*dims, batch) || !ws_ok(ws))
     return ECHO_EINVAL;
+  rc = check_launch(dims);
+  if (rc != ECHO_OK) return rc;
   StepArgs a = make_args(*dims, layer, batch, *ws, theta_mode);
   a.theta_upd = theta_mode == ECHO_THETA_EMA ? layer->theta : nullptr;
   a.guard_upd = layer->guard;
   rc = run_indexer(a, BEGIN_CLR_MANAGE, stream);
   if (rc != ECHO_OK) return rc;
-  // the histogram passes only run for requests the selection guard did not cover
-  LAUNCH(launch_topk_minmax(a, stream));
-  LAUNCH(launch_topk_hist(a, stream));
-  LAUNCH(launch_topk_collect(a, stream));
-  LAUNCH(launch_topk_resolve(a, true, stream));
-  rc = run_manage(a, stream);
+  LAUNCH(launch_topk(a, true, stream));
+  LAUNCH(launch_manage(a, true, true, stream));
+  return ECHO_OK;
+}
+
+int echo_kindex_pack(const echo_dims_t *dims, const uint8_t *rows, uint8_t *tiled,
+                     int64_t n_rows, hipStream_t stream) {
+  int rc = check_dims(dims);
   if (rc != ECHO_OK) return rc;
-  LAUNCH(launch_recall(a, true, stream));
+  if (!rows || !tiled || n_rows < 0 || n_rows % 16 != 0) return ECHO_EINVAL;
+  const int64_t bytes = n_rows * dims->head_dim;
+  if ((const uint8_t *)tiled < rows + bytes && rows < (const uint8_t *)tiled + bytes &&
+      n_rows > 0)
+    return ECHO_EINVAL;
+  if (((uintptr_t)rows & 15) != 0 || ((uintptr_t)tiled & 15) != 0) return ECHO_EINVAL;
+  LAUNCH(launch_kindex_pack(rows, tiled, n_rows, dims->head_dim, stream));
   return ECHO_OK;
 }
 

@@ -26,10 +26,14 @@ constexpr long long kSpinLimit = 100000000LL;  // 1 s of the 100 MHz constant cl
 
 // internal counters (Scratch::misc)
 enum {
-  M_TICKET_SCORE = 0,
-  M_TICKET_ALLOC = 1,
-  M_TOTAL_TILES = 2,
-  M_RESERVE = 3,
+  M_SLOTS = 0,        // scoring jobs (sum over requests of their waves)
+  M_TOTAL_TILES = 2,  // scoring work items of the batch
+  M_RESERVE = 3,      // sum of the prefetch caps
+  M_BAR0 = 4,         // grid-barrier arrival counters of the management kernel
+  M_BAR1 = 5,
+  M_BAR2 = 6,
+  M_DONE = 7,         // management workgroups finished
+  M_BAR3 = 8,
   M_NMISC = 16
 };
 
@@ -39,7 +43,7 @@ constexpr uint64_t kFlagP = 2ull << 32;  // inclusive prefix
 
 struct ReqInfo {
   int32_t ctx;     // context length (0 if the request's arguments were rejected)
-  int32_t base;    // first host id
+  int32_t base;    // first host id (a multiple of 16)
   int32_t cap;     // prefetch cap min(k, ceil(ctx/div))
   int32_t off;     // sum of earlier caps: first free-list position of this request
   int32_t tile0;   // first scoring work item of this request
@@ -48,7 +52,9 @@ struct ReqInfo {
   float theta;     // prefetch threshold
   int32_t use_guard;   // collect selection candidates with key <= guard_key
   uint32_t guard_key;  // top-k key of (last k-th score - margin), saturated
-  int32_t pad[6];
+  int32_t wb;      // scoring waves given to this request
+  int32_t slot0;   // first scoring job of this request
+  int32_t pad[4];
 };
 
 // Carved internal scratch.  Every region starts 256-byte aligned.
@@ -58,27 +64,20 @@ struct Scratch {
   ReqInfo *req;           // [max_batch]
   int32_t *misc;          // [M_NMISC]
   uint64_t *tstate;       // [max_tiles] scoring look-back states
-  int32_t *rq_next;       // [max_batch] next scoring work item of each request
-  uint32_t *kmin, *kmax;  // [max_batch] key range per request
-  uint32_t *thist;        // [max_batch][kBins]
-  uint32_t *tcand_key;    // [max_batch][max_ctx]
+  uint32_t *tcand_key;    // [max_batch][max_ctx] boundary-bin candidates of the top-k
   int32_t *tcand_idx;     // [max_batch][max_ctx]
-  int32_t *tcand_n;       // [max_batch]
-  int32_t *tbelow;        // [max_batch]
-  int32_t *tbin;          // [max_batch]
   uint32_t *tbits;        // [max_batch][bw] selection bitmap
   uint32_t *gcand_key;    // [max_tiles][kGuardSlots] candidates above the selection guard
   int32_t *gcand_idx;     // [max_tiles][kGuardSlots]
   int32_t *gcand_cnt;     // [max_tiles] candidates found in each work item
-  int32_t *gcand_n;       // [max_batch] total per request (no-return atomics)
-  int32_t *gcand_ovf;     // [max_batch] nonzero if a work item overflowed its slots
   int32_t *miss_i;        // [max_batch][top_k] position of each miss in sel_tok
   uint32_t *ehist;        // [kBins]
   uint32_t *ecand_key;    // [n_gpu]
   int32_t *ecand_idx;     // [n_gpu]
-  int32_t *ecnt;          // [4]: candidates, below, boundary bin
+  int32_t *ecnt;          // [4]: candidates of the rare exact eviction path
+  uint64_t *estate;       // [alloc tiles] eviction-rank look-back states
   uint64_t *astate;       // [alloc tiles] free-list look-back states
-  int32_t max_tiles, bw, atiles, cap_g;
+  int32_t max_tiles, bw, atiles, pad_;
 };
 
 inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
@@ -102,32 +101,23 @@ inline int64_t scratch_layout(const echo_dims_t &d, uint8_t *base, Scratch *s) {
   t.req = (ReqInfo *)take(B * sizeof(ReqInfo));
   t.misc = (int32_t *)take(M_NMISC * 4);
   t.tstate = (uint64_t *)take((int64_t)max_tiles * 8);
-  t.rq_next = (int32_t *)take(B * 4);
-  t.kmin = (uint32_t *)take(B * 4);
-  t.kmax = (uint32_t *)take(B * 4);
-  t.thist = (uint32_t *)take(B * kBins * 4);
   t.tcand_key = (uint32_t *)take(B * C * 4);
   t.tcand_idx = (int32_t *)take(B * C * 4);
-  t.tcand_n = (int32_t *)take(B * 4);
-  t.tbelow = (int32_t *)take(B * 4);
-  t.tbin = (int32_t *)take(B * 4);
   t.tbits = (uint32_t *)take(B * bw * 4);
-  const int32_t cap_g = (int32_t)(C < 4 * K ? C : 4 * K);
   t.gcand_key = (uint32_t *)take((int64_t)max_tiles * kGuardSlots * 4);
   t.gcand_idx = (int32_t *)take((int64_t)max_tiles * kGuardSlots * 4);
   t.gcand_cnt = (int32_t *)take((int64_t)max_tiles * 4);
-  t.gcand_n = (int32_t *)take(B * 4);
-  t.gcand_ovf = (int32_t *)take(B * 4);
   t.miss_i = (int32_t *)take(B * K * 4);
   t.ehist = (uint32_t *)take(kBins * 4);
   t.ecand_key = (uint32_t *)take(G * 4);
   t.ecand_idx = (int32_t *)take(G * 4);
   t.ecnt = (int32_t *)take(16);
+  t.estate = (uint64_t *)take((int64_t)atiles * 8);
   t.astate = (uint64_t *)take((int64_t)atiles * 8);
   t.max_tiles = max_tiles;
   t.bw = bw;
   t.atiles = atiles;
-  t.cap_g = cap_g;
+  t.pad_ = 0;
   if (s) *s = t;
   return off;
 }
@@ -236,10 +226,11 @@ __device__ inline uint64_t block_max_u64(uint64_t v, uint64_t *sh) {
 // Called by one whole wave.  Work item `tau` of a segment that starts at item
 // `seg0` publishes its own count `c`, walks back over earlier items of the same
 // segment (aggregates until an inclusive prefix is found) and publishes its
-// inclusive prefix.  Returns the exclusive prefix of `tau`.  Items are handed
-// out by an atomic ticket, so every earlier item belongs to a running or
-// finished workgroup and the wait always ends; a 1 s guard turns a broken
-// invariant into ECHO_ETIMEOUT instead of a hang.
+// inclusive prefix.  Returns the exclusive prefix of `tau`.  Callers guarantee
+// that every earlier item is owned by a resident wave that reaches it without
+// waiting on a later item, so the wait always ends; a 1 s guard turns a broken
+// invariant into ECHO_ETIMEOUT instead of a hang.  Only the state words cross
+// workgroups, as relaxed device-scope atomics: no cache flush is needed.
 __device__ inline int lookback(uint64_t *st, int tau, int seg0, int c, int32_t *status) {
   const int l = lane_id();
   if (tau == seg0) {
@@ -263,8 +254,8 @@ __device__ inline int lookback(uint64_t *st, int tau, int seg0, int c, int32_t *
     while (!__all((v >> 32) != 0)) {
       if ((v >> 32) == 0)
         v = __hip_atomic_load(&st[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (__any((long long)(wall_clock64() - t0) > kSpinLimit)) {
-        timed_out = true;
+      if (__any((long long)(wall_clock64() - t0) > kSpinLimit) || failed(status)) {
+        timed_out = true;  // or another workgroup already failed: stop waiting
         break;
       }
     }
@@ -286,6 +277,38 @@ __device__ inline int lookback(uint64_t *st, int tau, int seg0, int c, int32_t *
     __hip_atomic_store(&st[tau], kFlagP | (uint32_t)(E + c), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
   return E;
+}
+
+// ------------------------------------------------------------ grid barrier
+// Barrier over the `nblocks` workgroups of a launch that are all resident
+// (grids no larger than one workgroup per compute unit).  `ctr` is zero at
+// launch and used once.  Returns false, in every workgroup, if the status is
+// set meanwhile or the wait exceeds 1 s (which then sets ECHO_ETIMEOUT).
+__device__ inline bool grid_sync(int32_t *ctr, int nblocks, int32_t *status) {
+  __shared__ int s_ok;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();
+    __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int ok = 1;
+    const uint64_t t0 = wall_clock64();
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nblocks) {
+      if (failed(status)) {
+        ok = 0;
+        break;
+      }
+      if ((long long)(wall_clock64() - t0) > kSpinLimit) {
+        fail(status, ECHO_ETIMEOUT);
+        ok = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    __threadfence();
+    s_ok = ok;
+  }
+  __syncthreads();
+  return s_ok != 0;
 }
 
 // ------------------------------------------------------------ key orders

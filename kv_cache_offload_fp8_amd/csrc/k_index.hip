@@ -1,4 +1,5 @@
-// Step prologue and the fused lightning-indexer + prefetch kernel.
+// Step prologue, the indexer-K layout kernel and the fused lightning-indexer +
+// prefetch kernel.
 //
 // Scoring follows DeepSeek Sparse Attention's lightning indexer, which the ECHO
 // review ("Problem and motivation") names as the component that rates every past
@@ -22,24 +23,33 @@
 // instruction sums neighbouring products in a window about 2^-15 of the largest
 // one before the fp32 accumulation (measured on this chip), which bounds the
 // score error by a small multiple of 2^-15 * sum_j |w_j| sum_d |q_jd k_d|.
-// Two MFMAs per 16 heads x 16 tokens (hi, lo) run as fast as the bf16 path's
-// four, and the fp8->bf16 widening they replace costs 8 cycles per pair of bytes.
-// Each wave owns 64 tokens at a time: it streams their K rows straight from HBM
-// into MFMA operand registers (no LDS staging: every K byte is used by exactly
-// one lane), applies ReLU and the head weights in registers, and reduces the 64
-// heads with two
-// cross-lane adds.  A workgroup holds seven scoring waves and one copy wave.
-// Each scoring wave is an independent worker: it takes 256-token work items from
-// an atomic ticket (the next ticket is fetched while the current item streams),
-// keeps the next 64 tokens' K loads in flight while it computes, ranks its
-// prefetch candidates in token order with a decoupled look-back over the work
-// items of the request, installs them in the maps and hands (host row, slot)
-// pairs to the copy wave through an LDS ring.  The copy wave reads those rows
-// from mapped host memory and writes them to the GPU pool, so the PCIe latency
-// never stalls the HBM stream -- the MI355X form of the pages' dedicated
-// prefetch role inside the indexer pipeline.  Scoring waves also collect the
-// tokens whose score clears a guard just below the previous step's k-th score;
-// when at least k of them do, the exact top-k needs only those candidates.
+//
+// K is stored in the MFMA operand order (echo_kindex_pack): for each group of 16
+// tokens, one 16-byte load per lane reads 1 KB of contiguous memory holding
+// exactly the operand bytes of the 64 lanes, so every load instruction covers
+// whole cache lines (the row-major order needs two instructions per line and
+// streams about 15% slower).  Each wave owns 64 tokens at a time: it loads their
+// K straight into MFMA operand registers (no LDS staging: every K byte is used by
+// exactly one lane), keeps the next 64 tokens' loads in flight while it computes,
+// applies ReLU and the head weights in registers and reduces the 64 heads with
+// two cross-lane adds.
+//
+// Work assignment.  A workgroup holds seven scoring waves and one copy wave.
+// Request b gets wb scoring waves (chosen so that no wave takes more 256-token
+// work items than any other); its k-th wave scores items k, k + wb, k + 2wb, ...
+// in order.  A wave therefore loads its request's query once, takes no ticket
+// and touches no shared counter, and the items of one request are scored in
+// step by neighbouring waves, so the decoupled look-back that ranks prefetch
+// candidates in token order finds its predecessors done or nearly done.  The
+// prefetch epilogue of an item (residency check, look-back, map installs) runs
+// one chunk into the next item, after that item's loads are issued, so its map
+// lookups never drain the K stream.  Rows to fetch go to the workgroup's copy
+// wave through an LDS ring; the copy wave reads them from mapped host memory and
+// writes the GPU pool while scoring continues -- the MI355X form of the pages'
+// dedicated prefetch role inside the indexer pipeline.  Scoring waves also keep
+// the tokens whose score clears a guard just below the previous step's k-th
+// score in fixed per-item slots; when at least k are found, the exact top-k needs
+// only those candidates.
 #include "kernels.h"
 
 namespace echo {
@@ -57,13 +67,13 @@ __device__ static void build_request_table(const StepArgs &a, int roles) {
   const bool in = l < a.B;
   int ctx = in ? a.ctx_len[l] : 0;
   int base = in ? a.host_base[l] : 0;
-  bool bad = in && (ctx < 0 || ctx > a.max_ctx || base < 0 ||
+  bool bad = in && (ctx < 0 || ctx > a.max_ctx || base < 0 || (base & 15) != 0 ||
                     (int64_t)base + (int64_t)ctx > a.n_host);
   // disjoint host ranges
-  for (int o = 0; o < kWave; ++o) {
+#pragma unroll 8
+  for (int o = 0; o < a.B; ++o) {
     int c2 = __shfl(ctx, o), b2 = __shfl(base, o);
-    if (in && o != l && o < a.B && ctx > 0 && c2 > 0 && base < b2 + c2 && b2 < base + ctx)
-      bad = true;
+    if (in && o != l && ctx > 0 && c2 > 0 && base < b2 + c2 && b2 < base + ctx) bad = true;
   }
   const bool any_bad = __any(bad);
   if (any_bad) {
@@ -94,6 +104,25 @@ __device__ static void build_request_table(const StepArgs &a, int roles) {
       use_guard = 1;
     }
   }
+  // Scoring jobs: the smallest R with sum_b ceil(n_b / R) <= W items per wave,
+  // then wb = ceil(n_b / R) waves for request b.  With at least as many active
+  // requests as waves, every request gets one wave and waves take several jobs.
+  const int W = a.score_waves;
+  const int N = wave_sum(ntiles);
+  const int nact = wave_sum(ntiles > 0 ? 1 : 0);
+  int nmax = ntiles;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) nmax = max(nmax, __shfl_xor(nmax, o));
+  int R = nmax > 0 ? nmax : 1;
+  if (N > 0 && nact < W) {
+    // sum_b ceil(n_b / R) <= N / R + nact, so R = ceil(N / (W - nact)) always fits;
+    // scan up from the lower bound ceil(N / W) (usually one or two candidates)
+    const int hi = min(nmax, (N + (W - nact) - 1) / (W - nact));
+    R = max(1, (N + W - 1) / W);
+    while (R < hi && wave_sum((ntiles + R - 1) / R) > W) ++R;
+  }
+  const int wb = ntiles > 0 ? (ntiles + R - 1) / R : 0;
+  const int slot_incl = wave_incl_scan(wb);
   if (in) {
     ReqInfo r;
     r.use_guard = use_guard;
@@ -106,13 +135,14 @@ __device__ static void build_request_table(const StepArgs &a, int roles) {
     r.ntiles = ntiles;
     r.active = active && ctx > 0;
     r.theta = th;
+    r.wb = wb;
+    r.slot0 = slot_incl - wb;
     a.sc.req[l] = r;
   }
   if (l == kWave - 1) {
     a.sc.misc[M_TOTAL_TILES] = tile_incl;
     a.sc.misc[M_RESERVE] = cap_incl;
-    a.sc.misc[M_TICKET_SCORE] = 0;
-    a.sc.misc[M_TICKET_ALLOC] = 0;
+    a.sc.misc[M_SLOTS] = slot_incl;
   }
 }
 
@@ -177,25 +207,19 @@ __global__ __launch_bounds__(256) void k_begin(StepArgs a, int roles) {
   int blk = blockIdx.x;
   if (blk == 0) {
     if (roles & BEGIN_REQ) build_request_table(a, roles);
-    // small per-request arrays
+    // small per-request arrays and counters
     const int tid = threadIdx.x;
     if ((roles & BEGIN_CLR_INDEX) && tid < a.max_batch) {
       a.ws.n_pf[tid] = 0;
       a.ws.n_cand[tid] = 0;
-      a.sc.rq_next[tid] = 0;
     }
     if ((roles & BEGIN_CLR_INDEX) && tid == 0) a.ws.counters[ECHO_CNT_PREFETCH] = 0;
     if ((roles & BEGIN_CLR_TOPK) && tid == 0) a.ws.counters[ECHO_CNT_SHORTCUT] = 0;
-    if ((roles & BEGIN_CLR_TOPK) && tid < a.max_batch) {
-      a.sc.kmin[tid] = 0xFFFFFFFFu;
-      a.sc.kmax[tid] = 0u;
-      a.sc.tcand_n[tid] = 0;
-      a.sc.gcand_n[tid] = 0;
-      a.sc.gcand_ovf[tid] = 0;
-    }
-    if ((roles & BEGIN_CLR_MANAGE) && tid < 16) {
+    if (roles & BEGIN_CLR_MANAGE) {
       if (tid < 4) a.sc.ecnt[tid] = 0;
-      if (tid != ECHO_CNT_PREFETCH && tid != ECHO_CNT_SHORTCUT) a.ws.counters[tid] = 0;
+      if (tid >= M_BAR0 && tid <= M_BAR3) a.sc.misc[tid] = 0;
+      if (tid < ECHO_NCOUNTERS && tid != ECHO_CNT_PREFETCH && tid != ECHO_CNT_SHORTCUT)
+        a.ws.counters[tid] = 0;
     }
     return;
   }
@@ -211,9 +235,9 @@ __global__ __launch_bounds__(256) void k_begin(StepArgs a, int roles) {
   const int64_t i0 = (int64_t)blk * blockDim.x + threadIdx.x;
   const int64_t step = (int64_t)kBeginClearBlocks * blockDim.x;
   if (roles & BEGIN_CLR_INDEX) fill_u32((uint32_t *)a.sc.tstate, 2LL * a.sc.max_tiles, 0u, i0, step);
-  if (roles & BEGIN_CLR_TOPK) fill_u32(a.sc.thist, (int64_t)a.B * kBins, 0u, i0, step);
   if (roles & BEGIN_CLR_MANAGE) {
     fill_u32(a.sc.ehist, kBins, 0u, i0, step);
+    fill_u32((uint32_t *)a.sc.estate, 2LL * a.sc.atiles, 0u, i0, step);
     fill_u32((uint32_t *)a.sc.astate, 2LL * a.sc.atiles, 0u, i0, step);
   }
 }
@@ -224,26 +248,63 @@ hipError_t launch_begin(const StepArgs &a, int roles, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ----------------------------------------------------------- indexer K layout
+
+// Row-major [n_rows][D] -> tiled, one thread per 16-byte piece: piece q of group
+// g is load j = q / (D/2) of lane l = q % (D/2) = 16c + r, i.e. dims
+// 32c + 16j .. +15 of row 16g + r.
+__global__ __launch_bounds__(256) void k_kindex_pack(const uint8_t *rows, uint8_t *tiled,
+                                                     int64_t n_rows, int D) {
+  const int64_t pieces = n_rows * D / 16;
+  const int half = D / 2;
+  for (int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x; p < pieces;
+       p += (int64_t)gridDim.x * 256) {
+    const int64_t g = p / D;
+    const int q = (int)(p - g * D);
+    const int j = q / half, l = q - j * half;
+    const int c = l >> 4, r = l & 15;
+    const uint4 v = *(const uint4 *)(rows + (g * 16 + r) * D + 32 * c + 16 * j);
+    *(uint4 *)(tiled + p * 16) = v;
+  }
+}
+
+hipError_t launch_kindex_pack(const uint8_t *rows, uint8_t *tiled, int64_t n_rows, int D,
+                              hipStream_t s) {
+  const int64_t pieces = n_rows * D / 16;
+  if (pieces == 0) return hipSuccess;
+  int64_t grid = (pieces + 255) / 256;
+  if (grid > 8192) grid = 8192;
+  hipLaunchKernelGGL(k_kindex_pack, dim3((unsigned)grid), dim3(256), 0, s, rows, tiled, n_rows,
+                     D);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ score
 
 constexpr int kChunks = kScoreTile / 64;  // 64-token chunks per work item
 
-// K rows of one 64-token chunk for this lane: 4 MFMA sub-tiles of 16 tokens,
-// 32 bytes each (dims chunk .. chunk+31 of token s0 + 16u + row).  The loads are
-// branch-free -- out-of-range tokens and dims read a clamped in-bounds address
-// and are zeroed by a select -- so the compiler can count them exactly and keep
-// the next chunk in flight (a branch around a load makes it wait for all).
-__device__ inline void load_k_chunk(const StepArgs &a, const ReqInfo &r, int s0, int row,
-                                    int chunk, v8i (&kb)[4]) {
-  const int cl = chunk < a.D ? chunk : a.D - 32;
+// K operands of one 64-token chunk for this lane (tokens s0 .. s0+63 of request
+// r, s0 a multiple of 64): sub-tile u holds tokens s0 + 16u .. +15; this lane
+// feeds token s0 + 16u + (lane & 15) with dims 32c .. 32c+31, c = lane >> 4, read
+// as two 16-byte pieces at 16*lane and 8*D + 16*lane inside the token's 16-row
+// group.  The loads are branch-free -- tokens past the context and dims past D
+// read an in-bounds address of the request's last group and are zeroed by a
+// select -- so the compiler counts them exactly and keeps the next chunk in
+// flight (a branch around a load makes it wait for all of them).
+__device__ inline void load_k_chunk(const StepArgs &a, const ReqInfo &r, int s0, int lane,
+                                    v8i (&kb)[4]) {
+  const bool dim_ok = 32 * (lane >> 4) < a.D;
+  const int lp = dim_ok ? lane : (lane & 15);
+  const int glast = (r.ctx - 1) & ~15;
+  const int half = 8 * a.D;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const int s = s0 + u * 16 + row;
-    const bool ok = s < r.ctx && chunk < a.D;
-    const int sc = s < r.ctx ? s : r.ctx - 1;
-    const v4i *p = (const v4i *)(a.kidx + ((int64_t)r.base + sc) * a.D + cl);
-    const v4i x0 = __builtin_nontemporal_load(p);
-    const v4i x1 = __builtin_nontemporal_load(p + 1);
+    const int st = s0 + 16 * u;
+    const bool ok = dim_ok && st + (lane & 15) < r.ctx;
+    const int sg = st < r.ctx ? st : glast;
+    const uint8_t *p = a.kidx + ((int64_t)r.base + sg) * a.D + lp * 16;
+    const v4i x0 = __builtin_nontemporal_load((const v4i *)p);
+    const v4i x1 = __builtin_nontemporal_load((const v4i *)(p + half));
     v8i x;
     x[0] = ok ? x0[0] : 0; x[1] = ok ? x0[1] : 0; x[2] = ok ? x0[2] : 0; x[3] = ok ? x0[3] : 0;
     x[4] = ok ? x1[0] : 0; x[5] = ok ? x1[1] : 0; x[6] = ok ? x1[2] : 0; x[7] = ok ? x1[3] : 0;
@@ -279,12 +340,16 @@ __device__ inline float score_chunk(const v8i (&kb)[4], const v8i (&qa)[HG][2],
 }
 
 // LDS ring between the scoring waves (producers) and the copy wave (consumer).
-// Entry p lives at p % kRing and is valid once seq == p + 1.
+// Entry p lives at p % kRing and is valid once seq == p + 1.  Once every scoring
+// wave is done, the copy wave publishes how far it got (fhead) and all eight waves
+// split the entries left in [fhead, tail), which are all published by then.
 struct Ring {
   int32_t h[kRing], g[kRing], seq[kRing];
-  int32_t tail;  // next position to reserve
-  int32_t head;  // next position the copy wave will take
-  int32_t done;  // scoring waves that have finished
+  int32_t tail;   // next position to reserve
+  int32_t head;   // next position the copy wave will take
+  int32_t done;   // scoring waves that have finished
+  int32_t split;  // 1 once fhead is valid
+  int32_t fhead;  // where the shared drain starts
 };
 
 __device__ inline int lds_load(const int32_t *p) {
@@ -294,99 +359,212 @@ __device__ inline void lds_store(int32_t *p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// The copy wave: host rows -> GPU pool slots, up to 8 rows (8 x 72 chunks of
-// 16 bytes, 9 per lane) in flight per round.
-__device__ static void copy_wave(const StepArgs &a, Ring &ring) {
+constexpr int kCopyBatch = 16;  // rows taken from the ring per round
+constexpr int kCopyLoads = 8;   // 16-byte loads in flight per lane per round (unrolled below)
+
+// Copy the n <= 64 rows whose host id / slot lanes 0..n-1 hold, 8 KB at a time:
+// eight 16-byte host reads per lane in flight, then the eight HBM writes.
+__device__ static void copy_batch(const StepArgs &a, int my_h, int my_g, int n) {
   const int lane = lane_id();
   const int cpr = a.latent * 2 / 16;
-  const uint4 *src = (const uint4 *)a.host_kv;
-  uint4 *dst = (uint4 *)a.gpu_kv;
+  const v4i *src = (const v4i *)a.host_kv;
+  v4i *dst = (v4i *)a.gpu_kv;
+  const int nchunks = n * cpr;
+  for (int c0 = 0; c0 < nchunks; c0 += kCopyLoads * kWave) {
+    v4i v0, v1, v2, v3, v4, v5, v6, v7;
+    int64_t d0, d1, d2, d3, d4, d5, d6, d7;
+    // chunk u of this lane: host offset (row h, piece c) -> pool offset (slot g, piece c)
+#define ECHO_COPY_LOAD(u, v, d)                                          \
+    {                                                                    \
+      const int ci = c0 + (u) * kWave + lane;                            \
+      const int cc = ci < nchunks ? ci : nchunks - 1;                    \
+      const int e = cc / cpr;                                            \
+      const int hh = __shfl(my_h, e), gg = __shfl(my_g, e);              \
+      d = ci < nchunks ? (int64_t)gg * cpr + (cc - e * cpr) : -1;        \
+      if (ci < nchunks) v = src[(int64_t)hh * cpr + (cc - e * cpr)];     \
+    }
+    ECHO_COPY_LOAD(0, v0, d0) ECHO_COPY_LOAD(1, v1, d1) ECHO_COPY_LOAD(2, v2, d2)
+    ECHO_COPY_LOAD(3, v3, d3) ECHO_COPY_LOAD(4, v4, d4) ECHO_COPY_LOAD(5, v5, d5)
+    ECHO_COPY_LOAD(6, v6, d6) ECHO_COPY_LOAD(7, v7, d7)
+#undef ECHO_COPY_LOAD
+    if (d0 >= 0) dst[d0] = v0;
+    if (d1 >= 0) dst[d1] = v1;
+    if (d2 >= 0) dst[d2] = v2;
+    if (d3 >= 0) dst[d3] = v3;
+    if (d4 >= 0) dst[d4] = v4;
+    if (d5 >= 0) dst[d5] = v5;
+    if (d6 >= 0) dst[d6] = v6;
+    if (d7 >= 0) dst[d7] = v7;
+  }
+}
+
+// Part `part` of 8 of the entries [fhead, tail) once the drain is split.
+__device__ static void copy_share(const StepArgs &a, Ring &ring, int part) {
+  const int lane = lane_id();
+  const uint64_t t0 = wall_clock64();
+  while (lds_load(&ring.split) == 0) {
+    __builtin_amdgcn_s_sleep(2);
+    if ((long long)(wall_clock64() - t0) > kSpinLimit) {
+      if (lane == 0) fail(a.ws.status, ECHO_ETIMEOUT);
+      return;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  const int f = lds_load(&ring.fhead), t = lds_load(&ring.tail);
+  const int p0 = f + (t - f) * part / (kScoreWaves + 1);
+  const int p1 = f + (t - f) * (part + 1) / (kScoreWaves + 1);
+  for (int p = p0; p < p1; p += kCopyBatch) {
+    const int n = min(kCopyBatch, p1 - p);
+    const int my_h = lane < n ? lds_load(&ring.h[(p + lane) % kRing]) : 0;
+    const int my_g = lane < n ? lds_load(&ring.g[(p + lane) % kRing]) : 0;
+    copy_batch(a, my_h, my_g, n);
+  }
+}
+
+// The copy wave: host rows -> GPU pool slots.  While scoring waves run it takes
+// the ready run of up to 16 entries at its head; when all are done it hands the
+// rest to the shared drain.
+__device__ static void copy_wave(const StepArgs &a, Ring &ring) {
+  const int lane = lane_id();
   int head = 0;
-  uint64_t t0 = wall_clock64();
   while (true) {
+    if (lds_load(&ring.done) == kScoreWaves) {  // every entry is published
+      if (lane == 0) {
+        lds_store(&ring.fhead, head);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        lds_store(&ring.split, 1);
+      }
+      break;
+    }
     const int pos = head + lane;
-    const bool ready = lane < 8 && lds_load(&ring.seq[pos % kRing]) == pos + 1;
+    const bool ready = lane < kCopyBatch && lds_load(&ring.seq[pos % kRing]) == pos + 1;
     const uint64_t rm = __ballot(ready);
     const int n = rm == 0 ? 0 : __ffsll((unsigned long long)~rm) - 1;  // leading ready run
     if (n == 0) {
-      if (lds_load(&ring.done) == kScoreWaves && head == lds_load(&ring.tail)) break;
+      // producers bound their own waits and always end by counting themselves done
       __builtin_amdgcn_s_sleep(2);
-      if ((long long)(wall_clock64() - t0) > kSpinLimit) {
-        if (lane == 0) fail(a.ws.status, ECHO_ETIMEOUT);
-        break;
-      }
       continue;
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     const int my_h = lane < n ? lds_load(&ring.h[pos % kRing]) : 0;
     const int my_g = lane < n ? lds_load(&ring.g[pos % kRing]) : 0;
-    const int nchunks = n * cpr;
-    for (int c0 = lane; c0 < nchunks; c0 += 3 * 64) {  // three 16-byte loads in flight
-      const int ca = c0, cb = min(c0 + 64, nchunks - 1), cc = min(c0 + 128, nchunks - 1);
-      const int ea = ca / cpr, eb = cb / cpr, ec = cc / cpr;
-      const int ha = __shfl(my_h, ea), hb = __shfl(my_h, eb), hc = __shfl(my_h, ec);
-      const int ga = __shfl(my_g, ea), gb = __shfl(my_g, eb), gc = __shfl(my_g, ec);
-      const uint4 va = src[(int64_t)ha * cpr + (ca - ea * cpr)];
-      const uint4 vb = src[(int64_t)hb * cpr + (cb - eb * cpr)];
-      const uint4 vc = src[(int64_t)hc * cpr + (cc - ec * cpr)];
-      dst[(int64_t)ga * cpr + (ca - ea * cpr)] = va;
-      if (c0 + 64 < nchunks) dst[(int64_t)gb * cpr + (cb - eb * cpr)] = vb;
-      if (c0 + 128 < nchunks) dst[(int64_t)gc * cpr + (cc - ec * cpr)] = vc;
-    }
+    copy_batch(a, my_h, my_g, n);
     head += n;
     if (lane == 0) lds_store(&ring.head, head);
-    t0 = wall_clock64();
   }
+  copy_share(a, ring, kScoreWaves);
 }
 
-// Work items: 256-token tiles of one request, handed out in token order by a
-// per-request counter.  A wave starts on its "home" request and stays there, so
-// it loads that request's query once; when the request runs dry it moves to the
-// request with the most tiles left.  Returns (request, tile) or request -1.
-struct Tile {
-  int b, i;
-};
-
-__device__ inline Tile take_tile(const StepArgs &a, const ReqInfo *s_req, int b) {
+// Prefetch epilogue of work item pi of request r: candidates are the tokens above
+// the threshold (`above`) whose map entry (`gq`, read while scoring) is -1.
+// Their rank in token order comes from the look-back over the request's items;
+// ranks below the cap take free-list entries idxbuf[off + rank] (while the list
+// lasts), are installed in the maps with priority t, and go to the copy wave.
+// The request's last item publishes n_cand and n_pf.
+__device__ static void prefetch_epilogue(const StepArgs &a, const ReqInfo &r, int b, int pi,
+                                         const uint64_t (&above)[kChunks],
+                                         const int (&gq)[kChunks], Ring &ring, int t,
+                                         int nfree) {
   const int lane = lane_id();
-  while (true) {
-    if (b >= 0) {
-      int i = 0;
-      if (lane == 0) i = atomicAdd(&a.sc.rq_next[b], 1);
-      i = __builtin_amdgcn_readfirstlane(i);
-      if (i < s_req[b].ntiles) return Tile{b, i};
-    }
-    // this request is done: find the one with the most tiles left
-    int left = 0;
-    if (lane < a.B)
-      left = s_req[lane].ntiles -
-             __hip_atomic_load(&a.sc.rq_next[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    int best = left > 0 ? (left << 6) | lane : -1;
+  const int tau = r.tile0 + pi;
+  const int s_wave = pi * kScoreTile;
+  uint64_t cand[kChunks];
+  int c_all = 0;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) best = max(best, __shfl_xor(best, o));
-    best = __builtin_amdgcn_readfirstlane(best);
-    if (best < 0) return Tile{-1, 0};
-    b = best & 63;
+  for (int c = 0; c < kChunks; ++c) {
+    cand[c] = __ballot(((above[c] >> lane) & 1ull) && gq[c] == -1);
+    c_all += __popcll(cand[c]);
+  }
+  const int E = lookback(a.sc.tstate, tau, r.tile0, c_all, a.ws.status);
+  const int lim = nfree < a.n_gpu ? nfree : a.n_gpu;
+  int rank0 = E;
+  uint64_t emit[kChunks];
+  int slot[kChunks];
+  int ne = 0;
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const uint64_t m = cand[c];
+    slot[c] = -1;
+    if ((m >> lane) & 1ull) {
+      const int rank = rank0 + __popcll(m & lanemask_lt());
+      if (rank < r.cap) {
+        const int j = r.off + rank;
+        const int g = j < lim ? a.idxbuf[j] : -1;
+        if (g >= 0 && g < a.n_gpu) {
+          const int s = s_wave + c * 64 + lane;
+          const int64_t h = (int64_t)r.base + s;
+          a.h2g[h] = g;
+          a.g2h[g] = (int32_t)h;
+          a.freef[g] = 0;
+          a.prio[g] = t;
+          a.ws.pf_tok[(int64_t)b * a.K + rank] = s;
+          a.ws.pf_slot[(int64_t)b * a.K + rank] = g;
+          slot[c] = g;
+        }
+      }
+    }
+    emit[c] = __ballot(slot[c] >= 0);
+    ne += __popcll(emit[c]);
+    rank0 += __popcll(m);
+  }
+  if (ne) {  // hand the rows to the copy wave
+    int pos = 0;
+    if (lane == 0) pos = atomicAdd(&ring.tail, ne);
+    pos = __shfl(pos, 0);
+    const uint64_t tw = wall_clock64();
+    while (pos + ne - lds_load(&ring.head) > kRing) {  // wait for room
+      __builtin_amdgcn_s_sleep(1);
+      if (__any((long long)(wall_clock64() - tw) > kSpinLimit)) {
+        if (lane == 0) fail(a.ws.status, ECHO_ETIMEOUT);
+        break;
+      }
+    }
+    int p = pos;
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      if (slot[c] >= 0) {
+        const int q = (p + __popcll(emit[c] & lanemask_lt())) % kRing;
+        ring.h[q] = (int32_t)((int64_t)r.base + s_wave + c * 64 + lane);
+        ring.g[q] = slot[c];
+      }
+      p += __popcll(emit[c]);
+    }
+    __threadfence_block();
+    p = pos;
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      if (slot[c] >= 0) {
+        const int q = p + __popcll(emit[c] & lanemask_lt());
+        lds_store(&ring.seq[q % kRing], q + 1);
+      }
+      p += __popcll(emit[c]);
+    }
+  }
+  if (pi == r.ntiles - 1 && lane == 0) {
+    const int total = E + c_all;
+    const int take = min(r.cap, total);
+    const int npf = max(0, min(take, lim - r.off));
+    a.ws.n_cand[b] = total;
+    a.ws.n_pf[b] = npf;
+    if (npf) atomicAdd(&a.ws.counters[ECHO_CNT_PREFETCH], npf);
   }
 }
 
-template <int HG>
-__device__ static void score_wave(const StepArgs &a, const ReqInfo *s_req, Ring &ring,
-                                  int wave) {
-  int32_t *status = a.ws.status;
+// One scoring job: work items k, k + wb, ... of request b.  PF: prefetch is on
+// for this request (the residency of every token above the threshold is read
+// while scoring; the epilogue of item i runs one chunk into item i + wb).
+template <int HG, bool PF>
+__device__ static void score_job(const StepArgs &a, const ReqInfo &r, int b, int k, Ring &ring,
+                                 int t, int nfree) {
   const int lane = lane_id();
   // Operand layout: lane l feeds row (l & 15) of A (a head) and column (l & 15)
   // of B (a token) with the 32 bytes at dims chunk .. chunk+31,
   // chunk = 32*(l >> 4).  A and B use the same dims for the same lane, so the
   // MFMA sums q . k over all 128 dims whatever order it adds them in.
   const int row = lane & 15, chunk = (lane >> 4) * 32;
-  const int t = a.ctl[ECHO_CTL_STEP];
-  const int nfree = a.ctl[ECHO_CTL_NFREE];
-  if (a.B == 0) return;
-
   v8i qa[HG][2];
   float wr[HG][4];
-  auto load_query = [&](int b) {
+  {
     const uint8_t *qh = a.sc.qhi + (int64_t)b * kHeadsPad * kDimPad;
     const uint8_t *ql = a.sc.qlo + (int64_t)b * kHeadsPad * kDimPad;
 #pragma unroll
@@ -397,52 +575,52 @@ __device__ static void score_wave(const StepArgs &a, const ReqInfo *s_req, Ring 
       for (int rr = 0; rr < 4; ++rr)
         wr[hg][rr] = a.sc.wsc[(int64_t)b * kHeadsPad + hg * 16 + (lane >> 4) * 4 + rr];
     }
-  };
-
-  Tile cur = take_tile(a, s_req, wave % a.B);
-  if (cur.b < 0) return;
-  load_query(cur.b);
-  // Two K buffers: chunk c of a tile lives in kb[c & 1]; the next chunk (the
-  // next tile's first one at the end of a tile) is in flight while c computes.
-  // Everything read between two chunks -- the tile claim, the request record --
-  // is either a scalar load or issued before the stream loads, because vector
-  // loads retire in order and waiting for a late one would drain the stream.
+  }
+  float *out = a.ws.scores + (int64_t)b * a.max_ctx;
+  // Two K buffers: chunk c of an item lives in kb[c & 1]; the next chunk (the
+  // next item's first one at the end of an item) is in flight while c computes.
   v8i kb[2][4];
-  load_k_chunk(a, s_req[cur.b], cur.i * kScoreTile, row, chunk, kb[0]);
-
+  int i = k;
+  load_k_chunk(a, r, i * kScoreTile, lane, kb[0]);
+  bool have_prev = false;
+  int p_i = 0;
+  uint64_t p_above[kChunks];
+  int p_g[kChunks];
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    p_above[c] = 0;
+    p_g[c] = 0;
+  }
   while (true) {
-    const int b = __builtin_amdgcn_readfirstlane(cur.b);
-    const ReqInfo r = s_req[b];  // LDS: does not queue behind the K stream
-    const int tau = r.tile0 + cur.i;
-    const int s_wave = cur.i * kScoreTile;
-    int raw = 0;
-    if (lane == 0) raw = atomicAdd(&a.sc.rq_next[b], 1);  // claim the next tile
-    Tile nxt{-1, 0};
-    float *out = a.ws.scores + (int64_t)b * a.max_ctx;
+    const int ni = i + r.wb;
+    const bool has_next = ni < r.ntiles;
+    const int s_wave = i * kScoreTile;
+    const int tau = r.tile0 + i;
     uint64_t above[kChunks], gsel[kChunks];
     uint32_t keys[kChunks];
+    int gq[kChunks];
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
-      if (c + 1 < kChunks) {
-        load_k_chunk(a, r, s_wave + (c + 1) * 64, row, chunk, kb[(c + 1) & 1]);
-      } else {
-        const int ni = __builtin_amdgcn_readfirstlane(raw);
-        nxt = ni < r.ntiles ? Tile{b, ni} : take_tile(a, s_req, -1);
-        if (nxt.b >= 0) {
-          const ReqInfo rn = s_req[nxt.b];
-          load_k_chunk(a, rn, nxt.i * kScoreTile, row, chunk, kb[(c + 1) & 1]);
-        }
-      }
+      if (c + 1 < kChunks)
+        load_k_chunk(a, r, s_wave + (c + 1) * 64, lane, kb[(c + 1) & 1]);
+      else if (has_next)
+        load_k_chunk(a, r, ni * kScoreTile, lane, kb[0]);
       const float score = score_chunk<HG>(kb[c & 1], qa, wr, lane);
       const int s = s_wave + c * 64 + lane;
       const bool valid = s < r.ctx;
       if (valid) out[s] = score;
       keys[c] = topk_key(score);
-      above[c] = __ballot(r.active && valid && score > r.theta);
       gsel[c] = __ballot(r.use_guard && valid && keys[c] <= r.guard_key);
+      above[c] = 0;
+      gq[c] = 0;
+      if (PF) {
+        above[c] = __ballot(valid && score > r.theta);
+        gq[c] = a.h2g[(int64_t)r.base + (valid ? s : r.ctx - 1)];
+        if (c == 0 && have_prev) prefetch_epilogue(a, r, b, p_i, p_above, p_g, ring, t, nfree);
+      }
     }
 
-    // ---- top-k candidates above the selection guard: fixed slots of this tile
+    // ---- top-k candidates above the selection guard: fixed slots of this item
     if (r.use_guard) {
       int ng = 0;
 #pragma unroll
@@ -456,99 +634,43 @@ __device__ static void score_wave(const StepArgs &a, const ReqInfo *s_req, Ring 
         }
         ng += __popcll(gsel[c]);
       }
-      if (lane == 0) {
-        a.sc.gcand_cnt[tau] = ng;
-        if (ng) atomicAdd(&a.sc.gcand_n[b], ng);  // result unused: no wait
-        if (ng > kGuardSlots) atomicOr(&a.sc.gcand_ovf[b], 1);
-      }
+      if (lane == 0) a.sc.gcand_cnt[tau] = ng;
     }
+    if (PF) {
+      p_i = i;
+#pragma unroll
+      for (int c = 0; c < kChunks; ++c) {
+        p_above[c] = above[c];
+        p_g[c] = gq[c];
+      }
+      have_prev = true;
+    }
+    if (!has_next) break;
+    i = ni;
+  }
+  if (PF && have_prev) prefetch_epilogue(a, r, b, p_i, p_above, p_g, ring, t, nfree);
+}
 
-    // ---- prefetch: above the threshold and not resident, first cap in token order
-    if (r.active) {
-      int g_of[kChunks];
-#pragma unroll
-      for (int c = 0; c < kChunks; ++c) {  // one batch of map lookups per work item
-        g_of[c] = 0;
-        if ((above[c] >> lane) & 1ull) g_of[c] = a.h2g[(int64_t)r.base + s_wave + c * 64 + lane];
-      }
-      uint64_t cand[kChunks];
-      int c_all = 0;
-#pragma unroll
-      for (int c = 0; c < kChunks; ++c) {
-        cand[c] = __ballot(((above[c] >> lane) & 1ull) && g_of[c] == -1);
-        c_all += __popcll(cand[c]);
-      }
-      int base = lookback(a.sc.tstate, tau, r.tile0, c_all, status);
-      uint64_t emit[kChunks];
-      int slot[kChunks];
-      int ne = 0;
-#pragma unroll
-      for (int c = 0; c < kChunks; ++c) {
-        const uint64_t m = cand[c];
-        slot[c] = -1;
-        if ((m >> lane) & 1ull) {
-          const int rank = base + __popcll(m & lanemask_lt());
-          if (rank < r.cap) {
-            const int j = r.off + rank;
-            const int g = (j < nfree && j < a.n_gpu) ? a.idxbuf[j] : -1;
-            if (g >= 0 && g < a.n_gpu) {
-              const int s = s_wave + c * 64 + lane;
-              const int64_t h = (int64_t)r.base + s;
-              a.h2g[h] = g;
-              a.g2h[g] = (int32_t)h;
-              a.freef[g] = 0;
-              a.prio[g] = t;
-              a.ws.pf_tok[(int64_t)b * a.K + rank] = s;
-              a.ws.pf_slot[(int64_t)b * a.K + rank] = g;
-              slot[c] = g;
-            }
-          }
-        }
-        emit[c] = __ballot(slot[c] >= 0);
-        ne += __popcll(emit[c]);
-        base += __popcll(m);
-      }
-      if (ne) {  // hand the rows to the copy wave
-        int pos = 0;
-        if (lane == 0) pos = atomicAdd(&ring.tail, ne);
-        pos = __shfl(pos, 0);
-        const uint64_t tw = wall_clock64();
-        while (pos + ne - lds_load(&ring.head) > kRing) {  // wait for room
-          __builtin_amdgcn_s_sleep(1);
-          if (__any((long long)(wall_clock64() - tw) > kSpinLimit)) {
-            if (lane == 0) fail(status, ECHO_ETIMEOUT);
-            break;
-          }
-        }
-#pragma unroll
-        for (int c = 0; c < kChunks; ++c) {
-          if (slot[c] >= 0) {
-            const int p = (pos + __popcll(emit[c] & lanemask_lt())) % kRing;
-            ring.h[p] = (int32_t)((int64_t)r.base + s_wave + c * 64 + lane);
-            ring.g[p] = slot[c];
-          }
-          pos += __popcll(emit[c]);
-        }
-        __threadfence_block();
-        pos -= ne;
-#pragma unroll
-        for (int c = 0; c < kChunks; ++c) {
-          if (slot[c] >= 0) {
-            const int p = pos + __popcll(emit[c] & lanemask_lt());
-            lds_store(&ring.seq[p % kRing], p + 1);
-          }
-          pos += __popcll(emit[c]);
-        }
-        if (lane == 0) {
-          atomicAdd(&a.ws.n_pf[b], ne);
-          atomicAdd(&a.ws.counters[ECHO_CNT_PREFETCH], ne);
-        }
-      }
-      if (lane == 0 && c_all > 0) atomicAdd(&a.ws.n_cand[b], c_all);
-    }
-    if (nxt.b < 0) break;
-    if (nxt.b != b) load_query(nxt.b);
-    cur = nxt;
+// A scoring wave takes jobs w, w + W, ... (W = waves of the launch); job slots
+// are numbered request by request, so a wave meets its requests in increasing
+// order and every look-back wait is on an item that a resident wave reaches
+// without waiting on a later one.
+template <int HG>
+__device__ static void score_wave(const StepArgs &a, const ReqInfo *s_req, Ring &ring, int w) {
+  const int lane = lane_id();
+  const int S = a.sc.misc[M_SLOTS];
+  const int W = a.score_waves;
+  const int t = a.ctl[ECHO_CTL_STEP];
+  const int nfree = a.ctl[ECHO_CTL_NFREE];
+  const int send = lane < a.B ? s_req[lane].slot0 + s_req[lane].wb : 0;
+  for (int slot = w; slot < S; slot += W) {
+    const int b = __popcll(__ballot(lane < a.B && send <= slot));
+    const ReqInfo r = s_req[b];
+    const int k = slot - r.slot0;
+    if (r.active)
+      score_job<HG, true>(a, r, b, k, ring, t, nfree);
+    else
+      score_job<HG, false>(a, r, b, k, ring, t, nfree);
   }
 }
 
@@ -564,6 +686,8 @@ __global__ __launch_bounds__(512) void k_score(StepArgs a) {
     ring.tail = 0;
     ring.head = 0;
     ring.done = 0;
+    ring.split = 0;
+    ring.fhead = 0;
   }
   __syncthreads();
   const int wid = tid / kWave;
@@ -574,14 +698,12 @@ __global__ __launch_bounds__(512) void k_score(StepArgs a) {
   score_wave<HG>(a, s_req, ring, blockIdx.x * kScoreWaves + wid);
   __threadfence_block();
   if (lane_id() == 0) atomicAdd(&ring.done, 1);
+  copy_share(a, ring, wid);
 }
 
 hipError_t launch_score(const StepArgs &a, hipStream_t s) {
   const int hg = (a.H + 15) / 16;
-  // persistent grid: one workgroup (7 scoring waves + 1 copy wave) per CU
-  const int waves_needed = (a.sc.max_tiles + kScoreWaves - 1) / kScoreWaves;
-  int grid = waves_needed < 256 ? waves_needed : 256;
-  if (grid < 1) grid = 1;
+  const int grid = a.score_waves / kScoreWaves;
   switch (hg) {
     case 1: hipLaunchKernelGGL(k_score<1>, dim3(grid), dim3(512), 0, s, a); break;
     case 2: hipLaunchKernelGGL(k_score<2>, dim3(grid), dim3(512), 0, s, a); break;

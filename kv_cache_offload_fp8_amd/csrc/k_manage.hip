@@ -1,101 +1,297 @@
-// Allocation, recall, step advance and initialisation.
+// Eviction, allocation and recall in one kernel; standalone recall, step
+// advance and initialisation.
 //
-// Allocation (ECHO review, "Core method / in-graph per-layer cache
-// management": free slots are found by a parallel scan, and a counter hands
-// them out): one pass over the free bitmap in 4096-slot work items, ranked with
-// a decoupled look-back, so miss i (in request, token order) receives the i-th
-// free slot in ascending order and the leftover free slots are written back in
-// ascending order to the index buffer for the next step's prefetch.  Recall
-// (same section: a GPU kernel reads host memory directly) copies every missed
-// row from mapped pinned host memory into the GPU pool.
-#include "kernels.h"
+// Eviction (ECHO review, "Core method / in-graph per-layer cache management":
+// low-priority entries are evicted after the selected tokens are protected)
+// takes the n_evict occupied slots with the lowest (priority, slot) among those
+// with priority < t.  Allocation (same section: free slots are found by a
+// parallel scan and a counter hands them out) gives miss i the i-th free slot in
+// ascending order and writes the remaining free slots, ascending, to the index
+// buffer for the next step's prefetch.  Recall (same section: a GPU kernel reads
+// host memory directly) copies every missed row from mapped pinned host memory
+// into the GPU pool.
+//
+// MI355X mapping.  One 1024-thread workgroup per 4096 slots (4 contiguous slots
+// per thread), all resident at once.  Each workgroup histograms the age bin
+// (priority - t + 4096, clamped at 0) of its evictable slots in LDS and merges it
+// into a global histogram; after one grid barrier every workgroup finds the
+// boundary bin itself.  Bins 1..4095 hold one priority each, so the boundary
+// bin's slots are ranked by slot id alone with a decoupled look-back over the
+// workgroups; only a boundary in the clamped bin 0 (slots idle for 4096 steps or
+// more) needs the exact (priority, slot) select, done by one workgroup between
+// two more barriers.  A second look-back over the workgroups ranks the free
+// slots for the allocation, and each workgroup copies the rows it allocated.
+#include "select.h"
 
 namespace echo {
 
-__global__ __launch_bounds__(256) void k_alloc(StepArgs a) {
-  __shared__ int s_tau, s_E;
-  __shared__ int s_wcnt[4];
-  __shared__ int s_moff[kMaxBatch + 1];
-  if (failed(a.ws.status)) return;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  if (tid == 0) s_tau = atomicAdd(&a.sc.misc[M_TICKET_ALLOC], 1);
-  if (wid == 0) {  // exclusive prefix of the per-request miss counts
-    const int v = lane < a.B ? a.ws.n_miss[lane] : 0;
-    const int incl = wave_incl_scan(v);
-    if (lane < a.B) s_moff[lane] = incl - v;
-    if (lane == kWave - 1) s_moff[a.B] = incl;
-  }
-  __syncthreads();
-  const int tau = s_tau;
-  if (tau >= a.sc.atiles) return;
-  const int nmiss = s_moff[a.B];
-  const int t = a.ctl[ECHO_CTL_STEP];
-  const int g0 = tau * kSlotTile + wid * (kSlotTile / 4);
+__device__ static inline int evict_bin(int prio, int t) {
+  const int64_t v = (int64_t)prio - (int64_t)t + kBins;
+  return v < 0 ? 0 : (v > kBins - 1 ? kBins - 1 : (int)v);
+}
 
-  uint64_t masks[16];
-  int wc = 0;
-#pragma unroll
-  for (int it = 0; it < 16; ++it) {
-    const int g = g0 + it * kWave + lane;
-    const bool fr = g < a.n_gpu && a.freef[g] != 0;
-    masks[it] = __ballot(fr);
-    wc += __popcll(masks[it]);
-  }
-  if (lane == 0) s_wcnt[wid] = wc;
-  __syncthreads();
-  const int c = s_wcnt[0] + s_wcnt[1] + s_wcnt[2] + s_wcnt[3];
-  int base = 0;
-  for (int i = 0; i < wid; ++i) base += s_wcnt[i];
-  if (wid == 0) {
-    const int E = lookback(a.sc.astate, tau, 0, c, a.ws.status);
-    if (lane == 0) s_E = E;
-  }
-  __syncthreads();
-  base += s_E;
-#pragma unroll
-  for (int it = 0; it < 16; ++it) {
-    const uint64_t m = masks[it];
-    if ((m >> lane) & 1ull) {
-      const int g = g0 + it * kWave + lane;
-      const int rank = base + __popcll(m & lanemask_lt());
-      if (rank < nmiss) {
-        int b = 0;
-        for (int i = 1; i < a.B; ++i)
-          if (s_moff[i] <= rank) b = i;
-        const int j = rank - s_moff[b];
-        const int s = a.ws.miss_tok[(int64_t)b * a.K + j];
-        const int i = a.sc.miss_i[(int64_t)b * a.K + j];
-        const int64_t h = (int64_t)a.sc.req[b].base + s;
-        a.h2g[h] = g;
-        a.g2h[g] = (int32_t)h;
-        a.freef[g] = 0;
-        a.prio[g] = t;
-        a.ws.sel_slot[(int64_t)b * a.K + i] = g;
-        a.ws.recall_h[rank] = (int32_t)h;
-        a.ws.recall_g[rank] = g;
-      } else {
-        a.idxbuf[rank - nmiss] = g;
-      }
+__device__ static inline void evict_slot(const StepArgs &a, int g) {
+  const int h = a.g2h[g];
+  if (h >= 0 && (int64_t)h < a.n_host) a.h2g[h] = -1;
+  a.g2h[g] = -1;
+  a.freef[g] = 1;
+  a.prio[g] = -1;
+}
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// Copy `n` rows (host ids hs[i] -> slots gs[i], both in LDS) with the whole block,
+// four 16-byte loads in flight per thread.
+__device__ static void copy_rows(const StepArgs &a, const int32_t *hs, const int32_t *gs, int n) {
+  const int cpr = a.latent * 2 / 16;
+  const v4i *src = (const v4i *)a.host_kv;
+  v4i *dst = (v4i *)a.gpu_kv;
+  const int total = n * cpr;
+  for (int i0 = threadIdx.x; i0 < total; i0 += 4 * kSelThreads) {
+    v4i v0, v1, v2, v3;
+    int64_t d0, d1, d2, d3;
+#define ECHO_ROW_LOAD(u, v, d)                                         \
+    {                                                                  \
+      const int i = i0 + (u) * kSelThreads;                            \
+      const int ic = i < total ? i : total - 1;                        \
+      const int e = ic / cpr, c = ic - e * cpr;                        \
+      d = i < total ? (int64_t)gs[e] * cpr + c : -1;                   \
+      if (i < total) v = src[(int64_t)hs[e] * cpr + c];                \
     }
-    base += __popcll(m);
-  }
-  if (tau == a.sc.atiles - 1 && tid == 0) {
-    const int total = s_E + c;
-    a.ctl[ECHO_CTL_NFREE] = total > nmiss ? total - nmiss : 0;
-    a.ws.counters[ECHO_CNT_FREE_END] = total > nmiss ? total - nmiss : 0;
-    if (total < nmiss) fail(a.ws.status, ECHO_ECAPACITY);
+    ECHO_ROW_LOAD(0, v0, d0) ECHO_ROW_LOAD(1, v1, d1) ECHO_ROW_LOAD(2, v2, d2)
+    ECHO_ROW_LOAD(3, v3, d3)
+#undef ECHO_ROW_LOAD
+    if (d0 >= 0) dst[d0] = v0;
+    if (d1 >= 0) dst[d1] = v1;
+    if (d2 >= 0) dst[d2] = v2;
+    if (d3 >= 0) dst[d3] = v3;
   }
 }
 
-hipError_t launch_alloc(const StepArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(k_alloc, dim3(a.sc.atiles), dim3(256), 0, s, a);
+template <bool RECALL, bool ADVANCE>
+__global__ __launch_bounds__(kSelThreads) void k_manage(StepArgs a) {
+  __shared__ uint32_t s_hist[kBins];
+  __shared__ int32_t s_rh[kSlotTile], s_rg[kSlotTile];
+  __shared__ int sh[kSelThreads / kWave + 1];
+  __shared__ int s_moff[kMaxBatch + 1];
+  __shared__ int s_bin, s_below, s_E;
+  if (failed(a.ws.status)) return;
+  const int tid = threadIdx.x;
+  const int blk = blockIdx.x, nblk = gridDim.x;
+  const int t = a.ctl[ECHO_CTL_STEP];
+  const int g0 = blk * kSlotTile + tid * 4;
+
+  // ---- phase 1: free count, age histogram of the evictable slots
+  bool fr[4];
+  int pr[4];
+  for (int i = tid; i < kBins; i += kSelThreads) s_hist[i] = 0;
+  if (tid < kWave) {  // exclusive prefix of the per-request miss counts
+    const int v = tid < a.B ? a.ws.n_miss[tid] : 0;
+    const int incl = wave_incl_scan(v);
+    if (tid < a.B) s_moff[tid] = incl - v;
+    if (tid == kWave - 1) s_moff[a.B] = incl;
+  }
+  __syncthreads();
+  int nfree = 0, nev = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int g = g0 + u;
+    fr[u] = false;
+    pr[u] = t;
+    if (g < a.n_gpu) {
+      fr[u] = a.freef[g] != 0;
+      pr[u] = fr[u] ? t : a.prio[g];
+    }
+    if (fr[u]) ++nfree;
+    if (g < a.n_gpu && !fr[u] && pr[u] < t) {
+      ++nev;
+      atomicAdd(&s_hist[evict_bin(pr[u], t)], 1u);
+    }
+  }
+  int tot;
+  block_excl_scan<kSelThreads>((nfree << 16) | nev, sh, &tot);  // per block: < 2^13 each
+  for (int i = tid; i < kBins; i += kSelThreads)
+    if (s_hist[i]) atomicAdd(&a.sc.ehist[i], s_hist[i]);
+  if (tid == 0) {
+    atomicAdd(&a.ws.counters[ECHO_CNT_FREE], tot >> 16);
+    atomicAdd(&a.ws.counters[ECHO_CNT_EVICTABLE], tot & 0xFFFF);
+  }
+  if (!grid_sync(&a.sc.misc[M_BAR0], nblk, a.ws.status)) return;
+
+  // ---- phase 2: eviction
+  const int nmiss = __hip_atomic_load(&a.ws.counters[ECHO_CNT_MISS], __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+  const int F = __hip_atomic_load(&a.ws.counters[ECHO_CNT_FREE], __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+  const int nE = __hip_atomic_load(&a.ws.counters[ECHO_CNT_EVICTABLE], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+  if ((int64_t)F + nE < nmiss) {
+    if (tid == 0) fail(a.ws.status, ECHO_ECAPACITY);
+    return;
+  }
+  const int64_t want = (int64_t)nmiss + a.sc.misc[M_RESERVE] - F;
+  const int n_evict = (int)(want <= 0 ? 0 : (want < nE ? want : nE));
+  if (blk == 0 && tid == 0) a.ws.counters[ECHO_CNT_EVICT] = n_evict;
+  bool ev[4] = {false, false, false, false};
+  if (n_evict > 0) {
+    find_boundary<true>(a.sc.ehist, n_evict, &s_bin, &s_below, sh);
+    const int bstar = s_bin;
+    const int need = n_evict - s_below;
+    if (bstar > 0) {
+      // boundary bin = one priority: rank its slots by slot id across workgroups
+      int nb = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool evictable = g0 + u < a.n_gpu && !fr[u] && pr[u] < t;
+        const int bin = evictable ? evict_bin(pr[u], t) : kBins;
+        ev[u] = bin < bstar;
+        if (bin == bstar) ++nb;
+      }
+      int btot;
+      int rank = block_excl_scan<kSelThreads>(nb, sh, &btot);
+      if (tid < kWave) {
+        const int E = lookback(a.sc.estate, blk, 0, btot, a.ws.status);
+        if (tid == 0) s_E = E;
+      }
+      __syncthreads();
+      rank += s_E;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool evictable = g0 + u < a.n_gpu && !fr[u] && pr[u] < t;
+        if (evictable && evict_bin(pr[u], t) == bstar) {
+          if (rank < need) ev[u] = true;
+          ++rank;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (ev[u]) {
+          evict_slot(a, g0 + u);
+          fr[u] = true;
+        }
+    } else {
+      // boundary in the clamped bin: exact (priority, slot) select of its slots
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool evictable = g0 + u < a.n_gpu && !fr[u] && pr[u] < t;
+        if (evictable && evict_bin(pr[u], t) == 0) {
+          const int pos = atomicAdd(&a.sc.ecnt[0], 1);
+          a.sc.ecand_key[pos] = (uint32_t)pr[u];
+          a.sc.ecand_idx[pos] = g0 + u;
+        }
+      }
+      if (!grid_sync(&a.sc.misc[M_BAR1], nblk, a.ws.status)) return;
+      if (blk == 0) {
+        const int c = __hip_atomic_load(&a.sc.ecnt[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint64_t P;
+        int pos;
+        block_select(a.sc.ecand_key, a.sc.ecand_idx, c, need, &P, &pos);
+        for (int i = tid; i < c; i += kSelThreads) {
+          const uint32_t k = a.sc.ecand_key[i];
+          const int32_t g = a.sc.ecand_idx[i];
+          if (composite_selected(k, g, P, pos)) evict_slot(a, g);
+        }
+      }
+      if (!grid_sync(&a.sc.misc[M_BAR2], nblk, a.ws.status)) return;
+      // no bin lies below bin 0; slots of higher bins stay
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int g = g0 + u;
+        const bool evictable = g < a.n_gpu && !fr[u] && pr[u] < t;
+        if (evictable && evict_bin(pr[u], t) == 0 && a.freef[g])
+          fr[u] = true;  // evicted by workgroup 0 (made visible by the barrier's fences)
+      }
+    }
+  }
+
+  // ---- phase 3: allocation in ascending slot order
+  int nf = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) nf += fr[u] ? 1 : 0;
+  int ftot;
+  int rank = block_excl_scan<kSelThreads>(nf, sh, &ftot);
+  if (tid < kWave) {
+    const int E = lookback(a.sc.astate, blk, 0, ftot, a.ws.status);
+    if (tid == 0) s_E = E;
+  }
+  __syncthreads();
+  const int E = s_E;
+  rank += E;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    if (!fr[u]) continue;
+    const int g = g0 + u;
+    if (rank < nmiss) {
+      int b = 0;
+      for (int i = 1; i < a.B; ++i)
+        if (s_moff[i] <= rank) b = i;
+      const int j = rank - s_moff[b];
+      const int s = a.ws.miss_tok[(int64_t)b * a.K + j];
+      const int i = a.sc.miss_i[(int64_t)b * a.K + j];
+      const int64_t h = (int64_t)a.sc.req[b].base + s;
+      a.h2g[h] = g;
+      a.g2h[g] = (int32_t)h;
+      a.freef[g] = 0;
+      a.prio[g] = t;
+      a.ws.sel_slot[(int64_t)b * a.K + i] = g;
+      a.ws.recall_h[rank] = (int32_t)h;
+      a.ws.recall_g[rank] = g;
+    } else {
+      a.idxbuf[rank - nmiss] = g;
+    }
+    ++rank;
+  }
+  if (blk == nblk - 1 && tid == 0) {
+    const int total = E + ftot;
+    const int left = total > nmiss ? total - nmiss : 0;
+    a.ctl[ECHO_CTL_NFREE] = left;
+    a.ws.counters[ECHO_CNT_FREE_END] = left;
+    if (total < nmiss) fail(a.ws.status, ECHO_ECAPACITY);
+  }
+
+  // ---- phase 4: recall.  Misses take the lowest free slots, so the workgroups
+  // that allocated them are few; after a barrier every workgroup copies an equal
+  // share of the whole recall list instead.
+  if (RECALL && nmiss > 0) {
+    if (!grid_sync(&a.sc.misc[M_BAR3], nblk, a.ws.status)) return;
+    const int r0 = (int)((int64_t)nmiss * blk / nblk);
+    const int r1 = (int)((int64_t)nmiss * (blk + 1) / nblk);
+    for (int r = r0 + tid; r < r1; r += kSelThreads) {
+      s_rh[r - r0] = __hip_atomic_load(&a.ws.recall_h[r], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+      s_rg[r - r0] = __hip_atomic_load(&a.ws.recall_g[r], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    copy_rows(a, s_rh, s_rg, r1 - r0);
+  }
+  if (ADVANCE) {
+    __syncthreads();
+    if (tid == 0) {
+      const int done = __hip_atomic_fetch_add(&a.sc.misc[M_DONE], 1, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+      if (done == nblk - 1 && !failed(a.ws.status)) a.ctl[ECHO_CTL_STEP] = t + 1;
+    }
+  }
+}
+
+hipError_t launch_manage(const StepArgs &a, bool recall, bool advance, hipStream_t s) {
+  const dim3 grid(a.sc.atiles), block(kSelThreads);
+  if (recall && advance)
+    hipLaunchKernelGGL((k_manage<true, true>), grid, block, 0, s, a);
+  else if (recall)
+    hipLaunchKernelGGL((k_manage<true, false>), grid, block, 0, s, a);
+  else if (advance)
+    hipLaunchKernelGGL((k_manage<false, true>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((k_manage<false, false>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
-// Recall: rows of 16-byte chunks, four loads in flight per thread.
+// Standalone recall: rows of 16-byte chunks, four loads in flight per thread.
 constexpr int kRecallBlocks = 1024;
 
-__global__ __launch_bounds__(256) void k_recall(StepArgs a, int advance) {
+__global__ __launch_bounds__(256) void k_recall(StepArgs a) {
   if (failed(a.ws.status)) return;
   const int n = a.ws.counters[ECHO_CNT_MISS];
   const int cpr = a.latent * 2 / 16;
@@ -122,11 +318,10 @@ __global__ __launch_bounds__(256) void k_recall(StepArgs a, int advance) {
     for (int u = 0; u < 4; ++u)
       if (hh[u] >= 0) dst[(int64_t)gg[u] * cpr + cc[u]] = v[u];
   }
-  if (advance && blockIdx.x == 0 && threadIdx.x == 0) a.ctl[ECHO_CTL_STEP] += 1;
 }
 
-hipError_t launch_recall(const StepArgs &a, bool advance, hipStream_t s) {
-  hipLaunchKernelGGL(k_recall, dim3(kRecallBlocks), dim3(256), 0, s, a, advance ? 1 : 0);
+hipError_t launch_recall(const StepArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(k_recall, dim3(kRecallBlocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

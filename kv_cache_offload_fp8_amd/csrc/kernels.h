@@ -31,6 +31,8 @@ struct StepArgs {
   float *theta_upd;  // EMA state to update in the top-k epilogue, or null
   float *guard_upd;  // selection guard to refresh in the top-k epilogue, or null
   int32_t mode;
+  // launch shapes, fixed by the dims so that a captured graph stays valid
+  int32_t score_waves;  // scoring waves of the indexer launch (7 per workgroup)
   // workspace
   echo_ws_t ws;
   Scratch sc;
@@ -38,27 +40,28 @@ struct StepArgs {
 
 // begin-kernel roles
 enum {
-  BEGIN_REQ = 1,         // request table, tickets, reserve
+  BEGIN_REQ = 1,         // request table, scoring jobs, reserve
   BEGIN_Q = 2,           // fp8 hi/lo split of the query
-  BEGIN_CLR_INDEX = 4,   // look-back states, prefetch counters
-  BEGIN_CLR_TOPK = 8,    // histograms, candidate counts, key ranges
-  BEGIN_CLR_MANAGE = 16  // eviction histogram, candidate counts, allocation states
+  BEGIN_CLR_INDEX = 4,   // look-back states, prefetch outputs
+  BEGIN_CLR_TOPK = 8,    // shortcut counter
+  BEGIN_CLR_MANAGE = 16  // eviction histogram, look-back states, barriers, counters
 };
+
+// Workgroups of the indexer launch for these dims (one per compute unit at most).
+int score_grid(const echo_dims_t &d);
+// Compute units of the current device (cached per device).
+int device_cus();
 
 hipError_t launch_begin(const StepArgs &a, int roles, hipStream_t s);
 hipError_t launch_score(const StepArgs &a, hipStream_t s);
-hipError_t launch_topk_minmax(const StepArgs &a, hipStream_t s);
-hipError_t launch_topk_hist(const StepArgs &a, hipStream_t s);
-hipError_t launch_topk_collect(const StepArgs &a, hipStream_t s);
-hipError_t launch_topk_resolve(const StepArgs &a, bool protect, hipStream_t s);
+hipError_t launch_topk(const StepArgs &a, bool protect, hipStream_t s);
 hipError_t launch_protect(const StepArgs &a, hipStream_t s);
-hipError_t launch_evict_hist(const StepArgs &a, hipStream_t s);
-hipError_t launch_evict_collect(const StepArgs &a, hipStream_t s);
-hipError_t launch_evict_resolve(const StepArgs &a, hipStream_t s);
-hipError_t launch_alloc(const StepArgs &a, hipStream_t s);
-hipError_t launch_recall(const StepArgs &a, bool advance, hipStream_t s);
+hipError_t launch_manage(const StepArgs &a, bool recall, bool advance, hipStream_t s);
+hipError_t launch_recall(const StepArgs &a, hipStream_t s);
 hipError_t launch_step_advance(const StepArgs &a, hipStream_t s);
 hipError_t launch_meta_init(const StepArgs &a, hipStream_t s);
 hipError_t launch_ws_reset(const echo_ws_t &ws, hipStream_t s);
+hipError_t launch_kindex_pack(const uint8_t *rows, uint8_t *tiled, int64_t n_rows, int D,
+                              hipStream_t s);
 
 }  // namespace echo

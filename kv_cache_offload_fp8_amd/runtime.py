@@ -157,10 +157,22 @@ class Batch:
                                        _ptr(self.ctx) if self.B else None)
 
 
+def pack_kidx(dims: abi.echo_dims_t, rows: torch.Tensor, out: torch.Tensor = None) -> torch.Tensor:
+    """Indexer K rows (uint8 fp8 codes [n, D], row-major, on the device) in the tiled
+    layout the scoring kernel reads (echo_kindex_pack); n must be a multiple of 16."""
+    assert rows.dtype == torch.uint8 and rows.dim() == 2 and rows.is_contiguous()
+    if out is None:
+        out = torch.empty_like(rows)
+    assert out.shape == rows.shape and out.dtype == torch.uint8 and out.is_contiguous()
+    check(abi.echo_kindex_pack(dims, rows.data_ptr(), out.data_ptr(), rows.shape[0],
+                               stream_handle()), "echo_kindex_pack")
+    return out
+
+
 class Layer:
-    """Tensors of one layer.  `kidx` (uint8 [n_host, D]) and the host pool are shared
-    or owned by the caller; the metadata, GPU pool, queries, weights and EMA state are
-    allocated here."""
+    """Tensors of one layer.  `kidx` (uint8 [n_host, D] in the tiled layout of
+    pack_kidx) and the host pool are shared or owned by the caller; the metadata, GPU
+    pool, queries, weights and EMA state are allocated here."""
 
     def __init__(self, dims: abi.echo_dims_t, kidx: torch.Tensor, host: HostPool, batch: int,
                  device="cuda"):

@@ -37,9 +37,13 @@ def _gen(device, s: int) -> torch.Generator:
 
 
 def host_layout(ctx: np.ndarray) -> np.ndarray:
+    """First host id of each request: requests packed back to back, each starting on a
+    16-row boundary (the tiled indexer-K layout groups host ids by 16)."""
+    ctx = np.asarray(ctx, np.int64)
+    span = (ctx + 15) // 16 * 16
     base = np.zeros(ctx.size, np.int64)
     if ctx.size > 1:
-        base[1:] = np.cumsum(ctx.astype(np.int64))[:-1]
+        base[1:] = np.cumsum(span)[:-1]
     assert base.size == 0 or base[-1] + ctx[-1] < 2**31
     return base.astype(np.int32)
 

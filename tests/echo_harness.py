@@ -70,7 +70,8 @@ class Rig:
                                 max(1, self.B), mc, wl.latent, wl.alpha, wl.cap_div, steps)
         self.host = R.HostPool(wl.n_host, wl.latent)
         self.host.np[:] = self.inp.np_latents()
-        self.kidx = self.inp.kidx.to(device)
+        self.kidx_rows = self.inp.kidx.to(device)  # row-major, as the oracle reads it
+        self.kidx = R.pack_kidx(self.dims, self.kidx_rows)
         self.layer = R.Layer(self.dims, self.kidx, self.host, self.B, device)
         if self.B:
             self.layer.q.copy_(self.inp.q.to(device))

@@ -70,6 +70,7 @@ def test_workspace_size_and_bind():
     (dict(n_heads=0), abi.ECHO_EINVAL), (dict(top_k=0), abi.ECHO_EINVAL),
     (dict(ema_alpha=0.0), abi.ECHO_EINVAL), (dict(ema_alpha=1.5), abi.ECHO_EINVAL),
     (dict(n_host=1 << 31), abi.ECHO_EINVAL), (dict(q_ring=0), abi.ECHO_EINVAL),
+    (dict(n_host=2_000_008 + 4), abi.ECHO_EINVAL),
     (dict(n_heads=65), abi.ECHO_EUNSUPPORTED), (dict(head_dim=256), abi.ECHO_EUNSUPPORTED),
     (dict(head_dim=48), abi.ECHO_EUNSUPPORTED), (dict(top_k=4097), abi.ECHO_EUNSUPPORTED),
     (dict(max_batch=65), abi.ECHO_EUNSUPPORTED), (dict(latent_dim=575), abi.ECHO_EUNSUPPORTED),
@@ -99,6 +100,13 @@ def test_null_arguments_are_rejected_before_any_launch():
     assert abi.echo_ws_reset(d, None, 0) == abi.ECHO_EINVAL
     too_big = abi.echo_batch_t(9, 1, 1)  # batch above max_batch
     assert abi.echo_topk(d, 1, 65536, too_big, ws, None, 0) == abi.ECHO_EINVAL
+    # K layout: null, a row count that is not a whole number of 16-row groups,
+    # overlapping buffers, misaligned buffers
+    assert abi.echo_kindex_pack(d, None, 1 << 30, 16, 0) == abi.ECHO_EINVAL
+    assert abi.echo_kindex_pack(d, 1 << 30, None, 16, 0) == abi.ECHO_EINVAL
+    assert abi.echo_kindex_pack(d, 1 << 30, 1 << 31, 15, 0) == abi.ECHO_EINVAL
+    assert abi.echo_kindex_pack(d, 1 << 30, (1 << 30) + 1024, 16, 0) == abi.ECHO_EINVAL
+    assert abi.echo_kindex_pack(d, (1 << 30) + 8, 1 << 31, 16, 0) == abi.ECHO_EINVAL
 
 
 def test_status_strings():

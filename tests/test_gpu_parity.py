@@ -114,10 +114,11 @@ def test_topk_external_scores_with_ties(n, k):
     sc = rng.integers(0, 40, size=(B, n)).astype(np.float32)  # heavy ties
     sc[1] = rng.standard_normal(n).astype(np.float32) * 100
     sc[2, : n // 2] = 7.0
-    dims = R.make_dims(4, 32, k, 3 * n, 4096, B, n)
+    span = (n + 15) // 16 * 16
+    dims = R.make_dims(4, 32, k, B * span, 4096, B, n)
     ws = R.Workspace(dims)
     ws.reset()
-    batch = R.Batch(np.arange(B) * n, [n] * B)
+    batch = R.Batch(np.arange(B) * span, [n] * B)
     dev = torch.from_numpy(sc).cuda()
     theta = torch.full((B,), float("inf"), device="cuda")
     R.check(abi.echo_topk(dims, dev.data_ptr(), n, batch.struct, ws.ws, theta.data_ptr(),
@@ -166,6 +167,38 @@ def test_device_side_batch_check():
     st = layer.state()
     assert st["t"] == 0 and (st["h2g"] == -1).all() and (st["free"] == 1).all()
     rig.close()
+
+
+def test_misaligned_host_base_is_rejected_on_device():
+    wl = get("tiny").scaled(n_host=8192)
+    rig = H.Rig(wl, steps=1, ctx=[4096])
+    bad = R.Batch([8], [4000], "cuda")  # in range, no overlap, but not on a 16-row boundary
+    ws = R.Workspace(rig.dims)
+    ws.reset()
+    R.check(abi.echo_layer_step(rig.dims, rig.layer.struct, bad.struct, ws.ws, H.MODE_EMA,
+                                R.stream_handle()), "launch")
+    o = ws.read(1)
+    assert o["status"] == abi.ECHO_EDEVARG
+    st = rig.layer.state()
+    assert st["t"] == 0 and (st["h2g"] == -1).all() and (st["free"] == 1).all()
+    rig.close()
+
+
+@pytest.mark.parametrize("D", [32, 64, 96, 128])
+def test_kindex_pack_layout(D):
+    # the tiled layout is a fixed permutation inside each group of 16 rows
+    n = 16 * 37
+    rng = np.random.default_rng(D)
+    rows = rng.integers(0, 256, size=(n, D), dtype=np.uint8)
+    dims = R.make_dims(4, D, 256, n, 1024, 1, 4096)
+    tiled = R.pack_kidx(dims, torch.from_numpy(rows).cuda()).cpu().numpy().reshape(-1)
+    h = np.arange(n)[:, None]
+    d = np.arange(D)[None, :]
+    pos = 16 * D * (h // 16) + 8 * D * ((d % 32) // 16) + 256 * (d // 32) + 16 * (h % 16) + d % 16
+    expect = np.empty(n * D, np.uint8)
+    expect[pos.reshape(-1)] = rows.reshape(-1)
+    assert np.array_equal(tiled, expect)
+    assert np.unique(pos).size == n * D  # a permutation
 
 
 def test_context_edge_cases():
