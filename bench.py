@@ -9,8 +9,10 @@ protect/evict/alloc and recall for the whole batch.  The metric is layer-steps/s
 (layers x steps / elapsed).  Inputs are seeded synthetic tensors resident in HBM
 (and in pinned host memory for the host pool) before the timed region starts.
 
-Also reported: the indexer kernel's HBM roofline (algorithmic bytes: 128 B of K
-read + 4 B of score written per scored token), the recall host-link rate, the
+Also reported: the scoring kernel's HBM roofline (algorithmic bytes: 128 B of K
+read + 4 B of score written per scored token; measured with prefetch off, where
+the same kernel only scores), the layer step against its host-link floor (every
+prefetched or missed row crosses the link once), the recall host-link rate, the
 measured pinned host-link peaks, the GPU-cache hit rate and a CPU baseline of the
 oracle on a bounded sample of one layer-step.
 
@@ -48,12 +50,48 @@ def parse():
                    help="distinct pinned host pools; layers share them round-robin")
     p.add_argument("--breakdown-steps", type=int, default=2)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-requests", type=int, default=8)
+    p.add_argument("--cpu-sample-requests", type=int, default=32)
+    p.add_argument("--cpu-sample-steps", type=int, default=12,
+                   help="decode steps of layer 0 the CPU oracle runs (about 1 s each)")
     p.add_argument("--mode", default="ema", choices=["ema", "neg_inf", "pos_inf"])
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--cap-div", type=int, default=None,
                    help="override the prefetch cap divisor (cap = min(k, ceil(ctx/div)))")
+    p.add_argument("--pmc-calibrate", action="store_true",
+                   help="end with a 256 MiB device-to-device copy whose FETCH_SIZE / WRITE_SIZE "
+                        "counters scale the indexer's")
     return p.parse_args()
+
+
+def source_digest() -> str:
+    """sha1 over the HIP sources: the stored HBM-traffic figures hold only while it matches."""
+    import glob
+    import hashlib
+    h = hashlib.sha1()
+    for f in sorted(glob.glob(os.path.join(ROOT, "kv_cache_offload_fp8_amd", "csrc", "*"))):
+        if f.endswith((".hip", ".h")):
+            h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def stored_traffic():
+    """Bytes per launch of the scoring kernel from the committed counter summary
+    (profiles/k_score_capacity_traffic.txt), or None if it is missing or the
+    kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "k_score_capacity_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha1") != source_digest():
+        return None
+    try:
+        return int(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def main():
@@ -236,6 +274,13 @@ def main():
     log(f"[bench] indexer, prefetch off: {so_ms:.4f} ms = {so_gbps:.0f} GB/s "
         f"({so_gbps / HBM_PEAK_GBPS:.1%} of HBM peak)")
 
+    if args.pmc_calibrate:  # a plain copy of known size for the HBM-traffic counters
+        cal_src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        cal_dst = torch.empty_like(cal_src)
+        cal_dst.copy_(cal_src)
+        torch.cuda.synchronize()
+        del cal_src, cal_dst
+
     # ------------------------------------------------------ host-link peaks
     n_rows = min(wl.n_host, 65536)
     big = pools[0]
@@ -267,6 +312,14 @@ def main():
     log(f"[bench] host link: hipMemcpy H2D {memcpy_gbps:.1f} GB/s, zero-copy recall kernel "
         f"{zc_gbps:.1f} GB/s over {nz} rows")
 
+    # layer-step floor: every prefetched and missed row crosses the host link once
+    step_ms = ms_per_step / L
+    link_bytes = (float(prefetched.mean()) + float(misses.mean())) * row
+    link_floor_ms = link_bytes / (link_peak * 1e9) * 1e3
+    traffic = stored_traffic()
+    log(f"[bench] layer step {step_ms * 1e3:.1f} us; host-link floor "
+        f"{link_floor_ms * 1e3:.1f} us ({link_floor_ms / step_ms:.1%})")
+
     # ------------------------------------------------------- CPU baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -292,15 +345,22 @@ def main():
                                f"host pool {wl.n_host} x {wl.latent} bf16, rho {wl.rho}",
                    "global_batch": B, "seq_len": int(ctx.max()), "layers": L,
                    "threshold_mode": args.mode},
-        "roofline": {"kernel": "echo_indexer_prefetch (k_begin + k_score)", "bound": "hbm",
-                     "achieved": round(idx_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(idx_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "bytes_per_launch": idx_bytes, "avg_launch_ms": round(idx_ms, 5)},
-        "indexer_scoring_only": {"kernel": "echo_indexer_prefetch (k_begin + k_score), "
-                                           "threshold +inf", "avg_launch_ms": round(so_ms, 5),
-                                 "achieved": round(so_gbps, 1), "peak": HBM_PEAK_GBPS,
-                                 "unit": "GB/s", "frac": round(so_gbps / HBM_PEAK_GBPS, 4)},
-        "indexer_hbm_gbps": round(idx_gbps, 1),
+        "roofline": {"kernel": "lightning-indexer scoring: echo_indexer_prefetch with prefetch "
+                               "off = k_begin + k_score<4,false>",
+                     "bound": "hbm", "achieved": round(so_gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(so_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "bytes_per_launch": idx_bytes,
+                     "avg_launch_ms": round(so_ms, 5)},
+        "layer_step_link_roofline": {
+            "bound": "host link", "link_bytes_per_layer_step": int(link_bytes),
+            "floor_ms": round(link_floor_ms, 5), "measured_ms": round(step_ms, 5),
+            "frac": round(link_floor_ms / step_ms, 4), "link_peak_gbps": round(link_peak, 2),
+            "achieved_gbps": round(link_bytes / (step_ms * 1e-3) / 1e9, 2)},
+        "indexer_ema_standalone": {"avg_launch_ms": round(idx_ms, 5),
+                                   "hbm_gbps": round(idx_gbps, 1),
+                                   "note": "echo_indexer_prefetch alone also copies every "
+                                           "prefetched row before it returns"},
+        "indexer_hbm_gbps": round(so_gbps, 1),
         "recall_host_link_gbps": round(recall_gbps, 2),
         "recall_frac_of_link_peak": round(recall_gbps / link_peak, 4),
         "host_link_peak_gbps": {"hipMemcpy_h2d": round(memcpy_gbps, 2),
@@ -320,41 +380,44 @@ def main():
 
 
 def cpu_baseline(wl, ctx, base, lay0, rows0, args, dims):
-    """The oracle, as it stands, on a bounded sample of layer 0's first decode step:
-    the first `--cpu-sample-requests` requests of the batch.  Scaled to layer-steps/s
-    by the share of scored tokens the sample covers."""
+    """The oracle, as it stands, on a bounded sample: layer 0 of the same workload,
+    the first `--cpu-sample-requests` requests, `--cpu-sample-steps` decode steps in
+    EMA mode (its own scores).  Reported as layer-steps/s, scaled by the share of the
+    layer-step's scored tokens the sample covers."""
     import torch
 
     from oracle import oracle as O
     from synth import gen as G
 
     nb = max(1, min(args.cpu_sample_requests, ctx.size))
+    steps = max(1, min(args.cpu_sample_steps, lay0.q.shape[0]))
     sctx = ctx[:nb].astype(np.int32)
     sbase = G.host_layout(sctx)
     n = int(sctx.sum())
     n_rows = (int(sbase[-1]) + int(sctx[-1]) + 15) // 16 * 16
     kid = np.zeros((n_rows, wl.head_dim), np.uint8)
-    kdev = rows0
     for b in range(nb):
-        kid[sbase[b]:sbase[b] + sctx[b]] = kdev[int(base[b]):int(base[b]) + int(sctx[b])].cpu() \
+        kid[sbase[b]:sbase[b] + sctx[b]] = rows0[int(base[b]):int(base[b]) + int(sctx[b])].cpu() \
             .numpy()
-    q0 = lay0.q[0, :nb].contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+    qs = lay0.q[:steps, :nb].contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
     w0 = lay0.w[:nb].cpu().numpy()
     orc = O.OracleLayer(wl.heads, wl.head_dim, wl.top_k, wl.latent, n_rows, wl.n_gpu, nb,
                         wl.cap_div, wl.alpha, keep_pool=False)
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
     t0 = time.perf_counter()
-    o = orc.step(sbase, sctx, q0, w0, kid, None, mode=O.MODE_EMA)
+    for t in range(steps):
+        o = orc.step(sbase, sctx, qs[t], w0, kid, None, mode=O.MODE_EMA)
+        assert o["status"] == O.OK
     dt = time.perf_counter() - t0
-    assert o["status"] == O.OK
     frac = n / float(ctx.sum())
-    per_layer_step = dt / frac
-    log(f"[bench] cpu oracle: {nb} requests ({n} tokens) in {dt:.2f}s on {threads} threads "
-        f"-> {per_layer_step:.1f}s per full layer-step")
+    per_layer_step = dt / steps / frac
+    log(f"[bench] cpu oracle: {steps} steps x {nb} requests ({n} tokens each) in {dt:.2f}s on "
+        f"{threads} threads -> {per_layer_step:.2f}s per full layer-step")
     return {"value": round(1.0 / per_layer_step, 6), "unit": "layer-steps/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"layer 0, first decode step, {nb} of {ctx.size} requests ({n} scored "
-                      f"tokens, {frac:.3%} of the layer-step's tokens); time scaled by tokens"}
+            "sample": f"layer 0, decode steps 0..{steps - 1} in EMA mode, {nb} of {ctx.size} "
+                      f"requests ({n} scored tokens per step, {frac:.1%} of the layer-step's "
+                      f"tokens), {dt:.1f} s of CPU time; scaled by tokens"}
 
 
 if __name__ == "__main__":

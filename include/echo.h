@@ -115,7 +115,8 @@ typedef struct {
   uint8_t *free_flags; /* [n_gpu]   1 = free                                         */
 } echo_layer_meta_t;
 
-/* One layer's tensors. */
+/* One layer's tensors.  k_index, gpu_kv, host_kv and q must be 16-byte aligned
+ * (ECHO_EINVAL otherwise). */
 typedef struct {
   echo_layer_meta_t meta;
   const uint8_t *k_index;  /* n_host*head_dim bytes: indexer K, OCP fp8 E4M3FN, in the

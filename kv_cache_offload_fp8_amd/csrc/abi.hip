@@ -23,14 +23,17 @@ int device_cus() {
   return cache[dev];
 }
 
-int score_grid(const echo_dims_t &d) {
+void index_grid(const echo_dims_t &d, int *score_blocks, int *copy_blocks) {
+  const int cus = device_cus();
+  int gc = cus / 4 < kCopyBlocks ? cus / 4 : kCopyBlocks;
+  if (gc < 1) gc = 1;
   const int64_t max_tiles =
       (int64_t)d.max_batch * (((int64_t)d.max_ctx + kScoreTile - 1) / kScoreTile);
-  int64_t g = (max_tiles + kScoreWaves - 1) / kScoreWaves;
-  const int cus = device_cus();
-  if (g > cus) g = cus;
-  if (g < 1) g = 1;
-  return (int)g;
+  int64_t gs = (max_tiles + kScoreWaves - 1) / kScoreWaves;
+  if (gs > cus - gc) gs = cus - gc;
+  if (gs < 1) gs = 1;
+  *score_blocks = (int)gs;
+  *copy_blocks = gc;
 }
 
 }  // namespace echo
@@ -57,7 +60,10 @@ int check_dims(const echo_dims_t *d) {
 // for its grid barrier: at most one per compute unit.
 int check_launch(const echo_dims_t *d) {
   const int64_t atiles = ((int64_t)d->n_gpu + kSlotTile - 1) / kSlotTile;
-  if (atiles > device_cus()) return ECHO_EUNSUPPORTED;
+  int gs = 1, gc = 1;
+  index_grid(*d, &gs, &gc);
+  const int64_t copy_blocks = 2 * (int64_t)gc * kScoreWaves / 16;  // 16-wave workgroups
+  if (atiles + copy_blocks > device_cus()) return ECHO_EUNSUPPORTED;
   return ECHO_OK;
 }
 
@@ -113,6 +119,9 @@ bool layer_ok(const echo_layer_t *l, bool need_theta) {
   const echo_layer_meta_t &m = l->meta;
   if (!m.h2g || !m.g2h || !m.prio || !m.idxbuf || !m.free_flags) return false;
   if (!l->k_index || !l->gpu_kv || !l->host_kv || !l->q || !l->w || !l->ctl) return false;
+  if (((uintptr_t)l->q & 15) != 0 || ((uintptr_t)l->k_index & 15) != 0 ||
+      ((uintptr_t)l->gpu_kv & 15) != 0 || ((uintptr_t)l->host_kv & 15) != 0)
+    return false;  // 16-byte vector loads and stores
   if (need_theta && !l->theta) return false;
   return true;
 }
@@ -157,7 +166,11 @@ StepArgs make_args(const echo_dims_t &d, const echo_layer_t *l, const echo_batch
   a.theta_upd = nullptr;
   a.guard_upd = nullptr;
   a.mode = mode;
-  a.score_waves = score_grid(d) * kScoreWaves;
+  int gs = 1, gc = 1;
+  index_grid(d, &gs, &gc);
+  a.score_blocks = gs;
+  a.score_waves = gs * kScoreWaves;
+  a.copy_waves = gc * kScoreWaves;
   a.ws = ws;
   scratch_layout(d, ws.internal, &a.sc);
   return a;
@@ -309,6 +322,7 @@ int echo_layer_step(const echo_dims_t *dims, const echo_layer_t *layer, const ec
   StepArgs a = make_args(*dims, layer, batch, *ws, theta_mode);
   a.theta_upd = theta_mode == ECHO_THETA_EMA ? layer->theta : nullptr;
   a.guard_upd = layer->guard;
+  a.copy_handoff = 1;  // the prefetch copy runs on through top-k and management
   rc = run_indexer(a, BEGIN_CLR_MANAGE, stream);
   if (rc != ECHO_OK) return rc;
   LAUNCH(launch_topk(a, true, stream));

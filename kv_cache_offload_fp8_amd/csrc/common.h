@@ -15,8 +15,9 @@ constexpr int kHeadsPad = 64;     // indexer heads padded to 4 groups of 16 (MFM
 constexpr int kDimPad = 128;      // indexer dim padded to one 16x16x128 fp8 MFMA k-step
 constexpr int kScoreTile = 256;   // tokens per scoring work item (one wave, 4 x 64)
 constexpr int kGuardSlots = 32;   // selection-guard candidates kept per work item
-constexpr int kScoreWaves = 7;    // scoring waves per workgroup; the eighth copies rows
-constexpr int kRing = 1024;       // LDS ring of prefetched rows waiting for the copy wave
+constexpr int kScoreWaves = 8;    // waves per indexer workgroup (scoring or copying)
+constexpr int kCopyBlocks = 64;   // indexer workgroups that only copy prefetched rows
+constexpr int kCopyRows = 4;      // prefetch ranks a copy wave takes at a time
 constexpr uint32_t kGuardUlps = 1u << 18;  // selection guard margin: ~3% below last k-th score
 constexpr int kBins = 4096;       // first-level histogram bins
 constexpr int kSelChunk = 8192;   // tokens per block in the top-k histogram/collect passes
@@ -34,6 +35,8 @@ enum {
   M_BAR2 = 6,
   M_DONE = 7,         // management workgroups finished
   M_BAR3 = 8,
+  M_SCORE_DONE = 9,   // indexer scoring workgroups finished (copy hand-off)
+  M_TOPK_DONE = 10,   // top-k workgroups finished (copy hand-off)
   M_NMISC = 16
 };
 
@@ -70,6 +73,9 @@ struct Scratch {
   uint32_t *gcand_key;    // [max_tiles][kGuardSlots] candidates above the selection guard
   int32_t *gcand_idx;     // [max_tiles][kGuardSlots]
   int32_t *gcand_cnt;     // [max_tiles] candidates found in each work item
+  uint64_t *pfq;          // [max_batch][top_k] prefetch rows by rank: 1<<63 | h<<31 | slot
+  uint64_t *pfn;          // [max_batch] 1<<32 | prefetched count, once final
+  int32_t *cstate;        // [kCopyBlocks * kScoreWaves][2] copy-wave progress (block, done)
   int32_t *miss_i;        // [max_batch][top_k] position of each miss in sel_tok
   uint32_t *ehist;        // [kBins]
   uint32_t *ecand_key;    // [n_gpu]
@@ -107,6 +113,9 @@ inline int64_t scratch_layout(const echo_dims_t &d, uint8_t *base, Scratch *s) {
   t.gcand_key = (uint32_t *)take((int64_t)max_tiles * kGuardSlots * 4);
   t.gcand_idx = (int32_t *)take((int64_t)max_tiles * kGuardSlots * 4);
   t.gcand_cnt = (int32_t *)take((int64_t)max_tiles * 4);
+  t.pfq = (uint64_t *)take(B * K * 8);
+  t.pfn = (uint64_t *)take(B * 8);
+  t.cstate = (int32_t *)take(2 * kCopyBlocks * kScoreWaves * 4);
   t.miss_i = (int32_t *)take(B * K * 4);
   t.ehist = (uint32_t *)take(kBins * 4);
   t.ecand_key = (uint32_t *)take(G * 4);

@@ -34,7 +34,7 @@
 // applies ReLU and the head weights in registers and reduces the 64 heads with
 // two cross-lane adds.
 //
-// Work assignment.  A workgroup holds seven scoring waves and one copy wave.
+// Work assignment.  Most workgroups score (eight waves each); a few only copy.
 // Request b gets wb scoring waves (chosen so that no wave takes more 256-token
 // work items than any other); its k-th wave scores items k, k + wb, k + 2wb, ...
 // in order.  A wave therefore loads its request's query once, takes no ticket
@@ -43,14 +43,17 @@
 // candidates in token order finds its predecessors done or nearly done.  The
 // prefetch epilogue of an item (residency check, look-back, map installs) runs
 // one chunk into the next item, after that item's loads are issued, so its map
-// lookups never drain the K stream.  Rows to fetch go to the workgroup's copy
-// wave through an LDS ring; the copy wave reads them from mapped host memory and
-// writes the GPU pool while scoring continues -- the MI355X form of the pages'
-// dedicated prefetch role inside the indexer pipeline.  Scoring waves also keep
-// the tokens whose score clears a guard just below the previous step's k-th
+// lookups never drain the K stream.  Installed rows are published by rank as
+// self-validating 64-bit entries; the copy workgroups read them from mapped host
+// memory into the GPU pool while scoring continues -- the MI355X form of the
+// pages' dedicated prefetch role inside the indexer pipeline.  The copy runs on
+// workgroups of its own because host reads issued from a compute unit hold up
+// that unit's HBM stream (measured: scoring slowed from about 100 us to 190 us
+// when each workgroup also read its rows from the host).  Scoring waves also
+// keep the tokens whose score clears a guard just below the previous step's k-th
 // score in fixed per-item slots; when at least k are found, the exact top-k needs
 // only those candidates.
-#include "kernels.h"
+#include "copy.h"
 
 namespace echo {
 
@@ -159,14 +162,21 @@ __device__ static void stage_query(const StepArgs &a, int b) {
   const uint16_t *src = a.q + ((int64_t)slot * a.B + b) * a.H * a.D;
   float x[32];
   float amax = 0.0f;
+  // 32 bf16 = four 16-byte loads (D is a multiple of 32, so a part is all in or all out)
+  const bool in_part = j < a.H && part * 32 < a.D;
+  const uint4 *qv = (const uint4 *)(src + (in_part ? j * a.D + part * 32 : 0));
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const int d = part * 32 + i;
-    float v = 0.0f;
-    if (j < a.H && d < a.D) v = __uint_as_float((uint32_t)src[j * a.D + d] << 16);
-    x[i] = v;
-    amax = fmaxf(amax, fabsf(v));
+  for (int u = 0; u < 4; ++u) {
+    const uint4 w4 = in_part ? qv[u] : make_uint4(0, 0, 0, 0);
+    const uint32_t wd[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[u * 8 + 2 * k] = __uint_as_float(wd[k] << 16);
+      x[u * 8 + 2 * k + 1] = __uint_as_float(wd[k] & 0xFFFF0000u);
+    }
   }
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
   amax = fmaxf(amax, __shfl_xor(amax, 1));
   amax = fmaxf(amax, __shfl_xor(amax, 2));
   int e = 0;
@@ -214,10 +224,12 @@ __global__ __launch_bounds__(256) void k_begin(StepArgs a, int roles) {
       a.ws.n_cand[tid] = 0;
     }
     if ((roles & BEGIN_CLR_INDEX) && tid == 0) a.ws.counters[ECHO_CNT_PREFETCH] = 0;
+    if ((roles & BEGIN_CLR_INDEX) && (tid == M_SCORE_DONE || tid == M_TOPK_DONE))
+      a.sc.misc[tid] = 0;
     if ((roles & BEGIN_CLR_TOPK) && tid == 0) a.ws.counters[ECHO_CNT_SHORTCUT] = 0;
     if (roles & BEGIN_CLR_MANAGE) {
       if (tid < 4) a.sc.ecnt[tid] = 0;
-      if (tid >= M_BAR0 && tid <= M_BAR3) a.sc.misc[tid] = 0;
+      if (tid >= M_BAR0 && tid <= M_TOPK_DONE) a.sc.misc[tid] = 0;
       if (tid < ECHO_NCOUNTERS && tid != ECHO_CNT_PREFETCH && tid != ECHO_CNT_SHORTCUT)
         a.ws.counters[tid] = 0;
     }
@@ -234,7 +246,11 @@ __global__ __launch_bounds__(256) void k_begin(StepArgs a, int roles) {
   if (blk >= kBeginClearBlocks) return;
   const int64_t i0 = (int64_t)blk * blockDim.x + threadIdx.x;
   const int64_t step = (int64_t)kBeginClearBlocks * blockDim.x;
-  if (roles & BEGIN_CLR_INDEX) fill_u32((uint32_t *)a.sc.tstate, 2LL * a.sc.max_tiles, 0u, i0, step);
+  if (roles & BEGIN_CLR_INDEX) {
+    fill_u32((uint32_t *)a.sc.tstate, 2LL * a.sc.max_tiles, 0u, i0, step);
+    fill_u32((uint32_t *)a.sc.pfn, 2LL * a.max_batch, 0u, i0, step);
+    fill_u32((uint32_t *)a.sc.cstate, 2LL * kCopyBlocks * kScoreWaves, 0u, i0, step);
+  }
   if (roles & BEGIN_CLR_MANAGE) {
     fill_u32(a.sc.ehist, kBins, 0u, i0, step);
     fill_u32((uint32_t *)a.sc.estate, 2LL * a.sc.atiles, 0u, i0, step);
@@ -339,132 +355,16 @@ __device__ inline float score_chunk(const v8i (&kb)[4], const v8i (&qa)[HG][2],
   return sel == 0 ? sc4[0] : sel == 1 ? sc4[1] : sel == 2 ? sc4[2] : sc4[3];
 }
 
-// LDS ring between the scoring waves (producers) and the copy wave (consumer).
-// Entry p lives at p % kRing and is valid once seq == p + 1.  Once every scoring
-// wave is done, the copy wave publishes how far it got (fhead) and all eight waves
-// split the entries left in [fhead, tail), which are all published by then.
-struct Ring {
-  int32_t h[kRing], g[kRing], seq[kRing];
-  int32_t tail;   // next position to reserve
-  int32_t head;   // next position the copy wave will take
-  int32_t done;   // scoring waves that have finished
-  int32_t split;  // 1 once fhead is valid
-  int32_t fhead;  // where the shared drain starts
-};
-
-__device__ inline int lds_load(const int32_t *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-__device__ inline void lds_store(int32_t *p, int v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-
-constexpr int kCopyBatch = 16;  // rows taken from the ring per round
-constexpr int kCopyLoads = 8;   // 16-byte loads in flight per lane per round (unrolled below)
-
-// Copy the n <= 64 rows whose host id / slot lanes 0..n-1 hold, 8 KB at a time:
-// eight 16-byte host reads per lane in flight, then the eight HBM writes.
-__device__ static void copy_batch(const StepArgs &a, int my_h, int my_g, int n) {
-  const int lane = lane_id();
-  const int cpr = a.latent * 2 / 16;
-  const v4i *src = (const v4i *)a.host_kv;
-  v4i *dst = (v4i *)a.gpu_kv;
-  const int nchunks = n * cpr;
-  for (int c0 = 0; c0 < nchunks; c0 += kCopyLoads * kWave) {
-    v4i v0, v1, v2, v3, v4, v5, v6, v7;
-    int64_t d0, d1, d2, d3, d4, d5, d6, d7;
-    // chunk u of this lane: host offset (row h, piece c) -> pool offset (slot g, piece c)
-#define ECHO_COPY_LOAD(u, v, d)                                          \
-    {                                                                    \
-      const int ci = c0 + (u) * kWave + lane;                            \
-      const int cc = ci < nchunks ? ci : nchunks - 1;                    \
-      const int e = cc / cpr;                                            \
-      const int hh = __shfl(my_h, e), gg = __shfl(my_g, e);              \
-      d = ci < nchunks ? (int64_t)gg * cpr + (cc - e * cpr) : -1;        \
-      if (ci < nchunks) v = src[(int64_t)hh * cpr + (cc - e * cpr)];     \
-    }
-    ECHO_COPY_LOAD(0, v0, d0) ECHO_COPY_LOAD(1, v1, d1) ECHO_COPY_LOAD(2, v2, d2)
-    ECHO_COPY_LOAD(3, v3, d3) ECHO_COPY_LOAD(4, v4, d4) ECHO_COPY_LOAD(5, v5, d5)
-    ECHO_COPY_LOAD(6, v6, d6) ECHO_COPY_LOAD(7, v7, d7)
-#undef ECHO_COPY_LOAD
-    if (d0 >= 0) dst[d0] = v0;
-    if (d1 >= 0) dst[d1] = v1;
-    if (d2 >= 0) dst[d2] = v2;
-    if (d3 >= 0) dst[d3] = v3;
-    if (d4 >= 0) dst[d4] = v4;
-    if (d5 >= 0) dst[d5] = v5;
-    if (d6 >= 0) dst[d6] = v6;
-    if (d7 >= 0) dst[d7] = v7;
-  }
-}
-
-// Part `part` of 8 of the entries [fhead, tail) once the drain is split.
-__device__ static void copy_share(const StepArgs &a, Ring &ring, int part) {
-  const int lane = lane_id();
-  const uint64_t t0 = wall_clock64();
-  while (lds_load(&ring.split) == 0) {
-    __builtin_amdgcn_s_sleep(2);
-    if ((long long)(wall_clock64() - t0) > kSpinLimit) {
-      if (lane == 0) fail(a.ws.status, ECHO_ETIMEOUT);
-      return;
-    }
-  }
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  const int f = lds_load(&ring.fhead), t = lds_load(&ring.tail);
-  const int p0 = f + (t - f) * part / (kScoreWaves + 1);
-  const int p1 = f + (t - f) * (part + 1) / (kScoreWaves + 1);
-  for (int p = p0; p < p1; p += kCopyBatch) {
-    const int n = min(kCopyBatch, p1 - p);
-    const int my_h = lane < n ? lds_load(&ring.h[(p + lane) % kRing]) : 0;
-    const int my_g = lane < n ? lds_load(&ring.g[(p + lane) % kRing]) : 0;
-    copy_batch(a, my_h, my_g, n);
-  }
-}
-
-// The copy wave: host rows -> GPU pool slots.  While scoring waves run it takes
-// the ready run of up to 16 entries at its head; when all are done it hands the
-// rest to the shared drain.
-__device__ static void copy_wave(const StepArgs &a, Ring &ring) {
-  const int lane = lane_id();
-  int head = 0;
-  while (true) {
-    if (lds_load(&ring.done) == kScoreWaves) {  // every entry is published
-      if (lane == 0) {
-        lds_store(&ring.fhead, head);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        lds_store(&ring.split, 1);
-      }
-      break;
-    }
-    const int pos = head + lane;
-    const bool ready = lane < kCopyBatch && lds_load(&ring.seq[pos % kRing]) == pos + 1;
-    const uint64_t rm = __ballot(ready);
-    const int n = rm == 0 ? 0 : __ffsll((unsigned long long)~rm) - 1;  // leading ready run
-    if (n == 0) {
-      // producers bound their own waits and always end by counting themselves done
-      __builtin_amdgcn_s_sleep(2);
-      continue;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    const int my_h = lane < n ? lds_load(&ring.h[pos % kRing]) : 0;
-    const int my_g = lane < n ? lds_load(&ring.g[pos % kRing]) : 0;
-    copy_batch(a, my_h, my_g, n);
-    head += n;
-    if (lane == 0) lds_store(&ring.head, head);
-  }
-  copy_share(a, ring, kScoreWaves);
-}
-
 // Prefetch epilogue of work item pi of request r: candidates are the tokens above
 // the threshold (`above`) whose map entry (`gq`, read while scoring) is -1.
 // Their rank in token order comes from the look-back over the request's items;
 // ranks below the cap take free-list entries idxbuf[off + rank] (while the list
-// lasts), are installed in the maps with priority t, and go to the copy wave.
-// The request's last item publishes n_cand and n_pf.
+// lasts), are installed in the maps with priority t and published, by rank, to
+// the copy waves.  The request's last item publishes n_cand, n_pf and the final
+// count the copy waves stop at.
 __device__ static void prefetch_epilogue(const StepArgs &a, const ReqInfo &r, int b, int pi,
                                          const uint64_t (&above)[kChunks],
-                                         const int (&gq)[kChunks], Ring &ring, int t,
-                                         int nfree) {
+                                         const int (&gq)[kChunks], int t, int nfree) {
   const int lane = lane_id();
   const int tau = r.tile0 + pi;
   const int s_wave = pi * kScoreTile;
@@ -478,13 +378,9 @@ __device__ static void prefetch_epilogue(const StepArgs &a, const ReqInfo &r, in
   const int E = lookback(a.sc.tstate, tau, r.tile0, c_all, a.ws.status);
   const int lim = nfree < a.n_gpu ? nfree : a.n_gpu;
   int rank0 = E;
-  uint64_t emit[kChunks];
-  int slot[kChunks];
-  int ne = 0;
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
     const uint64_t m = cand[c];
-    slot[c] = -1;
     if ((m >> lane) & 1ull) {
       const int rank = rank0 + __popcll(m & lanemask_lt());
       if (rank < r.cap) {
@@ -499,46 +395,13 @@ __device__ static void prefetch_epilogue(const StepArgs &a, const ReqInfo &r, in
           a.prio[g] = t;
           a.ws.pf_tok[(int64_t)b * a.K + rank] = s;
           a.ws.pf_slot[(int64_t)b * a.K + rank] = g;
-          slot[c] = g;
+          __hip_atomic_store(&a.sc.pfq[(int64_t)b * a.K + rank],
+                             (1ull << 63) | ((uint64_t)h << 31) | (uint64_t)g, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
         }
       }
     }
-    emit[c] = __ballot(slot[c] >= 0);
-    ne += __popcll(emit[c]);
     rank0 += __popcll(m);
-  }
-  if (ne) {  // hand the rows to the copy wave
-    int pos = 0;
-    if (lane == 0) pos = atomicAdd(&ring.tail, ne);
-    pos = __shfl(pos, 0);
-    const uint64_t tw = wall_clock64();
-    while (pos + ne - lds_load(&ring.head) > kRing) {  // wait for room
-      __builtin_amdgcn_s_sleep(1);
-      if (__any((long long)(wall_clock64() - tw) > kSpinLimit)) {
-        if (lane == 0) fail(a.ws.status, ECHO_ETIMEOUT);
-        break;
-      }
-    }
-    int p = pos;
-#pragma unroll
-    for (int c = 0; c < kChunks; ++c) {
-      if (slot[c] >= 0) {
-        const int q = (p + __popcll(emit[c] & lanemask_lt())) % kRing;
-        ring.h[q] = (int32_t)((int64_t)r.base + s_wave + c * 64 + lane);
-        ring.g[q] = slot[c];
-      }
-      p += __popcll(emit[c]);
-    }
-    __threadfence_block();
-    p = pos;
-#pragma unroll
-    for (int c = 0; c < kChunks; ++c) {
-      if (slot[c] >= 0) {
-        const int q = p + __popcll(emit[c] & lanemask_lt());
-        lds_store(&ring.seq[q % kRing], q + 1);
-      }
-      p += __popcll(emit[c]);
-    }
   }
   if (pi == r.ntiles - 1 && lane == 0) {
     const int total = E + c_all;
@@ -547,6 +410,8 @@ __device__ static void prefetch_epilogue(const StepArgs &a, const ReqInfo &r, in
     a.ws.n_cand[b] = total;
     a.ws.n_pf[b] = npf;
     if (npf) atomicAdd(&a.ws.counters[ECHO_CNT_PREFETCH], npf);
+    __hip_atomic_store(&a.sc.pfn[b], (1ull << 32) | (uint64_t)npf, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -554,8 +419,8 @@ __device__ static void prefetch_epilogue(const StepArgs &a, const ReqInfo &r, in
 // for this request (the residency of every token above the threshold is read
 // while scoring; the epilogue of item i runs one chunk into item i + wb).
 template <int HG, bool PF>
-__device__ static void score_job(const StepArgs &a, const ReqInfo &r, int b, int k, Ring &ring,
-                                 int t, int nfree) {
+__device__ static void score_job(const StepArgs &a, const ReqInfo &r, int b, int k, int t,
+                                 int nfree) {
   const int lane = lane_id();
   // Operand layout: lane l feeds row (l & 15) of A (a head) and column (l & 15)
   // of B (a token) with the 32 bytes at dims chunk .. chunk+31,
@@ -616,7 +481,7 @@ __device__ static void score_job(const StepArgs &a, const ReqInfo &r, int b, int
       if (PF) {
         above[c] = __ballot(valid && score > r.theta);
         gq[c] = a.h2g[(int64_t)r.base + (valid ? s : r.ctx - 1)];
-        if (c == 0 && have_prev) prefetch_epilogue(a, r, b, p_i, p_above, p_g, ring, t, nfree);
+        if (c == 0 && have_prev) prefetch_epilogue(a, r, b, p_i, p_above, p_g, t, nfree);
       }
     }
 
@@ -648,15 +513,15 @@ __device__ static void score_job(const StepArgs &a, const ReqInfo &r, int b, int
     if (!has_next) break;
     i = ni;
   }
-  if (PF && have_prev) prefetch_epilogue(a, r, b, p_i, p_above, p_g, ring, t, nfree);
+  if (PF && have_prev) prefetch_epilogue(a, r, b, p_i, p_above, p_g, t, nfree);
 }
 
-// A scoring wave takes jobs w, w + W, ... (W = waves of the launch); job slots
-// are numbered request by request, so a wave meets its requests in increasing
-// order and every look-back wait is on an item that a resident wave reaches
-// without waiting on a later one.
-template <int HG>
-__device__ static void score_wave(const StepArgs &a, const ReqInfo *s_req, Ring &ring, int w) {
+// A scoring wave takes jobs w, w + W, ... (W = scoring waves of the launch); job
+// slots are numbered request by request, so a wave meets its requests in
+// increasing order and every look-back wait is on an item that a resident wave
+// reaches without waiting on a later one.
+template <int HG, bool ANY_PF>
+__device__ static void score_wave(const StepArgs &a, const ReqInfo *s_req, int w) {
   const int lane = lane_id();
   const int S = a.sc.misc[M_SLOTS];
   const int W = a.score_waves;
@@ -667,49 +532,53 @@ __device__ static void score_wave(const StepArgs &a, const ReqInfo *s_req, Ring 
     const int b = __popcll(__ballot(lane < a.B && send <= slot));
     const ReqInfo r = s_req[b];
     const int k = slot - r.slot0;
-    if (r.active)
-      score_job<HG, true>(a, r, b, k, ring, t, nfree);
+    if (ANY_PF && r.active)
+      score_job<HG, true>(a, r, b, k, t, nfree);
     else
-      score_job<HG, false>(a, r, b, k, ring, t, nfree);
+      score_job<HG, false>(a, r, b, k, t, nfree);
   }
 }
 
-template <int HG>
+// The first score_blocks workgroups score, the rest copy prefetched rows (until
+// scoring ends, when the copy continues in the step's next kernels, else to the
+// end).  ANY_PF = false (threshold +inf) compiles the prefetch path out.
+template <int HG, bool ANY_PF>
 __global__ __launch_bounds__(512) void k_score(StepArgs a) {
   __shared__ ReqInfo s_req[kMaxBatch];
-  __shared__ Ring ring;
+  __shared__ int s_left;
   if (failed(a.ws.status)) return;
   const int tid = threadIdx.x;
   for (int i = tid; i < a.B; i += blockDim.x) s_req[i] = a.sc.req[i];
-  for (int i = tid; i < kRing; i += blockDim.x) ring.seq[i] = 0;
-  if (tid == 0) {
-    ring.tail = 0;
-    ring.head = 0;
-    ring.done = 0;
-    ring.split = 0;
-    ring.fhead = 0;
-  }
+  if (tid == 0) s_left = kScoreWaves;
   __syncthreads();
   const int wid = tid / kWave;
-  if (wid == kScoreWaves) {
-    copy_wave(a, ring);
-    return;
+  if ((int)blockIdx.x < a.score_blocks) {
+    score_wave<HG, ANY_PF>(a, s_req, blockIdx.x * kScoreWaves + wid);
+    if (lane_id() == 0 && atomicSub(&s_left, 1) == 1)
+      __hip_atomic_fetch_add(&a.sc.misc[M_SCORE_DONE], 1, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+  } else if (ANY_PF) {
+    copy_worker(a, s_req, (blockIdx.x - a.score_blocks) * kScoreWaves + wid, 0, 1,
+                a.copy_handoff ? &a.sc.misc[M_SCORE_DONE] : nullptr, a.score_blocks);
   }
-  score_wave<HG>(a, s_req, ring, blockIdx.x * kScoreWaves + wid);
-  __threadfence_block();
-  if (lane_id() == 0) atomicAdd(&ring.done, 1);
-  copy_share(a, ring, wid);
+}
+
+template <bool ANY_PF>
+static void launch_score_hg(const StepArgs &a, int grid, hipStream_t s) {
+  switch ((a.H + 15) / 16) {
+    case 1: hipLaunchKernelGGL((k_score<1, ANY_PF>), dim3(grid), dim3(512), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_score<2, ANY_PF>), dim3(grid), dim3(512), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((k_score<3, ANY_PF>), dim3(grid), dim3(512), 0, s, a); break;
+    default: hipLaunchKernelGGL((k_score<4, ANY_PF>), dim3(grid), dim3(512), 0, s, a); break;
+  }
 }
 
 hipError_t launch_score(const StepArgs &a, hipStream_t s) {
-  const int hg = (a.H + 15) / 16;
-  const int grid = a.score_waves / kScoreWaves;
-  switch (hg) {
-    case 1: hipLaunchKernelGGL(k_score<1>, dim3(grid), dim3(512), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(k_score<2>, dim3(grid), dim3(512), 0, s, a); break;
-    case 3: hipLaunchKernelGGL(k_score<3>, dim3(grid), dim3(512), 0, s, a); break;
-    default: hipLaunchKernelGGL(k_score<4>, dim3(grid), dim3(512), 0, s, a); break;
-  }
+  const int grid = a.score_blocks + a.copy_waves / kScoreWaves;
+  if (a.mode == ECHO_THETA_POS_INF)
+    launch_score_hg<false>(a, grid, s);
+  else
+    launch_score_hg<true>(a, grid, s);
   return hipGetLastError();
 }
 

@@ -21,6 +21,7 @@
 // more) needs the exact (priority, slot) select, done by one workgroup between
 // two more barriers.  A second look-back over the workgroups ranks the free
 // slots for the allocation, and each workgroup copies the rows it allocated.
+#include "copy.h"
 #include "select.h"
 
 namespace echo {
@@ -77,7 +78,12 @@ __global__ __launch_bounds__(kSelThreads) void k_manage(StepArgs a) {
   __shared__ int s_bin, s_below, s_E;
   if (failed(a.ws.status)) return;
   const int tid = threadIdx.x;
-  const int blk = blockIdx.x, nblk = gridDim.x;
+  const int blk = blockIdx.x, nblk = a.sc.atiles;
+  if (blk >= nblk) {  // copy workgroup: finish the step's prefetch copy, two waves per copy wave
+    const int g = (blk - nblk) * (kSelThreads / kWave) + tid / kWave;
+    copy_worker(a, a.sc.req, g % a.copy_waves, g / a.copy_waves, 2, nullptr, 0);
+    return;
+  }
   const int t = a.ctl[ECHO_CTL_STEP];
   const int g0 = blk * kSlotTile + tid * 4;
 
@@ -276,7 +282,10 @@ __global__ __launch_bounds__(kSelThreads) void k_manage(StepArgs a) {
 }
 
 hipError_t launch_manage(const StepArgs &a, bool recall, bool advance, hipStream_t s) {
-  const dim3 grid(a.sc.atiles), block(kSelThreads);
+  // the first atiles workgroups manage slots (all resident, they meet at barriers);
+  // with a copy hand-off, more workgroups finish the prefetch copy beside them
+  const int extra = a.copy_handoff ? 2 * a.copy_waves / (kSelThreads / kWave) : 0;
+  const dim3 grid(a.sc.atiles + extra), block(kSelThreads);
   if (recall && advance)
     hipLaunchKernelGGL((k_manage<true, true>), grid, block, 0, s, a);
   else if (recall)

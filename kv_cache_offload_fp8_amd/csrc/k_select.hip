@@ -19,6 +19,7 @@
 // Protection (review, "Core method / in-graph per-layer cache management":
 // recall first looks the selected tokens up in the map) then sets priority t on
 // every resident selected token and lists the misses in token order.
+#include "copy.h"
 #include "select.h"
 
 namespace echo {
@@ -118,8 +119,13 @@ __global__ __launch_bounds__(kSelThreads) void k_topk(StepArgs a) {
   __shared__ uint64_t shu[kSelThreads / kWave];
   __shared__ int s_bin, s_below, s_cnt;
   if (failed(a.ws.status)) return;
-  const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
+  if ((int)blockIdx.x >= a.B) {  // copy workgroup: prefetched rows, until selection ends
+    copy_worker(a, a.sc.req, ((int)blockIdx.x - a.B) * (kSelThreads / kWave) + wid, 0, 1,
+                &a.sc.misc[M_TOPK_DONE], a.B);
+    return;
+  }
+  const int b = blockIdx.x;
   const ReqInfo r = a.sc.req[b];
   const int ctx = r.ctx;
   const int K = a.K;
@@ -294,6 +300,9 @@ __global__ __launch_bounds__(kSelThreads) void k_topk(StepArgs a) {
     __syncthreads();
     protect_request(a, b, s_sel, nsel, sh);
   }
+  __syncthreads();
+  if (tid == 0)
+    __hip_atomic_fetch_add(&a.sc.misc[M_TOPK_DONE], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __global__ __launch_bounds__(kSelThreads) void k_protect(StepArgs a) {
@@ -313,10 +322,13 @@ __global__ __launch_bounds__(kSelThreads) void k_protect(StepArgs a) {
 
 hipError_t launch_topk(const StepArgs &a, bool protect, hipStream_t s) {
   if (a.B == 0) return hipSuccess;
+  // copy workgroups continue the indexer's prefetch copy (one wave per copy wave)
+  const int extra = a.copy_handoff ? a.copy_waves / (kSelThreads / kWave) : 0;
+  const dim3 grid(a.B + extra);
   if (protect)
-    hipLaunchKernelGGL(k_topk<true>, dim3(a.B), dim3(kSelThreads), 0, s, a);
+    hipLaunchKernelGGL(k_topk<true>, grid, dim3(kSelThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(k_topk<false>, dim3(a.B), dim3(kSelThreads), 0, s, a);
+    hipLaunchKernelGGL(k_topk<false>, grid, dim3(kSelThreads), 0, s, a);
   return hipGetLastError();
 }
 

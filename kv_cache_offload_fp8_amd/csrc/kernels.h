@@ -32,7 +32,10 @@ struct StepArgs {
   float *guard_upd;  // selection guard to refresh in the top-k epilogue, or null
   int32_t mode;
   // launch shapes, fixed by the dims so that a captured graph stays valid
-  int32_t score_waves;  // scoring waves of the indexer launch (7 per workgroup)
+  int32_t score_blocks;  // indexer workgroups that score (the rest copy)
+  int32_t score_waves;   // score_blocks * kScoreWaves
+  int32_t copy_waves;    // copy workgroups * kScoreWaves
+  int32_t copy_handoff;  // 1: the copy continues in the top-k and management kernels
   // workspace
   echo_ws_t ws;
   Scratch sc;
@@ -47,8 +50,9 @@ enum {
   BEGIN_CLR_MANAGE = 16  // eviction histogram, look-back states, barriers, counters
 };
 
-// Workgroups of the indexer launch for these dims (one per compute unit at most).
-int score_grid(const echo_dims_t &d);
+// Scoring and copying workgroups of the indexer launch for these dims (together at
+// most one per compute unit, so that all of them are resident at once).
+void index_grid(const echo_dims_t &d, int *score_blocks, int *copy_blocks);
 // Compute units of the current device (cached per device).
 int device_cus();
 
