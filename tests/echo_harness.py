@@ -164,6 +164,18 @@ class Rig:
             gp = self.layer.gpu_kv.cpu().numpy().view(np.uint16)
             assert np.array_equal(gp, self.orc.pool), (tag, "pool bytes")
 
+    def gathered(self):
+        """GPU-pool rows of every request's selected tokens, in selection order (what the
+        sparse attention of the step would read)."""
+        torch.cuda.current_stream().synchronize()
+        n_sel = self.ws.n_sel[: self.B].cpu().numpy()
+        slots = self.ws.sel_slot[: self.B].cpu().numpy()
+        rows = []
+        for b in range(self.B):
+            g = torch.as_tensor(slots[b, : int(n_sel[b])].astype(np.int64), device="cuda")
+            rows.append(self.layer.gpu_kv[g].cpu().numpy().view(np.uint16))
+        return rows
+
     def hit_rates(self):
         hr = []
         for out, _ in self.history:
