@@ -23,10 +23,11 @@ int device_cus() {
   return cache[dev];
 }
 
-void index_grid(const echo_dims_t &d, int *score_blocks, int *copy_blocks) {
+void index_grid(const echo_dims_t &d, bool with_copy, int *score_blocks, int *copy_blocks) {
   const int cus = device_cus();
   int gc = cus / 4 < kCopyBlocks ? cus / 4 : kCopyBlocks;
   if (gc < 1) gc = 1;
+  if (!with_copy) gc = 0;  // prefetch off: every workgroup scores
   const int64_t max_tiles =
       (int64_t)d.max_batch * (((int64_t)d.max_ctx + kScoreTile - 1) / kScoreTile);
   int64_t gs = (max_tiles + kScoreWaves - 1) / kScoreWaves;
@@ -61,7 +62,7 @@ int check_dims(const echo_dims_t *d) {
 int check_launch(const echo_dims_t *d) {
   const int64_t atiles = ((int64_t)d->n_gpu + kSlotTile - 1) / kSlotTile;
   int gs = 1, gc = 1;
-  index_grid(*d, &gs, &gc);
+  index_grid(*d, true, &gs, &gc);
   const int64_t copy_blocks = 2 * (int64_t)gc * kScoreWaves / 16;  // 16-wave workgroups
   if (atiles + copy_blocks > device_cus()) return ECHO_EUNSUPPORTED;
   return ECHO_OK;
@@ -167,7 +168,7 @@ StepArgs make_args(const echo_dims_t &d, const echo_layer_t *l, const echo_batch
   a.guard_upd = nullptr;
   a.mode = mode;
   int gs = 1, gc = 1;
-  index_grid(d, &gs, &gc);
+  index_grid(d, mode != ECHO_THETA_POS_INF, &gs, &gc);
   a.score_blocks = gs;
   a.score_waves = gs * kScoreWaves;
   a.copy_waves = gc * kScoreWaves;

@@ -233,24 +233,29 @@ __device__ inline uint64_t block_max_u64(uint64_t v, uint64_t *sh) {
 
 // ------------------------------------------------------ decoupled look-back
 // Called by one whole wave.  Work item `tau` of a segment that starts at item
-// `seg0` publishes its own count `c`, walks back over earlier items of the same
-// segment (aggregates until an inclusive prefix is found) and publishes its
-// inclusive prefix.  Returns the exclusive prefix of `tau`.  Callers guarantee
-// that every earlier item is owned by a resident wave that reaches it without
-// waiting on a later item, so the wait always ends; a 1 s guard turns a broken
-// invariant into ECHO_ETIMEOUT instead of a hang.  Only the state words cross
-// workgroups, as relaxed device-scope atomics: no cache flush is needed.
-__device__ inline int lookback(uint64_t *st, int tau, int seg0, int c, int32_t *status) {
-  const int l = lane_id();
-  if (tau == seg0) {
-    if (l == 0)
-      __hip_atomic_store(&st[tau], kFlagP | (uint32_t)c, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-    return 0;
-  }
-  if (l == 0)
-    __hip_atomic_store(&st[tau], kFlagA | (uint32_t)c, __ATOMIC_RELAXED,
+// `seg0` publishes its own count `c` (lb_publish; the segment's first item
+// publishes it as its inclusive prefix), and later walks back over earlier items
+// of the same segment (aggregates until an inclusive prefix is found), publishes
+// its inclusive prefix and gets its exclusive prefix (lb_resolve).  A caller may
+// do other work between the two calls, so that the items before it have
+// published by the time it resolves.  Callers guarantee that every earlier item
+// is owned by a resident wave that publishes it without waiting on a later item,
+// so the wait always ends; a 1 s guard turns a broken invariant into
+// ECHO_ETIMEOUT instead of a hang.  Only the state words cross workgroups, as
+// relaxed device-scope atomics: no cache flush is needed.
+__device__ inline void lb_publish(uint64_t *st, int tau, int seg0, int c) {
+  if (lane_id() == 0)
+    __hip_atomic_store(&st[tau], (tau == seg0 ? kFlagP : kFlagA) | (uint32_t)c, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Second half of the look-back: item `tau` (whose count `c` lb_publish has
+// published) sums the aggregates of the items before it back to the nearest
+// inclusive prefix, publishes its own inclusive prefix and returns the exclusive
+// one.  Only the states up to that nearest prefix are waited for.
+__device__ inline int lb_resolve(uint64_t *st, int tau, int seg0, int c, int32_t *status) {
+  if (tau == seg0) return 0;
+  const int l = lane_id();
   int E = 0;
   int j = tau - 1;
   const uint64_t t0 = wall_clock64();
@@ -260,8 +265,14 @@ __device__ inline int lookback(uint64_t *st, int tau, int seg0, int c, int32_t *
     uint64_t v = idx >= seg0 ? __hip_atomic_load(&st[idx], __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT)
                              : kFlagP;
-    while (!__all((v >> 32) != 0)) {
-      if ((v >> 32) == 0)
+    uint64_t pm;
+    while (true) {
+      const uint64_t fm = __ballot((v >> 32) != 0);
+      pm = __ballot((v >> 32) == 2);
+      // lanes that matter: up to the nearest inclusive prefix, or all of them
+      const uint64_t need = pm ? ((pm & (0 - pm)) << 1) - 1 : ~0ull;
+      if ((fm & need) == need) break;
+      if (((v >> 32) == 0) && ((need >> l) & 1ull))
         v = __hip_atomic_load(&st[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (__any((long long)(wall_clock64() - t0) > kSpinLimit) || failed(status)) {
         timed_out = true;  // or another workgroup already failed: stop waiting
@@ -269,7 +280,6 @@ __device__ inline int lookback(uint64_t *st, int tau, int seg0, int c, int32_t *
       }
     }
     if (timed_out) break;
-    const uint64_t pm = __ballot((v >> 32) == 2);
     const int val = (int)(uint32_t)v;
     if (pm) {
       const int first = __ffsll((unsigned long long)pm) - 1;
@@ -286,6 +296,11 @@ __device__ inline int lookback(uint64_t *st, int tau, int seg0, int c, int32_t *
     __hip_atomic_store(&st[tau], kFlagP | (uint32_t)(E + c), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
   return E;
+}
+
+__device__ inline int lookback(uint64_t *st, int tau, int seg0, int c, int32_t *status) {
+  lb_publish(st, tau, seg0, c);
+  return lb_resolve(st, tau, seg0, c, status);
 }
 
 // ------------------------------------------------------------ grid barrier

@@ -83,6 +83,7 @@ __device__ inline void copy_worker(const StepArgs &a, const ReqInfo *req, int w,
     const ReqInfo &r = req[b];
     if (!r.active || r0 >= r.cap) continue;
     uint64_t t0 = wall_clock64();
+    int nap = 1;  // polls back off while nothing is ready: idle waves must not flood memory
     while (true) {
       if (stop && __hip_atomic_load(stop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
                       stop_target) {
@@ -118,9 +119,11 @@ __device__ inline void copy_worker(const StepArgs &a, const ReqInfo *req, int w,
                              __HIP_MEMORY_SCOPE_AGENT);
         done += ready;
         t0 = wall_clock64();
+        nap = 1;
         continue;
       }
-      __builtin_amdgcn_s_sleep(4);
+      for (int z = 0; z < nap; ++z) __builtin_amdgcn_s_sleep(8);  // 512 cycles each
+      nap = nap < 8 ? 2 * nap : 8;
       if (failed(a.ws.status)) return;
       if ((long long)(wall_clock64() - t0) > kSpinLimit) {
         if (lane == 0) fail(a.ws.status, ECHO_ETIMEOUT);

@@ -38,12 +38,14 @@
 // Request b gets wb scoring waves (chosen so that no wave takes more 256-token
 // work items than any other); its k-th wave scores items k, k + wb, k + 2wb, ...
 // in order.  A wave therefore loads its request's query once, takes no ticket
-// and touches no shared counter, and the items of one request are scored in
-// step by neighbouring waves, so the decoupled look-back that ranks prefetch
-// candidates in token order finds its predecessors done or nearly done.  The
-// prefetch epilogue of an item (residency check, look-back, map installs) runs
-// one chunk into the next item, after that item's loads are issued, so its map
-// lookups never drain the K stream.  Installed rows are published by rank as
+// and touches no shared counter (device-scope atomics on one address serialize:
+// a ticket counter per request doubled the scoring time), and the items of one
+// request are scored in step by neighbouring waves.  The prefetch epilogue of an
+// item (residency check, decoupled look-back, map installs) runs during the
+// wave's next item: the item's candidate count is published at that item's first
+// chunk and its rank resolved two chunks later, when the items before it have
+// published theirs, so the look-back rarely waits and its lookups never drain
+// the K stream.  Installed rows are published by rank as
 // self-validating 64-bit entries; the copy workgroups read them from mapped host
 // memory into the GPU pool while scoring continues -- the MI355X form of the
 // pages' dedicated prefetch role inside the indexer pipeline.  The copy runs on
@@ -149,60 +151,51 @@ __device__ static void build_request_table(const StepArgs &a, int roles) {
   }
 }
 
-// Stage one request's query for the scoring kernel: per head j a power-of-two
-// scale 2^e puts max |q_j| in [128, 256); q_hi = e4m3(q*2^e),
+// Stage a quarter of one request's query (16 heads) for the scoring kernel: per
+// head j a power-of-two scale 2^e puts max |q_j| in [128, 256); q_hi = e4m3(q*2^e),
 // q_lo = e4m3(q*2^e - q_hi), stored [64][128] zero-padded, and the weight
-// w_j * 2^-e (zero for padded heads).  Block of 256 threads, thread =
-// (head, quarter of the dims).
-__device__ static void stage_query(const StepArgs &a, int b) {
+// w_j * 2^-e (zero for padded heads).  Block of 256 threads: thread = (head of
+// the quarter, 8 dims); the 16 threads of a head are 16 neighbouring lanes.
+__device__ static void stage_query(const StepArgs &a, int b, int quarter) {
   const int tid = threadIdx.x;
-  const int j = tid >> 2, part = tid & 3;
+  const int j = quarter * 16 + (tid >> 4), d0 = (tid & 15) * 8;
   const int t = a.ctl[ECHO_CTL_STEP];
   const int slot = (int)((unsigned)t % (unsigned)a.q_ring);
   const uint16_t *src = a.q + ((int64_t)slot * a.B + b) * a.H * a.D;
-  float x[32];
-  float amax = 0.0f;
-  // 32 bf16 = four 16-byte loads (D is a multiple of 32, so a part is all in or all out)
-  const bool in_part = j < a.H && part * 32 < a.D;
-  const uint4 *qv = (const uint4 *)(src + (in_part ? j * a.D + part * 32 : 0));
+  // 8 bf16 = one 16-byte load (D is a multiple of 32: a group is all in or all out)
+  const bool in = j < a.H && d0 < a.D;
+  const uint4 w4 = in ? *(const uint4 *)(src + j * a.D + d0) : make_uint4(0, 0, 0, 0);
+  const uint32_t wd[4] = {w4.x, w4.y, w4.z, w4.w};
+  float x[8];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const uint4 w4 = in_part ? qv[u] : make_uint4(0, 0, 0, 0);
-    const uint32_t wd[4] = {w4.x, w4.y, w4.z, w4.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      x[u * 8 + 2 * k] = __uint_as_float(wd[k] << 16);
-      x[u * 8 + 2 * k + 1] = __uint_as_float(wd[k] & 0xFFFF0000u);
-    }
+  for (int k = 0; k < 4; ++k) {
+    x[2 * k] = __uint_as_float(wd[k] << 16);
+    x[2 * k + 1] = __uint_as_float(wd[k] & 0xFFFF0000u);
   }
+  float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
-  amax = fmaxf(amax, __shfl_xor(amax, 1));
-  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
   int e = 0;
   if (amax > 0.0f) {
     int E;
     frexpf(amax, &E);  // amax = m * 2^E, m in [0.5, 1)
     e = min(64, max(-64, 8 - E));
   }
-  uint32_t whi[8], wlo[8];
+  uint32_t whi[2] = {0, 0}, wlo[2] = {0, 0};
 #pragma unroll
-  for (int i = 0; i < 8; ++i) whi[i] = wlo[i] = 0;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
+  for (int i = 0; i < 8; ++i) {
     const float xs = ldexpf(x[i], e);
     const uint8_t h8 = e4m3_encode(xs);
     const uint8_t l8 = e4m3_encode(xs - e4m3_decode(h8));
     whi[i >> 2] |= (uint32_t)h8 << (8 * (i & 3));
     wlo[i >> 2] |= (uint32_t)l8 << (8 * (i & 3));
   }
-  uint4 *hv = (uint4 *)(a.sc.qhi + ((int64_t)b * kHeadsPad + j) * kDimPad + part * 32);
-  uint4 *lv = (uint4 *)(a.sc.qlo + ((int64_t)b * kHeadsPad + j) * kDimPad + part * 32);
-  hv[0] = make_uint4(whi[0], whi[1], whi[2], whi[3]);
-  hv[1] = make_uint4(whi[4], whi[5], whi[6], whi[7]);
-  lv[0] = make_uint4(wlo[0], wlo[1], wlo[2], wlo[3]);
-  lv[1] = make_uint4(wlo[4], wlo[5], wlo[6], wlo[7]);
-  if (part == 0)
+  const int64_t o = ((int64_t)b * kHeadsPad + j) * kDimPad + d0;
+  *(uint2 *)(a.sc.qhi + o) = make_uint2(whi[0], whi[1]);
+  *(uint2 *)(a.sc.qlo + o) = make_uint2(wlo[0], wlo[1]);
+  if (d0 == 0)
     a.sc.wsc[(int64_t)b * kHeadsPad + j] = j < a.H ? ldexpf(a.w[(int64_t)b * a.H + j], -e) : 0.0f;
 }
 
@@ -237,11 +230,11 @@ __global__ __launch_bounds__(256) void k_begin(StepArgs a, int roles) {
   }
   blk -= 1;
   if (roles & BEGIN_Q) {
-    if (blk < a.B) {
-      stage_query(a, blk);
+    if (blk < 4 * a.B) {
+      stage_query(a, blk >> 2, blk & 3);
       return;
     }
-    blk -= a.B;
+    blk -= 4 * a.B;
   }
   if (blk >= kBeginClearBlocks) return;
   const int64_t i0 = (int64_t)blk * blockDim.x + threadIdx.x;
@@ -259,7 +252,7 @@ __global__ __launch_bounds__(256) void k_begin(StepArgs a, int roles) {
 }
 
 hipError_t launch_begin(const StepArgs &a, int roles, hipStream_t s) {
-  const int grid = 1 + ((roles & BEGIN_Q) ? a.B : 0) + kBeginClearBlocks;
+  const int grid = 1 + ((roles & BEGIN_Q) ? 4 * a.B : 0) + kBeginClearBlocks;
   hipLaunchKernelGGL(k_begin, dim3(grid), dim3(256), 0, s, a, roles);
   return hipGetLastError();
 }
@@ -303,28 +296,30 @@ constexpr int kChunks = kScoreTile / 64;  // 64-token chunks per work item
 // r, s0 a multiple of 64): sub-tile u holds tokens s0 + 16u .. +15; this lane
 // feeds token s0 + 16u + (lane & 15) with dims 32c .. 32c+31, c = lane >> 4, read
 // as two 16-byte pieces at 16*lane and 8*D + 16*lane inside the token's 16-row
-// group.  The loads are branch-free -- tokens past the context and dims past D
-// read an in-bounds address of the request's last group and are zeroed by a
-// select -- so the compiler counts them exactly and keeps the next chunk in
-// flight (a branch around a load makes it wait for all of them).
+// group.  The loads go straight into the operand registers, with no select
+// after them, so the compiler waits for them only where the MFMA reads them and
+// the next chunk stays in flight while this one computes.  Tokens past the
+// context read the request's last group (in bounds; their scores are dropped),
+// and lanes whose dims lie past D read the same token's first 32 dims, which
+// meet the zero padding of q (an exact 0 for any finite e4m3 byte).
 __device__ inline void load_k_chunk(const StepArgs &a, const ReqInfo &r, int s0, int lane,
                                     v8i (&kb)[4]) {
   const bool dim_ok = 32 * (lane >> 4) < a.D;
   const int lp = dim_ok ? lane : (lane & 15);
   const int glast = (r.ctx - 1) & ~15;
   const int half = 8 * a.D;
+  // wave-uniform 64-bit group address + 32-bit lane offset: the loads use the
+  // scalar-base addressing form and need no per-lane 64-bit arithmetic
+  const uint32_t lo = (uint32_t)lp * 16u;
+  const int s0u = __builtin_amdgcn_readfirstlane(s0);
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const int st = s0 + 16 * u;
-    const bool ok = dim_ok && st + (lane & 15) < r.ctx;
+    const int st = s0u + 16 * u;
     const int sg = st < r.ctx ? st : glast;
-    const uint8_t *p = a.kidx + ((int64_t)r.base + sg) * a.D + lp * 16;
-    const v4i x0 = __builtin_nontemporal_load((const v4i *)p);
-    const v4i x1 = __builtin_nontemporal_load((const v4i *)(p + half));
-    v8i x;
-    x[0] = ok ? x0[0] : 0; x[1] = ok ? x0[1] : 0; x[2] = ok ? x0[2] : 0; x[3] = ok ? x0[3] : 0;
-    x[4] = ok ? x1[0] : 0; x[5] = ok ? x1[1] : 0; x[6] = ok ? x1[2] : 0; x[7] = ok ? x1[3] : 0;
-    kb[u] = x;
+    const uint8_t *g = a.kidx + ((int64_t)r.base + sg) * a.D;
+    const v4i x0 = __builtin_nontemporal_load((const v4i *)(g + lo));
+    const v4i x1 = __builtin_nontemporal_load((const v4i *)(g + (lo + (uint32_t)half)));
+    kb[u] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
   }
 }
 
@@ -344,8 +339,11 @@ __device__ inline float score_chunk(const v8i (&kb)[4], const v8i (&qa)[HG][2],
                                                              0, 0);
       acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[hg][1], kb[u], acc, 0, 0, 0, 0,
                                                              0, 0);
+      // ReLU as an integer max on the bits: one instruction, where fmaxf also
+      // quiets NaNs with a second one (an MFMA sum of finite products is finite)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) v += wr[hg][rr] * fmaxf(acc[rr], 0.0f);
+      for (int rr = 0; rr < 4; ++rr)
+        v += wr[hg][rr] * __int_as_float(max(__float_as_int(acc[rr]), 0));
     }
     v += __shfl_xor(v, 16);
     v += __shfl_xor(v, 32);
@@ -355,55 +353,74 @@ __device__ inline float score_chunk(const v8i (&kb)[4], const v8i (&qa)[HG][2],
   return sel == 0 ? sc4[0] : sel == 1 ? sc4[1] : sel == 2 ? sc4[2] : sc4[3];
 }
 
-// Prefetch epilogue of work item pi of request r: candidates are the tokens above
-// the threshold (`above`) whose map entry (`gq`, read while scoring) is -1.
-// Their rank in token order comes from the look-back over the request's items;
-// ranks below the cap take free-list entries idxbuf[off + rank] (while the list
-// lasts), are installed in the maps with priority t and published, by rank, to
-// the copy waves.  The request's last item publishes n_cand, n_pf and the final
-// count the copy waves stop at.
-__device__ static void prefetch_epilogue(const StepArgs &a, const ReqInfo &r, int b, int pi,
-                                         const uint64_t (&above)[kChunks],
-                                         const int (&gq)[kChunks], int t, int nfree) {
+// Prefetch epilogue of work item pi of request r, in two parts.  Candidates are
+// the tokens above the threshold (`above`) whose map entry (`gq`, read while
+// scoring) is -1; pf_publish counts them and publishes the count for the
+// look-back over the request's items.  pf_install, a few chunks later, gets
+// their rank in token order from the look-back; ranks below the cap take
+// free-list entries idxbuf[off + rank] (while the list lasts), are installed in
+// the maps with priority t and published, by rank, to the copy waves.  The
+// request's last item publishes n_cand, n_pf and the final count the copy waves
+// stop at.
+__device__ inline int pf_publish(const StepArgs &a, const ReqInfo &r, int pi,
+                                 const uint64_t (&above)[kChunks], const int (&gq)[kChunks],
+                                 uint64_t (&cand)[kChunks]) {
   const int lane = lane_id();
-  const int tau = r.tile0 + pi;
-  const int s_wave = pi * kScoreTile;
-  uint64_t cand[kChunks];
   int c_all = 0;
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
     cand[c] = __ballot(((above[c] >> lane) & 1ull) && gq[c] == -1);
     c_all += __popcll(cand[c]);
   }
-  const int E = lookback(a.sc.tstate, tau, r.tile0, c_all, a.ws.status);
+  lb_publish(a.sc.tstate, r.tile0 + pi, r.tile0, c_all);
+  return c_all;
+}
+
+__device__ static void pf_install(const StepArgs &a, const ReqInfo &r, int b, int pi,
+                                  const uint64_t (&cand)[kChunks], int c_all, int t,
+                                  int nfree) {
+  const bool last = pi == r.ntiles - 1;
+  // An item without candidates needs no rank; later items sum through its
+  // published count.  Only the request's last item must always resolve.
+  if (c_all == 0 && !last) return;
+  const int lane = lane_id();
+  const int s_wave = pi * kScoreTile;
+  const int E = lb_resolve(a.sc.tstate, r.tile0 + pi, r.tile0, c_all, a.ws.status);
   const int lim = nfree < a.n_gpu ? nfree : a.n_gpu;
-  int rank0 = E;
+  if (c_all > 0) {
+    // this lane's candidates (at most one per chunk): rank, free-list position and
+    // slot; the free-list reads are issued together, without branches
+    int rank[kChunks], gv[kChunks];
+    bool take[kChunks];
+    int rank0 = E;
 #pragma unroll
-  for (int c = 0; c < kChunks; ++c) {
-    const uint64_t m = cand[c];
-    if ((m >> lane) & 1ull) {
-      const int rank = rank0 + __popcll(m & lanemask_lt());
-      if (rank < r.cap) {
-        const int j = r.off + rank;
-        const int g = j < lim ? a.idxbuf[j] : -1;
-        if (g >= 0 && g < a.n_gpu) {
-          const int s = s_wave + c * 64 + lane;
-          const int64_t h = (int64_t)r.base + s;
-          a.h2g[h] = g;
-          a.g2h[g] = (int32_t)h;
-          a.freef[g] = 0;
-          a.prio[g] = t;
-          a.ws.pf_tok[(int64_t)b * a.K + rank] = s;
-          a.ws.pf_slot[(int64_t)b * a.K + rank] = g;
-          __hip_atomic_store(&a.sc.pfq[(int64_t)b * a.K + rank],
-                             (1ull << 63) | ((uint64_t)h << 31) | (uint64_t)g, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-        }
+    for (int c = 0; c < kChunks; ++c) {
+      const uint64_t m = cand[c];
+      rank[c] = rank0 + __popcll(m & lanemask_lt());
+      take[c] = ((m >> lane) & 1ull) && rank[c] < r.cap && r.off + rank[c] < lim;
+      rank0 += __popcll(m);
+    }
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) gv[c] = a.idxbuf[take[c] ? r.off + rank[c] : 0];
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int g = gv[c];
+      if (take[c] && g >= 0 && g < a.n_gpu) {
+        const int s = s_wave + c * 64 + lane;
+        const int64_t h = (int64_t)r.base + s;
+        a.h2g[h] = g;
+        a.g2h[g] = (int32_t)h;
+        a.freef[g] = 0;
+        a.prio[g] = t;
+        a.ws.pf_tok[(int64_t)b * a.K + rank[c]] = s;
+        a.ws.pf_slot[(int64_t)b * a.K + rank[c]] = g;
+        __hip_atomic_store(&a.sc.pfq[(int64_t)b * a.K + rank[c]],
+                           (1ull << 63) | ((uint64_t)h << 31) | (uint64_t)g, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-    rank0 += __popcll(m);
   }
-  if (pi == r.ntiles - 1 && lane == 0) {
+  if (last && lane == 0) {
     const int total = E + c_all;
     const int take = min(r.cap, total);
     const int npf = max(0, min(take, lim - r.off));
@@ -415,9 +432,15 @@ __device__ static void prefetch_epilogue(const StepArgs &a, const ReqInfo &r, in
   }
 }
 
-// One scoring job: work items k, k + wb, ... of request b.  PF: prefetch is on
-// for this request (the residency of every token above the threshold is read
-// while scoring; the epilogue of item i runs one chunk into item i + wb).
+// Chunk of the next item at which an item's epilogue resolves its rank: the
+// items before it publish their counts at chunk 0, so the look-back rarely waits.
+constexpr int kInstallChunk = 2;
+
+// One scoring job: work items k, k + wb, k + 2wb, ... of request b.  PF:
+// prefetch is on for this request (the residency of every token above the
+// threshold is read while scoring; the epilogue of an item runs during the
+// job's next item: its count is published at chunk 0, its rank resolved and its
+// rows installed at kInstallChunk).
 template <int HG, bool PF>
 __device__ static void score_job(const StepArgs &a, const ReqInfo &r, int b, int k, int t,
                                  int nfree) {
@@ -448,28 +471,31 @@ __device__ static void score_job(const StepArgs &a, const ReqInfo &r, int b, int
   int i = k;
   load_k_chunk(a, r, i * kScoreTile, lane, kb[0]);
   bool have_prev = false;
-  int p_i = 0;
-  uint64_t p_above[kChunks];
+  int p_i = 0, p_call = 0;
+  uint64_t p_above[kChunks], p_cand[kChunks];
   int p_g[kChunks];
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
     p_above[c] = 0;
+    p_cand[c] = 0;
     p_g[c] = 0;
   }
   while (true) {
-    const int ni = i + r.wb;
-    const bool has_next = ni < r.ntiles;
     const int s_wave = i * kScoreTile;
     const int tau = r.tile0 + i;
+    const int ni = i + r.wb;
     uint64_t above[kChunks], gsel[kChunks];
     uint32_t keys[kChunks];
     int gq[kChunks];
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
-      if (c + 1 < kChunks)
+      if (c + 1 < kChunks) {
         load_k_chunk(a, r, s_wave + (c + 1) * 64, lane, kb[(c + 1) & 1]);
-      else if (has_next)
-        load_k_chunk(a, r, ni * kScoreTile, lane, kb[0]);
+      } else {
+        // unconditional (the last item reloads its own first chunk): a load under
+        // a branch would make the compiler drain every load before the join
+        load_k_chunk(a, r, (ni < r.ntiles ? ni : i) * kScoreTile, lane, kb[0]);
+      }
       const float score = score_chunk<HG>(kb[c & 1], qa, wr, lane);
       const int s = s_wave + c * 64 + lane;
       const bool valid = s < r.ctx;
@@ -481,7 +507,8 @@ __device__ static void score_job(const StepArgs &a, const ReqInfo &r, int b, int
       if (PF) {
         above[c] = __ballot(valid && score > r.theta);
         gq[c] = a.h2g[(int64_t)r.base + (valid ? s : r.ctx - 1)];
-        if (c == 0 && have_prev) prefetch_epilogue(a, r, b, p_i, p_above, p_g, t, nfree);
+        if (c == 0 && have_prev) p_call = pf_publish(a, r, p_i, p_above, p_g, p_cand);
+        if (c == kInstallChunk && have_prev) pf_install(a, r, b, p_i, p_cand, p_call, t, nfree);
       }
     }
 
@@ -510,10 +537,27 @@ __device__ static void score_job(const StepArgs &a, const ReqInfo &r, int b, int
       }
       have_prev = true;
     }
-    if (!has_next) break;
+    if (ni >= r.ntiles) break;
     i = ni;
   }
-  if (PF && have_prev) prefetch_epilogue(a, r, b, p_i, p_above, p_g, t, nfree);
+  if (PF && have_prev) {
+    p_call = pf_publish(a, r, p_i, p_above, p_g, p_cand);
+    pf_install(a, r, b, p_i, p_cand, p_call, t, nfree);
+  }
+}
+
+// The request's fields in scalar registers: read from LDS they would sit in
+// vector registers, and every address derived from them would take per-lane
+// 64-bit arithmetic.
+__device__ inline ReqInfo wave_uniform(const ReqInfo &x) {
+  ReqInfo r;
+  static_assert(sizeof(ReqInfo) % 4 == 0, "ReqInfo is made of 32-bit fields");
+  const int32_t *src = (const int32_t *)&x;
+  int32_t *dst = (int32_t *)&r;
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(ReqInfo) / 4); ++i)
+    dst[i] = __builtin_amdgcn_readfirstlane(src[i]);
+  return r;
 }
 
 // A scoring wave takes jobs w, w + W, ... (W = scoring waves of the launch); job
@@ -530,7 +574,7 @@ __device__ static void score_wave(const StepArgs &a, const ReqInfo *s_req, int w
   const int send = lane < a.B ? s_req[lane].slot0 + s_req[lane].wb : 0;
   for (int slot = w; slot < S; slot += W) {
     const int b = __popcll(__ballot(lane < a.B && send <= slot));
-    const ReqInfo r = s_req[b];
+    const ReqInfo r = wave_uniform(s_req[b]);
     const int k = slot - r.slot0;
     if (ANY_PF && r.active)
       score_job<HG, true>(a, r, b, k, t, nfree);

@@ -51,8 +51,9 @@ enum {
 };
 
 // Scoring and copying workgroups of the indexer launch for these dims (together at
-// most one per compute unit, so that all of them are resident at once).
-void index_grid(const echo_dims_t &d, int *score_blocks, int *copy_blocks);
+// most one per compute unit, so that all of them are resident at once); without
+// prefetch there are no copy workgroups.
+void index_grid(const echo_dims_t &d, bool with_copy, int *score_blocks, int *copy_blocks);
 // Compute units of the current device (cached per device).
 int device_cus();
 
