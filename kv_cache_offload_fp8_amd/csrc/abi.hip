@@ -25,7 +25,7 @@ int device_cus() {
 
 void index_grid(const echo_dims_t &d, bool with_copy, int *score_blocks, int *copy_blocks) {
   const int cus = device_cus();
-  int gc = cus / 4 < kCopyBlocks ? cus / 4 : kCopyBlocks;
+  int gc = cus / 8 < kCopyBlocks ? cus / 8 : kCopyBlocks;
   if (gc < 1) gc = 1;
   if (!with_copy) gc = 0;  // prefetch off: every workgroup scores
   const int64_t max_tiles =

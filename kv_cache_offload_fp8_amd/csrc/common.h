@@ -298,6 +298,40 @@ __device__ inline int lb_resolve(uint64_t *st, int tau, int seg0, int c, int32_t
   return E;
 }
 
+// Non-blocking form of lb_resolve, in two halves so that the state loads of one
+// chunk are consumed only at the next: lb_try_load reads the 64 states before
+// `tau` (lane l: item tau - 1 - l); lb_try_finish returns false if one of them,
+// up to the nearest inclusive prefix, is not published yet (nothing is written
+// then).  Otherwise it completes the look-back like lb_resolve and returns true.
+__device__ inline uint64_t lb_try_load(const uint64_t *st, int tau, int seg0) {
+  const int idx = tau - 1 - lane_id();
+  return idx >= seg0 ? __hip_atomic_load(&st[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                     : kFlagP;
+}
+
+__device__ inline bool lb_try_finish(uint64_t *st, int tau, int seg0, int c, uint64_t v,
+                                     int32_t *status, int &E) {
+  if (tau == seg0) {
+    E = 0;
+    return true;
+  }
+  const uint64_t fm = __ballot((v >> 32) != 0);
+  const uint64_t pm = __ballot((v >> 32) == 2);
+  const uint64_t need = pm ? ((pm & (0 - pm)) << 1) - 1 : ~0ull;
+  if ((fm & need) != need) return false;
+  if (!pm) {  // 64 published aggregates and no prefix yet: walk on (nothing waits long)
+    E = lb_resolve(st, tau, seg0, c, status);
+    return true;
+  }
+  const int l = lane_id();
+  const int first = __ffsll((unsigned long long)pm) - 1;
+  E = wave_sum(l <= first ? (int)(uint32_t)v : 0);
+  if (l == 0)
+    __hip_atomic_store(&st[tau], kFlagP | (uint32_t)(E + c), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
 __device__ inline int lookback(uint64_t *st, int tau, int seg0, int c, int32_t *status) {
   lb_publish(st, tau, seg0, c);
   return lb_resolve(st, tau, seg0, c, status);

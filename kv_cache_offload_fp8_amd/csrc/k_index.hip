@@ -376,51 +376,55 @@ __device__ inline int pf_publish(const StepArgs &a, const ReqInfo &r, int pi,
   return c_all;
 }
 
-__device__ static void pf_install(const StepArgs &a, const ReqInfo &r, int b, int pi,
-                                  const uint64_t (&cand)[kChunks], int c_all, int t,
-                                  int nfree) {
-  const bool last = pi == r.ntiles - 1;
-  // An item without candidates needs no rank; later items sum through its
-  // published count.  Only the request's last item must always resolve.
-  if (c_all == 0 && !last) return;
+// Ranks and free-list reads of this lane's candidates in item pi (at most one
+// per chunk), given the item's exclusive prefix E: bit c of `tk` says whether
+// the chunk-c candidate takes a slot; the reads are issued together, without
+// branches, and consumed by pf_commit.
+__device__ inline void pf_plan(const StepArgs &a, const ReqInfo &r, const uint64_t (&cand)[kChunks],
+                               int E, int nfree, int (&rank)[kChunks], int &tk,
+                               int (&gv)[kChunks]) {
+  const int lane = lane_id();
+  const int lim = nfree < a.n_gpu ? nfree : a.n_gpu;
+  int rank0 = E;
+  tk = 0;
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const uint64_t m = cand[c];
+    rank[c] = rank0 + __popcll(m & lanemask_lt());
+    if (((m >> lane) & 1ull) && rank[c] < r.cap && r.off + rank[c] < lim) tk |= 1 << c;
+    rank0 += __popcll(m);
+  }
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) gv[c] = a.idxbuf[((tk >> c) & 1) ? r.off + rank[c] : 0];
+}
+
+// Installs the planned candidates of item pi (maps, priority t, the rank-ordered
+// lists and the copy queue); the request's last item also publishes n_cand, n_pf
+// and the final count the copy waves stop at.
+__device__ inline void pf_commit(const StepArgs &a, const ReqInfo &r, int b, int pi, int c_all,
+                                 int E, const int (&rank)[kChunks], int tk,
+                                 const int (&gv)[kChunks], int t, int nfree) {
   const int lane = lane_id();
   const int s_wave = pi * kScoreTile;
-  const int E = lb_resolve(a.sc.tstate, r.tile0 + pi, r.tile0, c_all, a.ws.status);
-  const int lim = nfree < a.n_gpu ? nfree : a.n_gpu;
-  if (c_all > 0) {
-    // this lane's candidates (at most one per chunk): rank, free-list position and
-    // slot; the free-list reads are issued together, without branches
-    int rank[kChunks], gv[kChunks];
-    bool take[kChunks];
-    int rank0 = E;
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c) {
-      const uint64_t m = cand[c];
-      rank[c] = rank0 + __popcll(m & lanemask_lt());
-      take[c] = ((m >> lane) & 1ull) && rank[c] < r.cap && r.off + rank[c] < lim;
-      rank0 += __popcll(m);
-    }
-#pragma unroll
-    for (int c = 0; c < kChunks; ++c) gv[c] = a.idxbuf[take[c] ? r.off + rank[c] : 0];
-#pragma unroll
-    for (int c = 0; c < kChunks; ++c) {
-      const int g = gv[c];
-      if (take[c] && g >= 0 && g < a.n_gpu) {
-        const int s = s_wave + c * 64 + lane;
-        const int64_t h = (int64_t)r.base + s;
-        a.h2g[h] = g;
-        a.g2h[g] = (int32_t)h;
-        a.freef[g] = 0;
-        a.prio[g] = t;
-        a.ws.pf_tok[(int64_t)b * a.K + rank[c]] = s;
-        a.ws.pf_slot[(int64_t)b * a.K + rank[c]] = g;
-        __hip_atomic_store(&a.sc.pfq[(int64_t)b * a.K + rank[c]],
-                           (1ull << 63) | ((uint64_t)h << 31) | (uint64_t)g, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-      }
+  for (int c = 0; c < kChunks; ++c) {
+    const int g = gv[c];
+    if (((tk >> c) & 1) && g >= 0 && g < a.n_gpu) {
+      const int s = s_wave + c * 64 + lane;
+      const int64_t h = (int64_t)r.base + s;
+      a.h2g[h] = g;
+      a.g2h[g] = (int32_t)h;
+      a.freef[g] = 0;
+      a.prio[g] = t;
+      a.ws.pf_tok[(int64_t)b * a.K + rank[c]] = s;
+      a.ws.pf_slot[(int64_t)b * a.K + rank[c]] = g;
+      __hip_atomic_store(&a.sc.pfq[(int64_t)b * a.K + rank[c]],
+                         (1ull << 63) | ((uint64_t)h << 31) | (uint64_t)g, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  if (last && lane == 0) {
+  if (pi == r.ntiles - 1 && lane == 0) {
+    const int lim = nfree < a.n_gpu ? nfree : a.n_gpu;
     const int total = E + c_all;
     const int take = min(r.cap, total);
     const int npf = max(0, min(take, lim - r.off));
@@ -432,18 +436,45 @@ __device__ static void pf_install(const StepArgs &a, const ReqInfo &r, int b, in
   }
 }
 
-// Chunk of the next item at which an item's epilogue resolves its rank: the
-// items before it publish their counts at chunk 0, so the look-back rarely waits.
-constexpr int kInstallChunk = 2;
+// Whether item pi's epilogue has anything to do after its count is published:
+// an item without candidates needs no rank (later items sum through its count),
+// except the request's last item, which publishes the totals.
+__device__ inline bool pf_needed(const ReqInfo &r, int pi, int c_all) {
+  return c_all > 0 || pi == r.ntiles - 1;
+}
 
-// One scoring job: work items k, k + wb, k + 2wb, ... of request b.  PF:
-// prefetch is on for this request (the residency of every token above the
-// threshold is read while scoring; the epilogue of an item runs during the
-// job's next item: its count is published at chunk 0, its rank resolved and its
-// rows installed at kInstallChunk).
+// Blocking epilogue: resolve item pi's rank, then install.
+__device__ static void pf_install(const StepArgs &a, const ReqInfo &r, int b, int pi,
+                                  const uint64_t (&cand)[kChunks], int c_all, int t,
+                                  int nfree) {
+  const int E = lb_resolve(a.sc.tstate, r.tile0 + pi, r.tile0, c_all, a.ws.status);
+  int rank[kChunks], tk = 0, gv[kChunks];
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) rank[c] = gv[c] = 0;
+  if (c_all > 0) pf_plan(a, r, cand, E, nfree, rank, tk, gv);
+  pf_commit(a, r, b, pi, c_all, E, rank, tk, gv, t, nfree);
+}
+
+// Epilogues waiting for their rank, per wave, in a ring in LDS.  An item's count
+// is published at the next item's chunk 0 and the item is queued; the oldest
+// queued item's look-back states are read at chunk 1 and examined at chunk 2
+// without waiting: if the items before it have all published, its free-list
+// reads go out at chunk 2 and its installs at chunk 3, else it stays queued for
+// the next item.  A wave that runs ahead of its neighbours therefore keeps
+// scoring; it waits only when the ring is full or at the end of its job, always
+// after publishing its own counts, so every wait ends.  (A short queue made the
+// waves of a request move in lockstep with the slowest of them: with more waves
+// per request the scoring time did not drop at all.)
+constexpr int kPending = 8;
+
+struct PendItem {
+  int32_t pi, c;
+  uint64_t cand[kChunks];
+};
+
 template <int HG, bool PF>
 __device__ static void score_job(const StepArgs &a, const ReqInfo &r, int b, int k, int t,
-                                 int nfree) {
+                                 int nfree, PendItem *pq) {
   const int lane = lane_id();
   // Operand layout: lane l feeds row (l & 15) of A (a head) and column (l & 15)
   // of B (a token) with the 32 bytes at dims chunk .. chunk+31,
@@ -470,16 +501,54 @@ __device__ static void score_job(const StepArgs &a, const ReqInfo &r, int b, int
   v8i kb[2][4];
   int i = k;
   load_k_chunk(a, r, i * kScoreTile, lane, kb[0]);
+  // the previous item's threshold bits and map entries (its epilogue's inputs)
   bool have_prev = false;
-  int p_i = 0, p_call = 0;
-  uint64_t p_above[kChunks], p_cand[kChunks];
+  int p_i = 0;
+  uint64_t p_above[kChunks];
   int p_g[kChunks];
+  // queued epilogues: ring pq[qh .. qh + qn) (see kPending), and the progress of
+  // the oldest one
+  int qh = 0, qn = 0;
+  uint64_t sv = 0;
+  bool planned = false;
+  int o_i = 0, o_c = 0;  // the oldest queued item and its count
+  int E0 = 0, tk = 0, rk[kChunks], gv[kChunks];
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
     p_above[c] = 0;
-    p_cand[c] = 0;
     p_g[c] = 0;
+    rk[c] = gv[c] = 0;
   }
+  auto read_oldest = [&]() {
+    o_i = __builtin_amdgcn_readfirstlane(pq[qh].pi);
+    o_c = __builtin_amdgcn_readfirstlane(pq[qh].c);
+  };
+  auto install_oldest = [&]() {  // blocking
+    uint64_t oc[kChunks];
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) oc[c] = pq[qh].cand[c];
+    read_oldest();
+    pf_install(a, r, b, o_i, oc, o_c, t, nfree);
+    qh = qh + 1 == kPending ? 0 : qh + 1;
+    --qn;
+  };
+  // publish the previous item's count and queue its epilogue (finishing the
+  // oldest queued one first if the ring is full)
+  auto publish_prev = [&]() {
+    uint64_t xc[kChunks];
+    const int xcall = pf_publish(a, r, p_i, p_above, p_g, xc);
+    if (!pf_needed(r, p_i, xcall)) return;
+    if (qn == kPending) install_oldest();
+    int slot = qh + qn;
+    slot = slot >= kPending ? slot - kPending : slot;
+    if (lane == 0) {
+      pq[slot].pi = p_i;
+      pq[slot].c = xcall;
+#pragma unroll
+      for (int c = 0; c < kChunks; ++c) pq[slot].cand[c] = xc[c];
+    }
+    ++qn;
+  };
   while (true) {
     const int s_wave = i * kScoreTile;
     const int tau = r.tile0 + i;
@@ -507,8 +576,28 @@ __device__ static void score_job(const StepArgs &a, const ReqInfo &r, int b, int
       if (PF) {
         above[c] = __ballot(valid && score > r.theta);
         gq[c] = a.h2g[(int64_t)r.base + (valid ? s : r.ctx - 1)];
-        if (c == 0 && have_prev) p_call = pf_publish(a, r, p_i, p_above, p_g, p_cand);
-        if (c == kInstallChunk && have_prev) pf_install(a, r, b, p_i, p_cand, p_call, t, nfree);
+        if (c == 0 && have_prev) publish_prev();
+        if (c == 1 && qn > 0) {
+          read_oldest();
+          sv = lb_try_load(a.sc.tstate, r.tile0 + o_i, r.tile0);
+        }
+        if (c == 2 && qn > 0 &&
+            lb_try_finish(a.sc.tstate, r.tile0 + o_i, r.tile0, o_c, sv, a.ws.status, E0)) {
+          tk = 0;
+          if (o_c > 0) {
+            uint64_t oc[kChunks];
+#pragma unroll
+            for (int cc = 0; cc < kChunks; ++cc) oc[cc] = pq[qh].cand[cc];
+            pf_plan(a, r, oc, E0, nfree, rk, tk, gv);
+          }
+          planned = true;
+        }
+        if (c == 3 && planned) {
+          pf_commit(a, r, b, o_i, o_c, E0, rk, tk, gv, t, nfree);
+          planned = false;
+          qh = qh + 1 == kPending ? 0 : qh + 1;
+          --qn;
+        }
       }
     }
 
@@ -541,8 +630,8 @@ __device__ static void score_job(const StepArgs &a, const ReqInfo &r, int b, int
     i = ni;
   }
   if (PF && have_prev) {
-    p_call = pf_publish(a, r, p_i, p_above, p_g, p_cand);
-    pf_install(a, r, b, p_i, p_cand, p_call, t, nfree);
+    publish_prev();
+    while (qn > 0) install_oldest();
   }
 }
 
@@ -565,7 +654,7 @@ __device__ inline ReqInfo wave_uniform(const ReqInfo &x) {
 // increasing order and every look-back wait is on an item that a resident wave
 // reaches without waiting on a later one.
 template <int HG, bool ANY_PF>
-__device__ static void score_wave(const StepArgs &a, const ReqInfo *s_req, int w) {
+__device__ static void score_wave(const StepArgs &a, const ReqInfo *s_req, int w, PendItem *pq) {
   const int lane = lane_id();
   const int S = a.sc.misc[M_SLOTS];
   const int W = a.score_waves;
@@ -577,9 +666,9 @@ __device__ static void score_wave(const StepArgs &a, const ReqInfo *s_req, int w
     const ReqInfo r = wave_uniform(s_req[b]);
     const int k = slot - r.slot0;
     if (ANY_PF && r.active)
-      score_job<HG, true>(a, r, b, k, t, nfree);
+      score_job<HG, true>(a, r, b, k, t, nfree, pq);
     else
-      score_job<HG, false>(a, r, b, k, t, nfree);
+      score_job<HG, false>(a, r, b, k, t, nfree, pq);
   }
 }
 
@@ -589,6 +678,7 @@ __device__ static void score_wave(const StepArgs &a, const ReqInfo *s_req, int w
 template <int HG, bool ANY_PF>
 __global__ __launch_bounds__(512) void k_score(StepArgs a) {
   __shared__ ReqInfo s_req[kMaxBatch];
+  __shared__ PendItem s_pend[ANY_PF ? kScoreWaves : 1][ANY_PF ? kPending : 1];
   __shared__ int s_left;
   if (failed(a.ws.status)) return;
   const int tid = threadIdx.x;
@@ -597,7 +687,8 @@ __global__ __launch_bounds__(512) void k_score(StepArgs a) {
   __syncthreads();
   const int wid = tid / kWave;
   if ((int)blockIdx.x < a.score_blocks) {
-    score_wave<HG, ANY_PF>(a, s_req, blockIdx.x * kScoreWaves + wid);
+    score_wave<HG, ANY_PF>(a, s_req, blockIdx.x * kScoreWaves + wid,
+                           &s_pend[ANY_PF ? wid : 0][0]);
     if (lane_id() == 0 && atomicSub(&s_left, 1) == 1)
       __hip_atomic_fetch_add(&a.sc.misc[M_SCORE_DONE], 1, __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);

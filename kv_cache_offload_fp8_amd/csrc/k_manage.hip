@@ -44,10 +44,13 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 // Copy `n` rows (host ids hs[i] -> slots gs[i], both in LDS) with the whole block,
 // four 16-byte loads in flight per thread.
 __device__ static void copy_rows(const StepArgs &a, const int32_t *hs, const int32_t *gs, int n) {
+  if (n <= 0) return;
   const int cpr = a.latent * 2 / 16;
   const v4i *src = (const v4i *)a.host_kv;
   v4i *dst = (v4i *)a.gpu_kv;
   const int total = n * cpr;
+  // no load or store under a branch (each would wait for the one before): threads
+  // past the last piece copy the last piece again, the same bytes to the same place
   for (int i0 = threadIdx.x; i0 < total; i0 += 4 * kSelThreads) {
     v4i v0, v1, v2, v3;
     int64_t d0, d1, d2, d3;
@@ -56,16 +59,16 @@ __device__ static void copy_rows(const StepArgs &a, const int32_t *hs, const int
       const int i = i0 + (u) * kSelThreads;                            \
       const int ic = i < total ? i : total - 1;                        \
       const int e = ic / cpr, c = ic - e * cpr;                        \
-      d = i < total ? (int64_t)gs[e] * cpr + c : -1;                   \
-      if (i < total) v = src[(int64_t)hs[e] * cpr + c];                \
+      d = (int64_t)gs[e] * cpr + c;                                    \
+      v = src[(int64_t)hs[e] * cpr + c];                               \
     }
     ECHO_ROW_LOAD(0, v0, d0) ECHO_ROW_LOAD(1, v1, d1) ECHO_ROW_LOAD(2, v2, d2)
     ECHO_ROW_LOAD(3, v3, d3)
 #undef ECHO_ROW_LOAD
-    if (d0 >= 0) dst[d0] = v0;
-    if (d1 >= 0) dst[d1] = v1;
-    if (d2 >= 0) dst[d2] = v2;
-    if (d3 >= 0) dst[d3] = v3;
+    dst[d0] = v0;
+    dst[d1] = v1;
+    dst[d2] = v2;
+    dst[d3] = v3;
   }
 }
 
@@ -298,34 +301,34 @@ hipError_t launch_manage(const StepArgs &a, bool recall, bool advance, hipStream
 }
 
 // Standalone recall: rows of 16-byte chunks, four loads in flight per thread.
-constexpr int kRecallBlocks = 1024;
+// The host link saturates with about 128-512 KB in flight and slows down with
+// several MB (measured: a 1 MB transfer at 48-50 GB/s with 32 workgroups, 39 GB/s
+// with 1024), so a small grid walks the list.  No load or store sits under a
+// branch: threads past the last piece copy the last piece again.
+constexpr int kRecallBlocks = 32;
 
 __global__ __launch_bounds__(256) void k_recall(StepArgs a) {
   if (failed(a.ws.status)) return;
   const int n = a.ws.counters[ECHO_CNT_MISS];
+  if (n <= 0) return;
   const int cpr = a.latent * 2 / 16;
   const int64_t total = (int64_t)n * cpr;
-  const uint4 *src = (const uint4 *)a.host_kv;
-  uint4 *dst = (uint4 *)a.gpu_kv;
+  const v4i *src = (const v4i *)a.host_kv;
+  v4i *dst = (v4i *)a.gpu_kv;
   const int64_t stride = (int64_t)gridDim.x * 256;
   for (int64_t i0 = (int64_t)blockIdx.x * 256 + threadIdx.x; i0 < total; i0 += 4 * stride) {
-    uint4 v[4];
-    int hh[4], gg[4], cc[4];
+    v4i v[4];
+    int64_t d[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int64_t i = i0 + u * stride;
-      hh[u] = -1;
-      if (i < total) {
-        const int r = (int)(i / cpr);
-        cc[u] = (int)(i - (int64_t)r * cpr);
-        hh[u] = a.ws.recall_h[r];
-        gg[u] = a.ws.recall_g[r];
-        v[u] = src[(int64_t)hh[u] * cpr + cc[u]];
-      }
+      const int64_t i = i0 + u * stride < total ? i0 + u * stride : total - 1;
+      const int r = (int)(i / cpr);
+      const int c = (int)(i - (int64_t)r * cpr);
+      d[u] = (int64_t)a.ws.recall_g[r] * cpr + c;
+      v[u] = src[(int64_t)a.ws.recall_h[r] * cpr + c];
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (hh[u] >= 0) dst[(int64_t)gg[u] * cpr + cc[u]] = v[u];
+    for (int u = 0; u < 4; ++u) dst[d[u]] = v[u];
   }
 }
 
