@@ -250,29 +250,61 @@ def main():
     idx_gbps = idx_bytes / (idx_ms * 1e-3) / 1e9
     row = wl.latent * 2
     recall_ms = ph[:, 3]
-    recall_gbps = float((misses * row).sum() / (recall_ms.sum() * 1e-3) / 1e9)
+    recall_eager_gbps = float((misses * row).sum() / (recall_ms.sum() * 1e-3) / 1e9)
+    # Recall rate as the step runs it, back to back in a graph: the last layer's
+    # miss list (still in the workspace) recalled `nrc` times into its pool (the
+    # same rows to the same slots each time), timed with events around one replay.
+    nrc = 32
+    rc_rows = int(ws.counters[abi.ECHO_CNT_MISS].item())
+    grc = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cs):
+        with torch.cuda.graph(grc, stream=cs):
+            for _ in range(nrc):
+                R.check(abi.echo_recall(dims, layers[-1].struct, ws.ws, cs.cuda_stream),
+                        "recall")
+    grc.replay()
+    torch.cuda.synchronize()
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r0.record()
+    grc.replay()
+    r1.record()
+    torch.cuda.synchronize()
+    rc_ms = r0.elapsed_time(r1) / nrc
+    recall_gbps = rc_rows * row / (rc_ms * 1e-3) / 1e9
+    del grc
     hit = float(1.0 - misses.sum() / max(1, selected.sum()))
     log(f"[bench] phases (ms, mean over {len(evs)} layer-steps): indexer {idx_ms:.4f} "
         f"topk {ph[:, 1].mean():.4f} alloc/evict {ph[:, 2].mean():.4f} "
         f"recall {recall_ms.mean():.4f}; hit rate {hit:.4f}; misses/layer-step "
         f"{misses.mean():.0f}; prefetched/layer-step {prefetched.mean():.0f}")
+    log(f"[bench] recall in a graph: {rc_rows} rows in {rc_ms * 1e3:.1f} us per launch = "
+        f"{recall_gbps:.1f} GB/s (eager, event per call: {recall_eager_gbps:.1f} GB/s)")
 
     # ------------------------------------- indexer with prefetch off (scoring only)
     # Threshold +inf: the same kernel scores every token but prefetches nothing and
     # changes no cache state, so this isolates the HBM-bound scoring stream.
     nso = min(L, 16)
-    so = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nso)]
-    for j in range(nso):
-        so[j][0].record(s)
-        R.check(abi.echo_indexer_prefetch(dims, layers[j].struct, batch.struct, ws.ws,
-                                          abi.ECHO_THETA_POS_INF, sh), "indexer")
-        so[j][1].record(s)
+    # back to back in a graph, as the step runs its kernels: one replay of nso
+    # calls (layers 0..nso-1), events around it on the stream it is replayed on
+    gso = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cs):
+        with torch.cuda.graph(gso, stream=cs):
+            for j in range(nso):
+                R.check(abi.echo_indexer_prefetch(dims, layers[j].struct, batch.struct, ws.ws,
+                                                  abi.ECHO_THETA_POS_INF, cs.cuda_stream),
+                        "indexer")
+    gso.replay()
     torch.cuda.synchronize()
-    so_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in so[1:]] or
-                          [so[0][0].elapsed_time(so[0][1])]))
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    gso.replay()
+    s1.record()
+    torch.cuda.synchronize()
+    so_ms = s0.elapsed_time(s1) / nso
+    del gso
     so_gbps = total_tok * BYTES_PER_SCORED_TOKEN / (so_ms * 1e-3) / 1e9
     log(f"[bench] indexer, prefetch off: {so_ms:.4f} ms = {so_gbps:.0f} GB/s "
-        f"({so_gbps / HBM_PEAK_GBPS:.1%} of HBM peak)")
+        f"({so_gbps / HBM_PEAK_GBPS:.1%} of HBM peak; {nso} calls back to back in a graph)")
 
     if args.pmc_calibrate:  # a plain copy of known size for the HBM-traffic counters
         cal_src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -346,7 +378,8 @@ def main():
                    "global_batch": B, "seq_len": int(ctx.max()), "layers": L,
                    "threshold_mode": args.mode},
         "roofline": {"kernel": "lightning-indexer scoring: echo_indexer_prefetch with prefetch "
-                               "off = k_begin + k_score<4,false>",
+                               "off = k_begin + k_score<4,false>, per call over "
+                               f"{nso} calls back to back in a graph",
                      "bound": "hbm", "achieved": round(so_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(so_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "bytes_per_launch": idx_bytes,
@@ -363,6 +396,10 @@ def main():
         "indexer_hbm_gbps": round(so_gbps, 1),
         "recall_host_link_gbps": round(recall_gbps, 2),
         "recall_frac_of_link_peak": round(recall_gbps / link_peak, 4),
+        "recall_measure": {"rows": rc_rows, "launch_ms": round(rc_ms, 5),
+                           "how": f"echo_recall of the last layer-step's miss list, {nrc} "
+                                  "launches back to back in a graph",
+                           "eager_event_per_call_gbps": round(recall_eager_gbps, 2)},
         "host_link_peak_gbps": {"hipMemcpy_h2d": round(memcpy_gbps, 2),
                                 "zero_copy_recall_kernel": round(zc_gbps, 2)},
         "phase_ms": {"indexer": round(idx_ms, 5), "topk": round(float(ph[:, 1].mean()), 5),

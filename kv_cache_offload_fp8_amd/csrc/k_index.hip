@@ -65,13 +65,17 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------------ begin
 
-__device__ static void build_request_table(const StepArgs &a, int roles) {
-  // one wave: lane b handles request b
+__device__ static void build_request_table(const StepArgs &a, int roles, int32_t st0) {
+  // one wave: lane b handles request b.  Every input is read before the status
+  // (st0, loaded by the caller) is looked at, so the reads take one round trip.
   const int l = threadIdx.x;
   if (l >= kWave) return;
   const bool in = l < a.B;
   int ctx = in ? a.ctx_len[l] : 0;
   int base = in ? a.host_base[l] : 0;
+  const float th_in = in && a.mode == ECHO_THETA_EMA ? a.theta[l] : __builtin_huge_valf();
+  const float g_in = in && a.guard ? a.guard[l] : __builtin_huge_valf();
+  if (st0 != 0) return;
   bool bad = in && (ctx < 0 || ctx > a.max_ctx || base < 0 || (base & 15) != 0 ||
                     (int64_t)base + (int64_t)ctx > a.n_host);
   // disjoint host ranges
@@ -93,7 +97,7 @@ __device__ static void build_request_table(const StepArgs &a, int roles) {
   int active = 0;
   float th = __builtin_huge_valf();
   if (a.mode == ECHO_THETA_EMA) {
-    th = in ? a.theta[l] : th;
+    th = th_in;
     active = !(isinf(th) && th > 0);
   } else if (a.mode == ECHO_THETA_NEG_INF) {
     th = -__builtin_huge_valf();
@@ -102,7 +106,7 @@ __device__ static void build_request_table(const StepArgs &a, int roles) {
   int use_guard = 0;
   uint32_t guard_key = 0xFFFFFFFFu;
   if (in && a.guard && ctx > a.K) {
-    const float g = a.guard[l];
+    const float g = g_in;
     if (!isinf(g) && !isnan(g)) {
       const uint32_t key = topk_key(g);
       guard_key = key > 0xFFFFFFFFu - kGuardUlps ? 0xFFFFFFFFu : key + kGuardUlps;
@@ -156,7 +160,7 @@ __device__ static void build_request_table(const StepArgs &a, int roles) {
 // q_lo = e4m3(q*2^e - q_hi), stored [64][128] zero-padded, and the weight
 // w_j * 2^-e (zero for padded heads).  Block of 256 threads: thread = (head of
 // the quarter, 8 dims); the 16 threads of a head are 16 neighbouring lanes.
-__device__ static void stage_query(const StepArgs &a, int b, int quarter) {
+__device__ static void stage_query(const StepArgs &a, int b, int quarter, int32_t st0) {
   const int tid = threadIdx.x;
   const int j = quarter * 16 + (tid >> 4), d0 = (tid & 15) * 8;
   const int t = a.ctl[ECHO_CTL_STEP];
@@ -165,6 +169,8 @@ __device__ static void stage_query(const StepArgs &a, int b, int quarter) {
   // 8 bf16 = one 16-byte load (D is a multiple of 32: a group is all in or all out)
   const bool in = j < a.H && d0 < a.D;
   const uint4 w4 = in ? *(const uint4 *)(src + j * a.D + d0) : make_uint4(0, 0, 0, 0);
+  const float wj = d0 == 0 && j < a.H ? a.w[(int64_t)b * a.H + j] : 0.0f;
+  if (st0 != 0) return;
   const uint32_t wd[4] = {w4.x, w4.y, w4.z, w4.w};
   float x[8];
 #pragma unroll
@@ -196,7 +202,7 @@ __device__ static void stage_query(const StepArgs &a, int b, int quarter) {
   *(uint2 *)(a.sc.qhi + o) = make_uint2(whi[0], whi[1]);
   *(uint2 *)(a.sc.qlo + o) = make_uint2(wlo[0], wlo[1]);
   if (d0 == 0)
-    a.sc.wsc[(int64_t)b * kHeadsPad + j] = j < a.H ? ldexpf(a.w[(int64_t)b * a.H + j], -e) : 0.0f;
+    a.sc.wsc[(int64_t)b * kHeadsPad + j] = j < a.H ? ldexpf(wj, -e) : 0.0f;
 }
 
 __device__ static void fill_u32(uint32_t *p, int64_t n, uint32_t v, int64_t i0, int64_t step) {
@@ -206,10 +212,13 @@ __device__ static void fill_u32(uint32_t *p, int64_t n, uint32_t v, int64_t i0, 
 constexpr int kBeginClearBlocks = 32;
 
 __global__ __launch_bounds__(256) void k_begin(StepArgs a, int roles) {
-  if (failed(a.ws.status)) return;
+  // the status is read here and looked at only after each role has issued its
+  // own reads (a kernel that follows an error changes nothing)
+  const int32_t st0 = __hip_atomic_load(a.ws.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   int blk = blockIdx.x;
   if (blk == 0) {
-    if (roles & BEGIN_REQ) build_request_table(a, roles);
+    if (roles & BEGIN_REQ) build_request_table(a, roles, st0);
+    if (st0 != 0) return;
     // small per-request arrays and counters
     const int tid = threadIdx.x;
     if ((roles & BEGIN_CLR_INDEX) && tid < a.max_batch) {
@@ -231,12 +240,12 @@ __global__ __launch_bounds__(256) void k_begin(StepArgs a, int roles) {
   blk -= 1;
   if (roles & BEGIN_Q) {
     if (blk < 4 * a.B) {
-      stage_query(a, blk >> 2, blk & 3);
+      stage_query(a, blk >> 2, blk & 3, st0);
       return;
     }
     blk -= 4 * a.B;
   }
-  if (blk >= kBeginClearBlocks) return;
+  if (blk >= kBeginClearBlocks || st0 != 0) return;
   const int64_t i0 = (int64_t)blk * blockDim.x + threadIdx.x;
   const int64_t step = (int64_t)kBeginClearBlocks * blockDim.x;
   if (roles & BEGIN_CLR_INDEX) {
@@ -679,12 +688,16 @@ template <int HG, bool ANY_PF>
 __global__ __launch_bounds__(512) void k_score(StepArgs a) {
   __shared__ ReqInfo s_req[kMaxBatch];
   __shared__ PendItem s_pend[ANY_PF ? kScoreWaves : 1][ANY_PF ? kPending : 1];
-  __shared__ int s_left;
-  if (failed(a.ws.status)) return;
+  __shared__ int s_left, s_dead;
   const int tid = threadIdx.x;
+  // the status and the request table in one round trip; the block decides as one
   for (int i = tid; i < a.B; i += blockDim.x) s_req[i] = a.sc.req[i];
-  if (tid == 0) s_left = kScoreWaves;
+  if (tid == 0) {
+    s_left = kScoreWaves;
+    s_dead = failed(a.ws.status);
+  }
   __syncthreads();
+  if (s_dead) return;
   const int wid = tid / kWave;
   if ((int)blockIdx.x < a.score_blocks) {
     score_wave<HG, ANY_PF>(a, s_req, blockIdx.x * kScoreWaves + wid,

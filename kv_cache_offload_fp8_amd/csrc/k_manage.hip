@@ -79,15 +79,18 @@ __global__ __launch_bounds__(kSelThreads) void k_manage(StepArgs a) {
   __shared__ int sh[kSelThreads / kWave + 1];
   __shared__ int s_moff[kMaxBatch + 1];
   __shared__ int s_bin, s_below, s_E;
-  if (failed(a.ws.status)) return;
+  // the status is looked at after the first reads are issued (one round trip)
+  const int32_t st0 = __hip_atomic_load(a.ws.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int tid = threadIdx.x;
   const int blk = blockIdx.x, nblk = a.sc.atiles;
   if (blk >= nblk) {  // copy workgroup: finish the step's prefetch copy, two waves per copy wave
+    if (st0 != 0) return;
     const int g = (blk - nblk) * (kSelThreads / kWave) + tid / kWave;
     copy_worker(a, a.sc.req, g % a.copy_waves, g / a.copy_waves, 2, nullptr, 0);
     return;
   }
   const int t = a.ctl[ECHO_CTL_STEP];
+  if (st0 != 0) return;
   const int g0 = blk * kSlotTile + tid * 4;
 
   // ---- phase 1: free count, age histogram of the evictable slots

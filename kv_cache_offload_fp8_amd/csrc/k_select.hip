@@ -118,15 +118,18 @@ __global__ __launch_bounds__(kSelThreads) void k_topk(StepArgs a) {
   __shared__ int sh[kSelThreads / kWave + 1];
   __shared__ uint64_t shu[kSelThreads / kWave];
   __shared__ int s_bin, s_below, s_cnt;
-  if (failed(a.ws.status)) return;
+  // the status is looked at after the first reads are issued (one round trip)
+  const int32_t st0 = __hip_atomic_load(a.ws.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
   if ((int)blockIdx.x >= a.B) {  // copy workgroup: prefetched rows, until selection ends
+    if (st0 != 0) return;
     copy_worker(a, a.sc.req, ((int)blockIdx.x - a.B) * (kSelThreads / kWave) + wid, 0, 1,
                 &a.sc.misc[M_TOPK_DONE], a.B);
     return;
   }
   const int b = blockIdx.x;
   const ReqInfo r = a.sc.req[b];
+  if (st0 != 0) return;
   const int ctx = r.ctx;
   const int K = a.K;
   const int nsel = ctx < K ? ctx : K;
