@@ -312,20 +312,22 @@ constexpr int kChunks = kScoreTile / 64;  // 64-token chunks per work item
 // and lanes whose dims lie past D read the same token's first 32 dims, which
 // meet the zero padding of q (an exact 0 for any finite e4m3 byte).
 __device__ inline void load_k_chunk(const StepArgs &a, const ReqInfo &r, int s0, int lane,
-                                    v8i (&kb)[4]) {
+                                    v8i (&kb)[4], bool real = true) {
   const bool dim_ok = 32 * (lane >> 4) < a.D;
   const int lp = dim_ok ? lane : (lane & 15);
   const int glast = (r.ctx - 1) & ~15;
-  const int half = 8 * a.D;
+  // real = false (no next item): every lane reads the same 16 bytes, one cache
+  // line per instruction, only to keep the load count the same on every path
+  const int half = real ? 8 * a.D : 0;
   // wave-uniform 64-bit group address + 32-bit lane offset: the loads use the
   // scalar-base addressing form and need no per-lane 64-bit arithmetic
-  const uint32_t lo = (uint32_t)lp * 16u;
+  const uint32_t lo = real ? (uint32_t)lp * 16u : 0u;
   const int s0u = __builtin_amdgcn_readfirstlane(s0);
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int st = s0u + 16 * u;
     const int sg = st < r.ctx ? st : glast;
-    const uint8_t *g = a.kidx + ((int64_t)r.base + sg) * a.D;
+    const uint8_t *g = real ? a.kidx + ((int64_t)r.base + sg) * a.D : a.kidx;
     const v4i x0 = __builtin_nontemporal_load((const v4i *)(g + lo));
     const v4i x1 = __builtin_nontemporal_load((const v4i *)(g + (lo + (uint32_t)half)));
     kb[u] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -570,9 +572,9 @@ __device__ static void score_job(const StepArgs &a, const ReqInfo &r, int b, int
       if (c + 1 < kChunks) {
         load_k_chunk(a, r, s_wave + (c + 1) * 64, lane, kb[(c + 1) & 1]);
       } else {
-        // unconditional (the last item reloads its own first chunk): a load under
+        // unconditional (after the last item, a one-line dummy read): a load under
         // a branch would make the compiler drain every load before the join
-        load_k_chunk(a, r, (ni < r.ntiles ? ni : i) * kScoreTile, lane, kb[0]);
+        load_k_chunk(a, r, (ni < r.ntiles ? ni : i) * kScoreTile, lane, kb[0], ni < r.ntiles);
       }
       const float score = score_chunk<HG>(kb[c & 1], qa, wr, lane);
       const int s = s_wave + c * 64 + lane;
