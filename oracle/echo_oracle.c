@@ -49,6 +49,9 @@
  *  R8  Alloc: miss i takes the i-th slot of the ascending free list after
  *      eviction, priority t; its latent row is copied from the host pool.
  *  R9  t (the decode-step counter) advances by one after a successful step.
+ *  R10 Append: the step's new token takes host id host_base + ctx of its
+ *      request; its indexer key and latent are written there and ctx grows by
+ *      one.  It is not placed in the GPU pool.
  */
 #include <math.h>
 #include <stdint.h>
@@ -57,6 +60,7 @@
 
 #define ORC_OK 0
 #define ORC_ECAPACITY (-4)
+#define ORC_EDEVARG (-6)
 
 #define ORC_MODE_EMA 0
 #define ORC_MODE_NEG_INF 1
@@ -373,5 +377,40 @@ int orc_layer_step(const orc_cfg *c, orc_state *st, int B,
   st->t = t + 1; /* R9 */
   free(E);
   free(F);
+  return ORC_OK;
+}
+
+/* Decode append and writeback, [P1] "Core method / in-graph per-layer cache
+ * management" (the KV of every token is backed up to the host pool when it is
+ * generated, and the indexer K stays on the GPU) and "Design trade-offs" (every
+ * new token is written back).  Reading R10: for request b the new token takes
+ * host id h = host_base[b] + ctx[b]; key row kidx[h] = k_new[b] (D bytes) and
+ * latent host_kv[h] = lat_new[b] (`latent` values); with `advance`, ctx[b] grows
+ * by one.  The requests are checked first, in order: no room (ctx[b] = max_ctx,
+ * h >= n_host, or h inside another request's range [host_base[o],
+ * host_base[o] + ctx[o]] counting that request's own new token) gives
+ * ORC_ECAPACITY, a host id some slot already maps (h2g[h] != -1) gives
+ * ORC_EDEVARG; the first such request decides and nothing is written. */
+int orc_append(int B, int D, int latent, int64_t n_host, int32_t max_ctx,
+               const int32_t *host_base, int32_t *ctx, const int32_t *h2g,
+               const uint8_t *k_new, const uint16_t *lat_new, uint8_t *kidx,
+               uint16_t *host_kv, int advance) {
+  for (int b = 0; b < B; ++b) {
+    const int64_t h = (int64_t)host_base[b] + ctx[b];
+    if (ctx[b] < 0 || ctx[b] >= max_ctx || host_base[b] < 0 || h >= n_host) return ORC_ECAPACITY;
+    for (int o = 0; o < B; ++o) {
+      if (o == b) continue;
+      if (h >= host_base[o] && h < (int64_t)host_base[o] + ctx[o] + 1) return ORC_ECAPACITY;
+    }
+    if (h2g[h] != -1) return ORC_EDEVARG;
+  }
+  for (int b = 0; b < B; ++b) {
+    const int64_t h = (int64_t)host_base[b] + ctx[b];
+    memcpy(kidx + h * D, k_new + (int64_t)b * D, (size_t)D);
+    if (host_kv)
+      memcpy(host_kv + h * latent, lat_new + (int64_t)b * latent, (size_t)latent * 2);
+  }
+  if (advance)
+    for (int b = 0; b < B; ++b) ctx[b] += 1;
   return ORC_OK;
 }

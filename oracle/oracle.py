@@ -18,7 +18,7 @@ SRC = os.path.join(HERE, "echo_oracle.c")
 LIB = os.path.join(HERE, "libecho_oracle.so")
 
 MODE_EMA, MODE_NEG_INF, MODE_POS_INF = 0, 1, 2
-OK, ECAPACITY = 0, -4
+OK, ECAPACITY, EDEVARG = 0, -4, -6
 
 
 def build(force: bool = False) -> str:
@@ -54,6 +54,10 @@ def lib() -> C.CDLL:
         _lib.orc_topk.argtypes = [C.c_void_p, C.c_int64, C.c_int, C.c_void_p, C.c_void_p]
         _lib.orc_ema_update.restype = C.c_float
         _lib.orc_ema_update.argtypes = [C.c_float, C.c_float, C.c_float]
+        _lib.orc_append.restype = C.c_int
+        _lib.orc_append.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int64, C.c_int32, C.c_void_p,
+                                    C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                    C.c_void_p, C.c_int]
         _lib.orc_layer_step.restype = C.c_int
         _lib.orc_layer_step.argtypes = [C.POINTER(Cfg), C.POINTER(State), C.c_int,
                                         C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
@@ -117,6 +121,27 @@ def topk(sc: np.ndarray, k: int) -> tuple[np.ndarray, float]:
     kth = np.zeros(1, np.float32)
     m = lib().orc_topk(_p(sc), sc.size, int(k), _p(sel), _p(kth))
     return sel[:m].copy(), float(kth[0])
+
+
+def append(host_base, ctx, h2g, k_new, lat_new, kidx, host_kv, max_ctx: int,
+           advance: bool = True) -> int:
+    """Decode append (orc_append): writes each request's new token into kidx (uint8
+    [n_host, D]) and host_kv (uint16 [n_host, latent] or None) at host_base + ctx, then
+    grows ctx (int32, in place) if ``advance``.  Returns OK or the error code."""
+    host_base = np.ascontiguousarray(host_base, np.int32)
+    assert ctx.dtype == np.int32 and ctx.flags["C_CONTIGUOUS"]
+    h2g = np.ascontiguousarray(h2g, np.int32)
+    k_new = np.ascontiguousarray(k_new, np.uint8)
+    lat_new = np.ascontiguousarray(lat_new, np.uint16)
+    B = int(ctx.size)
+    D = kidx.shape[1]
+    latent = lat_new.shape[1] if lat_new.ndim == 2 else 0
+    assert k_new.shape == (B, D) and kidx.flags["C_CONTIGUOUS"]
+    if host_kv is not None:
+        assert host_kv.flags["C_CONTIGUOUS"] and host_kv.shape[1] == latent
+    return lib().orc_append(B, D, latent, kidx.shape[0], int(max_ctx), _p(host_base), _p(ctx),
+                            _p(h2g), _p(k_new), _p(lat_new), _p(kidx),
+                            _p(host_kv) if host_kv is not None else None, int(bool(advance)))
 
 
 def ema_update(theta: float, s_k: float, alpha: float = 0.5) -> float:

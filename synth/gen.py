@@ -22,7 +22,7 @@ import torch
 
 from .configs import Workload
 
-T_K, T_LAT, T_W, T_Q0, T_QN = 1, 2, 3, 4, 5
+T_K, T_LAT, T_W, T_Q0, T_QN, T_APPEND = 1, 2, 3, 4, 5, 6
 
 
 def seed_for(wl: Workload, seed: int, *key: int) -> int:
@@ -36,11 +36,12 @@ def _gen(device, s: int) -> torch.Generator:
     return g
 
 
-def host_layout(ctx: np.ndarray) -> np.ndarray:
+def host_layout(ctx: np.ndarray, room: int = 0) -> np.ndarray:
     """First host id of each request: requests packed back to back, each starting on a
-    16-row boundary (the tiled indexer-K layout groups host ids by 16)."""
+    16-row boundary (the tiled indexer-K layout groups host ids by 16), with ``room``
+    free rows after each context for tokens appended later."""
     ctx = np.asarray(ctx, np.int64)
-    span = (ctx + 15) // 16 * 16
+    span = (ctx + room + 15) // 16 * 16
     base = np.zeros(ctx.size, np.int64)
     if ctx.size > 1:
         base[1:] = np.cumsum(span)[:-1]
@@ -133,10 +134,24 @@ class Inputs:
         return self.q[t].cpu().view(torch.int16).numpy().view(np.uint16)
 
 
+def gen_append(wl: Workload, layer: int, batch: int, step: int, seed=0):
+    """The new token of each request at decode step ``step``: uint8 fp8-E4M3FN key codes
+    [B, D] and bf16 latent codes as int16 [B, latent], N(0,1) like the history."""
+    k = np.zeros((batch, wl.head_dim), np.uint8)
+    lat = np.zeros((batch, wl.latent), np.int16)
+    for b in range(batch):
+        g = _gen("cpu", seed_for(wl, seed, layer, b, T_APPEND, step))
+        x = torch.randn((wl.head_dim,), generator=g, dtype=torch.float32)
+        y = torch.randn((wl.latent,), generator=g, dtype=torch.float32)
+        k[b] = x.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        lat[b] = y.to(torch.bfloat16).view(torch.int16).numpy()
+    return k, lat
+
+
 def make_inputs(wl: Workload, layer: int = 0, device="cpu", seed: int = 0, steps=None,
-                ctx=None, with_latents=True) -> Inputs:
+                ctx=None, with_latents=True, room: int = 0) -> Inputs:
     ctx = wl.contexts(seed) if ctx is None else np.asarray(ctx, np.int32)
-    base = host_layout(ctx)
+    base = host_layout(ctx, room)
     assert ctx.size == 0 or int(base[-1]) + int(ctx[-1]) <= wl.n_host, "host pool too small"
     steps = wl.steps if steps is None else steps
     kidx = gen_kidx(wl, layer, ctx, base, device, seed)

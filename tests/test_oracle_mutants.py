@@ -44,6 +44,12 @@ MUTANTS = {
     "prefetch_ignores_offset": ("int32_t g = F[off + r];", "int32_t g = F[r];"),
     "metadata_idxbuf_dropped": ("int64_t per_slot = 1 + 4 + 4 + 4;",
                                 "int64_t per_slot = 1 + 4 + 4;"),
+    "append_overwrites_last_row": ("const int64_t h = (int64_t)host_base[b] + ctx[b];\n    memcpy",
+                                   "const int64_t h = (int64_t)host_base[b] + ctx[b] - 1;\n"
+                                   "    memcpy"),
+    "append_ignores_neighbours": ("if (h >= host_base[o] && h < (int64_t)host_base[o] + ctx[o] + 1) "
+                                  "return ORC_ECAPACITY;",
+                                  "if (0) return ORC_ECAPACITY;"),
 }
 
 

@@ -380,3 +380,66 @@ def test_short_context_selects_everything_and_skips_ema():
     assert o["n_sel"].tolist() == [40, 64]
     assert o["sel_tok"][0, :40].tolist() == list(range(40))
     assert np.isinf(lay.theta[0]) and lay.theta[1] == o["kth"][1]
+
+
+# ---------------------------------------------------------------- decode append
+# R10 (append and writeback): each request's new token lands at host id
+# host_base + ctx, nothing else changes, and ctx grows by one; a request without
+# room or whose id is mapped stops the whole call with nothing written.
+
+def _append_case(B=3, D=8, latent=16, n_host=256, room=4, seed=0):
+    rng = np.random.default_rng(seed)
+    ctx = rng.integers(1, 40, B).astype(np.int32)
+    span = (ctx + room + 15) // 16 * 16
+    base = np.concatenate([[0], np.cumsum(span)[:-1]]).astype(np.int32)
+    kidx = rng.integers(0, 256, (n_host, D), dtype=np.uint8)
+    host = rng.integers(0, 65536, (n_host, latent), dtype=np.uint16)
+    k_new = rng.integers(0, 256, (B, D), dtype=np.uint8)
+    lat_new = rng.integers(0, 65536, (B, latent), dtype=np.uint16)
+    return ctx, base, kidx, host, k_new, lat_new
+
+
+def test_append_writes_exactly_the_next_row_of_each_request():
+    ctx, base, kidx, host, k_new, lat_new = _append_case()
+    k0, h0, c0 = kidx.copy(), host.copy(), ctx.copy()
+    h2g = np.full(kidx.shape[0], -1, np.int32)
+    assert O.append(base, ctx, h2g, k_new, lat_new, kidx, host, max_ctx=64) == O.OK
+    assert np.array_equal(ctx, c0 + 1)
+    rows = base.astype(np.int64) + c0
+    changed = np.nonzero((kidx != k0).any(1) | (host != h0).any(1))[0]
+    assert set(changed.tolist()) <= set(rows.tolist())
+    for b, h in enumerate(rows):
+        assert np.array_equal(kidx[h], k_new[b]) and np.array_equal(host[h], lat_new[b])
+    # without advance the same rows are written and ctx stays
+    c1 = ctx.copy()
+    assert O.append(base, ctx, h2g, k_new, lat_new, kidx, host, max_ctx=64,
+                    advance=False) == O.OK
+    assert np.array_equal(ctx, c1)
+    for b in range(ctx.size):
+        assert np.array_equal(kidx[int(base[b]) + int(c1[b])], k_new[b])
+
+
+def test_append_checks_room_and_mapping_and_writes_nothing_on_error():
+    ctx, base, kidx, host, k_new, lat_new = _append_case(room=0)
+    h2g = np.full(kidx.shape[0], -1, np.int32)
+    # request 0 ends exactly where request 1 starts: its next id is taken
+    ctx[0] = base[1] - base[0]
+    k0, h0, c0 = kidx.copy(), host.copy(), ctx.copy()
+    assert O.append(base, ctx, h2g, k_new, lat_new, kidx, host, max_ctx=64) == O.ECAPACITY
+    assert np.array_equal(kidx, k0) and np.array_equal(host, h0) and np.array_equal(ctx, c0)
+    # room everywhere, but one target id already mapped to a slot
+    ctx, base, kidx, host, k_new, lat_new = _append_case(room=8)
+    h2g = np.full(kidx.shape[0], -1, np.int32)
+    h2g[int(base[2]) + int(ctx[2])] = 5
+    c0 = ctx.copy()
+    assert O.append(base, ctx, h2g, k_new, lat_new, kidx, host, max_ctx=64) == O.EDEVARG
+    assert np.array_equal(ctx, c0)
+    # the context limit and the end of the host pool
+    h2g[:] = -1
+    ctx2 = ctx.copy()
+    ctx2[1] = 20
+    assert O.append(base, ctx2, h2g, k_new, lat_new, kidx, host, max_ctx=20) == O.ECAPACITY
+    base3 = base.copy()
+    base3[-1] = kidx.shape[0] - int(ctx[-1])
+    assert O.append(base3, ctx.copy(), h2g, k_new, lat_new, kidx, host, max_ctx=64) == \
+        O.ECAPACITY
