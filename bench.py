@@ -118,12 +118,12 @@ def main():
     mode = {"ema": abi.ECHO_THETA_EMA, "neg_inf": abi.ECHO_THETA_NEG_INF,
             "pos_inf": abi.ECHO_THETA_POS_INF}[args.mode]
     ctx = wl.contexts(args.seed)
-    base = G.host_layout(ctx)
+    base = G.host_layout(ctx, room=1)  # one free row per request: the append measurement
     B = int(ctx.size)
     total_tok = int(ctx.sum())
     q_ring = args.warmup + args.steps + args.breakdown_steps
-    dims = R.make_dims(wl.heads, wl.head_dim, wl.top_k, wl.n_host, wl.n_gpu, B, int(ctx.max()),
-                       wl.latent, wl.alpha, wl.cap_div, q_ring)
+    dims = R.make_dims(wl.heads, wl.head_dim, wl.top_k, wl.n_host, wl.n_gpu, B,
+                       int(ctx.max()) + 1, wl.latent, wl.alpha, wl.cap_div, q_ring)
     log(f"[bench] workload {wl.name}: B={B} ctx {ctx.min()}..{ctx.max()} (sum {total_tok}) "
         f"L={L} n_gpu={wl.n_gpu} n_host={wl.n_host} q_ring={q_ring}")
 
@@ -352,6 +352,34 @@ def main():
     log(f"[bench] layer step {step_ms * 1e3:.1f} us; host-link floor "
         f"{link_floor_ms * 1e3:.1f} us ({link_floor_ms / step_ms:.1%})")
 
+    # ----------------------------------------------- decode append (writeback)
+    # One step's new tokens appended to every layer, back to back in a graph, without
+    # advancing the contexts (each replay writes the same rows): the per-layer cost
+    # of keeping the indexer K on the GPU and backing each token up to the host pool.
+    k_new = torch.randint(0, 120, (B, wl.head_dim), dtype=torch.uint8, device=dev)
+    lat_new = torch.zeros((B, wl.latent), dtype=torch.int16, device=dev)
+    gap = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cs):
+        with torch.cuda.graph(gap, stream=cs):
+            for lay in layers:
+                R.check(abi.echo_append(dims, lay.struct, batch.host_base.data_ptr(),
+                                        batch.ctx.data_ptr(), B, k_new.data_ptr(),
+                                        lat_new.data_ptr(), ws.ws, 0, cs.cuda_stream), "append")
+    gap.replay()
+    torch.cuda.synchronize()
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record()
+    gap.replay()
+    a1.record()
+    torch.cuda.synchronize()
+    st = int(ws.status.item())
+    if st != 0:
+        raise SystemExit(f"device status after append: {abi.echo_status_string(st)}")
+    append_ms = a0.elapsed_time(a1) / L
+    del gap
+    log(f"[bench] append: {append_ms * 1e3:.1f} us per layer ({B} tokens: {B * wl.head_dim} B "
+        f"of indexer K in HBM, {B * row} B of latents to the host pool)")
+
     # ------------------------------------------------------- CPU baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -405,6 +433,10 @@ def main():
         "phase_ms": {"indexer": round(idx_ms, 5), "topk": round(float(ph[:, 1].mean()), 5),
                      "alloc_evict": round(float(ph[:, 2].mean()), 5),
                      "recall": round(float(recall_ms.mean()), 5)},
+        "append": {"ms_per_layer": round(append_ms, 5), "tokens": B,
+                   "host_bytes": B * row, "hbm_bytes": B * wl.head_dim,
+                   "how": f"echo_append on all {L} layers back to back in a graph, contexts "
+                          "not advanced"},
         "hit_rate": round(hit, 5),
         "topk_shortcut_requests_last_layer": f"{shortcut_last}/{B}",
         "misses_per_layer_step": round(float(misses.mean()), 1),

@@ -248,6 +248,33 @@ int echo_recall(const echo_dims_t *dims, const echo_layer_t *layer, const echo_w
 /* Advance the layer's step counter t by one (skipped if ws->status is set). */
 int echo_step_advance(const echo_layer_t *layer, const echo_ws_t *ws, hipStream_t stream);
 
+/* Decode append and writeback: the step's new token joins every request's
+ * context.  The ECHO review ("Core method / in-graph per-layer cache
+ * management") keeps the indexer K resident on the GPU and backs each token's KV
+ * up to the host pool when it is generated, so eviction moves no data; its
+ * "Design trade-offs" section counts that writeback of every new token.
+ *   host_base [batch]  device: first host id of each request (as in echo_batch_t)
+ *   ctx_len   [batch]  device, in/out: the new token goes to host id
+ *                      host_base[b] + ctx_len[b]; with advance != 0 the call then
+ *                      adds one to ctx_len[b]
+ *   k_new  [batch][D]       device: the token's indexer key, e4m3, row-major; it is
+ *                           written into layer->k_index in the tiled layout
+ *   latent_new [batch][latent] device, 16-byte aligned: the token's bf16 latent,
+ *                           written into layer->host_kv (mapped pinned host memory)
+ * layer->k_index and layer->host_kv are written through although the layer
+ * struct declares them const for the other calls.  Call it once per layer after
+ * that layer's step, with advance != 0 only for the last layer of the step.  The
+ * token is not placed in the GPU pool (it becomes resident when prefetched or
+ * recalled).  Errors: ECHO_EINVAL (host checks; batch 0 is a no-op).  Device:
+ * ECHO_ECAPACITY if a request has no room (ctx_len = max_ctx, host id >= n_host,
+ * or the id falls in another request's range including its own new token),
+ * ECHO_EDEVARG if a slot already maps the host id; the lowest such request
+ * decides, and nothing is written. */
+int echo_append(const echo_dims_t *dims, const echo_layer_t *layer, const int32_t *host_base,
+                int32_t *ctx_len, int32_t batch, const uint8_t *k_new,
+                const uint16_t *latent_new, const echo_ws_t *ws, int advance,
+                hipStream_t stream);
+
 /* Steps a0-a8 for one layer and one decode step, in order, on `stream`: indexer
  * + prefetch, top-k with the EMA update (mode EMA only), protect/evict/alloc,
  * recall, and the step-counter advance. */

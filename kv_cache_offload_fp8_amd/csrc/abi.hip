@@ -301,6 +301,25 @@ int echo_recall(const echo_dims_t *dims, const echo_layer_t *layer, const echo_w
   return ECHO_OK;
 }
 
+int echo_append(const echo_dims_t *dims, const echo_layer_t *layer, const int32_t *host_base,
+                int32_t *ctx_len, int32_t batch, const uint8_t *k_new, const uint16_t *latent_new,
+                const echo_ws_t *ws, int advance, hipStream_t stream) {
+  int rc = check_dims(dims);
+  if (rc != ECHO_OK) return rc;
+  if (!layer_ok(layer, false) || !ws_ok(ws)) return ECHO_EINVAL;
+  if (batch < 0 || batch > dims->max_batch) return ECHO_EINVAL;
+  if (batch == 0) return ECHO_OK;
+  if (!host_base || !ctx_len || !k_new || !latent_new || ((uintptr_t)latent_new & 15) != 0)
+    return ECHO_EINVAL;
+  echo_batch_t bt;
+  bt.batch = batch;
+  bt.host_base = host_base;
+  bt.ctx_len = ctx_len;
+  const StepArgs a = make_args(*dims, layer, &bt, *ws, ECHO_THETA_POS_INF);
+  LAUNCH(launch_append(a, k_new, latent_new, ctx_len, advance ? 1 : 0, stream));
+  return ECHO_OK;
+}
+
 int echo_step_advance(const echo_layer_t *layer, const echo_ws_t *ws, hipStream_t stream) {
   if (!layer || !layer->ctl || !ws || !ws->status) return ECHO_EINVAL;
   StepArgs a;

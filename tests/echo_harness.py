@@ -15,6 +15,7 @@ from kv_cache_offload_fp8_amd import abi
 from kv_cache_offload_fp8_amd import runtime as R
 from oracle import oracle as O
 from synth import make_inputs
+from synth.gen import gen_append
 
 MODE_EMA, MODE_NEG_INF, MODE_POS_INF = abi.ECHO_THETA_EMA, abi.ECHO_THETA_NEG_INF, \
     abi.ECHO_THETA_POS_INF
@@ -53,14 +54,30 @@ def assert_scores_close(gpu: np.ndarray, q_codes, w, krows, ctx_note=""):
     return ref
 
 
+def tile_kidx(rows: np.ndarray) -> np.ndarray:
+    """Row-major indexer K [n, D] (n a multiple of 16) in the tiled layout of
+    include/echo.h: byte d of host id h at 16*D*(h/16) + 8*D*((d%32)/16) +
+    256*(d/32) + 16*(h%16) + d%16."""
+    n, D = rows.shape
+    h = np.arange(n)[:, None]
+    d = np.arange(D)[None, :]
+    off = 16 * D * (h // 16) + 8 * D * ((d % 32) // 16) + 256 * (d // 32) + 16 * (h % 16) + d % 16
+    out = np.empty(n * D, np.uint8)
+    out[off.ravel()] = rows.ravel()
+    return out.reshape(n, D)
+
+
 class Rig:
     def __init__(self, wl, steps, device="cuda", ctx=None, n_gpu=None, n_host=None, seed=0,
-                 keep_pool=True, max_ctx=None, layer=0, cap_div=None, top_k=None):
+                 keep_pool=True, max_ctx=None, layer=0, cap_div=None, top_k=None, room=0):
         if n_gpu is not None or n_host is not None or cap_div is not None or top_k is not None:
             wl = wl.scaled(n_gpu=n_gpu or wl.n_gpu, n_host=n_host or wl.n_host,
                            cap_div=cap_div or wl.cap_div, top_k=top_k or wl.top_k)
         self.wl = wl
-        self.inp = make_inputs(wl, layer=layer, device="cpu", seed=seed, steps=steps, ctx=ctx)
+        self.inp = make_inputs(wl, layer=layer, device="cpu", seed=seed, steps=steps, ctx=ctx,
+                               room=room)
+        self.layer_id = layer
+        self.seed = seed
         self.ctx = self.inp.ctx
         self.base = self.inp.host_base
         self.B = int(self.ctx.size)
@@ -83,7 +100,10 @@ class Rig:
         self.orc = O.OracleLayer(wl.heads, wl.head_dim, wl.top_k, wl.latent, wl.n_host, wl.n_gpu,
                                  max(1, self.B), wl.cap_div, wl.alpha, keep_pool=keep_pool)
         self.np_kidx = self.inp.np_kidx()
-        self.np_host = self.host.np
+        # the oracle's own copy of the host pool: bytes the GPU writes there are
+        # compared with it, not read back by the oracle
+        self.orc_host = self.host.np.copy()
+        self.np_host = self.orc_host
         self.np_w = self.inp.np_w()
         self.t = 0
         self.history = []
@@ -163,6 +183,29 @@ class Rig:
             torch.cuda.current_stream().synchronize()
             gp = self.layer.gpu_kv.cpu().numpy().view(np.uint16)
             assert np.array_equal(gp, self.orc.pool), (tag, "pool bytes")
+
+    # ------------------------------------------------------------ decode append
+    def append_and_compare(self, advance=True, expect_status=0):
+        """echo_append of this step's new tokens against the oracle's append: device
+        context lengths, the whole tiled indexer K (against the oracle's rows tiled
+        here, independently of the library) and the host pool bytes."""
+        k_new, lat_new = gen_append(self.wl, self.layer_id, self.B, self.t, self.seed)
+        kd = torch.as_tensor(k_new, device="cuda")
+        ld = torch.as_tensor(lat_new, device="cuda")
+        R.check(abi.echo_append(self.dims, self.layer.struct, self.batch.host_base.data_ptr(),
+                                self.batch.ctx.data_ptr(), self.B, kd.data_ptr(),
+                                ld.data_ptr(), self.ws.ws, int(advance), R.stream_handle()),
+                "echo_append")
+        torch.cuda.current_stream().synchronize()
+        rc = O.append(self.base, self.ctx, self.orc.h2g, k_new, lat_new.view(np.uint16),
+                      self.np_kidx, self.orc_host, self.dims.max_ctx, advance)
+        st = int(self.ws.status.item())
+        assert st == rc == expect_status, ("append status", st, rc, expect_status)
+        assert np.array_equal(self.batch.ctx.cpu().numpy(), self.ctx), "ctx_len"
+        assert np.array_equal(self.layer.kidx.cpu().numpy(), tile_kidx(self.np_kidx)), \
+            "tiled indexer K"
+        assert np.array_equal(self.host.np, self.orc_host), "host pool bytes"
+        return rc
 
     def gathered(self):
         """GPU-pool rows of every request's selected tokens, in selection order (what the
