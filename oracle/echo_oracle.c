@@ -52,6 +52,9 @@
  *  R10 Append: the step's new token takes host id host_base + ctx of its
  *      request; its indexer key and latent are written there and ctx grows by
  *      one.  It is not placed in the GPU pool.
+ *  R11 Attention input: the rows a sparse attention reads are the latents of
+ *      the selected tokens in selection order; without offloading they come
+ *      straight from the full host copy.  Unused rows (i >= n_sel) are zero.
  */
 #include <math.h>
 #include <stdint.h>
@@ -413,4 +416,25 @@ int orc_append(int B, int D, int latent, int64_t n_host, int32_t max_ctx,
   if (advance)
     for (int b = 0; b < B; ++b) ctx[b] += 1;
   return ORC_OK;
+}
+
+/* Attention input without offloading, [P1] "Core method / decode" (after the
+ * exact top-k every selected token's KV must be present before the sparse
+ * attention runs; "lossless" means the attention sees exactly these rows) and
+ * [P2] (prediction only decides when data moves, never which data is read).
+ * Reading R11: out[b][i] = host_kv[host_base[b] + sel_tok[b][i]] (`latent`
+ * values) for i < n_sel[b], zero for n_sel[b] <= i < k.  sel_tok is [B][k]. */
+void orc_gather(int B, int k, int latent, const int32_t *host_base, const int32_t *sel_tok,
+                const int32_t *n_sel, const uint16_t *host_kv, uint16_t *out) {
+  for (int b = 0; b < B; ++b) {
+    for (int i = 0; i < k; ++i) {
+      uint16_t *o = out + ((int64_t)b * k + i) * latent;
+      if (i < n_sel[b]) {
+        const int64_t h = (int64_t)host_base[b] + sel_tok[(int64_t)b * k + i];
+        memcpy(o, host_kv + h * latent, (size_t)latent * 2);
+      } else {
+        memset(o, 0, (size_t)latent * 2);
+      }
+    }
+  }
 }

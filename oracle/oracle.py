@@ -58,6 +58,9 @@ def lib() -> C.CDLL:
         _lib.orc_append.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int64, C.c_int32, C.c_void_p,
                                     C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                     C.c_void_p, C.c_int]
+        _lib.orc_gather.restype = None
+        _lib.orc_gather.argtypes = [C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p,
+                                    C.c_void_p, C.c_void_p, C.c_void_p]
         _lib.orc_layer_step.restype = C.c_int
         _lib.orc_layer_step.argtypes = [C.POINTER(Cfg), C.POINTER(State), C.c_int,
                                         C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
@@ -142,6 +145,20 @@ def append(host_base, ctx, h2g, k_new, lat_new, kidx, host_kv, max_ctx: int,
     return lib().orc_append(B, D, latent, kidx.shape[0], int(max_ctx), _p(host_base), _p(ctx),
                             _p(h2g), _p(k_new), _p(lat_new), _p(kidx),
                             _p(host_kv) if host_kv is not None else None, int(bool(advance)))
+
+
+def gather(host_base, sel_tok, n_sel, host_kv) -> np.ndarray:
+    """Attention input without offloading (orc_gather): uint16 [B, k, latent], the host
+    latents of each request's selected tokens in selection order, zero past n_sel."""
+    host_base = np.ascontiguousarray(host_base, np.int32)
+    sel_tok = np.ascontiguousarray(sel_tok, np.int32)
+    n_sel = np.ascontiguousarray(n_sel, np.int32)
+    host_kv = np.ascontiguousarray(host_kv, np.uint16)
+    B, k = sel_tok.shape
+    latent = host_kv.shape[1]
+    out = np.empty((B, k, latent), np.uint16)
+    lib().orc_gather(B, k, latent, _p(host_base), _p(sel_tok), _p(n_sel), _p(host_kv), _p(out))
+    return out
 
 
 def ema_update(theta: float, s_k: float, alpha: float = 0.5) -> float:

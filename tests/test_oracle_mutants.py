@@ -47,6 +47,8 @@ MUTANTS = {
     "append_overwrites_last_row": ("const int64_t h = (int64_t)host_base[b] + ctx[b];\n    memcpy",
                                    "const int64_t h = (int64_t)host_base[b] + ctx[b] - 1;\n"
                                    "    memcpy"),
+    "gather_ignores_host_base": ("const int64_t h = (int64_t)host_base[b] + sel_tok[(int64_t)b * k + i];",
+                                 "const int64_t h = sel_tok[(int64_t)b * k + i];"),
     "append_ignores_neighbours": ("if (h >= host_base[o] && h < (int64_t)host_base[o] + ctx[o] + 1) "
                                   "return ORC_ECAPACITY;",
                                   "if (0) return ORC_ECAPACITY;"),

@@ -443,3 +443,32 @@ def test_append_checks_room_and_mapping_and_writes_nothing_on_error():
     base3[-1] = kidx.shape[0] - int(ctx[-1])
     assert O.append(base3, ctx.copy(), h2g, k_new, lat_new, kidx, host, max_ctx=64) == \
         O.ECAPACITY
+
+
+# ---------------------------------------------------------- attention input
+# R11: rows that name themselves.  Host row h holds h's own bytes, so every
+# gathered row must decode to host_base[b] + sel_tok[b][i]; rows past n_sel are 0.
+
+def test_gather_reads_the_selected_host_rows_in_selection_order():
+    rng = np.random.default_rng(3)
+    B, k, latent, n_host = 3, 16, 8, 300
+    host = np.zeros((n_host, latent), np.uint16)
+    host[:, 0] = np.arange(n_host) & 0xFFFF
+    host[:, 1] = np.arange(n_host) >> 16
+    host[:, 2:] = 0xABCD
+    base = np.array([0, 100, 220], np.int32)
+    ctx = np.array([90, 110, 60], np.int32)
+    n_sel = np.array([16, 9, 0], np.int32)
+    sel = np.full((B, k), -1, np.int32)
+    for b in range(B):
+        sel[b, :n_sel[b]] = rng.choice(ctx[b], n_sel[b], replace=False)
+    out = O.gather(base, sel, n_sel, host)
+    assert out.shape == (B, k, latent)
+    for b in range(B):
+        for i in range(k):
+            if i < n_sel[b]:
+                h = int(out[b, i, 0]) | (int(out[b, i, 1]) << 16)
+                assert h == base[b] + sel[b, i]
+                assert (out[b, i, 2:] == 0xABCD).all()
+            else:
+                assert not out[b, i].any()
