@@ -352,6 +352,33 @@ def main():
     log(f"[bench] layer step {step_ms * 1e3:.1f} us; host-link floor "
         f"{link_floor_ms * 1e3:.1f} us ({link_floor_ms / step_ms:.1%})")
 
+    # ----------------------------------------------- attention input (gather)
+    # The last layer-step's selections (still in the workspace) gathered from layer
+    # 0's pool into the dense [B][k][latent] attention input, 16 calls back to back in
+    # a graph.  HBM-bound: each selected row is read once and every output row written.
+    n_sel_tot = int(ws.n_sel[:B].sum().item())
+    gout = torch.empty((B, wl.top_k, wl.latent), dtype=torch.int16, device=dev)
+    ngr = 16
+    ggr = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cs):
+        with torch.cuda.graph(ggr, stream=cs):
+            for _ in range(ngr):
+                R.check(abi.echo_gather(dims, layers[0].struct, batch.struct, ws.ws,
+                                        gout.data_ptr(), cs.cuda_stream), "gather")
+    ggr.replay()
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record()
+    ggr.replay()
+    g1.record()
+    torch.cuda.synchronize()
+    gather_ms = g0.elapsed_time(g1) / ngr
+    del ggr, gout
+    gather_bytes = (n_sel_tot + B * wl.top_k) * row
+    gather_gbps = gather_bytes / (gather_ms * 1e-3) / 1e9
+    log(f"[bench] attention-input gather: {gather_ms * 1e3:.1f} us for {n_sel_tot} rows = "
+        f"{gather_gbps:.0f} GB/s ({gather_gbps / HBM_PEAK_GBPS:.1%} of HBM peak)")
+
     # ----------------------------------------------- decode append (writeback)
     # One step's new tokens appended to every layer, back to back in a graph, without
     # advancing the contexts (each replay writes the same rows): the per-layer cost
@@ -433,6 +460,10 @@ def main():
         "phase_ms": {"indexer": round(idx_ms, 5), "topk": round(float(ph[:, 1].mean()), 5),
                      "alloc_evict": round(float(ph[:, 2].mean()), 5),
                      "recall": round(float(recall_ms.mean()), 5)},
+        "attention_input_gather": {"ms_per_layer": round(gather_ms, 5), "rows": n_sel_tot,
+                                   "bytes": gather_bytes, "hbm_gbps": round(gather_gbps, 1),
+                                   "frac_of_hbm_peak": round(gather_gbps / HBM_PEAK_GBPS, 4),
+                                   "how": f"echo_gather, {ngr} calls back to back in a graph"},
         "append": {"ms_per_layer": round(append_ms, 5), "tokens": B,
                    "host_bytes": B * row, "hbm_bytes": B * wl.head_dim,
                    "how": f"echo_append on all {L} layers back to back in a graph, contexts "

@@ -248,6 +248,17 @@ int echo_recall(const echo_dims_t *dims, const echo_layer_t *layer, const echo_w
 /* Advance the layer's step counter t by one (skipped if ws->status is set). */
 int echo_step_advance(const echo_layer_t *layer, const echo_ws_t *ws, hipStream_t stream);
 
+/* Attention input: out[b][i] = the GPU-pool row (latent bf16 values) of request
+ * b's i-th selected token, gpu_kv[ws->sel_slot[b][i]], for i < ws->n_sel[b], and
+ * zero rows for n_sel[b] <= i < k.  The ECHO review ("Core method / decode") runs
+ * the sparse attention only after the exact top-k and the recall of every
+ * missing selected token, so these rows equal what the attention would read with
+ * no offloading at all.  out: device, [batch][k][latent] bf16, 16-byte aligned,
+ * caller-owned.  Call after the layer's step; a no-op if ws->status is set.
+ * Errors: ECHO_EINVAL (host checks). */
+int echo_gather(const echo_dims_t *dims, const echo_layer_t *layer, const echo_batch_t *batch,
+                const echo_ws_t *ws, uint16_t *out, hipStream_t stream);
+
 /* Decode append and writeback: the step's new token joins every request's
  * context.  The ECHO review ("Core method / in-graph per-layer cache
  * management") keeps the indexer K resident on the GPU and backs each token's KV

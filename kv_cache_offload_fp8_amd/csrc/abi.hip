@@ -301,6 +301,18 @@ int echo_recall(const echo_dims_t *dims, const echo_layer_t *layer, const echo_w
   return ECHO_OK;
 }
 
+int echo_gather(const echo_dims_t *dims, const echo_layer_t *layer, const echo_batch_t *batch,
+                const echo_ws_t *ws, uint16_t *out, hipStream_t stream) {
+  int rc = check_dims(dims);
+  if (rc != ECHO_OK) return rc;
+  if (!layer_ok(layer, false) || !batch_ok(*dims, batch) || !ws_ok(ws)) return ECHO_EINVAL;
+  if (batch->batch == 0) return ECHO_OK;
+  if (!out || ((uintptr_t)out & 15) != 0) return ECHO_EINVAL;
+  const StepArgs a = make_args(*dims, layer, batch, *ws, ECHO_THETA_POS_INF);
+  LAUNCH(launch_gather(a, out, stream));
+  return ECHO_OK;
+}
+
 int echo_append(const echo_dims_t *dims, const echo_layer_t *layer, const int32_t *host_base,
                 int32_t *ctx_len, int32_t batch, const uint8_t *k_new, const uint16_t *latent_new,
                 const echo_ws_t *ws, int advance, hipStream_t stream) {

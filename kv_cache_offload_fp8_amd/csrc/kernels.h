@@ -62,6 +62,7 @@ hipError_t launch_score(const StepArgs &a, hipStream_t s);
 hipError_t launch_topk(const StepArgs &a, bool protect, hipStream_t s);
 hipError_t launch_protect(const StepArgs &a, hipStream_t s);
 hipError_t launch_manage(const StepArgs &a, bool recall, bool advance, hipStream_t s);
+hipError_t launch_gather(const StepArgs &a, uint16_t *out, hipStream_t s);
 hipError_t launch_append(const StepArgs &a, const uint8_t *k_new, const uint16_t *lat_new,
                          int32_t *ctx_io, int advance, hipStream_t s);
 hipError_t launch_recall(const StepArgs &a, hipStream_t s);
