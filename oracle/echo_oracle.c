@@ -55,6 +55,13 @@
  *  R11 Attention input: the rows a sparse attention reads are the latents of
  *      the selected tokens in selection order; without offloading they come
  *      straight from the full host copy.  Unused rows (i >= n_sel) are zero.
+ *  R12 Request lifecycle: releasing (cancelling) a request gives back the GPU
+ *      slot of every token of its host range, clears the range's host-to-GPU
+ *      map, resets its EMA threshold to "no estimate" and empties it
+ *      (ctx = 0); no bytes move, the host copy stays.  Admitting a request
+ *      into an empty batch row sets its host range and length after checking
+ *      that the range fits, overlaps no live request and holds no mapped
+ *      token; its threshold starts at "no estimate".
  */
 #include <math.h>
 #include <stdint.h>
@@ -62,6 +69,7 @@
 #include <string.h>
 
 #define ORC_OK 0
+#define ORC_EINVAL (-1)
 #define ORC_ECAPACITY (-4)
 #define ORC_EDEVARG (-6)
 
@@ -437,4 +445,67 @@ void orc_gather(int B, int k, int latent, const int32_t *host_base, const int32_
       }
     }
   }
+}
+
+/* Request cancellation, [P1] "Systemic flaws" (the paper leaves request
+ * cancellation open) and "Limitations and future work" (final top-k and
+ * attention input must stay equal to the no-offload baseline under request
+ * cancellation), with the state of "Core method / in-graph per-layer cache
+ * management".  Reading R12: for every request b with mask[b] != 0, each host
+ * id h of [host_base[b], host_base[b] + ctx[b]) that maps a slot g gives it
+ * back (g2h[g] = -1, free[g] = 1, prio[g] = -1) and h2g[h] becomes -1; then
+ * theta[b] = +inf and ctx[b] = 0.  A masked request whose range does not fit
+ * (ctx < 0, ctx > max_ctx, host_base < 0 or past n_host) gives ORC_EDEVARG,
+ * checked for all masked requests before anything changes. */
+int orc_release(int B, int64_t n_host, int32_t max_ctx, const int32_t *host_base, int32_t *ctx,
+                const int32_t *mask, int32_t *h2g, int32_t *g2h, int32_t *prio, uint8_t *freef,
+                float *theta) {
+  for (int b = 0; b < B; ++b) {
+    if (!mask[b]) continue;
+    if (ctx[b] < 0 || ctx[b] > max_ctx || host_base[b] < 0 ||
+        (int64_t)host_base[b] + ctx[b] > n_host)
+      return ORC_EDEVARG;
+  }
+  for (int b = 0; b < B; ++b) {
+    if (!mask[b]) continue;
+    for (int32_t s = 0; s < ctx[b]; ++s) {
+      const int64_t h = (int64_t)host_base[b] + s;
+      const int32_t g = h2g[h];
+      if (g >= 0) {
+        g2h[g] = -1;
+        freef[g] = 1;
+        prio[g] = -1;
+      }
+      h2g[h] = -1;
+    }
+    theta[b] = INFINITY;
+    ctx[b] = 0;
+  }
+  return ORC_OK;
+}
+
+/* Request admission, the other half of R12.  Request b (an empty batch row)
+ * takes the host range [base, base + len).  Checks, in order: b outside
+ * [0, B), len outside [0, max_ctx], base < 0 or base + len > n_host give
+ * ORC_EINVAL; a row still in use (ctx[b] != 0) gives ORC_EDEVARG; a range
+ * meeting the range of another request o with ctx[o] > 0 gives
+ * ORC_ECAPACITY; a host id of the range that some slot still maps gives
+ * ORC_EDEVARG.  Nothing changes on an error.  Otherwise host_base[b] = base,
+ * ctx[b] = len, theta[b] = +inf. */
+int orc_admit(int B, int64_t n_host, int32_t max_ctx, int32_t *host_base, int32_t *ctx,
+              const int32_t *h2g, float *theta, int b, int32_t base, int32_t len) {
+  if (b < 0 || b >= B || len < 0 || len > max_ctx || base < 0 || (int64_t)base + len > n_host)
+    return ORC_EINVAL;
+  if (ctx[b] != 0) return ORC_EDEVARG;
+  for (int o = 0; o < B; ++o) {
+    if (o == b || ctx[o] <= 0) continue;
+    const int64_t lo = host_base[o], hi = (int64_t)host_base[o] + ctx[o];
+    if ((int64_t)base < hi && lo < (int64_t)base + len) return ORC_ECAPACITY;
+  }
+  for (int32_t s = 0; s < len; ++s)
+    if (h2g[(int64_t)base + s] != -1) return ORC_EDEVARG;
+  host_base[b] = base;
+  ctx[b] = len;
+  theta[b] = INFINITY;
+  return ORC_OK;
 }

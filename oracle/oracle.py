@@ -18,7 +18,7 @@ SRC = os.path.join(HERE, "echo_oracle.c")
 LIB = os.path.join(HERE, "libecho_oracle.so")
 
 MODE_EMA, MODE_NEG_INF, MODE_POS_INF = 0, 1, 2
-OK, ECAPACITY, EDEVARG = 0, -4, -6
+OK, EINVAL, ECAPACITY, EDEVARG = 0, -1, -4, -6
 
 
 def build(force: bool = False) -> str:
@@ -59,6 +59,11 @@ def lib() -> C.CDLL:
                                     C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                     C.c_void_p, C.c_int]
         _lib.orc_gather.restype = None
+        _lib.orc_release.restype = C.c_int
+        _lib.orc_release.argtypes = [C.c_int, C.c_int64, C.c_int32] + [C.c_void_p] * 8
+        _lib.orc_admit.restype = C.c_int
+        _lib.orc_admit.argtypes = [C.c_int, C.c_int64, C.c_int32] + [C.c_void_p] * 4 + \
+            [C.c_int, C.c_int32, C.c_int32]
         _lib.orc_gather.argtypes = [C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p,
                                     C.c_void_p, C.c_void_p, C.c_void_p]
         _lib.orc_layer_step.restype = C.c_int
@@ -159,6 +164,31 @@ def gather(host_base, sel_tok, n_sel, host_kv) -> np.ndarray:
     out = np.empty((B, k, latent), np.uint16)
     lib().orc_gather(B, k, latent, _p(host_base), _p(sel_tok), _p(n_sel), _p(host_kv), _p(out))
     return out
+
+
+def release(layer, host_base, ctx, mask, max_ctx: int) -> int:
+    """Request cancellation (orc_release) on an OracleLayer's state: the masked
+    requests' slots and map rows are given back, theta resets, ctx (int32, in place)
+    becomes 0.  Returns OK or the error code."""
+    host_base = np.ascontiguousarray(host_base, np.int32)
+    assert ctx.dtype == np.int32 and ctx.flags["C_CONTIGUOUS"]
+    mask = np.ascontiguousarray(mask, np.int32)
+    B = int(ctx.size)
+    assert host_base.size == B and mask.size == B and layer.theta.size >= B
+    return lib().orc_release(B, layer.cfg.n_host, int(max_ctx), _p(host_base), _p(ctx),
+                             _p(mask), _p(layer.h2g), _p(layer.g2h), _p(layer.prio),
+                             _p(layer.free), _p(layer.theta))
+
+
+def admit(layer, host_base, ctx, b: int, base: int, length: int, max_ctx: int) -> int:
+    """Request admission (orc_admit) into batch row b: host_base and ctx (int32, in
+    place) take (base, length) and theta[b] resets if the checks pass.  Returns OK or
+    the error code."""
+    assert host_base.dtype == np.int32 and host_base.flags["C_CONTIGUOUS"]
+    assert ctx.dtype == np.int32 and ctx.flags["C_CONTIGUOUS"]
+    B = int(ctx.size)
+    return lib().orc_admit(B, layer.cfg.n_host, int(max_ctx), _p(host_base), _p(ctx),
+                           _p(layer.h2g), _p(layer.theta), int(b), int(base), int(length))
 
 
 def ema_update(theta: float, s_k: float, alpha: float = 0.5) -> float:

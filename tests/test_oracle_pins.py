@@ -472,3 +472,132 @@ def test_gather_reads_the_selected_host_rows_in_selection_order():
                 assert (out[b, i, 2:] == 0xABCD).all()
             else:
                 assert not out[b, i].any()
+
+
+# ------------------------------------------------------------ request lifecycle
+def _two_requests_all_tails_resident():
+    """Two requests with external scores that select each request's first and last
+    tokens (plus a few between), two steps: every selected token ends resident."""
+    n_host, n_gpu, k, latent = 64, 24, 4, 2
+    lay = O.OracleLayer(H=1, D=1, k=k, latent=latent, n_host=n_host, n_gpu=n_gpu, max_batch=2,
+                        cap_div=64)
+    hk = (np.arange(n_host * latent, dtype=np.uint16) + 1).reshape(n_host, latent)
+    base = np.array([0, 20], np.int32)
+    ctx = np.array([20, 30], np.int32)
+    q = np.zeros((2, 1, 1), np.uint16)
+    w = np.zeros((2, 1), np.float32)
+    kidx = np.zeros((n_host, 1), np.uint8)
+    for winners in (((0, 19, 5, 7), (0, 29, 11, 3)), ((19, 2, 4, 8), (29, 1, 12, 13))):
+        sc = np.zeros((2, 30), np.float32)
+        for b in range(2):
+            for r, s in enumerate(winners[b]):
+                sc[b, s] = 50.0 - r
+        o = lay.step(base, ctx, q, w, kidx, hk, mode=O.MODE_POS_INF, ext_scores=sc)
+        assert o["status"] == O.OK
+    return lay, hk, base, ctx
+
+
+def _state(lay):
+    return [a.copy() for a in (lay.h2g, lay.g2h, lay.prio, lay.free, lay.theta)]
+
+
+def test_release_gives_back_exactly_the_request_slots():
+    lay, hk, base, ctx = _two_requests_all_tails_resident()
+    lay.theta[:] = [1.5, 2.5]
+    h2g, g2h, prio, free, theta = _state(lay)
+    r0 = np.arange(base[1], base[1] + ctx[1])
+    mine = h2g[r0][h2g[r0] >= 0]
+    assert h2g[base[1]] >= 0 and h2g[base[1] + ctx[1] - 1] >= 0 and mine.size == 7
+    c = ctx.copy()
+    assert O.release(lay, base, c, [0, 1], max_ctx=64) == O.OK
+    assert list(c) == [20, 0]
+    assert (lay.h2g[r0] == -1).all()
+    assert (lay.g2h[mine] == -1).all() and (lay.free[mine] == 1).all()
+    assert (lay.prio[mine] == -1).all()
+    assert lay.theta[1] == np.inf and lay.theta[0] == np.float32(1.5)
+    keep = np.ones(lay.g2h.size, bool)
+    keep[mine] = False
+    other = np.setdiff1d(np.arange(lay.h2g.size), r0)
+    assert np.array_equal(lay.h2g[other], h2g[other])
+    for cur, old in ((lay.g2h, g2h), (lay.prio, prio), (lay.free, free)):
+        assert np.array_equal(cur[keep], old[keep])
+    # the invariants of the maps still hold
+    res = np.nonzero(lay.h2g >= 0)[0]
+    assert np.array_equal(lay.g2h[lay.h2g[res]], res)
+    assert np.array_equal(lay.free == 1, lay.g2h == -1)
+    assert np.array_equal(lay.free == 1, lay.prio == -1)
+    assert res.size + int(lay.free.sum()) == lay.g2h.size
+
+
+def test_release_of_every_request_returns_the_initial_state():
+    lay, hk, base, ctx = _two_requests_all_tails_resident()
+    c = ctx.copy()
+    assert O.release(lay, base, c, [1, 1], max_ctx=64) == O.OK
+    fresh = O.OracleLayer(H=1, D=1, k=4, latent=2, n_host=64, n_gpu=24, max_batch=2, cap_div=64)
+    for cur, new in zip(_state(lay), _state(fresh)):
+        assert np.array_equal(cur, new)
+    assert list(c) == [0, 0]
+
+
+def test_release_rejects_a_range_that_does_not_fit_and_changes_nothing():
+    lay, hk, base, ctx = _two_requests_all_tails_resident()
+    before = _state(lay)
+    for bad_base, bad_ctx in (([0, 20], [20, 65]), ([0, -1], [20, 30]), ([0, 40], [20, 30]),
+                              ([0, 20], [20, -2])):
+        c = np.array(bad_ctx, np.int32)
+        assert O.release(lay, np.array(bad_base, np.int32), c, [1, 1], max_ctx=64) == O.EDEVARG
+        assert list(c) == bad_ctx
+        for cur, old in zip(_state(lay), before):
+            assert np.array_equal(cur, old)
+
+
+def test_admit_checks_in_order_and_changes_nothing_on_error():
+    lay, hk, base, ctx = _two_requests_all_tails_resident()
+    b0, c0 = base.copy(), ctx.copy()
+    c0[1] = 0                                   # row 1 emptied without a release:
+    #                                             its tokens stay mapped (stale)
+    cases = [(2, 50, 4, O.EINVAL), (-1, 50, 4, O.EINVAL), (1, 50, 65, O.EINVAL),
+             (1, -1, 4, O.EINVAL), (1, 60, 5, O.EINVAL), (0, 50, 4, O.EDEVARG),
+             (1, 15, 10, O.ECAPACITY), (1, 19, 1, O.ECAPACITY), (1, 20, 10, O.EDEVARG),
+             (1, 48, 1, O.EDEVARG)]
+    lay.h2g[48] = 3                             # a stale id outside every range
+    before = _state(lay)
+    for b, bs, n, want in cases:
+        hb, cc = b0.copy(), c0.copy()
+        assert O.admit(lay, hb, cc, b, bs, n, max_ctx=64) == want, (b, bs, n)
+        assert np.array_equal(hb, b0) and np.array_equal(cc, c0)
+        for cur, old in zip(_state(lay), before):
+            assert np.array_equal(cur, old)
+    # a free range after request 1's: admitted, threshold back to "no estimate"
+    lay.theta[1] = 7.0
+    hb, cc = b0.copy(), c0.copy()
+    assert O.admit(lay, hb, cc, 1, 50, 10, max_ctx=64) == O.OK
+    assert list(hb) == [0, 50] and list(cc) == [20, 10] and lay.theta[1] == np.inf
+    # touching ranges do not overlap; an empty range fits anywhere that is free
+    hb, cc = b0.copy(), c0.copy()
+    assert O.admit(lay, hb, cc, 1, 20, 0, max_ctx=64) == O.OK and list(cc) == [20, 0]
+
+
+def test_readmitted_request_starts_cold_and_stays_lossless():
+    wk = _small_workload(seed=5, B=3, ctx=(700, 513, 300), n_gpu=600, steps=6)
+    lay_ref, ref = _run_modes(wk, O.MODE_EMA)
+    lay = O.OracleLayer(wk["H"], wk["D"], wk["k"], 8, wk["n_host"], wk["n_gpu"], 3, cap_div=32)
+    ctx = wk["ctx"].copy()
+    base = wk["host_base"].copy()
+    for t, q in enumerate(wk["qs"]):
+        if t == 3:
+            assert O.release(lay, base, ctx, [0, 1, 0], max_ctx=700) == O.OK
+            assert O.admit(lay, base, ctx, 1, int(wk["host_base"][1]), int(wk["ctx"][1]),
+                           max_ctx=700) == O.OK
+        o = lay.step(base, ctx, q, wk["w"], wk["kidx"], wk["hk"], mode=O.MODE_EMA)
+        assert o["status"] == O.OK
+        _check_invariants(lay, o, ctx, base, wk["hk"])
+        ro, rows = ref[t]
+        for b in range(3):                      # selection never depends on the cache
+            n = int(o["n_sel"][b])
+            assert n == ro["n_sel"][b]
+            assert np.array_equal(o["sel_tok"][b, :n], ro["sel_tok"][b, :n])
+            assert np.array_equal(lay.pool[o["sel_slot"][b, :n]], rows[b])
+        if t == 3:                              # cold: no estimate, nothing resident
+            assert o["n_pf"][1] == 0 and o["n_miss"][1] == o["n_sel"][1] == wk["k"]
+            assert lay.theta[1] == o["kth"][1]
