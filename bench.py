@@ -407,6 +407,36 @@ def main():
     log(f"[bench] append: {append_ms * 1e3:.1f} us per layer ({B} tokens: {B * wl.head_dim} B "
         f"of indexer K in HBM, {B * row} B of latents to the host pool)")
 
+    # ----------------------------------------------- request release and admission
+    # Request 0 cancelled on every layer (its slots and map rows given back, the free
+    # list rebuilt), then admitted again into its own range; each call once per layer,
+    # eagerly (a second release would find nothing to free), with commit on the last.
+    mask = torch.zeros(B, dtype=torch.int32, device=dev)
+    mask[0] = 1
+    resident0 = int((layers[-1].h2g[int(base[0]):int(base[0]) + int(ctx[0])] >= 0).sum().item())
+    torch.cuda.synchronize()
+    r0, r1, r2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    r0.record(cs)
+    for i, lay in enumerate(layers):
+        R.check(abi.echo_release(dims, lay.struct, batch.host_base.data_ptr(),
+                                 batch.ctx.data_ptr(), B, mask.data_ptr(), int(i == L - 1),
+                                 ws.ws, cs.cuda_stream), "release")
+    r1.record(cs)
+    for i, lay in enumerate(layers):
+        R.check(abi.echo_admit(dims, lay.struct, batch.host_base.data_ptr(),
+                               batch.ctx.data_ptr(), B, 0, int(base[0]), int(ctx[0]),
+                               int(i == L - 1), ws.ws, cs.cuda_stream), "admit")
+    r2.record(cs)
+    torch.cuda.synchronize()
+    st = int(ws.status.item())
+    if st != 0:
+        raise SystemExit(f"device status after release/admit: {abi.echo_status_string(st)}")
+    release_ms = r0.elapsed_time(r1) / L
+    admit_ms = r1.elapsed_time(r2) / L
+    log(f"[bench] release of one request ({int(ctx[0])} tokens, {resident0} resident on the "
+        f"last layer): {release_ms * 1e3:.1f} us per layer; admission {admit_ms * 1e3:.1f} us "
+        "per layer")
+
     # ------------------------------------------------------- CPU baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -468,6 +498,11 @@ def main():
                    "host_bytes": B * row, "hbm_bytes": B * wl.head_dim,
                    "how": f"echo_append on all {L} layers back to back in a graph, contexts "
                           "not advanced"},
+        "lifecycle": {"release_ms_per_layer": round(release_ms, 5),
+                      "admit_ms_per_layer": round(admit_ms, 5), "request_tokens": int(ctx[0]),
+                      "resident_last_layer": resident0,
+                      "how": f"echo_release then echo_admit of request 0 on all {L} layers, "
+                             "eager, events on the launch stream"},
         "hit_rate": round(hit, 5),
         "topk_shortcut_requests_last_layer": f"{shortcut_last}/{B}",
         "misses_per_layer_step": round(float(misses.mean()), 1),

@@ -286,6 +286,44 @@ int echo_append(const echo_dims_t *dims, const echo_layer_t *layer, const int32_
                 const uint16_t *latent_new, const echo_ws_t *ws, int advance,
                 hipStream_t stream);
 
+/* Request release (cancellation) between decode steps.  The ECHO review leaves
+ * request cancellation open ("Systemic flaws") and asks that top-k and attention
+ * input stay equal to the no-offload baseline when requests are cancelled
+ * ("Limitations and future work"); the state is that of "Core method / in-graph
+ * per-layer cache management".  For every request b with mask[b] != 0, each host
+ * id of [host_base[b], host_base[b] + ctx_len[b]) that holds a GPU slot gives it
+ * back (g2h = -1, free = 1, prio = -1), the range's h2g rows become -1,
+ * theta[b] (and guard[b]) become +inf; no bytes move.  Then the ascending free
+ * list (meta.idxbuf, ctl[ECHO_CTL_NFREE]) is rebuilt.  With commit != 0,
+ * ctx_len[b] of every released request becomes 0.
+ *   host_base [batch], ctx_len [batch] (in/out), mask [batch]: device int32
+ * Call it between steps, once per layer, with commit != 0 only for the last
+ * layer (the batch row is shared by the layers).  Errors:
+ * ECHO_EINVAL (host checks; batch 0 is a no-op).  Device: ECHO_EDEVARG if a
+ * masked request's range does not fit (ctx_len outside [0, max_ctx], host_base
+ * < 0 or past n_host); all are checked first and nothing changes.  A no-op
+ * while ws->status holds an error. */
+int echo_release(const echo_dims_t *dims, const echo_layer_t *layer, const int32_t *host_base,
+                 int32_t *ctx_len, int32_t batch, const int32_t *mask, int commit,
+                 const echo_ws_t *ws, hipStream_t stream);
+
+/* Request admission into an empty batch row b (the other half of the lifecycle
+ * above): theta[b] = guard[b] = +inf (no estimate yet) and, with commit != 0,
+ * row b takes host ids [base, base + len) (host_base[b] = base, ctx_len[b] =
+ * len).  The caller has written (or will append) the range's indexer keys and
+ * host latents.
+ *   host_base [batch], ctx_len [batch]: device int32, in/out (row b is written)
+ * Errors: ECHO_EINVAL (host checks: b outside [0, batch), len outside
+ * [0, max_ctx], base < 0, base + len > n_host; nothing enqueued).  Device, in
+ * this order: ECHO_EDEVARG if ctx_len[b] != 0 (the row is in use: release it
+ * first), ECHO_ECAPACITY if the range meets the range of another request with
+ * ctx_len > 0, ECHO_EDEVARG if some slot still maps a host id of the range.
+ * Nothing is written on an error; a no-op while ws->status holds an error.  One
+ * call per layer, with commit != 0 only for the last, like echo_release. */
+int echo_admit(const echo_dims_t *dims, const echo_layer_t *layer, int32_t *host_base,
+               int32_t *ctx_len, int32_t batch, int32_t b, int32_t base, int32_t len,
+               int commit, const echo_ws_t *ws, hipStream_t stream);
+
 /* Steps a0-a8 for one layer and one decode step, in order, on `stream`: indexer
  * + prefetch, top-k with the EMA update (mode EMA only), protect/evict/alloc,
  * recall, and the step-counter advance. */

@@ -23,7 +23,7 @@ ECHO_CTL_STEP, ECHO_CTL_NFREE, ECHO_CTL_WORDS = 0, 1, 4
 EXPORTS = ("echo_meta_bytes", "echo_ws_bytes", "echo_ws_bind", "echo_meta_init",
            "echo_ws_reset", "echo_kindex_pack", "echo_indexer_prefetch", "echo_topk",
            "echo_cache_alloc_evict", "echo_recall", "echo_step_advance", "echo_layer_step",
-           "echo_append", "echo_gather", "echo_status_string")
+           "echo_append", "echo_gather", "echo_release", "echo_admit", "echo_status_string")
 
 P = C.c_void_p
 
@@ -83,6 +83,9 @@ def lib() -> C.CDLL:
             "echo_layer_step": (C.c_int, [dp, lp, bp, wp, C.c_int, P]),
             "echo_append": (C.c_int, [dp, lp, P, P, C.c_int32, P, P, wp, C.c_int, P]),
             "echo_gather": (C.c_int, [dp, lp, bp, wp, P, P]),
+            "echo_release": (C.c_int, [dp, lp, P, P, C.c_int32, P, C.c_int, wp, P]),
+            "echo_admit": (C.c_int, [dp, lp, P, P, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                     C.c_int, wp, P]),
             "echo_status_string": (C.c_char_p, [C.c_int]),
         }
         for name, (res, args) in sigs.items():
@@ -159,6 +162,21 @@ def echo_append(dims, layer, host_base: int, ctx_len: int, batch: int, k_new: in
 def echo_gather(dims, layer, batch, ws, out: int, stream: int) -> int:
     """out: device pointer to [batch][k][latent] bf16 (16-byte aligned)."""
     return lib().echo_gather(C.byref(dims), _ref(layer), _ref(batch), _ref(ws), out, stream)
+
+
+def echo_release(dims, layer, host_base: int, ctx_len: int, batch: int, mask: int,
+                 commit: int, ws, stream: int) -> int:
+    """host_base, ctx_len, mask: device int32 pointers (with commit, ctx_len of the
+    released requests becomes 0)."""
+    return lib().echo_release(C.byref(dims), _ref(layer), host_base, ctx_len, batch, mask,
+                              commit, _ref(ws), stream)
+
+
+def echo_admit(dims, layer, host_base: int, ctx_len: int, batch: int, b: int, base: int,
+               length: int, commit: int, ws, stream: int) -> int:
+    """host_base, ctx_len: device int32 pointers; with commit, row b takes (base, length)."""
+    return lib().echo_admit(C.byref(dims), _ref(layer), host_base, ctx_len, batch, b, base,
+                            length, commit, _ref(ws), stream)
 
 
 def echo_status_string(code: int) -> str:

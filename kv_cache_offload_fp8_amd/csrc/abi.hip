@@ -332,6 +332,43 @@ int echo_append(const echo_dims_t *dims, const echo_layer_t *layer, const int32_
   return ECHO_OK;
 }
 
+int echo_release(const echo_dims_t *dims, const echo_layer_t *layer, const int32_t *host_base,
+                 int32_t *ctx_len, int32_t batch, const int32_t *mask, int commit,
+                 const echo_ws_t *ws, hipStream_t stream) {
+  int rc = check_dims(dims);
+  if (rc != ECHO_OK) return rc;
+  if (!layer_ok(layer, true) || !ws_ok(ws)) return ECHO_EINVAL;
+  if (batch < 0 || batch > dims->max_batch) return ECHO_EINVAL;
+  if (batch == 0) return ECHO_OK;
+  if (!host_base || !ctx_len || !mask) return ECHO_EINVAL;
+  echo_batch_t bt;
+  bt.batch = batch;
+  bt.host_base = host_base;
+  bt.ctx_len = ctx_len;
+  const StepArgs a = make_args(*dims, layer, &bt, *ws, ECHO_THETA_POS_INF);
+  LAUNCH(launch_release(a, mask, ctx_len, commit ? 1 : 0, stream));
+  return ECHO_OK;
+}
+
+int echo_admit(const echo_dims_t *dims, const echo_layer_t *layer, int32_t *host_base,
+               int32_t *ctx_len, int32_t batch, int32_t b, int32_t base, int32_t len,
+               int commit, const echo_ws_t *ws, hipStream_t stream) {
+  int rc = check_dims(dims);
+  if (rc != ECHO_OK) return rc;
+  if (!layer_ok(layer, true) || !ws_ok(ws)) return ECHO_EINVAL;
+  if (batch < 0 || batch > dims->max_batch || !host_base || !ctx_len) return ECHO_EINVAL;
+  if (b < 0 || b >= batch || len < 0 || len > dims->max_ctx || base < 0 ||
+      (int64_t)base + len > dims->n_host)
+    return ECHO_EINVAL;
+  echo_batch_t bt;
+  bt.batch = batch;
+  bt.host_base = host_base;
+  bt.ctx_len = ctx_len;
+  const StepArgs a = make_args(*dims, layer, &bt, *ws, ECHO_THETA_POS_INF);
+  LAUNCH(launch_admit(a, b, base, len, host_base, ctx_len, commit ? 1 : 0, stream));
+  return ECHO_OK;
+}
+
 int echo_step_advance(const echo_layer_t *layer, const echo_ws_t *ws, hipStream_t stream) {
   if (!layer || !layer->ctl || !ws || !ws->status) return ECHO_EINVAL;
   StepArgs a;

@@ -65,6 +65,10 @@ hipError_t launch_manage(const StepArgs &a, bool recall, bool advance, hipStream
 hipError_t launch_gather(const StepArgs &a, uint16_t *out, hipStream_t s);
 hipError_t launch_append(const StepArgs &a, const uint8_t *k_new, const uint16_t *lat_new,
                          int32_t *ctx_io, int advance, hipStream_t s);
+hipError_t launch_release(const StepArgs &a, const int32_t *mask, int32_t *ctx_io, int commit,
+                          hipStream_t s);
+hipError_t launch_admit(const StepArgs &a, int b, int32_t base, int32_t len, int32_t *hb_io,
+                        int32_t *ctx_io, int commit, hipStream_t s);
 hipError_t launch_recall(const StepArgs &a, hipStream_t s);
 hipError_t launch_step_advance(const StepArgs &a, hipStream_t s);
 hipError_t launch_meta_init(const StepArgs &a, hipStream_t s);

@@ -207,6 +207,46 @@ class Rig:
         assert np.array_equal(self.host.np, self.orc_host), "host pool bytes"
         return rc
 
+    # ------------------------------------------------------------ request lifecycle
+    def release_and_compare(self, mask, commit=True, expect_status=0):
+        """echo_release of the masked requests against the oracle's release: status,
+        batch rows, maps, priorities, free flags, thresholds and the free list."""
+        mask = np.asarray(mask, np.int32)
+        m = torch.as_tensor(mask, device="cuda")
+        R.check(abi.echo_release(self.dims, self.layer.struct, self.batch.host_base.data_ptr(),
+                                 self.batch.ctx.data_ptr(), self.B, m.data_ptr(), int(commit),
+                                 self.ws.ws, R.stream_handle()), "echo_release")
+        rc = O.release(self.orc, self.base, self.ctx, mask, self.dims.max_ctx, commit)
+        self._compare_lifecycle(rc, expect_status, "release")
+        return rc
+
+    def admit_and_compare(self, b, base, length, commit=True, expect_status=0):
+        """echo_admit of row b against the oracle's admission (a host-side rejection
+        must be the oracle's EINVAL, with nothing enqueued)."""
+        ret = abi.echo_admit(self.dims, self.layer.struct, self.batch.host_base.data_ptr(),
+                             self.batch.ctx.data_ptr(), self.B, int(b), int(base), int(length),
+                             int(commit), self.ws.ws, R.stream_handle())
+        rc = O.admit(self.orc, self.base, self.ctx, b, base, length, self.dims.max_ctx, commit)
+        if ret != abi.ECHO_OK:
+            assert ret == rc == expect_status == O.EINVAL, ("admit", ret, rc, expect_status)
+            return rc
+        self._compare_lifecycle(rc, expect_status, "admit")
+        return rc
+
+    def _compare_lifecycle(self, rc, expect_status, tag):
+        torch.cuda.current_stream().synchronize()
+        st = int(self.ws.status.item())
+        assert st == rc == expect_status, (tag, "status", st, rc, expect_status)
+        assert np.array_equal(self.batch.ctx.cpu().numpy(), self.ctx), (tag, "ctx_len")
+        assert np.array_equal(self.batch.host_base.cpu().numpy(), self.base), (tag, "host_base")
+        g = self.layer.state()
+        for name in ("h2g", "g2h", "prio", "free"):
+            assert np.array_equal(g[name], getattr(self.orc, name)), (tag, name)
+        assert np.array_equal(g["theta"][: self.B], self.orc.theta[: self.B]), (tag, "theta")
+        nfree = int(self.orc.free.sum())
+        assert g["nfree"] == nfree, (tag, "nfree", g["nfree"], nfree)
+        assert np.array_equal(g["idxbuf"][:nfree], np.nonzero(self.orc.free)[0]), (tag, "idxbuf")
+
     def gathered(self):
         """GPU-pool rows of every request's selected tokens, in selection order (what the
         sparse attention of the step would read)."""

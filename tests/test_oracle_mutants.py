@@ -55,10 +55,11 @@ MUTANTS = {
                                  "(int64_t)host_base[b] + s;\n      const int32_t g = h2g[h];",
                                  "for (int32_t s = 0; s < ctx[b] - 1; ++s) {\n      const int64_t h = "
                                  "(int64_t)host_base[b] + s;\n      const int32_t g = h2g[h];"),
-    "release_keeps_threshold": ("    theta[b] = INFINITY;\n    ctx[b] = 0;\n", "    ctx[b] = 0;\n"),
+    "release_keeps_threshold": ("    theta[b] = INFINITY;\n    if (commit) ctx[b] = 0;\n",
+                                "    if (commit) ctx[b] = 0;\n"),
     "admit_ignores_overlap": ("if ((int64_t)base < hi && lo < (int64_t)base + len) return ORC_ECAPACITY;",
                               "(void)lo;\n    (void)hi;"),
-    "admit_keeps_threshold": ("  ctx[b] = len;\n  theta[b] = INFINITY;\n", "  ctx[b] = len;\n"),
+    "admit_keeps_threshold": ("  theta[b] = INFINITY;\n  if (commit) {", "  if (commit) {"),
     "append_ignores_neighbours": ("if (h >= host_base[o] && h < (int64_t)host_base[o] + ctx[o] + 1) "
                                   "return ORC_ECAPACITY;",
                                   "if (0) return ORC_ECAPACITY;"),

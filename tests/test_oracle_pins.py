@@ -601,3 +601,21 @@ def test_readmitted_request_starts_cold_and_stays_lossless():
         if t == 3:                              # cold: no estimate, nothing resident
             assert o["n_pf"][1] == 0 and o["n_miss"][1] == o["n_sel"][1] == wk["k"]
             assert lay.theta[1] == o["kth"][1]
+
+
+def test_lifecycle_without_commit_leaves_the_batch_row_to_the_last_layer():
+    lay, hk, base, ctx = _two_requests_all_tails_resident()
+    lay2, _, _, _ = _two_requests_all_tails_resident()
+    c = ctx.copy()
+    assert O.release(lay, base, c, [0, 1], max_ctx=64, commit=False) == O.OK
+    assert list(c) == [20, 30] and (lay.h2g[20:50] == -1).all()
+    assert O.release(lay2, base, c, [0, 1], max_ctx=64) == O.OK   # the last layer
+    assert list(c) == [20, 0]
+    for cur, new in zip(_state(lay), _state(lay2)):
+        assert np.array_equal(cur, new)
+    hb = base.copy()
+    lay.theta[1] = 3.0
+    assert O.admit(lay, hb, c, 1, 20, 30, max_ctx=64, commit=False) == O.OK
+    assert list(hb) == [0, 20] and list(c) == [20, 0] and lay.theta[1] == np.inf
+    assert O.admit(lay2, hb, c, 1, 24, 26, max_ctx=64) == O.OK
+    assert list(hb) == [0, 24] and list(c) == [20, 26]
