@@ -62,6 +62,19 @@
  *      into an empty batch row sets its host range and length after checking
  *      that the range fits, overlaps no live request and holds no mapped
  *      token; its threshold starts at "no estimate".
+ *  R13 Chunked prefill: one request's history of N tokens is fixed while a
+ *      chunk of C queries is scored against it (the chunk's own tokens are
+ *      not offloaded yet).  Each query keeps its exact top-k.  Its coarse
+ *      candidates are the tokens whose 256-bucket key of
+ *      fp16(fp32(score - pred)) lies strictly above the bucket where the
+ *      count from the top first reaches k (every token if N <= k); pred is
+ *      the caller's predicted k-th score for the query (0 if none given).
+ *      The union of the candidates is installed first (the transfer that
+ *      overlaps the next chunk's scoring), then the rest of the union of the
+ *      selections, each at the next ascending free slot, with priority t.
+ *      The pool is sized to hold the chunk's union: a prefill chunk evicts
+ *      nothing and reports a capacity error, changing nothing, if the free
+ *      slots do not suffice.
  */
 #include <math.h>
 #include <stdint.h>
@@ -454,12 +467,13 @@ void orc_gather(int B, int k, int latent, const int32_t *host_base, const int32_
  * management".  Reading R12: for every request b with mask[b] != 0, each host
  * id h of [host_base[b], host_base[b] + ctx[b]) that maps a slot g gives it
  * back (g2h[g] = -1, free[g] = 1, prio[g] = -1) and h2g[h] becomes -1; then
- * theta[b] = +inf and ctx[b] = 0.  A masked request whose range does not fit
+ * theta[b] = +inf, and with `commit` ctx[b] = 0 (the batch row is shared by all
+ * layers: it is emptied with the last one).  A masked request whose range does not fit
  * (ctx < 0, ctx > max_ctx, host_base < 0 or past n_host) gives ORC_EDEVARG,
  * checked for all masked requests before anything changes. */
 int orc_release(int B, int64_t n_host, int32_t max_ctx, const int32_t *host_base, int32_t *ctx,
                 const int32_t *mask, int32_t *h2g, int32_t *g2h, int32_t *prio, uint8_t *freef,
-                float *theta) {
+                float *theta, int commit) {
   for (int b = 0; b < B; ++b) {
     if (!mask[b]) continue;
     if (ctx[b] < 0 || ctx[b] > max_ctx || host_base[b] < 0 ||
@@ -479,7 +493,7 @@ int orc_release(int B, int64_t n_host, int32_t max_ctx, const int32_t *host_base
       h2g[h] = -1;
     }
     theta[b] = INFINITY;
-    ctx[b] = 0;
+    if (commit) ctx[b] = 0;
   }
   return ORC_OK;
 }
@@ -490,10 +504,10 @@ int orc_release(int B, int64_t n_host, int32_t max_ctx, const int32_t *host_base
  * ORC_EINVAL; a row still in use (ctx[b] != 0) gives ORC_EDEVARG; a range
  * meeting the range of another request o with ctx[o] > 0 gives
  * ORC_ECAPACITY; a host id of the range that some slot still maps gives
- * ORC_EDEVARG.  Nothing changes on an error.  Otherwise host_base[b] = base,
- * ctx[b] = len, theta[b] = +inf. */
+ * ORC_EDEVARG.  Nothing changes on an error.  Otherwise theta[b] = +inf, and
+ * with `commit` (the last layer) host_base[b] = base and ctx[b] = len. */
 int orc_admit(int B, int64_t n_host, int32_t max_ctx, int32_t *host_base, int32_t *ctx,
-              const int32_t *h2g, float *theta, int b, int32_t base, int32_t len) {
+              const int32_t *h2g, float *theta, int b, int32_t base, int32_t len, int commit) {
   if (b < 0 || b >= B || len < 0 || len > max_ctx || base < 0 || (int64_t)base + len > n_host)
     return ORC_EINVAL;
   if (ctx[b] != 0) return ORC_EDEVARG;
@@ -504,8 +518,164 @@ int orc_admit(int B, int64_t n_host, int32_t max_ctx, int32_t *host_base, int32_
   }
   for (int32_t s = 0; s < len; ++s)
     if (h2g[(int64_t)base + s] != -1) return ORC_EDEVARG;
-  host_base[b] = base;
-  ctx[b] = len;
   theta[b] = INFINITY;
+  if (commit) {
+    host_base[b] = base;
+    ctx[b] = len;
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------ chunked prefill */
+
+/* IEEE binary16 bits of an fp32 value, round to nearest, ties to even
+ * (magnitudes from 65520 up become infinity).  Written from the format: a
+ * normal half has 10 fraction bits, exponent bias 15; a subnormal is m*2^-24.
+ * NaN gives 0x7E00. */
+uint16_t orc_f16_bits(float x) {
+  const uint16_t sign = signbit(x) ? 0x8000 : 0;
+  double a = fabs((double)x);
+  if (isnan(x)) return 0x7E00;
+  if (a >= 65536.0) return sign | 0x7C00;
+  int e;
+  frexp(a, &e); /* a = f * 2^e, f in [0.5, 1): the leading bit is 2^(e-1) */
+  e -= 1;
+  if (a == 0.0) return sign;
+  double quantum = e < -14 ? ldexp(1.0, -24) : ldexp(1.0, e - 10);
+  double m = nearbyint(a / quantum); /* exact quotient, ties to even */
+  if (e < -14) return sign | (uint16_t)m; /* m = 1024 is the smallest normal */
+  return sign | (uint16_t)(((e + 15) << 10) + (int)m - 1024);
+}
+
+/* The 256 coarse buckets: the top byte of an order key of the half bits
+ * (larger value, larger key; -0 counts as +0). */
+int orc_f16_bucket(uint16_t u) {
+  if (u == 0x8000) u = 0;
+  const uint16_t key = (u & 0x8000) ? (uint16_t)~u : (uint16_t)(u | 0x8000);
+  return key >> 8;
+}
+
+/* Coarse bucket of a score, shifted by the predicted k-th score: the
+ * difference is taken in fp32, then rounded to half precision. */
+static int coarse_bucket(float score, float pred) {
+  const float d = score - pred;
+  return orc_f16_bucket(orc_f16_bits(d));
+}
+
+typedef struct {
+  float *scores;     /* [C][N]                                         */
+  int32_t *sel;      /* [C][k]  each query's top-k, ascending           */
+  int32_t *n_sel;    /* [C]                                             */
+  float *kth;        /* [C]     k-th highest score                      */
+  int32_t *beta;     /* [C]     boundary bucket, -1 if N <= k           */
+  int32_t *n_qcand;  /* [C]     coarse candidates of each query         */
+  int32_t *cand;     /* [N]     union of the candidates, ascending      */
+  int32_t *uni;      /* [N]     union of the selections, ascending      */
+  int32_t *pf_h;     /* [N]     candidate installs: host id, slot       */
+  int32_t *pf_g;
+  int32_t *miss_h;   /* [N]     remaining installs: host id, slot       */
+  int32_t *miss_g;
+  int32_t n_cand, n_uni, n_pf, n_miss;
+} orc_prefill_out;
+
+/* One prefill chunk, [P1] "Core method / prefill" (query chunks; chunk i's
+ * identified candidates move while chunk i+1 is scored; a 256-bucket coarse
+ * histogram keeps the strictly-high buckets and leaves the threshold bucket
+ * for later; subtracting the predicted k-th score refines the buckets near
+ * the boundary; the exact fetch afterwards covers what was missed) and
+ * "Core method / prefetch inside the indexer pipeline" (prefill splits the
+ * indexer's work by query chunk).  Reading R13.
+ * q: bf16 [C][H][D]; w: fp32 [C][H]; kidx: e4m3 [n_host][D]; the history is
+ * host ids hb .. hb+N-1; pred: [C] or NULL; ext_scores: [C][N] or NULL.
+ * Returns ORC_OK or ORC_ECAPACITY (outputs up to the unions still set). */
+int orc_prefill_chunk(const orc_cfg *c, orc_state *st, int C, int32_t hb, int64_t N,
+                      const uint16_t *q, const float *w, const uint8_t *kidx, const float *pred,
+                      const uint16_t *host_kv, const float *ext_scores, orc_prefill_out *o) {
+  const int k = c->k;
+  /* scores, one query at a time */
+  for (int i = 0; i < C; ++i) {
+    float *row = o->scores + (int64_t)i * N;
+    if (ext_scores)
+      memcpy(row, ext_scores + (int64_t)i * N, sizeof(float) * (size_t)N);
+    else
+      orc_scores(c->H, c->D, q + (int64_t)i * c->H * c->D, w + (int64_t)i * c->H,
+                 kidx + (int64_t)hb * c->D, N, row);
+  }
+  uint8_t *cflag = (uint8_t *)calloc((size_t)(N > 0 ? N : 1), 1);
+  uint8_t *uflag = (uint8_t *)calloc((size_t)(N > 0 ? N : 1), 1);
+  for (int i = 0; i < C; ++i) {
+    const float *row = o->scores + (int64_t)i * N;
+    /* coarse candidates */
+    int32_t nq = 0;
+    if (N <= k) {
+      o->beta[i] = -1;
+      for (int64_t s = 0; s < N; ++s) cflag[s] = 1;
+      nq = (int32_t)N;
+    } else {
+      const float p = pred ? pred[i] : 0.0f;
+      int64_t hist[256] = {0};
+      for (int64_t s = 0; s < N; ++s) hist[coarse_bucket(row[s], p)] += 1;
+      int beta = 255;
+      int64_t above = 0; /* tokens in buckets higher than beta */
+      while (above + hist[beta] < k) above += hist[beta--];
+      o->beta[i] = beta;
+      for (int64_t s = 0; s < N; ++s)
+        if (coarse_bucket(row[s], p) > beta) {
+          cflag[s] = 1;
+          ++nq;
+        }
+    }
+    o->n_qcand[i] = nq;
+    /* exact top-k */
+    int32_t *sel = o->sel + (int64_t)i * k;
+    o->n_sel[i] = orc_topk(row, N, k, sel, &o->kth[i]);
+    for (int j = 0; j < o->n_sel[i]; ++j) uflag[sel[j]] = 1;
+  }
+  o->n_cand = o->n_uni = 0;
+  for (int64_t s = 0; s < N; ++s) {
+    if (cflag[s]) o->cand[o->n_cand++] = (int32_t)s;
+    if (uflag[s]) o->uni[o->n_uni++] = (int32_t)s;
+  }
+  free(cflag);
+  free(uflag);
+  o->n_pf = o->n_miss = 0;
+  /* capacity first: nothing changes if the union does not fit */
+  int32_t *F = (int32_t *)malloc(sizeof(int32_t) * (size_t)(c->n_gpu > 0 ? c->n_gpu : 1));
+  int32_t nF = 0;
+  for (int32_t g = 0; g < c->n_gpu; ++g)
+    if (st->freef[g]) F[nF++] = g;
+  int64_t need = 0;
+  for (int32_t j = 0; j < o->n_uni; ++j)
+    if (st->h2g[(int64_t)hb + o->uni[j]] == -1) ++need;
+  if (need > nF) {
+    free(F);
+    return ORC_ECAPACITY;
+  }
+  const int32_t t = st->t;
+  int32_t next = 0;
+  for (int32_t j = 0; j < o->n_cand; ++j) { /* the early transfer */
+    const int64_t h = (int64_t)hb + o->cand[j];
+    if (st->h2g[h] >= 0) {
+      st->prio[st->h2g[h]] = t;
+    } else {
+      const int32_t g = F[next++];
+      install(c, st, h, g, host_kv);
+      o->pf_h[o->n_pf] = (int32_t)h;
+      o->pf_g[o->n_pf++] = g;
+    }
+  }
+  for (int32_t j = 0; j < o->n_uni; ++j) { /* the exact fetch */
+    const int64_t h = (int64_t)hb + o->uni[j];
+    if (st->h2g[h] >= 0) {
+      st->prio[st->h2g[h]] = t;
+    } else {
+      const int32_t g = F[next++];
+      install(c, st, h, g, host_kv);
+      o->miss_h[o->n_miss] = (int32_t)h;
+      o->miss_g[o->n_miss++] = g;
+    }
+  }
+  free(F);
+  st->t = t + 1;
   return ORC_OK;
 }

@@ -60,10 +60,19 @@ def lib() -> C.CDLL:
                                     C.c_void_p, C.c_int]
         _lib.orc_gather.restype = None
         _lib.orc_release.restype = C.c_int
-        _lib.orc_release.argtypes = [C.c_int, C.c_int64, C.c_int32] + [C.c_void_p] * 8
+        _lib.orc_release.argtypes = [C.c_int, C.c_int64, C.c_int32] + [C.c_void_p] * 8 + \
+            [C.c_int]
         _lib.orc_admit.restype = C.c_int
         _lib.orc_admit.argtypes = [C.c_int, C.c_int64, C.c_int32] + [C.c_void_p] * 4 + \
-            [C.c_int, C.c_int32, C.c_int32]
+            [C.c_int, C.c_int32, C.c_int32, C.c_int]
+        _lib.orc_f16_bits.restype = C.c_uint16
+        _lib.orc_f16_bits.argtypes = [C.c_float]
+        _lib.orc_f16_bucket.restype = C.c_int
+        _lib.orc_f16_bucket.argtypes = [C.c_uint16]
+        _lib.orc_prefill_chunk.restype = C.c_int
+        _lib.orc_prefill_chunk.argtypes = [C.POINTER(Cfg), C.POINTER(State), C.c_int, C.c_int32,
+                                           C.c_int64] + [C.c_void_p] * 6 + \
+            [C.POINTER(PrefillOut)]
         _lib.orc_gather.argtypes = [C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p,
                                     C.c_void_p, C.c_void_p, C.c_void_p]
         _lib.orc_layer_step.restype = C.c_int
@@ -84,6 +93,12 @@ class State(C.Structure):
     _fields_ = [("h2g", C.c_void_p), ("g2h", C.c_void_p), ("prio", C.c_void_p),
                 ("freef", C.c_void_p), ("theta", C.c_void_p), ("t", C.c_int32),
                 ("pool", C.c_void_p)]
+
+
+class PrefillOut(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("scores", "sel", "n_sel", "kth", "beta", "n_qcand",
+                                          "cand", "uni", "pf_h", "pf_g", "miss_h", "miss_g")] + \
+        [(n, C.c_int32) for n in ("n_cand", "n_uni", "n_pf", "n_miss")]
 
 
 class Out(C.Structure):
@@ -166,10 +181,10 @@ def gather(host_base, sel_tok, n_sel, host_kv) -> np.ndarray:
     return out
 
 
-def release(layer, host_base, ctx, mask, max_ctx: int) -> int:
+def release(layer, host_base, ctx, mask, max_ctx: int, commit: bool = True) -> int:
     """Request cancellation (orc_release) on an OracleLayer's state: the masked
-    requests' slots and map rows are given back, theta resets, ctx (int32, in place)
-    becomes 0.  Returns OK or the error code."""
+    requests' slots and map rows are given back, theta resets, and with ``commit`` ctx
+    (int32, in place) becomes 0.  Returns OK or the error code."""
     host_base = np.ascontiguousarray(host_base, np.int32)
     assert ctx.dtype == np.int32 and ctx.flags["C_CONTIGUOUS"]
     mask = np.ascontiguousarray(mask, np.int32)
@@ -177,18 +192,75 @@ def release(layer, host_base, ctx, mask, max_ctx: int) -> int:
     assert host_base.size == B and mask.size == B and layer.theta.size >= B
     return lib().orc_release(B, layer.cfg.n_host, int(max_ctx), _p(host_base), _p(ctx),
                              _p(mask), _p(layer.h2g), _p(layer.g2h), _p(layer.prio),
-                             _p(layer.free), _p(layer.theta))
+                             _p(layer.free), _p(layer.theta), int(bool(commit)))
 
 
-def admit(layer, host_base, ctx, b: int, base: int, length: int, max_ctx: int) -> int:
-    """Request admission (orc_admit) into batch row b: host_base and ctx (int32, in
-    place) take (base, length) and theta[b] resets if the checks pass.  Returns OK or
-    the error code."""
+def admit(layer, host_base, ctx, b: int, base: int, length: int, max_ctx: int,
+          commit: bool = True) -> int:
+    """Request admission (orc_admit) into batch row b: if the checks pass theta[b]
+    resets and, with ``commit``, host_base and ctx (int32, in place) take (base,
+    length).  Returns OK or the error code."""
     assert host_base.dtype == np.int32 and host_base.flags["C_CONTIGUOUS"]
     assert ctx.dtype == np.int32 and ctx.flags["C_CONTIGUOUS"]
     B = int(ctx.size)
     return lib().orc_admit(B, layer.cfg.n_host, int(max_ctx), _p(host_base), _p(ctx),
-                           _p(layer.h2g), _p(layer.theta), int(b), int(base), int(length))
+                           _p(layer.h2g), _p(layer.theta), int(b), int(base), int(length),
+                           int(bool(commit)))
+
+
+def f16_bits(x: float) -> int:
+    return lib().orc_f16_bits(float(x))
+
+
+def f16_bucket(u: int) -> int:
+    return lib().orc_f16_bucket(int(u))
+
+
+def prefill_chunk(layer, hb: int, N: int, q, w, kidx, pred=None, host_kv=None,
+                  ext_scores=None) -> dict:
+    """One chunked-prefill step (orc_prefill_chunk) on an OracleLayer's state.  q: uint16
+    [C, H, D]; w: float32 [C, H]; kidx: uint8 [n_host, D]; pred: float32 [C] or None;
+    ext_scores: float32 [C, N] or None.  Returns the outputs (lists trimmed)."""
+    cfg = layer.cfg
+    q = np.ascontiguousarray(q, np.uint16)
+    w = np.ascontiguousarray(w, np.float32)
+    kidx = np.ascontiguousarray(kidx, np.uint8)
+    Cq = q.shape[0]
+    assert q.shape == (Cq, cfg.H, cfg.D) and w.shape == (Cq, cfg.H)
+    assert kidx.shape == (cfg.n_host, cfg.D) and 0 <= hb and hb + N <= cfg.n_host
+    k = cfg.k
+    o = dict(scores=np.zeros((Cq, max(N, 1)), np.float32), sel=np.full((Cq, k), -1, np.int32),
+             n_sel=np.zeros(Cq, np.int32), kth=np.zeros(Cq, np.float32),
+             beta=np.zeros(Cq, np.int32), n_qcand=np.zeros(Cq, np.int32))
+    for n in ("cand", "uni", "pf_h", "pf_g", "miss_h", "miss_g"):
+        o[n] = np.full(max(N, 1), -1, np.int32)
+    out = PrefillOut(*[_p(o[n]) for n in ("scores", "sel", "n_sel", "kth", "beta", "n_qcand",
+                                           "cand", "uni", "pf_h", "pf_g", "miss_h", "miss_g")],
+                     0, 0, 0, 0)
+    if pred is not None:
+        pred = np.ascontiguousarray(pred, np.float32)
+        assert pred.shape == (Cq,)
+    if ext_scores is not None:
+        ext_scores = np.ascontiguousarray(ext_scores, np.float32)
+        assert ext_scores.shape == (Cq, N)
+    if host_kv is not None:
+        host_kv = np.ascontiguousarray(host_kv, np.uint16)
+    theta = np.ascontiguousarray(layer.theta)
+    st = State(_p(layer.h2g), _p(layer.g2h), _p(layer.prio), _p(layer.free), _p(theta), layer.t,
+               _p(layer.pool) if layer.pool is not None else None)
+    rc = lib().orc_prefill_chunk(C.byref(cfg), C.byref(st), Cq, int(hb), int(N), _p(q), _p(w),
+                                 _p(kidx), _p(pred) if pred is not None else None,
+                                 _p(host_kv) if host_kv is not None else None,
+                                 _p(ext_scores) if ext_scores is not None else None,
+                                 C.byref(out))
+    layer.t = st.t
+    o["scores"] = o["scores"][:, :N]
+    o["cand"] = o["cand"][: out.n_cand]
+    o["uni"] = o["uni"][: out.n_uni]
+    o["pf_h"], o["pf_g"] = o["pf_h"][: out.n_pf], o["pf_g"][: out.n_pf]
+    o["miss_h"], o["miss_g"] = o["miss_h"][: out.n_miss], o["miss_g"][: out.n_miss]
+    o["status"] = rc
+    return o
 
 
 def ema_update(theta: float, s_k: float, alpha: float = 0.5) -> float:

@@ -60,6 +60,21 @@ MUTANTS = {
     "admit_ignores_overlap": ("if ((int64_t)base < hi && lo < (int64_t)base + len) return ORC_ECAPACITY;",
                               "(void)lo;\n    (void)hi;"),
     "admit_keeps_threshold": ("  theta[b] = INFINITY;\n  if (commit) {", "  if (commit) {"),
+    "f16_ties_away_from_zero": ("double m = nearbyint(a / quantum);", "double m = round(a / quantum);"),
+    "f16_subnormal_step": ("e < -14 ? ldexp(1.0, -24)", "e < -14 ? ldexp(1.0, -23)"),
+    "bucket_low_byte": ("  return key >> 8;\n", "  return key & 0xFF;\n"),
+    "coarse_shift_added": ("const float d = score - pred;", "const float d = score + pred;"),
+    "coarse_shift_dropped": ("const float d = score - pred;", "const float d = score;"),
+    "coarse_keeps_boundary_bucket": ("if (coarse_bucket(row[s], p) > beta) {",
+                                     "if (coarse_bucket(row[s], p) >= beta) {"),
+    "prefill_exact_before_early": ("for (int32_t j = 0; j < o->n_cand; ++j) { /* the early transfer */",
+                                   "for (int32_t j = 0; j < 0; ++j) { /* the early transfer */"),
+    "prefill_no_protect": ("    if (st->h2g[h] >= 0) {\n      st->prio[st->h2g[h]] = t;\n    } else {\n"
+                           "      const int32_t g = F[next++];\n      install(c, st, h, g, host_kv);\n"
+                           "      o->miss_h",
+                           "    if (st->h2g[h] >= 0) {\n      ;\n    } else {\n"
+                           "      const int32_t g = F[next++];\n      install(c, st, h, g, host_kv);\n"
+                           "      o->miss_h"),
     "append_ignores_neighbours": ("if (h >= host_base[o] && h < (int64_t)host_base[o] + ctx[o] + 1) "
                                   "return ORC_ECAPACITY;",
                                   "if (0) return ORC_ECAPACITY;"),

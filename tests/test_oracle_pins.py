@@ -619,3 +619,214 @@ def test_lifecycle_without_commit_leaves_the_batch_row_to_the_last_layer():
     assert list(hb) == [0, 20] and list(c) == [20, 0] and lay.theta[1] == np.inf
     assert O.admit(lay2, hb, c, 1, 24, 26, max_ctx=64) == O.OK
     assert list(hb) == [0, 24] and list(c) == [20, 26]
+
+
+# ------------------------------------------------------------ chunked prefill
+def test_f16_rounding_matches_numpy_including_ties_and_subnormals():
+    rng = np.random.default_rng(11)
+    bits = rng.integers(0, 2**32, size=60000, dtype=np.uint64).astype(np.uint32)
+    vals = bits.view(np.float32)
+    vals = vals[np.isfinite(vals)]
+    # exact ties between neighbouring halves, normal and subnormal, both signs
+    h = rng.integers(1, 0x7BFF, size=4000).astype(np.uint16)
+    lo = h.view(np.float16).astype(np.float64)
+    hi = (h + 1).view(np.float16).astype(np.float64)
+    ties = ((lo + hi) / 2).astype(np.float32)
+    extra = np.array([0.0, -0.0, 65504, 65519.99, 65520, 65536, 1e30, -1e30, 2**-24, 2**-25,
+                      3 * 2**-26, 2**-14, 2**-15 * 1.5, 0.1, -7.5], np.float32)
+    for v in np.concatenate([vals, ties, -ties, extra]):
+        want = int(np.float32(v).astype(np.float16).view(np.uint16))
+        assert O.f16_bits(float(v)) == want, (float(v), hex(want))
+
+
+def test_f16_buckets_by_hand_and_monotone():
+    # fp16 of 0..7: 0x0000 0x3C00 0x4000 0x4200 0x4400 0x4500 0x4600 0x4700; a non-negative
+    # half u has key u | 0x8000, a negative one the complement
+    by_hand = {0.0: 0x80, 1.0: 0xBC, 2.0: 0xC0, 3.0: 0xC2, 4.0: 0xC4, 5.0: 0xC5, 6.0: 0xC6,
+               7.0: 0xC7, -1.0: 0x43, -0.0: 0x80, 255 * 2**-24: 0x80, 2**-16: 0x81,
+               2**-14: 0x84}
+    for x, b in by_hand.items():
+        assert O.f16_bucket(O.f16_bits(x)) == b, x
+    xs = np.sort(np.random.default_rng(2).standard_normal(3000).astype(np.float32) * 50)
+    bk = [O.f16_bucket(O.f16_bits(float(x))) for x in xs]
+    assert all(a <= b for a, b in zip(bk, bk[1:]))
+
+
+def _prefill_layer(n_host, n_gpu, k, latent=2, H=1, D=1):
+    lay = O.OracleLayer(H=H, D=D, k=k, latent=latent, n_host=n_host, n_gpu=n_gpu, max_batch=1)
+    hk = (np.arange(n_host * latent, dtype=np.uint16) + 1).reshape(n_host, latent)
+    return lay, hk
+
+
+def _prefill_ext(lay, hk, scores, pred=None, hb=0):
+    Cq, N = scores.shape
+    q = np.zeros((Cq, lay.cfg.H, lay.cfg.D), np.uint16)
+    w = np.zeros((Cq, lay.cfg.H), np.float32)
+    kidx = np.zeros((lay.cfg.n_host, lay.cfg.D), np.uint8)
+    return O.prefill_chunk(lay, hb, N, q, w, kidx, pred=pred, host_kv=hk,
+                           ext_scores=np.asarray(scores, np.float32))
+
+
+def test_prefill_coarse_candidates_by_hand():
+    lay, hk = _prefill_layer(64, 32, k=2)
+    perm = [3, 7, 0, 5, 1, 6, 2, 4]
+    o = _prefill_ext(lay, hk, np.array([perm], np.float32))
+    # buckets of 7 and 6 are 0xC7 and 0xC6: two tokens reach k = 2 at 0xC6
+    assert o["beta"][0] == 0xC6 and list(o["cand"]) == [1] and list(o["uni"]) == [1, 5]
+    lay, hk = _prefill_layer(64, 32, k=3)
+    o = _prefill_ext(lay, hk, np.array([perm], np.float32))
+    assert o["beta"][0] == 0xC5 and list(o["cand"]) == [1, 5]
+    # 12 .. 13.5 share bucket 0xCA: with no prediction nothing is strictly above
+    sc = np.array([[10, 10.5, 11, 11.5, 12, 12.5, 13, 13.5]], np.float32)
+    lay, hk = _prefill_layer(64, 32, k=3)
+    o = _prefill_ext(lay, hk, sc)
+    assert o["beta"][0] == 0xCA and o["n_qcand"][0] == 0 and list(o["uni"]) == [5, 6, 7]
+    assert list(o["miss_h"]) == [5, 6, 7] and o["pf_h"].size == 0
+    # predicted k-th 12.5: differences 1, 0.5, 0 sit in buckets 0xBC, 0xB8, 0x80
+    lay, hk = _prefill_layer(64, 32, k=3)
+    o = _prefill_ext(lay, hk, sc, pred=np.array([12.5], np.float32))
+    assert o["beta"][0] == 0x80 and list(o["cand"]) == [6, 7]
+    assert list(o["pf_h"]) == [6, 7] and list(o["pf_g"]) == [0, 1]
+    assert list(o["miss_h"]) == [5] and list(o["miss_g"]) == [2]
+
+
+def _prefill_workload(seed=0, C=6, N=700, H=4, D=32, k=64, chunks=3, rho=0.9, n_gpu=1000):
+    rng = np.random.default_rng(seed)
+    n_host = N + 40
+    hb = 16
+    kid = torch.from_numpy(rng.standard_normal((n_host, D)).astype(np.float32))
+    kidx = kid.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    hk = rng.integers(0, 65536, size=(n_host, 8)).astype(np.uint16)
+    st = rng.standard_normal((H, D)).astype(np.float32)
+    qs, ws = [], []
+    for _ in range(chunks):
+        rows = []
+        for _ in range(C):  # AR(1) along the prompt positions
+            rows.append(torch.from_numpy(st).to(torch.bfloat16).view(torch.int16).numpy()
+                        .view(np.uint16))
+            st = rho * st + np.sqrt(1 - rho * rho) * rng.standard_normal(st.shape) \
+                .astype(np.float32)
+        qs.append(np.stack(rows))
+        ws.append(rng.random((C, H)).astype(np.float32))
+    return dict(N=N, H=H, D=D, k=k, n_host=n_host, hb=hb, kidx=kidx, hk=hk, qs=qs, ws=ws,
+                n_gpu=n_gpu)
+
+
+def _prefill_run(wk, use_pred=True, n_gpu=None):
+    lay = O.OracleLayer(wk["H"], wk["D"], wk["k"], 8, wk["n_host"], n_gpu or wk["n_gpu"], 1)
+    outs, pred = [], None
+    for q, w in zip(wk["qs"], wk["ws"]):
+        before = dict(h2g=lay.h2g.copy(), free=lay.free.copy(), t=lay.t)
+        o = O.prefill_chunk(lay, wk["hb"], wk["N"], q, w, wk["kidx"], pred=pred,
+                            host_kv=wk["hk"])
+        outs.append((o, before, dict(h2g=lay.h2g.copy(), prio=lay.prio.copy(), t=lay.t)))
+        if o["status"] != O.OK:
+            break
+        pred = o["kth"].copy() if use_pred else None
+    return lay, outs
+
+
+def test_prefill_candidates_are_exact_top_k_members():
+    # every token above a query's boundary bucket is one of its exact top-k (the
+    # bucket of a rounded difference never decreases as the score grows)
+    wk = _prefill_workload()
+    for use_pred in (False, True):
+        lay, outs = _prefill_run(wk, use_pred)
+        pred = None
+        for o, _, _ in outs:
+            assert o["status"] == O.OK
+            union = set()
+            for i in range(o["kth"].size):
+                sel = set(o["sel"][i, : o["n_sel"][i]].tolist())
+                assert len(sel) == wk["k"]
+                row = o["scores"][i]
+                p = np.float32(0.0 if pred is None else pred[i])
+                above = {s for s in range(wk["N"])
+                         if O.f16_bucket(O.f16_bits(float(row[s] - p))) > o["beta"][i]}
+                assert above <= sel and len(above) == o["n_qcand"][i] < wk["k"]
+                union |= above
+            assert sorted(union) == o["cand"].tolist()
+            assert set(o["cand"].tolist()) <= set(o["uni"].tolist())
+            pred = o["kth"].copy() if use_pred else None
+
+
+def test_prefill_prediction_equal_to_the_kth_puts_the_boundary_at_zero():
+    wk = _prefill_workload(seed=4)
+    lay, outs = _prefill_run(wk, use_pred=False)
+    o0 = outs[0][0]
+    # the same chunk again on a fresh layer, predicted k-th = the exact k-th
+    lay2 = O.OracleLayer(wk["H"], wk["D"], wk["k"], 8, wk["n_host"], wk["n_gpu"], 1)
+    o1 = O.prefill_chunk(lay2, wk["hb"], wk["N"], wk["qs"][0], wk["ws"][0], wk["kidx"],
+                         pred=o0["kth"], host_kv=wk["hk"])
+    for i in range(o0["kth"].size):
+        assert o1["beta"][i] == 0x80                       # difference 0 is bucket 0x80
+        row = o0["scores"][i]
+        sel = o0["sel"][i, : o0["n_sel"][i]]
+        near = int(((row[sel] - o0["kth"][i]) < 2.0**-16).sum())
+        assert o1["n_qcand"][i] == wk["k"] - near          # all but the ties near the k-th
+        assert o1["n_qcand"][i] >= o0["n_qcand"][i]
+    assert np.array_equal(o1["uni"], o0["uni"]) and o1["pf_h"].size >= o0["pf_h"].size
+
+
+def test_prefill_state_after_each_chunk():
+    wk = _prefill_workload(seed=7, chunks=4)
+    lay, outs = _prefill_run(wk)
+    hb = wk["hb"]
+    for o, before, after in outs:
+        assert o["status"] == O.OK
+        t = before["t"]
+        assert after["t"] == t + 1
+        hu = hb + o["uni"]
+        assert (after["h2g"][hu] >= 0).all()                       # the union is resident
+        assert (after["prio"][after["h2g"][hu]] == t).all()         # and protected
+        was = before["h2g"][hu] >= 0
+        # the early transfer: exactly the candidates that were not resident, in order
+        hc = hb + o["cand"]
+        assert np.array_equal(o["pf_h"], hc[before["h2g"][hc] < 0])
+        # then the rest of the union, in order
+        rest = np.setdiff1d(hu[~was], o["pf_h"])
+        assert np.array_equal(o["miss_h"], rest)
+        # both take the lowest free slots, in that order
+        free0 = np.nonzero(before["free"])[0]
+        n = o["pf_h"].size + o["miss_h"].size
+        assert np.array_equal(np.concatenate([o["pf_g"], o["miss_g"]]), free0[:n])
+        assert np.array_equal(after["h2g"][o["pf_h"]], o["pf_g"])
+    # maps are inverses and the pool holds the host rows of every resident token
+    res = np.nonzero(lay.h2g >= 0)[0]
+    assert np.array_equal(lay.g2h[lay.h2g[res]], res)
+    assert np.array_equal(lay.free == 1, lay.g2h == -1)
+    assert np.array_equal(lay.free == 1, lay.prio == -1)
+    assert np.array_equal(lay.pool[lay.h2g[res]], wk["hk"][res])
+    # later chunks reuse what earlier ones brought in
+    assert outs[-1][0]["miss_h"].size + outs[-1][0]["pf_h"].size < outs[0][0]["uni"].size
+
+
+def test_prefill_selection_does_not_depend_on_the_prediction():
+    wk = _prefill_workload(seed=9, chunks=3)
+    lay_a, a = _prefill_run(wk, use_pred=False)
+    lay_b, b = _prefill_run(wk, use_pred=True)
+    for (oa, _, _), (ob, _, _) in zip(a, b):
+        assert np.array_equal(oa["uni"], ob["uni"]) and np.array_equal(oa["sel"], ob["sel"])
+        assert np.array_equal(oa["kth"].view(np.uint32), ob["kth"].view(np.uint32))
+    res = np.nonzero(lay_a.h2g >= 0)[0]
+    assert np.array_equal(res, np.nonzero(lay_b.h2g >= 0)[0])
+    assert np.array_equal(lay_a.pool[lay_a.h2g[res]], lay_b.pool[lay_b.h2g[res]])
+
+
+def test_prefill_capacity_error_changes_nothing_and_short_history_takes_everything():
+    wk = _prefill_workload(seed=3, chunks=1)
+    lay = O.OracleLayer(wk["H"], wk["D"], wk["k"], 8, wk["n_host"], 100, 1)
+    snap = lay.snapshot()
+    o = O.prefill_chunk(lay, wk["hb"], wk["N"], wk["qs"][0], wk["ws"][0], wk["kidx"],
+                        host_kv=wk["hk"])
+    assert o["status"] == O.ECAPACITY and o["uni"].size > 100
+    for key, v in snap.items():
+        cur = getattr(lay, key)
+        assert (cur == v) if key == "t" else np.array_equal(cur, v)
+    # a history no longer than k: every token is selected and moves early
+    lay = O.OracleLayer(wk["H"], wk["D"], 64, 8, wk["n_host"], 200, 1)
+    o = O.prefill_chunk(lay, wk["hb"], 50, wk["qs"][0], wk["ws"][0], wk["kidx"],
+                        host_kv=wk["hk"])
+    assert o["status"] == O.OK and (o["beta"] == -1).all()
+    assert list(o["uni"]) == list(range(50)) == list(o["cand"])
+    assert np.array_equal(o["pf_h"], wk["hb"] + np.arange(50)) and o["miss_h"].size == 0
