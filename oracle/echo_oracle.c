@@ -73,8 +73,11 @@
  *      overlaps the next chunk's scoring), then the rest of the union of the
  *      selections, each at the next ascending free slot, with priority t.
  *      The pool is sized to hold the chunk's union: a prefill chunk evicts
- *      nothing and reports a capacity error, changing nothing, if the free
- *      slots do not suffice.
+ *      nothing.  Capacity is checked per stage, as each stage's set becomes
+ *      known: if the candidates that are not resident exceed the free slots,
+ *      nothing changes; if the rest of the union then exceeds what is left,
+ *      the candidates stay installed and nothing else changes (the step
+ *      counter does not advance).  Both report a capacity error.
  */
 #include <math.h>
 #include <stdint.h>
@@ -587,7 +590,8 @@ typedef struct {
  * indexer's work by query chunk).  Reading R13.
  * q: bf16 [C][H][D]; w: fp32 [C][H]; kidx: e4m3 [n_host][D]; the history is
  * host ids hb .. hb+N-1; pred: [C] or NULL; ext_scores: [C][N] or NULL.
- * Returns ORC_OK or ORC_ECAPACITY (outputs up to the unions still set). */
+ * Returns ORC_OK or ORC_ECAPACITY (outputs up to the unions still set; after
+ * a capacity error in the second stage the first stage's installs stand). */
 int orc_prefill_chunk(const orc_cfg *c, orc_state *st, int C, int32_t hb, int64_t N,
                       const uint16_t *q, const float *w, const uint8_t *kidx, const float *pred,
                       const uint16_t *host_kv, const float *ext_scores, orc_prefill_out *o) {
@@ -639,20 +643,19 @@ int orc_prefill_chunk(const orc_cfg *c, orc_state *st, int C, int32_t hb, int64_
   free(cflag);
   free(uflag);
   o->n_pf = o->n_miss = 0;
-  /* capacity first: nothing changes if the union does not fit */
   int32_t *F = (int32_t *)malloc(sizeof(int32_t) * (size_t)(c->n_gpu > 0 ? c->n_gpu : 1));
   int32_t nF = 0;
   for (int32_t g = 0; g < c->n_gpu; ++g)
     if (st->freef[g]) F[nF++] = g;
-  int64_t need = 0;
-  for (int32_t j = 0; j < o->n_uni; ++j)
-    if (st->h2g[(int64_t)hb + o->uni[j]] == -1) ++need;
+  const int32_t t = st->t;
+  int32_t next = 0;
+  int64_t need = 0; /* each stage checks its own set against the free slots left */
+  for (int32_t j = 0; j < o->n_cand; ++j)
+    if (st->h2g[(int64_t)hb + o->cand[j]] == -1) ++need;
   if (need > nF) {
     free(F);
     return ORC_ECAPACITY;
   }
-  const int32_t t = st->t;
-  int32_t next = 0;
   for (int32_t j = 0; j < o->n_cand; ++j) { /* the early transfer */
     const int64_t h = (int64_t)hb + o->cand[j];
     if (st->h2g[h] >= 0) {
@@ -663,6 +666,13 @@ int orc_prefill_chunk(const orc_cfg *c, orc_state *st, int C, int32_t hb, int64_
       o->pf_h[o->n_pf] = (int32_t)h;
       o->pf_g[o->n_pf++] = g;
     }
+  }
+  need = 0;
+  for (int32_t j = 0; j < o->n_uni; ++j)
+    if (st->h2g[(int64_t)hb + o->uni[j]] == -1) ++need;
+  if (need > nF - next) {
+    free(F);
+    return ORC_ECAPACITY;
   }
   for (int32_t j = 0; j < o->n_uni; ++j) { /* the exact fetch */
     const int64_t h = (int64_t)hb + o->uni[j];

@@ -813,16 +813,35 @@ def test_prefill_selection_does_not_depend_on_the_prediction():
     assert np.array_equal(lay_a.pool[lay_a.h2g[res]], lay_b.pool[lay_b.h2g[res]])
 
 
-def test_prefill_capacity_error_changes_nothing_and_short_history_takes_everything():
+def _same(lay, snap):
+    for key, v in snap.items():
+        cur = getattr(lay, key)
+        assert (cur == v) if key == "t" else np.array_equal(cur, v), key
+
+
+def test_prefill_capacity_errors_per_stage_and_short_history_takes_everything():
     wk = _prefill_workload(seed=3, chunks=1)
-    lay = O.OracleLayer(wk["H"], wk["D"], wk["k"], 8, wk["n_host"], 100, 1)
+    probe = O.OracleLayer(wk["H"], wk["D"], wk["k"], 8, wk["n_host"], wk["n_gpu"], 1)
+    full = O.prefill_chunk(probe, wk["hb"], wk["N"], wk["qs"][0], wk["ws"][0], wk["kidx"],
+                           pred=None, host_kv=wk["hk"])
+    n_c, n_u = full["cand"].size, full["uni"].size
+    assert 0 < n_c < n_u
+    # too few slots for the candidates: nothing changes
+    lay = O.OracleLayer(wk["H"], wk["D"], wk["k"], 8, wk["n_host"], n_c - 1, 1)
     snap = lay.snapshot()
     o = O.prefill_chunk(lay, wk["hb"], wk["N"], wk["qs"][0], wk["ws"][0], wk["kidx"],
                         host_kv=wk["hk"])
-    assert o["status"] == O.ECAPACITY and o["uni"].size > 100
-    for key, v in snap.items():
-        cur = getattr(lay, key)
-        assert (cur == v) if key == "t" else np.array_equal(cur, v)
+    assert o["status"] == O.ECAPACITY and o["pf_h"].size == 0
+    _same(lay, snap)
+    # room for the candidates only: they stay installed, nothing else changes
+    lay = O.OracleLayer(wk["H"], wk["D"], wk["k"], 8, wk["n_host"], n_u - 1, 1)
+    o = O.prefill_chunk(lay, wk["hb"], wk["N"], wk["qs"][0], wk["ws"][0], wk["kidx"],
+                        host_kv=wk["hk"])
+    assert o["status"] == O.ECAPACITY and o["miss_h"].size == 0 and lay.t == 0
+    assert np.array_equal(o["pf_h"], wk["hb"] + full["cand"])
+    assert np.array_equal(o["pf_g"], np.arange(n_c))
+    assert np.array_equal(np.nonzero(lay.h2g >= 0)[0], o["pf_h"])
+    assert int(lay.free.sum()) == n_u - 1 - n_c
     # a history no longer than k: every token is selected and moves early
     lay = O.OracleLayer(wk["H"], wk["D"], 64, 8, wk["n_host"], 200, 1)
     o = O.prefill_chunk(lay, wk["hb"], 50, wk["qs"][0], wk["ws"][0], wk["kidx"],
