@@ -32,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0  # dense fp8 MFMA
 BYTES_PER_SCORED_TOKEN = 128 + 4
 
 
@@ -57,6 +58,9 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--cap-div", type=int, default=None,
                    help="override the prefetch cap divisor (cap = min(k, ceil(ctx/div)))")
+    p.add_argument("--no-prefill", action="store_true",
+                   help="skip the chunked-prefill measurement")
+    p.add_argument("--prefill-chunks", type=int, default=4)
     p.add_argument("--pmc-calibrate", action="store_true",
                    help="end with a 256 MiB device-to-device copy whose FETCH_SIZE / WRITE_SIZE "
                         "counters scale the indexer's")
@@ -437,6 +441,9 @@ def main():
         f"last layer): {release_ms * 1e3:.1f} us per layer; admission {admit_ms * 1e3:.1f} us "
         "per layer")
 
+    # ------------------------------------------------------- chunked prefill
+    prefill = None if args.no_prefill else prefill_measure(args, dev)
+
     # ------------------------------------------------------- CPU baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -503,6 +510,7 @@ def main():
                       "resident_last_layer": resident0,
                       "how": f"echo_release then echo_admit of request 0 on all {L} layers, "
                              "eager, events on the launch stream"},
+        "prefill": prefill,
         "hit_rate": round(hit, 5),
         "topk_shortcut_requests_last_layer": f"{shortcut_last}/{B}",
         "misses_per_layer_step": round(float(misses.mean()), 1),
@@ -512,6 +520,143 @@ def main():
     for hp in pools:
         hp.close()
     print(json.dumps(out), flush=True)
+
+
+def prefill_measure(args, dev):
+    """Chunked prefill on the prefill workload (one request, 100,000-token history,
+    64 x 128 indexer, top-2048 per query, 200,000 GPU slots, 2M host tokens), for each
+    query-chunk size: the chunk pipeline with the copies on a second stream (the early
+    candidates' copy overlaps the exact selection and the next chunk's scoring) against
+    the same calls run one after another on one stream, from a cold GPU pool; and the
+    scoring call's fp8 MFMA rate (algorithmic 2*C*N*H*D flop per chunk)."""
+    import torch
+
+    from kv_cache_offload_fp8_amd import abi
+    from kv_cache_offload_fp8_amd import runtime as R
+    from synth import gen as G
+    from synth import get
+    from synth.configs import PREFILL_CHUNKS
+
+    wl = get("prefill")
+    N, chunks = wl.ctx_lo, max(2, args.prefill_chunks)
+    dims = R.make_dims(wl.heads, wl.head_dim, wl.top_k, wl.n_host, wl.n_gpu, 1, N, wl.latent,
+                       wl.alpha, wl.cap_div, 1)
+    ctx = np.array([N], np.int32)
+    base = G.host_layout(ctx)
+    host = R.HostPool(wl.n_host, wl.latent)
+    lat = G.gen_latents(wl, 0, ctx, base, dev, args.seed,
+                        out=torch.empty((wl.n_host, wl.latent), dtype=torch.int16, device=dev))
+    host.tensor.copy_(lat)
+    del lat
+    rows = G.gen_kidx(wl, 0, ctx, base, dev, args.seed)
+    kidx = R.pack_kidx(dims, rows, torch.empty_like(rows))
+    del rows
+    layer = R.Layer(dims, kidx, host, 1, dev)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    out = {"workload": f"prefill: 1 request, history {N}, 64x128, k {wl.top_k}, "
+                       f"{wl.n_gpu} GPU slots, {wl.n_host} host tokens, {chunks} chunks",
+           "chunks": {}}
+    for C in PREFILL_CHUNKS:
+        q, w = G.gen_prefill_qw(wl, 0, C, chunks, dev, args.seed)
+        pws = R.PrefillWorkspace(dims, C, dev)
+        structs = [abi.echo_prefill_chunk_t(C, int(base[0]), N, q[c].data_ptr(), w[c].data_ptr(),
+                                            pws.kth.data_ptr() if c else None)
+                   for c in range(chunks)]
+
+        def call(fn, c, st):
+            R.check(fn(dims, layer.struct, structs[c], pws.ws, st.cuda_stream), fn.__name__)
+
+        def copy(which, st):
+            R.check(abi.echo_prefill_copy(dims, layer.struct, pws.ws, which, st.cuda_stream),
+                    "echo_prefill_copy")
+
+        def fresh():
+            torch.cuda.synchronize()
+            layer.init()
+            pws.reset()
+            torch.cuda.synchronize()
+
+        def run(overlap, stats=None):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ea = eb = None
+            e0.record(s1)
+            for c in range(chunks):
+                call(abi.echo_prefill_score, c, s1)
+                if overlap and ea is not None:
+                    s1.wait_event(ea)
+                call(abi.echo_prefill_early, c, s1)
+                if overlap:
+                    ev = torch.cuda.Event()
+                    ev.record(s1)
+                    s2.wait_event(ev)
+                    copy(0, s2)
+                    ea = torch.cuda.Event()
+                    ea.record(s2)
+                    if eb is not None:
+                        s1.wait_event(eb)
+                call(abi.echo_prefill_select, c, s1)
+                if overlap:
+                    ev = torch.cuda.Event()
+                    ev.record(s1)
+                    s2.wait_event(ev)
+                    copy(1, s2)
+                    eb = torch.cuda.Event()
+                    eb.record(s2)
+                else:
+                    copy(0, s1)
+                    copy(1, s1)
+                if stats is not None:
+                    torch.cuda.synchronize()
+                    cnt = pws.counts.cpu().numpy()
+                    stats.append([int(cnt[abi.ECHO_PF_CNT_UNION]), int(cnt[abi.ECHO_PF_CNT_CAND]),
+                                  int(cnt[abi.ECHO_PF_CNT_EARLY]), int(cnt[abi.ECHO_PF_CNT_LATE])])
+            if overlap:
+                s1.wait_event(eb)
+            e1.record(s1)
+            torch.cuda.synchronize()
+            st = int(pws.status.item())
+            if st != 0:
+                raise SystemExit(f"prefill status {abi.echo_status_string(st)}")
+            return e0.elapsed_time(e1)
+
+        stats = []
+        fresh()
+        run(True, stats)          # untimed: counts per chunk
+        fresh()
+        run(True)                 # warm the code paths
+        times = {}
+        for overlap in (True, False):
+            fresh()
+            times[overlap] = run(overlap)
+        # the scoring call alone (stage, MFMA scores, coarse pass, candidate list)
+        fresh()
+        es, ee = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 4
+        es.record(s1)
+        for _ in range(reps):
+            call(abi.echo_prefill_score, 1, s1)
+        ee.record(s1)
+        torch.cuda.synchronize()
+        score_ms = es.elapsed_time(ee) / reps
+        flop = 2.0 * C * N * wl.heads * wl.head_dim
+        tflops = flop / (score_ms * 1e-3) / 1e12
+        rows_moved = sum(x[2] + x[3] for x in stats)
+        out["chunks"][str(C)] = {
+            "ms_per_chunk_overlapped": round(times[True] / chunks, 4),
+            "ms_per_chunk_serial": round(times[False] / chunks, 4),
+            "overlap_speedup": round(times[False] / times[True], 4),
+            "score_call_ms": round(score_ms, 4),
+            "score_call_tflops_algorithmic": round(tflops, 1),
+            "score_call_frac_of_fp8_peak": round(tflops / FP8_PEAK_TFLOPS, 4),
+            "rows_over_host_link": rows_moved,
+            "per_chunk_union_cand_early_late": stats}
+        log(f"[bench] prefill C={C}: {times[True] / chunks:.3f} ms/chunk with the copies "
+            f"overlapped, {times[False] / chunks:.3f} serial ({times[False] / times[True]:.3f}x); "
+            f"scoring call {score_ms:.3f} ms = {tflops:.0f} TFLOP/s algorithmic "
+            f"({tflops / FP8_PEAK_TFLOPS:.1%} of fp8 peak); union/cand/early/late {stats}")
+        del pws, q, w
+    host.close()
+    return out
 
 
 def cpu_baseline(wl, ctx, base, lay0, rows0, args, dims):

@@ -84,6 +84,15 @@ enum {
   ECHO_CTL_WORDS = 4
 };
 
+/* Counts written by the chunked-prefill calls (echo_prefill_ws_t.counts). */
+enum {
+  ECHO_PF_CNT_CAND = 0,  /* tokens in the union of the coarse candidates             */
+  ECHO_PF_CNT_UNION = 1, /* tokens in the union of the exact selections              */
+  ECHO_PF_CNT_EARLY = 2, /* candidates installed early (pf_h / pf_g)                 */
+  ECHO_PF_CNT_LATE = 3,  /* the rest of the union installed after the exact select   */
+  ECHO_PF_NCOUNTS = 8
+};
+
 /* Shapes.  Supported by this build: 1 <= n_heads <= 64; head_dim in {32, 64, 96,
  * 128}; 1 <= top_k <= 4096; latent_dim*2 a multiple of 16 bytes; n_host < 2^31
  * and a multiple of 16;
@@ -330,6 +339,104 @@ int echo_admit(const echo_dims_t *dims, const echo_layer_t *layer, int32_t *host
 int echo_layer_step(const echo_dims_t *dims, const echo_layer_t *layer,
                     const echo_batch_t *batch, const echo_ws_t *ws, int theta_mode,
                     hipStream_t stream);
+
+/* ------------------------------------------------------- chunked prefill */
+
+/* One prefill chunk: C queries scored against one request's history of N tokens
+ * (host ids host_base .. host_base + N - 1, indexer K resident in the layer's
+ * tiled K).  The chunk's own tokens are not part of the history. */
+typedef struct {
+  int32_t queries;   /* C, host value, 1 <= C <= max_chunk                          */
+  int32_t host_base; /* host value, a multiple of 16, host_base + N <= n_host      */
+  int32_t hist_len;  /* N, host value, 1 <= N <= max_ctx                            */
+  const uint16_t *q; /* [C][n_heads][head_dim] bf16, device, 16-byte aligned        */
+  const float *w;    /* [C][n_heads] fp32 head weights, device                      */
+  const float *pred; /* [C] device: predicted k-th score per query, or NULL (0)     */
+} echo_prefill_chunk_t;
+
+/* Prefill workspace: one caller-allocated device buffer carved by
+ * echo_prefill_ws_bind.  The named arrays are outputs the caller may read. */
+typedef struct {
+  int32_t max_chunk;
+  float *scores;     /* [max_chunk][N] indexer scores of the last chunk (row stride N) */
+  int32_t *sel;      /* [max_chunk][top_k] each query's top-k, ascending               */
+  int32_t *n_sel;    /* [max_chunk] min(top_k, N)                                      */
+  float *kth;        /* [max_chunk] each query's k-th highest score                    */
+  int32_t *beta;     /* [max_chunk] boundary bucket, -1 if N <= top_k                  */
+  int32_t *n_qcand;  /* [max_chunk] coarse candidates of each query                    */
+  int32_t *cand;     /* [max_ctx] union of the candidates, ascending tokens            */
+  int32_t *uni;      /* [max_ctx] union of the selections, ascending tokens            */
+  int32_t *pf_h;     /* [max_ctx] early installs: host ids, in candidate order         */
+  int32_t *pf_g;     /* [max_ctx] their slots                                          */
+  int32_t *miss_h;   /* [max_ctx] later installs: host ids, in union order             */
+  int32_t *miss_g;   /* [max_ctx] their slots                                          */
+  int32_t *counts;   /* [ECHO_PF_NCOUNTS]                                              */
+  int32_t *status;   /* [1] sticky device status of the prefill calls                  */
+  uint8_t *internal; /* scratch between the calls (must start zeroed: bind + reset)    */
+  size_t internal_bytes;
+} echo_prefill_ws_t;
+
+/* Bytes of a prefill workspace for chunks of up to max_chunk queries (0 if the
+ * dims or max_chunk are invalid: 1 <= max_chunk <= 4096, max_ctx <= 2^22). */
+size_t echo_prefill_ws_bytes(const echo_dims_t *dims, int32_t max_chunk);
+
+/* Carve `base` (device, >= echo_prefill_ws_bytes, 256-byte aligned) into *pws.
+ * Host-only.  The buffer must then be cleared with echo_prefill_ws_reset. */
+int echo_prefill_ws_bind(const echo_dims_t *dims, int32_t max_chunk, void *base, size_t bytes,
+                         echo_prefill_ws_t *pws);
+
+/* Clear status, counts and internal flags (fill kernels, no memset nodes). */
+int echo_prefill_ws_reset(const echo_dims_t *dims, const echo_prefill_ws_t *pws,
+                          hipStream_t stream);
+
+/* Chunked prefill, part 1: scores and coarse candidates.  The ECHO
+ * review ("Core method / prefill"): chunk i's identified candidates move while
+ * chunk i+1 is scored; a 256-bucket coarse histogram keeps the strictly-high
+ * buckets and leaves the threshold bucket to the exact selection; subtracting a
+ * predicted k-th score refines the buckets near the boundary.  "Core method /
+ * prefetch inside the indexer pipeline": prefill splits the indexer's work by
+ * query chunk.  Per query i the call writes scores[i][0..N) (the decode
+ * formula), beta[i] = the bucket of fp16(score - pred[i]) at which the count from
+ * the top first reaches top_k (-1 if N <= top_k) and n_qcand[i]; cand = the
+ * ascending union of the tokens above their query's boundary (every token if
+ * N <= top_k).  The prefill calls are no-ops while pws->status holds an error.
+ * Errors: ECHO_EINVAL (host checks), ECHO_EUNSUPPORTED. */
+int echo_prefill_score(const echo_dims_t *dims, const echo_layer_t *layer,
+                       const echo_prefill_chunk_t *chunk, const echo_prefill_ws_t *pws,
+                       hipStream_t stream);
+
+/* Chunked prefill, part 2: the early install (same passages).  In cand order, a
+ * resident token gets priority t (the layer's step counter) and the others take
+ * the lowest free slots (meta.idxbuf, ascending), listed in pf_h / pf_g.  Copy
+ * them with echo_prefill_copy(list 0), on another stream if wanted, while the
+ * exact selection and the next chunk's scoring run; the next chunk's
+ * echo_prefill_early rewrites the list, so order it after that copy.  Device:
+ * ECHO_ECAPACITY if the candidates without a slot exceed the free slots
+ * (nothing installed). */
+int echo_prefill_early(const echo_dims_t *dims, const echo_layer_t *layer,
+                       const echo_prefill_chunk_t *chunk, const echo_prefill_ws_t *pws,
+                       hipStream_t stream);
+
+/* Chunked prefill, part 3: the exact fetch.  Per query, the top_k tokens by
+ * (score desc, token asc), written ascending into sel[i], with n_sel[i] and
+ * kth[i] (pass kth as the next chunk's pred); uni = their ascending union.  In
+ * uni order a resident token gets priority t and the others take the next free
+ * slots after the early installs (miss_h / miss_g; copy them with
+ * echo_prefill_copy(list 1)).  Then t advances and the ascending free list is
+ * rebuilt.  The chunk must be the one given to echo_prefill_score and
+ * echo_prefill_early, and the next chunk's echo_prefill_select rewrites list 1,
+ * so order it after that list's copy.  Device:
+ * ECHO_ECAPACITY if the rest of the union exceeds the free slots left (the early
+ * installs stand; t does not advance).  A prefill chunk evicts nothing. */
+int echo_prefill_select(const echo_dims_t *dims, const echo_layer_t *layer,
+                        const echo_prefill_chunk_t *chunk, const echo_prefill_ws_t *pws,
+                        hipStream_t stream);
+
+/* Copy the host rows of install list 0 (early) or 1 (later) into the GPU pool,
+ * reading mapped host memory directly.  Order it after the call that wrote the
+ * list (echo_prefill_early for list 0, echo_prefill_select for list 1). */
+int echo_prefill_copy(const echo_dims_t *dims, const echo_layer_t *layer,
+                      const echo_prefill_ws_t *pws, int list, hipStream_t stream);
 
 /* ------------------------------------------------------------- diagnostics */
 

@@ -23,7 +23,10 @@ ECHO_CTL_STEP, ECHO_CTL_NFREE, ECHO_CTL_WORDS = 0, 1, 4
 EXPORTS = ("echo_meta_bytes", "echo_ws_bytes", "echo_ws_bind", "echo_meta_init",
            "echo_ws_reset", "echo_kindex_pack", "echo_indexer_prefetch", "echo_topk",
            "echo_cache_alloc_evict", "echo_recall", "echo_step_advance", "echo_layer_step",
-           "echo_append", "echo_gather", "echo_release", "echo_admit", "echo_status_string")
+           "echo_append", "echo_gather", "echo_release", "echo_admit", "echo_prefill_ws_bytes",
+           "echo_prefill_ws_bind", "echo_prefill_ws_reset", "echo_prefill_score",
+           "echo_prefill_early",
+           "echo_prefill_select", "echo_prefill_copy", "echo_status_string")
 
 P = C.c_void_p
 
@@ -54,6 +57,21 @@ class echo_ws_t(C.Structure):
                 ("n_miss", P), ("recall_h", P), ("recall_g", P), ("counters", P),
                 ("status", P), ("internal", P), ("internal_bytes", C.c_size_t)]
 
+
+class echo_prefill_chunk_t(C.Structure):
+    _fields_ = [("queries", C.c_int32), ("host_base", C.c_int32), ("hist_len", C.c_int32),
+                ("q", P), ("w", P), ("pred", P)]
+
+
+class echo_prefill_ws_t(C.Structure):
+    _fields_ = [("max_chunk", C.c_int32)] + \
+        [(n, P) for n in ("scores", "sel", "n_sel", "kth", "beta", "n_qcand", "cand", "uni",
+                          "pf_h", "pf_g", "miss_h", "miss_g", "counts", "status",
+                          "internal")] + [("internal_bytes", C.c_size_t)]
+
+
+ECHO_PF_CNT_CAND, ECHO_PF_CNT_UNION, ECHO_PF_CNT_EARLY, ECHO_PF_CNT_LATE = 0, 1, 2, 3
+ECHO_PF_NCOUNTS = 8
 
 _lib = None
 
@@ -86,6 +104,17 @@ def lib() -> C.CDLL:
             "echo_release": (C.c_int, [dp, lp, P, P, C.c_int32, P, C.c_int, wp, P]),
             "echo_admit": (C.c_int, [dp, lp, P, P, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                      C.c_int, wp, P]),
+            "echo_prefill_ws_bytes": (C.c_size_t, [dp, C.c_int32]),
+            "echo_prefill_ws_bind": (C.c_int, [dp, C.c_int32, P, C.c_size_t,
+                                               C.POINTER(echo_prefill_ws_t)]),
+            "echo_prefill_ws_reset": (C.c_int, [dp, C.POINTER(echo_prefill_ws_t), P]),
+            "echo_prefill_score": (C.c_int, [dp, lp, C.POINTER(echo_prefill_chunk_t),
+                                             C.POINTER(echo_prefill_ws_t), P]),
+            "echo_prefill_early": (C.c_int, [dp, lp, C.POINTER(echo_prefill_chunk_t),
+                                             C.POINTER(echo_prefill_ws_t), P]),
+            "echo_prefill_select": (C.c_int, [dp, lp, C.POINTER(echo_prefill_chunk_t),
+                                              C.POINTER(echo_prefill_ws_t), P]),
+            "echo_prefill_copy": (C.c_int, [dp, lp, C.POINTER(echo_prefill_ws_t), C.c_int, P]),
             "echo_status_string": (C.c_char_p, [C.c_int]),
         }
         for name, (res, args) in sigs.items():
@@ -177,6 +206,38 @@ def echo_admit(dims, layer, host_base: int, ctx_len: int, batch: int, b: int, ba
     """host_base, ctx_len: device int32 pointers; with commit, row b takes (base, length)."""
     return lib().echo_admit(C.byref(dims), _ref(layer), host_base, ctx_len, batch, b, base,
                             length, commit, _ref(ws), stream)
+
+
+def echo_prefill_ws_bytes(dims, max_chunk: int) -> int:
+    return lib().echo_prefill_ws_bytes(C.byref(dims), max_chunk)
+
+
+def echo_prefill_ws_bind(dims, max_chunk: int, base: int, nbytes: int, pws) -> int:
+    return lib().echo_prefill_ws_bind(C.byref(dims), max_chunk, base, nbytes, C.byref(pws))
+
+
+def echo_prefill_ws_reset(dims, pws, stream: int) -> int:
+    return lib().echo_prefill_ws_reset(C.byref(dims), C.byref(pws), stream)
+
+
+def echo_prefill_score(dims, layer, chunk, pws, stream: int) -> int:
+    return lib().echo_prefill_score(C.byref(dims), _ref(layer), C.byref(chunk), C.byref(pws),
+                                    stream)
+
+
+def echo_prefill_early(dims, layer, chunk, pws, stream: int) -> int:
+    return lib().echo_prefill_early(C.byref(dims), _ref(layer), C.byref(chunk), C.byref(pws),
+                                    stream)
+
+
+def echo_prefill_select(dims, layer, chunk, pws, stream: int) -> int:
+    return lib().echo_prefill_select(C.byref(dims), _ref(layer), C.byref(chunk), C.byref(pws),
+                                     stream)
+
+
+def echo_prefill_copy(dims, layer, pws, which: int, stream: int) -> int:
+    """which: 0 = the early installs, 1 = the later ones."""
+    return lib().echo_prefill_copy(C.byref(dims), _ref(layer), C.byref(pws), which, stream)
 
 
 def echo_status_string(code: int) -> str:

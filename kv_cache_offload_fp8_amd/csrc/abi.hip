@@ -182,6 +182,112 @@ StepArgs make_args(const echo_dims_t &d, const echo_layer_t *l, const echo_batch
     if ((x) != hipSuccess) return ECHO_EHIP; \
   } while (0)
 
+// ------------------------------------------------------------ prefill workspace
+struct PrefillLayout {
+  int64_t scores, sel, n_sel, kth, beta, n_qcand, cand, uni, pf_h, pf_g, miss_h, miss_g, counts,
+      status, internal, qhi, qlo, wsc, cflag, uflag, seg, total;
+};
+
+int64_t round_seg(int64_t n) { return (n + kPfSeg - 1) / kPfSeg * kPfSeg; }
+
+bool prefill_layout(const echo_dims_t *d, int32_t max_chunk, PrefillLayout *L) {
+  if (check_dims(d) != ECHO_OK || max_chunk < 1 || max_chunk > 4096 || d->max_ctx > (1 << 22))
+    return false;
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t o = off;
+    off += (bytes + 255) / 256 * 256;
+    return o;
+  };
+  const int64_t C = max_chunk, N = d->max_ctx, K = d->top_k;
+  L->scores = take(C * N * 4);
+  L->sel = take(C * K * 4);
+  L->n_sel = take(C * 4);
+  L->kth = take(C * 4);
+  L->beta = take(C * 4);
+  L->n_qcand = take(C * 4);
+  L->cand = take(N * 4);
+  L->uni = take(N * 4);
+  L->pf_h = take(N * 4);
+  L->pf_g = take(N * 4);
+  L->miss_h = take(N * 4);
+  L->miss_g = take(N * 4);
+  L->counts = take(ECHO_PF_NCOUNTS * 4);
+  L->status = take(4);
+  L->internal = off;
+  L->qhi = take(C * kHeadsPad * kDimPad);
+  L->qlo = take(C * kHeadsPad * kDimPad);
+  L->wsc = take(C * kHeadsPad * 4);
+  L->cflag = take(round_seg(N));
+  L->uflag = take(round_seg(N));
+  L->seg = take((round_seg(N) / kPfSeg + 1) * 4);
+  L->total = off;
+  return true;
+}
+
+bool prefill_ws_ok(const echo_prefill_ws_t *w) {
+  return w && w->max_chunk >= 1 && w->scores && w->sel && w->n_sel && w->kth && w->beta &&
+         w->n_qcand && w->cand && w->uni && w->pf_h && w->pf_g && w->miss_h && w->miss_g &&
+         w->counts && w->status && w->internal;
+}
+
+void fill_prefill_ws(const echo_dims_t &d, const echo_prefill_ws_t *w, PrefillArgs *p) {
+  PrefillLayout L;
+  prefill_layout(&d, w->max_chunk, &L);
+  uint8_t *in = w->internal;
+  p->scores = w->scores;
+  p->sel = w->sel;
+  p->n_sel = w->n_sel;
+  p->kth = w->kth;
+  p->beta = w->beta;
+  p->n_qcand = w->n_qcand;
+  p->cand = w->cand;
+  p->uni = w->uni;
+  p->pf_h = w->pf_h;
+  p->pf_g = w->pf_g;
+  p->miss_h = w->miss_h;
+  p->miss_g = w->miss_g;
+  p->counts = w->counts;
+  p->status = w->status;
+  p->qhi = in + (L.qhi - L.internal);
+  p->qlo = in + (L.qlo - L.internal);
+  p->wsc = (float *)(in + (L.wsc - L.internal));
+  p->cflag = in + (L.cflag - L.internal);
+  p->uflag = in + (L.uflag - L.internal);
+  p->seg = (int32_t *)(in + (L.seg - L.internal));
+}
+
+int prefill_args(const echo_dims_t *dims, const echo_layer_t *layer,
+                 const echo_prefill_chunk_t *c, const echo_prefill_ws_t *pws, StepArgs *a,
+                 PrefillArgs *p) {
+  int rc = check_dims(dims);
+  if (rc != ECHO_OK) return rc;
+  if (!layer_ok(layer, false) || !prefill_ws_ok(pws) || !c) return ECHO_EINVAL;
+  PrefillLayout L;
+  if (!prefill_layout(dims, pws->max_chunk, &L)) return ECHO_EINVAL;
+  if (c->queries < 1 || c->queries > pws->max_chunk || c->hist_len < 1 ||
+      c->hist_len > dims->max_ctx || c->host_base < 0 || c->host_base % 16 != 0 ||
+      (int64_t)c->host_base + c->hist_len > dims->n_host || !c->q || !c->w ||
+      ((uintptr_t)c->q & 15) != 0)
+    return ECHO_EINVAL;
+  *a = make_args(*dims, layer, nullptr, echo_ws_t(), ECHO_THETA_POS_INF);
+  memset(p, 0, sizeof *p);
+  fill_prefill_ws(*dims, pws, p);
+  p->C = c->queries;
+  p->N = c->hist_len;
+  p->hb = c->host_base;
+  p->q = c->q;
+  p->w = c->w;
+  p->pred = c->pred;
+  p->qblocks = (c->queries + 15) / 16;
+  const int nch = (c->hist_len + 63) / 64;
+  int ts = (1024 + p->qblocks - 1) / p->qblocks;
+  ts = (ts + 7) / 8 * 8;
+  const int tmax = (nch + 7) / 8 * 8;
+  p->tsplits = ts < 8 ? 8 : (ts > tmax ? tmax : ts);
+  return ECHO_OK;
+}
+
 int run_indexer(const StepArgs &a, int extra_roles, hipStream_t s) {
   LAUNCH(launch_begin(a, BEGIN_REQ | BEGIN_Q | BEGIN_CLR_INDEX | BEGIN_CLR_TOPK | extra_roles, s));
   LAUNCH(launch_score(a, s));
@@ -366,6 +472,94 @@ int echo_admit(const echo_dims_t *dims, const echo_layer_t *layer, int32_t *host
   bt.ctx_len = ctx_len;
   const StepArgs a = make_args(*dims, layer, &bt, *ws, ECHO_THETA_POS_INF);
   LAUNCH(launch_admit(a, b, base, len, host_base, ctx_len, commit ? 1 : 0, stream));
+  return ECHO_OK;
+}
+
+size_t echo_prefill_ws_bytes(const echo_dims_t *dims, int32_t max_chunk) {
+  PrefillLayout L;
+  if (!prefill_layout(dims, max_chunk, &L)) return 0;
+  return (size_t)L.total;
+}
+
+int echo_prefill_ws_bind(const echo_dims_t *dims, int32_t max_chunk, void *base, size_t bytes,
+                         echo_prefill_ws_t *pws) {
+  PrefillLayout L;
+  if (!prefill_layout(dims, max_chunk, &L)) return ECHO_EINVAL;
+  if (!base || !pws || ((uintptr_t)base & 255) != 0 || bytes < (size_t)L.total)
+    return ECHO_EINVAL;
+  uint8_t *p = (uint8_t *)base;
+  pws->max_chunk = max_chunk;
+  pws->scores = (float *)(p + L.scores);
+  pws->sel = (int32_t *)(p + L.sel);
+  pws->n_sel = (int32_t *)(p + L.n_sel);
+  pws->kth = (float *)(p + L.kth);
+  pws->beta = (int32_t *)(p + L.beta);
+  pws->n_qcand = (int32_t *)(p + L.n_qcand);
+  pws->cand = (int32_t *)(p + L.cand);
+  pws->uni = (int32_t *)(p + L.uni);
+  pws->pf_h = (int32_t *)(p + L.pf_h);
+  pws->pf_g = (int32_t *)(p + L.pf_g);
+  pws->miss_h = (int32_t *)(p + L.miss_h);
+  pws->miss_g = (int32_t *)(p + L.miss_g);
+  pws->counts = (int32_t *)(p + L.counts);
+  pws->status = (int32_t *)(p + L.status);
+  pws->internal = p + L.internal;
+  pws->internal_bytes = (size_t)(L.total - L.internal);
+  return ECHO_OK;
+}
+
+int echo_prefill_ws_reset(const echo_dims_t *dims, const echo_prefill_ws_t *pws,
+                          hipStream_t stream) {
+  if (check_dims(dims) != ECHO_OK || !prefill_ws_ok(pws)) return ECHO_EINVAL;
+  LAUNCH(launch_fill_zero((uint32_t *)pws->counts, ECHO_PF_NCOUNTS, stream));
+  LAUNCH(launch_fill_zero((uint32_t *)pws->status, 1, stream));
+  LAUNCH(launch_fill_zero((uint32_t *)pws->internal, (int64_t)(pws->internal_bytes / 4), stream));
+  return ECHO_OK;
+}
+
+int echo_prefill_score(const echo_dims_t *dims, const echo_layer_t *layer,
+                       const echo_prefill_chunk_t *chunk, const echo_prefill_ws_t *pws,
+                       hipStream_t stream) {
+  StepArgs a;
+  PrefillArgs p;
+  const int rc = prefill_args(dims, layer, chunk, pws, &a, &p);
+  if (rc != ECHO_OK) return rc;
+  LAUNCH(launch_prefill_score(a, p, stream));
+  return ECHO_OK;
+}
+
+int echo_prefill_early(const echo_dims_t *dims, const echo_layer_t *layer,
+                       const echo_prefill_chunk_t *chunk, const echo_prefill_ws_t *pws,
+                       hipStream_t stream) {
+  StepArgs a;
+  PrefillArgs p;
+  const int rc = prefill_args(dims, layer, chunk, pws, &a, &p);
+  if (rc != ECHO_OK) return rc;
+  LAUNCH(launch_prefill_early(a, p, stream));
+  return ECHO_OK;
+}
+
+int echo_prefill_select(const echo_dims_t *dims, const echo_layer_t *layer,
+                        const echo_prefill_chunk_t *chunk, const echo_prefill_ws_t *pws,
+                        hipStream_t stream) {
+  StepArgs a;
+  PrefillArgs p;
+  const int rc = prefill_args(dims, layer, chunk, pws, &a, &p);
+  if (rc != ECHO_OK) return rc;
+  LAUNCH(launch_prefill_exact(a, p, stream));
+  return ECHO_OK;
+}
+
+int echo_prefill_copy(const echo_dims_t *dims, const echo_layer_t *layer,
+                      const echo_prefill_ws_t *pws, int list, hipStream_t stream) {
+  if (check_dims(dims) != ECHO_OK) return ECHO_EINVAL;
+  if (!layer_ok(layer, false) || !prefill_ws_ok(pws) || (list != 0 && list != 1))
+    return ECHO_EINVAL;
+  StepArgs a = make_args(*dims, layer, nullptr, echo_ws_t(), ECHO_THETA_POS_INF);
+  PrefillArgs p;
+  memset(&p, 0, sizeof p);
+  fill_prefill_ws(*dims, pws, &p);
+  LAUNCH(launch_prefill_copy(a, p, list, stream));
   return ECHO_OK;
 }
 

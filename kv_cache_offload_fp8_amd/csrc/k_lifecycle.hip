@@ -18,8 +18,6 @@ namespace echo {
 
 constexpr int kReleaseThreads = 256;
 constexpr int kReleaseBlocksX = 64;  // workgroups per released request
-constexpr int kListThreads = 1024;
-constexpr int kListSlots = 16;  // free flags per thread per round of the list rebuild
 
 // Every workgroup checks every masked request (the same data, so every
 // workgroup reaches the same verdict); the first one reports it.
@@ -72,23 +70,7 @@ __global__ __launch_bounds__(kListThreads) void k_release_finish(StepArgs a, con
     if (a.guard) a.guard[tid] = __builtin_huge_valf();
     if (commit) ctx_io[tid] = 0;
   }
-  int off = 0;
-  for (int64_t g0 = 0; g0 < a.n_gpu; g0 += (int64_t)kListThreads * kListSlots) {
-    const int64_t gs = g0 + (int64_t)tid * kListSlots;
-    uint32_t bits = 0;  // bit i: slot gs + i is free
-#pragma unroll
-    for (int i = 0; i < kListSlots; ++i)
-      if (gs + i < a.n_gpu && a.freef[gs + i]) bits |= 1u << i;
-    int total;
-    int r = off + block_excl_scan<kListThreads>(__popc(bits), sh, &total);
-    while (bits) {
-      const int i = __ffs(bits) - 1;
-      a.idxbuf[r++] = (int32_t)(gs + i);
-      bits &= bits - 1;
-    }
-    off += total;
-  }
-  if (tid == 0) a.ctl[ECHO_CTL_NFREE] = off;
+  rebuild_free_list(a, sh);
 }
 
 hipError_t launch_release(const StepArgs &a, const int32_t *mask, int32_t *ctx_io, int commit,

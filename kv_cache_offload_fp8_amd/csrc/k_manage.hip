@@ -381,6 +381,12 @@ __global__ __launch_bounds__(256) void k_fill_zero(uint32_t *p, int64_t n) {
     p[i] = 0;
 }
 
+hipError_t launch_fill_zero(uint32_t *p, int64_t n_words, hipStream_t s) {
+  hipLaunchKernelGGL(k_fill_zero, dim3(n_words > 256 * 1024 ? 1024 : 64), dim3(256), 0, s, p,
+                     n_words);
+  return hipGetLastError();
+}
+
 hipError_t launch_ws_reset(const echo_ws_t &ws, hipStream_t s) {
   hipLaunchKernelGGL(k_fill_zero, dim3(1), dim3(256), 0, s, (uint32_t *)ws.status, (int64_t)1);
   hipLaunchKernelGGL(k_fill_zero, dim3(1), dim3(256), 0, s, (uint32_t *)ws.counters,

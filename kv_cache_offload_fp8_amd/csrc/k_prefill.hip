@@ -1,0 +1,501 @@
+// Chunked-prefill selection.
+//
+// The ECHO review ("Core method / prefill") splits a prefill into query chunks.
+// While chunk i+1 is scored, the KV of the candidates already identified for
+// chunk i moves over the host link.  The candidates come from a 256-bucket coarse
+// histogram instead of a full top-k: the buckets strictly above the one holding
+// the k-th score are certain members, and the boundary bucket waits for the exact
+// selection.  Subtracting a predicted k-th score first makes the buckets fine near
+// the boundary, so more tokens are certain; the exact fetch afterwards covers the
+// rest.  "Core method / prefetch inside the indexer pipeline" splits the
+// indexer's prefill work by query chunk.
+//
+// One request's history of N tokens (host ids hb .. hb+N-1, K resident in HBM in
+// the tiled layout) is scored against the chunk's C queries.  Kernels per chunk:
+//   k_pf_stage    q split into fp8 hi/lo with a per-head power-of-two scale
+//   k_pf_score    scores [C][N] on the fp8 MFMA (the heads x tokens contraction
+//                 for every query; each wave keeps two queries' operands in
+//                 registers and streams 64-token K chunks; the grid is placed so
+//                 that the workgroups of one XCD share one token range through
+//                 its L2)
+//   k_pf_coarse   per query: the bucket histogram of fp16(score - pred), the
+//                 boundary bucket, and the candidate flags above it
+//   k_pf_flags_*  the union of flags as an ascending token list
+//   k_pf_inst_*   install a list in order: resident tokens get priority t, the
+//                 others take the next ascending free slots (idxbuf)
+//   k_pf_exact    per query: exact top-k by (score desc, token asc), written in
+//                 ascending token order, and its k-th score
+//   k_pf_copy     host rows of an install list into the GPU pool
+//   k_pf_finish   step counter and the rebuilt free list
+// The early install and its copy run right after the coarse pass, so the copy
+// (on its own stream) overlaps the exact selection and the next chunk's scoring.
+#include "kernels.h"
+#include "select.h"
+
+namespace echo {
+
+typedef int v8i_pf __attribute__((ext_vector_type(8)));
+typedef float v4f_pf __attribute__((ext_vector_type(4)));
+typedef int v4i_pf __attribute__((ext_vector_type(4)));
+
+constexpr int kPfWaves = 8;        // waves per scoring workgroup
+constexpr int kPfQ = 2;            // queries per wave
+constexpr int kPfQBlock = kPfWaves * kPfQ;
+constexpr int kPfCopyBlocks = 32;  // a small grid keeps about 256 KB of host reads in flight
+
+// The status as one workgroup sees it: read once and shared, so that all of its
+// waves take the same branch before the block barriers that follow.
+__device__ inline bool block_failed(const int32_t *status) {
+  __shared__ int s_failed;
+  if (threadIdx.x == 0) s_failed = failed(status) ? 1 : 0;
+  __syncthreads();
+  const bool f = s_failed != 0;
+  __syncthreads();
+  return f;
+}
+
+// ------------------------------------------------------------------ stage
+// Query i, heads quarter*16 .. +15: thread = (head, 8 dims).  q' = q * 2^e with
+// max |q'| in [128, 256); q_hi = e4m3(q'), q_lo = e4m3(q' - q_hi); the head weight
+// takes 2^-e (ReLU is positively homogeneous).  Zero for padded heads and dims.
+__global__ __launch_bounds__(256) void k_pf_stage(StepArgs a, PrefillArgs p) {
+  if (failed(p.status)) return;
+  const int i = blockIdx.x >> 2, quarter = blockIdx.x & 3;
+  const int tid = threadIdx.x;
+  const int j = quarter * 16 + (tid >> 4), d0 = (tid & 15) * 8;
+  const uint16_t *src = p.q + (int64_t)i * a.H * a.D;
+  const bool in = j < a.H && d0 < a.D;
+  const uint4 w4 = in ? *(const uint4 *)(src + j * a.D + d0) : make_uint4(0, 0, 0, 0);
+  const float wj = d0 == 0 && j < a.H ? p.w[(int64_t)i * a.H + j] : 0.0f;
+  const uint32_t wd[4] = {w4.x, w4.y, w4.z, w4.w};
+  float x[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    x[2 * k] = __uint_as_float(wd[k] << 16);
+    x[2 * k + 1] = __uint_as_float(wd[k] & 0xFFFF0000u);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(x[k]));
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  int e = 0;
+  if (amax > 0.0f) {
+    int E;
+    frexpf(amax, &E);
+    e = min(64, max(-64, 8 - E));
+  }
+  uint32_t whi[2] = {0, 0}, wlo[2] = {0, 0};
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float xs = ldexpf(x[k], e);
+    const uint8_t h8 = e4m3_encode(xs);
+    const uint8_t l8 = e4m3_encode(xs - e4m3_decode(h8));
+    whi[k >> 2] |= (uint32_t)h8 << (8 * (k & 3));
+    wlo[k >> 2] |= (uint32_t)l8 << (8 * (k & 3));
+  }
+  const int64_t o = ((int64_t)i * kHeadsPad + j) * kDimPad + d0;
+  *(uint2 *)(p.qhi + o) = make_uint2(whi[0], whi[1]);
+  *(uint2 *)(p.qlo + o) = make_uint2(wlo[0], wlo[1]);
+  if (d0 == 0) p.wsc[(int64_t)i * kHeadsPad + j] = j < a.H ? ldexpf(wj, -e) : 0.0f;
+}
+
+// ------------------------------------------------------------------ score
+// K operands of history tokens s0 .. s0+63 (s0 a multiple of 64): sub-tile u holds
+// tokens s0 + 16u .. +15; lane l feeds token s0 + 16u + (l & 15) with dims
+// 32(l >> 4) .. +31, two 16-byte pieces at 16 l and 8 D + 16 l inside the token's
+// group of 16 (hb is a multiple of 16).  Tokens past the history read its last
+// group (their scores are dropped); lanes whose dims lie past D read the first 32
+// dims, which meet q's zero padding.
+__device__ inline void pf_load_k(const StepArgs &a, const PrefillArgs &p, int s0, int lane,
+                                 v8i_pf (&kb)[4]) {
+  const int lp = 32 * (lane >> 4) < a.D ? lane : (lane & 15);
+  const int glast = (p.N - 1) & ~15;
+  const uint32_t lo = (uint32_t)lp * 16u, hi = lo + 8u * (uint32_t)a.D;
+  const int s0u = __builtin_amdgcn_readfirstlane(s0);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int st = s0u + 16 * u;
+    const int sg = st < p.N ? st : glast;
+    const uint8_t *g = a.kidx + ((int64_t)p.hb + sg) * a.D;
+    const v4i_pf x0 = *(const v4i_pf *)(g + lo);
+    const v4i_pf x1 = *(const v4i_pf *)(g + hi);
+    kb[u] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+}
+
+// Lane l returns the score of token s0 + l for one query (four head groups, q_hi
+// and q_lo terms, ReLU as an integer max, the weighted sum over the lane's heads,
+// then over the four lane groups that share a token).
+__device__ inline float pf_score64(const v8i_pf (&kb)[4], const v8i_pf (&qa)[4][2],
+                                   const float (&wr)[4][4], int lane) {
+  float sc4[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    float v = 0.0f;
+#pragma unroll
+    for (int hg = 0; hg < 4; ++hg) {
+      v4f_pf acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[hg][0], kb[u], acc, 0, 0, 0, 0,
+                                                             0, 0);
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[hg][1], kb[u], acc, 0, 0, 0, 0,
+                                                             0, 0);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        v += wr[hg][rr] * __int_as_float(max(__float_as_int(acc[rr]), 0));
+    }
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    sc4[u] = v;
+  }
+  const int sel = lane >> 4;
+  return sel == 0 ? sc4[0] : sel == 1 ? sc4[1] : sel == 2 ? sc4[2] : sc4[3];
+}
+
+// Workgroup b: XCD x = b % 8 (the hardware's round-robin placement) takes token
+// splits x * tsplits/8 .. , all query blocks of one split before the next, so the
+// workgroups resident on one XCD read the same K range through its L2.
+__global__ __launch_bounds__(kPfWaves * kWave) void k_pf_score(StepArgs a, PrefillArgs p) {
+  if (failed(p.status)) return;
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int b = blockIdx.x, xcd = b & 7, jj = b >> 3;
+  const int ts = xcd * (p.tsplits >> 3) + jj / p.qblocks, qb = jj % p.qblocks;
+  const int q0 = qb * kPfQBlock + wave * kPfQ;
+  if (q0 >= p.C) return;  // wave-uniform; no barrier follows
+  const int nch = (p.N + 63) >> 6;
+  const int per = (nch + p.tsplits - 1) / p.tsplits;
+  const int c0 = ts * per, c1 = min(nch, c0 + per);
+  if (c0 >= c1) return;
+  const int row = lane & 15, chunk = (lane >> 4) * 32;
+  v8i_pf qa[kPfQ][4][2];
+  float wr[kPfQ][4][4];
+#pragma unroll
+  for (int u = 0; u < kPfQ; ++u) {
+    const int qi = min(q0 + u, p.C - 1);  // a missing second query repeats the first
+    const uint8_t *qh = p.qhi + (int64_t)qi * kHeadsPad * kDimPad;
+    const uint8_t *ql = p.qlo + (int64_t)qi * kHeadsPad * kDimPad;
+#pragma unroll
+    for (int hg = 0; hg < 4; ++hg) {
+      qa[u][hg][0] = *(const v8i_pf *)(qh + (hg * 16 + row) * kDimPad + chunk);
+      qa[u][hg][1] = *(const v8i_pf *)(ql + (hg * 16 + row) * kDimPad + chunk);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        wr[u][hg][rr] = p.wsc[(int64_t)qi * kHeadsPad + hg * 16 + (lane >> 4) * 4 + rr];
+    }
+  }
+  auto emit = [&](const v8i_pf (&kb)[4], int c) {
+    const int s = c * 64 + lane;
+#pragma unroll
+    for (int u = 0; u < kPfQ; ++u) {
+      const float v = pf_score64(kb, qa[u], wr[u], lane);
+      if (q0 + u < p.C && s < p.N) p.scores[(int64_t)(q0 + u) * p.N + s] = v;
+    }
+  };
+  v8i_pf k0[4], k1[4];
+  pf_load_k(a, p, c0 * 64, lane, k0);
+  for (int c = c0; c < c1; c += 2) {  // two register sets: chunk c + 1 loads while c computes
+    if (c + 1 < c1) pf_load_k(a, p, (c + 1) * 64, lane, k1);
+    emit(k0, c);
+    if (c + 2 < c1) pf_load_k(a, p, (c + 2) * 64, lane, k0);
+    if (c + 1 < c1) emit(k1, c + 1);
+  }
+}
+
+// ------------------------------------------------------------------ coarse
+// Bucket of a score shifted by the predicted k-th score: the difference in fp32,
+// rounded to half precision (nearest even), then the top byte of an order key of
+// the half bits (larger value, larger key; -0 counts as +0).
+__device__ inline int pf_bucket(float score, float pred) {
+  const _Float16 h = (_Float16)(score - pred);
+  uint16_t u = __builtin_bit_cast(uint16_t, h);
+  if (u == 0x8000) u = 0;
+  const uint16_t key = (u & 0x8000) ? (uint16_t)~u : (uint16_t)(u | 0x8000);
+  return key >> 8;
+}
+
+__global__ __launch_bounds__(kSelThreads) void k_pf_coarse(StepArgs a, PrefillArgs p) {
+  __shared__ uint32_t hist[256];
+  __shared__ int sh[kSelThreads / kWave + 1];
+  __shared__ int s_beta;
+  if (block_failed(p.status)) return;
+  const int i = blockIdx.x, tid = threadIdx.x;
+  const float *row = p.scores + (int64_t)i * p.N;
+  const float pr = p.pred ? p.pred[i] : 0.0f;
+  int beta = -1;
+  if (p.N > a.K) {
+    if (tid < 256) hist[tid] = 0;
+    if (tid == 0) s_beta = 0;
+    __syncthreads();
+    for (int s = tid; s < p.N; s += kSelThreads) atomicAdd(&hist[pf_bucket(row[s], pr)], 1u);
+    __syncthreads();
+    // thread t < 256 holds bucket 255 - t: the boundary is the first one, from the
+    // top, at which the running count reaches k
+    const int c = tid < 256 ? (int)hist[255 - tid] : 0;
+    int tot;
+    const int excl = block_excl_scan<kSelThreads>(c, sh, &tot);
+    if (tid < 256 && excl < a.K && excl + c >= a.K) s_beta = 255 - tid;
+    __syncthreads();
+    beta = s_beta;
+  }
+  int cnt = 0;
+  for (int s = tid; s < p.N; s += kSelThreads) {
+    if (beta < 0 || pf_bucket(row[s], pr) > beta) {
+      p.cflag[s] = 1;
+      ++cnt;
+    }
+  }
+  int tot;
+  block_excl_scan<kSelThreads>(cnt, sh, &tot);
+  if (tid == 0) {
+    p.beta[i] = beta;
+    p.n_qcand[i] = tot;
+  }
+}
+
+// ------------------------------------------------------------------ lists
+// Ordered passes over segments of kPfSeg entries, 4 per thread: a count per
+// segment, then each segment's prefix from the counts before it and a block scan.
+__device__ inline int pf_seg_before(const int32_t *seg, int blk, int nseg, int *total, int *sh) {
+  const int tid = threadIdx.x;
+  const int v = tid < nseg ? seg[tid] : 0;
+  int tot;
+  const int excl = block_excl_scan<kSelThreads>(v, sh, &tot);
+  __shared__ int s_before;
+  if (tid == blk) s_before = excl;
+  __syncthreads();
+  *total = tot;
+  const int r = s_before;
+  __syncthreads();
+  return r;
+}
+
+// flags -> count per segment
+__global__ __launch_bounds__(kSelThreads) void k_pf_flags_count(PrefillArgs p, const uint8_t *flag) {
+  __shared__ int sh[kSelThreads / kWave + 1];
+  if (block_failed(p.status)) return;
+  const int s = blockIdx.x * kPfSeg + threadIdx.x * 4;
+  const uint32_t f = *(const uint32_t *)(flag + s);  // padded to whole segments, zero past N
+  int tot;
+  block_excl_scan<kSelThreads>(__popc(f & 0x01010101u), sh, &tot);
+  if (threadIdx.x == 0) p.seg[blockIdx.x] = tot;
+}
+
+// flags -> ascending list (and the flags cleared for the next chunk)
+__global__ __launch_bounds__(kSelThreads) void k_pf_flags_list(PrefillArgs p, uint8_t *flag,
+                                                               int32_t *list, int which) {
+  __shared__ int sh[kSelThreads / kWave + 1];
+  if (block_failed(p.status)) return;
+  const int nseg = gridDim.x;
+  int total;
+  const int before = pf_seg_before(p.seg, blockIdx.x, nseg, &total, sh);
+  const int s = blockIdx.x * kPfSeg + threadIdx.x * 4;
+  uint32_t f = *(const uint32_t *)(flag + s) & 0x01010101u;
+  int tot;
+  int r = before + block_excl_scan<kSelThreads>(__popc(f), sh, &tot);
+  if (f) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      if ((f >> (8 * v)) & 1) list[r++] = s + v;
+    *(uint32_t *)(flag + s) = 0;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) p.counts[which] = total;
+}
+
+// install pass 1: tokens of the list without a slot, per segment
+__global__ __launch_bounds__(kSelThreads) void k_pf_inst_count(StepArgs a, PrefillArgs p,
+                                                               const int32_t *list, int which) {
+  __shared__ int sh[kSelThreads / kWave + 1];
+  if (block_failed(p.status)) return;
+  const int n = p.counts[which];
+  int cnt = 0;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int j = blockIdx.x * kPfSeg + threadIdx.x * 4 + v;
+    if (j < n && a.h2g[(int64_t)p.hb + list[j]] == -1) ++cnt;
+  }
+  int tot;
+  block_excl_scan<kSelThreads>(cnt, sh, &tot);
+  if (threadIdx.x == 0) p.seg[blockIdx.x] = tot;
+}
+
+// install pass 2: in list order, a resident token gets priority t; the r-th one
+// without a slot takes free slot idxbuf[cursor + r].  Every workgroup checks the
+// total against the free slots first, so none writes if they do not suffice.
+__global__ __launch_bounds__(kSelThreads) void k_pf_inst_write(StepArgs a, PrefillArgs p,
+                                                               const int32_t *list, int which,
+                                                               int late, int32_t *out_h,
+                                                               int32_t *out_g) {
+  __shared__ int sh[kSelThreads / kWave + 1];
+  if (block_failed(p.status)) return;
+  const int n = p.counts[which];
+  const int t = a.ctl[ECHO_CTL_STEP];
+  const int nfree = a.ctl[ECHO_CTL_NFREE];
+  const int cursor = late ? p.counts[ECHO_PF_CNT_EARLY] : 0;
+  int total;
+  const int before = pf_seg_before(p.seg, blockIdx.x, gridDim.x, &total, sh);
+  if (cursor + total > nfree) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) fail(p.status, ECHO_ECAPACITY);
+    return;
+  }
+  int64_t h[4];
+  int32_t g[4];
+  int cnt = 0;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int j = blockIdx.x * kPfSeg + threadIdx.x * 4 + v;
+    h[v] = j < n ? (int64_t)p.hb + list[j] : -1;
+    g[v] = j < n ? a.h2g[h[v]] : 0;
+    if (j < n && g[v] == -1) ++cnt;
+  }
+  int tot;
+  int r = before + block_excl_scan<kSelThreads>(cnt, sh, &tot);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    if (h[v] < 0) continue;
+    if (g[v] >= 0) {
+      a.prio[g[v]] = t;
+    } else {
+      const int32_t gs = a.idxbuf[cursor + r];
+      a.h2g[h[v]] = gs;
+      a.g2h[gs] = (int32_t)h[v];
+      a.freef[gs] = 0;
+      a.prio[gs] = t;
+      out_h[r] = (int32_t)h[v];
+      out_g[r] = gs;
+      ++r;
+    }
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0)
+    p.counts[late ? ECHO_PF_CNT_LATE : ECHO_PF_CNT_EARLY] = total;
+}
+
+// ------------------------------------------------------------------ exact
+__global__ __launch_bounds__(kSelThreads) void k_pf_exact(StepArgs a, PrefillArgs p) {
+  __shared__ int sh[kSelThreads / kWave + 1];
+  __shared__ uint64_t shu[kSelThreads / kWave];
+  if (block_failed(p.status)) return;
+  const int i = blockIdx.x, tid = threadIdx.x;
+  const float *row = p.scores + (int64_t)i * p.N;
+  uint64_t P;
+  int pos;
+  block_select_by([=](int s) { return ((uint64_t)topk_key(row[s]) << 32) | (uint32_t)s; }, p.N,
+                  a.K, &P, &pos);
+  int32_t *out = p.sel + (int64_t)i * a.K;
+  int written = 0;
+  uint64_t worst = 0;  // the largest selected composite: the k-th in selection order
+  for (int base = 0; base < p.N; base += kPfSeg) {
+    uint32_t keys[4];
+    int cnt = 0;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int s = base + tid * 4 + v;
+      keys[v] = s < p.N ? topk_key(row[s]) : 0xFFFFFFFFu;
+      const bool in = s < p.N && composite_selected(keys[v], s, P, pos);
+      cnt += in ? 1 : 0;
+    }
+    int tot;
+    int r = written + block_excl_scan<kSelThreads>(cnt, sh, &tot);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int s = base + tid * 4 + v;
+      if (s < p.N && composite_selected(keys[v], s, P, pos)) {
+        out[r++] = s;
+        p.uflag[s] = 1;
+        const uint64_t x = ((uint64_t)keys[v] << 32) | (uint32_t)s;
+        worst = x > worst ? x : worst;
+      }
+    }
+    written += tot;
+  }
+  worst = block_max_u64<kSelThreads>(worst, shu);
+  if (tid == 0) {
+    p.n_sel[i] = written;
+    p.kth[i] = score_of_key((uint32_t)(worst >> 32));
+  }
+}
+
+// ------------------------------------------------------------------ copy
+__global__ __launch_bounds__(256) void k_pf_copy(StepArgs a, PrefillArgs p, const int32_t *hl,
+                                                 const int32_t *gl, int which) {
+  if (failed(p.status)) return;
+  const int n = p.counts[which];
+  if (n <= 0) return;
+  const int cpr = a.latent * 2 / 16;
+  const int64_t total = (int64_t)n * cpr;
+  const v4i_pf *src = (const v4i_pf *)a.host_kv;
+  v4i_pf *dst = (v4i_pf *)a.gpu_kv;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i0 = (int64_t)blockIdx.x * 256 + threadIdx.x; i0 < total; i0 += 4 * stride) {
+    v4i_pf v[4];
+    int64_t d[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {  // past the end: the last piece again (no branch)
+      const int64_t x = i0 + u * stride < total ? i0 + u * stride : total - 1;
+      const int r = (int)(x / cpr);
+      const int c = (int)(x - (int64_t)r * cpr);
+      d[u] = (int64_t)gl[r] * cpr + c;
+      v[u] = src[(int64_t)hl[r] * cpr + c];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) dst[d[u]] = v[u];
+  }
+}
+
+// ------------------------------------------------------------------ finish
+__global__ __launch_bounds__(kListThreads) void k_pf_finish(StepArgs a, PrefillArgs p) {
+  __shared__ int sh[kListThreads / kWave + 1];
+  if (block_failed(p.status)) return;
+  rebuild_free_list(a, sh);
+  if (threadIdx.x == 0) a.ctl[ECHO_CTL_STEP] += 1;
+}
+
+// ------------------------------------------------------------------ launchers
+hipError_t launch_prefill_score(const StepArgs &a, const PrefillArgs &p, hipStream_t s) {
+  const int nseg = (p.N + kPfSeg - 1) / kPfSeg;
+  hipLaunchKernelGGL(k_pf_stage, dim3(p.C * 4), dim3(256), 0, s, a, p);
+  hipLaunchKernelGGL(k_pf_score, dim3(p.qblocks * p.tsplits), dim3(kPfWaves * kWave), 0, s, a,
+                     p);
+  hipLaunchKernelGGL(k_pf_coarse, dim3(p.C), dim3(kSelThreads), 0, s, a, p);
+  hipLaunchKernelGGL(k_pf_flags_count, dim3(nseg), dim3(kSelThreads), 0, s, p,
+                     (const uint8_t *)p.cflag);
+  hipLaunchKernelGGL(k_pf_flags_list, dim3(nseg), dim3(kSelThreads), 0, s, p, p.cflag, p.cand,
+                     (int)ECHO_PF_CNT_CAND);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_early(const StepArgs &a, const PrefillArgs &p, hipStream_t s) {
+  const int nseg = (p.N + kPfSeg - 1) / kPfSeg;
+  hipLaunchKernelGGL(k_pf_inst_count, dim3(nseg), dim3(kSelThreads), 0, s, a, p,
+                     (const int32_t *)p.cand, (int)ECHO_PF_CNT_CAND);
+  hipLaunchKernelGGL(k_pf_inst_write, dim3(nseg), dim3(kSelThreads), 0, s, a, p,
+                     (const int32_t *)p.cand, (int)ECHO_PF_CNT_CAND, 0, p.pf_h, p.pf_g);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_exact(const StepArgs &a, const PrefillArgs &p, hipStream_t s) {
+  const int nseg = (p.N + kPfSeg - 1) / kPfSeg;
+  hipLaunchKernelGGL(k_pf_exact, dim3(p.C), dim3(kSelThreads), 0, s, a, p);
+  hipLaunchKernelGGL(k_pf_flags_count, dim3(nseg), dim3(kSelThreads), 0, s, p,
+                     (const uint8_t *)p.uflag);
+  hipLaunchKernelGGL(k_pf_flags_list, dim3(nseg), dim3(kSelThreads), 0, s, p, p.uflag, p.uni,
+                     (int)ECHO_PF_CNT_UNION);
+  hipLaunchKernelGGL(k_pf_inst_count, dim3(nseg), dim3(kSelThreads), 0, s, a, p,
+                     (const int32_t *)p.uni, (int)ECHO_PF_CNT_UNION);
+  hipLaunchKernelGGL(k_pf_inst_write, dim3(nseg), dim3(kSelThreads), 0, s, a, p,
+                     (const int32_t *)p.uni, (int)ECHO_PF_CNT_UNION, 1, p.miss_h, p.miss_g);
+  hipLaunchKernelGGL(k_pf_finish, dim3(1), dim3(kListThreads), 0, s, a, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_copy(const StepArgs &a, const PrefillArgs &p, int list, hipStream_t s) {
+  if (list == 0)
+    hipLaunchKernelGGL(k_pf_copy, dim3(kPfCopyBlocks), dim3(256), 0, s, a, p,
+                       (const int32_t *)p.pf_h, (const int32_t *)p.pf_g, (int)ECHO_PF_CNT_EARLY);
+  else
+    hipLaunchKernelGGL(k_pf_copy, dim3(kPfCopyBlocks), dim3(256), 0, s, a, p,
+                       (const int32_t *)p.miss_h, (const int32_t *)p.miss_g,
+                       (int)ECHO_PF_CNT_LATE);
+  return hipGetLastError();
+}
+
+}  // namespace echo

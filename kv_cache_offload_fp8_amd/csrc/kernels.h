@@ -41,6 +41,59 @@ struct StepArgs {
   Scratch sc;
 };
 
+// One chunked-prefill call: the chunk (host values and device inputs), the
+// prefill workspace, and the scoring grid.
+struct PrefillArgs {
+  int32_t C, N, hb;            // queries, history tokens, first host id of the history
+  const uint16_t *q;           // [C][H][D] bf16
+  const float *w;              // [C][H]
+  const float *pred;           // [C] or null
+  float *scores;               // [max_chunk][N] (row stride N)
+  int32_t *sel, *n_sel;        // [max_chunk][K], [max_chunk]
+  float *kth;                  // [max_chunk]
+  int32_t *beta, *n_qcand;     // [max_chunk]
+  int32_t *cand, *uni;         // [max_ctx]
+  int32_t *pf_h, *pf_g, *miss_h, *miss_g;  // [max_ctx]
+  int32_t *counts, *status;
+  uint8_t *qhi, *qlo;          // [max_chunk][kHeadsPad][kDimPad]
+  float *wsc;                  // [max_chunk][kHeadsPad]
+  uint8_t *cflag, *uflag;      // [max_ctx rounded up to kPfSeg]
+  int32_t *seg;                // [max_ctx / kPfSeg + 1]
+  int32_t qblocks, tsplits;    // scoring grid: query blocks x token splits
+};
+constexpr int kPfSeg = 4096;   // list entries per workgroup of the ordered passes
+
+hipError_t launch_prefill_score(const StepArgs &a, const PrefillArgs &p, hipStream_t s);
+hipError_t launch_prefill_early(const StepArgs &a, const PrefillArgs &p, hipStream_t s);
+hipError_t launch_prefill_exact(const StepArgs &a, const PrefillArgs &p, hipStream_t s);
+hipError_t launch_prefill_copy(const StepArgs &a, const PrefillArgs &p, int list, hipStream_t s);
+
+// The ascending free list (idxbuf[0 .. nfree)) rebuilt from the free flags by one
+// workgroup of kListThreads threads (16 flags per thread per round, block scan).
+// `sh` needs kListThreads / 64 + 1 ints of shared memory.
+constexpr int kListThreads = 1024;
+constexpr int kListSlots = 16;
+__device__ inline void rebuild_free_list(const StepArgs &a, int *sh) {
+  const int tid = threadIdx.x;
+  int off = 0;
+  for (int64_t g0 = 0; g0 < a.n_gpu; g0 += (int64_t)kListThreads * kListSlots) {
+    const int64_t gs = g0 + (int64_t)tid * kListSlots;
+    uint32_t bits = 0;  // bit i: slot gs + i is free
+#pragma unroll
+    for (int i = 0; i < kListSlots; ++i)
+      if (gs + i < a.n_gpu && a.freef[gs + i]) bits |= 1u << i;
+    int total;
+    int r = off + block_excl_scan<kListThreads>(__popc(bits), sh, &total);
+    while (bits) {
+      const int i = __ffs(bits) - 1;
+      a.idxbuf[r++] = (int32_t)(gs + i);
+      bits &= bits - 1;
+    }
+    off += total;
+  }
+  if (tid == 0) a.ctl[ECHO_CTL_NFREE] = off;
+}
+
 // begin-kernel roles
 enum {
   BEGIN_REQ = 1,         // request table, scoring jobs, reserve
@@ -73,6 +126,7 @@ hipError_t launch_recall(const StepArgs &a, hipStream_t s);
 hipError_t launch_step_advance(const StepArgs &a, hipStream_t s);
 hipError_t launch_meta_init(const StepArgs &a, hipStream_t s);
 hipError_t launch_ws_reset(const echo_ws_t &ws, hipStream_t s);
+hipError_t launch_fill_zero(uint32_t *p, int64_t n_words, hipStream_t s);
 hipError_t launch_kindex_pack(const uint8_t *rows, uint8_t *tiled, int64_t n_rows, int D,
                               hipStream_t s);
 

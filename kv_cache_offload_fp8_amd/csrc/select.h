@@ -45,10 +45,10 @@ __device__ inline void find_boundary(const uint32_t *hist, int need, int *s_bin,
 }
 
 // MSD radix select of the `need` smallest composites x = (key << 32) | idx among
-// `c` candidates (keys and indices in global memory, unique composites).  On
-// return, candidate x is selected iff (x >> *pos) <= *P.
-__device__ inline void block_select(const uint32_t *ckey, const int32_t *cidx, int c, int need,
-                                    uint64_t *P_out, int *pos_out) {
+// `c` candidates, candidate i being get(i) (unique composites).  On return,
+// candidate x is selected iff (x >> *pos) <= *P.
+template <class Get>
+__device__ inline void block_select_by(Get get, int c, int need, uint64_t *P_out, int *pos_out) {
   __shared__ uint32_t s_hist[2048];
   __shared__ int sh[kSelThreads / kWave + 1];
   __shared__ uint64_t shu[kSelThreads / kWave];
@@ -61,7 +61,7 @@ __device__ inline void block_select(const uint32_t *ckey, const int32_t *cidx, i
   }
   uint64_t mn = ~0ull, mx = 0;
   for (int i = tid; i < c; i += kSelThreads) {
-    const uint64_t x = ((uint64_t)ckey[i] << 32) | (uint32_t)cidx[i];
+    const uint64_t x = get(i);
     mn = x < mn ? x : mn;
     mx = x > mx ? x : mx;
   }
@@ -78,7 +78,7 @@ __device__ inline void block_select(const uint32_t *ckey, const int32_t *cidx, i
     for (int i = tid; i < 2048; i += kSelThreads) s_hist[i] = 0;
     __syncthreads();
     for (int i = tid; i < c; i += kSelThreads) {
-      const uint64_t x = ((uint64_t)ckey[i] << 32) | (uint32_t)cidx[i];
+      const uint64_t x = get(i);
       if ((pos >= 64 ? 0 : (x >> pos)) == P)
         atomicAdd(&s_hist[(x >> npos) & (uint64_t)(nb - 1)], 1u);
     }
@@ -106,6 +106,13 @@ __device__ inline void block_select(const uint32_t *ckey, const int32_t *cidx, i
   }
   *P_out = P;
   *pos_out = pos;
+}
+
+// The same over keys and indices in global memory.
+__device__ inline void block_select(const uint32_t *ckey, const int32_t *cidx, int c, int need,
+                                    uint64_t *P_out, int *pos_out) {
+  block_select_by([=](int i) { return ((uint64_t)ckey[i] << 32) | (uint32_t)cidx[i]; }, c, need,
+                  P_out, pos_out);
 }
 
 __device__ inline bool composite_selected(uint32_t key, int32_t idx, uint64_t P, int pos) {

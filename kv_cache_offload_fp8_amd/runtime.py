@@ -148,6 +148,45 @@ class Workspace:
         return o
 
 
+class PrefillWorkspace:
+    """One device buffer carved by echo_prefill_ws_bind, with typed views."""
+
+    def __init__(self, dims: abi.echo_dims_t, max_chunk: int, device="cuda"):
+        self.dims = dims
+        n = abi.echo_prefill_ws_bytes(dims, max_chunk)
+        if n == 0:
+            raise ValueError("invalid dims or chunk size for the prefill workspace")
+        self.buf = torch.zeros(n, dtype=torch.uint8, device=device)
+        self.ws = abi.echo_prefill_ws_t()
+        check(abi.echo_prefill_ws_bind(dims, max_chunk, _ptr(self.buf), n, self.ws),
+              "echo_prefill_ws_bind")
+        base = _ptr(self.buf)
+        Cq, Nx, K = max_chunk, dims.max_ctx, dims.top_k
+
+        def view(field, dtype, count):
+            off = getattr(self.ws, field) - base
+            itemsize = torch.empty((), dtype=dtype).element_size()
+            return self.buf[off:off + count * itemsize].view(dtype)
+
+        self.scores_flat = view("scores", torch.float32, Cq * Nx)
+        self.sel = view("sel", torch.int32, Cq * K).view(Cq, K)
+        for name, dt in (("n_sel", torch.int32), ("kth", torch.float32), ("beta", torch.int32),
+                         ("n_qcand", torch.int32)):
+            setattr(self, name, view(name, dt, Cq))
+        for name in ("cand", "uni", "pf_h", "pf_g", "miss_h", "miss_g"):
+            setattr(self, name, view(name, torch.int32, Nx))
+        self.counts = view("counts", torch.int32, abi.ECHO_PF_NCOUNTS)
+        self.status = view("status", torch.int32, 1)
+        self.reset()
+
+    def reset(self):
+        check(abi.echo_prefill_ws_reset(self.dims, self.ws, stream_handle()),
+              "echo_prefill_ws_reset")
+
+    def scores(self, C: int, N: int) -> torch.Tensor:
+        return self.scores_flat[: C * N].view(C, N)
+
+
 class Batch:
     def __init__(self, host_base, ctx, device="cuda"):
         self.host_base = torch.as_tensor(np.asarray(host_base, np.int32), device=device)

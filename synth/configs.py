@@ -62,7 +62,14 @@ WORKLOADS = {
     # batch 16 x 100K, rho 0.5 for low locality, 200K GPU slots, 2M host tokens
     "low_locality": Workload("low_locality", 4, 16, 100_000, 100_000, 1, 64, 128, 2048,
                              200_000, 2_000_000, 0.5, 32),
+    # chunked prefill: one request, 100K history, 64x128, k=2048 per query, 200K GPU slots,
+    # 2M host tokens; rho is the AR(1) coefficient along prompt positions, steps the chunks
+    "prefill": Workload("prefill", 5, 1, 100_000, 100_000, 1, 64, 128, 2048, 200_000,
+                        2_000_000, 0.98, 4),
 }
+
+# query-chunk sizes of the prefill workload
+PREFILL_CHUNKS = (256, 512)
 
 
 def get(name: str) -> Workload:

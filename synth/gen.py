@@ -10,6 +10,9 @@ Recipe (seed 0 unless stated; every tensor has its own substream, keyed by
                     state kept in fp32, emitted as bf16 at every step;
   * host layout   request b owns host ids host_base[b] .. host_base[b]+ctx[b]-1,
                     host_base[b] = sum of the earlier contexts.
+  * prefill       one request's history as above; the chunk queries follow the
+                    AR(1) recipe along the prompt positions, head weights
+                    U[0, 1) per position.
 Generation runs with torch on the requested device: the same seed gives the same
 tensor on the same device type (CPU and GPU streams differ from each other).
 """
@@ -22,7 +25,7 @@ import torch
 
 from .configs import Workload
 
-T_K, T_LAT, T_W, T_Q0, T_QN, T_APPEND = 1, 2, 3, 4, 5, 6
+T_K, T_LAT, T_W, T_Q0, T_QN, T_APPEND, T_PQ, T_PW = 1, 2, 3, 4, 5, 6, 7, 8
 
 
 def seed_for(wl: Workload, seed: int, *key: int) -> int:
@@ -107,6 +110,27 @@ def gen_q(wl: Workload, layer: int, batch: int, steps: int, device, seed=0) -> t
                 st = wl.rho * st + c * eps
             out[t, b] = st.to(torch.bfloat16)
     return out
+
+
+def gen_prefill_qw(wl: Workload, layer: int, chunk: int, chunks: int, device, seed=0):
+    """Prefill queries and weights for ``chunks`` chunks of ``chunk`` prompt positions:
+    bf16 q [chunks, C, H, D] following the AR(1) recipe along the prompt positions
+    (coefficient wl.rho) and fp32 w [chunks, C, H] ~ U[0, 1) per position."""
+    n = chunk * chunks
+    gq = _gen(device, seed_for(wl, seed, layer, 0, T_PQ))
+    gw = _gen(device, seed_for(wl, seed, layer, 0, T_PW))
+    c = float(np.sqrt(max(0.0, 1.0 - wl.rho * wl.rho)))
+    eps = torch.randn((n, wl.heads, wl.head_dim), generator=gq, device=device,
+                      dtype=torch.float32)
+    q = torch.empty((n, wl.heads, wl.head_dim), dtype=torch.bfloat16, device=device)
+    st = eps[0]
+    q[0] = st.to(torch.bfloat16)
+    for i in range(1, n):
+        st = wl.rho * st + c * eps[i]
+        q[i] = st.to(torch.bfloat16)
+    w = torch.rand((n, wl.heads), generator=gw, device=device, dtype=torch.float32)
+    return (q.view(chunks, chunk, wl.heads, wl.head_dim),
+            w.view(chunks, chunk, wl.heads))
 
 
 @dataclass

@@ -15,7 +15,7 @@ from kv_cache_offload_fp8_amd import abi
 from kv_cache_offload_fp8_amd import runtime as R
 from oracle import oracle as O
 from synth import make_inputs
-from synth.gen import gen_append
+from synth.gen import gen_append, gen_prefill_qw
 
 MODE_EMA, MODE_NEG_INF, MODE_POS_INF = abi.ECHO_THETA_EMA, abi.ECHO_THETA_NEG_INF, \
     abi.ECHO_THETA_POS_INF
@@ -265,6 +265,121 @@ class Rig:
             sel = int(out["n_sel"].sum())
             hr.append(1.0 - int(out["n_miss"].sum()) / sel if sel else 1.0)
         return hr
+
+    def close(self):
+        torch.cuda.synchronize()
+        self.host.close()
+
+
+class PrefillRig:
+    """One request's history of N tokens (host ids 0 .. N-1) on a fresh layer, chunks of C
+    prefill queries run through echo_prefill_score / _copy / _select and compared with
+    the oracle's prefill chunk, which is fed the GPU's scores."""
+
+    def __init__(self, wl, N, C, chunks, n_gpu=None, n_host=None, top_k=None, seed=0,
+                 layer=0, device="cuda", use_pred=True):
+        wl = wl.scaled(n_gpu=n_gpu or wl.n_gpu, n_host=n_host or wl.n_host,
+                       top_k=top_k or wl.top_k)
+        self.wl, self.N, self.C, self.chunks, self.use_pred = wl, N, C, chunks, use_pred
+        self.inp = make_inputs(wl, layer=layer, device="cpu", seed=seed, steps=1, ctx=[N])
+        self.hb = int(self.inp.host_base[0])
+        self.dims = R.make_dims(wl.heads, wl.head_dim, wl.top_k, wl.n_host, wl.n_gpu, 1, N,
+                                wl.latent, wl.alpha, wl.cap_div, 1)
+        self.host = R.HostPool(wl.n_host, wl.latent)
+        self.host.np[:] = self.inp.np_latents()
+        self.kidx = R.pack_kidx(self.dims, self.inp.kidx.to(device))
+        self.layer = R.Layer(self.dims, self.kidx, self.host, 1, device)
+        self.layer.init()
+        self.pws = R.PrefillWorkspace(self.dims, C, device)
+        q, w = gen_prefill_qw(wl, layer, C, chunks, "cpu", seed)
+        self.q_np = q.view(torch.int16).numpy().view(np.uint16)
+        self.w_np = w.numpy()
+        self.q_dev, self.w_dev = q.to(device), w.to(device)
+        self.np_kidx = self.inp.np_kidx()
+        self.orc_host = self.host.np.copy()
+        self.orc = O.OracleLayer(wl.heads, wl.head_dim, wl.top_k, wl.latent, wl.n_host, wl.n_gpu,
+                                 1)
+        self.pred = None  # the oracle's view of the prediction the GPU used
+        self.c = 0
+
+    def chunk(self, c):
+        pred = self.pws.kth.data_ptr() if (self.use_pred and c > 0) else None
+        return abi.echo_prefill_chunk_t(self.C, self.hb, self.N, self.q_dev[c].data_ptr(),
+                                        self.w_dev[c].data_ptr(), pred)
+
+    def gpu_chunk(self, c):
+        st = R.stream_handle()
+        ch = self.chunk(c)
+        R.check(abi.echo_prefill_score(self.dims, self.layer.struct, ch, self.pws.ws, st),
+                "echo_prefill_score")
+        R.check(abi.echo_prefill_early(self.dims, self.layer.struct, ch, self.pws.ws, st),
+                "echo_prefill_early")
+        R.check(abi.echo_prefill_copy(self.dims, self.layer.struct, self.pws.ws, 0, st),
+                "echo_prefill_copy")
+        R.check(abi.echo_prefill_select(self.dims, self.layer.struct, ch, self.pws.ws, st),
+                "echo_prefill_select")
+        R.check(abi.echo_prefill_copy(self.dims, self.layer.struct, self.pws.ws, 1, st),
+                "echo_prefill_copy")
+
+    def step_and_compare(self, check_rows=None, expect_status=0, fail_stage=None):
+        """One chunk on both sides.  check_rows: the query rows whose scores are checked
+        against the oracle's own (None: all).  fail_stage: "early" or "late" when a
+        capacity error is expected in that stage."""
+        c = self.c
+        C, N, k = self.C, self.N, self.wl.top_k
+        pred_used = self.pws.kth[:C].cpu().numpy().copy() if (self.use_pred and c > 0) \
+            else None
+        self.gpu_chunk(c)
+        torch.cuda.current_stream().synchronize()
+        P = self.pws
+        status = int(P.status.item())
+        sc = P.scores(C, N).cpu().numpy()
+        rows = range(C) if check_rows is None else check_rows
+        for i in rows:
+            assert_scores_close(sc[i], self.q_np[c, i], self.w_np[c, i],
+                                self.np_kidx[self.hb:self.hb + N], f"chunk {c} query {i}")
+        o = O.prefill_chunk(self.orc, self.hb, N, self.q_np[c], self.w_np[c], self.np_kidx,
+                            pred=pred_used, host_kv=self.orc_host, ext_scores=sc)
+        tag = f"chunk {c}"
+        assert status == o["status"] == expect_status, (tag, "status", status, o["status"])
+        cnt = P.counts.cpu().numpy()
+        assert np.array_equal(P.beta[:C].cpu().numpy(), o["beta"]), (tag, "beta")
+        assert np.array_equal(P.n_qcand[:C].cpu().numpy(), o["n_qcand"]), (tag, "n_qcand")
+        assert cnt[abi.ECHO_PF_CNT_CAND] == o["cand"].size, (tag, "n_cand")
+        assert np.array_equal(P.cand[: o["cand"].size].cpu().numpy(), o["cand"]), (tag, "cand")
+        if status == 0 or fail_stage == "late":
+            n_pf = o["pf_h"].size
+            assert cnt[abi.ECHO_PF_CNT_EARLY] == n_pf, (tag, "n_early")
+            assert np.array_equal(P.pf_h[:n_pf].cpu().numpy(), o["pf_h"]), (tag, "pf_h")
+            assert np.array_equal(P.pf_g[:n_pf].cpu().numpy(), o["pf_g"]), (tag, "pf_g")
+        if status == 0:
+            assert np.array_equal(P.n_sel[:C].cpu().numpy(), o["n_sel"]), (tag, "n_sel")
+            gsel = P.sel[:C].cpu().numpy()
+            for i in range(C):
+                n = int(o["n_sel"][i])
+                assert np.array_equal(gsel[i, :n], o["sel"][i, :n]), (tag, "sel", i)
+            assert np.array_equal(P.kth[:C].cpu().numpy().view(np.uint32),
+                                  o["kth"].view(np.uint32)), (tag, "kth")
+            assert cnt[abi.ECHO_PF_CNT_UNION] == o["uni"].size, (tag, "n_union")
+            assert np.array_equal(P.uni[: o["uni"].size].cpu().numpy(), o["uni"]), (tag, "uni")
+            nm = o["miss_h"].size
+            assert cnt[abi.ECHO_PF_CNT_LATE] == nm, (tag, "n_late")
+            assert np.array_equal(P.miss_h[:nm].cpu().numpy(), o["miss_h"]), (tag, "miss_h")
+            assert np.array_equal(P.miss_g[:nm].cpu().numpy(), o["miss_g"]), (tag, "miss_g")
+        st = self.layer.state()
+        for name in ("h2g", "g2h", "prio", "free"):
+            assert np.array_equal(st[name], getattr(self.orc, name)), (tag, name)
+        assert st["t"] == self.orc.t, (tag, "t", st["t"], self.orc.t)
+        if status == 0:
+            nfree = int(self.orc.free.sum())
+            assert st["nfree"] == nfree, (tag, "nfree")
+            assert np.array_equal(st["idxbuf"][:nfree], np.nonzero(self.orc.free)[0]), \
+                (tag, "idxbuf")
+        gp = self.layer.gpu_kv.cpu().numpy().view(np.uint16)
+        assert np.array_equal(gp, self.orc.pool), (tag, "pool bytes")
+        if status == 0:
+            self.c += 1
+        return o, dict(status=status, counts=cnt)
 
     def close(self):
         torch.cuda.synchronize()

@@ -1,0 +1,101 @@
+"""Chunked-prefill selection (echo_prefill_score / _copy / _select) against the oracle,
+through the C ABI.
+
+Each chunk of queries is scored against one request's history on the GPU; the
+scores are checked against the oracle's own (|rel| <= 2e-3 plus the cancellation
+allowance), and the oracle, fed the GPU's scores, must then agree bit for bit on
+everything decided from them: each query's boundary bucket and candidate count,
+the union of candidates, each query's exact top-k and k-th score, the union of
+selections, both install lists (host ids and slots), the maps, priorities, free
+flags, free list, step counter and the GPU-pool bytes.  Later chunks pass the
+previous chunk's k-th scores as the prediction, as the benchmark does.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from synth import get
+
+from . import echo_harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _run(rig, chunks, check_rows=None):
+    for _ in range(chunks):
+        o, g = rig.step_and_compare(check_rows=check_rows)
+        _say(f"  chunk {rig.c - 1}: union {o['uni'].size}, candidates {o['cand'].size}, "
+             f"early {o['pf_h'].size}, late {o['miss_h'].size}, "
+             f"beta {np.unique(o['beta'])[:6]}")
+    return o
+
+
+@pytest.mark.parametrize("use_pred", [False, True])
+def test_prefill_64x128_ragged(use_pred):
+    # 40 queries (not a multiple of 16), a 3000-token history (not a multiple of 64)
+    _say(f"prefill 64x128: N 3000, C 40, k 256, pred {use_pred}")
+    wl = get("prefill").scaled(rho=0.9)
+    rig = H.PrefillRig(wl, N=3000, C=40, chunks=3, n_gpu=4000, n_host=4096, top_k=256,
+                       use_pred=use_pred)
+    _run(rig, 3)
+    rig.close()
+
+
+def test_prefill_4x32_small_heads():
+    _say("prefill 4x32: N 1000, C 20, k 64")
+    wl = get("tiny").scaled(rho=0.8)
+    rig = H.PrefillRig(wl, N=1000, C=20, chunks=3, n_gpu=1500, n_host=1024, top_k=64)
+    _run(rig, 3)
+    rig.close()
+
+
+def test_prefill_history_not_longer_than_k():
+    _say("prefill: N 200 <= k 256")
+    wl = get("prefill").scaled(rho=0.9)
+    rig = H.PrefillRig(wl, N=200, C=17, chunks=2, n_gpu=512, n_host=1024, top_k=256)
+    o = _run(rig, 2)
+    assert (o["beta"] == -1).all() and o["uni"].size == 200
+    rig.close()
+
+
+def test_prefill_capacity_errors():
+    wl = get("prefill").scaled(rho=0.9)
+    # probe the sizes with a roomy pool
+    probe = H.PrefillRig(wl, N=2000, C=24, chunks=1, n_gpu=3000, n_host=2048, top_k=128)
+    o, _ = probe.step_and_compare()
+    n_c, n_u = o["cand"].size, o["uni"].size
+    probe.close()
+    _say(f"prefill capacity: candidates {n_c}, union {n_u}")
+    assert 0 < n_c < n_u
+    # room for fewer than the candidates: nothing installed
+    rig = H.PrefillRig(wl, N=2000, C=24, chunks=1, n_gpu=n_c - 1, n_host=2048, top_k=128)
+    rig.step_and_compare(expect_status=O.ECAPACITY, fail_stage="early")
+    rig.close()
+    # room for the candidates only: they stay, the step counter does not move
+    rig = H.PrefillRig(wl, N=2000, C=24, chunks=1, n_gpu=n_u - 1, n_host=2048, top_k=128)
+    rig.step_and_compare(expect_status=O.ECAPACITY, fail_stage="late")
+    rig.close()
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("C", [256, 512])
+def test_prefill_full_size(C):
+    # 100K history, 64x128, k = 2048, 200K slots, 2M host tokens; scores of four
+    # query rows are checked against the oracle's own, everything else bit for bit
+    _say(f"prefill full size: N 100,000, C {C}, 2 chunks")
+    rig = H.PrefillRig(get("prefill"), N=100_000, C=C, chunks=2)
+    _run(rig, 2, check_rows=[0, 1, C // 2, C - 1])
+    rig.close()
