@@ -61,6 +61,8 @@ def parse():
     p.add_argument("--no-prefill", action="store_true",
                    help="skip the chunked-prefill measurement")
     p.add_argument("--prefill-chunks", type=int, default=4)
+    p.add_argument("--prefill-only", action="store_true",
+                   help="run only the chunked-prefill measurement and print its JSON object")
     p.add_argument("--pmc-calibrate", action="store_true",
                    help="end with a 256 MiB device-to-device copy whose FETCH_SIZE / WRITE_SIZE "
                         "counters scale the indexer's")
@@ -115,6 +117,9 @@ def main():
 
     torch.cuda.set_device(0)
     dev = "cuda"
+    if args.prefill_only:
+        print(json.dumps({"prefill": prefill_measure(args, dev)}), flush=True)
+        return
     wl = get(args.workload)
     if args.cap_div:
         wl = wl.scaled(cap_div=args.cap_div)

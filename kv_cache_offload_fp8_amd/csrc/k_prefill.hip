@@ -26,7 +26,8 @@
 //   k_pf_exact    per query: exact top-k by (score desc, token asc), written in
 //                 ascending token order, and its k-th score
 //   k_pf_copy     host rows of an install list into the GPU pool
-//   k_pf_finish   step counter and the rebuilt free list
+//   k_pf_shift_*  the unused rest of the free list moved to its front, the step
+//                 counter
 // The early install and its copy run right after the coarse pass, so the copy
 // (on its own stream) overlaps the exact selection and the next chunk's scoring.
 #include "kernels.h"
@@ -38,9 +39,6 @@ typedef int v8i_pf __attribute__((ext_vector_type(8)));
 typedef float v4f_pf __attribute__((ext_vector_type(4)));
 typedef int v4i_pf __attribute__((ext_vector_type(4)));
 
-constexpr int kPfWaves = 8;        // waves per scoring workgroup
-constexpr int kPfQ = 2;            // queries per wave
-constexpr int kPfQBlock = kPfWaves * kPfQ;
 constexpr int kPfCopyBlocks = 32;  // a small grid keeps about 256 KB of host reads in flight
 
 // The status as one workgroup sees it: read once and shared, so that all of its
@@ -370,35 +368,83 @@ __global__ __launch_bounds__(kSelThreads) void k_pf_inst_write(StepArgs a, Prefi
 }
 
 // ------------------------------------------------------------------ exact
+// Query i's top-k: the tokens above the boundary bucket (n_qcand[i] < k of them,
+// all certain) and the k - n_qcand[i] best of the boundary bucket by (score desc,
+// token asc) -- the bucket of a rounded difference never decreases as the score
+// grows, so the order of the whole row is bucket by bucket.  The boundary
+// bucket's (key, token) composites are gathered in LDS (one atomic per wave) and
+// selected there; a bucket too large for LDS falls back to the radix select over
+// the whole row.  pred[i] is read before kth[i] is written (the caller may pass
+// this workspace's kth as pred).
+constexpr int kPfBoundaryCap = 6144;
+
 __global__ __launch_bounds__(kSelThreads) void k_pf_exact(StepArgs a, PrefillArgs p) {
   __shared__ int sh[kSelThreads / kWave + 1];
   __shared__ uint64_t shu[kSelThreads / kWave];
+  __shared__ uint64_t s_list[kPfBoundaryCap];
+  __shared__ int s_n;
   if (block_failed(p.status)) return;
-  const int i = blockIdx.x, tid = threadIdx.x;
+  const int i = blockIdx.x, tid = threadIdx.x, lane = lane_id();
   const float *row = p.scores + (int64_t)i * p.N;
-  uint64_t P;
-  int pos;
-  block_select_by([=](int s) { return ((uint64_t)topk_key(row[s]) << 32) | (uint32_t)s; }, p.N,
-                  a.K, &P, &pos);
+  const float pr = p.pred ? p.pred[i] : 0.0f;
+  const int beta = p.beta[i];
+  const int above = p.n_qcand[i];
+  uint64_t P = ~0ull;
+  int pos = 0;
+  bool in_lds = false;
+  if (beta >= 0) {
+    if (tid == 0) s_n = 0;
+    __syncthreads();
+    for (int s0 = 0; s0 < p.N; s0 += kSelThreads) {
+      const int s = s0 + tid;
+      const float v = s < p.N ? row[s] : 0.0f;
+      const bool m = s < p.N && pf_bucket(v, pr) == beta;
+      const uint64_t bal = __ballot(m);
+      int b0 = 0;
+      if (lane == 0 && bal) b0 = atomicAdd(&s_n, __popcll(bal));
+      b0 = __shfl(b0, 0);
+      const int idx = b0 + __popcll(bal & lanemask_lt());
+      if (m && idx < kPfBoundaryCap) s_list[idx] = ((uint64_t)topk_key(v) << 32) | (uint32_t)s;
+    }
+    __syncthreads();
+    const int n = s_n;
+    in_lds = n <= kPfBoundaryCap;
+    if (in_lds)
+      block_select_by([&](int j) { return s_list[j]; }, n, a.K - above, &P, &pos);
+    else
+      block_select_by([=](int s) { return ((uint64_t)topk_key(row[s]) << 32) | (uint32_t)s; },
+                      p.N, a.K, &P, &pos);
+  }
   int32_t *out = p.sel + (int64_t)i * a.K;
   int written = 0;
   uint64_t worst = 0;  // the largest selected composite: the k-th in selection order
   for (int base = 0; base < p.N; base += kPfSeg) {
     uint32_t keys[4];
+    bool in[4];
     int cnt = 0;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int s = base + tid * 4 + v;
-      keys[v] = s < p.N ? topk_key(row[s]) : 0xFFFFFFFFu;
-      const bool in = s < p.N && composite_selected(keys[v], s, P, pos);
-      cnt += in ? 1 : 0;
+      const float x = s < p.N ? row[s] : 0.0f;
+      keys[v] = topk_key(x);
+      bool sel = s < p.N;
+      if (sel && beta >= 0) {
+        if (in_lds) {
+          const int b = pf_bucket(x, pr);
+          sel = b > beta || (b == beta && composite_selected(keys[v], s, P, pos));
+        } else {
+          sel = composite_selected(keys[v], s, P, pos);
+        }
+      }
+      in[v] = sel;
+      cnt += sel ? 1 : 0;
     }
     int tot;
     int r = written + block_excl_scan<kSelThreads>(cnt, sh, &tot);
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int s = base + tid * 4 + v;
-      if (s < p.N && composite_selected(keys[v], s, P, pos)) {
+      if (in[v]) {
+        const int s = base + tid * 4 + v;
         out[r++] = s;
         p.uflag[s] = 1;
         const uint64_t x = ((uint64_t)keys[v] << 32) | (uint32_t)s;
@@ -442,11 +488,30 @@ __global__ __launch_bounds__(256) void k_pf_copy(StepArgs a, PrefillArgs p, cons
 }
 
 // ------------------------------------------------------------------ finish
-__global__ __launch_bounds__(kListThreads) void k_pf_finish(StepArgs a, PrefillArgs p) {
-  __shared__ int sh[kListThreads / kWave + 1];
-  if (block_failed(p.status)) return;
-  rebuild_free_list(a, sh);
-  if (threadIdx.x == 0) a.ctl[ECHO_CTL_STEP] += 1;
+// The installs took idxbuf[0 .. used) in order, so the free slots left are the
+// rest of the list, still ascending: move it to the front (through a buffer, in
+// two launches, so that no workgroup reads what another has overwritten), then
+// the free-list length and the step counter.
+constexpr int kPfShiftBlocks = 256;
+
+__global__ __launch_bounds__(256) void k_pf_shift_out(StepArgs a, PrefillArgs p) {
+  if (failed(p.status)) return;
+  const int used = p.counts[ECHO_PF_CNT_EARLY] + p.counts[ECHO_PF_CNT_LATE];
+  const int left = a.ctl[ECHO_CTL_NFREE] - used;
+  for (int j = blockIdx.x * 256 + threadIdx.x; j < left; j += kPfShiftBlocks * 256)
+    p.tmp[j] = a.idxbuf[used + j];
+  if (blockIdx.x == 0 && threadIdx.x == 0) p.counts[ECHO_PF_CNT_LEFT] = left;
+}
+
+__global__ __launch_bounds__(256) void k_pf_shift_in(StepArgs a, PrefillArgs p) {
+  if (failed(p.status)) return;
+  const int left = p.counts[ECHO_PF_CNT_LEFT];
+  for (int j = blockIdx.x * 256 + threadIdx.x; j < left; j += kPfShiftBlocks * 256)
+    a.idxbuf[j] = p.tmp[j];
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    a.ctl[ECHO_CTL_NFREE] = left;
+    a.ctl[ECHO_CTL_STEP] += 1;
+  }
 }
 
 // ------------------------------------------------------------------ launchers
@@ -483,7 +548,8 @@ hipError_t launch_prefill_exact(const StepArgs &a, const PrefillArgs &p, hipStre
                      (const int32_t *)p.uni, (int)ECHO_PF_CNT_UNION);
   hipLaunchKernelGGL(k_pf_inst_write, dim3(nseg), dim3(kSelThreads), 0, s, a, p,
                      (const int32_t *)p.uni, (int)ECHO_PF_CNT_UNION, 1, p.miss_h, p.miss_g);
-  hipLaunchKernelGGL(k_pf_finish, dim3(1), dim3(kListThreads), 0, s, a, p);
+  hipLaunchKernelGGL(k_pf_shift_out, dim3(kPfShiftBlocks), dim3(256), 0, s, a, p);
+  hipLaunchKernelGGL(k_pf_shift_in, dim3(kPfShiftBlocks), dim3(256), 0, s, a, p);
   return hipGetLastError();
 }
 

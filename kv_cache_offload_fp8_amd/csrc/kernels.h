@@ -59,9 +59,14 @@ struct PrefillArgs {
   float *wsc;                  // [max_chunk][kHeadsPad]
   uint8_t *cflag, *uflag;      // [max_ctx rounded up to kPfSeg]
   int32_t *seg;                // [max_ctx / kPfSeg + 1]
+  int32_t *tmp;                // [n_gpu] free-list buffer
   int32_t qblocks, tsplits;    // scoring grid: query blocks x token splits
 };
 constexpr int kPfSeg = 4096;   // list entries per workgroup of the ordered passes
+constexpr int ECHO_PF_CNT_LEFT = 5;  // internal count: free slots left after a chunk
+constexpr int kPfWaves = 8;    // waves per prefill scoring workgroup
+constexpr int kPfQ = 2;        // queries per prefill scoring wave
+constexpr int kPfQBlock = kPfWaves * kPfQ;  // queries per prefill scoring workgroup
 
 hipError_t launch_prefill_score(const StepArgs &a, const PrefillArgs &p, hipStream_t s);
 hipError_t launch_prefill_early(const StepArgs &a, const PrefillArgs &p, hipStream_t s);
