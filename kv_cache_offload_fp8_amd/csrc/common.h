@@ -390,29 +390,4 @@ __device__ inline int bin_shift(uint32_t kmin, uint32_t kmax) {
   return bits > 12 ? bits - 12 : 0;
 }
 
-// ------------------------------------------------------------ fp8 E4M3FN
-// Round-to-nearest-even encode of a finite float with |x| < 464 (the scaled
-// queries never need saturation).
-__device__ inline uint8_t e4m3_encode(float x) {
-  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
-  const float a = fabsf(x);
-  if (a == 0.0f) return (uint8_t)sign;
-  int E = (int)((__float_as_uint(a) >> 23) & 0xFF) - 127;
-  if (E < -6) {  // subnormal range: multiples of 2^-9 (m == 8 is the smallest normal)
-    const int m = (int)rintf(a * 512.0f);
-    return (uint8_t)(sign | (uint32_t)m);
-  }
-  int m = (int)rintf((ldexpf(a, -E) - 1.0f) * 8.0f);  // 0..8
-  if (m == 8) {
-    m = 0;
-    E += 1;
-  }
-  return (uint8_t)(sign | (uint32_t)((E + 7) << 3) | (uint32_t)m);
-}
-__device__ inline float e4m3_decode(uint8_t c) {
-  const int e = (c >> 3) & 0xF, m = c & 7;
-  const float v = e == 0 ? ldexpf((float)m, -9) : ldexpf(1.0f + m * 0.125f, e - 7);
-  return (c & 0x80) ? -v : v;
-}
-
 }  // namespace echo

@@ -83,14 +83,22 @@ __global__ __launch_bounds__(256) void k_pf_stage(StepArgs a, PrefillArgs p) {
     frexpf(amax, &E);
     e = min(64, max(-64, 8 - E));
   }
-  uint32_t whi[2] = {0, 0}, wlo[2] = {0, 0};
+  // the hardware conversion: round to nearest even, OCP E4M3FN (no value
+  // reaches the saturation range)
+  const float sc = ldexpf(1.0f, e);  // exact: |e| <= 64
+  uint32_t whi[2], wlo[2];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const float xs = ldexpf(x[k], e);
-    const uint8_t h8 = e4m3_encode(xs);
-    const uint8_t l8 = e4m3_encode(xs - e4m3_decode(h8));
-    whi[k >> 2] |= (uint32_t)h8 << (8 * (k & 3));
-    wlo[k >> 2] |= (uint32_t)l8 << (8 * (k & 3));
+  for (int k = 0; k < 2; ++k) {
+    const float x0 = x[4 * k] * sc, x1 = x[4 * k + 1] * sc;
+    const float x2 = x[4 * k + 2] * sc, x3 = x[4 * k + 3] * sc;
+    int h = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+    h = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, h, true);
+    int l = __builtin_amdgcn_cvt_pk_fp8_f32(x0 - __builtin_amdgcn_cvt_f32_fp8(h, 0),
+                                            x1 - __builtin_amdgcn_cvt_f32_fp8(h, 1), 0, false);
+    l = __builtin_amdgcn_cvt_pk_fp8_f32(x2 - __builtin_amdgcn_cvt_f32_fp8(h, 2),
+                                        x3 - __builtin_amdgcn_cvt_f32_fp8(h, 3), l, true);
+    whi[k] = (uint32_t)h;
+    wlo[k] = (uint32_t)l;
   }
   const int64_t o = ((int64_t)i * kHeadsPad + j) * kDimPad + d0;
   *(uint2 *)(p.qhi + o) = make_uint2(whi[0], whi[1]);
