@@ -69,14 +69,19 @@ def parse():
     return p.parse_args()
 
 
+# the sources the scoring kernel and its launch are built from
+SCORE_SOURCES = ("kv_cache_offload_fp8_amd/csrc/k_index.hip", "kv_cache_offload_fp8_amd/csrc/copy.h",
+                 "kv_cache_offload_fp8_amd/csrc/kernels.h", "kv_cache_offload_fp8_amd/csrc/common.h",
+                 "include/echo.h")
+
+
 def source_digest() -> str:
-    """sha1 over the HIP sources: the stored HBM-traffic figures hold only while it matches."""
-    import glob
+    """sha1 over the scoring kernel's sources: the stored HBM-traffic figures hold only
+    while it matches."""
     import hashlib
     h = hashlib.sha1()
-    for f in sorted(glob.glob(os.path.join(ROOT, "kv_cache_offload_fp8_amd", "csrc", "*"))):
-        if f.endswith((".hip", ".h")):
-            h.update(open(f, "rb").read())
+    for f in SCORE_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
     return h.hexdigest()
 
 

@@ -731,6 +731,35 @@ static void launch_score_hg(const StepArgs &a, int grid, hipStream_t s) {
   }
 }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n < 1)
+      n = 1;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+void index_grid(const echo_dims_t &d, bool with_copy, int *score_blocks, int *copy_blocks) {
+  const int cus = device_cus();
+  int gc = cus / 8 < kCopyBlocks ? cus / 8 : kCopyBlocks;
+  if (gc < 1) gc = 1;
+  if (!with_copy) gc = 0;  // prefetch off: every workgroup scores
+  const int64_t max_tiles =
+      (int64_t)d.max_batch * (((int64_t)d.max_ctx + kScoreTile - 1) / kScoreTile);
+  int64_t gs = (max_tiles + kScoreWaves - 1) / kScoreWaves;
+  if (gs > cus - gc) gs = cus - gc;
+  if (gs < 1) gs = 1;
+  *score_blocks = (int)gs;
+  *copy_blocks = gc;
+}
+
 hipError_t launch_score(const StepArgs &a, hipStream_t s) {
   const int grid = a.score_blocks + a.copy_waves / kScoreWaves;
   if (a.mode == ECHO_THETA_POS_INF)

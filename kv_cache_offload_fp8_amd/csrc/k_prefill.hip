@@ -30,7 +30,7 @@
 //                 counter
 // The early install and its copy run right after the coarse pass, so the copy
 // (on its own stream) overlaps the exact selection and the next chunk's scoring.
-#include "kernels.h"
+#include "prefill.h"
 #include "select.h"
 
 namespace echo {
