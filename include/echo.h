@@ -211,6 +211,19 @@ int echo_kindex_pack(const echo_dims_t *dims, const uint8_t *rows, uint8_t *tile
 
 /* ------------------------------------------------------ the hot path */
 
+/* The two halves of echo_indexer_prefetch, for callers that time or schedule
+ * them apart (same passages, same arguments): echo_indexer_begin enqueues the
+ * query prologue (request table, fp8 query split, cleared per-call state) and
+ * echo_indexer_score the scoring + prefetch kernel, which must follow it on the
+ * same stream with the same arguments and nothing between them that uses the
+ * workspace.  Errors: as echo_indexer_prefetch. */
+int echo_indexer_begin(const echo_dims_t *dims, const echo_layer_t *layer,
+                       const echo_batch_t *batch, const echo_ws_t *ws, int theta_mode,
+                       hipStream_t stream);
+int echo_indexer_score(const echo_dims_t *dims, const echo_layer_t *layer,
+                       const echo_batch_t *batch, const echo_ws_t *ws, int theta_mode,
+                       hipStream_t stream);
+
 /* Steps a0-a2: query prologue, lightning-indexer scoring
  * score[b,s] = sum_j w[b,j] * max(0, q[b,j,:] . K[host_base[b]+s,:]) for s < ctx_len[b]
  * (DeepSeek Sparse Attention's indexer, which the ECHO review's "Problem and

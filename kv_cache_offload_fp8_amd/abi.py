@@ -23,7 +23,7 @@ ECHO_CTL_STEP, ECHO_CTL_NFREE, ECHO_CTL_WORDS = 0, 1, 4
 EXPORTS = ("echo_meta_bytes", "echo_ws_bytes", "echo_ws_bind", "echo_meta_init",
            "echo_ws_reset", "echo_kindex_pack", "echo_indexer_prefetch", "echo_topk",
            "echo_cache_alloc_evict", "echo_recall", "echo_step_advance", "echo_layer_step",
-           "echo_append", "echo_gather", "echo_release", "echo_admit", "echo_prefill_ws_bytes",
+           "echo_indexer_begin", "echo_indexer_score", "echo_append", "echo_gather", "echo_release", "echo_admit", "echo_prefill_ws_bytes",
            "echo_prefill_ws_bind", "echo_prefill_ws_reset", "echo_prefill_score",
            "echo_prefill_early",
            "echo_prefill_select", "echo_prefill_copy", "echo_status_string")
@@ -94,6 +94,8 @@ def lib() -> C.CDLL:
             "echo_ws_reset": (C.c_int, [dp, wp, P]),
             "echo_kindex_pack": (C.c_int, [dp, P, P, C.c_int64, P]),
             "echo_indexer_prefetch": (C.c_int, [dp, lp, bp, wp, C.c_int, P]),
+            "echo_indexer_begin": (C.c_int, [dp, lp, bp, wp, C.c_int, P]),
+            "echo_indexer_score": (C.c_int, [dp, lp, bp, wp, C.c_int, P]),
             "echo_topk": (C.c_int, [dp, P, C.c_int64, bp, wp, P, P]),
             "echo_cache_alloc_evict": (C.c_int, [dp, lp, bp, wp, P]),
             "echo_recall": (C.c_int, [dp, lp, wp, P]),
@@ -156,6 +158,16 @@ def echo_kindex_pack(dims, rows: int, tiled: int, n_rows: int, stream: int) -> i
 def echo_indexer_prefetch(dims, layer, batch, ws, theta_mode: int, stream: int) -> int:
     return lib().echo_indexer_prefetch(C.byref(dims), _ref(layer), _ref(batch), _ref(ws),
                                        theta_mode, stream)
+
+
+def echo_indexer_begin(dims, layer, batch, ws, theta_mode: int, stream: int) -> int:
+    return lib().echo_indexer_begin(C.byref(dims), _ref(layer), _ref(batch), _ref(ws),
+                                    theta_mode, stream)
+
+
+def echo_indexer_score(dims, layer, batch, ws, theta_mode: int, stream: int) -> int:
+    return lib().echo_indexer_score(C.byref(dims), _ref(layer), _ref(batch), _ref(ws),
+                                    theta_mode, stream)
 
 
 def echo_topk(dims, scores: int, score_stride: int, batch, ws, theta, stream: int) -> int:

@@ -340,6 +340,32 @@ int echo_indexer_prefetch(const echo_dims_t *dims, const echo_layer_t *layer,
   return run_indexer(a, 0, stream);
 }
 
+int echo_indexer_begin(const echo_dims_t *dims, const echo_layer_t *layer,
+                       const echo_batch_t *batch, const echo_ws_t *ws, int theta_mode,
+                       hipStream_t stream) {
+  int rc = check_dims(dims);
+  if (rc != ECHO_OK) return rc;
+  if (theta_mode < ECHO_THETA_EMA || theta_mode > ECHO_THETA_POS_INF) return ECHO_EINVAL;
+  if (!layer_ok(layer, theta_mode == ECHO_THETA_EMA) || !batch_ok(*dims, batch) || !ws_ok(ws))
+    return ECHO_EINVAL;
+  const StepArgs a = make_args(*dims, layer, batch, *ws, theta_mode);
+  LAUNCH(launch_begin(a, BEGIN_REQ | BEGIN_Q | BEGIN_CLR_INDEX | BEGIN_CLR_TOPK, stream));
+  return ECHO_OK;
+}
+
+int echo_indexer_score(const echo_dims_t *dims, const echo_layer_t *layer,
+                       const echo_batch_t *batch, const echo_ws_t *ws, int theta_mode,
+                       hipStream_t stream) {
+  int rc = check_dims(dims);
+  if (rc != ECHO_OK) return rc;
+  if (theta_mode < ECHO_THETA_EMA || theta_mode > ECHO_THETA_POS_INF) return ECHO_EINVAL;
+  if (!layer_ok(layer, theta_mode == ECHO_THETA_EMA) || !batch_ok(*dims, batch) || !ws_ok(ws))
+    return ECHO_EINVAL;
+  const StepArgs a = make_args(*dims, layer, batch, *ws, theta_mode);
+  LAUNCH(launch_score(a, stream));
+  return ECHO_OK;
+}
+
 int echo_topk(const echo_dims_t *dims, const float *scores, int64_t score_stride,
               const echo_batch_t *batch, const echo_ws_t *ws, float *theta, hipStream_t stream) {
   int rc = check_dims(dims);
