@@ -99,3 +99,43 @@ def test_prefill_full_size(C):
     rig = H.PrefillRig(get("prefill"), N=100_000, C=C, chunks=2)
     _run(rig, 2, check_rows=[0, 1, C // 2, C - 1])
     rig.close()
+
+
+def test_prefill_graph_replay_matches_eager():
+    # three chunks captured in one graph (fixed shapes and pointers; the later chunks
+    # read the previous chunk's k-th scores as their prediction), replayed twice from
+    # a fresh layer; every replay must leave what the eager calls leave
+    wl = get("prefill").scaled(rho=0.9)
+    kw = dict(N=3000, C=40, chunks=3, n_gpu=4000, n_host=4096, top_k=256)
+    _say("prefill graph replay: N 3000, C 40, 3 chunks")
+    eager = H.PrefillRig(wl, **kw)
+    _run(eager, 3)
+    graph = H.PrefillRig(wl, **kw)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for c in range(3):
+                graph.gpu_chunk(c)
+    torch.cuda.current_stream().wait_stream(s)
+    ref = eager.layer.state()
+    ref_pool = eager.layer.gpu_kv.clone()
+    C, N = kw["C"], kw["N"]
+    for rep in range(2):
+        graph.layer.init()
+        graph.pws.reset()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(graph.pws.status.item()) == 0
+        st = graph.layer.state()
+        for key in ("h2g", "g2h", "prio", "free", "idxbuf"):
+            assert np.array_equal(st[key], ref[key]), (rep, key)
+        assert st["t"] == ref["t"] == 3 and st["nfree"] == ref["nfree"]
+        assert torch.equal(graph.layer.gpu_kv, ref_pool), rep
+        assert torch.equal(graph.pws.scores(C, N), eager.pws.scores(C, N)), rep
+        assert torch.equal(graph.pws.sel[:C], eager.pws.sel[:C]), rep
+        assert torch.equal(graph.pws.counts, eager.pws.counts), rep
+    graph.close()
+    eager.close()
