@@ -121,3 +121,47 @@ def test_binding_has_no_compute_fallback():
     src = open(os.path.join(ROOT, "kv_cache_offload_fp8_amd", "abi.py")).read()
     src += open(os.path.join(ROOT, "kv_cache_offload_fp8_amd", "runtime.py")).read()
     assert "oracle" not in src
+
+
+def test_newer_entry_points_check_arguments_before_any_launch():
+    _lib_or_skip()
+    d = _dims()
+    ws = abi.echo_ws_t()
+    layer = abi.echo_layer_t()
+    batch = abi.echo_batch_t(1, None, None)
+    for fn in (abi.echo_indexer_begin, abi.echo_indexer_score):
+        assert fn(d, None, None, None, 0, 0) == abi.ECHO_EINVAL
+        assert fn(d, layer, batch, ws, 7, 0) == abi.ECHO_EINVAL
+    assert abi.echo_gather(d, None, batch, ws, 1 << 30, 0) == abi.ECHO_EINVAL
+    assert abi.echo_append(d, None, 1, 1, 1, 1, 1 << 30, ws, 1, 0) == abi.ECHO_EINVAL
+    assert abi.echo_release(d, None, 1, 1, 1, 1, 1, ws, 0) == abi.ECHO_EINVAL
+    assert abi.echo_release(d, layer, 1, 1, 1, None, 1, ws, 0) == abi.ECHO_EINVAL
+    assert abi.echo_admit(d, None, 1, 1, 1, 0, 0, 16, 1, ws, 0) == abi.ECHO_EINVAL
+    pws = abi.echo_prefill_ws_t()
+    chunk = abi.echo_prefill_chunk_t(4, 0, 1000, 1 << 30, 1 << 30, None)
+    for fn in (abi.echo_prefill_score, abi.echo_prefill_early, abi.echo_prefill_select):
+        assert fn(d, layer, chunk, pws, 0) == abi.ECHO_EINVAL
+    assert abi.echo_prefill_copy(d, layer, pws, 0, 0) == abi.ECHO_EINVAL
+    assert abi.echo_prefill_ws_reset(d, pws, 0) == abi.ECHO_EINVAL
+
+
+def test_prefill_workspace_size_and_bind():
+    _lib_or_skip()
+    d = _dims()
+    assert abi.echo_prefill_ws_bytes(d, 0) == 0
+    assert abi.echo_prefill_ws_bytes(d, 4097) == 0
+    n = abi.echo_prefill_ws_bytes(d, 64)
+    m = abi.echo_prefill_ws_bytes(d, 128)
+    # the score rows grow with the chunk: at least max_ctx floats per extra query
+    assert n > 64 * d.max_ctx * 4 and m - n >= 64 * d.max_ctx * 4
+    pws = abi.echo_prefill_ws_t()
+    base = 1 << 32
+    assert abi.echo_prefill_ws_bind(d, 64, base + 16, n, pws) == abi.ECHO_EINVAL  # misaligned
+    assert abi.echo_prefill_ws_bind(d, 64, base, n - 1, pws) == abi.ECHO_EINVAL   # too small
+    assert abi.echo_prefill_ws_bind(d, 64, base, n, pws) == abi.ECHO_OK
+    ptrs = [getattr(pws, f) for f in ("scores", "sel", "n_sel", "kth", "beta", "n_qcand", "cand",
+                                      "uni", "pf_h", "pf_g", "miss_h", "miss_g", "counts",
+                                      "status", "internal")]
+    assert all(p % 256 == 0 and base <= p < base + n for p in ptrs)
+    assert len(set(ptrs)) == len(ptrs) and ptrs == sorted(ptrs)
+    assert pws.max_chunk == 64 and pws.internal + pws.internal_bytes == base + n
