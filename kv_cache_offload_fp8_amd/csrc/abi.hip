@@ -155,7 +155,7 @@ StepArgs make_args(const echo_dims_t &d, const echo_layer_t *l, const echo_batch
 // ------------------------------------------------------------ prefill workspace
 struct PrefillLayout {
   int64_t scores, sel, n_sel, kth, beta, n_qcand, cand, uni, pf_h, pf_g, miss_h, miss_g, counts,
-      status, internal, qhi, qlo, wsc, cflag, uflag, seg, tmp, total;
+      status, internal, qhi, qlo, wsc, cflag, uflag, seg, tmp, hist, total;
 };
 
 int64_t round_seg(int64_t n) { return (n + kPfSeg - 1) / kPfSeg * kPfSeg; }
@@ -192,6 +192,7 @@ bool prefill_layout(const echo_dims_t *d, int32_t max_chunk, PrefillLayout *L) {
   L->uflag = take(round_seg(N));
   L->seg = take((round_seg(N) / kPfSeg + 1) * 4);
   L->tmp = take((int64_t)d->n_gpu * 4);
+  L->hist = take(C * 256 * 4);
   L->total = off;
   return true;
 }
@@ -227,6 +228,7 @@ void fill_prefill_ws(const echo_dims_t &d, const echo_prefill_ws_t *w, PrefillAr
   p->uflag = in + (L.uflag - L.internal);
   p->seg = (int32_t *)(in + (L.seg - L.internal));
   p->tmp = (int32_t *)(in + (L.tmp - L.internal));
+  p->hist = (uint32_t *)(in + (L.hist - L.internal));
 }
 
 int prefill_args(const echo_dims_t *dims, const echo_layer_t *layer,

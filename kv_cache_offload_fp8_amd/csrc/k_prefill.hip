@@ -17,9 +17,10 @@
 //                 for every query; each wave keeps two queries' operands in
 //                 registers and streams 64-token K chunks; the grid is placed so
 //                 that the workgroups of one XCD share one token range through
-//                 its L2)
-//   k_pf_coarse   per query: the bucket histogram of fp16(score - pred), the
-//                 boundary bucket, and the candidate flags above it
+//                 its L2), and each query's histogram of the coarse buckets of
+//                 fp16(score - pred), counted in LDS as the scores are made
+//   k_pf_coarse   per query: the boundary bucket from that histogram, and the
+//                 candidate flags above it (one pass over the row)
 //   k_pf_flags_*  the union of flags as an ascending token list
 //   k_pf_inst_*   install a list in order: resident tokens get priority t, the
 //                 others take the next ascending free slots (idxbuf)
@@ -104,6 +105,7 @@ __global__ __launch_bounds__(256) void k_pf_stage(StepArgs a, PrefillArgs p) {
   *(uint2 *)(p.qhi + o) = make_uint2(whi[0], whi[1]);
   *(uint2 *)(p.qlo + o) = make_uint2(wlo[0], wlo[1]);
   if (d0 == 0) p.wsc[(int64_t)i * kHeadsPad + j] = j < a.H ? ldexpf(wj, -e) : 0.0f;
+  if (tid < 64) p.hist[(int64_t)i * 256 + quarter * 64 + tid] = 0;  // this chunk's histogram
 }
 
 // ------------------------------------------------------------------ score
@@ -158,56 +160,6 @@ __device__ inline float pf_score64(const v8i_pf (&kb)[4], const v8i_pf (&qa)[4][
   return sel == 0 ? sc4[0] : sel == 1 ? sc4[1] : sel == 2 ? sc4[2] : sc4[3];
 }
 
-// Workgroup b: XCD x = b % 8 (the hardware's round-robin placement) takes token
-// splits x * tsplits/8 .. , all query blocks of one split before the next, so the
-// workgroups resident on one XCD read the same K range through its L2.
-__global__ __launch_bounds__(kPfWaves * kWave) void k_pf_score(StepArgs a, PrefillArgs p) {
-  if (failed(p.status)) return;
-  const int lane = lane_id(), wave = threadIdx.x / kWave;
-  const int b = blockIdx.x, xcd = b & 7, jj = b >> 3;
-  const int ts = xcd * (p.tsplits >> 3) + jj / p.qblocks, qb = jj % p.qblocks;
-  const int q0 = qb * kPfQBlock + wave * kPfQ;
-  if (q0 >= p.C) return;  // wave-uniform; no barrier follows
-  const int nch = (p.N + 63) >> 6;
-  const int per = (nch + p.tsplits - 1) / p.tsplits;
-  const int c0 = ts * per, c1 = min(nch, c0 + per);
-  if (c0 >= c1) return;
-  const int row = lane & 15, chunk = (lane >> 4) * 32;
-  v8i_pf qa[kPfQ][4][2];
-  float wr[kPfQ][4][4];
-#pragma unroll
-  for (int u = 0; u < kPfQ; ++u) {
-    const int qi = min(q0 + u, p.C - 1);  // a missing second query repeats the first
-    const uint8_t *qh = p.qhi + (int64_t)qi * kHeadsPad * kDimPad;
-    const uint8_t *ql = p.qlo + (int64_t)qi * kHeadsPad * kDimPad;
-#pragma unroll
-    for (int hg = 0; hg < 4; ++hg) {
-      qa[u][hg][0] = *(const v8i_pf *)(qh + (hg * 16 + row) * kDimPad + chunk);
-      qa[u][hg][1] = *(const v8i_pf *)(ql + (hg * 16 + row) * kDimPad + chunk);
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        wr[u][hg][rr] = p.wsc[(int64_t)qi * kHeadsPad + hg * 16 + (lane >> 4) * 4 + rr];
-    }
-  }
-  auto emit = [&](const v8i_pf (&kb)[4], int c) {
-    const int s = c * 64 + lane;
-#pragma unroll
-    for (int u = 0; u < kPfQ; ++u) {
-      const float v = pf_score64(kb, qa[u], wr[u], lane);
-      if (q0 + u < p.C && s < p.N) p.scores[(int64_t)(q0 + u) * p.N + s] = v;
-    }
-  };
-  v8i_pf k0[4], k1[4];
-  pf_load_k(a, p, c0 * 64, lane, k0);
-  for (int c = c0; c < c1; c += 2) {  // two register sets: chunk c + 1 loads while c computes
-    if (c + 1 < c1) pf_load_k(a, p, (c + 1) * 64, lane, k1);
-    emit(k0, c);
-    if (c + 2 < c1) pf_load_k(a, p, (c + 2) * 64, lane, k0);
-    if (c + 1 < c1) emit(k1, c + 1);
-  }
-}
-
-// ------------------------------------------------------------------ coarse
 // Bucket of a score shifted by the predicted k-th score: the difference in fp32,
 // rounded to half precision (nearest even), then the top byte of an order key of
 // the half bits (larger value, larger key; -0 counts as +0).
@@ -219,8 +171,73 @@ __device__ inline int pf_bucket(float score, float pred) {
   return key >> 8;
 }
 
+// Workgroup b: XCD x = b % 8 (the hardware's round-robin placement) takes token
+// splits x * tsplits/8 .. , all query blocks of one split before the next, so the
+// workgroups resident on one XCD read the same K range through its L2.
+__global__ __launch_bounds__(kPfWaves * kWave) void k_pf_score(StepArgs a, PrefillArgs p) {
+  // per-query histograms of this workgroup's coarse buckets, flushed at the end
+  __shared__ uint32_t s_hist[kPfQBlock][256];
+  for (int i = threadIdx.x; i < kPfQBlock * 256; i += kPfWaves * kWave) (&s_hist[0][0])[i] = 0;
+  __syncthreads();
+  const bool dead = failed(p.status);
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int b = blockIdx.x, xcd = b & 7, jj = b >> 3;
+  const int ts = xcd * (p.tsplits >> 3) + jj / p.qblocks, qb = jj % p.qblocks;
+  const int q0 = qb * kPfQBlock + wave * kPfQ;
+  const int nch = (p.N + 63) >> 6;
+  const int per = (nch + p.tsplits - 1) / p.tsplits;
+  const int c0 = ts * per, c1 = min(nch, c0 + per);
+  // a wave with no query or no tokens does no work but still meets the barriers
+  if (!dead && q0 < p.C && c0 < c1) {
+    const int row = lane & 15, chunk = (lane >> 4) * 32;
+    v8i_pf qa[kPfQ][4][2];
+    float wr[kPfQ][4][4];
+    float pr[kPfQ];
+#pragma unroll
+    for (int u = 0; u < kPfQ; ++u) {
+      const int qi = min(q0 + u, p.C - 1);  // a missing second query repeats the first
+      pr[u] = p.pred ? p.pred[qi] : 0.0f;
+      const uint8_t *qh = p.qhi + (int64_t)qi * kHeadsPad * kDimPad;
+      const uint8_t *ql = p.qlo + (int64_t)qi * kHeadsPad * kDimPad;
+#pragma unroll
+      for (int hg = 0; hg < 4; ++hg) {
+        qa[u][hg][0] = *(const v8i_pf *)(qh + (hg * 16 + row) * kDimPad + chunk);
+        qa[u][hg][1] = *(const v8i_pf *)(ql + (hg * 16 + row) * kDimPad + chunk);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          wr[u][hg][rr] = p.wsc[(int64_t)qi * kHeadsPad + hg * 16 + (lane >> 4) * 4 + rr];
+      }
+    }
+    auto emit = [&](const v8i_pf (&kb)[4], int c) {
+      const int s = c * 64 + lane;
+#pragma unroll
+      for (int u = 0; u < kPfQ; ++u) {
+        const float v = pf_score64(kb, qa[u], wr[u], lane);
+        if (q0 + u < p.C && s < p.N) {
+          p.scores[(int64_t)(q0 + u) * p.N + s] = v;
+          atomicAdd(&s_hist[wave * kPfQ + u][pf_bucket(v, pr[u])], 1u);
+        }
+      }
+    };
+    v8i_pf k0[4], k1[4];
+    pf_load_k(a, p, c0 * 64, lane, k0);
+    for (int c = c0; c < c1; c += 2) {  // two register sets: chunk c + 1 loads while c computes
+      if (c + 1 < c1) pf_load_k(a, p, (c + 1) * 64, lane, k1);
+      emit(k0, c);
+      if (c + 2 < c1) pf_load_k(a, p, (c + 2) * 64, lane, k0);
+      if (c + 1 < c1) emit(k1, c + 1);
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kPfQBlock * 256; i += kPfWaves * kWave) {
+    const int qq = qb * kPfQBlock + i / 256;
+    const uint32_t v = (&s_hist[0][0])[i];
+    if (v && qq < p.C) atomicAdd(&p.hist[(int64_t)qq * 256 + (i & 255)], v);
+  }
+}
+
+// ------------------------------------------------------------------ coarse
 __global__ __launch_bounds__(kSelThreads) void k_pf_coarse(StepArgs a, PrefillArgs p) {
-  __shared__ uint32_t hist[256];
   __shared__ int sh[kSelThreads / kWave + 1];
   __shared__ int s_beta;
   if (block_failed(p.status)) return;
@@ -229,14 +246,11 @@ __global__ __launch_bounds__(kSelThreads) void k_pf_coarse(StepArgs a, PrefillAr
   const float pr = p.pred ? p.pred[i] : 0.0f;
   int beta = -1;
   if (p.N > a.K) {
-    if (tid < 256) hist[tid] = 0;
     if (tid == 0) s_beta = 0;
-    __syncthreads();
-    for (int s = tid; s < p.N; s += kSelThreads) atomicAdd(&hist[pf_bucket(row[s], pr)], 1u);
-    __syncthreads();
-    // thread t < 256 holds bucket 255 - t: the boundary is the first one, from the
-    // top, at which the running count reaches k
-    const int c = tid < 256 ? (int)hist[255 - tid] : 0;
+    // the row's histogram, built by the scoring kernel; thread t < 256 holds bucket
+    // 255 - t: the boundary is the first one, from the top, at which the running
+    // count reaches k
+    const int c = tid < 256 ? (int)p.hist[(int64_t)i * 256 + 255 - tid] : 0;
     int tot;
     const int excl = block_excl_scan<kSelThreads>(c, sh, &tot);
     if (tid < 256 && excl < a.K && excl + c >= a.K) s_beta = 255 - tid;

@@ -24,6 +24,7 @@ struct PrefillArgs {
   uint8_t *cflag, *uflag;      // [max_ctx rounded up to kPfSeg]
   int32_t *seg;                // [max_ctx / kPfSeg + 1]
   int32_t *tmp;                // [n_gpu] free-list buffer
+  uint32_t *hist;              // [max_chunk][256] coarse-bucket histogram per query
   int32_t qblocks, tsplits;    // scoring grid: query blocks x token splits
 };
 constexpr int kPfSeg = 4096;   // list entries per workgroup of the ordered passes
