@@ -325,19 +325,28 @@ __device__ inline void load_k_chunk(const StepArgs &a, const ReqInfo &r, int s0,
   const int lp = dim_ok ? lane : (lane & 15);
   const int glast = (r.ctx - 1) & ~15;
   // real = false (no next item): every lane reads the same 16 bytes, one cache
-  // line per instruction, only to keep the load count the same on every path
-  const int half = real ? 8 * a.D : 0;
+  // line per instruction, only to keep the load count the same on every path.
+  // The choice is made on offsets, as products with a wave-uniform 0/1 that went
+  // through readfirstlane: a select between two pointers lets the compiler turn
+  // the load of a select into a select of two loads, which it lowers into two
+  // exec-masked load paths joined by a wait for every load in flight (once per
+  // work item, measured 3-4% of the scoring time).
+  const uint32_t rl = (uint32_t)__builtin_amdgcn_readfirstlane(real ? 1 : 0);
+  const uint32_t half = (uint32_t)(8 * a.D) * rl;
   // wave-uniform 64-bit group address + 32-bit lane offset: the loads use the
   // scalar-base addressing form and need no per-lane 64-bit arithmetic
-  const uint32_t lo = real ? (uint32_t)lp * 16u : 0u;
+  const uint32_t lo = (uint32_t)lp * 16u * rl;
   const int s0u = __builtin_amdgcn_readfirstlane(s0);
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int st = s0u + 16 * u;
     const int sg = st < r.ctx ? st : glast;
-    const uint8_t *g = real ? a.kidx + ((int64_t)r.base + sg) * a.D : a.kidx;
+    const uint64_t go = (uint64_t)(((int64_t)r.base + sg) * a.D) * rl;
+    const uint32_t go_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)go);
+    const uint32_t go_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(go >> 32));
+    const uint8_t *g = a.kidx + (((uint64_t)go_hi << 32) | go_lo);
     const v4i x0 = __builtin_nontemporal_load((const v4i *)(g + lo));
-    const v4i x1 = __builtin_nontemporal_load((const v4i *)(g + (lo + (uint32_t)half)));
+    const v4i x1 = __builtin_nontemporal_load((const v4i *)(g + (lo + half)));
     kb[u] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
   }
 }
@@ -710,7 +719,10 @@ __global__ __launch_bounds__(512) void k_score(StepArgs a) {
   if (s_dead) return;
   const int wid = tid / kWave;
   if ((int)blockIdx.x < a.score_blocks) {
-    score_wave<HG, ANY_PF>(a, s_req, blockIdx.x * kScoreWaves + wid,
+    // the wave index through readfirstlane: every job index derived from it is
+    // then known to be wave-uniform and lives in scalar registers
+    score_wave<HG, ANY_PF>(a, s_req,
+                           __builtin_amdgcn_readfirstlane((int)blockIdx.x * kScoreWaves + wid),
                            &s_pend[ANY_PF ? wid : 0][0]);
     if (lane_id() == 0 && atomicSub(&s_left, 1) == 1)
       __hip_atomic_fetch_add(&a.sc.misc[M_SCORE_DONE], 1, __ATOMIC_RELAXED,
