@@ -145,6 +145,22 @@ __device__ inline void fail(int32_t *status, int code) {
 __device__ inline int lane_id() { return threadIdx.x & (kWave - 1); }
 __device__ inline uint64_t lanemask_lt() { return (1ull << lane_id()) - 1ull; }
 
+// v summed over the four lanes l, l^16, l^32, l^48, returned in all four: first
+// the pairs 16 apart, then 32 apart.  gfx950's lane-swap instructions do the
+// exchange in the vector ALU (v_permlane16_swap swaps rows 1 and 3 of its first
+// operand with rows 0 and 2 of its second, v_permlane32_swap the upper half of
+// the first with the lower half of the second; with both operands v, the two
+// results hold v and its partner in every lane), where a cross-lane shuffle
+// goes through the LDS crossbar and waits for its return.
+__device__ inline float sum_lane_groups16(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float v16 = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+  const uint32_t w = __float_as_uint(v16);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+}
+
 __device__ inline int wave_sum(int v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);

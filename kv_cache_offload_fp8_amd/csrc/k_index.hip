@@ -373,8 +373,7 @@ __device__ inline float score_chunk(const v8i (&kb)[4], const v8i (&qa)[HG][2],
       for (int rr = 0; rr < 4; ++rr)
         v += wr[hg][rr] * __int_as_float(max(__float_as_int(acc[rr]), 0));
     }
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
+    v = sum_lane_groups16(v);
     sc4[u] = v;  // every lane with (lane & 15) == i holds the score of token 16u + i
   }
   const int sel = lane >> 4;

@@ -152,8 +152,7 @@ __device__ inline float pf_score64(const v8i_pf (&kb)[4], const v8i_pf (&qa)[4][
       for (int rr = 0; rr < 4; ++rr)
         v += wr[hg][rr] * __int_as_float(max(__float_as_int(acc[rr]), 0));
     }
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
+    v = sum_lane_groups16(v);
     sc4[u] = v;
   }
   const int sel = lane >> 4;
@@ -219,12 +218,17 @@ __global__ __launch_bounds__(kPfWaves * kWave) void k_pf_score(StepArgs a, Prefi
         }
       }
     };
+    // Two register sets: chunk c + 1 loads while c computes.  The loads are
+    // unconditional, clamped to the split's last chunk (at most two extra chunk
+    // reads per wave, from L2): a load under a branch would leave the compiler
+    // unable to count the loads in flight at the join, and it would wait for all
+    // of them there, once per pair of chunks.
     v8i_pf k0[4], k1[4];
     pf_load_k(a, p, c0 * 64, lane, k0);
-    for (int c = c0; c < c1; c += 2) {  // two register sets: chunk c + 1 loads while c computes
-      if (c + 1 < c1) pf_load_k(a, p, (c + 1) * 64, lane, k1);
+    for (int c = c0; c < c1; c += 2) {
+      pf_load_k(a, p, min(c + 1, c1 - 1) * 64, lane, k1);
       emit(k0, c);
-      if (c + 2 < c1) pf_load_k(a, p, (c + 2) * 64, lane, k0);
+      pf_load_k(a, p, min(c + 2, c1 - 1) * 64, lane, k0);
       if (c + 1 < c1) emit(k1, c + 1);
     }
   }
