@@ -319,10 +319,13 @@ __device__ inline int lb_resolve(uint64_t *st, int tau, int seg0, int c, int32_t
 // `tau` (lane l: item tau - 1 - l); lb_try_finish returns false if one of them,
 // up to the nearest inclusive prefix, is not published yet (nothing is written
 // then).  Otherwise it completes the look-back like lb_resolve and returns true.
+// Every lane loads (lanes before the segment read its first state) and the value
+// is not looked at here: a select right after the load would wait for it, and
+// for every load issued before it, on the spot.  lb_try_finish masks those lanes.
 __device__ inline uint64_t lb_try_load(const uint64_t *st, int tau, int seg0) {
   const int idx = tau - 1 - lane_id();
-  return idx >= seg0 ? __hip_atomic_load(&st[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                     : kFlagP;
+  return __hip_atomic_load(&st[idx >= seg0 ? idx : seg0], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ inline bool lb_try_finish(uint64_t *st, int tau, int seg0, int c, uint64_t v,
@@ -331,6 +334,7 @@ __device__ inline bool lb_try_finish(uint64_t *st, int tau, int seg0, int c, uin
     E = 0;
     return true;
   }
+  if (tau - 1 - lane_id() < seg0) v = kFlagP;  // before the segment: an inclusive prefix of 0
   const uint64_t fm = __ballot((v >> 32) != 0);
   const uint64_t pm = __ballot((v >> 32) == 2);
   const uint64_t need = pm ? ((pm & (0 - pm)) << 1) - 1 : ~0ull;

@@ -403,13 +403,14 @@ __device__ inline int pf_publish(const StepArgs &a, const ReqInfo &r, int pi,
   return c_all;
 }
 
-// Ranks and free-list reads of this lane's candidates in item pi (at most one
-// per chunk), given the item's exclusive prefix E: bit c of `tk` says whether
-// the chunk-c candidate takes a slot; the reads are issued together, without
-// branches, and consumed by pf_commit.
+// Ranks of this lane's candidates in item pi (at most one per chunk), given the
+// item's exclusive prefix E: bit c of `tk` says whether the chunk-c candidate
+// takes a slot, and gi[c] is the free-list position it reads (0, a dummy read,
+// where it takes none).  The caller issues the reads together, without branches,
+// and pf_commit consumes them.
 __device__ inline void pf_plan(const StepArgs &a, const ReqInfo &r, const uint64_t (&cand)[kChunks],
                                int E, int nfree, int (&rank)[kChunks], int &tk,
-                               int (&gv)[kChunks]) {
+                               int (&gi)[kChunks]) {
   const int lane = lane_id();
   const int lim = nfree < a.n_gpu ? nfree : a.n_gpu;
   int rank0 = E;
@@ -422,7 +423,7 @@ __device__ inline void pf_plan(const StepArgs &a, const ReqInfo &r, const uint64
     rank0 += __popcll(m);
   }
 #pragma unroll
-  for (int c = 0; c < kChunks; ++c) gv[c] = a.idxbuf[((tk >> c) & 1) ? r.off + rank[c] : 0];
+  for (int c = 0; c < kChunks; ++c) gi[c] = ((tk >> c) & 1) ? r.off + rank[c] : 0;
 }
 
 // Installs the planned candidates of item pi (maps, priority t, the rank-ordered
@@ -475,10 +476,12 @@ __device__ static void pf_install(const StepArgs &a, const ReqInfo &r, int b, in
                                   const uint64_t (&cand)[kChunks], int c_all, int t,
                                   int nfree) {
   const int E = lb_resolve(a.sc.tstate, r.tile0 + pi, r.tile0, c_all, a.ws.status);
-  int rank[kChunks], tk = 0, gv[kChunks];
+  int rank[kChunks], tk = 0, gi[kChunks], gv[kChunks];
 #pragma unroll
-  for (int c = 0; c < kChunks; ++c) rank[c] = gv[c] = 0;
-  if (c_all > 0) pf_plan(a, r, cand, E, nfree, rank, tk, gv);
+  for (int c = 0; c < kChunks; ++c) rank[c] = gi[c] = 0;
+  if (c_all > 0) pf_plan(a, r, cand, E, nfree, rank, tk, gi);
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) gv[c] = a.idxbuf[gi[c]];
   pf_commit(a, r, b, pi, c_all, E, rank, tk, gv, t, nfree);
 }
 
@@ -585,6 +588,13 @@ __device__ static void score_job(const StepArgs &a, const ReqInfo &r, int b, int
     int gq[kChunks];
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
+      const int s = s_wave + c * 64 + lane;
+      const bool valid = s < r.ctx;
+      // the chunk's map entries go out before the next chunk's K loads: they are
+      // consumed an item later, and a load issued after those K loads could not
+      // be waited for without waiting for them too
+      gq[c] = 0;
+      if (PF) gq[c] = a.h2g[(int64_t)r.base + (valid ? s : r.ctx - 1)];
       if (c + 1 < kChunks) {
         load_k_chunk(a, r, s_wave + (c + 1) * 64, lane, kb[(c + 1) & 1]);
       } else {
@@ -593,31 +603,38 @@ __device__ static void score_job(const StepArgs &a, const ReqInfo &r, int b, int
         load_k_chunk(a, r, (ni < r.ntiles ? ni : i) * kScoreTile, lane, kb[0], ni < r.ntiles);
       }
       const float score = score_chunk<HG>(kb[c & 1], qa, wr, lane);
-      const int s = s_wave + c * 64 + lane;
-      const bool valid = s < r.ctx;
       if (valid) out[s] = score;
       keys[c] = topk_key(score);
       gsel[c] = __ballot(r.use_guard && valid && keys[c] <= r.guard_key);
       above[c] = 0;
-      gq[c] = 0;
       if (PF) {
         above[c] = __ballot(valid && score > r.theta);
-        gq[c] = a.h2g[(int64_t)r.base + (valid ? s : r.ctx - 1)];
         if (c == 0 && have_prev) publish_prev();
-        if (c == 1 && qn > 0) {
-          read_oldest();
-          sv = lb_try_load(a.sc.tstate, r.tile0 + o_i, r.tile0);
+        // The look-back state loads (chunk 1) and the free-list reads (chunk 2) go
+        // out on every item, dummy ones when nothing is queued or planned: loads
+        // issued on some paths only would leave the compiler unable to count the
+        // loads in flight where their results are used, and it would wait for all.
+        if (c == 1) {
+          if (qn > 0) read_oldest();
+          sv = lb_try_load(a.sc.tstate, r.tile0 + (qn > 0 ? o_i : 0), r.tile0);
         }
-        if (c == 2 && qn > 0 &&
-            lb_try_finish(a.sc.tstate, r.tile0 + o_i, r.tile0, o_c, sv, a.ws.status, E0)) {
-          tk = 0;
-          if (o_c > 0) {
-            uint64_t oc[kChunks];
+        if (c == 2) {
+          int gi[kChunks];
 #pragma unroll
-            for (int cc = 0; cc < kChunks; ++cc) oc[cc] = pq[qh].cand[cc];
-            pf_plan(a, r, oc, E0, nfree, rk, tk, gv);
+          for (int cc = 0; cc < kChunks; ++cc) gi[cc] = 0;
+          tk = 0;
+          if (qn > 0 &&
+              lb_try_finish(a.sc.tstate, r.tile0 + o_i, r.tile0, o_c, sv, a.ws.status, E0)) {
+            if (o_c > 0) {
+              uint64_t oc[kChunks];
+#pragma unroll
+              for (int cc = 0; cc < kChunks; ++cc) oc[cc] = pq[qh].cand[cc];
+              pf_plan(a, r, oc, E0, nfree, rk, tk, gi);
+            }
+            planned = true;
           }
-          planned = true;
+#pragma unroll
+          for (int cc = 0; cc < kChunks; ++cc) gv[cc] = a.idxbuf[gi[cc]];
         }
         if (c == 3 && planned) {
           pf_commit(a, r, b, o_i, o_c, E0, rk, tk, gv, t, nfree);
