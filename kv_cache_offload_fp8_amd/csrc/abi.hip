@@ -588,8 +588,13 @@ int echo_layer_step(const echo_dims_t *dims, const echo_layer_t *layer, const ec
   a.copy_handoff = 1;  // the prefetch copy runs on through top-k and management
   rc = run_indexer(a, BEGIN_CLR_MANAGE, stream);
   if (rc != ECHO_OK) return rc;
-  LAUNCH(launch_topk(a, true, stream));
-  LAUNCH(launch_manage(a, true, true, stream));
+  if (a.B > 0 && select_manage_blocks(a) <= device_cus()) {
+    // one launch: the prefetch copy runs on from selection into management
+    LAUNCH(launch_select_manage(a, stream));
+  } else {
+    LAUNCH(launch_topk(a, true, stream));
+    LAUNCH(launch_manage(a, true, true, stream));
+  }
   return ECHO_OK;
 }
 

@@ -389,6 +389,34 @@ __device__ inline bool grid_sync(int32_t *ctr, int nblocks, int32_t *status) {
   return s_ok != 0;
 }
 
+// Wait, as a whole workgroup, until *ctr reaches `target` (counted by other
+// workgroups of the launch, each after a fence): false if the status fails
+// meanwhile or the wait exceeds the spin limit (then ECHO_ETIMEOUT).
+__device__ inline bool wait_count(int32_t *ctr, int target, int32_t *status) {
+  __shared__ int s_ok;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int ok = 1;
+    const uint64_t t0 = wall_clock64();
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      if (failed(status)) {
+        ok = 0;
+        break;
+      }
+      if ((long long)(wall_clock64() - t0) > kSpinLimit) {
+        fail(status, ECHO_ETIMEOUT);
+        ok = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    __threadfence();
+    s_ok = ok;
+  }
+  __syncthreads();
+  return s_ok != 0;
+}
+
 // ------------------------------------------------------------ key orders
 // Order-preserving map of a finite fp32 value to uint32 (-0 treated as +0).
 __device__ inline uint32_t f32_order(float f) {

@@ -21,8 +21,7 @@
 // more) needs the exact (priority, slot) select, done by one workgroup between
 // two more barriers.  A second look-back over the workgroups ranks the free
 // slots for the allocation, and each workgroup copies the rows it allocated.
-#include "copy.h"
-#include "select.h"
+#include "topk.h"
 
 namespace echo {
 
@@ -72,23 +71,18 @@ __device__ static void copy_rows(const StepArgs &a, const int32_t *hs, const int
   }
 }
 
+// Eviction, allocation, recall and the step counter for slot tile `blk` of
+// a.sc.atiles (all of them resident: they meet at grid barriers).  st0: the
+// status word, read at the kernel's start.
 template <bool RECALL, bool ADVANCE>
-__global__ __launch_bounds__(kSelThreads) void k_manage(StepArgs a) {
+__device__ static void manage_block(const StepArgs &a, int blk, int32_t st0) {
   __shared__ uint32_t s_hist[kBins];
   __shared__ int32_t s_rh[kSlotTile], s_rg[kSlotTile];
   __shared__ int sh[kSelThreads / kWave + 1];
   __shared__ int s_moff[kMaxBatch + 1];
   __shared__ int s_bin, s_below, s_E;
-  // the status is looked at after the first reads are issued (one round trip)
-  const int32_t st0 = __hip_atomic_load(a.ws.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int tid = threadIdx.x;
-  const int blk = blockIdx.x, nblk = a.sc.atiles;
-  if (blk >= nblk) {  // copy workgroup: finish the step's prefetch copy, two waves per copy wave
-    if (st0 != 0) return;
-    const int g = (blk - nblk) * (kSelThreads / kWave) + tid / kWave;
-    copy_worker(a, a.sc.req, g % a.copy_waves, g / a.copy_waves, 2, nullptr, 0);
-    return;
-  }
+  const int nblk = a.sc.atiles;
   const int t = a.ctl[ECHO_CTL_STEP];
   if (st0 != 0) return;
   const int g0 = blk * kSlotTile + tid * 4;
@@ -285,6 +279,62 @@ __global__ __launch_bounds__(kSelThreads) void k_manage(StepArgs a) {
       if (done == nblk - 1 && !failed(a.ws.status)) a.ctl[ECHO_CTL_STEP] = t + 1;
     }
   }
+}
+
+// copy workgroup w of a management launch: finish the step's prefetch copy, two
+// waves per copy wave
+__device__ static void manage_copy(const StepArgs &a, int w) {
+  const int g = w * (kSelThreads / kWave) + (int)threadIdx.x / kWave;
+  copy_worker(a, a.sc.req, g % a.copy_waves, g / a.copy_waves, 2, nullptr, 0);
+}
+
+template <bool RECALL, bool ADVANCE>
+__global__ __launch_bounds__(kSelThreads) void k_manage(StepArgs a) {
+  // the status is looked at after the first reads are issued (one round trip)
+  const int32_t st0 = __hip_atomic_load(a.ws.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int blk = blockIdx.x, nblk = a.sc.atiles;
+  if (blk >= nblk) {
+    if (st0 == 0) manage_copy(a, blk - nblk);
+    return;
+  }
+  manage_block<RECALL, ADVANCE>(a, blk, st0);
+}
+
+// Top-k, protection, management and the rest of the prefetch copy of a layer step
+// in one launch: workgroups [0, B) select (one request each), [B, B + atiles)
+// manage the slots once every selection is done, and the rest copy prefetched
+// rows from the launch's start to its end.  Compared with two launches, the copy
+// does not stop and restart between selection and management.  Every workgroup
+// is resident (the launch is used only when they fit one per compute unit).
+template <bool RECALL, bool ADVANCE>
+__global__ __launch_bounds__(kSelThreads) void k_select_manage(StepArgs a) {
+  const int32_t st0 = __hip_atomic_load(a.ws.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int blk = blockIdx.x;
+  if (blk < a.B) {
+    topk_block<true>(a, blk, st0);
+    return;
+  }
+  const int mb = blk - a.B, nblk = a.sc.atiles;
+  if (mb >= nblk) {
+    if (st0 == 0) manage_copy(a, mb - nblk);
+    return;
+  }
+  if (st0 != 0) return;
+  // priorities, miss lists and counts of every request are final once all the
+  // selecting workgroups have counted themselves done
+  if (!wait_count(&a.sc.misc[M_TOPK_DONE], a.B, a.ws.status)) return;
+  manage_block<RECALL, ADVANCE>(a, mb, 0);
+}
+
+// Workgroups of the fused launch: selection + management + copy.
+int select_manage_blocks(const StepArgs &a) {
+  return a.B + a.sc.atiles + 2 * a.copy_waves / (kSelThreads / kWave);
+}
+
+hipError_t launch_select_manage(const StepArgs &a, hipStream_t s) {
+  const dim3 grid(select_manage_blocks(a)), block(kSelThreads);
+  hipLaunchKernelGGL((k_select_manage<true, true>), grid, block, 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_manage(const StepArgs &a, bool recall, bool advance, hipStream_t s) {

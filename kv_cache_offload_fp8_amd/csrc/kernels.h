@@ -88,6 +88,10 @@ hipError_t launch_score(const StepArgs &a, hipStream_t s);
 hipError_t launch_topk(const StepArgs &a, bool protect, hipStream_t s);
 hipError_t launch_protect(const StepArgs &a, hipStream_t s);
 hipError_t launch_manage(const StepArgs &a, bool recall, bool advance, hipStream_t s);
+// top-k (with protection), management (recall, step advance) and the prefetch copy
+// in one launch of select_manage_blocks(a) workgroups, all resident
+int select_manage_blocks(const StepArgs &a);
+hipError_t launch_select_manage(const StepArgs &a, hipStream_t s);
 hipError_t launch_gather(const StepArgs &a, uint16_t *out, hipStream_t s);
 hipError_t launch_append(const StepArgs &a, const uint8_t *k_new, const uint16_t *lat_new,
                          int32_t *ctx_io, int advance, hipStream_t s);
