@@ -209,3 +209,27 @@ def test_context_edge_cases():
     for mode in (H.MODE_EMA, H.MODE_NEG_INF, H.MODE_EMA, H.MODE_EMA):
         rig.step_and_compare(mode)
     rig.close()
+
+
+@pytest.mark.parametrize("mode", [H.MODE_EMA, H.MODE_NEG_INF])
+def test_two_launch_step_when_the_fused_launch_does_not_fit(mode):
+    # echo_layer_step runs selection and management in one launch only when its
+    # workgroups (one per request, one per 4096 slots, the copy workgroups) fit one
+    # per compute unit; 64 requests and 700,000 slots (171 slot tiles) do not, so the
+    # step takes the two-launch path: top-k with its copy hand-off, then management.
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    n_gpu, B = 700_000, 64
+    tiles = -(-n_gpu // 4096)
+    copy_wgs = min(cus // 8, 64)  # the indexer's copy workgroups, as management launches them
+    if B + tiles + copy_wgs <= cus:
+        pytest.skip(f"{B + tiles + copy_wgs} workgroups fit {cus} compute units")
+    rng = np.random.default_rng(5)
+    ctx = [int(c) for c in rng.integers(300, 700, size=B)]
+    wl = get("tiny").scaled(n_host=48_000, rho=0.9)
+    _say(f"two-launch step: B={B}, n_gpu={n_gpu}, {cus} CUs, mode {mode}")
+    rig = H.Rig(wl, steps=4, ctx=ctx, n_gpu=n_gpu)
+    for _ in range(4):
+        out, _ = rig.step_and_compare(mode)
+        assert out["status"] == 0
+    assert sum(int(o["n_pf"].sum()) for _, o in rig.history) > 0
+    rig.close()
