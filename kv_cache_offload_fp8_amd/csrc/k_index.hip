@@ -505,15 +505,24 @@ struct PendItem {
 // Scores a wave holds in LDS before it writes them out (items of 256 tokens).
 constexpr int kDeferItems = 8;
 
-// Job k of request r: its items k, k + wb, ...  Scores are written to LDS
-// (`sbuf`, kDeferItems items of this wave) and go out to HBM only when that
-// buffer is full or the job ends.  Score stores interleaved with the K stream
+// A scoring wave's LDS: the scores and selection-guard candidates of its
+// buffered items.
+struct WaveBuf {
+  float score[kDeferItems * kScoreTile];
+  uint32_t gkey[kDeferItems * kGuardSlots];
+  int32_t gidx[kDeferItems * kGuardSlots];
+  int32_t gcnt[kDeferItems];
+};
+
+// Job k of request r: its items k, k + wb, ...  Scores and selection-guard
+// candidates are written to LDS (`wbuf`, kDeferItems items of this wave) and go
+// out to HBM only when that buffer is full or the job ends.  Score stores interleaved with the K stream
 // cost more than their bytes: on 2.8M tokens, leaving them out shortened the
 // launch by 5-8 us of about 70, and gathering them at the end of each wave's
 // job shortened it by 4-5 us.
 template <int HG, bool PF>
 __device__ static void score_job(const StepArgs &a, const ReqInfo &r, int b, int k, int t,
-                                 int nfree, PendItem *pq, float *sbuf) {
+                                 int nfree, PendItem *pq, WaveBuf *wbuf) {
   const int lane = lane_id();
   // Operand layout: lane l feeds row (l & 15) of A (a head) and column (l & 15)
   // of B (a token) with the 32 bytes at dims chunk .. chunk+31,
@@ -535,17 +544,28 @@ __device__ static void score_job(const StepArgs &a, const ReqInfo &r, int b, int
     }
   }
   float *out = a.ws.scores + (int64_t)b * a.max_ctx;
-  // buffered items: i0, i0 + wb, ... (nbuf of them); each lane writes out the
-  // scores it put in LDS itself, so no other lane's writes need to be waited for
+  // buffered items: i0, i0 + wb, ... (nbuf of them).  Each lane writes out the
+  // scores it put in LDS itself; guard candidates were put there by other lanes
+  // of the wave, whose LDS writes the fence orders before these reads.
   int nbuf = 0, i0 = k;
   auto flush = [&]() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     for (int j = 0; j < nbuf; ++j) {
       const int it = i0 + j * r.wb;
 #pragma unroll
       for (int c = 0; c < kChunks; ++c) {
         const int s = it * kScoreTile + c * 64 + lane;
-        const float v = sbuf[(j * kChunks + c) * 64 + lane];
+        const float v = wbuf->score[(j * kChunks + c) * 64 + lane];
         if (s < r.ctx) out[s] = v;
+      }
+      if (r.use_guard) {
+        const int64_t tau = r.tile0 + it;
+        const int n = wbuf->gcnt[j];
+        if (lane < kGuardSlots && lane < n) {
+          a.sc.gcand_key[tau * kGuardSlots + lane] = wbuf->gkey[j * kGuardSlots + lane];
+          a.sc.gcand_idx[tau * kGuardSlots + lane] = wbuf->gidx[j * kGuardSlots + lane];
+        }
+        if (lane == 0) a.sc.gcand_cnt[tau] = n;
       }
     }
   };
@@ -604,7 +624,6 @@ __device__ static void score_job(const StepArgs &a, const ReqInfo &r, int b, int
   };
   while (true) {
     const int s_wave = i * kScoreTile;
-    const int tau = r.tile0 + i;
     const int ni = i + r.wb;
     uint64_t above[kChunks], gsel[kChunks];
     uint32_t keys[kChunks];
@@ -626,7 +645,7 @@ __device__ static void score_job(const StepArgs &a, const ReqInfo &r, int b, int
         load_k_chunk(a, r, (ni < r.ntiles ? ni : i) * kScoreTile, lane, kb[0], ni < r.ntiles);
       }
       const float score = score_chunk<HG>(kb[c & 1], qa, wr, lane);
-      sbuf[(nbuf * kChunks + c) * 64 + lane] = score;
+      wbuf->score[(nbuf * kChunks + c) * 64 + lane] = score;
       keys[c] = topk_key(score);
       gsel[c] = __ballot(r.use_guard && valid && keys[c] <= r.guard_key);
       above[c] = 0;
@@ -669,6 +688,7 @@ __device__ static void score_job(const StepArgs &a, const ReqInfo &r, int b, int
     }
 
     // ---- top-k candidates above the selection guard: fixed slots of this item
+    // (buffered in LDS with the scores and written to item r.tile0 + i at the flush)
     if (r.use_guard) {
       int ng = 0;
 #pragma unroll
@@ -676,13 +696,13 @@ __device__ static void score_job(const StepArgs &a, const ReqInfo &r, int b, int
         if ((gsel[c] >> lane) & 1ull) {
           const int p = ng + __popcll(gsel[c] & lanemask_lt());
           if (p < kGuardSlots) {
-            a.sc.gcand_key[(int64_t)tau * kGuardSlots + p] = keys[c];
-            a.sc.gcand_idx[(int64_t)tau * kGuardSlots + p] = s_wave + c * 64 + lane;
+            wbuf->gkey[nbuf * kGuardSlots + p] = keys[c];
+            wbuf->gidx[nbuf * kGuardSlots + p] = s_wave + c * 64 + lane;
           }
         }
         ng += __popcll(gsel[c]);
       }
-      if (lane == 0) a.sc.gcand_cnt[tau] = ng;
+      if (lane == 0) wbuf->gcnt[nbuf] = ng;
     }
     if (PF) {
       p_i = i;
@@ -728,7 +748,7 @@ __device__ inline ReqInfo wave_uniform(const ReqInfo &x) {
 // reaches without waiting on a later one.
 template <int HG, bool ANY_PF>
 __device__ static void score_wave(const StepArgs &a, const ReqInfo *s_req, int w, PendItem *pq,
-                                  float *sbuf) {
+                                  WaveBuf *wbuf) {
   const int lane = lane_id();
   const int S = a.sc.misc[M_SLOTS];
   const int W = a.score_waves;
@@ -740,9 +760,9 @@ __device__ static void score_wave(const StepArgs &a, const ReqInfo *s_req, int w
     const ReqInfo r = wave_uniform(s_req[b]);
     const int k = slot - r.slot0;
     if (ANY_PF && r.active)
-      score_job<HG, true>(a, r, b, k, t, nfree, pq, sbuf);
+      score_job<HG, true>(a, r, b, k, t, nfree, pq, wbuf);
     else
-      score_job<HG, false>(a, r, b, k, t, nfree, pq, sbuf);
+      score_job<HG, false>(a, r, b, k, t, nfree, pq, wbuf);
   }
 }
 
@@ -753,7 +773,7 @@ template <int HG, bool ANY_PF>
 __global__ __launch_bounds__(512) void k_score(StepArgs a) {
   __shared__ ReqInfo s_req[kMaxBatch];
   __shared__ PendItem s_pend[ANY_PF ? kScoreWaves : 1][ANY_PF ? kPending : 1];
-  __shared__ float s_scores[kScoreWaves][kDeferItems * kScoreTile];  // 64 KB
+  __shared__ WaveBuf s_wbuf[kScoreWaves];  // 81 KB
   __shared__ int s_left, s_dead;
   const int tid = threadIdx.x;
   // the status and the request table in one round trip; the block decides as one
@@ -770,7 +790,7 @@ __global__ __launch_bounds__(512) void k_score(StepArgs a) {
     // then known to be wave-uniform and lives in scalar registers
     score_wave<HG, ANY_PF>(a, s_req,
                            __builtin_amdgcn_readfirstlane((int)blockIdx.x * kScoreWaves + wid),
-                           &s_pend[ANY_PF ? wid : 0][0], &s_scores[wid][0]);
+                           &s_pend[ANY_PF ? wid : 0][0], &s_wbuf[wid]);
     if (lane_id() == 0 && atomicSub(&s_left, 1) == 1)
       __hip_atomic_fetch_add(&a.sc.misc[M_SCORE_DONE], 1, __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
