@@ -32,7 +32,9 @@
 // K straight into MFMA operand registers (no LDS staging: every K byte is used by
 // exactly one lane), keeps the next 64 tokens' loads in flight while it computes,
 // applies ReLU and the head weights in registers and reduces the 64 heads with
-// two cross-lane adds.
+// two cross-lane adds.  Scores (and selection-guard candidates) collect in the
+// wave's LDS and are written out at the end of its job, so no global store sits
+// between its K loads.
 //
 // Work assignment.  Most workgroups score (eight waves each); a few only copy.
 // Request b gets wb scoring waves (chosen so that no wave takes more 256-token
