@@ -1,5 +1,5 @@
-// Eviction, allocation and recall in one kernel; standalone recall, step
-// advance and initialisation.
+// Eviction, allocation and recall in one kernel, alone or fused with top-k for
+// the layer step; standalone recall, step advance and initialisation.
 //
 // Eviction (ECHO review, "Core method / in-graph per-layer cache management":
 // low-priority entries are evicted after the selected tokens are protected)
@@ -20,7 +20,13 @@
 // workgroups; only a boundary in the clamped bin 0 (slots idle for 4096 steps or
 // more) needs the exact (priority, slot) select, done by one workgroup between
 // two more barriers.  A second look-back over the workgroups ranks the free
-// slots for the allocation, and each workgroup copies the rows it allocated.
+// slots for the allocation; after a last barrier the workgroups split the recall
+// list evenly and copy its rows.
+//
+// In the layer step the same management workgroups run inside one launch with
+// the per-request top-k workgroups (they wait for a count of finished
+// selections) and with copy workgroups that finish the step's prefetch copy from
+// the launch's start to its end.
 #include "topk.h"
 
 namespace echo {
