@@ -66,23 +66,25 @@ __device__ inline void copy_batch(const StepArgs &a, int my_h, int my_g, int n) 
   }
 }
 
-// What a copy wave reads before a batch, in one round trip: the stop flag, the
-// entries of the block's ranks not yet copied (lane l: rank r0 + done + l) and the
-// request's final count.
+// What a copy wave reads before a batch, in one round trip: the stop and slow
+// counters, the entries of the block's ranks not yet copied (lane l: rank
+// r0 + done + l) and the request's final count.
 struct CopyView {
-  int sv;
+  int sv, sl;
   uint64_t e, fin;
 };
 
 __device__ inline CopyView copy_view(const StepArgs &a, const int32_t *stop, int b, int r0,
-                                     int done) {
+                                     int done, const int32_t *slow = nullptr) {
   const int lane = lane_id();
   const int rank = r0 + done + lane;
   const bool mine = lane < kCopyRows - done && rank < a.K;
   const int r_any = r0 + done < a.K ? r0 + done : a.K - 1;
   CopyView v;
   v.sv = 0;
+  v.sl = 0x7FFFFFFF;
   if (stop) v.sv = __hip_atomic_load(stop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (slow) v.sl = __hip_atomic_load(slow, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // every lane loads (lanes past the block reread its first entry): no branch
   v.e = __hip_atomic_load(&a.sc.pfq[(int64_t)b * a.K + (mine ? rank : r_any)], __ATOMIC_RELAXED,
                           __HIP_MEMORY_SCOPE_AGENT);
@@ -95,13 +97,16 @@ __device__ inline CopyView copy_view(const StepArgs &a, const int32_t *stop, int
 // blocks (blocks i_cur + q, i_cur + q + m, ...; part 0 resumes the saved partial
 // block).  With `stop` set, the wave leaves before its next batch once *stop
 // reaches `stop_target`, saving its progress (m must be 1); otherwise it copies
-// every row it owns.  A batch that completes its block reads the next block's
-// entries before its own host reads, so that round trip overlaps the copy; a
-// complete block is left without reading it again.  The loop keeps to register
+// every row it owns.  With `slow` set, batches stay as small as a stoppable
+// wave's while *slow is below `slow_target` (fewer host reads in flight while
+// latency-bound work runs beside the copy).  A batch that completes its block
+// reads the next block's entries before its own host reads, so that round trip
+// overlaps the copy; a complete block is left without reading it again.  The loop keeps to register
 // arithmetic otherwise (block -> request and rank stepped without division, each
 // request's cap in a lane register): a batch is about one host-link round trip.
 __device__ inline void copy_worker(const StepArgs &a, const ReqInfo *req, int w, int q, int m,
-                                   const int32_t *stop, int stop_target) {
+                                   const int32_t *stop, int stop_target,
+                                   const int32_t *slow = nullptr, int slow_target = 0) {
   const int lane = lane_id();
   w = __builtin_amdgcn_readfirstlane(w);  // one wave, one copy worker
   const int NW = a.copy_waves, B = a.B;
@@ -130,7 +135,7 @@ __device__ inline void copy_worker(const StepArgs &a, const ReqInfo *req, int w,
   uint64_t t0 = 0;  // start of the current wait for entries (0: not waiting)
   int nap = 1;  // polls back off while nothing is ready: idle waves must not flood memory
   bool ahead = false;  // `view` already holds block i's entries (read during the last batch)
-  CopyView view = {0, 0, 0};
+  CopyView view = {0, 0x7FFFFFFF, 0, 0};
   while (x < nblocks) {
     const int r0 = g * kCopyRows;
     if (r0 >= __builtin_amdgcn_readlane(lcap, b)) {
@@ -139,7 +144,7 @@ __device__ inline void copy_worker(const StepArgs &a, const ReqInfo *req, int w,
       ahead = false;
       continue;
     }
-    if (!ahead) view = copy_view(a, stop, b, r0, done);
+    if (!ahead) view = copy_view(a, stop, b, r0, done, slow);
     ahead = false;
     if (stop && view.sv >= stop_target) {
       if (lane == 0) {  // hand the rest to the next kernel of the step
@@ -161,7 +166,7 @@ __device__ inline void copy_worker(const StepArgs &a, const ReqInfo *req, int w,
     // (host reads in flight slow the scoring waves' HBM stream on every compute
     // unit, not only their own).
     const int ready = min(min(__ffsll((unsigned long long)~have) - 1, need - done),
-                          stop ? kCopyRowsStoppable : kCopyRows);
+                          (stop || view.sl < slow_target) ? kCopyRowsStoppable : kCopyRows);
     if (ready > 0) {
       const int rank = r0 + done + lane;
       const int cb = b, d0 = done;
@@ -172,7 +177,7 @@ __device__ inline void copy_worker(const StepArgs &a, const ReqInfo *req, int w,
         advance();
         done = 0;
         if (x < nblocks) {
-          view = copy_view(a, stop, b, g * kCopyRows, 0);
+          view = copy_view(a, stop, b, g * kCopyRows, 0, slow);
           ahead = true;
         }
       }
