@@ -105,6 +105,23 @@ def stored_traffic():
         return None
 
 
+def replay_median_ms(graph, n):
+    """Median duration of n replays of `graph`, each timed with events on the current
+    stream after the previous one has finished."""
+    import torch
+    times = []
+    for _ in range(n):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    times.sort()
+    return 0.5 * (times[(n - 1) // 2] + times[n // 2])
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -298,9 +315,13 @@ def main():
     # Threshold +inf: the same kernel scores every token but prefetches nothing and
     # changes no cache state, so this isolates the HBM-bound scoring stream.
     nso = min(L, 16)
-    nrep = 10  # replays timed together (the mean over them is steadier than one)
-    # back to back in a graph, as the step runs its kernels: nrep replays of nso
-    # calls (layers 0..nso-1), events around them on the stream they are replayed on
+    nrep = 10
+    # back to back in a graph, as the step runs its kernels: nso calls (layers
+    # 0..nso-1) per replay.  Each of nrep replays is timed on its own with events on
+    # the stream it is replayed on, after the previous one has finished, and the
+    # median is taken.  (Replays launched back to back vary between replays by about
+    # 10%: the scoring graph runs once per layer-step in the decode step, between
+    # link-bound kernels, not back to back with itself.)
     gso = torch.cuda.CUDAGraph()
     with torch.cuda.stream(cs):
         with torch.cuda.graph(gso, stream=cs):
@@ -310,21 +331,15 @@ def main():
                         "indexer")
     gso.replay()
     torch.cuda.synchronize()
-    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s0.record()
-    for _ in range(nrep):
-        gso.replay()
-    s1.record()
-    torch.cuda.synchronize()
-    so_ms = s0.elapsed_time(s1) / (nso * nrep)
+    so_ms = replay_median_ms(gso, nrep) / nso
     del gso
     so_gbps = total_tok * BYTES_PER_SCORED_TOKEN / (so_ms * 1e-3) / 1e9
     log(f"[bench] indexer, prefetch off: {so_ms:.4f} ms = {so_gbps:.0f} GB/s "
         f"({so_gbps / HBM_PEAK_GBPS:.1%} of HBM peak; {nso} calls back to back in a graph, "
-        f"{nrep} replays)")
+        f"median of {nrep} replays)")
     # the scoring kernel alone: the same graph with only the prologue of every call
-    # (echo_indexer_begin), events around nrep replays; the difference per call is
-    # the scoring kernel's launch duration in the graph
+    # (echo_indexer_begin), timed the same way; the difference per call is the
+    # scoring kernel's launch duration in the graph
     gbg = torch.cuda.CUDAGraph()
     with torch.cuda.stream(cs):
         with torch.cuda.graph(gbg, stream=cs):
@@ -333,19 +348,13 @@ def main():
                                                abi.ECHO_THETA_POS_INF, cs.cuda_stream), "begin")
     gbg.replay()
     torch.cuda.synchronize()
-    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    b0.record()
-    for _ in range(nrep):
-        gbg.replay()
-    b1.record()
-    torch.cuda.synchronize()
-    begin_ms = b0.elapsed_time(b1) / (nso * nrep)
+    begin_ms = replay_median_ms(gbg, nrep) / nso
     del gbg
     ks_ms = so_ms - begin_ms
     ks_gbps = total_tok * BYTES_PER_SCORED_TOKEN / (ks_ms * 1e-3) / 1e9
     log(f"[bench] scoring kernel (k_score, prefetch off): {ks_ms:.4f} ms per launch = "
         f"{ks_gbps:.0f} GB/s ({ks_gbps / HBM_PEAK_GBPS:.1%} of HBM peak): {so_ms:.4f} ms per "
-        f"call less {begin_ms:.4f} ms per prologue, both graph-timed over {nrep} x {nso} calls")
+        f"call less {begin_ms:.4f} ms per prologue, both the median of {nrep} replays of {nso} calls")
 
     if args.pmc_calibrate:  # a plain copy of known size for the HBM-traffic counters
         cal_src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -508,15 +517,15 @@ def main():
                    "threshold_mode": args.mode},
         "roofline": {"kernel": "lightning-indexer scoring kernel k_score<4,false> (prefetch "
                                f"off): a graph of {nso} echo_indexer_prefetch calls less a "
-                               f"graph of their {nso} prologues, each replayed {nrep} times, "
-                               "event-timed per launch on the replay stream",
+                               f"graph of their {nso} prologues, each the median of {nrep} "
+                               "replays timed one at a time with events on the replay stream",
                      "bound": "hbm", "achieved": round(ks_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(ks_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "bytes_per_launch": idx_bytes,
                      "avg_launch_ms": round(ks_ms, 5)},
         "indexer_call": {"what": "echo_indexer_prefetch with prefetch off = k_begin + "
                                  f"k_score<4,false>, per call over {nso} calls back to back "
-                                 f"in a graph, replayed {nrep} times",
+                                 f"in a graph, median of {nrep} replays",
                          "ms": round(so_ms, 5), "prologue_ms": round(begin_ms, 5),
                          "hbm_gbps": round(so_gbps, 1),
                          "frac_of_hbm_peak": round(so_gbps / HBM_PEAK_GBPS, 4)},
