@@ -74,6 +74,7 @@ class Rig:
             wl = wl.scaled(n_gpu=n_gpu or wl.n_gpu, n_host=n_host or wl.n_host,
                            cap_div=cap_div or wl.cap_div, top_k=top_k or wl.top_k)
         self.wl = wl
+        self.separate = False  # True: gpu_step makes the five separate calls
         self.inp = make_inputs(wl, layer=layer, device="cpu", seed=seed, steps=steps, ctx=ctx,
                                room=room)
         self.layer_id = layer
@@ -110,8 +111,25 @@ class Rig:
 
     # ------------------------------------------------------------ GPU calls
     def gpu_step(self, mode):
+        if self.separate:
+            self.gpu_step_separate(mode)
+            return
         R.check(abi.echo_layer_step(self.dims, self.layer.struct, self.batch.struct, self.ws.ws,
                                     mode, R.stream_handle()), "echo_layer_step")
+
+    def gpu_step_separate(self, mode):
+        """The same step as the five calls echo_layer_step fuses: indexer + prefetch,
+        top-k (with the EMA update in mode EMA), protect/evict/allocate, recall, and
+        the step-counter advance."""
+        s = R.stream_handle()
+        L, Bt, W = self.layer.struct, self.batch.struct, self.ws.ws
+        R.check(abi.echo_indexer_prefetch(self.dims, L, Bt, W, mode, s), "echo_indexer_prefetch")
+        theta = self.layer.theta.data_ptr() if mode == MODE_EMA else None
+        R.check(abi.echo_topk(self.dims, self.ws.scores.data_ptr(), self.dims.max_ctx, Bt, W,
+                              theta, s), "echo_topk")
+        R.check(abi.echo_cache_alloc_evict(self.dims, L, Bt, W, s), "echo_cache_alloc_evict")
+        R.check(abi.echo_recall(self.dims, L, W, s), "echo_recall")
+        R.check(abi.echo_step_advance(L, W, s), "echo_step_advance")
 
     def gpu_scores(self) -> np.ndarray:
         torch.cuda.current_stream().synchronize()

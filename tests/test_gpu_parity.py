@@ -107,6 +107,27 @@ def test_graph_replay_matches_eager():
     graph.close()
 
 
+@pytest.mark.parametrize("mode", [H.MODE_EMA, H.MODE_NEG_INF, H.MODE_POS_INF])
+def test_separate_calls_match_the_oracle(mode):
+    # echo_indexer_prefetch -> echo_topk -> echo_cache_alloc_evict -> echo_recall ->
+    # echo_step_advance, one call each, step by step against the oracle (the same
+    # results echo_layer_step gives in one call)
+    wl = get("single_layer").scaled(rho=0.6, steps=6)
+    ctx = [3000, 1777, 2561]
+    _say(f"separate calls: 64x128 ragged {ctx}, mode {mode}")
+    rig = H.Rig(wl, steps=6, ctx=ctx, n_gpu=3 * 256 + 2 * 120, n_host=8000, top_k=256,
+                cap_div=64)
+    rig.separate = True
+    for _ in range(6):
+        out, _ = rig.step_and_compare(mode)
+        assert out["status"] == 0
+    assert sum(int(o["n_evict"]) for _, o in rig.history) > 0
+    assert sum(int(o["n_miss"].sum()) for _, o in rig.history) > 0
+    if mode != H.MODE_POS_INF:
+        assert sum(int(o["n_pf"].sum()) for _, o in rig.history) > 0
+    rig.close()
+
+
 @pytest.mark.parametrize("n,k", [(5000, 256), (256, 256), (100, 256), (257, 256), (9000, 2048)])
 def test_topk_external_scores_with_ties(n, k):
     rng = np.random.default_rng(n + k)
