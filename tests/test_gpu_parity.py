@@ -128,6 +128,24 @@ def test_separate_calls_match_the_oracle(mode):
     rig.close()
 
 
+@pytest.mark.parametrize("mode", [H.MODE_EMA, H.MODE_NEG_INF])
+def test_largest_top_k_with_eviction(mode):
+    # top_k = 4096, the largest the library takes, with contexts k - 1, k, k + 1 and
+    # 9000, and a pool that holds one step's selection plus a little: later steps
+    # evict
+    wl = get("tiny").scaled(rho=0.7)
+    ctx = [4095, 4096, 4097, 9000]
+    _say(f"top_k 4096, ctx {ctx}, mode {mode}")
+    rig = H.Rig(wl, steps=4, ctx=ctx, n_gpu=17_500, n_host=24_000, top_k=4096, cap_div=64)
+    for _ in range(4):
+        out, _ = rig.step_and_compare(mode)
+        assert out["status"] == 0
+        assert list(out["n_sel"][:4]) == [4095, 4096, 4096, 4096]
+    assert sum(int(o["n_evict"]) for _, o in rig.history) > 0
+    assert sum(int(o["n_pf"].sum()) for _, o in rig.history) > 0
+    rig.close()
+
+
 @pytest.mark.parametrize("n,k", [(5000, 256), (256, 256), (100, 256), (257, 256), (9000, 2048)])
 def test_topk_external_scores_with_ties(n, k):
     rng = np.random.default_rng(n + k)
