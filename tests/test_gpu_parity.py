@@ -128,6 +128,23 @@ def test_separate_calls_match_the_oracle(mode):
     rig.close()
 
 
+@pytest.mark.parametrize("heads,dim", [(20, 64), (33, 96), (48, 128), (1, 32)])
+def test_head_groups_and_dims(heads, dim):
+    # the scoring kernel runs 1-4 groups of 16 heads (padded) over head dims of 32-128:
+    # two and three groups, a group padded from one head, and every dim but the
+    # tiny (4 x 32) and full (64 x 128) shapes other tests use
+    wl = get("tiny").scaled(heads=heads, head_dim=dim, rho=0.7)
+    ctx = [1500, 3001, 257]
+    _say(f"{heads} heads x {dim}, ctx {ctx}")
+    rig = H.Rig(wl, steps=4, ctx=ctx, n_gpu=3 * 256 + 2 * 120, n_host=8000, top_k=256,
+                cap_div=64)
+    for _ in range(4):
+        out, _ = rig.step_and_compare(H.MODE_EMA)
+        assert out["status"] == 0
+    assert sum(int(o["n_evict"]) for _, o in rig.history) > 0
+    rig.close()
+
+
 @pytest.mark.parametrize("mode", [H.MODE_EMA, H.MODE_NEG_INF])
 def test_largest_top_k_with_eviction(mode):
     # top_k = 4096, the largest the library takes, with contexts k - 1, k, k + 1 and
