@@ -62,6 +62,15 @@ def test_prefill_4x32_small_heads():
     rig.close()
 
 
+@pytest.mark.parametrize("heads,dim", [(20, 64), (33, 96)])
+def test_prefill_head_and_dim_shapes(heads, dim):
+    _say(f"prefill {heads}x{dim}: N 1000, C 20, k 64")
+    wl = get("tiny").scaled(heads=heads, head_dim=dim, rho=0.8)
+    rig = H.PrefillRig(wl, N=1000, C=20, chunks=3, n_gpu=1500, n_host=1024, top_k=64)
+    _run(rig, 3)
+    rig.close()
+
+
 def test_prefill_history_not_longer_than_k():
     _say("prefill: N 200 <= k 256")
     wl = get("prefill").scaled(rho=0.9)
