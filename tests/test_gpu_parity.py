@@ -145,6 +145,25 @@ def test_head_groups_and_dims(heads, dim):
     rig.close()
 
 
+def test_layers_share_one_workspace():
+    # as in a decode step: three layers (their own K, queries, pools and metadata)
+    # step in turn through one workspace, each against its own oracle layer
+    wl = get("single_layer").scaled(rho=0.6, steps=4)
+    ctx = [3000, 1777, 2561]
+    _say(f"3 layers, one workspace, ctx {ctx}")
+    rigs = [H.Rig(wl, steps=4, ctx=ctx, n_gpu=3 * 256 + 2 * 120, n_host=8000, top_k=256,
+                  cap_div=64, layer=l) for l in range(3)]
+    for r in rigs[1:]:
+        r.ws = rigs[0].ws
+    for _ in range(4):
+        for r in rigs:
+            out, _ = r.step_and_compare(H.MODE_EMA)
+            assert out["status"] == 0
+    for r in rigs:
+        assert sum(int(o["n_evict"]) for _, o in r.history) > 0
+        r.close()
+
+
 @pytest.mark.parametrize("mode", [H.MODE_EMA, H.MODE_NEG_INF])
 def test_largest_top_k_with_eviction(mode):
     # top_k = 4096, the largest the library takes, with contexts k - 1, k, k + 1 and
