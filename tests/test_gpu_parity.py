@@ -164,6 +164,47 @@ def test_layers_share_one_workspace():
         r.close()
 
 
+def test_two_layer_graph_matches_eager():
+    # the decode step as the benchmark runs it: several layers sharing one workspace,
+    # captured in one graph; every replay equals the same calls made eagerly
+    wl = get("tiny").scaled(rho=0.8)
+    kw = dict(steps=5, ctx=[2000, 900], n_gpu=1600, n_host=4096, cap_div=32)
+    eager = [H.Rig(wl, layer=l, **kw) for l in range(2)]
+    graph = [H.Rig(wl, layer=l, **kw) for l in range(2)]
+    eager[1].ws = eager[0].ws
+    graph[1].ws = graph[0].ws
+    _say("two layers, one workspace, graph against eager")
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for r in graph:
+                r.gpu_step(H.MODE_EMA)
+    torch.cuda.synchronize()
+    for t in range(5):
+        for r in eager:
+            r.gpu_step(H.MODE_EMA)
+        g.replay()
+        torch.cuda.synchronize()
+        for re_, rg in zip(eager, graph):
+            a, b = re_.layer.state(), rg.layer.state()
+            for key in ("h2g", "g2h", "prio", "free", "theta", "idxbuf"):
+                assert np.array_equal(a[key], b[key]), (t, key)
+            assert a["t"] == b["t"] == t + 1
+            assert torch.equal(re_.layer.gpu_kv, rg.layer.gpu_kv)
+        oa, ob = eager[0].ws.read(2), graph[0].ws.read(2)  # the last layer's outputs
+        assert oa["status"] == ob["status"] == 0
+        for key in ("n_sel", "n_pf", "n_miss", "kth"):
+            assert np.array_equal(oa[key], ob[key]), (t, key)
+        for b in range(2):
+            for key, n in (("sel_tok", "n_sel"), ("sel_slot", "n_sel"), ("pf_tok", "n_pf"),
+                           ("pf_slot", "n_pf"), ("miss_tok", "n_miss")):
+                m = int(oa[n][b])
+                assert np.array_equal(oa[key][b, :m], ob[key][b, :m]), (t, key, b)
+    for r in eager + graph:
+        r.close()
+
+
 @pytest.mark.parametrize("mode", [H.MODE_EMA, H.MODE_NEG_INF])
 def test_largest_top_k_with_eviction(mode):
     # top_k = 4096, the largest the library takes, with contexts k - 1, k, k + 1 and
