@@ -126,8 +126,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the decode hot "
-              "path shards by request, one independent copy per GPU, and this build measures "
-              "the single-GPU share.", file=sys.stderr)
+              "path shards by request, one independent copy per GPU, and this benchmark "
+              "measures the single-GPU share.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -165,3 +165,15 @@ def test_prefill_workspace_size_and_bind():
     assert all(p % 256 == 0 and base <= p < base + n for p in ptrs)
     assert len(set(ptrs)) == len(ptrs) and ptrs == sorted(ptrs)
     assert pws.max_chunk == 64 and pws.internal + pws.internal_bytes == base + n
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # one process per GPU, each with its own requests: the benchmark measures one GPU
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr and r.stdout == ""
