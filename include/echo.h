@@ -20,7 +20,7 @@
  *    frees or synchronizes; each call validates its arguments on the host, enqueues
  *    kernels on `stream` and returns.  Every call can be captured in a hipGraph.
  *  - Host-side return codes: ECHO_OK, or ECHO_EINVAL (bad argument or shape; nothing
- *    was enqueued), ECHO_EUNSUPPORTED (a shape this build has no kernel for), or
+ *    was enqueued), ECHO_EUNSUPPORTED (a shape this library has no kernel for), or
  *    ECHO_EHIP (a launch failed).
  *  - Errors found on the device (capacity, bad device-side lengths, a stuck wait)
  *    are written to `ws->status`: the first error wins and stays until
@@ -52,7 +52,7 @@ enum {
   ECHO_OK = 0,
   ECHO_EINVAL = -1,       /* argument or shape check failed                    */
   ECHO_EHIP = -2,         /* a kernel launch failed                            */
-  ECHO_EUNSUPPORTED = -3, /* shape with no kernel in this build                */
+  ECHO_EUNSUPPORTED = -3, /* shape with no kernel in this library              */
   ECHO_ECAPACITY = -4,    /* device: free + evictable slots < missed tokens    */
   ECHO_ETIMEOUT = -5,     /* device: a cross-workgroup wait exceeded 1 s       */
   ECHO_EDEVARG = -6       /* device: ctx_len/host_base out of range or overlap */
@@ -93,7 +93,7 @@ enum {
   ECHO_PF_NCOUNTS = 8
 };
 
-/* Shapes.  Supported by this build: 1 <= n_heads <= 64; head_dim in {32, 64, 96,
+/* Shapes.  Supported by this library: 1 <= n_heads <= 64; head_dim in {32, 64, 96,
  * 128}; 1 <= top_k <= 4096; latent_dim*2 a multiple of 16 bytes; n_host < 2^31
  * and a multiple of 16;
  * 1 <= n_gpu < 2^31; 1 <= max_batch <= 64; 1 <= max_ctx < 2^31; prefetch_cap_div
