@@ -417,28 +417,34 @@ int orc_layer_step(const orc_cfg *c, orc_state *st, int B,
  * h >= n_host, or h inside another request's range [host_base[o],
  * host_base[o] + ctx[o]] counting that request's own new token) gives
  * ORC_ECAPACITY, a host id some slot already maps (h2g[h] != -1) gives
- * ORC_EDEVARG; the first such request decides and nothing is written. */
+ * ORC_EDEVARG; the first such request decides and nothing is written.
+ * A batch row with ctx[b] = 0 is empty (never admitted, or released): it takes
+ * no token, is not checked, does not grow, and its stale host_base occupies no
+ * range in the other requests' checks. */
 int orc_append(int B, int D, int latent, int64_t n_host, int32_t max_ctx,
                const int32_t *host_base, int32_t *ctx, const int32_t *h2g,
                const uint8_t *k_new, const uint16_t *lat_new, uint8_t *kidx,
                uint16_t *host_kv, int advance) {
   for (int b = 0; b < B; ++b) {
+    if (ctx[b] == 0) continue; /* an empty row */
     const int64_t h = (int64_t)host_base[b] + ctx[b];
     if (ctx[b] < 0 || ctx[b] >= max_ctx || host_base[b] < 0 || h >= n_host) return ORC_ECAPACITY;
     for (int o = 0; o < B; ++o) {
-      if (o == b) continue;
+      if (o == b || ctx[o] == 0) continue;
       if (h >= host_base[o] && h < (int64_t)host_base[o] + ctx[o] + 1) return ORC_ECAPACITY;
     }
     if (h2g[h] != -1) return ORC_EDEVARG;
   }
   for (int b = 0; b < B; ++b) {
+    if (ctx[b] == 0) continue;
     const int64_t h = (int64_t)host_base[b] + ctx[b];
     memcpy(kidx + h * D, k_new + (int64_t)b * D, (size_t)D);
     if (host_kv)
       memcpy(host_kv + h * latent, lat_new + (int64_t)b * latent, (size_t)latent * 2);
   }
   if (advance)
-    for (int b = 0; b < B; ++b) ctx[b] += 1;
+    for (int b = 0; b < B; ++b)
+      if (ctx[b] != 0) ctx[b] += 1;
   return ORC_OK;
 }
 

@@ -75,6 +75,14 @@ MUTANTS = {
                            "    if (st->h2g[h] >= 0) {\n      ;\n    } else {\n"
                            "      const int32_t g = F[next++];\n      install(c, st, h, g, host_kv);\n"
                            "      o->miss_h"),
+    "append_writes_empty_rows": ("    if (ctx[b] == 0) continue; /* an empty row */\n", ""),
+    "append_empty_row_blocks_neighbours": ("      if (o == b || ctx[o] == 0) continue;",
+                                           "      if (o == b) continue;"),
+    "append_writes_empty_row_bytes": ("  for (int b = 0; b < B; ++b) {\n    if (ctx[b] == 0) continue;\n"
+                                      "    const int64_t h = (int64_t)host_base[b] + ctx[b];\n    memcpy",
+                                      "  for (int b = 0; b < B; ++b) {\n"
+                                      "    const int64_t h = (int64_t)host_base[b] + ctx[b];\n    memcpy"),
+    "append_grows_empty_rows": ("      if (ctx[b] != 0) ctx[b] += 1;", "      ctx[b] += 1;"),
     "append_ignores_neighbours": ("if (h >= host_base[o] && h < (int64_t)host_base[o] + ctx[o] + 1) "
                                   "return ORC_ECAPACITY;",
                                   "if (0) return ORC_ECAPACITY;"),

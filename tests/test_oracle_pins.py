@@ -445,6 +445,33 @@ def test_append_checks_room_and_mapping_and_writes_nothing_on_error():
         O.ECAPACITY
 
 
+def test_append_skips_empty_rows_and_their_stale_ranges():
+    # Hand-derived.  Row 1 is empty (ctx 0, released) and its stale host_base 10 is
+    # exactly request 0's next id; row 3 is empty with a stale base whose id is mapped.
+    # Rows 0 and 2 take their tokens at ids 10 and 37; the empty rows take nothing,
+    # block nothing and do not grow.
+    D, latent, n_host = 4, 8, 64
+    base = np.array([0, 10, 32, 20], np.int32)
+    ctx = np.array([10, 0, 5, 0], np.int32)
+    kidx = np.zeros((n_host, D), np.uint8)
+    host = np.zeros((n_host, latent), np.uint16)
+    k_new = (np.arange(4 * D, dtype=np.uint8).reshape(4, D) + 1)
+    lat_new = (np.arange(4 * latent, dtype=np.uint16).reshape(4, latent) + 100)
+    h2g = np.full(n_host, -1, np.int32)
+    h2g[20] = 3
+    assert O.append(base, ctx, h2g, k_new, lat_new, kidx, host, max_ctx=64) == O.OK
+    assert ctx.tolist() == [11, 0, 6, 0]
+    assert np.array_equal(kidx[10], k_new[0]) and np.array_equal(host[10], lat_new[0])
+    assert np.array_equal(kidx[37], k_new[2]) and np.array_equal(host[37], lat_new[2])
+    written = np.nonzero(kidx.any(1) | host.any(1))[0].tolist()
+    assert written == [10, 37]
+    # without advance: the same two rows again, contexts unchanged
+    ctx2 = np.array([10, 0, 5, 0], np.int32)
+    assert O.append(base, ctx2, h2g, k_new, lat_new, kidx, host, max_ctx=64,
+                    advance=False) == O.OK
+    assert ctx2.tolist() == [10, 0, 5, 0]
+
+
 # ---------------------------------------------------------- attention input
 # R11: rows that name themselves.  Host row h holds h's own bytes, so every
 # gathered row must decode to host_base[b] + sel_tok[b][i]; rows past n_sel are 0.
