@@ -32,15 +32,18 @@ __global__ __launch_bounds__(kAppendThreads) void k_append(StepArgs a, const uin
   if (st0 != 0) return;
   // Checks, lane b for request b: room below max_ctx and n_host, no collision with
   // another request's range (counting that request's own new token), and a host id
-  // that no slot maps yet.  The lowest failing request decides the status.
+  // that no slot maps yet.  The lowest failing request decides the status.  A row
+  // with ctx 0 is empty (released or never admitted): it is not checked, takes no
+  // token, and its stale host_base blocks nobody.
   if (tid < kWave) {
     int code = 0;
-    if (tid < a.B) {
+    if (tid < a.B && s_ctx[tid] != 0) {
       const int s = s_ctx[tid];
       const int64_t h = (int64_t)s_base[tid] + s;
       if (s < 0 || s >= a.max_ctx || s_base[tid] < 0 || h >= a.n_host) code = ECHO_ECAPACITY;
       for (int o = 0; o < a.B && code == 0; ++o)
-        if (o != tid && h >= s_base[o] && h < (int64_t)s_base[o] + s_ctx[o] + 1)
+        if (o != tid && s_ctx[o] != 0 && h >= s_base[o] &&
+            h < (int64_t)s_base[o] + s_ctx[o] + 1)
           code = ECHO_ECAPACITY;
       if (code == 0 && a.h2g[h] != -1) code = ECHO_EDEVARG;
     }
@@ -60,6 +63,7 @@ __global__ __launch_bounds__(kAppendThreads) void k_append(StepArgs a, const uin
   const int D = a.D;
   for (int i = tid; i < a.B * D; i += kAppendThreads) {
     const int b = i / D, d = i - b * D;
+    if (s_ctx[b] == 0) continue;
     const int64_t h = (int64_t)s_base[b] + s_ctx[b];
     const int64_t off = 16LL * D * (h >> 4) + 8LL * D * ((d & 31) >> 4) + 256LL * (d >> 5) +
                         16 * (h & 15) + (d & 15);
@@ -71,10 +75,11 @@ __global__ __launch_bounds__(kAppendThreads) void k_append(StepArgs a, const uin
   uint4 *dst = (uint4 *)const_cast<uint16_t *>(a.host_kv);
   for (int i = tid; i < a.B * cpr; i += kAppendThreads) {
     const int b = i / cpr, c = i - b * cpr;
+    if (s_ctx[b] == 0) continue;
     const int64_t h = (int64_t)s_base[b] + s_ctx[b];
     dst[h * cpr + c] = src[i];
   }
-  if (advance && tid < a.B) ctx_io[tid] = s_ctx[tid] + 1;
+  if (advance && tid < a.B && s_ctx[tid] != 0) ctx_io[tid] = s_ctx[tid] + 1;
 }
 
 hipError_t launch_append(const StepArgs &a, const uint8_t *k_new, const uint16_t *lat_new,

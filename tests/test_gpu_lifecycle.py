@@ -174,3 +174,31 @@ def test_release_at_scale_with_eviction_pressure():
         _say(f"  step {t}: missed {int(out['n_miss'].sum())}, evicted {int(o['n_evict'])}")
         _lossless(rig, out)
     rig.close()
+
+
+@pytest.mark.parametrize("mode", [H.MODE_EMA, H.MODE_NEG_INF])
+def test_append_skips_released_row_until_readmitted(mode):
+    # Request 1 (host ids 3008 ..) is cancelled at step 2.  The decode appends that
+    # follow must leave its empty row alone (no token, no growth), and its stale base
+    # must not block request 0, which grows into ids 3008 .. 3011 from step 4 on.
+    # At step 5 request 1 is admitted again, at 3024 (clear of request 0's growth),
+    # over 1761 tokens whose keys are already in place, and grows with the others.
+    ctx = [3004, 1777, 2561]
+    steps = 8
+    _say(f"append around a released row, mode {mode}")
+    wl = get("single_layer").scaled(rho=0.6, steps=steps)
+    rig = H.Rig(wl, steps=steps, ctx=ctx, n_gpu=3 * 256 + 2 * 120, n_host=8000, top_k=256,
+                cap_div=64, max_ctx=max(ctx) + steps)
+    assert list(rig.base) == [0, 3008, 4800]
+    for t in range(steps):
+        if t == 2:
+            assert rig.release_and_compare([0, 1, 0]) == O.OK
+        if t == 5:
+            assert int(rig.ctx[1]) == 0
+            assert rig.admit_and_compare(1, 3024, 1761) == O.OK
+        out, o = rig.step_and_compare(mode)
+        _lossless(rig, out)
+        assert rig.append_and_compare() == O.OK
+        _say(f"  step {t}: ctx {list(rig.ctx)}, missed {list(out['n_miss'])}")
+    assert list(rig.ctx) == [3004 + steps, 1761 + 3, 2561 + steps]
+    rig.close()
