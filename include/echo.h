@@ -55,7 +55,8 @@ enum {
   ECHO_EUNSUPPORTED = -3, /* shape with no kernel in this library              */
   ECHO_ECAPACITY = -4,    /* device: free + evictable slots < missed tokens    */
   ECHO_ETIMEOUT = -5,     /* device: a cross-workgroup wait exceeded 1 s       */
-  ECHO_EDEVARG = -6       /* device: ctx_len/host_base out of range or overlap */
+  ECHO_EDEVARG = -6,      /* device: ctx_len/host_base out of range or overlap */
+  ECHO_ECORRUPT = -7      /* device: echo_check_invariants found a violation   */
 };
 
 /* Prefetch threshold modes.  EMA: the threshold is the exponential moving
@@ -302,7 +303,9 @@ int echo_gather(const echo_dims_t *dims, const echo_layer_t *layer, const echo_b
  * ECHO_ECAPACITY if a request has no room (ctx_len = max_ctx, host id >= n_host,
  * or the id falls in another request's range including its own new token),
  * ECHO_EDEVARG if a slot already maps the host id; the lowest such request
- * decides, and nothing is written. */
+ * decides, and nothing is written.  A row with ctx_len 0 is empty (released, or
+ * never admitted): it takes no token, does not grow, and its stale host_base
+ * takes no part in the other requests' room checks. */
 int echo_append(const echo_dims_t *dims, const echo_layer_t *layer, const int32_t *host_base,
                 int32_t *ctx_len, int32_t batch, const uint8_t *k_new,
                 const uint16_t *latent_new, const echo_ws_t *ws, int advance,
@@ -348,7 +351,18 @@ int echo_admit(const echo_dims_t *dims, const echo_layer_t *layer, int32_t *host
 
 /* Steps a0-a8 for one layer and one decode step, in order, on `stream`: indexer
  * + prefetch, top-k with the EMA update (mode EMA only), protect/evict/alloc,
- * recall, and the step-counter advance. */
+ * recall, and the step-counter advance.  The ECHO review's "Core method / decode"
+ * gives the order (prefetch while the indexer scores, exact top-k, then recall of
+ * every selected token that is still missing, before the sparse attention);
+ * "Core method / in-graph per-layer cache management" keeps every layer's
+ * management on the GPU inside the captured graph, with no per-layer CPU
+ * control; "Core method / prefetch inside the indexer pipeline" overlaps the
+ * prefetch transfers with scoring.  Here the prefetch copy also runs on through
+ * top-k and management and is complete when the call's last kernel ends.  The
+ * results equal those of echo_indexer_prefetch, echo_topk (theta updated in mode
+ * EMA), echo_cache_alloc_evict, echo_recall and echo_step_advance called in
+ * turn.  Errors: as those calls; ECHO_EUNSUPPORTED if the indexer launch cannot
+ * keep all of its workgroups resident. */
 int echo_layer_step(const echo_dims_t *dims, const echo_layer_t *layer,
                     const echo_batch_t *batch, const echo_ws_t *ws, int theta_mode,
                     hipStream_t stream);
@@ -452,6 +466,40 @@ int echo_prefill_copy(const echo_dims_t *dims, const echo_layer_t *layer,
                       const echo_prefill_ws_t *pws, int list, hipStream_t stream);
 
 /* ------------------------------------------------------------- diagnostics */
+
+/* Indices into the report of echo_check_invariants: violations of each kind, then
+ * two counts. */
+enum {
+  ECHO_INV_H2G = 0,       /* host ids whose h2g entry is neither -1 nor a slot mapping back */
+  ECHO_INV_G2H = 1,       /* slots whose g2h entry is neither -1 nor a host id mapping back */
+  ECHO_INV_FREE = 2,      /* slots where "free", "g2h = -1" and "prio = -1" disagree         */
+  ECHO_INV_PRIO = 3,      /* occupied slots with a priority outside [0, t)                  */
+  ECHO_INV_FREE_LIST = 4, /* free-list entries not free or not ascending, plus one if its
+                             length differs from the number of free slots                  */
+  ECHO_INV_SELECTED = 5,  /* selected tokens (batch given) not resident at their reported
+                             slot with priority t - 1                                      */
+  ECHO_INV_RESIDENT = 6,  /* count: host ids that hold a slot                               */
+  ECHO_INV_OCCUPIED = 7,  /* count: slots that are not free                                 */
+  ECHO_INV_WORDS = 8
+};
+
+/* Debug check of one layer's cache-management state (ECHO review, "Core method /
+ * in-graph per-layer cache management": free bitmap, priorities, index buffer and
+ * the two maps; "Systemic flaws": correctness depends on the order of
+ * allocation, protection, map updates and transfers).  Checks that h2g and g2h
+ * are mutual inverses, that free <=> g2h = -1 <=> prio = -1, that every occupied
+ * slot's priority lies in [0, t) with t = ctl[ECHO_CTL_STEP], and that
+ * idxbuf[0 .. ctl[ECHO_CTL_NFREE]) is the ascending list of all free slots.  With
+ * `batch` not NULL it also checks the last step's selection in ws (sel_tok,
+ * n_sel, sel_slot): every selected token holds the reported slot, with priority
+ * t - 1; pass it only right after a step that ended with status 0.
+ *   report: device int32 [ECHO_INV_WORDS], caller-owned, overwritten.
+ * If any violation is counted, or the resident and occupied counts differ,
+ * ws->status becomes ECHO_ECORRUPT (unless an earlier error holds it).  Reads the
+ * state only, and runs whatever the status.  Errors: ECHO_EINVAL (host checks). */
+int echo_check_invariants(const echo_dims_t *dims, const echo_layer_t *layer,
+                          const echo_batch_t *batch, const echo_ws_t *ws, int32_t *report,
+                          hipStream_t stream);
 
 /* Static string for a status code. */
 const char *echo_status_string(int code);

@@ -13,12 +13,15 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libecho.so")
 
 ECHO_OK, ECHO_EINVAL, ECHO_EHIP, ECHO_EUNSUPPORTED = 0, -1, -2, -3
-ECHO_ECAPACITY, ECHO_ETIMEOUT, ECHO_EDEVARG = -4, -5, -6
+ECHO_ECAPACITY, ECHO_ETIMEOUT, ECHO_EDEVARG, ECHO_ECORRUPT = -4, -5, -6, -7
 ECHO_THETA_EMA, ECHO_THETA_NEG_INF, ECHO_THETA_POS_INF = 0, 1, 2
 (ECHO_CNT_MISS, ECHO_CNT_EVICT, ECHO_CNT_FREE, ECHO_CNT_EVICTABLE, ECHO_CNT_FREE_END,
  ECHO_CNT_PREFETCH, ECHO_CNT_SHORTCUT) = range(7)
 ECHO_NCOUNTERS = 16
 ECHO_CTL_STEP, ECHO_CTL_NFREE, ECHO_CTL_WORDS = 0, 1, 4
+(ECHO_INV_H2G, ECHO_INV_G2H, ECHO_INV_FREE, ECHO_INV_PRIO, ECHO_INV_FREE_LIST, ECHO_INV_SELECTED,
+ ECHO_INV_RESIDENT, ECHO_INV_OCCUPIED) = range(8)
+ECHO_INV_WORDS = 8
 
 EXPORTS = ("echo_meta_bytes", "echo_ws_bytes", "echo_ws_bind", "echo_meta_init",
            "echo_ws_reset", "echo_kindex_pack", "echo_indexer_prefetch", "echo_topk",
@@ -26,7 +29,8 @@ EXPORTS = ("echo_meta_bytes", "echo_ws_bytes", "echo_ws_bind", "echo_meta_init",
            "echo_indexer_begin", "echo_indexer_score", "echo_append", "echo_gather", "echo_release", "echo_admit", "echo_prefill_ws_bytes",
            "echo_prefill_ws_bind", "echo_prefill_ws_reset", "echo_prefill_score",
            "echo_prefill_early",
-           "echo_prefill_select", "echo_prefill_copy", "echo_status_string")
+           "echo_prefill_select", "echo_prefill_copy", "echo_check_invariants",
+           "echo_status_string")
 
 P = C.c_void_p
 
@@ -117,6 +121,7 @@ def lib() -> C.CDLL:
             "echo_prefill_select": (C.c_int, [dp, lp, C.POINTER(echo_prefill_chunk_t),
                                               C.POINTER(echo_prefill_ws_t), P]),
             "echo_prefill_copy": (C.c_int, [dp, lp, C.POINTER(echo_prefill_ws_t), C.c_int, P]),
+            "echo_check_invariants": (C.c_int, [dp, lp, bp, wp, P, P]),
             "echo_status_string": (C.c_char_p, [C.c_int]),
         }
         for name, (res, args) in sigs.items():
@@ -250,6 +255,12 @@ def echo_prefill_select(dims, layer, chunk, pws, stream: int) -> int:
 def echo_prefill_copy(dims, layer, pws, which: int, stream: int) -> int:
     """which: 0 = the early installs, 1 = the later ones."""
     return lib().echo_prefill_copy(C.byref(dims), _ref(layer), C.byref(pws), which, stream)
+
+
+def echo_check_invariants(dims, layer, batch, ws, report: int, stream: int) -> int:
+    """report: device pointer to int32 [ECHO_INV_WORDS]; batch may be None."""
+    return lib().echo_check_invariants(C.byref(dims), _ref(layer), _ref(batch), _ref(ws),
+                                       report, stream)
 
 
 def echo_status_string(code: int) -> str:

@@ -612,6 +612,18 @@ int echo_kindex_pack(const echo_dims_t *dims, const uint8_t *rows, uint8_t *tile
   return ECHO_OK;
 }
 
+int echo_check_invariants(const echo_dims_t *dims, const echo_layer_t *layer,
+                          const echo_batch_t *batch, const echo_ws_t *ws, int32_t *report,
+                          hipStream_t stream) {
+  int rc = check_dims(dims);
+  if (rc != ECHO_OK) return rc;
+  if (!layer_ok(layer, false) || !ws_ok(ws) || !report) return ECHO_EINVAL;
+  if (batch && !batch_ok(*dims, batch)) return ECHO_EINVAL;
+  const StepArgs a = make_args(*dims, layer, batch, *ws, ECHO_THETA_POS_INF);
+  LAUNCH(launch_check_invariants(a, batch && batch->batch > 0 ? 1 : 0, report, stream));
+  return ECHO_OK;
+}
+
 const char *echo_status_string(int code) {
   switch (code) {
     case ECHO_OK: return "ok";
@@ -621,6 +633,7 @@ const char *echo_status_string(int code) {
     case ECHO_ECAPACITY: return "GPU pool too small for the missed tokens";
     case ECHO_ETIMEOUT: return "cross-workgroup wait timed out";
     case ECHO_EDEVARG: return "device-side batch arguments out of range or overlapping";
+    case ECHO_ECORRUPT: return "cache-management state violates an invariant";
     default: return "unknown status";
   }
 }

@@ -104,6 +104,8 @@ hipError_t launch_step_advance(const StepArgs &a, hipStream_t s);
 hipError_t launch_meta_init(const StepArgs &a, hipStream_t s);
 hipError_t launch_ws_reset(const echo_ws_t &ws, hipStream_t s);
 hipError_t launch_fill_zero(uint32_t *p, int64_t n_words, hipStream_t s);
+hipError_t launch_check_invariants(const StepArgs &a, int check_sel, int32_t *report,
+                                   hipStream_t s);
 hipError_t launch_kindex_pack(const uint8_t *rows, uint8_t *tiled, int64_t n_rows, int D,
                               hipStream_t s);
 

@@ -111,7 +111,7 @@ def test_null_arguments_are_rejected_before_any_launch():
 
 def test_status_strings():
     _lib_or_skip()
-    for code in (0, -1, -2, -3, -4, -5, -6):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
         s = abi.echo_status_string(code)
         assert s and s != "unknown status"
     assert abi.echo_status_string(42) == "unknown status"
@@ -143,6 +143,11 @@ def test_newer_entry_points_check_arguments_before_any_launch():
         assert fn(d, layer, chunk, pws, 0) == abi.ECHO_EINVAL
     assert abi.echo_prefill_copy(d, layer, pws, 0, 0) == abi.ECHO_EINVAL
     assert abi.echo_prefill_ws_reset(d, pws, 0) == abi.ECHO_EINVAL
+    # the invariant check: null layer, workspace or report, a batch above max_batch
+    assert abi.echo_check_invariants(d, None, None, ws, 1 << 30, 0) == abi.ECHO_EINVAL
+    assert abi.echo_check_invariants(d, layer, None, ws, 1 << 30, 0) == abi.ECHO_EINVAL
+    assert abi.echo_check_invariants(d, layer, abi.echo_batch_t(9, 1, 1), ws, 1 << 30, 0) == \
+        abi.ECHO_EINVAL
 
 
 def test_prefill_workspace_size_and_bind():
