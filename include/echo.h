@@ -56,7 +56,8 @@ enum {
   ECHO_ECAPACITY = -4,    /* device: free + evictable slots < missed tokens    */
   ECHO_ETIMEOUT = -5,     /* device: a cross-workgroup wait exceeded 1 s       */
   ECHO_EDEVARG = -6,      /* device: ctx_len/host_base out of range or overlap */
-  ECHO_ECORRUPT = -7      /* device: echo_check_invariants found a violation   */
+  ECHO_ECORRUPT = -7,     /* device: echo_check_invariants found a violation   */
+  ECHO_ESCRATCH = -8      /* the shape needs more than the static scratch      */
 };
 
 /* Prefetch threshold modes.  EMA: the threshold is the exponential moving
@@ -348,6 +349,33 @@ int echo_release(const echo_dims_t *dims, const echo_layer_t *layer, const int32
 int echo_admit(const echo_dims_t *dims, const echo_layer_t *layer, int32_t *host_base,
                int32_t *ctx_len, int32_t batch, int32_t b, int32_t base, int32_t len,
                int commit, const echo_ws_t *ws, hipStream_t stream);
+
+/* echo_topk for callers that cannot allocate: code under graph capture, tight
+ * serving loops, harnesses that forbid device allocation.  It computes exactly
+ * what echo_topk computes (same selection, k-th scores and threshold update, same
+ * kernels), but takes its outputs as plain device arrays instead of a workspace
+ * and keeps its internal scratch (request table, selection bitmap, boundary-bin
+ * candidates, counters) in a static device array of the library, 32 MiB on each
+ * GPU, held until the process ends.  The call allocates nothing.
+ *   scores   [batch][score_stride] fp32, device, score_stride >= max_ctx
+ *   sel_tok  [batch][top_k] int32, device: selected tokens, ascending
+ *   n_sel    [batch] int32, device: min(top_k, ctx)
+ *   kth      [batch] fp32, device: k-th highest score
+ *   theta    [batch] fp32, device, or NULL: EMA thresholds updated as echo_topk does
+ *   status   [1] int32, device: sticky status of the call, like echo_ws_t.status
+ *            (a device-side batch error sets it; while it is set the call changes
+ *            nothing); the caller clears it.
+ * The scratch needs 64 bytes per request for the request table, about
+ * max_ctx / 8 bytes per request for the bitmap and 8 * max_ctx bytes per request
+ * for the candidates (each region rounded up to 256 bytes), plus a few hundred
+ * bytes: up to 32 requests of 100,000 tokens fit.  Larger dims return
+ * ECHO_ESCRATCH with nothing enqueued.  Every call on a GPU uses that GPU's one
+ * array: calls that overlap on one GPU (other streams, other threads) race and
+ * give wrong results; calls ordered on one stream do not.  Errors: ECHO_EINVAL
+ * (host checks), ECHO_ESCRATCH, ECHO_EHIP. */
+int echo_topk_noalloc(const echo_dims_t *dims, const float *scores, int64_t score_stride,
+                      const echo_batch_t *batch, int32_t *sel_tok, int32_t *n_sel, float *kth,
+                      float *theta, int32_t *status, hipStream_t stream);
 
 /* Steps a0-a8 for one layer and one decode step, in order, on `stream`: indexer
  * + prefetch, top-k with the EMA update (mode EMA only), protect/evict/alloc,

@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libecho.so")
 
 ECHO_OK, ECHO_EINVAL, ECHO_EHIP, ECHO_EUNSUPPORTED = 0, -1, -2, -3
-ECHO_ECAPACITY, ECHO_ETIMEOUT, ECHO_EDEVARG, ECHO_ECORRUPT = -4, -5, -6, -7
+ECHO_ECAPACITY, ECHO_ETIMEOUT, ECHO_EDEVARG, ECHO_ECORRUPT, ECHO_ESCRATCH = -4, -5, -6, -7, -8
 ECHO_THETA_EMA, ECHO_THETA_NEG_INF, ECHO_THETA_POS_INF = 0, 1, 2
 (ECHO_CNT_MISS, ECHO_CNT_EVICT, ECHO_CNT_FREE, ECHO_CNT_EVICTABLE, ECHO_CNT_FREE_END,
  ECHO_CNT_PREFETCH, ECHO_CNT_SHORTCUT) = range(7)
@@ -30,7 +30,7 @@ EXPORTS = ("echo_meta_bytes", "echo_ws_bytes", "echo_ws_bind", "echo_meta_init",
            "echo_prefill_ws_bind", "echo_prefill_ws_reset", "echo_prefill_score",
            "echo_prefill_early",
            "echo_prefill_select", "echo_prefill_copy", "echo_check_invariants",
-           "echo_status_string")
+           "echo_topk_noalloc", "echo_status_string")
 
 P = C.c_void_p
 
@@ -122,6 +122,7 @@ def lib() -> C.CDLL:
                                               C.POINTER(echo_prefill_ws_t), P]),
             "echo_prefill_copy": (C.c_int, [dp, lp, C.POINTER(echo_prefill_ws_t), C.c_int, P]),
             "echo_check_invariants": (C.c_int, [dp, lp, bp, wp, P, P]),
+            "echo_topk_noalloc": (C.c_int, [dp, P, C.c_int64, bp, P, P, P, P, P, P]),
             "echo_status_string": (C.c_char_p, [C.c_int]),
         }
         for name, (res, args) in sigs.items():
@@ -178,6 +179,13 @@ def echo_indexer_score(dims, layer, batch, ws, theta_mode: int, stream: int) -> 
 def echo_topk(dims, scores: int, score_stride: int, batch, ws, theta, stream: int) -> int:
     return lib().echo_topk(C.byref(dims), scores, score_stride, _ref(batch), _ref(ws), theta,
                            stream)
+
+
+def echo_topk_noalloc(dims, scores: int, score_stride: int, batch, sel_tok: int, n_sel: int,
+                      kth: int, theta, status: int, stream: int) -> int:
+    """All pointers are device addresses; theta may be None."""
+    return lib().echo_topk_noalloc(C.byref(dims), scores, score_stride, _ref(batch), sel_tok,
+                                   n_sel, kth, theta, status, stream)
 
 
 def echo_cache_alloc_evict(dims, layer, batch, ws, stream: int) -> int:

@@ -3,10 +3,19 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "kernels.h"
 #include "prefill.h"
 
 using namespace echo;
+
+// Scratch of echo_topk_noalloc: a file-scope device array, one copy on every GPU
+// the library runs on, held until the process ends.  In host code the name is only
+// a stand-in; the device address comes from hipGetSymbolAddress (per device, in
+// static_scratch below) and is what kernels and fills receive.
+constexpr int64_t kStaticScratchBytes = 32LL << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
 
 
 namespace {
@@ -145,6 +154,53 @@ StepArgs make_args(const echo_dims_t &d, const echo_layer_t *l, const echo_batch
   a.ws = ws;
   scratch_layout(d, ws.internal, &a.sc);
   return a;
+}
+
+// Device address of `scratch` on the current device, looked up once per device
+// with that device current and kept for the process's lifetime.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+int static_scratch(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ECHO_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return ECHO_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ECHO_OK;
+}
+
+// The part of the internal scratch that the top-k call uses (request table,
+// counters, selection bitmap, boundary-bin candidates), plus the workspace counter
+// words, laid out from `base`; with base == nullptr only measures it.  The other
+// Scratch pointers stay null.
+int64_t topk_scratch_layout(const echo_dims_t &d, uint8_t *base, Scratch *s,
+                            int32_t **counters) {
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) -> uint8_t * {
+    uint8_t *p = base ? base + off : nullptr;
+    off = align256(off + bytes);
+    return p;
+  };
+  const int64_t B = d.max_batch, C = d.max_ctx;
+  Scratch t;
+  memset(&t, 0, sizeof t);
+  t.bw = (int32_t)((C + 63) / 64 * 2);
+  t.max_tiles = (int32_t)(B * ((C + kScoreTile - 1) / kScoreTile));
+  t.req = (ReqInfo *)take(B * sizeof(ReqInfo));
+  t.misc = (int32_t *)take(M_NMISC * 4);
+  int32_t *cnt = (int32_t *)take(ECHO_NCOUNTERS * 4);
+  t.tbits = (uint32_t *)take(B * t.bw * 4);
+  t.tcand_key = (uint32_t *)take(B * C * 4);
+  t.tcand_idx = (int32_t *)take(B * C * 4);
+  if (s) *s = t;
+  if (counters) *counters = cnt;
+  return off;
 }
 
 #define LAUNCH(x)                           \
@@ -378,6 +434,39 @@ int echo_topk(const echo_dims_t *dims, const float *scores, int64_t score_stride
   a.scores_in = scores;
   a.score_stride = score_stride;
   a.theta_upd = theta;
+  LAUNCH(launch_begin(a, BEGIN_REQ | BEGIN_CLR_TOPK, stream));
+  LAUNCH(launch_topk(a, false, stream));
+  return ECHO_OK;
+}
+
+int echo_topk_noalloc(const echo_dims_t *dims, const float *scores, int64_t score_stride,
+                      const echo_batch_t *batch, int32_t *sel_tok, int32_t *n_sel, float *kth,
+                      float *theta, int32_t *status, hipStream_t stream) {
+  int rc = check_dims(dims);
+  if (rc != ECHO_OK) return rc;
+  if (!scores || score_stride < dims->max_ctx || !batch_ok(*dims, batch) || !sel_tok ||
+      !n_sel || !kth || !status)
+    return ECHO_EINVAL;
+  if (topk_scratch_layout(*dims, nullptr, nullptr, nullptr) > kStaticScratchBytes)
+    return ECHO_ESCRATCH;
+  void *base = nullptr;
+  rc = static_scratch(&base);
+  if (rc != ECHO_OK) return rc;
+  echo_ws_t ws;
+  memset(&ws, 0, sizeof ws);
+  ws.sel_tok = sel_tok;
+  ws.n_sel = n_sel;
+  ws.kth = kth;
+  ws.status = status;
+  StepArgs a = make_args(*dims, nullptr, batch, ws, ECHO_THETA_POS_INF);
+  topk_scratch_layout(*dims, (uint8_t *)base, &a.sc, &a.ws.counters);
+  a.scores_in = scores;
+  a.score_stride = score_stride;
+  a.theta_upd = theta;
+  // the array keeps the previous call's contents: the counters start at zero (fill
+  // kernels, not memset nodes); everything else is written before it is read
+  LAUNCH(launch_fill_zero((uint32_t *)a.sc.misc, M_NMISC, stream));
+  LAUNCH(launch_fill_zero((uint32_t *)a.ws.counters, ECHO_NCOUNTERS, stream));
   LAUNCH(launch_begin(a, BEGIN_REQ | BEGIN_CLR_TOPK, stream));
   LAUNCH(launch_topk(a, false, stream));
   return ECHO_OK;
@@ -634,6 +723,7 @@ const char *echo_status_string(int code) {
     case ECHO_ETIMEOUT: return "cross-workgroup wait timed out";
     case ECHO_EDEVARG: return "device-side batch arguments out of range or overlapping";
     case ECHO_ECORRUPT: return "cache-management state violates an invariant";
+    case ECHO_ESCRATCH: return "the call needs more than the library's static scratch";
     default: return "unknown status";
   }
 }

@@ -111,7 +111,7 @@ def test_null_arguments_are_rejected_before_any_launch():
 
 def test_status_strings():
     _lib_or_skip()
-    for code in (0, -1, -2, -3, -4, -5, -6, -7):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         s = abi.echo_status_string(code)
         assert s and s != "unknown status"
     assert abi.echo_status_string(42) == "unknown status"
@@ -143,6 +143,17 @@ def test_newer_entry_points_check_arguments_before_any_launch():
         assert fn(d, layer, chunk, pws, 0) == abi.ECHO_EINVAL
     assert abi.echo_prefill_copy(d, layer, pws, 0, 0) == abi.ECHO_EINVAL
     assert abi.echo_prefill_ws_reset(d, pws, 0) == abi.ECHO_EINVAL
+    # the top-k call without a workspace: null outputs or status, a short stride
+    b1 = abi.echo_batch_t(1, 1 << 30, 1 << 30)
+    for args in ((None, 65536, b1, 1, 1, 1, None, 1), (1, 65536, b1, None, 1, 1, None, 1),
+                 (1, 65536, b1, 1, 1, 1, None, None), (1, 100, b1, 1, 1, 1, None, 1)):
+        assert abi.echo_topk_noalloc(d, *args, 0) == abi.ECHO_EINVAL
+    # dims whose scratch exceeds the 32 MiB static array are refused before any launch
+    big = _dims(max_batch=64, max_ctx=100_000, n_host=6_400_000)
+    assert abi.echo_topk_noalloc(big, 1, 100_000, b1, 1, 1, 1, None, 1, 0) == abi.ECHO_ESCRATCH
+    fits = _dims(max_batch=32, max_ctx=100_000, n_host=3_200_000)
+    assert abi.echo_topk_noalloc(fits, None, 100_000, b1, 1, 1, 1, None, 1, 0) == \
+        abi.ECHO_EINVAL
     # the invariant check: null layer, workspace or report, a batch above max_batch
     assert abi.echo_check_invariants(d, None, None, ws, 1 << 30, 0) == abi.ECHO_EINVAL
     assert abi.echo_check_invariants(d, layer, None, ws, 1 << 30, 0) == abi.ECHO_EINVAL
