@@ -66,6 +66,15 @@ def parse():
     p.add_argument("--pmc-calibrate", action="store_true",
                    help="end with a 256 MiB device-to-device copy whose FETCH_SIZE / WRITE_SIZE "
                         "counters scale the indexer's")
+    p.add_argument("--headline-only", action="store_true",
+                   help="only the timed decode steps of the workload (for kernel traces of the "
+                        "step as it runs)")
+    p.add_argument("--no-ablation", action="store_true",
+                   help="skip the threshold-mode ablation and the prefetch-cap sweep")
+    p.add_argument("--no-other-workloads", action="store_true",
+                   help="skip the low-locality and single-layer decode workloads")
+    p.add_argument("--cap-sweep", default="128,192,384",
+                   help="prefetch cap divisors measured beside the workload's own")
     return p.parse_args()
 
 
@@ -105,6 +114,35 @@ def stored_traffic():
         return None
 
 
+def stored_step_kernel(total_tok):
+    """The scoring kernel as the decode step runs it (k_score<4,true>: prefetch on, its
+    copy handed over to the next kernel), from the committed kernel-trace summary
+    (profiles/k_score_in_step_capacity.txt), or None if it is missing or the scoring
+    kernel's sources changed since the trace was taken."""
+    path = os.path.join(ROOT, "profiles", "k_score_in_step_capacity.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha1") != source_digest():
+        return None
+    try:
+        ms = float(kv["avg_launch_us"]) / 1e3
+        n = int(kv["launches"])
+    except (KeyError, ValueError):
+        return None
+    gbps = total_tok * BYTES_PER_SCORED_TOKEN / (ms * 1e-3) / 1e9
+    return {"kernel": "k_score<4,true> inside the captured decode step (EMA prefetch on, host "
+                      "reads of the prefetch copy in flight on other compute units)",
+            "avg_launch_ms": round(ms, 5), "launches": n, "hbm_gbps": round(gbps, 1),
+            "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+            "source": "profiles/k_score_in_step_capacity.txt (rocprofv3 kernel trace of "
+                      "bench.py --headline-only)"}
+
+
 def replay_median_ms(graph, n):
     """Median duration of n replays of `graph`, each timed with events on the current
     stream after the previous one has finished."""
@@ -122,6 +160,169 @@ def replay_median_ms(graph, n):
     return 0.5 * (times[(n - 1) // 2] + times[n // 2])
 
 
+class Decode:
+    """One decode workload on the device: its layers (tiled indexer K, queries,
+    weights, metadata and GPU pool), pinned host pools shared round-robin by the
+    layers, the batch and one workspace shared by every layer."""
+
+    def __init__(self, wl, args, dev, L, npools, q_ring, room=0, keep_rows0=False):
+        import torch
+
+        from kv_cache_offload_fp8_amd import runtime as R
+        from synth import gen as G
+
+        self.wl, self.L, self.dev = wl, L, dev
+        self.ctx = wl.contexts(args.seed)
+        self.base = G.host_layout(self.ctx, room=room)
+        self.B = int(self.ctx.size)
+        self.total_tok = int(self.ctx.sum())
+        self.q_ring = q_ring
+        self.dims = self.make_dims(wl.cap_div)
+        t0 = time.time()
+        self.pools = []
+        for i in range(max(1, min(npools, L))):
+            hp = R.HostPool(wl.n_host, wl.latent)
+            lat = G.gen_latents(wl, i, self.ctx, self.base, dev, args.seed,
+                                out=torch.empty((wl.n_host, wl.latent), dtype=torch.int16,
+                                                device=dev))
+            hp.tensor.copy_(lat)
+            del lat
+            self.pools.append(hp)
+        self.layers = []
+        rows = torch.empty((wl.n_host, wl.head_dim), dtype=torch.uint8, device=dev)
+        self.rows0 = None
+        for l in range(L):
+            rows.zero_()
+            G.gen_kidx(wl, l, self.ctx, self.base, dev, args.seed, out=rows)
+            if l == 0 and keep_rows0:
+                self.rows0 = rows.clone()
+            kidx = R.pack_kidx(self.dims, rows, torch.empty_like(rows))
+            lay = R.Layer(self.dims, kidx, self.pools[l % len(self.pools)], self.B, dev)
+            lay.q.copy_(G.gen_q(wl, l, self.B, q_ring, dev, args.seed))
+            lay.w.copy_(G.gen_w(wl, l, self.B, dev, args.seed))
+            lay.init()
+            self.layers.append(lay)
+        del rows
+        self.batch = R.Batch(self.base, self.ctx, dev)
+        self.ws = R.Workspace(self.dims, dev)
+        self.ws.reset()
+        torch.cuda.synchronize()
+        log(f"[bench] {wl.name}: B={self.B} ctx {self.ctx.min()}..{self.ctx.max()} (sum "
+            f"{self.total_tok}) L={L} n_gpu={wl.n_gpu} n_host={wl.n_host}: {len(self.pools)} "
+            f"host pools, {L} layers ready ({time.time() - t0:.1f}s)")
+
+    def make_dims(self, cap_div):
+        from kv_cache_offload_fp8_amd import runtime as R
+        wl = self.wl
+        return R.make_dims(wl.heads, wl.head_dim, wl.top_k, wl.n_host, wl.n_gpu, self.B,
+                           int(self.ctx.max()) + 1, wl.latent, wl.alpha, cap_div, self.q_ring)
+
+    def reinit(self):
+        import torch
+        for lay in self.layers:
+            lay.init()
+        self.ws.reset()
+        torch.cuda.synchronize()
+
+    def capture(self, mode, dims, stream):
+        """One decode step (every layer's echo_layer_step) captured in one hipGraph."""
+        import torch
+
+        from kv_cache_offload_fp8_amd import abi
+        from kv_cache_offload_fp8_amd import runtime as R
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                for lay in self.layers:
+                    R.check(abi.echo_layer_step(dims, lay.struct, self.batch.struct, self.ws.ws,
+                                                mode, stream.cuda_stream), "echo_layer_step")
+        torch.cuda.synchronize()
+        return g
+
+    def stats(self):
+        import torch
+        return torch.stack([lay.stats for lay in self.layers]).cpu().numpy().astype(np.int64)
+
+    def status(self, what):
+        from kv_cache_offload_fp8_amd import abi
+        st = int(self.ws.status.item())
+        if st != 0:
+            raise SystemExit(f"device status after {what}: {abi.echo_status_string(st)}")
+
+    def run(self, mode, steps, warmup, stream, cap_div=None, init=True):
+        """Capture a decode step, replay it `warmup` times untimed, then time `steps`
+        replays between synchronizations.  Returns the timing and the layers' running
+        totals over the timed replays."""
+        import torch
+        dims = self.dims if cap_div is None else self.make_dims(cap_div)
+        if init:
+            self.reinit()
+        g = self.capture(mode, dims, stream)
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        self.status("warmup")
+        s0 = self.stats()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        ev0.record()
+        for _ in range(steps):
+            g.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        gpu_ms = ev0.elapsed_time(ev1)
+        elapsed = max(wall, gpu_ms / 1e3)
+        self.status("timed steps")
+        delta = self.stats() - s0
+        del g
+        return dict(elapsed=elapsed, ms_per_step=elapsed * 1e3 / steps,
+                    layer_steps_per_s=steps * self.L / elapsed,
+                    us_per_layer_step=elapsed * 1e6 / (steps * self.L), stats=delta, steps=steps)
+
+    def close(self):
+        for hp in self.pools:
+            hp.close()
+        self.pools = []
+        self.layers = []
+
+
+def totals_summary(delta, steps, row_bytes, link_peak=None, us_per_layer_step=None):
+    """Per-layer-step figures from the layers' running totals over timed replays."""
+    from kv_cache_offload_fp8_amd import abi
+    L = delta.shape[0]
+    tot = delta.sum(0)
+    ls = max(1, int(tot[abi.ECHO_STAT_STEPS]))
+    sel = max(1, int(tot[abi.ECHO_STAT_SELECTED]))
+    pf = int(tot[abi.ECHO_STAT_PREFETCHED])
+    per_layer_hit = 1.0 - delta[:, abi.ECHO_STAT_MISSED] / np.maximum(
+        1, delta[:, abi.ECHO_STAT_SELECTED])
+    worst = np.argsort(per_layer_hit)[:3]
+    tot = [int(x) for x in tot]
+    out = {
+        "layer_steps_counted": ls,
+        "hit_rate": round(1.0 - tot[abi.ECHO_STAT_MISSED] / sel, 5),
+        "selected_per_layer_step": round(sel / ls, 1),
+        "misses_per_layer_step": round(tot[abi.ECHO_STAT_MISSED] / ls, 1),
+        "prefetched_per_layer_step": round(pf / ls, 1),
+        "prefetch_candidates_per_layer_step": round(tot[abi.ECHO_STAT_CANDIDATES] / ls, 1),
+        "prefetch_selected_same_step_frac": round(tot[abi.ECHO_STAT_PF_SELECTED] / max(1, pf), 4),
+        "evicted_per_layer_step": round(tot[abi.ECHO_STAT_EVICTED] / ls, 1),
+        "link_mb_per_layer_step": round((pf + tot[abi.ECHO_STAT_MISSED]) * row_bytes / ls / 1e6,
+                                        3),
+    }
+    if L > 1:
+        out["per_layer_hit_rate_min"] = round(float(per_layer_hit.min()), 5)
+        out["lowest_hit_layers"] = [[int(l), round(float(per_layer_hit[l]), 4)] for l in worst]
+    if link_peak and us_per_layer_step:
+        link_us = (pf + tot[abi.ECHO_STAT_MISSED]) * row_bytes / ls / (link_peak * 1e3)
+        out["link_floor_us"] = round(float(link_us), 2)
+        out["link_floor_frac"] = round(float(link_us / us_per_layer_step), 4)
+    assert steps * L == ls, (steps, L, ls)
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -135,7 +336,6 @@ def main():
     from kv_cache_offload_fp8_amd import abi
     from kv_cache_offload_fp8_amd import runtime as R
     from synth import get
-    from synth import gen as G
 
     torch.cuda.set_device(0)
     dev = "cuda"
@@ -146,107 +346,53 @@ def main():
     if args.cap_div:
         wl = wl.scaled(cap_div=args.cap_div)
     L = args.layers or wl.layers
-    mode = {"ema": abi.ECHO_THETA_EMA, "neg_inf": abi.ECHO_THETA_NEG_INF,
-            "pos_inf": abi.ECHO_THETA_POS_INF}[args.mode]
-    ctx = wl.contexts(args.seed)
-    base = G.host_layout(ctx, room=1)  # one free row per request: the append measurement
-    B = int(ctx.size)
-    total_tok = int(ctx.sum())
+    mode_of = {"ema": abi.ECHO_THETA_EMA, "neg_inf": abi.ECHO_THETA_NEG_INF,
+               "pos_inf": abi.ECHO_THETA_POS_INF}
+    mode = mode_of[args.mode]
     q_ring = args.warmup + args.steps + args.breakdown_steps
-    dims = R.make_dims(wl.heads, wl.head_dim, wl.top_k, wl.n_host, wl.n_gpu, B,
-                       int(ctx.max()) + 1, wl.latent, wl.alpha, wl.cap_div, q_ring)
-    log(f"[bench] workload {wl.name}: B={B} ctx {ctx.min()}..{ctx.max()} (sum {total_tok}) "
-        f"L={L} n_gpu={wl.n_gpu} n_host={wl.n_host} q_ring={q_ring}")
-
-    # ---------------------------------------------------------------- setup
-    t0 = time.time()
-    npools = max(1, min(args.host_pools, L))
-    pools = []
-    for i in range(npools):
-        hp = R.HostPool(wl.n_host, wl.latent)
-        lat = G.gen_latents(wl, i, ctx, base, dev, args.seed,
-                            out=torch.empty((wl.n_host, wl.latent), dtype=torch.int16,
-                                            device=dev))
-        hp.tensor.copy_(lat)
-        del lat
-        pools.append(hp)
-    log(f"[bench] {npools} host pools of {wl.n_host * wl.latent * 2 / 1e9:.2f} GB ready "
-        f"({time.time() - t0:.1f}s)")
-    layers = []
-    rows = torch.empty((wl.n_host, wl.head_dim), dtype=torch.uint8, device=dev)
-    rows0 = None  # layer 0's row-major K, for the CPU baseline
-    for l in range(L):
-        rows.zero_()
-        G.gen_kidx(wl, l, ctx, base, dev, args.seed, out=rows)
-        if l == 0:
-            rows0 = rows.clone()
-        kidx = R.pack_kidx(dims, rows, torch.empty_like(rows))
-        lay = R.Layer(dims, kidx, pools[l % npools], B, dev)
-        lay.q.copy_(G.gen_q(wl, l, B, q_ring, dev, args.seed))
-        lay.w.copy_(G.gen_w(wl, l, B, dev, args.seed))
-        lay.init()
-        layers.append(lay)
-    del rows
-    batch = R.Batch(base, ctx, dev)
-    ws = R.Workspace(dims, dev)
-    ws.reset()
-    torch.cuda.synchronize()
-    log(f"[bench] {L} layers ready ({time.time() - t0:.1f}s); meta/layer "
-        f"{layers[0].meta_bytes()} B = echo_meta_bytes {abi.echo_meta_bytes(wl.n_host, wl.n_gpu)}")
-
-    def one_step(stream):
-        for lay in layers:
-            R.check(abi.echo_layer_step(dims, lay.struct, batch.struct, ws.ws, mode, stream),
-                    "echo_layer_step")
-
-    # ------------------------------------------------------- graph capture
-    g = torch.cuda.CUDAGraph()
+    # one free row per request: the append measurement writes there
+    D = Decode(wl, args, dev, L, args.host_pools, q_ring, room=1,
+               keep_rows0=not args.no_cpu_baseline)
+    dims, layers, batch, ws, B = D.dims, D.layers, D.batch, D.ws, D.B
+    ctx, base, total_tok = D.ctx, D.base, D.total_tok
+    log(f"[bench] meta/layer {layers[0].meta_bytes()} B = echo_meta_bytes "
+        f"{abi.echo_meta_bytes(wl.n_host, wl.n_gpu)}")
     cs = torch.cuda.Stream()
-    with torch.cuda.stream(cs):
-        with torch.cuda.graph(g, stream=cs):
-            one_step(cs.cuda_stream)
-    torch.cuda.synchronize()
-    log("[bench] captured one decode step "
-        f"({L} layers) in a graph; warmup {args.warmup}")
-    for _ in range(args.warmup):
-        g.replay()
-    torch.cuda.synchronize()
-    st = int(ws.status.item())
-    if st != 0:
-        raise SystemExit(f"device status after warmup: {abi.echo_status_string(st)}")
+    row = wl.latent * 2
 
     # -------------------------------------------------------- timed region
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
-        g.replay()
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    gpu_ms = ev0.elapsed_time(ev1)
-    elapsed = max(wall, gpu_ms / 1e3)
-    st = int(ws.status.item())
-    if st != 0:
-        raise SystemExit(f"device status after timed steps: {abi.echo_status_string(st)}")
+    head = D.run(mode, args.steps, args.warmup, cs, init=False)
+    ms_per_step = head["ms_per_step"]
+    layer_steps_per_s = head["layer_steps_per_s"]
     shortcut_last = int(ws.counters[abi.ECHO_CNT_SHORTCUT].item())
-    ms_per_step = elapsed * 1e3 / args.steps
-    layer_steps_per_s = args.steps * L / elapsed
     log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step, "
         f"{layer_steps_per_s:.1f} layer-steps/s")
+    timed = totals_summary(head["stats"], args.steps, row)
+    log(f"[bench] timed replays: {timed}")
+    if args.headline_only:
+        print(json.dumps({"metric": "decode layer-steps/s", "value": round(layer_steps_per_s, 3),
+                          "unit": "layer-steps/s", "steps": args.steps,
+                          "ms_per_step": round(ms_per_step, 4), "timed_replays": timed}),
+              flush=True)
+        D.close()
+        return
 
     # ------------------------------------------- per-phase breakdown (eager)
+    # The same layer steps as the five separate calls, with events between them;
+    # each layer's threshold before the step, its k-th scores, prefetch list and
+    # selection are kept for the threshold and prefetch-usefulness figures.
     s = torch.cuda.current_stream()
     sh = s.cuda_stream
     nph = 4
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nph + 1)]
            for _ in range(args.breakdown_steps * L)]
-    miss_rows, sel_rows, pf_rows, sc_rows = [], [], [], []
+    miss_rows = []
+    keep = []  # per (step, layer): theta before, kth, n_pf, pf_tok, n_sel, sel_tok
     i = 0
     for _ in range(args.breakdown_steps):
         for lay in layers:
             e = evs[i]
+            theta_before = lay.theta[:B].clone()
             e[0].record(s)
             R.check(abi.echo_indexer_prefetch(dims, lay.struct, batch.struct, ws.ws, mode, sh),
                     "indexer")
@@ -261,53 +407,30 @@ def main():
             R.check(abi.echo_recall(dims, lay.struct, ws.ws, sh), "recall")
             e[4].record(s)
             R.check(abi.echo_step_advance(lay.struct, ws.ws, sh), "advance")
-            c = ws.counters.clone()
-            miss_rows.append(c[abi.ECHO_CNT_MISS])
-            pf_rows.append(c[abi.ECHO_CNT_PREFETCH])
-            sc_rows.append(c[abi.ECHO_CNT_SHORTCUT])
-            sel_rows.append(ws.n_sel[:B].sum())
+            miss_rows.append(ws.counters[abi.ECHO_CNT_MISS].clone())
+            keep.append((theta_before, ws.kth[:B].clone(), ws.n_pf[:B].clone(),
+                         ws.pf_tok[:B].clone(), ws.n_sel[:B].clone(), ws.sel_tok[:B].clone()))
             i += 1
     torch.cuda.synchronize()
-    st = int(ws.status.item())
-    if st != 0:
-        raise SystemExit(f"device status after breakdown: {abi.echo_status_string(st)}")
+    D.status("breakdown")
     ph = np.array([[evs[j][p].elapsed_time(evs[j][p + 1]) for p in range(nph)]
                    for j in range(len(evs))])  # ms
     misses = np.array([int(x) for x in miss_rows])
-    prefetched = np.array([int(x) for x in pf_rows])
-    selected = np.array([int(x) for x in sel_rows])
     idx_ms = float(ph[:, 0].mean())
     idx_bytes = total_tok * BYTES_PER_SCORED_TOKEN
     idx_gbps = idx_bytes / (idx_ms * 1e-3) / 1e9
-    row = wl.latent * 2
     recall_ms = ph[:, 3]
     recall_eager_gbps = float((misses * row).sum() / (recall_ms.sum() * 1e-3) / 1e9)
+    thr = threshold_and_usefulness(keep, L, args.breakdown_steps, wl.top_k, ctx)
+    log(f"[bench] phases (ms, mean over {len(evs)} layer-steps): indexer {idx_ms:.4f} "
+        f"topk {ph[:, 1].mean():.4f} alloc/evict {ph[:, 2].mean():.4f} "
+        f"recall {recall_ms.mean():.4f}; threshold and usefulness {thr}")
     # Recall rate as the step runs it, back to back in a graph: the last layer's
     # miss list (still in the workspace) recalled `nrc` times into its pool (the
     # same rows to the same slots each time), timed with events around one replay.
     nrc = 32
-    rc_rows = int(ws.counters[abi.ECHO_CNT_MISS].item())
-    grc = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(cs):
-        with torch.cuda.graph(grc, stream=cs):
-            for _ in range(nrc):
-                R.check(abi.echo_recall(dims, layers[-1].struct, ws.ws, cs.cuda_stream),
-                        "recall")
-    grc.replay()
-    torch.cuda.synchronize()
-    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    r0.record()
-    grc.replay()
-    r1.record()
-    torch.cuda.synchronize()
-    rc_ms = r0.elapsed_time(r1) / nrc
+    rc_rows, rc_ms = recall_in_graph(D, layers[-1], nrc, cs)
     recall_gbps = rc_rows * row / (rc_ms * 1e-3) / 1e9
-    del grc
-    hit = float(1.0 - misses.sum() / max(1, selected.sum()))
-    log(f"[bench] phases (ms, mean over {len(evs)} layer-steps): indexer {idx_ms:.4f} "
-        f"topk {ph[:, 1].mean():.4f} alloc/evict {ph[:, 2].mean():.4f} "
-        f"recall {recall_ms.mean():.4f}; hit rate {hit:.4f}; misses/layer-step "
-        f"{misses.mean():.0f}; prefetched/layer-step {prefetched.mean():.0f}")
     log(f"[bench] recall in a graph: {rc_rows} rows in {rc_ms * 1e3:.1f} us per launch = "
         f"{recall_gbps:.1f} GB/s (eager, event per call: {recall_eager_gbps:.1f} GB/s)")
 
@@ -364,41 +487,19 @@ def main():
         del cal_src, cal_dst
 
     # ------------------------------------------------------ host-link peaks
-    n_rows = min(wl.n_host, 65536)
-    big = pools[0]
-    dst = torch.empty((n_rows, wl.latent), dtype=torch.int16, device=dev)
-    src = big.tensor[:n_rows]
-    for _ in range(2):
-        dst.copy_(src, non_blocking=True)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(5):
-        dst.copy_(src, non_blocking=True)
-    e1.record()
-    torch.cuda.synchronize()
-    memcpy_gbps = 5 * n_rows * row / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    # zero-copy: echo_recall over a synthetic recall list of n_rows rows into layer 0's pool
-    nz = min(n_rows, B * wl.top_k, wl.n_gpu)
-    ws.recall_h[:nz] = torch.arange(nz, dtype=torch.int32, device=dev)
-    ws.recall_g[:nz] = torch.arange(nz, dtype=torch.int32, device=dev)
-    ws.counters[abi.ECHO_CNT_MISS] = nz
-    R.check(abi.echo_recall(dims, layers[0].struct, ws.ws, sh), "recall")
-    e0.record()
-    for _ in range(5):
-        R.check(abi.echo_recall(dims, layers[0].struct, ws.ws, sh), "recall")
-    e1.record()
-    torch.cuda.synchronize()
-    zc_gbps = 5 * nz * row / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    memcpy_gbps, zc_gbps = link_peaks(D, sh)
     link_peak = max(memcpy_gbps, zc_gbps)
     log(f"[bench] host link: hipMemcpy H2D {memcpy_gbps:.1f} GB/s, zero-copy recall kernel "
-        f"{zc_gbps:.1f} GB/s over {nz} rows")
+        f"{zc_gbps:.1f} GB/s")
 
-    # layer-step floor: every prefetched and missed row crosses the host link once
+    # layer-step floor: every prefetched and missed row of the timed replays crosses
+    # the host link once
     step_ms = ms_per_step / L
-    link_bytes = (float(prefetched.mean()) + float(misses.mean())) * row
+    timed = totals_summary(head["stats"], args.steps, row, link_peak, step_ms * 1e3)
+    link_bytes = timed["link_mb_per_layer_step"] * 1e6
     link_floor_ms = link_bytes / (link_peak * 1e9) * 1e3
     traffic = stored_traffic()
+    in_step = stored_step_kernel(total_tok)
     log(f"[bench] layer step {step_ms * 1e3:.1f} us; host-link floor "
         f"{link_floor_ms * 1e3:.1f} us ({link_floor_ms / step_ms:.1%})")
 
@@ -449,9 +550,7 @@ def main():
     gap.replay()
     a1.record()
     torch.cuda.synchronize()
-    st = int(ws.status.item())
-    if st != 0:
-        raise SystemExit(f"device status after append: {abi.echo_status_string(st)}")
+    D.status("append")
     append_ms = a0.elapsed_time(a1) / L
     del gap
     log(f"[bench] append: {append_ms * 1e3:.1f} us per layer ({B} tokens: {B * wl.head_dim} B "
@@ -478,22 +577,59 @@ def main():
                                int(i == L - 1), ws.ws, cs.cuda_stream), "admit")
     r2.record(cs)
     torch.cuda.synchronize()
-    st = int(ws.status.item())
-    if st != 0:
-        raise SystemExit(f"device status after release/admit: {abi.echo_status_string(st)}")
+    D.status("release/admit")
     release_ms = r0.elapsed_time(r1) / L
     admit_ms = r1.elapsed_time(r2) / L
     log(f"[bench] release of one request ({int(ctx[0])} tokens, {resident0} resident on the "
         f"last layer): {release_ms * 1e3:.1f} us per layer; admission {admit_ms * 1e3:.1f} us "
         "per layer")
 
+    # ------------------------------------------------------- CPU baselines
+    cpu = cpu1 = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, ctx, base, layers[0], D.rows0, args, dims, threads=0)
+        cpu1 = cpu_baseline(wl, ctx, base, layers[0], D.rows0, args, dims, threads=1)
+
+    # --------------------------------- threshold ablation and prefetch-cap sweep
+    ablation = sweep = None
+    if not args.no_ablation:
+        ablation = {args.mode: dict(layer_steps_per_s=round(layer_steps_per_s, 2),
+                                    us_per_layer_step=round(step_ms * 1e3, 2), **timed)}
+        for m in ("ema", "pos_inf", "neg_inf"):
+            if m == args.mode:
+                continue
+            r = D.run(mode_of[m], args.steps, args.warmup, cs)
+            ablation[m] = dict(layer_steps_per_s=round(r["layer_steps_per_s"], 2),
+                               us_per_layer_step=round(r["us_per_layer_step"], 2),
+                               **totals_summary(r["stats"], args.steps, row, link_peak,
+                                                r["us_per_layer_step"]))
+            log(f"[bench] {wl.name}, threshold {m}: {r['layer_steps_per_s']:.1f} layer-steps/s")
+        ablation["ema_speedup_vs_pos_inf"] = round(
+            ablation["ema"]["layer_steps_per_s"] / ablation["pos_inf"]["layer_steps_per_s"], 4)
+        sweep = {str(wl.cap_div): dict(layer_steps_per_s=round(layer_steps_per_s, 2), **timed)}
+        for cd in [int(x) for x in args.cap_sweep.split(",") if x.strip()]:
+            if cd == wl.cap_div:
+                continue
+            r = D.run(mode, args.steps, args.warmup, cs, cap_div=cd)
+            sweep[str(cd)] = dict(layer_steps_per_s=round(r["layer_steps_per_s"], 2),
+                                  **totals_summary(r["stats"], args.steps, row, link_peak,
+                                                   r["us_per_layer_step"]))
+            log(f"[bench] {wl.name}, cap divisor {cd}: {r['layer_steps_per_s']:.1f} "
+                f"layer-steps/s, {sweep[str(cd)]}")
+    D.close()
+    del D, layers, ws, batch
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------- the other decode workloads
+    others = None
+    if not args.no_other_workloads:
+        others = {}
+        for name in ("low_locality", "single_layer"):
+            others[name] = other_workload(get(name), args, dev, cs, mode_of, link_peak)
+
     # ------------------------------------------------------- chunked prefill
     prefill = None if args.no_prefill else prefill_measure(args, dev)
-
-    # ------------------------------------------------------- CPU baseline
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, ctx, base, layers[0], rows0, args, dims)
 
     out = {
         "metric": "decode layer-steps/s @100K ctx; indexer HBM GB/s % peak; recall host-link GB/s",
@@ -514,7 +650,7 @@ def main():
                                f"{wl.head_dim}, top-k {wl.top_k}, GPU pool {wl.n_gpu}/layer, "
                                f"host pool {wl.n_host} x {wl.latent} bf16, rho {wl.rho}",
                    "global_batch": B, "seq_len": int(ctx.max()), "layers": L,
-                   "threshold_mode": args.mode},
+                   "threshold_mode": args.mode, "prefetch_cap_div": wl.cap_div},
         "roofline": {"kernel": "lightning-indexer scoring kernel k_score<4,false> (prefetch "
                                f"off): a graph of {nso} echo_indexer_prefetch calls less a "
                                f"graph of their {nso} prologues, each the median of {nrep} "
@@ -523,6 +659,7 @@ def main():
                      "unit": "GB/s", "frac": round(ks_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "bytes_per_launch": idx_bytes,
                      "avg_launch_ms": round(ks_ms, 5)},
+        "scoring_in_step": in_step,
         "indexer_call": {"what": "echo_indexer_prefetch with prefetch off = k_begin + "
                                  f"k_score<4,false>, per call over {nso} calls back to back "
                                  f"in a graph, median of {nrep} replays",
@@ -533,7 +670,10 @@ def main():
             "bound": "host link", "link_bytes_per_layer_step": int(link_bytes),
             "floor_ms": round(link_floor_ms, 5), "measured_ms": round(step_ms, 5),
             "frac": round(link_floor_ms / step_ms, 4), "link_peak_gbps": round(link_peak, 2),
-            "achieved_gbps": round(link_bytes / (step_ms * 1e-3) / 1e9, 2)},
+            "achieved_gbps": round(link_bytes / (step_ms * 1e-3) / 1e9, 2),
+            "rows_from": "the layers' running totals over the timed replays"},
+        "timed_replays": timed,
+        "threshold_and_prefetch_usefulness": thr,
         "indexer_ema_standalone": {"avg_launch_ms": round(idx_ms, 5),
                                    "hbm_gbps": round(idx_gbps, 1),
                                    "note": "echo_indexer_prefetch alone also copies every "
@@ -549,7 +689,8 @@ def main():
                                 "zero_copy_recall_kernel": round(zc_gbps, 2)},
         "phase_ms": {"indexer": round(idx_ms, 5), "topk": round(float(ph[:, 1].mean()), 5),
                      "alloc_evict": round(float(ph[:, 2].mean()), 5),
-                     "recall": round(float(recall_ms.mean()), 5)},
+                     "recall": round(float(recall_ms.mean()), 5),
+                     "how": "the five separate calls, eager, events between them"},
         "attention_input_gather": {"ms_per_layer": round(gather_ms, 5), "rows": n_sel_tot,
                                    "bytes": gather_bytes, "hbm_gbps": round(gather_gbps, 1),
                                    "frac_of_hbm_peak": round(gather_gbps / HBM_PEAK_GBPS, 4),
@@ -563,16 +704,153 @@ def main():
                       "resident_last_layer": resident0,
                       "how": f"echo_release then echo_admit of request 0 on all {L} layers, "
                              "eager, events on the launch stream"},
+        "threshold_ablation": ablation,
+        "prefetch_cap_sweep": sweep,
+        "other_workloads": others,
         "prefill": prefill,
-        "hit_rate": round(hit, 5),
+        "hit_rate": timed["hit_rate"],
         "topk_shortcut_requests_last_layer": f"{shortcut_last}/{B}",
-        "misses_per_layer_step": round(float(misses.mean()), 1),
-        "prefetched_per_layer_step": round(float(prefetched.mean()), 1),
+        "misses_per_layer_step": timed["misses_per_layer_step"],
+        "prefetched_per_layer_step": timed["prefetched_per_layer_step"],
         "cpu_baseline": cpu,
+        "cpu_baseline_single_thread": cpu1,
     }
-    for hp in pools:
-        hp.close()
     print(json.dumps(out), flush=True)
+
+
+def threshold_and_usefulness(keep, L, steps, k, ctx):
+    """From the eager breakdown steps: how far each layer's EMA threshold was from the
+    step's k-th score, and what became of the prefetched tokens -- selected by the same
+    step, by the next step only, or by neither."""
+    th_err, same, nxt, pf_total, pf_checked = [], 0, 0, 0, 0
+    per_layer = np.zeros(L)
+    full = np.asarray(ctx) >= k
+    for j, (th, kth, npf, pft, nsel, selt) in enumerate(keep):
+        th, kth = th.cpu().numpy(), kth.cpu().numpy()
+        ok = full & np.isfinite(th) & (np.abs(kth) > 0)
+        if ok.any():
+            e = np.abs(th[ok] - kth[ok]) / np.abs(kth[ok])
+            th_err.append(float(e.mean()))
+            per_layer[j % L] += float(e.mean()) / steps
+        if j + L >= len(keep):
+            continue  # no next step to look at
+        npf, pft = npf.cpu().numpy(), pft.cpu().numpy()
+        nsel, selt = nsel.cpu().numpy(), selt.cpu().numpy()
+        nsel2, selt2 = keep[j + L][4].cpu().numpy(), keep[j + L][5].cpu().numpy()
+        for b in range(npf.size):
+            p = pft[b, : int(npf[b])]
+            if p.size == 0:
+                continue
+            s1 = np.isin(p, selt[b, : int(nsel[b])])
+            s2 = np.isin(p[~s1], selt2[b, : int(nsel2[b])])
+            same += int(s1.sum())
+            nxt += int(s2.sum())
+            pf_checked += p.size
+        pf_total += int(npf.sum())
+    return {
+        "threshold_rel_err_vs_kth_mean": round(float(np.mean(th_err)), 5) if th_err else None,
+        "threshold_rel_err_layers_0_30_60": [round(float(per_layer[l]), 5)
+                                             for l in (0, L // 2, L - 1) if l < L],
+        "prefetched_checked": pf_checked,
+        "selected_same_step_frac": round(same / max(1, pf_checked), 4),
+        "selected_next_step_only_frac": round(nxt / max(1, pf_checked), 4),
+        "selected_within_two_steps_frac": round((same + nxt) / max(1, pf_checked), 4),
+        "how": "eager breakdown steps: |theta before the step - the step's k-th score| / k-th "
+               "score, over requests with ctx >= k; each prefetched token of a step looked up "
+               "in that step's selection and the next step's"}
+
+
+def recall_in_graph(D, lay, nrc, cs):
+    """The workspace's recall list (the last layer-step's misses) recalled `nrc` times
+    back to back in a graph; returns (rows, ms per launch)."""
+    import torch
+
+    from kv_cache_offload_fp8_amd import abi
+    from kv_cache_offload_fp8_amd import runtime as R
+    rows = int(D.ws.counters[abi.ECHO_CNT_MISS].item())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cs):
+        with torch.cuda.graph(g, stream=cs):
+            for _ in range(nrc):
+                R.check(abi.echo_recall(D.dims, lay.struct, D.ws.ws, cs.cuda_stream), "recall")
+    g.replay()
+    torch.cuda.synchronize()
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r0.record()
+    g.replay()
+    r1.record()
+    torch.cuda.synchronize()
+    return rows, r0.elapsed_time(r1) / nrc
+
+
+def link_peaks(D, sh):
+    """Pinned host -> device: hipMemcpy and the zero-copy recall kernel, in GB/s."""
+    import torch
+
+    from kv_cache_offload_fp8_amd import abi
+    from kv_cache_offload_fp8_amd import runtime as R
+    wl = D.wl
+    row = wl.latent * 2
+    n_rows = min(wl.n_host, 65536)
+    dst = torch.empty((n_rows, wl.latent), dtype=torch.int16, device=D.dev)
+    src = D.pools[0].tensor[:n_rows]
+    for _ in range(2):
+        dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src, non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    memcpy_gbps = 5 * n_rows * row / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    # zero-copy: echo_recall over a synthetic recall list of nz rows into layer 0's pool
+    ws = D.ws
+    nz = min(n_rows, D.B * wl.top_k, wl.n_gpu)
+    ws.recall_h[:nz] = torch.arange(nz, dtype=torch.int32, device=D.dev)
+    ws.recall_g[:nz] = torch.arange(nz, dtype=torch.int32, device=D.dev)
+    ws.counters[abi.ECHO_CNT_MISS] = nz
+    R.check(abi.echo_recall(D.dims, D.layers[0].struct, ws.ws, sh), "recall")
+    e0.record()
+    for _ in range(5):
+        R.check(abi.echo_recall(D.dims, D.layers[0].struct, ws.ws, sh), "recall")
+    e1.record()
+    torch.cuda.synchronize()
+    zc_gbps = 5 * nz * row / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    return memcpy_gbps, zc_gbps
+
+
+def other_workload(wl, args, dev, cs, mode_of, link_peak):
+    """One of the other decode workloads of the same path (one layer): EMA against
+    prefetch off (threshold +inf) and -inf, each from a fresh layer, with the recall
+    rate of one layer-step's misses in a graph."""
+    import torch
+    q_ring = args.warmup + args.steps
+    D = Decode(wl, args, dev, 1, 1, q_ring)
+    row = wl.latent * 2
+    out = {"workload": f"{wl.name}: batch {D.B}, ctx {wl.ctx_lo}"
+                       + (f"..{wl.ctx_hi}" if wl.ctx_hi != wl.ctx_lo else "")
+                       + f", 1 layer, indexer {wl.heads}x{wl.head_dim}, top-k {wl.top_k}, "
+                         f"GPU pool {wl.n_gpu}, host pool {wl.n_host}, rho {wl.rho}"}
+    for m in ("ema", "pos_inf", "neg_inf"):
+        r = D.run(mode_of[m], args.steps, args.warmup, cs)
+        res = dict(layer_steps_per_s=round(r["layer_steps_per_s"], 2),
+                   us_per_layer_step=round(r["us_per_layer_step"], 2),
+                   **totals_summary(r["stats"], args.steps, row, link_peak,
+                                    r["us_per_layer_step"]))
+        nrc = 32
+        rows, ms = recall_in_graph(D, D.layers[0], nrc, cs)
+        if rows:
+            res["recall_rows"] = rows
+            res["recall_gbps"] = round(rows * row / (ms * 1e-3) / 1e9, 2)
+            res["recall_frac_of_link_peak"] = round(res["recall_gbps"] / link_peak, 4)
+        out[m] = res
+        log(f"[bench] {wl.name}, threshold {m}: {res}")
+    out["ema_speedup_vs_pos_inf"] = round(out["ema"]["layer_steps_per_s"] /
+                                          out["pos_inf"]["layer_steps_per_s"], 4)
+    D.close()
+    torch.cuda.synchronize()
+    return out
 
 
 def prefill_measure(args, dev):
@@ -712,11 +990,13 @@ def prefill_measure(args, dev):
     return out
 
 
-def cpu_baseline(wl, ctx, base, lay0, rows0, args, dims):
+def cpu_baseline(wl, ctx, base, lay0, rows0, args, dims, threads=0):
     """The oracle, as it stands, on a bounded sample: layer 0 of the same workload,
     the first `--cpu-sample-requests` requests, `--cpu-sample-steps` decode steps in
-    EMA mode (its own scores).  Reported as layer-steps/s, scaled by the share of the
-    layer-step's scored tokens the sample covers."""
+    EMA mode (its own scores), on every host thread (threads=0) or on `threads`.
+    Reported as layer-steps/s, scaled by the share of the layer-step's scored tokens
+    the sample covers.  One thread takes a smaller sample (4 requests, 2 steps) so
+    that it stays near 10 s."""
     import torch
 
     from oracle import oracle as O
@@ -724,6 +1004,8 @@ def cpu_baseline(wl, ctx, base, lay0, rows0, args, dims):
 
     nb = max(1, min(args.cpu_sample_requests, ctx.size))
     steps = max(1, min(args.cpu_sample_steps, lay0.q.shape[0]))
+    if threads == 1:
+        nb, steps = min(nb, 4), min(steps, 2)
     sctx = ctx[:nb].astype(np.int32)
     sbase = G.host_layout(sctx)
     n = int(sctx.sum())
@@ -736,12 +1018,16 @@ def cpu_baseline(wl, ctx, base, lay0, rows0, args, dims):
     w0 = lay0.w[:nb].cpu().numpy()
     orc = O.OracleLayer(wl.heads, wl.head_dim, wl.top_k, wl.latent, n_rows, wl.n_gpu, nb,
                         wl.cap_div, wl.alpha, keep_pool=False)
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    prev = O.set_threads(threads) if threads else None
+    used = threads or int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
     t0 = time.perf_counter()
     for t in range(steps):
         o = orc.step(sbase, sctx, qs[t], w0, kid, None, mode=O.MODE_EMA)
         assert o["status"] == O.OK
     dt = time.perf_counter() - t0
+    if prev:
+        O.set_threads(prev)
+    threads = used
     frac = n / float(ctx.sum())
     per_layer_step = dt / steps / frac
     log(f"[bench] cpu oracle: {steps} steps x {nb} requests ({n} tokens each) in {dt:.2f}s on "

@@ -79,6 +79,23 @@ enum {
   ECHO_NCOUNTERS = 16
 };
 
+/* Running totals of one layer (echo_layer_t.stats, uint64), added to by
+ * echo_layer_step (a step that ends with a device error may have added part of
+ * its counts; STEPS counts completed steps) and cleared by echo_meta_init.  They
+ * measure how useful the prefetch is (ECHO review, "Key observations",
+ * observation 2, and "Limitations and future work": the wasted prefetch traffic
+ * and the final recall count are worth recording). */
+enum {
+  ECHO_STAT_STEPS = 0,       /* layer steps counted                                     */
+  ECHO_STAT_SELECTED = 1,    /* selected tokens                                         */
+  ECHO_STAT_MISSED = 2,      /* selected tokens not resident after prefetch (recalled)  */
+  ECHO_STAT_PREFETCHED = 3,  /* tokens prefetched while scoring                         */
+  ECHO_STAT_PF_SELECTED = 4, /* of those, tokens selected by the same step's top-k      */
+  ECHO_STAT_CANDIDATES = 5,  /* prefetch candidates before the cap                      */
+  ECHO_STAT_EVICTED = 6,     /* slots evicted                                           */
+  ECHO_STAT_WORDS = 8
+};
+
 /* Words of per-layer control state (echo_layer_t.ctl). */
 enum {
   ECHO_CTL_STEP = 0,  /* decode-step counter t of this layer                        */
@@ -143,6 +160,7 @@ typedef struct {
                               are, the full-score passes are skipped); results never
                               depend on it. */
   int32_t *ctl;            /* [ECHO_CTL_WORDS] step counter and free-list length      */
+  uint64_t *stats;         /* [ECHO_STAT_WORDS] running totals, or NULL (not kept)   */
 } echo_layer_t;
 
 typedef struct {
@@ -191,7 +209,7 @@ int echo_ws_bind(const echo_dims_t *dims, void *base, size_t bytes, echo_ws_t *w
 
 /* Reset one layer: every slot free (free=1, prio=-1, g2h=-1), h2g=-1 for every
  * host token, idxbuf = 0..n_gpu-1, theta = guard = +inf for max_batch requests,
- * step 0. */
+ * step 0, and the running totals (if kept) zero. */
 int echo_meta_init(const echo_dims_t *dims, const echo_layer_t *layer, hipStream_t stream);
 
 /* Clear the workspace (status, counters and internal scratch). */

@@ -19,6 +19,9 @@ ECHO_THETA_EMA, ECHO_THETA_NEG_INF, ECHO_THETA_POS_INF = 0, 1, 2
  ECHO_CNT_PREFETCH, ECHO_CNT_SHORTCUT) = range(7)
 ECHO_NCOUNTERS = 16
 ECHO_CTL_STEP, ECHO_CTL_NFREE, ECHO_CTL_WORDS = 0, 1, 4
+(ECHO_STAT_STEPS, ECHO_STAT_SELECTED, ECHO_STAT_MISSED, ECHO_STAT_PREFETCHED,
+ ECHO_STAT_PF_SELECTED, ECHO_STAT_CANDIDATES, ECHO_STAT_EVICTED) = range(7)
+ECHO_STAT_WORDS = 8
 (ECHO_INV_H2G, ECHO_INV_G2H, ECHO_INV_FREE, ECHO_INV_PRIO, ECHO_INV_FREE_LIST, ECHO_INV_SELECTED,
  ECHO_INV_RESIDENT, ECHO_INV_OCCUPIED) = range(8)
 ECHO_INV_WORDS = 8
@@ -48,7 +51,7 @@ class echo_layer_meta_t(C.Structure):
 
 class echo_layer_t(C.Structure):
     _fields_ = [("meta", echo_layer_meta_t), ("k_index", P), ("gpu_kv", P), ("host_kv", P),
-                ("q", P), ("w", P), ("theta", P), ("guard", P), ("ctl", P)]
+                ("q", P), ("w", P), ("theta", P), ("guard", P), ("ctl", P), ("stats", P)]
 
 
 class echo_batch_t(C.Structure):

@@ -141,6 +141,7 @@ StepArgs make_args(const echo_dims_t &d, const echo_layer_t *l, const echo_batch
     a.guard = l->guard;
     a.ctl = l->ctl;
   }
+  a.stats = nullptr;  // only the layer step adds to the running totals
   a.scores_in = ws.scores;
   a.score_stride = d.max_ctx;
   a.theta_upd = nullptr;
@@ -374,6 +375,7 @@ int echo_meta_init(const echo_dims_t *dims, const echo_layer_t *layer, hipStream
   echo_ws_t none;
   memset(&none, 0, sizeof none);
   StepArgs a = make_args(*dims, layer, nullptr, none, ECHO_THETA_POS_INF);
+  a.stats = layer->stats;
   LAUNCH(launch_meta_init(a, stream));
   return ECHO_OK;
 }
@@ -674,6 +676,7 @@ int echo_layer_step(const echo_dims_t *dims, const echo_layer_t *layer, const ec
   StepArgs a = make_args(*dims, layer, batch, *ws, theta_mode);
   a.theta_upd = theta_mode == ECHO_THETA_EMA ? layer->theta : nullptr;
   a.guard_upd = layer->guard;
+  a.stats = layer->stats;
   a.copy_handoff = 1;  // the prefetch copy runs on through top-k and management
   rc = run_indexer(a, BEGIN_CLR_MANAGE, stream);
   if (rc != ECHO_OK) return rc;

@@ -143,7 +143,11 @@ __device__ static void manage_block(const StepArgs &a, int blk, int32_t st0) {
   }
   const int64_t want = (int64_t)nmiss + a.sc.misc[M_RESERVE] - F;
   const int n_evict = (int)(want <= 0 ? 0 : (want < nE ? want : nE));
-  if (blk == 0 && tid == 0) a.ws.counters[ECHO_CNT_EVICT] = n_evict;
+  if (blk == 0 && tid == 0) {
+    a.ws.counters[ECHO_CNT_EVICT] = n_evict;
+    if (a.stats && n_evict > 0) atomicAdd((unsigned long long *)&a.stats[ECHO_STAT_EVICTED],
+                                          (unsigned long long)n_evict);
+  }
   bool ev[4] = {false, false, false, false};
   if (n_evict > 0) {
     find_boundary<true>(a.sc.ehist, n_evict, &s_bin, &s_below, sh);
@@ -282,7 +286,10 @@ __device__ static void manage_block(const StepArgs &a, int blk, int32_t st0) {
     if (tid == 0) {
       const int done = __hip_atomic_fetch_add(&a.sc.misc[M_DONE], 1, __ATOMIC_RELAXED,
                                               __HIP_MEMORY_SCOPE_AGENT);
-      if (done == nblk - 1 && !failed(a.ws.status)) a.ctl[ECHO_CTL_STEP] = t + 1;
+      if (done == nblk - 1 && !failed(a.ws.status)) {
+        a.ctl[ECHO_CTL_STEP] = t + 1;
+        if (a.stats) atomicAdd((unsigned long long *)&a.stats[ECHO_STAT_STEPS], 1ull);
+      }
     }
   }
 }
@@ -429,6 +436,7 @@ __global__ __launch_bounds__(256) void k_meta_init(StepArgs a) {
     a.ctl[ECHO_CTL_NFREE] = a.n_gpu;
     for (int w = 2; w < ECHO_CTL_WORDS; ++w) a.ctl[w] = 0;
   }
+  if (a.stats && i0 < ECHO_STAT_WORDS) a.stats[i0] = 0;
 }
 
 hipError_t launch_meta_init(const StepArgs &a, hipStream_t s) {

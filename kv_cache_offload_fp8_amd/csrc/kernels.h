@@ -25,6 +25,7 @@ struct StepArgs {
   float *theta;   // prefetch threshold state (read by the prologue)
   float *guard;   // last k-th score per request (selection guard), or null
   int32_t *ctl;
+  uint64_t *stats;  // running totals of the layer (echo_layer_step only), or null
   // scores read by the top-k passes
   const float *scores_in;
   int64_t score_stride;

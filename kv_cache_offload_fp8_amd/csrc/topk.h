@@ -81,9 +81,9 @@ __device__ static void lds_kth_key(const uint32_t *keys, int c, int need, uint32
 }
 
 // Protect the selected tokens of request b (held in LDS) and list its misses in
-// token order.
-__device__ static void protect_request(const StepArgs &a, int b, const int32_t *s_sel, int n,
-                                       int *sh) {
+// token order.  Returns the number of misses (in every thread).
+__device__ static int protect_request(const StepArgs &a, int b, const int32_t *s_sel, int n,
+                                      int *sh) {
   const int t = a.ctl[ECHO_CTL_STEP];
   const int base = a.sc.req[b].base;
   int off = 0;
@@ -111,6 +111,40 @@ __device__ static void protect_request(const StepArgs &a, int b, const int32_t *
   if (threadIdx.x == 0) {
     a.ws.n_miss[b] = off;
     atomicAdd(&a.ws.counters[ECHO_CNT_MISS], off);
+  }
+  return off;
+}
+
+// Running totals of request b's step (a.stats): selected, missed, prefetched and
+// candidate counts, and how many of the prefetched tokens the step selected.  The
+// prefetch list pf_tok (final when the scoring kernel ended) and the selection s_sel
+// (in LDS) are both in ascending token order; each prefetched token is looked up in
+// the selection by binary search.
+__device__ static void add_step_stats(const StepArgs &a, int b, const int32_t *s_sel, int nsel,
+                                      int nmiss, int *sh) {
+  const int npf = a.ws.n_pf[b];
+  const int ncand = a.ws.n_cand[b];
+  const int32_t *pf = a.ws.pf_tok + (int64_t)b * a.K;
+  int found = 0;
+  for (int i = threadIdx.x; i < npf; i += kSelThreads) {
+    const int s = pf[i];
+    int lo = 0, hi = nsel;  // first position whose token is >= s
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (s_sel[mid] < s) lo = mid + 1;
+      else hi = mid;
+    }
+    found += (lo < nsel && s_sel[lo] == s) ? 1 : 0;
+  }
+  int tot;
+  block_excl_scan<kSelThreads>(found, sh, &tot);
+  if (threadIdx.x == 0) {
+    unsigned long long *st = (unsigned long long *)a.stats;
+    atomicAdd(&st[ECHO_STAT_SELECTED], (unsigned long long)nsel);
+    atomicAdd(&st[ECHO_STAT_MISSED], (unsigned long long)nmiss);
+    atomicAdd(&st[ECHO_STAT_PREFETCHED], (unsigned long long)npf);
+    atomicAdd(&st[ECHO_STAT_PF_SELECTED], (unsigned long long)tot);
+    atomicAdd(&st[ECHO_STAT_CANDIDATES], (unsigned long long)ncand);
   }
 }
 
@@ -299,7 +333,8 @@ __device__ static void topk_block(const StepArgs &a, int b, int32_t st0) {
   }
   if (PROTECT) {
     __syncthreads();
-    protect_request(a, b, s_sel, nsel, sh);
+    const int nmiss = protect_request(a, b, s_sel, nsel, sh);
+    if (a.stats) add_step_stats(a, b, s_sel, nsel, nmiss, sh);
   }
   // done: the fence makes this workgroup's selection, priorities and miss list
   // visible before the count (management waits for it in the fused kernel)

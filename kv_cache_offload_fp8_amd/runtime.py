@@ -231,13 +231,14 @@ class Layer:
         self.theta = torch.empty(dims.max_batch, dtype=torch.float32, device=device)
         self.guard = torch.empty(dims.max_batch, dtype=torch.float32, device=device)
         self.ctl = torch.zeros(abi.ECHO_CTL_WORDS, dtype=torch.int32, device=device)
+        self.stats = torch.zeros(abi.ECHO_STAT_WORDS, dtype=torch.int64, device=device)
         self.kidx = kidx
         self.host = host
         meta = abi.echo_layer_meta_t(_ptr(self.h2g), _ptr(self.g2h), _ptr(self.prio),
                                      _ptr(self.idxbuf), _ptr(self.free))
         self.struct = abi.echo_layer_t(meta, _ptr(kidx), _ptr(self.gpu_kv), host.dev_ptr,
                                        _ptr(self.q), _ptr(self.w), _ptr(self.theta),
-                                       _ptr(self.guard), _ptr(self.ctl))
+                                       _ptr(self.guard), _ptr(self.ctl), _ptr(self.stats))
 
     def meta_bytes(self) -> int:
         return sum(t.numel() * t.element_size()

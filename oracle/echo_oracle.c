@@ -80,9 +80,19 @@
  *      counter does not advance).  Both report a capacity error.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* Threads of the scoring loop's OpenMP team (the CPU baseline times the oracle on one
+ * thread and on every core).  Returns the previous maximum.  No arithmetic of the
+ * method depends on it. */
+int orc_set_threads(int n) {
+  const int old = omp_get_max_threads();
+  if (n > 0) omp_set_num_threads(n);
+  return old;
+}
 
 #define ORC_OK 0
 #define ORC_EINVAL (-1)

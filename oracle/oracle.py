@@ -45,6 +45,8 @@ def lib() -> C.CDLL:
         _lib.orc_e4m3_value.argtypes = [C.c_uint8]
         _lib.orc_bf16_value.restype = C.c_double
         _lib.orc_bf16_value.argtypes = [C.c_uint16]
+        _lib.orc_set_threads.restype = C.c_int
+        _lib.orc_set_threads.argtypes = [C.c_int]
         _lib.orc_meta_bytes.restype = C.c_int64
         _lib.orc_meta_bytes.argtypes = [C.c_int64, C.c_int64]
         _lib.orc_scores.restype = None
@@ -112,6 +114,11 @@ class Out(C.Structure):
 def _p(a: np.ndarray) -> int:
     assert a.flags["C_CONTIGUOUS"], "oracle buffers must be contiguous"
     return a.ctypes.data
+
+
+def set_threads(n: int) -> int:
+    """OpenMP threads of the oracle's scoring loop; returns the previous maximum."""
+    return lib().orc_set_threads(int(n))
 
 
 def e4m3_value(code: int) -> float:

@@ -56,9 +56,13 @@ WORKLOADS = {
     "single_layer": Workload("single_layer", 2, 8, 65536, 65536, 1, 64, 128, 2048, 200_000,
                              2_000_000, 0.98, 64),
     # batch 32, ctx U{80K..100K}, 61 layers, 110K GPU slots per layer.  32 x 90K on average
-    # exceeds a 2M host pool, so the host pool holds 3.2M tokens.
+    # exceeds a 2M host pool, so the host pool holds 3.2M tokens.  The prefetch cap (the
+    # pages only say it grows with the context) is ceil(ctx / 256): on this pool a sweep of
+    # the divisor from 96 to 384 was fastest at 256, where the reserve the cap implies
+    # (the sum of the caps stays free for the next step's prefetch) evicts fewer tokens
+    # that are selected again, at the same hit rate as 128.
     "capacity": Workload("capacity", 3, 32, 80_000, 100_000, 61, 64, 128, 2048, 110_000,
-                         3_200_000, 0.98, 32),
+                         3_200_000, 0.98, 32, cap_div=256),
     # batch 16 x 100K, rho 0.5 for low locality, 200K GPU slots, 2M host tokens
     "low_locality": Workload("low_locality", 4, 16, 100_000, 100_000, 1, 64, 128, 2048,
                              200_000, 2_000_000, 0.5, 32),

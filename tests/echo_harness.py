@@ -154,6 +154,10 @@ class Rig:
         self.np_w = self.inp.np_w()
         self.t = 0
         self.history = []
+        # the running totals echo_layer_step keeps (echo_layer_t.stats), as the
+        # oracle's outputs add up; compared while every step so far ended cleanly
+        self.exp_stats = np.zeros(abi.ECHO_STAT_WORDS, np.int64)
+        self.stats_valid = True
 
     # ------------------------------------------------------------ GPU calls
     def gpu_step(self, mode):
@@ -206,10 +210,29 @@ class Rig:
         self.compare(out, st, o, t, check_pool)
         assert out["status"] == expect_status, (f"step {t}: status {out['status']}",
                                                 abi.echo_status_string(int(out["status"])))
+        if o["status"] != O.OK:
+            self.stats_valid = False
+        if not self.separate and self.stats_valid:
+            self.compare_stats(o, t)
         self.history.append((out, o))
         if o["status"] == O.OK:
             self.t += 1
         return out, o
+
+    def compare_stats(self, o, t):
+        e = self.exp_stats
+        e[abi.ECHO_STAT_STEPS] += 1
+        e[abi.ECHO_STAT_SELECTED] += int(o["n_sel"].sum())
+        e[abi.ECHO_STAT_MISSED] += int(o["n_miss"].sum())
+        e[abi.ECHO_STAT_PREFETCHED] += int(o["n_pf"].sum())
+        e[abi.ECHO_STAT_CANDIDATES] += int(o["n_cand"].sum())
+        e[abi.ECHO_STAT_EVICTED] += int(o["n_evict"])
+        for b in range(self.B):
+            pf = o["pf_tok"][b, : int(o["n_pf"][b])]
+            sel = o["sel_tok"][b, : int(o["n_sel"][b])]
+            e[abi.ECHO_STAT_PF_SELECTED] += int(np.intersect1d(pf, sel).size)
+        got = self.layer.stats.cpu().numpy()
+        assert np.array_equal(got, e), (f"step {t}", "running totals", got, e)
 
     def compare(self, out, st, o, t, check_pool=True):
         tag = f"step {t}"
@@ -259,6 +282,7 @@ class Rig:
         t - 4096 fall into the eviction histogram's clamped oldest bin."""
         torch.cuda.current_stream().synchronize()
         self.layer.ctl[abi.ECHO_CTL_STEP] = int(t)
+        # the totals carry on: the jump skips no step of this layer's own
         torch.cuda.current_stream().synchronize()
         self.orc.t = int(t)
         self.t = int(t)

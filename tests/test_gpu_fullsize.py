@@ -50,12 +50,14 @@ def test_single_layer_full_size():
 
 @pytest.mark.timeout(900)
 def test_capacity_one_layer_full_size():
-    # one layer of the capacity workload: batch 32, ctx U[80K, 100K], 110,000 slots,
-    # 3.2M host tokens; the pool is too small for two steps' selections, so the
-    # third step evicts
-    _say("capacity, layer 30: 32 x U[80K,100K], EMA, 3 steps")
-    rig = H.Rig(get("capacity"), steps=3, layer=30)
-    _run(rig, 3, H.MODE_EMA)
+    # one layer of the capacity workload as the benchmark runs it: batch 32, ctx
+    # U[80K, 100K], 110,000 slots, 3.2M host tokens, prefetch cap ceil(ctx / 256); the
+    # pool fills up over the first steps (65,536 cold misses, then about 10,000
+    # prefetched rows a step) and the reserve for the next prefetch makes the fifth
+    # step evict
+    _say("capacity, layer 30: 32 x U[80K,100K], EMA, 5 steps")
+    rig = H.Rig(get("capacity"), steps=5, layer=30)
+    _run(rig, 5, H.MODE_EMA)
     assert sum(int(o["n_evict"]) for _, o in rig.history) > 0
     rig.close()
 

@@ -224,6 +224,7 @@ def test_two_layer_graph_matches_eager():
                 assert np.array_equal(a[key], b[key]), (t, key)
             assert a["t"] == b["t"] == t + 1
             assert torch.equal(re_.layer.gpu_kv, rg.layer.gpu_kv)
+            assert torch.equal(re_.layer.stats, rg.layer.stats)  # running totals too
         oa, ob = eager[0].ws.read(2), graph[0].ws.read(2)  # the last layer's outputs
         assert oa["status"] == ob["status"] == 0
         for key in ("n_sel", "n_pf", "n_miss", "kth"):
