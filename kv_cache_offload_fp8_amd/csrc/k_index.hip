@@ -787,17 +787,20 @@ __global__ __launch_bounds__(512) void k_score(StepArgs a) {
   __syncthreads();
   if (s_dead) return;
   const int wid = tid / kWave;
-  if ((int)blockIdx.x < a.score_blocks) {
+  int role_idx;
+  const bool copy = xcd_copy_role((int)blockIdx.x, (int)gridDim.x, a.copy_waves / kScoreWaves,
+                                  &role_idx);
+  if (!copy) {
     // the wave index through readfirstlane: every job index derived from it is
     // then known to be wave-uniform and lives in scalar registers
     score_wave<HG, ANY_PF>(a, s_req,
-                           __builtin_amdgcn_readfirstlane((int)blockIdx.x * kScoreWaves + wid),
+                           __builtin_amdgcn_readfirstlane(role_idx * kScoreWaves + wid),
                            &s_pend[ANY_PF ? wid : 0][0], &s_wbuf[wid]);
     if (lane_id() == 0 && atomicSub(&s_left, 1) == 1)
       __hip_atomic_fetch_add(&a.sc.misc[M_SCORE_DONE], 1, __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
   } else if (ANY_PF) {
-    copy_worker(a, s_req, (blockIdx.x - a.score_blocks) * kScoreWaves + wid, 0, 1,
+    copy_worker(a, s_req, role_idx * kScoreWaves + wid, 0, 1,
                 a.copy_handoff ? &a.sc.misc[M_SCORE_DONE] : nullptr, a.score_blocks);
   }
 }

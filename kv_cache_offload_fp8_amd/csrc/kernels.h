@@ -68,6 +68,29 @@ __device__ inline void rebuild_free_list(const StepArgs &a, int *sh) {
   if (tid == 0) a.ctl[ECHO_CTL_NFREE] = off;
 }
 
+// Workgroup roles by XCD.  MI355X deals consecutive workgroup ids to its eight XCDs
+// in turn.  When the grid has room, the nc copy workgroups take ids 0, 8, 16, ...,
+// so that all of them sit on one XCD and only that XCD's L2 carries the
+// long-latency host reads, while the workgroups that stream HBM run on the other
+// seven (measured in the capacity layer step: the scoring kernel 96-98 us with its
+// 32 copy workgroups on one XCD; the decode step 2.3% faster than with them
+// spread over all eight).  Otherwise the last nc ids copy.  Returns true for a
+// copy workgroup; *idx is its rank among the copy workgroups, or among the others.
+__device__ inline bool xcd_copy_role(int bid, int grid, int nc, int *idx) {
+  if (nc > 0 && 8 * (nc - 1) < grid) {
+    if ((bid & 7) == 0 && (bid >> 3) < nc) {
+      *idx = bid >> 3;
+      return true;
+    }
+    const int below = (bid + 7) >> 3;  // copy ids 0, 8, .. below bid
+    *idx = bid - (below < nc ? below : nc);
+    return false;
+  }
+  const int first = grid - nc;
+  *idx = bid >= first ? bid - first : bid;
+  return bid >= first;
+}
+
 // begin-kernel roles
 enum {
   BEGIN_REQ = 1,         // request table, scoring jobs, reserve
