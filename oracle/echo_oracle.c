@@ -78,6 +78,17 @@
  *      nothing changes; if the rest of the union then exceeds what is left,
  *      the candidates stay installed and nothing else changes (the step
  *      counter does not advance).  Both report a capacity error.
+ *  R14 Page tables: a request's tokens need not occupy one contiguous host
+ *      range.  The host pool is cut into pages of 16 consecutive host ids
+ *      (one group of the tiled indexer K), and a request holds a list of
+ *      pages: its token s is host id 16 * page[s / 16] + s % 16.  Every map,
+ *      score, install, copy and release goes through that translation;
+ *      nothing else in the step changes.  Pages of live requests are
+ *      distinct: admission checks that the new request's pages are in the
+ *      pool, listed once, and shared with no live request (a page shared with
+ *      one is a capacity error, like an overlapping range); a decode append
+ *      writes into the page its request lists for the new token (the caller
+ *      hands out pages) and checks that it exists and is not mapped.
  */
 #include <math.h>
 #include <omp.h>
@@ -98,6 +109,34 @@ int orc_set_threads(int n) {
 #define ORC_EINVAL (-1)
 #define ORC_ECAPACITY (-4)
 #define ORC_EDEVARG (-6)
+
+/* Where each request's tokens live in the host pool (R14).  With a page table
+ * (pages != NULL), token s of request b is host id
+ * 16 * pages[b * page_stride + s / 16] + s % 16; without one, host_base[b] + s.
+ * host_base is written by admission in the contiguous case. */
+typedef struct {
+  int32_t *host_base;   /* [B], or NULL with a page table */
+  const int32_t *pages; /* [B][page_stride], or NULL     */
+  int32_t page_stride;
+} orc_tokmap;
+
+static int64_t host_id(const orc_tokmap *m, int b, int64_t s) {
+  if (m->pages) return 16 * (int64_t)m->pages[(int64_t)b * m->page_stride + s / 16] + s % 16;
+  return (int64_t)m->host_base[b] + s;
+}
+
+/* Whether request b's first n tokens all have a host id in [0, n_host): every page
+ * they use lies in the pool (with a page table), or the range fits (without). */
+static int tokens_fit(const orc_tokmap *m, int b, int64_t n, int64_t n_host) {
+  if (n < 0) return 0;
+  if (!m->pages) return m->host_base[b] >= 0 && (int64_t)m->host_base[b] + n <= n_host;
+  if ((n + 15) / 16 > m->page_stride) return 0;
+  for (int64_t j = 0; j < (n + 15) / 16; ++j) {
+    const int32_t p = m->pages[(int64_t)b * m->page_stride + j];
+    if (p < 0 || 16 * (int64_t)p + 16 > n_host) return 0;
+  }
+  return 1;
+}
 
 #define ORC_MODE_EMA 0
 #define ORC_MODE_NEG_INF 1
@@ -274,10 +313,10 @@ static int cmp_prio_slot(const void *a, const void *b) {
 /* One decode step of one layer for a batch of B requests.
  * q: bf16 [B][H][D]; w: fp32 [B][H]; kidx: e4m3 [n_host][D];
  * host_kv: bf16 [n_host][latent] (may be NULL when st->pool is NULL);
- * host_base/ctx: [B] (request b owns host ids host_base[b] + s, s < ctx[b]);
+ * map/ctx: request b's token s < ctx[b] is host id host_id(map, b, s);
  * ext_scores: NULL, or [B][ctx_stride] scores to use instead of computing. */
 int orc_layer_step(const orc_cfg *c, orc_state *st, int B,
-                   const int32_t *host_base, const int32_t *ctx,
+                   const orc_tokmap *map, const int32_t *ctx,
                    const uint16_t *q, const float *w, const uint8_t *kidx,
                    const uint16_t *host_kv, int mode, const float *ext_scores,
                    int64_t ctx_stride, orc_out *o) {
@@ -289,11 +328,19 @@ int orc_layer_step(const orc_cfg *c, orc_state *st, int B,
   /* scores (P1 problem statement; R1, R2) */
   for (int b = 0; b < B; ++b) {
     float *sb = o->scores + (int64_t)b * ctx_stride;
-    if (ext_scores)
+    if (ext_scores) {
       memcpy(sb, ext_scores + (int64_t)b * ctx_stride, sizeof(float) * (size_t)ctx[b]);
-    else
+    } else if (!map->pages) {
       orc_scores(c->H, c->D, q + (int64_t)b * c->H * c->D, w + (int64_t)b * c->H,
-                 kidx + (int64_t)host_base[b] * c->D, ctx[b], sb);
+                 kidx + (int64_t)map->host_base[b] * c->D, ctx[b], sb);
+    } else { /* the request's key rows, gathered in token order */
+      uint8_t *rows = (uint8_t *)malloc((size_t)(ctx[b] > 0 ? ctx[b] : 1) * (size_t)c->D);
+      for (int64_t s = 0; s < ctx[b]; ++s)
+        memcpy(rows + s * c->D, kidx + host_id(map, b, s) * c->D, (size_t)c->D);
+      orc_scores(c->H, c->D, q + (int64_t)b * c->H * c->D, w + (int64_t)b * c->H, rows, ctx[b],
+                 sb);
+      free(rows);
+    }
   }
 
   /* prefetch during scoring (P1 decode; R5) */
@@ -319,7 +366,7 @@ int orc_layer_step(const orc_cfg *c, orc_state *st, int B,
     if (active) {
       const float *sb = o->scores + (int64_t)b * ctx_stride;
       for (int64_t s = 0; s < ctx[b]; ++s) {
-        int64_t h = host_base[b] + s;
+        int64_t h = host_id(map, b, s);
         if (sb[s] > th && st->h2g[h] == -1) {
           ++ncand;
           if (r < cap && off + r < nF) {
@@ -354,7 +401,7 @@ int orc_layer_step(const orc_cfg *c, orc_state *st, int B,
     int32_t nm = 0;
     for (int i = 0; i < o->n_sel[b]; ++i) {
       int32_t s = o->sel_tok[(int64_t)b * k + i];
-      int64_t h = host_base[b] + s;
+      int64_t h = host_id(map, b, s);
       int32_t g = st->h2g[h];
       o->sel_slot[(int64_t)b * k + i] = g;
       if (g >= 0)
@@ -403,11 +450,11 @@ int orc_layer_step(const orc_cfg *c, orc_state *st, int B,
   for (int b = 0; b < B; ++b) {
     for (int j = 0; j < o->n_miss[b]; ++j, ++i) {
       int32_t s = o->miss_tok[(int64_t)b * k + j];
-      int64_t h = host_base[b] + s;
+      int64_t h = host_id(map, b, s);
       install(c, st, h, F[i], host_kv);
     }
     for (int j = 0; j < o->n_sel[b]; ++j) {
-      int64_t h = host_base[b] + o->sel_tok[(int64_t)b * k + j];
+      int64_t h = host_id(map, b, o->sel_tok[(int64_t)b * k + j]);
       o->sel_slot[(int64_t)b * k + j] = st->h2g[h];
     }
   }
@@ -421,33 +468,39 @@ int orc_layer_step(const orc_cfg *c, orc_state *st, int B,
  * management" (the KV of every token is backed up to the host pool when it is
  * generated, and the indexer K stays on the GPU) and "Design trade-offs" (every
  * new token is written back).  Reading R10: for request b the new token takes
- * host id h = host_base[b] + ctx[b]; key row kidx[h] = k_new[b] (D bytes) and
+ * host id h = host_id(map, b, ctx[b]); key row kidx[h] = k_new[b] (D bytes) and
  * latent host_kv[h] = lat_new[b] (`latent` values); with `advance`, ctx[b] grows
  * by one.  The requests are checked first, in order: no room (ctx[b] = max_ctx,
- * h >= n_host, or h inside another request's range [host_base[o],
- * host_base[o] + ctx[o]] counting that request's own new token) gives
- * ORC_ECAPACITY, a host id some slot already maps (h2g[h] != -1) gives
- * ORC_EDEVARG; the first such request decides and nothing is written.
+ * the id outside the pool -- past n_host, or with a page table a page slot past
+ * page_stride or a page outside the pool -- or, without a page table, h inside
+ * another request's range [host_base[o], host_base[o] + ctx[o]] counting that
+ * request's own new token) gives ORC_ECAPACITY, a host id some slot already maps
+ * (h2g[h] != -1) gives ORC_EDEVARG; the first such request decides and nothing
+ * is written.  With a page table the page is the caller's choice (R14).
  * A batch row with ctx[b] = 0 is empty (never admitted, or released): it takes
  * no token, is not checked, does not grow, and its stale host_base occupies no
  * range in the other requests' checks. */
 int orc_append(int B, int D, int latent, int64_t n_host, int32_t max_ctx,
-               const int32_t *host_base, int32_t *ctx, const int32_t *h2g,
+               const orc_tokmap *map, int32_t *ctx, const int32_t *h2g,
                const uint8_t *k_new, const uint16_t *lat_new, uint8_t *kidx,
                uint16_t *host_kv, int advance) {
   for (int b = 0; b < B; ++b) {
     if (ctx[b] == 0) continue; /* an empty row */
-    const int64_t h = (int64_t)host_base[b] + ctx[b];
-    if (ctx[b] < 0 || ctx[b] >= max_ctx || host_base[b] < 0 || h >= n_host) return ORC_ECAPACITY;
-    for (int o = 0; o < B; ++o) {
-      if (o == b || ctx[o] == 0) continue;
-      if (h >= host_base[o] && h < (int64_t)host_base[o] + ctx[o] + 1) return ORC_ECAPACITY;
+    if (ctx[b] < 0 || ctx[b] >= max_ctx || !tokens_fit(map, b, (int64_t)ctx[b] + 1, n_host))
+      return ORC_ECAPACITY;
+    const int64_t h = host_id(map, b, ctx[b]);
+    if (!map->pages) {
+      const int32_t *hb = map->host_base;
+      for (int o = 0; o < B; ++o) {
+        if (o == b || ctx[o] == 0) continue;
+        if (h >= hb[o] && h < (int64_t)hb[o] + ctx[o] + 1) return ORC_ECAPACITY;
+      }
     }
     if (h2g[h] != -1) return ORC_EDEVARG;
   }
   for (int b = 0; b < B; ++b) {
     if (ctx[b] == 0) continue;
-    const int64_t h = (int64_t)host_base[b] + ctx[b];
+    const int64_t h = host_id(map, b, ctx[b]);
     memcpy(kidx + h * D, k_new + (int64_t)b * D, (size_t)D);
     if (host_kv)
       memcpy(host_kv + h * latent, lat_new + (int64_t)b * latent, (size_t)latent * 2);
@@ -462,15 +515,15 @@ int orc_append(int B, int D, int latent, int64_t n_host, int32_t max_ctx,
  * exact top-k every selected token's KV must be present before the sparse
  * attention runs; "lossless" means the attention sees exactly these rows) and
  * [P2] (prediction only decides when data moves, never which data is read).
- * Reading R11: out[b][i] = host_kv[host_base[b] + sel_tok[b][i]] (`latent`
+ * Reading R11: out[b][i] = host_kv[host_id(map, b, sel_tok[b][i])] (`latent`
  * values) for i < n_sel[b], zero for n_sel[b] <= i < k.  sel_tok is [B][k]. */
-void orc_gather(int B, int k, int latent, const int32_t *host_base, const int32_t *sel_tok,
+void orc_gather(int B, int k, int latent, const orc_tokmap *map, const int32_t *sel_tok,
                 const int32_t *n_sel, const uint16_t *host_kv, uint16_t *out) {
   for (int b = 0; b < B; ++b) {
     for (int i = 0; i < k; ++i) {
       uint16_t *o = out + ((int64_t)b * k + i) * latent;
       if (i < n_sel[b]) {
-        const int64_t h = (int64_t)host_base[b] + sel_tok[(int64_t)b * k + i];
+        const int64_t h = host_id(map, b, sel_tok[(int64_t)b * k + i]);
         memcpy(o, host_kv + h * latent, (size_t)latent * 2);
       } else {
         memset(o, 0, (size_t)latent * 2);
@@ -484,25 +537,26 @@ void orc_gather(int B, int k, int latent, const int32_t *host_base, const int32_
  * attention input must stay equal to the no-offload baseline under request
  * cancellation), with the state of "Core method / in-graph per-layer cache
  * management".  Reading R12: for every request b with mask[b] != 0, each host
- * id h of [host_base[b], host_base[b] + ctx[b]) that maps a slot g gives it
+ * id h = host_id(map, b, s), s < ctx[b], that maps a slot g gives it
  * back (g2h[g] = -1, free[g] = 1, prio[g] = -1) and h2g[h] becomes -1; then
  * theta[b] = +inf, and with `commit` ctx[b] = 0 (the batch row is shared by all
- * layers: it is emptied with the last one).  A masked request whose range does not fit
- * (ctx < 0, ctx > max_ctx, host_base < 0 or past n_host) gives ORC_EDEVARG,
- * checked for all masked requests before anything changes. */
-int orc_release(int B, int64_t n_host, int32_t max_ctx, const int32_t *host_base, int32_t *ctx,
+ * layers: it is emptied with the last one).  A masked request whose tokens do not
+ * fit (ctx < 0, ctx > max_ctx, an id outside the pool: host_base < 0 or past
+ * n_host, or a page outside the pool or past page_stride) gives ORC_EDEVARG,
+ * checked for all masked requests before anything changes.  The host pages stay
+ * the caller's (R14). */
+int orc_release(int B, int64_t n_host, int32_t max_ctx, const orc_tokmap *map, int32_t *ctx,
                 const int32_t *mask, int32_t *h2g, int32_t *g2h, int32_t *prio, uint8_t *freef,
                 float *theta, int commit) {
   for (int b = 0; b < B; ++b) {
     if (!mask[b]) continue;
-    if (ctx[b] < 0 || ctx[b] > max_ctx || host_base[b] < 0 ||
-        (int64_t)host_base[b] + ctx[b] > n_host)
+    if (ctx[b] < 0 || ctx[b] > max_ctx || !tokens_fit(map, b, ctx[b], n_host))
       return ORC_EDEVARG;
   }
   for (int b = 0; b < B; ++b) {
     if (!mask[b]) continue;
     for (int32_t s = 0; s < ctx[b]; ++s) {
-      const int64_t h = (int64_t)host_base[b] + s;
+      const int64_t h = host_id(map, b, s);
       const int32_t g = h2g[h];
       if (g >= 0) {
         g2h[g] = -1;
@@ -518,28 +572,53 @@ int orc_release(int B, int64_t n_host, int32_t max_ctx, const int32_t *host_base
 }
 
 /* Request admission, the other half of R12.  Request b (an empty batch row)
- * takes the host range [base, base + len).  Checks, in order: b outside
- * [0, B), len outside [0, max_ctx], base < 0 or base + len > n_host give
- * ORC_EINVAL; a row still in use (ctx[b] != 0) gives ORC_EDEVARG; a range
- * meeting the range of another request o with ctx[o] > 0 gives
- * ORC_ECAPACITY; a host id of the range that some slot still maps gives
- * ORC_EDEVARG.  Nothing changes on an error.  Otherwise theta[b] = +inf, and
- * with `commit` (the last layer) host_base[b] = base and ctx[b] = len. */
-int orc_admit(int B, int64_t n_host, int32_t max_ctx, int32_t *host_base, int32_t *ctx,
+ * takes len tokens.  Without a page table they are the host range
+ * [base, base + len); with one (R14) they are the first len ids of the pages the
+ * caller listed in row b of the table, and base is not used.  Checks, in order:
+ * b outside [0, B), len outside [0, max_ctx], or (without a page table) base < 0
+ * or base + len > n_host give ORC_EINVAL; a row still in use (ctx[b] != 0) gives
+ * ORC_EDEVARG; with a page table, more pages than page_stride, a page outside
+ * the pool or a page listed twice gives ORC_EDEVARG; a range meeting the range of
+ * another request o with ctx[o] > 0 (with a page table: a page that one of o's
+ * tokens uses) gives ORC_ECAPACITY; a host id of the new tokens that some slot
+ * still maps gives ORC_EDEVARG.  Nothing changes on an error.  Otherwise
+ * theta[b] = +inf, and with `commit` (the last layer) ctx[b] = len and, without a
+ * page table, host_base[b] = base. */
+int orc_admit(int B, int64_t n_host, int32_t max_ctx, const orc_tokmap *map, int32_t *ctx,
               const int32_t *h2g, float *theta, int b, int32_t base, int32_t len, int commit) {
-  if (b < 0 || b >= B || len < 0 || len > max_ctx || base < 0 || (int64_t)base + len > n_host)
-    return ORC_EINVAL;
+  if (b < 0 || b >= B || len < 0 || len > max_ctx) return ORC_EINVAL;
+  if (!map->pages && (base < 0 || (int64_t)base + len > n_host)) return ORC_EINVAL;
   if (ctx[b] != 0) return ORC_EDEVARG;
-  for (int o = 0; o < B; ++o) {
-    if (o == b || ctx[o] <= 0) continue;
-    const int64_t lo = host_base[o], hi = (int64_t)host_base[o] + ctx[o];
-    if ((int64_t)base < hi && lo < (int64_t)base + len) return ORC_ECAPACITY;
+  const int64_t np = ((int64_t)len + 15) / 16;
+  if (map->pages) {
+    if (np > map->page_stride) return ORC_EDEVARG;
+    const int32_t *row = map->pages + (int64_t)b * map->page_stride;
+    for (int64_t j = 0; j < np; ++j) {
+      if (row[j] < 0 || 16 * (int64_t)row[j] + 16 > n_host) return ORC_EDEVARG;
+      for (int64_t i = 0; i < j; ++i)
+        if (row[i] == row[j]) return ORC_EDEVARG;
+    }
+    for (int o = 0; o < B; ++o) {
+      if (o == b || ctx[o] <= 0) continue;
+      const int32_t *ro = map->pages + (int64_t)o * map->page_stride;
+      for (int64_t i = 0; i < ((int64_t)ctx[o] + 15) / 16; ++i)
+        for (int64_t j = 0; j < np; ++j)
+          if (ro[i] == row[j]) return ORC_ECAPACITY;
+    }
+    for (int32_t s = 0; s < len; ++s)
+      if (h2g[16 * (int64_t)row[s / 16] + s % 16] != -1) return ORC_EDEVARG;
+  } else {
+    for (int o = 0; o < B; ++o) {
+      if (o == b || ctx[o] <= 0) continue;
+      const int64_t lo = map->host_base[o], hi = (int64_t)map->host_base[o] + ctx[o];
+      if ((int64_t)base < hi && lo < (int64_t)base + len) return ORC_ECAPACITY;
+    }
+    for (int32_t s = 0; s < len; ++s)
+      if (h2g[(int64_t)base + s] != -1) return ORC_EDEVARG;
   }
-  for (int32_t s = 0; s < len; ++s)
-    if (h2g[(int64_t)base + s] != -1) return ORC_EDEVARG;
   theta[b] = INFINITY;
   if (commit) {
-    host_base[b] = base;
+    if (!map->pages) map->host_base[b] = base;
     ctx[b] = len;
   }
   return ORC_OK;

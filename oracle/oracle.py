@@ -57,16 +57,16 @@ def lib() -> C.CDLL:
         _lib.orc_ema_update.restype = C.c_float
         _lib.orc_ema_update.argtypes = [C.c_float, C.c_float, C.c_float]
         _lib.orc_append.restype = C.c_int
-        _lib.orc_append.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int64, C.c_int32, C.c_void_p,
-                                    C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
-                                    C.c_void_p, C.c_int]
+        _lib.orc_append.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int64, C.c_int32,
+                                    C.POINTER(TokMap), C.c_void_p, C.c_void_p, C.c_void_p,
+                                    C.c_void_p, C.c_void_p, C.c_void_p, C.c_int]
         _lib.orc_gather.restype = None
         _lib.orc_release.restype = C.c_int
-        _lib.orc_release.argtypes = [C.c_int, C.c_int64, C.c_int32] + [C.c_void_p] * 8 + \
-            [C.c_int]
+        _lib.orc_release.argtypes = [C.c_int, C.c_int64, C.c_int32, C.POINTER(TokMap)] + \
+            [C.c_void_p] * 7 + [C.c_int]
         _lib.orc_admit.restype = C.c_int
-        _lib.orc_admit.argtypes = [C.c_int, C.c_int64, C.c_int32] + [C.c_void_p] * 4 + \
-            [C.c_int, C.c_int32, C.c_int32, C.c_int]
+        _lib.orc_admit.argtypes = [C.c_int, C.c_int64, C.c_int32, C.POINTER(TokMap)] + \
+            [C.c_void_p] * 3 + [C.c_int, C.c_int32, C.c_int32, C.c_int]
         _lib.orc_f16_bits.restype = C.c_uint16
         _lib.orc_f16_bits.argtypes = [C.c_float]
         _lib.orc_f16_bucket.restype = C.c_int
@@ -75,14 +75,39 @@ def lib() -> C.CDLL:
         _lib.orc_prefill_chunk.argtypes = [C.POINTER(Cfg), C.POINTER(State), C.c_int, C.c_int32,
                                            C.c_int64] + [C.c_void_p] * 6 + \
             [C.POINTER(PrefillOut)]
-        _lib.orc_gather.argtypes = [C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p,
+        _lib.orc_gather.argtypes = [C.c_int, C.c_int, C.c_int, C.POINTER(TokMap), C.c_void_p,
                                     C.c_void_p, C.c_void_p, C.c_void_p]
         _lib.orc_layer_step.restype = C.c_int
         _lib.orc_layer_step.argtypes = [C.POINTER(Cfg), C.POINTER(State), C.c_int,
-                                        C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                        C.POINTER(TokMap), C.c_void_p, C.c_void_p, C.c_void_p,
                                         C.c_void_p, C.c_void_p, C.c_int, C.c_void_p,
                                         C.c_int64, C.POINTER(Out)]
     return _lib
+
+
+class TokMap(C.Structure):
+    """Where each request's tokens live: host_base (contiguous ranges) or a page table
+    [B][page_stride] of 16-id host pages (R14 in the C source)."""
+    _fields_ = [("host_base", C.c_void_p), ("pages", C.c_void_p), ("page_stride", C.c_int32)]
+
+
+def _tokmap(host_base, pages):
+    """(TokMap, arrays it points into).  pages: int32 [B, page_stride] or None."""
+    if pages is not None:
+        pages = np.ascontiguousarray(pages, np.int32)
+        assert pages.ndim == 2
+        return TokMap(None, pages.ctypes.data, pages.shape[1]), (pages,)
+    assert host_base.dtype == np.int32 and host_base.flags["C_CONTIGUOUS"]
+    return TokMap(host_base.ctypes.data, None, 0), (host_base,)
+
+
+def page_host_ids(pages, ctx):
+    """Host ids of each request's tokens under a page table: list of int64 arrays."""
+    out = []
+    for b, n in enumerate(np.asarray(ctx)):
+        s = np.arange(int(n), dtype=np.int64)
+        out.append(16 * pages[b, s // 16].astype(np.int64) + s % 16)
+    return out
 
 
 class Cfg(C.Structure):
@@ -154,11 +179,12 @@ def topk(sc: np.ndarray, k: int) -> tuple[np.ndarray, float]:
 
 
 def append(host_base, ctx, h2g, k_new, lat_new, kidx, host_kv, max_ctx: int,
-           advance: bool = True) -> int:
+           advance: bool = True, pages=None) -> int:
     """Decode append (orc_append): writes each request's new token into kidx (uint8
-    [n_host, D]) and host_kv (uint16 [n_host, latent] or None) at host_base + ctx, then
-    grows ctx (int32, in place) if ``advance``.  Returns OK or the error code."""
-    host_base = np.ascontiguousarray(host_base, np.int32)
+    [n_host, D]) and host_kv (uint16 [n_host, latent] or None) at its next host id
+    (host_base + ctx, or through the page table ``pages``), then grows ctx (int32, in
+    place) if ``advance``.  Returns OK or the error code."""
+    host_base = np.ascontiguousarray(host_base if host_base is not None else [0], np.int32)
     assert ctx.dtype == np.int32 and ctx.flags["C_CONTIGUOUS"]
     h2g = np.ascontiguousarray(h2g, np.int32)
     k_new = np.ascontiguousarray(k_new, np.uint8)
@@ -169,48 +195,55 @@ def append(host_base, ctx, h2g, k_new, lat_new, kidx, host_kv, max_ctx: int,
     assert k_new.shape == (B, D) and kidx.flags["C_CONTIGUOUS"]
     if host_kv is not None:
         assert host_kv.flags["C_CONTIGUOUS"] and host_kv.shape[1] == latent
-    return lib().orc_append(B, D, latent, kidx.shape[0], int(max_ctx), _p(host_base), _p(ctx),
+    tm, _keep = _tokmap(host_base, pages)
+    return lib().orc_append(B, D, latent, kidx.shape[0], int(max_ctx), C.byref(tm), _p(ctx),
                             _p(h2g), _p(k_new), _p(lat_new), _p(kidx),
                             _p(host_kv) if host_kv is not None else None, int(bool(advance)))
 
 
-def gather(host_base, sel_tok, n_sel, host_kv) -> np.ndarray:
+def gather(host_base, sel_tok, n_sel, host_kv, pages=None) -> np.ndarray:
     """Attention input without offloading (orc_gather): uint16 [B, k, latent], the host
     latents of each request's selected tokens in selection order, zero past n_sel."""
-    host_base = np.ascontiguousarray(host_base, np.int32)
+    host_base = np.ascontiguousarray(host_base if host_base is not None else [0], np.int32)
     sel_tok = np.ascontiguousarray(sel_tok, np.int32)
     n_sel = np.ascontiguousarray(n_sel, np.int32)
     host_kv = np.ascontiguousarray(host_kv, np.uint16)
     B, k = sel_tok.shape
     latent = host_kv.shape[1]
     out = np.empty((B, k, latent), np.uint16)
-    lib().orc_gather(B, k, latent, _p(host_base), _p(sel_tok), _p(n_sel), _p(host_kv), _p(out))
+    tm, _keep = _tokmap(host_base, pages)
+    lib().orc_gather(B, k, latent, C.byref(tm), _p(sel_tok), _p(n_sel), _p(host_kv), _p(out))
     return out
 
 
-def release(layer, host_base, ctx, mask, max_ctx: int, commit: bool = True) -> int:
+def release(layer, host_base, ctx, mask, max_ctx: int, commit: bool = True, pages=None) -> int:
     """Request cancellation (orc_release) on an OracleLayer's state: the masked
     requests' slots and map rows are given back, theta resets, and with ``commit`` ctx
     (int32, in place) becomes 0.  Returns OK or the error code."""
-    host_base = np.ascontiguousarray(host_base, np.int32)
+    host_base = np.ascontiguousarray(host_base if host_base is not None else [0], np.int32)
     assert ctx.dtype == np.int32 and ctx.flags["C_CONTIGUOUS"]
     mask = np.ascontiguousarray(mask, np.int32)
     B = int(ctx.size)
-    assert host_base.size == B and mask.size == B and layer.theta.size >= B
-    return lib().orc_release(B, layer.cfg.n_host, int(max_ctx), _p(host_base), _p(ctx),
+    assert (pages is not None or host_base.size == B) and mask.size == B and \
+        layer.theta.size >= B
+    tm, _keep = _tokmap(host_base, pages)
+    return lib().orc_release(B, layer.cfg.n_host, int(max_ctx), C.byref(tm), _p(ctx),
                              _p(mask), _p(layer.h2g), _p(layer.g2h), _p(layer.prio),
                              _p(layer.free), _p(layer.theta), int(bool(commit)))
 
 
 def admit(layer, host_base, ctx, b: int, base: int, length: int, max_ctx: int,
-          commit: bool = True) -> int:
+          commit: bool = True, pages=None) -> int:
     """Request admission (orc_admit) into batch row b: if the checks pass theta[b]
-    resets and, with ``commit``, host_base and ctx (int32, in place) take (base,
-    length).  Returns OK or the error code."""
-    assert host_base.dtype == np.int32 and host_base.flags["C_CONTIGUOUS"]
+    resets and, with ``commit``, ctx[b] = length and (without a page table) host_base[b]
+    = base (int32 arrays, in place).  With ``pages`` the caller has written row b of the
+    page table.  Returns OK or the error code."""
+    if host_base is None:
+        host_base = np.zeros(1, np.int32)
     assert ctx.dtype == np.int32 and ctx.flags["C_CONTIGUOUS"]
     B = int(ctx.size)
-    return lib().orc_admit(B, layer.cfg.n_host, int(max_ctx), _p(host_base), _p(ctx),
+    tm, _keep = _tokmap(host_base, pages)
+    return lib().orc_admit(B, layer.cfg.n_host, int(max_ctx), C.byref(tm), _p(ctx),
                            _p(layer.h2g), _p(layer.theta), int(b), int(base), int(length),
                            int(bool(commit)))
 
@@ -289,13 +322,16 @@ class OracleLayer:
         self.t = 0
         self.max_batch = max_batch
 
-    def step(self, host_base, ctx, q, w, kidx, host_kv, mode=MODE_EMA, ext_scores=None):
+    def step(self, host_base, ctx, q, w, kidx, host_kv, mode=MODE_EMA, ext_scores=None,
+             pages=None):
         """One decode step.  q: uint16 [B, H, D]; w: float32 [B, H]; kidx: uint8 [n_host, D];
-        host_kv: uint16 [n_host, latent] or None; ext_scores: float32 [B, >= max ctx] or None.
+        host_kv: uint16 [n_host, latent] or None; ext_scores: float32 [B, >= max ctx] or None;
+        pages: int32 [B, page_stride] page table, or None for host_base ranges.
         Returns a dict of outputs (numpy arrays, trimmed to their counts)."""
         cfg = self.cfg
         k = cfg.k
-        host_base = np.ascontiguousarray(host_base, np.int32)
+        host_base = np.ascontiguousarray(host_base if host_base is not None else
+                                         np.zeros(len(ctx), np.int32), np.int32)
         ctx = np.ascontiguousarray(ctx, np.int32)
         B = int(ctx.size)
         stride = max(1, int(ctx.max()) if B else 1)
@@ -307,8 +343,10 @@ class OracleLayer:
         kidx = np.ascontiguousarray(kidx, np.uint8)
         assert q.shape == (B, cfg.H, cfg.D) and w.shape == (B, cfg.H)
         assert kidx.shape == (cfg.n_host, cfg.D)
-        if B:
+        if B and pages is None:
             assert int((host_base.astype(np.int64) + ctx).max()) <= cfg.n_host
+        if B and pages is not None:
+            assert all(int(h.max()) < cfg.n_host for h in page_host_ids(pages, ctx) if h.size)
         if host_kv is not None:
             host_kv = np.ascontiguousarray(host_kv, np.uint16)
             assert host_kv.shape == (cfg.n_host, cfg.latent)
@@ -325,7 +363,8 @@ class OracleLayer:
         theta = np.ascontiguousarray(self.theta)
         st = State(_p(self.h2g), _p(self.g2h), _p(self.prio), _p(self.free), _p(theta), self.t,
                    _p(self.pool) if self.pool is not None else None)
-        rc = lib().orc_layer_step(C.byref(cfg), C.byref(st), B, _p(host_base), _p(ctx), _p(q),
+        tm, _keep = _tokmap(host_base, pages)
+        rc = lib().orc_layer_step(C.byref(cfg), C.byref(st), B, C.byref(tm), _p(ctx), _p(q),
                                   _p(w), _p(kidx),
                                   _p(host_kv) if host_kv is not None else None, int(mode),
                                   _p(ext_scores) if ext_scores is not None else None,

@@ -44,17 +44,16 @@ MUTANTS = {
     "prefetch_ignores_offset": ("int32_t g = F[off + r];", "int32_t g = F[r];"),
     "metadata_idxbuf_dropped": ("int64_t per_slot = 1 + 4 + 4 + 4;",
                                 "int64_t per_slot = 1 + 4 + 4;"),
-    "append_overwrites_last_row": ("const int64_t h = (int64_t)host_base[b] + ctx[b];\n    memcpy",
-                                   "const int64_t h = (int64_t)host_base[b] + ctx[b] - 1;\n"
-                                   "    memcpy"),
-    "gather_ignores_host_base": ("const int64_t h = (int64_t)host_base[b] + sel_tok[(int64_t)b * k + i];",
+    "append_overwrites_last_row": ("const int64_t h = host_id(map, b, ctx[b]);\n    memcpy",
+                                   "const int64_t h = host_id(map, b, ctx[b] - 1);\n    memcpy"),
+    "gather_ignores_token_map": ("const int64_t h = host_id(map, b, sel_tok[(int64_t)b * k + i]);",
                                  "const int64_t h = sel_tok[(int64_t)b * k + i];"),
     "release_keeps_priority": ("        freef[g] = 1;\n        prio[g] = -1;\n",
                                "        freef[g] = 1;\n"),
     "release_skips_last_token": ("for (int32_t s = 0; s < ctx[b]; ++s) {\n      const int64_t h = "
-                                 "(int64_t)host_base[b] + s;\n      const int32_t g = h2g[h];",
+                                 "host_id(map, b, s);\n      const int32_t g = h2g[h];",
                                  "for (int32_t s = 0; s < ctx[b] - 1; ++s) {\n      const int64_t h = "
-                                 "(int64_t)host_base[b] + s;\n      const int32_t g = h2g[h];"),
+                                 "host_id(map, b, s);\n      const int32_t g = h2g[h];"),
     "release_keeps_threshold": ("    theta[b] = INFINITY;\n    if (commit) ctx[b] = 0;\n",
                                 "    if (commit) ctx[b] = 0;\n"),
     "admit_ignores_overlap": ("if ((int64_t)base < hi && lo < (int64_t)base + len) return ORC_ECAPACITY;",
@@ -79,13 +78,26 @@ MUTANTS = {
     "append_empty_row_blocks_neighbours": ("      if (o == b || ctx[o] == 0) continue;",
                                            "      if (o == b) continue;"),
     "append_writes_empty_row_bytes": ("  for (int b = 0; b < B; ++b) {\n    if (ctx[b] == 0) continue;\n"
-                                      "    const int64_t h = (int64_t)host_base[b] + ctx[b];\n    memcpy",
+                                      "    const int64_t h = host_id(map, b, ctx[b]);\n    memcpy",
                                       "  for (int b = 0; b < B; ++b) {\n"
-                                      "    const int64_t h = (int64_t)host_base[b] + ctx[b];\n    memcpy"),
+                                      "    const int64_t h = host_id(map, b, ctx[b]);\n    memcpy"),
     "append_grows_empty_rows": ("      if (ctx[b] != 0) ctx[b] += 1;", "      ctx[b] += 1;"),
-    "append_ignores_neighbours": ("if (h >= host_base[o] && h < (int64_t)host_base[o] + ctx[o] + 1) "
-                                  "return ORC_ECAPACITY;",
+    "append_ignores_neighbours": ("if (h >= hb[o] && h < (int64_t)hb[o] + ctx[o] + 1) return ORC_ECAPACITY;",
                                   "if (0) return ORC_ECAPACITY;"),
+    # page tables (R14)
+    "page_offset_dropped": ("return 16 * (int64_t)m->pages[(int64_t)b * m->page_stride + s / 16] + s % 16;",
+                            "return 16 * (int64_t)m->pages[(int64_t)b * m->page_stride + s / 16];"),
+    "page_stride_ignored": ("return 16 * (int64_t)m->pages[(int64_t)b * m->page_stride + s / 16] + s % 16;",
+                            "return 16 * (int64_t)m->pages[(int64_t)b + s / 16] + s % 16;"),
+    "paged_scores_read_row_order": ("memcpy(rows + s * c->D, kidx + host_id(map, b, s) * c->D, (size_t)c->D);",
+                                    "memcpy(rows + s * c->D, kidx + s * c->D, (size_t)c->D);"),
+    "paged_prefetch_ignores_pages": ("        int64_t h = host_id(map, b, s);\n        if (sb[s] > th",
+                                     "        int64_t h = s;\n        if (sb[s] > th"),
+    "admit_ignores_shared_page": ("if (ro[i] == row[j]) return ORC_ECAPACITY;", "(void)ro;"),
+    "admit_ignores_repeated_page": ("if (row[i] == row[j]) return ORC_EDEVARG;", "(void)i;"),
+    "admit_page_range_unchecked": ("if (row[j] < 0 || 16 * (int64_t)row[j] + 16 > n_host) return ORC_EDEVARG;",
+                                   "(void)n_host;"),
+    "page_fit_unchecked": ("if (p < 0 || 16 * (int64_t)p + 16 > n_host) return 0;", "(void)p;"),
 }
 
 

@@ -876,3 +876,178 @@ def test_prefill_capacity_errors_per_stage_and_short_history_takes_everything():
     assert o["status"] == O.OK and (o["beta"] == -1).all()
     assert list(o["uni"]) == list(range(50)) == list(o["cand"])
     assert np.array_equal(o["pf_h"], wk["hb"] + np.arange(50)) and o["miss_h"].size == 0
+
+
+# ------------------------------------------------------------------ page tables
+# R14: with a page table a request's token s is host id 16 * page[s // 16] + s % 16.
+# Pinned by invariance (the method's results do not depend on where the pages lie;
+# only the host ids in the maps move with the pages) and by hand-derived cases.
+
+def _scatter_pages(wk, seed, spare=5):
+    """The contiguous workload's requests moved to scattered pages: returns (pages
+    [B, stride], kidx, hk, n_host, perm) where perm maps each contiguous host id of a
+    request token to its paged host id."""
+    rng = np.random.default_rng(seed)
+    ctx, base = wk["ctx"], wk["host_base"]
+    npages = [(int(c) + 15) // 16 for c in ctx]
+    stride = max(npages) + 2
+    total = sum(npages)
+    phys = rng.permutation(total + spare)[:total]  # distinct pages anywhere in the pool
+    n_host = 16 * (total + spare)
+    pages = np.full((len(ctx), stride), -1, np.int32)
+    kidx = np.zeros((n_host, wk["D"]), np.uint8)
+    hk = np.zeros((n_host, wk["hk"].shape[1]), np.uint16)
+    perm = {}
+    i = 0
+    for b, c in enumerate(ctx):
+        for j in range(npages[b]):
+            pages[b, j] = phys[i]
+            i += 1
+        for s in range(int(c)):
+            h0 = int(base[b]) + s
+            h1 = 16 * int(pages[b, s // 16]) + s % 16
+            kidx[h1] = wk["kidx"][h0]
+            hk[h1] = wk["hk"][h0]
+            perm[h0] = h1
+    return pages, kidx, hk, n_host, perm
+
+
+@pytest.mark.parametrize("mode", [O.MODE_EMA, O.MODE_NEG_INF])
+def test_scattered_pages_give_the_same_steps_with_moved_host_ids(mode):
+    # a ragged batch under eviction pressure, run once with contiguous ranges and once
+    # with every request's pages scattered over a larger pool in random order
+    wk = _small_workload(ctx=(300, 177, 250), B=3, n_gpu=3 * 64 + 50, steps=6, rho=0.7)
+    pages, kidx2, hk2, n_host2, perm = _scatter_pages(wk, seed=4)
+    H, D, k = wk["H"], wk["D"], wk["k"]
+    a = O.OracleLayer(H, D, k, 8, wk["n_host"], wk["n_gpu"], 3, cap_div=32)
+    p = O.OracleLayer(H, D, k, 8, n_host2, wk["n_gpu"], 3, cap_div=32)
+    ids = np.array(sorted(perm), np.int64)
+    moved = np.array([perm[h] for h in ids], np.int64)
+    for t, q in enumerate(wk["qs"]):
+        oa = a.step(wk["host_base"], wk["ctx"], q, wk["w"], wk["kidx"], wk["hk"], mode=mode)
+        op = p.step(None, wk["ctx"], q, wk["w"], kidx2, hk2, mode=mode, pages=pages)
+        assert oa["status"] == op["status"] == O.OK
+        for key in ("scores", "sel_tok", "sel_slot", "n_sel", "kth", "pf_tok", "pf_slot", "n_pf",
+                    "n_cand", "miss_tok", "n_miss", "evicted"):
+            assert np.array_equal(oa[key], op[key]), (t, key)
+        assert oa["n_evict"] == op["n_evict"]
+        assert np.array_equal(a.theta, p.theta) and a.t == p.t
+        assert np.array_equal(a.prio, p.prio) and np.array_equal(a.free, p.free)
+        assert np.array_equal(a.pool, p.pool), (t, "pool bytes")
+        # the maps, with host ids carried along by the pages
+        assert np.array_equal(p.h2g[moved], a.h2g[ids])
+        others = np.setdiff1d(np.arange(n_host2), moved)
+        assert (p.h2g[others] == -1).all()
+        occ = a.g2h >= 0
+        assert np.array_equal(p.g2h[~occ], a.g2h[~occ])
+        assert np.array_equal(p.g2h[occ], [perm[int(h)] for h in a.g2h[occ]])
+    assert sum(int(o) for o in [a.t]) == 6
+
+
+def test_paged_append_writes_into_the_listed_page_by_hand():
+    # request 0 holds pages [5, 2], request 1 pages [0, 7]; contexts 16 and 20:
+    # request 0's token 16 opens its second page (id 16*2 + 0 = 32), request 1's
+    # token 20 is id 16*7 + 4 = 116
+    D, latent, n_host = 4, 8, 160
+    pages = np.array([[5, 2, -1], [0, 7, -1]], np.int32)
+    ctx = np.array([16, 20], np.int32)
+    kidx = np.zeros((n_host, D), np.uint8)
+    host = np.zeros((n_host, latent), np.uint16)
+    k_new = np.array([[1, 2, 3, 4], [5, 6, 7, 8]], np.uint8)
+    lat_new = (np.arange(2 * latent, dtype=np.uint16).reshape(2, latent) + 9)
+    h2g = np.full(n_host, -1, np.int32)
+    assert O.append(None, ctx, h2g, k_new, lat_new, kidx, host, max_ctx=48,
+                    pages=pages) == O.OK
+    assert ctx.tolist() == [17, 21]
+    assert np.nonzero(kidx.any(1))[0].tolist() == [32, 116]
+    assert np.array_equal(kidx[32], k_new[0]) and np.array_equal(host[116], lat_new[1])
+    # no page listed for the next token (slot 2 holds -1), a page slot past the table,
+    # a page past the pool, and a mapped id: each stops the call with nothing written
+    k0, c0 = kidx.copy(), np.array([32, 21], np.int32)
+    assert O.append(None, c0, h2g, k_new, lat_new, kidx, host, max_ctx=64,
+                    pages=pages) == O.ECAPACITY
+    c1 = np.array([48, 21], np.int32)
+    assert O.append(None, c1, h2g, k_new, lat_new, kidx, host, max_ctx=64,
+                    pages=pages) == O.ECAPACITY
+    far = pages.copy()
+    far[1, 1] = 10  # ids 160..175: past the pool
+    assert O.append(None, np.array([17, 21], np.int32), h2g, k_new, lat_new, kidx, host,
+                    max_ctx=64, pages=far) == O.ECAPACITY
+    h2g[16 * 7 + 5] = 3
+    assert O.append(None, np.array([17, 21], np.int32), h2g, k_new, lat_new, kidx, host,
+                    max_ctx=64, pages=pages) == O.EDEVARG
+    assert np.array_equal(kidx, k0) and c0.tolist() == [32, 21]
+
+
+def test_paged_release_gives_back_the_slots_of_the_listed_pages_by_hand():
+    # request 0: pages [3, 0], 20 tokens (ids 48..63 and 0..3); request 1: page [1],
+    # 10 tokens (ids 16..25).  Slots: 48 -> 1, 50 -> 4, 2 -> 0 (request 0), 20 -> 2
+    # (request 1), and id 5 -> 3 (page 0 but past request 0's 20 tokens)
+    lay = O.OracleLayer(H=1, D=1, k=4, latent=2, n_host=80, n_gpu=6, max_batch=2)
+    for h, g in ((48, 1), (50, 4), (2, 0), (20, 2), (5, 3)):
+        lay.h2g[h], lay.g2h[g], lay.free[g], lay.prio[g] = g, h, 0, 7
+    pages = np.array([[3, 0], [1, -1]], np.int32)
+    ctx = np.array([20, 10], np.int32)
+    lay.theta[:] = [4.0, 5.0]
+    assert O.release(lay, None, ctx, [1, 0], max_ctx=32, pages=pages) == O.OK
+    assert ctx.tolist() == [0, 10]
+    assert lay.free.tolist() == [1, 1, 0, 0, 1, 1]
+    assert lay.g2h.tolist() == [-1, -1, 20, 5, -1, -1]
+    assert (lay.h2g[[48, 50, 2]] == -1).all() and lay.h2g[20] == 2 and lay.h2g[5] == 3
+    assert lay.theta.tolist() == [np.inf, 5.0]
+    # a page outside the pool: nothing changes
+    bad = np.array([[3, 0], [9, -1]], np.int32)
+    before = [x.copy() for x in (lay.h2g, lay.g2h, lay.free)]
+    assert O.release(lay, None, np.array([0, 10], np.int32), [0, 1], max_ctx=32,
+                     pages=bad) == O.EDEVARG
+    for x, y in zip((lay.h2g, lay.g2h, lay.free), before):
+        assert np.array_equal(x, y)
+
+
+def test_paged_admission_checks_in_order_and_reuses_a_hole_by_hand():
+    # a pool of 120 host ids: pages 0..6 are whole, page 7 would run past the pool;
+    # request 0 lives on pages [6, 1]; row 1 is empty
+    lay = O.OracleLayer(H=1, D=1, k=4, latent=2, n_host=120, n_gpu=4, max_batch=2)
+    ctx = np.array([30, 0], np.int32)
+    pages = np.array([[6, 1, -1], [-1, -1, -1]], np.int32)
+
+    def admit(row1, n, expect):
+        pg = pages.copy()
+        pg[1] = row1
+        c = ctx.copy()
+        th = lay.theta.copy()
+        assert O.admit(lay, None, c, 1, 0, n, max_ctx=48, pages=pg) == expect, (row1, n)
+        if expect != O.OK:
+            assert np.array_equal(c, ctx) and np.array_equal(lay.theta, th)
+        return c
+
+    admit([2, 3, 4], 49, O.EINVAL)                       # longer than max_ctx
+    c = ctx.copy()
+    c[1] = 5
+    assert O.admit(lay, None, c, 1, 0, 10, max_ctx=48, pages=pages) == O.EDEVARG  # in use
+    admit([2, 7, -1], 20, O.EDEVARG)                     # page 7 runs past the pool
+    admit([2, -1, 3], 20, O.EDEVARG)                     # no page listed for token 16
+    admit([2, 2, -1], 20, O.EDEVARG)                     # a page listed twice
+    admit([2, 1, -1], 20, O.ECAPACITY)                   # page 1 is request 0's
+    lay.h2g[16 * 3 + 2] = 0                              # token 18 (page 3) still mapped
+    lay.g2h[0], lay.free[0], lay.prio[0] = 16 * 3 + 2, 0, 0
+    admit([2, 3, -1], 20, O.EDEVARG)
+    admit([2, 3, -1], 18, O.OK)                          # 18 tokens stop before that id
+    # page 1 of request 0 is only its tokens 16..29: a third page of row 1 past its 20
+    # tokens is not checked; pages 2 and 0 are a hole no live request uses
+    lay.theta[1] = 3.0
+    c = admit([2, 0, 1], 20, O.OK)
+    assert c.tolist() == [30, 20] and lay.theta[1] == np.inf
+
+
+def test_paged_gather_reads_the_rows_of_the_listed_pages():
+    # host row h holds h itself, so each gathered row names the id it came from
+    n_host, latent = 96, 4
+    host = np.zeros((n_host, latent), np.uint16)
+    host[:, 0] = np.arange(n_host)
+    pages = np.array([[4, 0], [2, 5]], np.int32)
+    sel = np.array([[0, 15, 16, 17], [3, 20, 0, 0]], np.int32)
+    n_sel = np.array([4, 2], np.int32)
+    out = O.gather(None, sel, n_sel, host, pages=pages)
+    assert out[0, :, 0].tolist() == [64, 79, 0, 1]
+    assert out[1, :2, 0].tolist() == [35, 84] and not out[1, 2:].any()
