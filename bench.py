@@ -540,8 +540,7 @@ def main():
     with torch.cuda.stream(cs):
         with torch.cuda.graph(gap, stream=cs):
             for lay in layers:
-                R.check(abi.echo_append(dims, lay.struct, batch.host_base.data_ptr(),
-                                        batch.ctx.data_ptr(), B, k_new.data_ptr(),
+                R.check(abi.echo_append(dims, lay.struct, batch.struct, k_new.data_ptr(),
                                         lat_new.data_ptr(), ws.ws, 0, cs.cuda_stream), "append")
     gap.replay()
     torch.cuda.synchronize()
@@ -567,13 +566,11 @@ def main():
     r0, r1, r2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
     r0.record(cs)
     for i, lay in enumerate(layers):
-        R.check(abi.echo_release(dims, lay.struct, batch.host_base.data_ptr(),
-                                 batch.ctx.data_ptr(), B, mask.data_ptr(), int(i == L - 1),
-                                 ws.ws, cs.cuda_stream), "release")
+        R.check(abi.echo_release(dims, lay.struct, batch.struct, mask.data_ptr(),
+                                 int(i == L - 1), ws.ws, cs.cuda_stream), "release")
     r1.record(cs)
     for i, lay in enumerate(layers):
-        R.check(abi.echo_admit(dims, lay.struct, batch.host_base.data_ptr(),
-                               batch.ctx.data_ptr(), B, 0, int(base[0]), int(ctx[0]),
+        R.check(abi.echo_admit(dims, lay.struct, batch.struct, 0, int(base[0]), int(ctx[0]),
                                int(i == L - 1), ws.ws, cs.cuda_stream), "admit")
     r2.record(cs)
     torch.cuda.synchronize()

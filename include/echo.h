@@ -27,10 +27,14 @@
  *    echo_ws_reset.  Once it is set, every later kernel of every call is a no-op,
  *    and the metadata stays consistent (mutual maps, free flags, priorities).
  *    Read it after your own synchronization.
- *  - Token identities: request b of a batch owns host ids
+ *  - Token identities: without a page table, request b of a batch owns host ids
  *    host_base[b] .. host_base[b] + ctx_len[b] - 1; ranges of different requests
  *    must not overlap, and every host_base is a multiple of 16 (both checked on
- *    the device: ECHO_EDEVARG).
+ *    the device: ECHO_EDEVARG).  With a page table (echo_batch_t.page_table), the
+ *    host pool is cut into pages of 16 host ids and token s of request b is host
+ *    id 16 * page_table[b * page_stride + s / 16] + s % 16; the pages a request
+ *    uses must lie in the pool (checked on the device: ECHO_EDEVARG) and must not
+ *    be shared with another live request (checked by echo_admit).
  *  - The indexer K cache is kept in the tiled layout that the gfx950 fp8 MFMA
  *    consumes (see echo_kindex_pack): host ids are grouped by 16, and group g
  *    holds bytes [16*g*D, 16*(g+1)*D), D = head_dim.
@@ -163,10 +167,22 @@ typedef struct {
   uint64_t *stats;         /* [ECHO_STAT_WORDS] running totals, or NULL (not kept)   */
 } echo_layer_t;
 
+/* The batch.  Where a request's tokens live is either one contiguous host range
+ * (host_base) or a page table: the ECHO review leaves request cancellation and
+ * host-pool exhaustion open ("Systemic flaws"), and pages let a new request use
+ * any free host pages, holes left by released requests included.  A page is 16
+ * host ids, one group of the tiled indexer K (echo_kindex_pack).  The lifecycle
+ * calls (echo_append, echo_release, echo_admit) write ctx_len (and, echo_admit
+ * without a page table, host_base) through although they are declared const for
+ * the step calls. */
 typedef struct {
-  int32_t batch;            /* B, host value, 0 <= B <= max_batch                  */
-  const int32_t *host_base; /* [B] device: first host id of each request           */
-  const int32_t *ctx_len;   /* [B] device: context length, 0 <= ctx <= max_ctx      */
+  int32_t batch;             /* B, host value, 0 <= B <= max_batch                  */
+  const int32_t *host_base;  /* [B] device: first host id of each request; not used
+                                (may be NULL) with a page table                      */
+  const int32_t *ctx_len;    /* [B] device: context length, 0 <= ctx <= max_ctx      */
+  const int32_t *page_table; /* [B][page_stride] device, or NULL: host page of each
+                                16-token page of each request's context              */
+  int32_t page_stride;       /* host value, >= 1 with a page table: entries per row  */
 } echo_batch_t;
 
 /* Workspace: one caller-allocated device buffer carved by echo_ws_bind.  The
@@ -306,10 +322,10 @@ int echo_gather(const echo_dims_t *dims, const echo_layer_t *layer, const echo_b
  * management") keeps the indexer K resident on the GPU and backs each token's KV
  * up to the host pool when it is generated, so eviction moves no data; its
  * "Design trade-offs" section counts that writeback of every new token.
- *   host_base [batch]  device: first host id of each request (as in echo_batch_t)
- *   ctx_len   [batch]  device, in/out: the new token goes to host id
- *                      host_base[b] + ctx_len[b]; with advance != 0 the call then
- *                      adds one to ctx_len[b]
+ *   batch    the batch; the new token of request b is its token ctx_len[b], at host
+ *            id host_base[b] + ctx_len[b] or, with a page table, in the page that
+ *            row b lists for it (the caller hands out pages); with advance != 0
+ *            the call then adds one to batch->ctx_len[b] (written through)
  *   k_new  [batch][D]       device: the token's indexer key, e4m3, row-major; it is
  *                           written into layer->k_index in the tiled layout
  *   latent_new [batch][latent] device, 16-byte aligned: the token's bf16 latent,
@@ -319,54 +335,59 @@ int echo_gather(const echo_dims_t *dims, const echo_layer_t *layer, const echo_b
  * that layer's step, with advance != 0 only for the last layer of the step.  The
  * token is not placed in the GPU pool (it becomes resident when prefetched or
  * recalled).  Errors: ECHO_EINVAL (host checks; batch 0 is a no-op).  Device:
- * ECHO_ECAPACITY if a request has no room (ctx_len = max_ctx, host id >= n_host,
- * or the id falls in another request's range including its own new token),
- * ECHO_EDEVARG if a slot already maps the host id; the lowest such request
- * decides, and nothing is written.  A row with ctx_len 0 is empty (released, or
- * never admitted): it takes no token, does not grow, and its stale host_base
- * takes no part in the other requests' room checks. */
-int echo_append(const echo_dims_t *dims, const echo_layer_t *layer, const int32_t *host_base,
-                int32_t *ctx_len, int32_t batch, const uint8_t *k_new,
-                const uint16_t *latent_new, const echo_ws_t *ws, int advance,
-                hipStream_t stream);
+ * ECHO_ECAPACITY if a request has no room (ctx_len = max_ctx; the id at or past
+ * n_host; with a page table, a page slot past page_stride or a listed page outside
+ * the pool; without one, the id inside another request's range including its own
+ * new token), ECHO_EDEVARG if a slot already maps the host id; the lowest such
+ * request decides, and nothing is written.  A row with ctx_len 0 is empty
+ * (released, or never admitted): it takes no token, does not grow, and its stale
+ * host_base takes no part in the other requests' room checks. */
+int echo_append(const echo_dims_t *dims, const echo_layer_t *layer, const echo_batch_t *batch,
+                const uint8_t *k_new, const uint16_t *latent_new, const echo_ws_t *ws,
+                int advance, hipStream_t stream);
 
 /* Request release (cancellation) between decode steps.  The ECHO review leaves
  * request cancellation open ("Systemic flaws") and asks that top-k and attention
  * input stay equal to the no-offload baseline when requests are cancelled
  * ("Limitations and future work"); the state is that of "Core method / in-graph
  * per-layer cache management".  For every request b with mask[b] != 0, each host
- * id of [host_base[b], host_base[b] + ctx_len[b]) that holds a GPU slot gives it
- * back (g2h = -1, free = 1, prio = -1), the range's h2g rows become -1,
- * theta[b] (and guard[b]) become +inf; no bytes move.  Then the ascending free
- * list (meta.idxbuf, ctl[ECHO_CTL_NFREE]) is rebuilt.  With commit != 0,
- * ctx_len[b] of every released request becomes 0.
- *   host_base [batch], ctx_len [batch] (in/out), mask [batch]: device int32
+ * id of its tokens (its range, or the ids its pages give its ctx_len[b] tokens)
+ * that holds a GPU slot gives it back (g2h = -1, free = 1, prio = -1), those h2g
+ * rows become -1, theta[b] (and guard[b]) become +inf; no bytes move, and host
+ * pages stay the caller's to reuse.  Then the ascending free list (meta.idxbuf,
+ * ctl[ECHO_CTL_NFREE]) is rebuilt.  With commit != 0, batch->ctx_len[b] of every
+ * released request becomes 0 (written through).
+ *   mask [batch]: device int32
  * Call it between steps, once per layer, with commit != 0 only for the last
  * layer (the batch row is shared by the layers).  Errors:
  * ECHO_EINVAL (host checks; batch 0 is a no-op).  Device: ECHO_EDEVARG if a
- * masked request's range does not fit (ctx_len outside [0, max_ctx], host_base
- * < 0 or past n_host); all are checked first and nothing changes.  A no-op
+ * masked request's tokens do not fit (ctx_len outside [0, max_ctx]; host_base < 0
+ * or the range past n_host; with a page table, more pages than page_stride or a
+ * page outside the pool); all are checked first and nothing changes.  A no-op
  * while ws->status holds an error. */
-int echo_release(const echo_dims_t *dims, const echo_layer_t *layer, const int32_t *host_base,
-                 int32_t *ctx_len, int32_t batch, const int32_t *mask, int commit,
-                 const echo_ws_t *ws, hipStream_t stream);
+int echo_release(const echo_dims_t *dims, const echo_layer_t *layer, const echo_batch_t *batch,
+                 const int32_t *mask, int commit, const echo_ws_t *ws, hipStream_t stream);
 
 /* Request admission into an empty batch row b (the other half of the lifecycle
  * above): theta[b] = guard[b] = +inf (no estimate yet) and, with commit != 0,
- * row b takes host ids [base, base + len) (host_base[b] = base, ctx_len[b] =
- * len).  The caller has written (or will append) the range's indexer keys and
- * host latents.
- *   host_base [batch], ctx_len [batch]: device int32, in/out (row b is written)
+ * row b takes len tokens: without a page table the host ids [base, base + len)
+ * (host_base[b] = base), with one the first len ids of the pages the caller has
+ * written into row b of the page table (base is not used); ctx_len[b] = len.  The
+ * caller has written (or will append) those tokens' indexer keys and host latents.
  * Errors: ECHO_EINVAL (host checks: b outside [0, batch), len outside
- * [0, max_ctx], base < 0, base + len > n_host; nothing enqueued).  Device, in
- * this order: ECHO_EDEVARG if ctx_len[b] != 0 (the row is in use: release it
- * first), ECHO_ECAPACITY if the range meets the range of another request with
- * ctx_len > 0, ECHO_EDEVARG if some slot still maps a host id of the range.
- * Nothing is written on an error; a no-op while ws->status holds an error.  One
- * call per layer, with commit != 0 only for the last, like echo_release. */
-int echo_admit(const echo_dims_t *dims, const echo_layer_t *layer, int32_t *host_base,
-               int32_t *ctx_len, int32_t batch, int32_t b, int32_t base, int32_t len,
-               int commit, const echo_ws_t *ws, hipStream_t stream);
+ * [0, max_ctx]; without a page table base < 0 or base + len > n_host; nothing
+ * enqueued).  Device, in this order: ECHO_EDEVARG if ctx_len[b] != 0 (the row is
+ * in use: release it first); with a page table, ECHO_EDEVARG if the len tokens
+ * need more pages than page_stride, or one of their pages lies outside the pool or
+ * is listed twice; ECHO_ECAPACITY if the range meets the range of another request
+ * with ctx_len > 0 (with a page table: one of their pages is a page another live
+ * request's tokens use); ECHO_EDEVARG if some slot still maps a host id of the
+ * new tokens.  Nothing is written on an error; a no-op while ws->status holds an
+ * error.  One call per layer, with commit != 0 only for the last, like
+ * echo_release. */
+int echo_admit(const echo_dims_t *dims, const echo_layer_t *layer, const echo_batch_t *batch,
+               int32_t b, int32_t base, int32_t len, int commit, const echo_ws_t *ws,
+               hipStream_t stream);
 
 /* echo_topk for callers that cannot allocate: code under graph capture, tight
  * serving loops, harnesses that forbid device allocation.  It computes exactly

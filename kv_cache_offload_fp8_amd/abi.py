@@ -55,7 +55,8 @@ class echo_layer_t(C.Structure):
 
 
 class echo_batch_t(C.Structure):
-    _fields_ = [("batch", C.c_int32), ("host_base", P), ("ctx_len", P)]
+    _fields_ = [("batch", C.c_int32), ("host_base", P), ("ctx_len", P), ("page_table", P),
+                ("page_stride", C.c_int32)]
 
 
 class echo_ws_t(C.Structure):
@@ -108,11 +109,11 @@ def lib() -> C.CDLL:
             "echo_recall": (C.c_int, [dp, lp, wp, P]),
             "echo_step_advance": (C.c_int, [lp, wp, P]),
             "echo_layer_step": (C.c_int, [dp, lp, bp, wp, C.c_int, P]),
-            "echo_append": (C.c_int, [dp, lp, P, P, C.c_int32, P, P, wp, C.c_int, P]),
+            "echo_append": (C.c_int, [dp, lp, bp, P, P, wp, C.c_int, P]),
             "echo_gather": (C.c_int, [dp, lp, bp, wp, P, P]),
-            "echo_release": (C.c_int, [dp, lp, P, P, C.c_int32, P, C.c_int, wp, P]),
-            "echo_admit": (C.c_int, [dp, lp, P, P, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
-                                     C.c_int, wp, P]),
+            "echo_release": (C.c_int, [dp, lp, bp, P, C.c_int, wp, P]),
+            "echo_admit": (C.c_int, [dp, lp, bp, C.c_int32, C.c_int32, C.c_int32, C.c_int, wp,
+                                     P]),
             "echo_prefill_ws_bytes": (C.c_size_t, [dp, C.c_int32]),
             "echo_prefill_ws_bind": (C.c_int, [dp, C.c_int32, P, C.c_size_t,
                                                C.POINTER(echo_prefill_ws_t)]),
@@ -208,12 +209,12 @@ def echo_layer_step(dims, layer, batch, ws, theta_mode: int, stream: int) -> int
                                  stream)
 
 
-def echo_append(dims, layer, host_base: int, ctx_len: int, batch: int, k_new: int,
-                latent_new: int, ws, advance: int, stream: int) -> int:
-    """host_base, ctx_len, k_new, latent_new: device pointers (ctx_len is updated in place
-    when advance != 0)."""
-    return lib().echo_append(C.byref(dims), _ref(layer), host_base, ctx_len, batch, k_new,
-                             latent_new, _ref(ws), advance, stream)
+def echo_append(dims, layer, batch, k_new: int, latent_new: int, ws, advance: int,
+                stream: int) -> int:
+    """k_new, latent_new: device pointers; batch.ctx_len is updated in place when
+    advance != 0."""
+    return lib().echo_append(C.byref(dims), _ref(layer), _ref(batch), k_new, latent_new,
+                             _ref(ws), advance, stream)
 
 
 def echo_gather(dims, layer, batch, ws, out: int, stream: int) -> int:
@@ -221,19 +222,19 @@ def echo_gather(dims, layer, batch, ws, out: int, stream: int) -> int:
     return lib().echo_gather(C.byref(dims), _ref(layer), _ref(batch), _ref(ws), out, stream)
 
 
-def echo_release(dims, layer, host_base: int, ctx_len: int, batch: int, mask: int,
-                 commit: int, ws, stream: int) -> int:
-    """host_base, ctx_len, mask: device int32 pointers (with commit, ctx_len of the
-    released requests becomes 0)."""
-    return lib().echo_release(C.byref(dims), _ref(layer), host_base, ctx_len, batch, mask,
-                              commit, _ref(ws), stream)
+def echo_release(dims, layer, batch, mask: int, commit: int, ws, stream: int) -> int:
+    """mask: device int32 pointer; with commit, batch.ctx_len of the released requests
+    becomes 0."""
+    return lib().echo_release(C.byref(dims), _ref(layer), _ref(batch), mask, commit, _ref(ws),
+                              stream)
 
 
-def echo_admit(dims, layer, host_base: int, ctx_len: int, batch: int, b: int, base: int,
-               length: int, commit: int, ws, stream: int) -> int:
-    """host_base, ctx_len: device int32 pointers; with commit, row b takes (base, length)."""
-    return lib().echo_admit(C.byref(dims), _ref(layer), host_base, ctx_len, batch, b, base,
-                            length, commit, _ref(ws), stream)
+def echo_admit(dims, layer, batch, b: int, base: int, length: int, commit: int, ws,
+               stream: int) -> int:
+    """With commit, row b of the batch takes (base, length), or length tokens on the pages
+    of its page-table row."""
+    return lib().echo_admit(C.byref(dims), _ref(layer), _ref(batch), b, base, length, commit,
+                            _ref(ws), stream)
 
 
 def echo_prefill_ws_bytes(dims, max_chunk: int) -> int:

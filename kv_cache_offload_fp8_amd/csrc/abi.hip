@@ -90,8 +90,9 @@ bool ws_ok(const echo_ws_t *ws) {
 
 bool batch_ok(const echo_dims_t &d, const echo_batch_t *b) {
   if (!b || b->batch < 0 || b->batch > d.max_batch) return false;
-  if (b->batch > 0 && (!b->host_base || !b->ctx_len)) return false;
-  return true;
+  if (b->batch > 0 && !b->ctx_len) return false;
+  if (b->page_table) return b->page_stride >= 1;
+  return b->batch == 0 || b->host_base;
 }
 
 bool layer_ok(const echo_layer_t *l, bool need_theta) {
@@ -125,6 +126,8 @@ StepArgs make_args(const echo_dims_t &d, const echo_layer_t *l, const echo_batch
     a.B = bt->batch;
     a.host_base = bt->host_base;
     a.ctx_len = bt->ctx_len;
+    a.pages = bt->page_table;
+    a.page_stride = bt->page_table ? bt->page_stride : 0;
   }
   if (l) {
     a.h2g = l->meta.h2g;
@@ -510,59 +513,43 @@ int echo_gather(const echo_dims_t *dims, const echo_layer_t *layer, const echo_b
   return ECHO_OK;
 }
 
-int echo_append(const echo_dims_t *dims, const echo_layer_t *layer, const int32_t *host_base,
-                int32_t *ctx_len, int32_t batch, const uint8_t *k_new, const uint16_t *latent_new,
-                const echo_ws_t *ws, int advance, hipStream_t stream) {
+int echo_append(const echo_dims_t *dims, const echo_layer_t *layer, const echo_batch_t *batch,
+                const uint8_t *k_new, const uint16_t *latent_new, const echo_ws_t *ws,
+                int advance, hipStream_t stream) {
   int rc = check_dims(dims);
   if (rc != ECHO_OK) return rc;
-  if (!layer_ok(layer, false) || !ws_ok(ws)) return ECHO_EINVAL;
-  if (batch < 0 || batch > dims->max_batch) return ECHO_EINVAL;
-  if (batch == 0) return ECHO_OK;
-  if (!host_base || !ctx_len || !k_new || !latent_new || ((uintptr_t)latent_new & 15) != 0)
-    return ECHO_EINVAL;
-  echo_batch_t bt;
-  bt.batch = batch;
-  bt.host_base = host_base;
-  bt.ctx_len = ctx_len;
-  const StepArgs a = make_args(*dims, layer, &bt, *ws, ECHO_THETA_POS_INF);
-  LAUNCH(launch_append(a, k_new, latent_new, ctx_len, advance ? 1 : 0, stream));
+  if (!layer_ok(layer, false) || !ws_ok(ws) || !batch_ok(*dims, batch)) return ECHO_EINVAL;
+  if (batch->batch == 0) return ECHO_OK;
+  if (!k_new || !latent_new || ((uintptr_t)latent_new & 15) != 0) return ECHO_EINVAL;
+  const StepArgs a = make_args(*dims, layer, batch, *ws, ECHO_THETA_POS_INF);
+  LAUNCH(launch_append(a, k_new, latent_new, const_cast<int32_t *>(batch->ctx_len),
+                       advance ? 1 : 0, stream));
   return ECHO_OK;
 }
 
-int echo_release(const echo_dims_t *dims, const echo_layer_t *layer, const int32_t *host_base,
-                 int32_t *ctx_len, int32_t batch, const int32_t *mask, int commit,
-                 const echo_ws_t *ws, hipStream_t stream) {
+int echo_release(const echo_dims_t *dims, const echo_layer_t *layer, const echo_batch_t *batch,
+                 const int32_t *mask, int commit, const echo_ws_t *ws, hipStream_t stream) {
   int rc = check_dims(dims);
   if (rc != ECHO_OK) return rc;
-  if (!layer_ok(layer, true) || !ws_ok(ws)) return ECHO_EINVAL;
-  if (batch < 0 || batch > dims->max_batch) return ECHO_EINVAL;
-  if (batch == 0) return ECHO_OK;
-  if (!host_base || !ctx_len || !mask) return ECHO_EINVAL;
-  echo_batch_t bt;
-  bt.batch = batch;
-  bt.host_base = host_base;
-  bt.ctx_len = ctx_len;
-  const StepArgs a = make_args(*dims, layer, &bt, *ws, ECHO_THETA_POS_INF);
-  LAUNCH(launch_release(a, mask, ctx_len, commit ? 1 : 0, stream));
+  if (!layer_ok(layer, true) || !ws_ok(ws) || !batch_ok(*dims, batch)) return ECHO_EINVAL;
+  if (batch->batch == 0) return ECHO_OK;
+  if (!mask) return ECHO_EINVAL;
+  const StepArgs a = make_args(*dims, layer, batch, *ws, ECHO_THETA_POS_INF);
+  LAUNCH(launch_release(a, mask, const_cast<int32_t *>(batch->ctx_len), commit ? 1 : 0, stream));
   return ECHO_OK;
 }
 
-int echo_admit(const echo_dims_t *dims, const echo_layer_t *layer, int32_t *host_base,
-               int32_t *ctx_len, int32_t batch, int32_t b, int32_t base, int32_t len,
-               int commit, const echo_ws_t *ws, hipStream_t stream) {
+int echo_admit(const echo_dims_t *dims, const echo_layer_t *layer, const echo_batch_t *batch,
+               int32_t b, int32_t base, int32_t len, int commit, const echo_ws_t *ws,
+               hipStream_t stream) {
   int rc = check_dims(dims);
   if (rc != ECHO_OK) return rc;
-  if (!layer_ok(layer, true) || !ws_ok(ws)) return ECHO_EINVAL;
-  if (batch < 0 || batch > dims->max_batch || !host_base || !ctx_len) return ECHO_EINVAL;
-  if (b < 0 || b >= batch || len < 0 || len > dims->max_ctx || base < 0 ||
-      (int64_t)base + len > dims->n_host)
-    return ECHO_EINVAL;
-  echo_batch_t bt;
-  bt.batch = batch;
-  bt.host_base = host_base;
-  bt.ctx_len = ctx_len;
-  const StepArgs a = make_args(*dims, layer, &bt, *ws, ECHO_THETA_POS_INF);
-  LAUNCH(launch_admit(a, b, base, len, host_base, ctx_len, commit ? 1 : 0, stream));
+  if (!layer_ok(layer, true) || !ws_ok(ws) || !batch_ok(*dims, batch)) return ECHO_EINVAL;
+  if (b < 0 || b >= batch->batch || len < 0 || len > dims->max_ctx) return ECHO_EINVAL;
+  if (!batch->page_table && (base < 0 || (int64_t)base + len > dims->n_host)) return ECHO_EINVAL;
+  const StepArgs a = make_args(*dims, layer, batch, *ws, ECHO_THETA_POS_INF);
+  LAUNCH(launch_admit(a, b, base, len, const_cast<int32_t *>(batch->host_base),
+                      const_cast<int32_t *>(batch->ctx_len), commit ? 1 : 0, stream));
   return ECHO_OK;
 }
 

@@ -83,6 +83,7 @@ struct Scratch {
   int32_t *ecnt;          // [4]: candidates of the rare exact eviction path
   uint64_t *estate;       // [alloc tiles] eviction-rank look-back states
   uint64_t *astate;       // [alloc tiles] free-list look-back states
+  uint32_t *pgbits;       // [n_host / 512] one bit per host page (admission with pages)
   int32_t max_tiles, bw, atiles, pad_;
 };
 
@@ -123,6 +124,7 @@ inline int64_t scratch_layout(const echo_dims_t &d, uint8_t *base, Scratch *s) {
   t.ecnt = (int32_t *)take(16);
   t.estate = (uint64_t *)take((int64_t)atiles * 8);
   t.astate = (uint64_t *)take((int64_t)atiles * 8);
+  t.pgbits = (uint32_t *)take((d.n_host / 16 + 31) / 32 * 4);
   t.max_tiles = max_tiles;
   t.bw = bw;
   t.atiles = atiles;

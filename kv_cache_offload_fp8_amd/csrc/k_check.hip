@@ -83,8 +83,9 @@ __global__ __launch_bounds__(kCheckThreads) void k_inv_scan(StepArgs a, int chec
       ns = ns < 0 ? 0 : (ns > a.K ? a.K : ns);
       if (i >= ns) continue;
       const int32_t s = a.ws.sel_tok[j];
-      const int64_t h = (int64_t)a.host_base[b] + s;
-      bool ok = s >= 0 && s < a.ctx_len[b] && h >= 0 && h < a.n_host;
+      bool ok = s >= 0 && s < a.ctx_len[b] && (!a.pages || s < 16 * a.page_stride);
+      const int64_t h = ok ? token_host(a, b, a.pages ? 0 : a.host_base[b], s) : -1;
+      ok = ok && h >= 0 && h < a.n_host;
       if (ok) {
         const int32_t g = a.h2g[h];
         ok = g >= 0 && g < a.n_gpu && g == a.ws.sel_slot[j] && a.prio[g] == t - 1;

@@ -74,17 +74,24 @@ __device__ static void build_request_table(const StepArgs &a, int roles, int32_t
   if (l >= kWave) return;
   const bool in = l < a.B;
   int ctx = in ? a.ctx_len[l] : 0;
-  int base = in ? a.host_base[l] : 0;
+  int base = in && !a.pages ? a.host_base[l] : 0;
   const float th_in = in && a.mode == ECHO_THETA_EMA ? a.theta[l] : __builtin_huge_valf();
   const float g_in = in && a.guard ? a.guard[l] : __builtin_huge_valf();
   if (st0 != 0) return;
-  bool bad = in && (ctx < 0 || ctx > a.max_ctx || base < 0 || (base & 15) != 0 ||
-                    (int64_t)base + (int64_t)ctx > a.n_host);
-  // disjoint host ranges
+  bool bad;
+  if (a.pages) {
+    // page table: the context fits the row (the pages themselves are checked by the
+    // clear workgroups of this kernel; distinct pages are the admission's check)
+    bad = in && (ctx < 0 || ctx > a.max_ctx || (ctx + 15) / 16 > a.page_stride);
+  } else {
+    bad = in && (ctx < 0 || ctx > a.max_ctx || base < 0 || (base & 15) != 0 ||
+                 (int64_t)base + (int64_t)ctx > a.n_host);
+    // disjoint host ranges
 #pragma unroll 8
-  for (int o = 0; o < a.B; ++o) {
-    int c2 = __shfl(ctx, o), b2 = __shfl(base, o);
-    if (in && o != l && ctx > 0 && c2 > 0 && base < b2 + c2 && b2 < base + ctx) bad = true;
+    for (int o = 0; o < a.B; ++o) {
+      int c2 = __shfl(ctx, o), b2 = __shfl(base, o);
+      if (in && o != l && ctx > 0 && c2 > 0 && base < b2 + c2 && b2 < base + ctx) bad = true;
+    }
   }
   const bool any_bad = __any(bad);
   if (any_bad) {
@@ -268,6 +275,20 @@ __global__ __launch_bounds__(256) void k_begin(StepArgs a, int roles) {
     fill_u32((uint32_t *)a.sc.estate, 2LL * a.sc.atiles, 0u, i0, step);
     fill_u32((uint32_t *)a.sc.astate, 2LL * a.sc.atiles, 0u, i0, step);
   }
+  if ((roles & BEGIN_REQ) && a.pages) {
+    // every page a request's tokens use lies in the pool (out-of-range contexts are
+    // the request table's error)
+    const int64_t n = (int64_t)a.B * a.page_stride;
+    bool bad = false;
+    for (int64_t i = i0; i < n; i += step) {
+      const int b = (int)(i / a.page_stride);
+      const int j = (int)(i - (int64_t)b * a.page_stride);
+      const int c = a.ctx_len[b];
+      if (c > 0 && c <= a.max_ctx && j < (c + 15) / 16 && !page_in_pool(a, a.pages[i]))
+        bad = true;
+    }
+    if (bad) fail(a.ws.status, ECHO_EDEVARG);
+  }
 }
 
 hipError_t launch_begin(const StepArgs &a, int roles, hipStream_t s) {
@@ -311,8 +332,27 @@ hipError_t launch_kindex_pack(const uint8_t *rows, uint8_t *tiled, int64_t n_row
 
 constexpr int kChunks = kScoreTile / 64;  // 64-token chunks per work item
 
+// Tiled-K groups (host id / 16, wave-uniform) of the four 16-token sub-tiles of
+// the chunk that starts at token s0 (a multiple of 64) of request b: from the page
+// table (PAGED, one page per group: scalar loads, issued a chunk before the K loads
+// that use them), or from the request's contiguous range.  Sub-tiles past the
+// context take the request's last group (in bounds; their scores are dropped).
+template <bool PAGED>
+__device__ inline void chunk_groups(const StepArgs &a, const ReqInfo &r, int b, int s0,
+                                    int32_t (&grp)[4]) {
+  const int glast = (r.ctx - 1) & ~15;
+  const int s0u = __builtin_amdgcn_readfirstlane(s0);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int st = s0u + 16 * u;
+    const int sg = st < r.ctx ? st : glast;
+    const int32_t g = PAGED ? a.pages[(int64_t)b * a.page_stride + (sg >> 4)] : (r.base + sg) >> 4;
+    grp[u] = __builtin_amdgcn_readfirstlane(g);
+  }
+}
+
 // K operands of one 64-token chunk for this lane (tokens s0 .. s0+63 of request
-// r, s0 a multiple of 64): sub-tile u holds tokens s0 + 16u .. +15; this lane
+// r, s0 a multiple of 64, in the groups `grp`): sub-tile u holds tokens s0 + 16u .. +15; this lane
 // feeds token s0 + 16u + (lane & 15) with dims 32c .. 32c+31, c = lane >> 4, read
 // as two 16-byte pieces at 16*lane and 8*D + 16*lane inside the token's 16-row
 // group.  The loads go straight into the operand registers, with no select
@@ -321,11 +361,10 @@ constexpr int kChunks = kScoreTile / 64;  // 64-token chunks per work item
 // context read the request's last group (in bounds; their scores are dropped),
 // and lanes whose dims lie past D read the same token's first 32 dims, which
 // meet the zero padding of q (an exact 0 for any finite e4m3 byte).
-__device__ inline void load_k_chunk(const StepArgs &a, const ReqInfo &r, int s0, int lane,
+__device__ inline void load_k_chunk(const StepArgs &a, const int32_t (&grp)[4], int lane,
                                     v8i (&kb)[4], bool real = true) {
   const bool dim_ok = 32 * (lane >> 4) < a.D;
   const int lp = dim_ok ? lane : (lane & 15);
-  const int glast = (r.ctx - 1) & ~15;
   // real = false (no next item): every lane reads the same 16 bytes, one cache
   // line per instruction, only to keep the load count the same on every path.
   // The choice is made on offsets, as products with a wave-uniform 0/1 that went
@@ -338,12 +377,9 @@ __device__ inline void load_k_chunk(const StepArgs &a, const ReqInfo &r, int s0,
   // wave-uniform 64-bit group address + 32-bit lane offset: the loads use the
   // scalar-base addressing form and need no per-lane 64-bit arithmetic
   const uint32_t lo = (uint32_t)lp * 16u * rl;
-  const int s0u = __builtin_amdgcn_readfirstlane(s0);
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const int st = s0u + 16 * u;
-    const int sg = st < r.ctx ? st : glast;
-    const uint64_t go = (uint64_t)(((int64_t)r.base + sg) * a.D) * rl;
+    const uint64_t go = (uint64_t)((int64_t)grp[u] * 16 * a.D) * rl;
     const uint32_t go_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)go);
     const uint32_t go_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(go >> 32));
     const uint8_t *g = a.kidx + (((uint64_t)go_hi << 32) | go_lo);
@@ -431,9 +467,11 @@ __device__ inline void pf_plan(const StepArgs &a, const ReqInfo &r, const uint64
 // Installs the planned candidates of item pi (maps, priority t, the rank-ordered
 // lists and the copy queue); the request's last item also publishes n_cand, n_pf
 // and the final count the copy waves stop at.
+template <bool PAGED>
 __device__ inline void pf_commit(const StepArgs &a, const ReqInfo &r, int b, int pi, int c_all,
                                  int E, const int (&rank)[kChunks], int tk,
-                                 const int (&gv)[kChunks], int t, int nfree) {
+                                 const int (&gv)[kChunks], const int (&gp)[kChunks], int t,
+                                 int nfree) {
   const int lane = lane_id();
   const int s_wave = pi * kScoreTile;
 #pragma unroll
@@ -441,7 +479,7 @@ __device__ inline void pf_commit(const StepArgs &a, const ReqInfo &r, int b, int
     const int g = gv[c];
     if (((tk >> c) & 1) && g >= 0 && g < a.n_gpu) {
       const int s = s_wave + c * 64 + lane;
-      const int64_t h = (int64_t)r.base + s;
+      const int64_t h = PAGED ? 16LL * gp[c] + (s & 15) : (int64_t)r.base + s;
       a.h2g[h] = g;
       a.g2h[g] = (int32_t)h;
       a.freef[g] = 0;
@@ -473,18 +511,35 @@ __device__ inline bool pf_needed(const ReqInfo &r, int pi, int c_all) {
   return c_all > 0 || pi == r.ntiles - 1;
 }
 
+// Page-table entries of the planned candidates of item pi (0 where a lane takes no
+// slot: a dummy in-bounds read), issued with the free-list reads.
+template <bool PAGED>
+__device__ inline void pf_pages(const StepArgs &a, int b, int pi, int tk, int (&gp)[kChunks]) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    gp[c] = 0;
+    if (PAGED) {
+      const int s = pi * kScoreTile + c * 64 + lane;
+      gp[c] = a.pages[(int64_t)b * a.page_stride + (((tk >> c) & 1) ? (s >> 4) : 0)];
+    }
+  }
+}
+
 // Blocking epilogue: resolve item pi's rank, then install.
+template <bool PAGED>
 __device__ static void pf_install(const StepArgs &a, const ReqInfo &r, int b, int pi,
                                   const uint64_t (&cand)[kChunks], int c_all, int t,
                                   int nfree) {
   const int E = lb_resolve(a.sc.tstate, r.tile0 + pi, r.tile0, c_all, a.ws.status);
-  int rank[kChunks], tk = 0, gi[kChunks], gv[kChunks];
+  int rank[kChunks], tk = 0, gi[kChunks], gv[kChunks], gp[kChunks];
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) rank[c] = gi[c] = 0;
   if (c_all > 0) pf_plan(a, r, cand, E, nfree, rank, tk, gi);
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) gv[c] = a.idxbuf[gi[c]];
-  pf_commit(a, r, b, pi, c_all, E, rank, tk, gv, t, nfree);
+  pf_pages<PAGED>(a, b, pi, tk, gp);
+  pf_commit<PAGED>(a, r, b, pi, c_all, E, rank, tk, gv, gp, t, nfree);
 }
 
 // Epilogues waiting for their rank, per wave, in a ring in LDS.  An item's count
@@ -522,7 +577,7 @@ struct WaveBuf {
 // cost more than their bytes: on 2.8M tokens, leaving them out shortened the
 // launch by 5-8 us of about 70, and gathering them at the end of each wave's
 // job shortened it by 4-5 us.
-template <int HG, bool PF>
+template <int HG, bool PF, bool PAGED>
 __device__ static void score_job(const StepArgs &a, const ReqInfo &r, int b, int k, int t,
                                  int nfree, PendItem *pq, WaveBuf *wbuf) {
   const int lane = lane_id();
@@ -575,7 +630,12 @@ __device__ static void score_job(const StepArgs &a, const ReqInfo &r, int b, int
   // next item's first one at the end of an item) is in flight while c computes.
   v8i kb[2][4];
   int i = k;
-  load_k_chunk(a, r, i * kScoreTile, lane, kb[0]);
+  // groups of the chunk being scored (gcur) and of the chunk whose loads go out next
+  // (gnext); each chunk's groups are read one chunk before its loads are issued
+  int32_t gcur[4], gnext[4];
+  chunk_groups<PAGED>(a, r, b, i * kScoreTile, gcur);
+  load_k_chunk(a, gcur, lane, kb[0]);
+  chunk_groups<PAGED>(a, r, b, i * kScoreTile + 64, gnext);
   // the previous item's threshold bits and map entries (its epilogue's inputs)
   bool have_prev = false;
   int p_i = 0;
@@ -587,12 +647,12 @@ __device__ static void score_job(const StepArgs &a, const ReqInfo &r, int b, int
   uint64_t sv = 0;
   bool planned = false;
   int o_i = 0, o_c = 0;  // the oldest queued item and its count
-  int E0 = 0, tk = 0, rk[kChunks], gv[kChunks];
+  int E0 = 0, tk = 0, rk[kChunks], gv[kChunks], gp[kChunks];
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
     p_above[c] = 0;
     p_g[c] = 0;
-    rk[c] = gv[c] = 0;
+    rk[c] = gv[c] = gp[c] = 0;
   }
   auto read_oldest = [&]() {
     o_i = __builtin_amdgcn_readfirstlane(pq[qh].pi);
@@ -603,7 +663,7 @@ __device__ static void score_job(const StepArgs &a, const ReqInfo &r, int b, int
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) oc[c] = pq[qh].cand[c];
     read_oldest();
-    pf_install(a, r, b, o_i, oc, o_c, t, nfree);
+    pf_install<PAGED>(a, r, b, o_i, oc, o_c, t, nfree);
     qh = qh + 1 == kPending ? 0 : qh + 1;
     --qn;
   };
@@ -638,13 +698,31 @@ __device__ static void score_job(const StepArgs &a, const ReqInfo &r, int b, int
       // consumed an item later, and a load issued after those K loads could not
       // be waited for without waiting for them too
       gq[c] = 0;
-      if (PF) gq[c] = a.h2g[(int64_t)r.base + (valid ? s : r.ctx - 1)];
+      if (PF) {
+        // this lane's token (or the request's last one past the context), in the
+        // group of its sub-tile
+        const int ts = valid ? s : r.ctx - 1;
+        const int u = lane >> 4;
+        const int32_t g = u == 0 ? gcur[0] : u == 1 ? gcur[1] : u == 2 ? gcur[2] : gcur[3];
+        gq[c] = a.h2g[16LL * g + (ts & 15)];
+      }
       if (c + 1 < kChunks) {
-        load_k_chunk(a, r, s_wave + (c + 1) * 64, lane, kb[(c + 1) & 1]);
+        load_k_chunk(a, gnext, lane, kb[(c + 1) & 1]);
       } else {
         // unconditional (after the last item, a one-line dummy read): a load under
         // a branch would make the compiler drain every load before the join
-        load_k_chunk(a, r, (ni < r.ntiles ? ni : i) * kScoreTile, lane, kb[0], ni < r.ntiles);
+        load_k_chunk(a, gnext, lane, kb[0], ni < r.ntiles);
+      }
+      {  // the groups of the chunk after the one just issued
+        int32_t gafter[4];
+        const int s_after = c + 2 < kChunks ? s_wave + (c + 2) * 64
+                            : (ni < r.ntiles ? ni * kScoreTile + (c + 2 - kChunks) * 64 : s_wave);
+        chunk_groups<PAGED>(a, r, b, s_after, gafter);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          gcur[u] = gnext[u];
+          gnext[u] = gafter[u];
+        }
       }
       const float score = score_chunk<HG>(kb[c & 1], qa, wr, lane);
       wbuf->score[(nbuf * kChunks + c) * 64 + lane] = score;
@@ -679,9 +757,10 @@ __device__ static void score_job(const StepArgs &a, const ReqInfo &r, int b, int
           }
 #pragma unroll
           for (int cc = 0; cc < kChunks; ++cc) gv[cc] = a.idxbuf[gi[cc]];
+          pf_pages<PAGED>(a, b, qn > 0 ? o_i : 0, tk, gp);
         }
         if (c == 3 && planned) {
-          pf_commit(a, r, b, o_i, o_c, E0, rk, tk, gv, t, nfree);
+          pf_commit<PAGED>(a, r, b, o_i, o_c, E0, rk, tk, gv, gp, t, nfree);
           planned = false;
           qh = qh + 1 == kPending ? 0 : qh + 1;
           --qn;
@@ -748,7 +827,7 @@ __device__ inline ReqInfo wave_uniform(const ReqInfo &x) {
 // slots are numbered request by request, so a wave meets its requests in
 // increasing order and every look-back wait is on an item that a resident wave
 // reaches without waiting on a later one.
-template <int HG, bool ANY_PF>
+template <int HG, bool ANY_PF, bool PAGED>
 __device__ static void score_wave(const StepArgs &a, const ReqInfo *s_req, int w, PendItem *pq,
                                   WaveBuf *wbuf) {
   const int lane = lane_id();
@@ -762,16 +841,16 @@ __device__ static void score_wave(const StepArgs &a, const ReqInfo *s_req, int w
     const ReqInfo r = wave_uniform(s_req[b]);
     const int k = slot - r.slot0;
     if (ANY_PF && r.active)
-      score_job<HG, true>(a, r, b, k, t, nfree, pq, wbuf);
+      score_job<HG, true, PAGED>(a, r, b, k, t, nfree, pq, wbuf);
     else
-      score_job<HG, false>(a, r, b, k, t, nfree, pq, wbuf);
+      score_job<HG, false, PAGED>(a, r, b, k, t, nfree, pq, wbuf);
   }
 }
 
 // The first score_blocks workgroups score, the rest copy prefetched rows (until
 // scoring ends, when the copy continues in the step's next kernels, else to the
 // end).  ANY_PF = false (threshold +inf) compiles the prefetch path out.
-template <int HG, bool ANY_PF>
+template <int HG, bool ANY_PF, bool PAGED>
 __global__ __launch_bounds__(512) void k_score(StepArgs a) {
   __shared__ ReqInfo s_req[kMaxBatch];
   __shared__ PendItem s_pend[ANY_PF ? kScoreWaves : 1][ANY_PF ? kPending : 1];
@@ -793,7 +872,7 @@ __global__ __launch_bounds__(512) void k_score(StepArgs a) {
   if (!copy) {
     // the wave index through readfirstlane: every job index derived from it is
     // then known to be wave-uniform and lives in scalar registers
-    score_wave<HG, ANY_PF>(a, s_req,
+    score_wave<HG, ANY_PF, PAGED>(a, s_req,
                            __builtin_amdgcn_readfirstlane(role_idx * kScoreWaves + wid),
                            &s_pend[ANY_PF ? wid : 0][0], &s_wbuf[wid]);
     if (lane_id() == 0 && atomicSub(&s_left, 1) == 1)
@@ -805,13 +884,13 @@ __global__ __launch_bounds__(512) void k_score(StepArgs a) {
   }
 }
 
-template <bool ANY_PF>
+template <bool ANY_PF, bool PAGED>
 static void launch_score_hg(const StepArgs &a, int grid, hipStream_t s) {
   switch ((a.H + 15) / 16) {
-    case 1: hipLaunchKernelGGL((k_score<1, ANY_PF>), dim3(grid), dim3(512), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_score<2, ANY_PF>), dim3(grid), dim3(512), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((k_score<3, ANY_PF>), dim3(grid), dim3(512), 0, s, a); break;
-    default: hipLaunchKernelGGL((k_score<4, ANY_PF>), dim3(grid), dim3(512), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((k_score<1, ANY_PF, PAGED>), dim3(grid), dim3(512), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_score<2, ANY_PF, PAGED>), dim3(grid), dim3(512), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((k_score<3, ANY_PF, PAGED>), dim3(grid), dim3(512), 0, s, a); break;
+    default: hipLaunchKernelGGL((k_score<4, ANY_PF, PAGED>), dim3(grid), dim3(512), 0, s, a); break;
   }
 }
 
@@ -846,10 +925,14 @@ void index_grid(const echo_dims_t &d, bool with_copy, int *score_blocks, int *co
 
 hipError_t launch_score(const StepArgs &a, hipStream_t s) {
   const int grid = a.score_blocks + a.copy_waves / kScoreWaves;
-  if (a.mode == ECHO_THETA_POS_INF)
-    launch_score_hg<false>(a, grid, s);
-  else
-    launch_score_hg<true>(a, grid, s);
+  const bool pf = a.mode != ECHO_THETA_POS_INF;
+  if (a.pages) {
+    if (pf) launch_score_hg<true, true>(a, grid, s);
+    else launch_score_hg<false, true>(a, grid, s);
+  } else {
+    if (pf) launch_score_hg<true, false>(a, grid, s);
+    else launch_score_hg<false, false>(a, grid, s);
+  }
   return hipGetLastError();
 }
 

@@ -11,42 +11,59 @@
 // stays where it is.  The ascending free list that the next step's prefetch
 // hands out is rebuilt from the free flags.  Admission puts a new request into
 // an empty batch row after checking its host range against the live requests
-// and the map.
+// and the map.  With a page table a request's tokens live on pages of 16 host
+// ids anywhere in the pool: release walks its tokens through the table (the
+// pages stay the caller's to hand out again) and admission checks that the new
+// request's pages lie in the pool, are listed once and belong to no live request
+// (a bitmap over the pool's pages), which is what lets a new request fill the
+// holes that released ones leave.
 #include "kernels.h"
 
 namespace echo {
 
 constexpr int kReleaseThreads = 256;
 constexpr int kReleaseBlocksX = 64;  // workgroups per released request
+constexpr int kCheckGrid = 64;       // workgroups of the page checks
 
-// Every workgroup checks every masked request (the same data, so every
-// workgroup reaches the same verdict); the first one reports it.
-__global__ __launch_bounds__(kReleaseThreads) void k_release_free(StepArgs a,
-                                                                  const int32_t *mask) {
-  __shared__ int s_bad;
+// Every masked request's tokens must fit: its context in [0, max_ctx] and its
+// range in the pool, or (page table) its pages in the table and in the pool.  Any
+// failure sets ECHO_EDEVARG, which turns the rest of the release into a no-op.
+__global__ __launch_bounds__(kReleaseThreads) void k_release_check(StepArgs a,
+                                                                   const int32_t *mask) {
+  if (failed(a.ws.status)) return;
   const int tid = threadIdx.x;
-  const int32_t st0 = __hip_atomic_load(a.ws.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (tid < kWave) {
-    bool bad = false;
-    if (tid < a.B && mask[tid]) {
-      const int32_t n = a.ctx_len[tid], hb = a.host_base[tid];
-      bad = n < 0 || n > a.max_ctx || hb < 0 || (int64_t)hb + n > a.n_host;
-    }
-    const uint64_t any = __ballot(bad);
-    if (tid == 0) {
-      s_bad = any != 0;
-      if (any && blockIdx.x == 0 && blockIdx.y == 0 && st0 == 0) fail(a.ws.status, ECHO_EDEVARG);
+  bool bad = false;
+  if (blockIdx.x == 0 && tid < a.B && mask[tid]) {
+    const int32_t n = a.ctx_len[tid];
+    if (n < 0 || n > a.max_ctx) bad = true;
+    else if (a.pages) bad = (n + 15) / 16 > a.page_stride;
+    else bad = a.host_base[tid] < 0 || (int64_t)a.host_base[tid] + n > a.n_host;
+  }
+  if (a.pages) {
+    const int64_t total = (int64_t)a.B * a.page_stride;
+    for (int64_t i = (int64_t)blockIdx.x * kReleaseThreads + tid; i < total;
+         i += (int64_t)gridDim.x * kReleaseThreads) {
+      const int b = (int)(i / a.page_stride);
+      const int j = (int)(i - (int64_t)b * a.page_stride);
+      const int32_t n = a.ctx_len[b];
+      if (mask[b] && n > 0 && n <= a.max_ctx && j < (n + 15) / 16 && !page_in_pool(a, a.pages[i]))
+        bad = true;
     }
   }
-  __syncthreads();
-  if (st0 != 0 || s_bad) return;
+  if (bad) fail(a.ws.status, ECHO_EDEVARG);
+}
+
+__global__ __launch_bounds__(kReleaseThreads) void k_release_free(StepArgs a,
+                                                                  const int32_t *mask) {
+  if (failed(a.ws.status)) return;  // an earlier error, or k_release_check's verdict
+  const int tid = threadIdx.x;
   const int b = blockIdx.y;
   if (!mask[b]) return;
-  const int64_t base = a.host_base[b];
+  const int32_t base = a.pages ? 0 : a.host_base[b];
   const int32_t n = a.ctx_len[b];
   for (int32_t s = blockIdx.x * kReleaseThreads + tid; s < n;
        s += kReleaseBlocksX * kReleaseThreads) {
-    const int64_t h = base + s;
+    const int64_t h = token_host(a, b, base, s);
     const int32_t g = a.h2g[h];
     if (g >= 0 && g < a.n_gpu) {
       a.g2h[g] = -1;
@@ -75,6 +92,7 @@ __global__ __launch_bounds__(kListThreads) void k_release_finish(StepArgs a, con
 
 hipError_t launch_release(const StepArgs &a, const int32_t *mask, int32_t *ctx_io, int commit,
                           hipStream_t s) {
+  hipLaunchKernelGGL(k_release_check, dim3(kCheckGrid), dim3(kReleaseThreads), 0, s, a, mask);
   hipLaunchKernelGGL(k_release_free, dim3(kReleaseBlocksX, a.B), dim3(kReleaseThreads), 0, s, a,
                      mask);
   hipLaunchKernelGGL(k_release_finish, dim3(1), dim3(kListThreads), 0, s, a, mask, ctx_io,
@@ -82,11 +100,64 @@ hipError_t launch_release(const StepArgs &a, const int32_t *mask, int32_t *ctx_i
   return hipGetLastError();
 }
 
-// Admission of request b with host range [base, base + len) (checked on the host
-// against n_host and max_ctx).  Checks, in this order: the row is empty
-// (EDEVARG otherwise), no live request's range meets the new one (ECAPACITY),
-// no token of the range is mapped (EDEVARG).  Nothing is written on an error;
-// otherwise the threshold resets and, with `commit`, the batch row is written.
+// Admission with a page table, before k_admit: the row is empty (EDEVARG
+// otherwise), the new tokens need at most page_stride pages (EDEVARG), and the
+// page bitmap is cleared.
+__global__ __launch_bounds__(kListThreads) void k_admit_pages_begin(StepArgs a, int b, int32_t len,
+                                                                    const int32_t *ctx_io) {
+  if (failed(a.ws.status)) return;
+  const int tid = threadIdx.x;
+  if (tid == 0 && (ctx_io[b] != 0 || (len + 15) / 16 > a.page_stride))
+    fail(a.ws.status, ECHO_EDEVARG);
+  const int64_t words = (a.n_host / 16 + 31) / 32;
+  for (int64_t i = tid; i < words; i += kListThreads) a.sc.pgbits[i] = 0;
+}
+
+// The new request's pages: each in the pool and listed once (EDEVARG), marked in
+// the bitmap.
+__global__ __launch_bounds__(kReleaseThreads) void k_admit_pages_mark(StepArgs a, int b,
+                                                                      int32_t len) {
+  if (failed(a.ws.status)) return;
+  const int np = (len + 15) / 16;
+  bool bad = false;
+  for (int j = blockIdx.x * kReleaseThreads + threadIdx.x; j < np;
+       j += gridDim.x * kReleaseThreads) {
+    const int32_t p = a.pages[(int64_t)b * a.page_stride + j];
+    if (!page_in_pool(a, p)) {
+      bad = true;
+    } else {
+      const uint32_t bit = 1u << (p & 31);
+      if (atomicOr(&a.sc.pgbits[p >> 5], bit) & bit) bad = true;  // listed twice
+    }
+  }
+  if (bad) fail(a.ws.status, ECHO_EDEVARG);
+}
+
+// No page of a live request's tokens is one of the new request's (ECAPACITY).
+__global__ __launch_bounds__(kReleaseThreads) void k_admit_pages_overlap(StepArgs a, int b,
+                                                                         const int32_t *ctx_io) {
+  if (failed(a.ws.status)) return;
+  const int64_t total = (int64_t)a.B * a.page_stride;
+  bool hit = false;
+  for (int64_t i = (int64_t)blockIdx.x * kReleaseThreads + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * kReleaseThreads) {
+    const int o = (int)(i / a.page_stride);
+    const int j = (int)(i - (int64_t)o * a.page_stride);
+    const int32_t n = ctx_io[o];
+    if (o == b || n <= 0 || j >= (n + 15) / 16) continue;
+    const int32_t p = a.pages[i];
+    if (page_in_pool(a, p) && ((a.sc.pgbits[p >> 5] >> (p & 31)) & 1u)) hit = true;
+  }
+  if (hit) fail(a.ws.status, ECHO_ECAPACITY);
+}
+
+// Admission of request b with len tokens: the host range [base, base + len)
+// (checked on the host against n_host and max_ctx), or the pages of row b of the
+// page table (checked by the three kernels above).  Checks here, in this order:
+// without a page table, the row is empty (EDEVARG otherwise) and no live request's
+// range meets the new one (ECAPACITY); in both cases, no new token is mapped
+// (EDEVARG).  Nothing is written on an error; otherwise the threshold resets and,
+// with `commit`, the batch row is written.
 __global__ __launch_bounds__(kListThreads) void k_admit(StepArgs a, int b, int32_t base,
                                                         int32_t len, int32_t *hb_io,
                                                         int32_t *ctx_io, int commit) {
@@ -95,7 +166,7 @@ __global__ __launch_bounds__(kListThreads) void k_admit(StepArgs a, int b, int32
   const int tid = threadIdx.x;
   if (tid < kWave) {
     int code = 0;  // lane o: does request o block the admission?
-    if (tid < a.B) {
+    if (!a.pages && tid < a.B) {
       const int32_t n = ctx_io[tid];
       if (tid == b) {
         if (n != 0) code = ECHO_EDEVARG;
@@ -113,7 +184,8 @@ __global__ __launch_bounds__(kListThreads) void k_admit(StepArgs a, int b, int32
   int code = s_code;
   if (code == 0) {
     int stale = 0;
-    for (int32_t s = tid; s < len; s += kListThreads) stale |= a.h2g[(int64_t)base + s] != -1;
+    for (int32_t s = tid; s < len; s += kListThreads)
+      stale |= a.h2g[token_host(a, b, base, s)] != -1;
     if (__syncthreads_or(stale)) code = ECHO_EDEVARG;
   }
   if (tid != 0) return;
@@ -122,7 +194,7 @@ __global__ __launch_bounds__(kListThreads) void k_admit(StepArgs a, int b, int32
     return;
   }
   if (commit) {
-    hb_io[b] = base;
+    if (!a.pages) hb_io[b] = base;
     ctx_io[b] = len;
   }
   a.theta[b] = __builtin_huge_valf();
@@ -131,6 +203,13 @@ __global__ __launch_bounds__(kListThreads) void k_admit(StepArgs a, int b, int32
 
 hipError_t launch_admit(const StepArgs &a, int b, int32_t base, int32_t len, int32_t *hb_io,
                         int32_t *ctx_io, int commit, hipStream_t s) {
+  if (a.pages) {
+    hipLaunchKernelGGL(k_admit_pages_begin, dim3(1), dim3(kListThreads), 0, s, a, b, len, ctx_io);
+    hipLaunchKernelGGL(k_admit_pages_mark, dim3(kCheckGrid), dim3(kReleaseThreads), 0, s, a, b,
+                       len);
+    hipLaunchKernelGGL(k_admit_pages_overlap, dim3(kCheckGrid), dim3(kReleaseThreads), 0, s, a,
+                       b, ctx_io);
+  }
   hipLaunchKernelGGL(k_admit, dim3(1), dim3(kListThreads), 0, s, a, b, base, len, hb_io, ctx_io,
                      commit);
   return hipGetLastError();

@@ -244,7 +244,7 @@ __device__ static void manage_block(const StepArgs &a, int blk, int32_t st0) {
       const int j = rank - s_moff[b];
       const int s = a.ws.miss_tok[(int64_t)b * a.K + j];
       const int i = a.sc.miss_i[(int64_t)b * a.K + j];
-      const int64_t h = (int64_t)a.sc.req[b].base + s;
+      const int64_t h = token_host(a, b, a.sc.req[b].base, s);
       a.h2g[h] = g;
       a.g2h[g] = (int32_t)h;
       a.freef[g] = 0;

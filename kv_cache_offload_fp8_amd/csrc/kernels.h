@@ -14,6 +14,8 @@ struct StepArgs {
   // batch (B is a host value baked into the launch)
   int32_t B;
   const int32_t *host_base, *ctx_len;
+  const int32_t *pages;  // [B][page_stride] host page of each 16-token page, or null
+  int32_t page_stride;
   // layer
   int32_t *h2g, *g2h, *prio, *idxbuf;
   uint8_t *freef;
@@ -41,6 +43,18 @@ struct StepArgs {
   echo_ws_t ws;
   Scratch sc;
 };
+
+// Host id of token s of request b: through the page table (a page is 16 host ids,
+// one tiled-K group), or in the contiguous range that starts at `base`.
+__device__ inline int64_t token_host(const StepArgs &a, int b, int32_t base, int32_t s) {
+  if (a.pages) return 16LL * a.pages[(int64_t)b * a.page_stride + (s >> 4)] + (s & 15);
+  return (int64_t)base + s;
+}
+
+// Whether host page p lies in the pool (all 16 of its ids below n_host).
+__device__ inline bool page_in_pool(const StepArgs &a, int32_t p) {
+  return p >= 0 && 16LL * p + 16 <= a.n_host;
+}
 
 // The ascending free list (idxbuf[0 .. nfree)) rebuilt from the free flags by one
 // workgroup of kListThreads threads (16 flags per thread per round, block scan).

@@ -93,7 +93,7 @@ __device__ static int protect_request(const StepArgs &a, int b, const int32_t *s
     int s = 0, g = -1;
     if (valid) {
       s = s_sel[i];
-      const int64_t h = (int64_t)base + s;
+      const int64_t h = token_host(a, b, base, s);
       if (h >= 0 && h < a.n_host) g = a.h2g[h];
       if (g >= a.n_gpu) g = -1;
       if (g >= 0) a.prio[g] = t;

@@ -188,12 +188,23 @@ class PrefillWorkspace:
 
 
 class Batch:
-    def __init__(self, host_base, ctx, device="cuda"):
-        self.host_base = torch.as_tensor(np.asarray(host_base, np.int32), device=device)
+    """Device batch rows: contiguous host ranges (host_base), or a page table
+    [B, page_stride] of 16-id host pages (pages; host_base is then not used)."""
+
+    def __init__(self, host_base, ctx, device="cuda", pages=None):
         self.ctx = torch.as_tensor(np.asarray(ctx, np.int32), device=device)
         self.B = int(self.ctx.numel())
-        self.struct = abi.echo_batch_t(self.B, _ptr(self.host_base) if self.B else None,
-                                       _ptr(self.ctx) if self.B else None)
+        self.host_base = torch.as_tensor(np.asarray(host_base if host_base is not None else
+                                                    np.zeros(self.B), np.int32), device=device)
+        self.pages = None
+        stride = 0
+        if pages is not None:
+            self.pages = torch.as_tensor(np.ascontiguousarray(pages, np.int32), device=device)
+            stride = int(self.pages.shape[1])
+        self.struct = abi.echo_batch_t(
+            self.B, _ptr(self.host_base) if self.B and pages is None else None,
+            _ptr(self.ctx) if self.B else None,
+            _ptr(self.pages) if self.pages is not None else None, stride)
 
 
 def pack_kidx(dims: abi.echo_dims_t, rows: torch.Tensor, out: torch.Tensor = None) -> torch.Tensor:

@@ -471,8 +471,9 @@ int orc_layer_step(const orc_cfg *c, orc_state *st, int B,
  * host id h = host_id(map, b, ctx[b]); key row kidx[h] = k_new[b] (D bytes) and
  * latent host_kv[h] = lat_new[b] (`latent` values); with `advance`, ctx[b] grows
  * by one.  The requests are checked first, in order: no room (ctx[b] = max_ctx,
- * the id outside the pool -- past n_host, or with a page table a page slot past
- * page_stride or a page outside the pool -- or, without a page table, h inside
+ * the id outside the pool -- past n_host, or with a page table the new token's
+ * page slot past page_stride or its page outside the pool -- or, without a page
+ * table, h inside
  * another request's range [host_base[o], host_base[o] + ctx[o]] counting that
  * request's own new token) gives ORC_ECAPACITY, a host id some slot already maps
  * (h2g[h] != -1) gives ORC_EDEVARG; the first such request decides and nothing
@@ -486,8 +487,15 @@ int orc_append(int B, int D, int latent, int64_t n_host, int32_t max_ctx,
                uint16_t *host_kv, int advance) {
   for (int b = 0; b < B; ++b) {
     if (ctx[b] == 0) continue; /* an empty row */
-    if (ctx[b] < 0 || ctx[b] >= max_ctx || !tokens_fit(map, b, (int64_t)ctx[b] + 1, n_host))
+    if (ctx[b] < 0 || ctx[b] >= max_ctx) return ORC_ECAPACITY;
+    if (map->pages) { /* the page listed for the new token: in the table, in the pool */
+      const int64_t j = ctx[b] / 16;
+      if (j >= map->page_stride) return ORC_ECAPACITY;
+      const int32_t p = map->pages[(int64_t)b * map->page_stride + j];
+      if (p < 0 || 16 * (int64_t)p + 16 > n_host) return ORC_ECAPACITY;
+    } else if (!tokens_fit(map, b, (int64_t)ctx[b] + 1, n_host)) {
       return ORC_ECAPACITY;
+    }
     const int64_t h = host_id(map, b, ctx[b]);
     if (!map->pages) {
       const int32_t *hb = map->host_base;

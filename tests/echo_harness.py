@@ -113,9 +113,28 @@ def tile_kidx(rows: np.ndarray) -> np.ndarray:
     return out.reshape(n, D)
 
 
+def scatter_pages(base, ctx, room, n_host, seed, stride_extra=0):
+    """A page table for requests laid out at host_base (each owning ceil((ctx + room) / 16)
+    pages): every page of the pool moved to a random other page.  Returns (pages
+    [B, stride] (-1 past each request's pages), perm: old page -> new page)."""
+    npool = n_host // 16
+    perm = np.random.default_rng(seed).permutation(npool).astype(np.int64)
+    span = (np.asarray(ctx, np.int64) + room + 15) // 16
+    stride = int(span.max() if span.size else 1) + stride_extra
+    pages = np.full((len(ctx), max(1, stride)), -1, np.int32)
+    for b in range(len(ctx)):
+        first = int(base[b]) // 16
+        pages[b, : span[b]] = perm[first: first + span[b]]
+    return pages, perm
+
+
 class Rig:
     def __init__(self, wl, steps, device="cuda", ctx=None, n_gpu=None, n_host=None, seed=0,
-                 keep_pool=True, max_ctx=None, layer=0, cap_div=None, top_k=None, room=0):
+                 keep_pool=True, max_ctx=None, layer=0, cap_div=None, top_k=None, room=0,
+                 paged=False, page_seed=7, stride_extra=0):
+        """paged: the requests' pages scattered over the host pool in random order, with
+        a page table on both sides (the oracle's R14); stride_extra: spare page-table
+        entries per request."""
         if n_gpu is not None or n_host is not None or cap_div is not None or top_k is not None:
             wl = wl.scaled(n_gpu=n_gpu or wl.n_gpu, n_host=n_host or wl.n_host,
                            cap_div=cap_div or wl.cap_div, top_k=top_k or wl.top_k)
@@ -133,20 +152,35 @@ class Rig:
         self.dims = R.make_dims(wl.heads, wl.head_dim, wl.top_k, wl.n_host, wl.n_gpu,
                                 max(1, self.B), mc, wl.latent, wl.alpha, wl.cap_div, steps)
         self.host = R.HostPool(wl.n_host, wl.latent)
-        self.host.np[:] = self.inp.np_latents()
-        self.kidx_rows = self.inp.kidx.to(device)  # row-major, as the oracle reads it
+        self.pages = None
+        kid = self.inp.np_kidx()
+        lat = self.inp.np_latents()
+        if paged:
+            # every host page moved to its image under a random permutation of the pool
+            self.pages, perm = scatter_pages(self.base, self.ctx, room, wl.n_host, page_seed,
+                                             stride_extra)
+            self.page_perm = perm
+            src = (np.arange(wl.n_host) // 16).astype(np.int64)
+            dst = 16 * perm[src] + np.arange(wl.n_host) % 16
+            kid2 = np.empty_like(kid)
+            kid2[dst] = kid
+            lat2 = np.empty_like(lat)
+            lat2[dst] = lat
+            kid, lat = kid2, lat2
+        self.host.np[:] = lat
+        self.kidx_rows = torch.from_numpy(kid).to(device)  # row-major, as the oracle reads it
         self.kidx = R.pack_kidx(self.dims, self.kidx_rows)
         self.layer = R.Layer(self.dims, self.kidx, self.host, self.B, device)
         if self.B:
             self.layer.q.copy_(self.inp.q.to(device))
             self.layer.w.copy_(self.inp.w.to(device))
         self.layer.init()
-        self.batch = R.Batch(self.base, self.ctx, device)
+        self.batch = R.Batch(self.base, self.ctx, device, pages=self.pages)
         self.ws = R.Workspace(self.dims, device)
         self.ws.reset()
         self.orc = O.OracleLayer(wl.heads, wl.head_dim, wl.top_k, wl.latent, wl.n_host, wl.n_gpu,
                                  max(1, self.B), wl.cap_div, wl.alpha, keep_pool=keep_pool)
-        self.np_kidx = self.inp.np_kidx()
+        self.np_kidx = kid
         # the oracle's own copy of the host pool: bytes the GPU writes there are
         # compared with it, not read back by the oracle
         self.orc_host = self.host.np.copy()
@@ -158,6 +192,22 @@ class Rig:
         # oracle's outputs add up; compared while every step so far ended cleanly
         self.exp_stats = np.zeros(abi.ECHO_STAT_WORDS, np.int64)
         self.stats_valid = True
+
+    def host_ids(self, b, toks):
+        """Host ids of request b's tokens `toks` (through the page table if any)."""
+        toks = np.asarray(toks, np.int64)
+        if self.pages is None:
+            return int(self.base[b]) + toks
+        return 16 * self.pages[b, toks // 16].astype(np.int64) + toks % 16
+
+    def set_pages(self, b, row):
+        """Write page-table row b on both sides (the caller's page allocation)."""
+        row = np.asarray(row, np.int32)
+        self.pages[b, :] = -1
+        self.pages[b, : row.size] = row
+        torch.cuda.current_stream().synchronize()
+        self.batch.pages[b] = torch.as_tensor(self.pages[b], device=self.batch.pages.device)
+        torch.cuda.current_stream().synchronize()
 
     # ------------------------------------------------------------ GPU calls
     def gpu_step(self, mode):
@@ -197,16 +247,15 @@ class Rig:
             for b in range(self.B):
                 n = int(self.ctx[b])
                 if n:
-                    h0 = int(self.base[b])
                     note = f"step {t} request {b}"
-                    ref, allow = assert_scores_close(sc[b, :n], q_t[b], self.np_w[b],
-                                                     self.np_kidx[h0:h0 + n], note,
+                    rows = self.np_kidx[self.host_ids(b, np.arange(n))]
+                    ref, allow = assert_scores_close(sc[b, :n], q_t[b], self.np_w[b], rows, note,
                                                      with_allowance=True)
                     if out["status"] == 0:
                         assert_topk_set_clause(out["sel_tok"][b, :int(out["n_sel"][b])], ref,
                                                allow, self.wl.top_k, note)
         o = self.orc.step(self.base, self.ctx, q_t, self.np_w, self.np_kidx, self.np_host,
-                          mode=mode, ext_scores=sc)
+                          mode=mode, ext_scores=sc, pages=self.pages)
         self.compare(out, st, o, t, check_pool)
         assert out["status"] == expect_status, (f"step {t}: status {out['status']}",
                                                 abi.echo_status_string(int(out["status"])))
@@ -288,20 +337,28 @@ class Rig:
         self.t = int(t)
 
     # ------------------------------------------------------------ decode append
-    def append_and_compare(self, advance=True, expect_status=0):
+    def append_and_compare(self, advance=True, expect_status=0, new_pages=None):
         """echo_append of this step's new tokens against the oracle's append: device
         context lengths, the whole tiled indexer K (against the oracle's rows tiled
-        here, independently of the library) and the host pool bytes."""
+        here, independently of the library) and the host pool bytes.  With a page
+        table, new_pages (an iterator of free host pages) gives every request whose
+        next token opens a page that page first."""
+        if self.pages is not None and new_pages is not None:
+            for b in range(self.B):
+                c = int(self.ctx[b])
+                if c and c % 16 == 0 and c // 16 < self.pages.shape[1]:
+                    row = self.pages[b].copy()
+                    row[c // 16] = next(new_pages)
+                    self.set_pages(b, row[row >= 0])
         k_new, lat_new = gen_append(self.wl, self.layer_id, self.B, self.t, self.seed)
         kd = torch.as_tensor(k_new, device="cuda")
         ld = torch.as_tensor(lat_new, device="cuda")
-        R.check(abi.echo_append(self.dims, self.layer.struct, self.batch.host_base.data_ptr(),
-                                self.batch.ctx.data_ptr(), self.B, kd.data_ptr(),
+        R.check(abi.echo_append(self.dims, self.layer.struct, self.batch.struct, kd.data_ptr(),
                                 ld.data_ptr(), self.ws.ws, int(advance), R.stream_handle()),
                 "echo_append")
         torch.cuda.current_stream().synchronize()
         rc = O.append(self.base, self.ctx, self.orc.h2g, k_new, lat_new.view(np.uint16),
-                      self.np_kidx, self.orc_host, self.dims.max_ctx, advance)
+                      self.np_kidx, self.orc_host, self.dims.max_ctx, advance, pages=self.pages)
         st = int(self.ws.status.item())
         assert st == rc == expect_status, ("append status", st, rc, expect_status)
         assert np.array_equal(self.batch.ctx.cpu().numpy(), self.ctx), "ctx_len"
@@ -316,20 +373,20 @@ class Rig:
         batch rows, maps, priorities, free flags, thresholds and the free list."""
         mask = np.asarray(mask, np.int32)
         m = torch.as_tensor(mask, device="cuda")
-        R.check(abi.echo_release(self.dims, self.layer.struct, self.batch.host_base.data_ptr(),
-                                 self.batch.ctx.data_ptr(), self.B, m.data_ptr(), int(commit),
-                                 self.ws.ws, R.stream_handle()), "echo_release")
-        rc = O.release(self.orc, self.base, self.ctx, mask, self.dims.max_ctx, commit)
+        R.check(abi.echo_release(self.dims, self.layer.struct, self.batch.struct, m.data_ptr(),
+                                 int(commit), self.ws.ws, R.stream_handle()), "echo_release")
+        rc = O.release(self.orc, self.base, self.ctx, mask, self.dims.max_ctx, commit,
+                       pages=self.pages)
         self._compare_lifecycle(rc, expect_status, "release")
         return rc
 
     def admit_and_compare(self, b, base, length, commit=True, expect_status=0):
         """echo_admit of row b against the oracle's admission (a host-side rejection
         must be the oracle's EINVAL, with nothing enqueued)."""
-        ret = abi.echo_admit(self.dims, self.layer.struct, self.batch.host_base.data_ptr(),
-                             self.batch.ctx.data_ptr(), self.B, int(b), int(base), int(length),
-                             int(commit), self.ws.ws, R.stream_handle())
-        rc = O.admit(self.orc, self.base, self.ctx, b, base, length, self.dims.max_ctx, commit)
+        ret = abi.echo_admit(self.dims, self.layer.struct, self.batch.struct, int(b), int(base),
+                             int(length), int(commit), self.ws.ws, R.stream_handle())
+        rc = O.admit(self.orc, self.base, self.ctx, b, base, length, self.dims.max_ctx, commit,
+                     pages=self.pages)
         if ret != abi.ECHO_OK:
             assert ret == rc == expect_status == O.EINVAL, ("admit", ret, rc, expect_status)
             return rc
@@ -341,7 +398,9 @@ class Rig:
         st = int(self.ws.status.item())
         assert st == rc == expect_status, (tag, "status", st, rc, expect_status)
         assert np.array_equal(self.batch.ctx.cpu().numpy(), self.ctx), (tag, "ctx_len")
-        assert np.array_equal(self.batch.host_base.cpu().numpy(), self.base), (tag, "host_base")
+        if self.pages is None:
+            assert np.array_equal(self.batch.host_base.cpu().numpy(), self.base), \
+                (tag, "host_base")
         g = self.layer.state()
         for name in ("h2g", "g2h", "prio", "free"):
             assert np.array_equal(g[name], getattr(self.orc, name)), (tag, name)

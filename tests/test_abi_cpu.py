@@ -133,10 +133,15 @@ def test_newer_entry_points_check_arguments_before_any_launch():
         assert fn(d, None, None, None, 0, 0) == abi.ECHO_EINVAL
         assert fn(d, layer, batch, ws, 7, 0) == abi.ECHO_EINVAL
     assert abi.echo_gather(d, None, batch, ws, 1 << 30, 0) == abi.ECHO_EINVAL
-    assert abi.echo_append(d, None, 1, 1, 1, 1, 1 << 30, ws, 1, 0) == abi.ECHO_EINVAL
-    assert abi.echo_release(d, None, 1, 1, 1, 1, 1, ws, 0) == abi.ECHO_EINVAL
-    assert abi.echo_release(d, layer, 1, 1, 1, None, 1, ws, 0) == abi.ECHO_EINVAL
-    assert abi.echo_admit(d, None, 1, 1, 1, 0, 0, 16, 1, ws, 0) == abi.ECHO_EINVAL
+    b1 = abi.echo_batch_t(1, 1 << 30, 1 << 30, None, 0)
+    assert abi.echo_append(d, None, b1, 1, 1 << 30, ws, 1, 0) == abi.ECHO_EINVAL
+    assert abi.echo_release(d, None, b1, 1, 1, ws, 0) == abi.ECHO_EINVAL
+    assert abi.echo_release(d, layer, b1, None, 1, ws, 0) == abi.ECHO_EINVAL
+    assert abi.echo_admit(d, None, b1, 0, 0, 16, 1, ws, 0) == abi.ECHO_EINVAL
+    # a page table needs a stride of at least one entry; without one, host_base is needed
+    for bad in (abi.echo_batch_t(1, None, 1 << 30, 1 << 30, 0),
+                abi.echo_batch_t(1, None, 1 << 30, None, 0)):
+        assert abi.echo_layer_step(d, layer, bad, ws, 0, 0) == abi.ECHO_EINVAL
     pws = abi.echo_prefill_ws_t()
     chunk = abi.echo_prefill_chunk_t(4, 0, 1000, 1 << 30, 1 << 30, None)
     for fn in (abi.echo_prefill_score, abi.echo_prefill_early, abi.echo_prefill_select):

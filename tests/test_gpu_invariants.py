@@ -35,8 +35,9 @@ def _say(msg):
     print(msg, flush=True)
 
 
-def numpy_counts(st, n_sel, sel_tok, sel_slot, base, ctx, check_sel=True):
-    """The invariants of echo_check_invariants, counted on state read back."""
+def numpy_counts(st, n_sel, sel_tok, sel_slot, host_ids, ctx, check_sel=True):
+    """The invariants of echo_check_invariants, counted on state read back;
+    host_ids(b, s) gives the host id of request b's token s."""
     h2g, g2h, prio, free = st["h2g"], st["g2h"], st["prio"], st["free"].astype(np.int64)
     n_host, n_gpu, t = h2g.size, g2h.size, st["t"]
     c = np.zeros(abi.ECHO_INV_WORDS, np.int64)
@@ -67,8 +68,9 @@ def numpy_counts(st, n_sel, sel_tok, sel_slot, base, ctx, check_sel=True):
             n = int(np.clip(n_sel[b], 0, sel_tok.shape[1]))
             for i in range(n):
                 s = int(sel_tok[b, i])
-                h = int(base[b]) + s
-                good = 0 <= s < ctx[b] and 0 <= h < n_host
+                good = 0 <= s < ctx[b]
+                h = int(host_ids(b, [s])[0]) if good else -1
+                good = good and 0 <= h < n_host
                 if good:
                     g = int(h2g[h])
                     good = 0 <= g < n_gpu and g == sel_slot[b, i] and prio[g] == t - 1
@@ -89,7 +91,7 @@ def _expected(rig):
     torch.cuda.current_stream().synchronize()
     out = rig.ws.read(rig.B)
     return numpy_counts(rig.layer.state(), out["n_sel"], out["sel_tok"], out["sel_slot"],
-                        rig.base, rig.ctx)
+                        rig.host_ids, rig.ctx)
 
 
 def test_clean_state_after_every_step_and_each_corruption_is_reported():

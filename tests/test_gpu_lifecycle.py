@@ -42,7 +42,7 @@ def _lossless(rig, out):
     rows = rig.gathered()
     for b in range(rig.B):
         n = int(out["n_sel"][b])
-        hs = int(rig.base[b]) + out["sel_tok"][b, :n]
+        hs = rig.host_ids(b, out["sel_tok"][b, :n])
         assert np.array_equal(rows[b], rig.orc_host[hs]), ("attention input", b)
 
 
