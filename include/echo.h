@@ -20,8 +20,12 @@
  *    frees or synchronizes; each call validates its arguments on the host, enqueues
  *    kernels on `stream` and returns.  Every call can be captured in a hipGraph.
  *  - Host-side return codes: ECHO_OK, or ECHO_EINVAL (bad argument or shape; nothing
- *    was enqueued), ECHO_EUNSUPPORTED (a shape this library has no kernel for), or
- *    ECHO_EHIP (a launch failed).
+ *    was enqueued), ECHO_EUNSUPPORTED (a shape this library has no kernel for, or
+ *    a launch whose workgroups wait on each other -- scoring with prefetch,
+ *    management -- and would not all fit on the compute units at once by the
+ *    runtime's occupancy query), or ECHO_EHIP (a launch failed).  Those waits also
+ *    give up after 1 s (ECHO_ETIMEOUT below), so work of another process holding
+ *    compute units for longer ends the step with an error, never a hang.
  *  - Errors found on the device (capacity, bad device-side lengths, a stuck wait)
  *    are written to `ws->status`: the first error wins and stays until
  *    echo_ws_reset.  Once it is set, every later kernel of every call is a no-op,
@@ -148,7 +152,15 @@ typedef struct {
 } echo_layer_meta_t;
 
 /* One layer's tensors.  k_index, gpu_kv, host_kv and q must be 16-byte aligned
- * (ECHO_EINVAL otherwise). */
+ * (ECHO_EINVAL otherwise).
+ *
+ * Between calls, a layer's whole cache-management state is in meta (five
+ * arrays), gpu_kv, theta, guard, ctl and stats; the workspace carries nothing
+ * from one step to the next, and the maps hold indices, not addresses.  The ECHO
+ * review ("Critical analysis / systemic flaws") notes that the full host copy of
+ * the cache is not a persistence mechanism: a byte copy of these buffers is one.
+ * Written back, at the same or other addresses and with any workspace, the
+ * following steps give bit-identical results. */
 typedef struct {
   echo_layer_meta_t meta;
   const uint8_t *k_index;  /* n_host*head_dim bytes: indexer K, OCP fp8 E4M3FN, in the

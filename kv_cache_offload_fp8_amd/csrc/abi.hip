@@ -36,14 +36,19 @@ int check_dims(const echo_dims_t *d) {
   return ECHO_OK;
 }
 
-// The management kernel keeps all of its workgroups (one per 4096 slots) resident
-// for its grid barrier: at most one per compute unit.
+// The management kernel keeps all of its workgroups (one per 4096 slots, plus the
+// copy workgroups) resident for its grid barrier, and the scoring kernel all of its
+// workgroups for the look-back and the copy queue: each grid must fit what the
+// compute units hold at once, by the runtime's occupancy query.
 int check_launch(const echo_dims_t *d) {
   const int64_t atiles = ((int64_t)d->n_gpu + kSlotTile - 1) / kSlotTile;
   int gs = 1, gc = 1;
   index_grid(*d, true, &gs, &gc);
   const int64_t copy_blocks = 2 * (int64_t)gc * kScoreWaves / 16;  // 16-wave workgroups
-  if (atiles + copy_blocks > device_cus()) return ECHO_EUNSUPPORTED;
+  if (atiles + copy_blocks > (int64_t)manage_resident_per_cu() * device_cus())
+    return ECHO_EUNSUPPORTED;
+  if ((int64_t)gs + gc > (int64_t)score_resident_per_cu() * device_cus())
+    return ECHO_EUNSUPPORTED;
   return ECHO_OK;
 }
 
@@ -322,7 +327,15 @@ int prefill_args(const echo_dims_t *dims, const echo_layer_t *layer,
   return ECHO_OK;
 }
 
+// The scoring launch's workgroups all resident (see check_launch).
+int check_score_launch(const StepArgs &a) {
+  const int64_t grid = (int64_t)a.score_blocks + a.copy_waves / kScoreWaves;
+  return grid > (int64_t)score_resident_per_cu() * device_cus() ? ECHO_EUNSUPPORTED : ECHO_OK;
+}
+
 int run_indexer(const StepArgs &a, int extra_roles, hipStream_t s) {
+  const int rc = check_score_launch(a);
+  if (rc != ECHO_OK) return rc;
   LAUNCH(launch_begin(a, BEGIN_REQ | BEGIN_Q | BEGIN_CLR_INDEX | BEGIN_CLR_TOPK | extra_roles, s));
   LAUNCH(launch_score(a, s));
   return ECHO_OK;
@@ -425,6 +438,8 @@ int echo_indexer_score(const echo_dims_t *dims, const echo_layer_t *layer,
   if (!layer_ok(layer, theta_mode == ECHO_THETA_EMA) || !batch_ok(*dims, batch) || !ws_ok(ws))
     return ECHO_EINVAL;
   const StepArgs a = make_args(*dims, layer, batch, *ws, theta_mode);
+  rc = check_score_launch(a);
+  if (rc != ECHO_OK) return rc;
   LAUNCH(launch_score(a, stream));
   return ECHO_OK;
 }
@@ -667,7 +682,7 @@ int echo_layer_step(const echo_dims_t *dims, const echo_layer_t *layer, const ec
   a.copy_handoff = 1;  // the prefetch copy runs on through top-k and management
   rc = run_indexer(a, BEGIN_CLR_MANAGE, stream);
   if (rc != ECHO_OK) return rc;
-  if (a.B > 0 && select_manage_blocks(a) <= device_cus()) {
+  if (a.B > 0 && select_manage_blocks(a) <= manage_resident_per_cu() * device_cus()) {
     // one launch: the prefetch copy runs on from selection into management
     LAUNCH(launch_select_manage(a, stream));
   } else {

@@ -909,6 +909,39 @@ int device_cus() {
   return cache[dev];
 }
 
+int score_resident_per_cu() {
+  static int cache[64] = {0};  // per device: 0 not asked yet, -1 none fits, else the count
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cache[dev] == 0) {
+    const void *fns[] = {
+        reinterpret_cast<const void *>(&k_score<1, false, false>),
+        reinterpret_cast<const void *>(&k_score<2, false, false>),
+        reinterpret_cast<const void *>(&k_score<3, false, false>),
+        reinterpret_cast<const void *>(&k_score<4, false, false>),
+        reinterpret_cast<const void *>(&k_score<1, true, false>),
+        reinterpret_cast<const void *>(&k_score<2, true, false>),
+        reinterpret_cast<const void *>(&k_score<3, true, false>),
+        reinterpret_cast<const void *>(&k_score<4, true, false>),
+        reinterpret_cast<const void *>(&k_score<1, false, true>),
+        reinterpret_cast<const void *>(&k_score<2, false, true>),
+        reinterpret_cast<const void *>(&k_score<3, false, true>),
+        reinterpret_cast<const void *>(&k_score<4, false, true>),
+        reinterpret_cast<const void *>(&k_score<1, true, true>),
+        reinterpret_cast<const void *>(&k_score<2, true, true>),
+        reinterpret_cast<const void *>(&k_score<3, true, true>),
+        reinterpret_cast<const void *>(&k_score<4, true, true>)};
+    int m = 1 << 30;
+    for (const void *f : fns) {
+      int n = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, 512, 0) != hipSuccess) n = 0;
+      m = n < m ? n : m;
+    }
+    cache[dev] = m > 0 ? m : -1;
+  }
+  return cache[dev] > 0 ? cache[dev] : 0;
+}
+
 void index_grid(const echo_dims_t &d, bool with_copy, int *score_blocks, int *copy_blocks) {
   const int cus = device_cus();
   int gc = cus / 8 < kCopyBlocks ? cus / 8 : kCopyBlocks;

@@ -343,6 +343,27 @@ __global__ __launch_bounds__(kSelThreads) void k_select_manage(StepArgs a) {
   manage_block<RECALL, ADVANCE>(a, mb, 0);
 }
 
+int manage_resident_per_cu() {
+  static int cache[64] = {0};  // per device: 0 not asked yet, -1 none fits, else the count
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cache[dev] == 0) {
+    const void *fns[] = {reinterpret_cast<const void *>(&k_select_manage<true, true>),
+                         reinterpret_cast<const void *>(&k_manage<true, true>),
+                         reinterpret_cast<const void *>(&k_manage<true, false>),
+                         reinterpret_cast<const void *>(&k_manage<false, true>),
+                         reinterpret_cast<const void *>(&k_manage<false, false>)};
+    int m = 1 << 30;
+    for (const void *f : fns) {
+      int n = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, kSelThreads, 0) != hipSuccess) n = 0;
+      m = n < m ? n : m;
+    }
+    cache[dev] = m > 0 ? m : -1;
+  }
+  return cache[dev] > 0 ? cache[dev] : 0;
+}
+
 // Workgroups of the fused launch: selection + management + copy.
 int select_manage_blocks(const StepArgs &a) {
   return a.B + a.sc.atiles + 2 * a.copy_waves / (kSelThreads / kWave);

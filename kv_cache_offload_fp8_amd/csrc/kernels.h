@@ -120,6 +120,13 @@ enum {
 void index_grid(const echo_dims_t &d, bool with_copy, int *score_blocks, int *copy_blocks);
 // Compute units of the current device (cached per device).
 int device_cus();
+// Workgroups of the launches whose workgroups wait on each other (the scoring kernel's
+// look-back and copy queue; the grid barriers of selection + management and of
+// management) that one compute unit holds at once, the least over their variants, from
+// the runtime's occupancy query (cached per device; 0 if one does not fit).  Such a
+// launch is made only when its grid fits that many per compute unit.
+int score_resident_per_cu();
+int manage_resident_per_cu();
 
 hipError_t launch_begin(const StepArgs &a, int roles, hipStream_t s);
 hipError_t launch_score(const StepArgs &a, hipStream_t s);
