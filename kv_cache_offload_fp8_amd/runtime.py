@@ -258,6 +258,24 @@ class Layer:
     def init(self):
         check(abi.echo_meta_init(self.dims, self.struct, stream_handle()), "echo_meta_init")
 
+    # Between calls the layer's whole cache-management state is in these buffers (the
+    # workspace carries nothing from one step to the next): a copy of their bytes is a
+    # checkpoint, and written back -- here or into another Layer of the same dims -- the
+    # following steps give bit-identical results.
+    STATE = ("h2g", "g2h", "prio", "idxbuf", "free", "gpu_kv", "theta", "guard", "ctl",
+             "stats")
+
+    def snapshot(self) -> dict:
+        """Device copies of the layer's state buffers (stream-ordered)."""
+        return {n: getattr(self, n).clone() for n in self.STATE}
+
+    def restore(self, snap: dict) -> None:
+        """Write a snapshot back (stream-ordered); shapes must match."""
+        for n in self.STATE:
+            dst = getattr(self, n)
+            assert snap[n].shape == dst.shape and snap[n].dtype == dst.dtype, n
+            dst.copy_(snap[n])
+
     def state(self) -> dict:
         torch.cuda.current_stream().synchronize()
         return dict(h2g=self.h2g.cpu().numpy(), g2h=self.g2h.cpu().numpy(),
