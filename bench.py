@@ -143,10 +143,13 @@ def stored_step_kernel(total_tok):
                       "bench.py --headline-only)"}
 
 
-def replay_median_ms(graph, n):
+def replay_median_ms(graph, n, warm=5):
     """Median duration of n replays of `graph`, each timed with events on the current
-    stream after the previous one has finished."""
+    stream after the previous one has finished, after `warm` untimed replays (the first
+    replays after idle or link-bound work measured 3-8% slower than the ones after them)."""
     import torch
+    for _ in range(warm):
+        graph.replay()
     times = []
     for _ in range(n):
         torch.cuda.synchronize()
@@ -651,7 +654,8 @@ def main():
         "roofline": {"kernel": "lightning-indexer scoring kernel k_score<4,false> (prefetch "
                                f"off): a graph of {nso} echo_indexer_prefetch calls less a "
                                f"graph of their {nso} prologues, each the median of {nrep} "
-                               "replays timed one at a time with events on the replay stream",
+                               "replays timed one at a time with events on the replay stream, "
+                               "after 5 untimed replays",
                      "bound": "hbm", "achieved": round(ks_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(ks_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "bytes_per_launch": idx_bytes,
