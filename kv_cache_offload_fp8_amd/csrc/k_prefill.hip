@@ -409,6 +409,7 @@ __global__ __launch_bounds__(kSelThreads) void k_pf_exact(StepArgs a, PrefillArg
   __shared__ uint64_t shu[kSelThreads / kWave];
   __shared__ uint64_t s_list[kPfBoundaryCap];
   __shared__ int s_n;
+  __shared__ SelectLds s_sel_lds;
   if (block_failed(p.status)) return;
   const int i = blockIdx.x, tid = threadIdx.x, lane = lane_id();
   const float *row = p.scores + (int64_t)i * p.N;
@@ -436,10 +437,12 @@ __global__ __launch_bounds__(kSelThreads) void k_pf_exact(StepArgs a, PrefillArg
     const int n = s_n;
     in_lds = n <= kPfBoundaryCap;
     if (in_lds)
-      block_select_by([&](int j) { return s_list[j]; }, n, a.K - above, &P, &pos);
+      block_select_by<kSelThreads>([&](int j) { return s_list[j]; }, n, a.K - above, &P, &pos,
+                                   s_sel_lds);
     else
-      block_select_by([=](int s) { return ((uint64_t)topk_key(row[s]) << 32) | (uint32_t)s; },
-                      p.N, a.K, &P, &pos);
+      block_select_by<kSelThreads>(
+          [=](int s) { return ((uint64_t)topk_key(row[s]) << 32) | (uint32_t)s; }, p.N, a.K, &P,
+          &pos, s_sel_lds);
   }
   int32_t *out = p.sel + (int64_t)i * a.K;
   int written = 0;

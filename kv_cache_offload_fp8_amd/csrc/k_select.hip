@@ -14,7 +14,8 @@ __global__ __launch_bounds__(kSelThreads) void k_topk(StepArgs a) {
                 &a.sc.misc[M_TOPK_DONE], a.B);
     return;
   }
-  topk_block<PROTECT>(a, blockIdx.x, st0);
+  __shared__ TopkLds L;
+  topk_block<PROTECT>(a, blockIdx.x, st0, L);
 }
 
 __global__ __launch_bounds__(kSelThreads) void k_protect(StepArgs a) {

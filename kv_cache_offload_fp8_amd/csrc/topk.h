@@ -30,21 +30,33 @@ namespace echo {
 
 constexpr int kGuardLds = 8192;  // guard candidates the LDS path holds
 
+// Shared memory of topk_block (and of the helpers it calls).
+struct TopkLds {
+  uint32_t key[kGuardLds];  // guard keys, or the full path's histogram
+  int32_t idx[kGuardLds];
+  int32_t sel[4096];
+  int sh[kMaxSelWaves + 1];
+  uint64_t shu[kMaxSelWaves];
+  int bin, below, cnt;
+  uint32_t h256[256];  // lds_kth_key
+  int s2[2];
+  SelectLds sel_lds;
+};
+
 // k-th smallest of `c` keys in LDS (1 <= need <= c): the key kb and how many keys
-// equal to kb belong to the selection.
+// equal to kb belong to the selection.  h256, s2: 256 + 2 words of shared memory.
+template <int NT>
 __device__ static void lds_kth_key(const uint32_t *keys, int c, int need, uint32_t *kb_out,
-                                   int *rem_out) {
-  __shared__ uint32_t h256[256];
-  __shared__ int s2[2];
+                                   int *rem_out, uint32_t *h256, int *s2) {
   const int tid = threadIdx.x;
   uint32_t prefix = 0;
   int rem = need;
 #pragma unroll
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    for (int i = tid; i < 256; i += kSelThreads) h256[i] = 0;
+    for (int i = tid; i < 256; i += NT) h256[i] = 0;
     __syncthreads();
-    for (int i = tid; i < c; i += kSelThreads) {
+    for (int i = tid; i < c; i += NT) {
       const uint32_t k = keys[i];
       const bool match = pass == 0 ? true : ((k >> (shift + 8)) == prefix);
       if (match) atomicAdd(&h256[(k >> shift) & 255u], 1u);
@@ -82,12 +94,13 @@ __device__ static void lds_kth_key(const uint32_t *keys, int c, int need, uint32
 
 // Protect the selected tokens of request b (held in LDS) and list its misses in
 // token order.  Returns the number of misses (in every thread).
+template <int NT = kSelThreads>
 __device__ static int protect_request(const StepArgs &a, int b, const int32_t *s_sel, int n,
                                       int *sh) {
   const int t = a.ctl[ECHO_CTL_STEP];
   const int base = a.sc.req[b].base;
   int off = 0;
-  for (int i0 = 0; i0 < n; i0 += kSelThreads) {
+  for (int i0 = 0; i0 < n; i0 += NT) {
     const int i = i0 + threadIdx.x;
     const bool valid = i < n && s_sel[i] >= 0;
     int s = 0, g = -1;
@@ -101,7 +114,7 @@ __device__ static int protect_request(const StepArgs &a, int b, const int32_t *s
     }
     const int miss = (valid && g < 0) ? 1 : 0;
     int tot;
-    const int pos = off + block_excl_scan<kSelThreads>(miss, sh, &tot);
+    const int pos = off + block_excl_scan<NT>(miss, sh, &tot);
     if (miss) {
       a.ws.miss_tok[(int64_t)b * a.K + pos] = s;
       a.sc.miss_i[(int64_t)b * a.K + pos] = i;
@@ -120,13 +133,14 @@ __device__ static int protect_request(const StepArgs &a, int b, const int32_t *s
 // prefetch list pf_tok (final when the scoring kernel ended) and the selection s_sel
 // (in LDS) are both in ascending token order; each prefetched token is looked up in
 // the selection by binary search.
+template <int NT>
 __device__ static void add_step_stats(const StepArgs &a, int b, const int32_t *s_sel, int nsel,
                                       int nmiss, int *sh) {
   const int npf = a.ws.n_pf[b];
   const int ncand = a.ws.n_cand[b];
   const int32_t *pf = a.ws.pf_tok + (int64_t)b * a.K;
   int found = 0;
-  for (int i = threadIdx.x; i < npf; i += kSelThreads) {
+  for (int i = threadIdx.x; i < npf; i += NT) {
     const int s = pf[i];
     int lo = 0, hi = nsel;  // first position whose token is >= s
     while (lo < hi) {
@@ -137,7 +151,7 @@ __device__ static void add_step_stats(const StepArgs &a, int b, const int32_t *s
     found += (lo < nsel && s_sel[lo] == s) ? 1 : 0;
   }
   int tot;
-  block_excl_scan<kSelThreads>(found, sh, &tot);
+  block_excl_scan<NT>(found, sh, &tot);
   if (threadIdx.x == 0) {
     unsigned long long *st = (unsigned long long *)a.stats;
     atomicAdd(&st[ECHO_STAT_SELECTED], (unsigned long long)nsel);
@@ -149,16 +163,15 @@ __device__ static void add_step_stats(const StepArgs &a, int b, const int32_t *s
 }
 
 // Top-k of request b, its threshold / guard updates and (PROTECT) the protection
-// of its selection, by one 1024-thread workgroup; at the end the workgroup adds
+// of its selection, by one workgroup of NT threads; at the end the workgroup adds
 // one to misc[M_TOPK_DONE].  st0: the status word, read at the kernel's start.
-template <bool PROTECT>
-__device__ static void topk_block(const StepArgs &a, int b, int32_t st0) {
-  __shared__ uint32_t s_key[kGuardLds];  // guard keys, or the full path's histogram
-  __shared__ int32_t s_idx[kGuardLds];
-  __shared__ int32_t s_sel[4096];
-  __shared__ int sh[kSelThreads / kWave + 1];
-  __shared__ uint64_t shu[kSelThreads / kWave];
-  __shared__ int s_bin, s_below, s_cnt;
+template <bool PROTECT, int NT = kSelThreads>
+__device__ static void topk_block(const StepArgs &a, int b, int32_t st0, TopkLds &L) {
+  uint32_t *const s_key = L.key;
+  int32_t *const s_idx = L.idx;
+  int32_t *const s_sel = L.sel;
+  int *const sh = L.sh;
+  uint64_t *const shu = L.shu;
   const int tid = threadIdx.x, lane = lane_id(), wid = tid / kWave;
   const ReqInfo r = a.sc.req[b];
   if (st0 != 0) return;
@@ -170,17 +183,17 @@ __device__ static void topk_block(const StepArgs &a, int b, int32_t st0) {
   float kth;
   if (ctx <= K) {
     uint64_t mx = 0;
-    for (int i = tid; i < ctx; i += kSelThreads) {
+    for (int i = tid; i < ctx; i += NT) {
       s_sel[i] = i;
       sel_out[i] = i;
       const uint64_t k = topk_key(sc[i]);
       mx = k > mx ? k : mx;
     }
-    mx = block_max_u64<kSelThreads>(mx, shu);
+    mx = block_max_u64<NT>(mx, shu);
     kth = ctx > 0 ? score_of_key((uint32_t)mx) : __builtin_nanf("");
   } else {
     // ---- guard path availability: per-item candidate counts of this request
-    const int per = (r.ntiles + kSelThreads - 1) / kSelThreads;
+    const int per = (r.ntiles + NT - 1) / NT;
     const int t0 = min(r.ntiles, tid * per), t1 = min(r.ntiles, t0 + per);
     int mine = 0, ovf = 0;
     if (r.use_guard) {
@@ -191,7 +204,7 @@ __device__ static void topk_block(const StepArgs &a, int b, int32_t st0) {
       }
     }
     int tot;
-    int p = block_excl_scan<kSelThreads>(mine, sh, &tot);
+    int p = block_excl_scan<NT>(mine, sh, &tot);
     const bool any_ovf = __syncthreads_or(ovf) != 0;
     if (r.use_guard && !any_ovf && tot >= K && tot <= kGuardLds) {
       for (int ti = t0; ti < t1; ++ti) {
@@ -205,16 +218,16 @@ __device__ static void topk_block(const StepArgs &a, int b, int32_t st0) {
       __syncthreads();
       uint32_t kb;
       int rem;
-      lds_kth_key(s_key, tot, K, &kb, &rem);
+      lds_kth_key<NT>(s_key, tot, K, &kb, &rem, L.h256, L.s2);
       // ordered write-out: keys below kb, then the first `rem` keys equal to kb
       int c_lt = 0, c_eq = 0;
-      for (int i0 = 0; i0 < tot; i0 += kSelThreads) {
+      for (int i0 = 0; i0 < tot; i0 += NT) {
         const int i = i0 + tid;
         const bool v = i < tot;
         const uint32_t k = v ? s_key[i] : 0xFFFFFFFFu;
         const bool lt = v && k < kb, eq = v && k == kb;
         int rt;
-        const int ex = block_excl_scan<kSelThreads>((lt ? 1 << 16 : 0) | (eq ? 1 : 0), sh, &rt);
+        const int ex = block_excl_scan<NT>((lt ? 1 << 16 : 0) | (eq ? 1 : 0), sh, &rt);
         const int eq_before = c_eq + (ex & 0xFFFF);
         if (lt || (eq && eq_before < rem)) {
           const int pos = c_lt + (ex >> 16) + min(eq_before, rem);
@@ -232,26 +245,26 @@ __device__ static void topk_block(const StepArgs &a, int b, int32_t st0) {
       uint32_t *ckey = a.sc.tcand_key + (int64_t)b * a.max_ctx;
       int32_t *cidx = a.sc.tcand_idx + (int64_t)b * a.max_ctx;
       uint64_t mn = ~0ull, mx = 0;
-      for (int s = tid; s < ctx; s += kSelThreads) {
+      for (int s = tid; s < ctx; s += NT) {
         const uint64_t k = topk_key(sc[s]);
         mn = k < mn ? k : mn;
         mx = k > mx ? k : mx;
       }
-      mn = block_min_u64<kSelThreads>(mn, shu);
-      mx = block_max_u64<kSelThreads>(mx, shu);
+      mn = block_min_u64<NT>(mn, shu);
+      mx = block_max_u64<NT>(mx, shu);
       const uint32_t kmin = (uint32_t)mn;
       const int shift = bin_shift(kmin, (uint32_t)mx);
       uint32_t *hist = s_key;
-      for (int i = tid; i < kBins; i += kSelThreads) hist[i] = 0;
-      if (tid == 0) s_cnt = 0;
+      for (int i = tid; i < kBins; i += NT) hist[i] = 0;
+      if (tid == 0) L.cnt = 0;
       __syncthreads();
-      for (int s = tid; s < ctx; s += kSelThreads)
+      for (int s = tid; s < ctx; s += NT)
         atomicAdd(&hist[min((topk_key(sc[s]) - kmin) >> shift, (uint32_t)(kBins - 1))], 1u);
       __syncthreads();
-      find_boundary<false>(hist, K, &s_bin, &s_below, sh);
-      const uint32_t bstar = (uint32_t)s_bin;
-      const int below = s_below;
-      for (int s0 = wid * kWave; s0 < ctx; s0 += kSelThreads) {
+      find_boundary<false, NT>(hist, K, &L.bin, &L.below, sh);
+      const uint32_t bstar = (uint32_t)L.bin;
+      const int below = L.below;
+      for (int s0 = wid * kWave; s0 < ctx; s0 += NT) {
         const int s = s0 + lane;
         const bool valid = s < ctx;
         const uint32_t key = valid ? topk_key(sc[s]) : 0u;
@@ -265,7 +278,7 @@ __device__ static void topk_block(const StepArgs &a, int b, int32_t st0) {
         const uint64_t cm = __ballot(cand);
         if (cm) {
           int basepos = 0;
-          if (lane == 0) basepos = atomicAdd(&s_cnt, __popcll(cm));
+          if (lane == 0) basepos = atomicAdd(&L.cnt, __popcll(cm));
           basepos = __shfl(basepos, 0);
           if (cand) {
             const int pos = basepos + __popcll(cm & lanemask_lt());
@@ -276,14 +289,14 @@ __device__ static void topk_block(const StepArgs &a, int b, int32_t st0) {
       }
       __threadfence_block();
       __syncthreads();
-      const int c = s_cnt;
+      const int c = L.cnt;
       uint64_t P;
       int pos;
-      block_select(ckey, cidx, c, K - below, &P, &pos);
+      block_select<NT>(ckey, cidx, c, K - below, &P, &pos, L.sel_lds);
       __threadfence_block();
       __syncthreads();
       uint64_t kmax_sel = 0;
-      for (int i = tid; i < c; i += kSelThreads) {
+      for (int i = tid; i < c; i += NT) {
         const uint32_t k = ckey[i];
         const int32_t s = cidx[i];
         if (composite_selected(k, s, P, pos)) {
@@ -291,19 +304,19 @@ __device__ static void topk_block(const StepArgs &a, int b, int32_t st0) {
           kmax_sel = k > kmax_sel ? k : kmax_sel;
         }
       }
-      kmax_sel = block_max_u64<kSelThreads>(kmax_sel, shu);
+      kmax_sel = block_max_u64<NT>(kmax_sel, shu);
       kth = score_of_key((uint32_t)kmax_sel);
       __threadfence_block();
       __syncthreads();
       // ordered extraction of the selection bitmap
       const int nwords = (ctx + 31) / 32;
-      const int wper = (nwords + kSelThreads - 1) / kSelThreads;
+      const int wper = (nwords + NT - 1) / NT;
       const int w0 = tid * wper, w1 = min(nwords, w0 + wper);
       int cnt = 0;
       for (int wi = w0; wi < w1; ++wi)
         cnt += __popc(__hip_atomic_load(&bits[wi], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
       int rt;
-      int q = block_excl_scan<kSelThreads>(cnt, sh, &rt);
+      int q = block_excl_scan<NT>(cnt, sh, &rt);
       for (int wi = w0; wi < w1; ++wi) {
         uint32_t x = __hip_atomic_load(&bits[wi], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         while (x) {
@@ -333,8 +346,8 @@ __device__ static void topk_block(const StepArgs &a, int b, int32_t st0) {
   }
   if (PROTECT) {
     __syncthreads();
-    const int nmiss = protect_request(a, b, s_sel, nsel, sh);
-    if (a.stats) add_step_stats(a, b, s_sel, nsel, nmiss, sh);
+    const int nmiss = protect_request<NT>(a, b, s_sel, nsel, sh);
+    if (a.stats) add_step_stats<NT>(a, b, s_sel, nsel, nmiss, sh);
   }
   // done: the fence makes this workgroup's selection, priorities and miss list
   // visible before the count (management waits for it in the fused kernel)
