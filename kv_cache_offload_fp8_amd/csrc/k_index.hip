@@ -47,7 +47,9 @@
 // wave's next item: the item's candidate count is published at that item's first
 // chunk and its rank resolved two chunks later, when the items before it have
 // published theirs, so the look-back rarely waits and its lookups never drain
-// the K stream.  Installed rows are published by rank as
+// the K stream.  Only a job's first item is resolved at once: the items before it
+// are the other waves' first items, finished at about the same time, and its rows
+// then reach the copy about 7 us sooner (1.2% on the capacity layer step).  Installed rows are published by rank as
 // self-validating 64-bit entries; the copy workgroups read them from mapped host
 // memory into the GPU pool while scoring continues -- the MI355X form of the
 // pages' dedicated prefetch role inside the indexer pipeline.  The copy runs on
@@ -793,6 +795,14 @@ __device__ static void score_job(const StepArgs &a, const ReqInfo &r, int b, int
         p_g[c] = gq[c];
       }
       have_prev = true;
+      if (i == k && ni < r.ntiles) {
+        // the job's first item: its rank now, so that its rows reach the copy
+        // waves early (the items before it are the other waves' first items,
+        // finished at about the same time)
+        publish_prev();
+        while (qn > 0) install_oldest();
+        have_prev = false;
+      }
     }
     if (++nbuf == kDeferItems) {
       flush();
