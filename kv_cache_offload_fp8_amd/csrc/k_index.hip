@@ -49,10 +49,11 @@
 // published theirs, so the look-back rarely waits and its lookups never drain
 // the K stream.  Only a job's first item is resolved at once: the items before it
 // are the other waves' first items, finished at about the same time, and its rows
-// then reach the copy about 7 us sooner (1.2% on the capacity layer step).  Installed rows are published by rank as
-// self-validating 64-bit entries; the copy workgroups read them from mapped host
-// memory into the GPU pool while scoring continues -- the MI355X form of the
-// pages' dedicated prefetch role inside the indexer pipeline.  The copy runs on
+// then reach the copy about 7 us sooner (1.2% on the capacity layer step).
+// Installed rows are published by rank as self-validating 64-bit entries; the
+// copy workgroups read them from mapped host memory into the GPU pool while
+// scoring continues -- the MI355X form of the pages' dedicated prefetch role
+// inside the indexer pipeline.  The copy runs on
 // workgroups of its own because host reads issued from a compute unit hold up
 // that unit's HBM stream (measured: scoring slowed from about 100 us to 190 us
 // when each workgroup also read its rows from the host).  Scoring waves also
