@@ -74,12 +74,9 @@ __global__ __launch_bounds__(kReleaseThreads) void k_release_free(StepArgs a,
   }
 }
 
-// After the slots are back: thresholds, empty rows (with `commit`: the batch
-// row is shared by the layers and is emptied with the last), and the ascending free list
-// (idxbuf[0 .. nfree)) rebuilt by a block scan over the free flags.
-__global__ __launch_bounds__(kListThreads) void k_release_finish(StepArgs a, const int32_t *mask,
-                                                                 int32_t *ctx_io, int commit) {
-  __shared__ int sh[kListThreads / kWave + 1];
+// After the slots are back: thresholds and empty rows (with `commit`: the batch
+// row is shared by the layers and is emptied with the last).
+__global__ void k_release_finish(StepArgs a, const int32_t *mask, int32_t *ctx_io, int commit) {
   if (failed(a.ws.status)) return;  // also set by k_release_free's range check
   const int tid = threadIdx.x;
   if (tid < a.B && mask[tid]) {
@@ -87,7 +84,54 @@ __global__ __launch_bounds__(kListThreads) void k_release_finish(StepArgs a, con
     if (a.guard) a.guard[tid] = __builtin_huge_valf();
     if (commit) ctx_io[tid] = 0;
   }
-  rebuild_free_list(a, sh);
+}
+
+// The ascending free list (idxbuf[0 .. nfree)) rebuilt from the free flags, because
+// the next step's prefetch hands out idxbuf[off + rank]: one 1024-thread workgroup
+// per slot tile of kSlotTile slots (4 per thread).  k_free_count stores each tile's
+// free count; k_free_write sums the counts of the tiles before its own, ranks its
+// free slots with a block scan and writes them; the last tile writes nfree.  (One
+// workgroup scanning all 110,000 slots took about 41 us; two launches of 27 take a
+// few.)
+constexpr int kFreeThreads = 1024;
+constexpr int kFreeSpt = kSlotTile / kFreeThreads;
+
+__global__ __launch_bounds__(kFreeThreads) void k_free_count(StepArgs a) {
+  __shared__ int sh[kFreeThreads / kWave + 1];
+  if (failed(a.ws.status)) return;
+  const int64_t g0 = (int64_t)blockIdx.x * kSlotTile + (int64_t)threadIdx.x * kFreeSpt;
+  int n = 0;
+#pragma unroll
+  for (int u = 0; u < kFreeSpt; ++u)
+    if (g0 + u < a.n_gpu && a.freef[g0 + u]) ++n;
+  int tot;
+  block_excl_scan<kFreeThreads>(n, sh, &tot);
+  if (threadIdx.x == 0) ((int32_t *)a.sc.astate)[blockIdx.x] = tot;
+}
+
+__global__ __launch_bounds__(kFreeThreads) void k_free_write(StepArgs a) {
+  __shared__ int sh[kFreeThreads / kWave + 1];
+  if (failed(a.ws.status)) return;
+  const int tid = threadIdx.x, blk = blockIdx.x;
+  const int32_t *cnt = (const int32_t *)a.sc.astate;
+  int before = 0;  // free slots in the tiles before this one
+  for (int i = tid; i < blk; i += kFreeThreads) before += cnt[i];
+  int total_before;
+  block_excl_scan<kFreeThreads>(before, sh, &total_before);
+  const int64_t g0 = (int64_t)blk * kSlotTile + (int64_t)tid * kFreeSpt;
+  bool fr[kFreeSpt];
+  int n = 0;
+#pragma unroll
+  for (int u = 0; u < kFreeSpt; ++u) {
+    fr[u] = g0 + u < a.n_gpu && a.freef[g0 + u] != 0;
+    n += fr[u] ? 1 : 0;
+  }
+  int tot;
+  int r = total_before + block_excl_scan<kFreeThreads>(n, sh, &tot);
+#pragma unroll
+  for (int u = 0; u < kFreeSpt; ++u)
+    if (fr[u]) a.idxbuf[r++] = (int32_t)(g0 + u);
+  if (blk == (int)gridDim.x - 1 && tid == 0) a.ctl[ECHO_CTL_NFREE] = total_before + tot;
 }
 
 hipError_t launch_release(const StepArgs &a, const int32_t *mask, int32_t *ctx_io, int commit,
@@ -95,8 +139,9 @@ hipError_t launch_release(const StepArgs &a, const int32_t *mask, int32_t *ctx_i
   hipLaunchKernelGGL(k_release_check, dim3(kCheckGrid), dim3(kReleaseThreads), 0, s, a, mask);
   hipLaunchKernelGGL(k_release_free, dim3(kReleaseBlocksX, a.B), dim3(kReleaseThreads), 0, s, a,
                      mask);
-  hipLaunchKernelGGL(k_release_finish, dim3(1), dim3(kListThreads), 0, s, a, mask, ctx_io,
-                     commit);
+  hipLaunchKernelGGL(k_release_finish, dim3(1), dim3(kMaxBatch), 0, s, a, mask, ctx_io, commit);
+  hipLaunchKernelGGL(k_free_count, dim3(a.sc.atiles), dim3(kFreeThreads), 0, s, a);
+  hipLaunchKernelGGL(k_free_write, dim3(a.sc.atiles), dim3(kFreeThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -56,31 +56,8 @@ __device__ inline bool page_in_pool(const StepArgs &a, int32_t p) {
   return p >= 0 && 16LL * p + 16 <= a.n_host;
 }
 
-// The ascending free list (idxbuf[0 .. nfree)) rebuilt from the free flags by one
-// workgroup of kListThreads threads (16 flags per thread per round, block scan).
-// `sh` needs kListThreads / 64 + 1 ints of shared memory.
+// Threads of the one-workgroup admission kernels.
 constexpr int kListThreads = 1024;
-constexpr int kListSlots = 16;
-__device__ inline void rebuild_free_list(const StepArgs &a, int *sh) {
-  const int tid = threadIdx.x;
-  int off = 0;
-  for (int64_t g0 = 0; g0 < a.n_gpu; g0 += (int64_t)kListThreads * kListSlots) {
-    const int64_t gs = g0 + (int64_t)tid * kListSlots;
-    uint32_t bits = 0;  // bit i: slot gs + i is free
-#pragma unroll
-    for (int i = 0; i < kListSlots; ++i)
-      if (gs + i < a.n_gpu && a.freef[gs + i]) bits |= 1u << i;
-    int total;
-    int r = off + block_excl_scan<kListThreads>(__popc(bits), sh, &total);
-    while (bits) {
-      const int i = __ffs(bits) - 1;
-      a.idxbuf[r++] = (int32_t)(gs + i);
-      bits &= bits - 1;
-    }
-    off += total;
-  }
-  if (tid == 0) a.ctl[ECHO_CTL_NFREE] = off;
-}
 
 // Workgroup roles by XCD.  MI355X deals consecutive workgroup ids to its eight XCDs
 // in turn.  When the grid has room, the nc copy workgroups take ids 0, 8, 16, ...,
