@@ -996,8 +996,8 @@ def cpu_baseline(wl, ctx, base, lay0, rows0, args, dims, threads=0):
     the first `--cpu-sample-requests` requests, `--cpu-sample-steps` decode steps in
     EMA mode (its own scores), on every host thread (threads=0) or on `threads`.
     Reported as layer-steps/s, scaled by the share of the layer-step's scored tokens
-    the sample covers.  One thread takes a smaller sample (4 requests, 2 steps) so
-    that it stays near 10 s."""
+    the sample covers.  One thread takes a smaller sample (8 requests, 6 steps: about
+    10 s of CPU time)."""
     import torch
 
     from oracle import oracle as O
@@ -1006,7 +1006,7 @@ def cpu_baseline(wl, ctx, base, lay0, rows0, args, dims, threads=0):
     nb = max(1, min(args.cpu_sample_requests, ctx.size))
     steps = max(1, min(args.cpu_sample_steps, lay0.q.shape[0]))
     if threads == 1:
-        nb, steps = min(nb, 4), min(steps, 2)
+        nb, steps = min(nb, 8), min(steps, 6)
     sctx = ctx[:nb].astype(np.int32)
     sbase = G.host_layout(sctx)
     n = int(sctx.sum())
