@@ -69,6 +69,8 @@ def parse():
     p.add_argument("--headline-only", action="store_true",
                    help="only the timed decode steps of the workload (for kernel traces of the "
                         "step as it runs)")
+    p.add_argument("--no-paged", action="store_true",
+                   help="skip the decode step with page tables")
     p.add_argument("--no-ablation", action="store_true",
                    help="skip the threshold-mode ablation and the prefetch-cap sweep")
     p.add_argument("--no-other-workloads", action="store_true",
@@ -219,6 +221,25 @@ class Decode:
         wl = self.wl
         return R.make_dims(wl.heads, wl.head_dim, wl.top_k, wl.n_host, wl.n_gpu, self.B,
                            int(self.ctx.max()) + 1, wl.latent, wl.alpha, cap_div, self.q_ring)
+
+    def paged_batch(self, seed):
+        """The same requests on 16-id host pages scattered over the whole pool: every page
+        the contiguous layout uses is replaced by a page drawn without replacement from a
+        seeded permutation of all the pool's pages.  The data stay where they are (every
+        token's K and latent are i.i.d. draws, so the scores keep their distribution); only
+        the addressing of every kernel changes."""
+        from kv_cache_offload_fp8_amd import runtime as R
+        npages = self.wl.n_host // 16
+        span = (self.ctx.astype(np.int64) + 15) // 16
+        stride = int(span.max())
+        perm = np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(0x9A6E,))) \
+            .permutation(npages).astype(np.int32)
+        pages = np.full((self.B, stride), -1, np.int32)
+        off = 0
+        for b in range(self.B):
+            pages[b, : span[b]] = perm[off: off + span[b]]
+            off += int(span[b])
+        return R.Batch(None, self.ctx, self.dev, pages=pages)
 
     def reinit(self):
         import torch
@@ -616,6 +637,23 @@ def main():
                                                    r["us_per_layer_step"]))
             log(f"[bench] {wl.name}, cap divisor {cd}: {r['layer_steps_per_s']:.1f} "
                 f"layer-steps/s, {sweep[str(cd)]}")
+    # -------------------------------- the same decode step with page tables
+    paged = None
+    if not args.no_paged:
+        contiguous = D.batch
+        D.batch = D.paged_batch(args.seed)
+        r = D.run(mode, args.steps, args.warmup, cs)
+        D.batch = contiguous
+        paged = dict(layer_steps_per_s=round(r["layer_steps_per_s"], 2),
+                     us_per_layer_step=round(r["us_per_layer_step"], 2),
+                     vs_contiguous=round(r["layer_steps_per_s"] / layer_steps_per_s, 4),
+                     **totals_summary(r["stats"], args.steps, row, link_peak,
+                                      r["us_per_layer_step"]),
+                     how="every request's 16-id pages scattered over the whole host pool "
+                         "through a page table (echo_batch_t.page_table); the same data, "
+                         "steps and timing as the headline")
+        log(f"[bench] {wl.name} with page tables: {r['layer_steps_per_s']:.1f} layer-steps/s "
+            f"({paged['vs_contiguous']:.3f} of contiguous)")
     D.close()
     del D, layers, ws, batch
     torch.cuda.synchronize()
@@ -707,6 +745,7 @@ def main():
                              "eager, events on the launch stream"},
         "threshold_ablation": ablation,
         "prefetch_cap_sweep": sweep,
+        "paged_step": paged,
         "other_workloads": others,
         "prefill": prefill,
         "hit_rate": timed["hit_rate"],

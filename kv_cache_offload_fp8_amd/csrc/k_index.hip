@@ -70,7 +70,30 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------------ begin
 
-__device__ static void build_request_table(const StepArgs &a, int roles, int32_t st0) {
+// Whether two requests' contiguous host ranges overlap, by the four waves of the
+// calling workgroup: lane l holds request l, and wave w compares it with requests
+// w, w + 4, ... (read from their lanes with scalar lane reads).  One wave walking
+// all 32 requests took about 3 us of the prologue.  Block-uniform result.
+__device__ static bool ranges_overlap(const StepArgs &a) {
+  __shared__ int s_ovl;
+  const int tid = threadIdx.x, l = tid & (kWave - 1), w = tid / kWave;
+  const bool in = l < a.B;
+  const int ctx = in ? a.ctx_len[l] : 0;
+  const int base = in ? a.host_base[l] : 0;
+  if (tid == 0) s_ovl = 0;
+  bool bad = false;
+  for (int o = w; o < a.B; o += 4) {
+    const int c2 = __builtin_amdgcn_readlane(ctx, o), b2 = __builtin_amdgcn_readlane(base, o);
+    if (in && o != l && ctx > 0 && c2 > 0 && base < b2 + c2 && b2 < base + ctx) bad = true;
+  }
+  __syncthreads();
+  if (__any(bad) && l == 0) s_ovl = 1;
+  __syncthreads();
+  return s_ovl != 0;
+}
+
+__device__ static void build_request_table(const StepArgs &a, int roles, int32_t st0,
+                                           bool overlap) {
   // one wave: lane b handles request b.  Every input is read before the status
   // (st0, loaded by the caller) is looked at, so the reads take one round trip.
   const int l = threadIdx.x;
@@ -89,12 +112,7 @@ __device__ static void build_request_table(const StepArgs &a, int roles, int32_t
   } else {
     bad = in && (ctx < 0 || ctx > a.max_ctx || base < 0 || (base & 15) != 0 ||
                  (int64_t)base + (int64_t)ctx > a.n_host);
-    // disjoint host ranges
-#pragma unroll 8
-    for (int o = 0; o < a.B; ++o) {
-      int c2 = __shfl(ctx, o), b2 = __shfl(base, o);
-      if (in && o != l && ctx > 0 && c2 > 0 && base < b2 + c2 && b2 < base + ctx) bad = true;
-    }
+    bad = bad || overlap;  // disjoint host ranges
   }
   const bool any_bad = __any(bad);
   if (any_bad) {
@@ -231,13 +249,36 @@ __device__ static void fill_u32(uint32_t *p, int64_t n, uint32_t v, int64_t i0, 
 
 constexpr int kBeginClearBlocks = 32;
 
+// With a page table: every page a request's tokens use lies in the pool
+// (out-of-range contexts are the request table's error).  kPageBlocks workgroups,
+// kPageBlocks / B per request, each taking every (kPageBlocks / B)-th run of 256
+// entries of its request's row (no division per entry).
+constexpr int kPageBlocks = 256;
+
+__device__ static void check_pages(const StepArgs &a, int blk) {
+  const int bpr = kPageBlocks / a.B;  // B <= kMaxBatch = 64, so at least 4
+  const int b = blk / bpr, part = blk - b * bpr;
+  if (b >= a.B) return;
+  const int c = a.ctx_len[b];
+  if (c <= 0 || c > a.max_ctx) return;
+  const int np = (c + 15) / 16 < a.page_stride ? (c + 15) / 16 : a.page_stride;
+  const int32_t *row = a.pages + (int64_t)b * a.page_stride;
+  bool bad = false;
+  for (int j = part * 256 + (int)threadIdx.x; j < np; j += bpr * 256)
+    bad |= !page_in_pool(a, row[j]);
+  if (bad) fail(a.ws.status, ECHO_EDEVARG);
+}
+
 __global__ __launch_bounds__(256) void k_begin(StepArgs a, int roles) {
   // the status is read here and looked at only after each role has issued its
   // own reads (a kernel that follows an error changes nothing)
   const int32_t st0 = __hip_atomic_load(a.ws.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   int blk = blockIdx.x;
   if (blk == 0) {
-    if (roles & BEGIN_REQ) build_request_table(a, roles, st0);
+    if (roles & BEGIN_REQ) {
+      const bool overlap = !a.pages && a.B > 1 && ranges_overlap(a);
+      build_request_table(a, roles, st0, overlap);
+    }
     if (st0 != 0) return;
     // small per-request arrays and counters
     const int tid = threadIdx.x;
@@ -265,7 +306,12 @@ __global__ __launch_bounds__(256) void k_begin(StepArgs a, int roles) {
     }
     blk -= 4 * a.B;
   }
-  if (blk >= kBeginClearBlocks || st0 != 0) return;
+  if (blk >= kBeginClearBlocks) {
+    blk -= kBeginClearBlocks;
+    if ((roles & BEGIN_REQ) && a.pages && st0 == 0 && a.B > 0) check_pages(a, blk);
+    return;
+  }
+  if (st0 != 0) return;
   const int64_t i0 = (int64_t)blk * blockDim.x + threadIdx.x;
   const int64_t step = (int64_t)kBeginClearBlocks * blockDim.x;
   if (roles & BEGIN_CLR_INDEX) {
@@ -278,24 +324,11 @@ __global__ __launch_bounds__(256) void k_begin(StepArgs a, int roles) {
     fill_u32((uint32_t *)a.sc.estate, 2LL * a.sc.atiles, 0u, i0, step);
     fill_u32((uint32_t *)a.sc.astate, 2LL * a.sc.atiles, 0u, i0, step);
   }
-  if ((roles & BEGIN_REQ) && a.pages) {
-    // every page a request's tokens use lies in the pool (out-of-range contexts are
-    // the request table's error)
-    const int64_t n = (int64_t)a.B * a.page_stride;
-    bool bad = false;
-    for (int64_t i = i0; i < n; i += step) {
-      const int b = (int)(i / a.page_stride);
-      const int j = (int)(i - (int64_t)b * a.page_stride);
-      const int c = a.ctx_len[b];
-      if (c > 0 && c <= a.max_ctx && j < (c + 15) / 16 && !page_in_pool(a, a.pages[i]))
-        bad = true;
-    }
-    if (bad) fail(a.ws.status, ECHO_EDEVARG);
-  }
 }
 
 hipError_t launch_begin(const StepArgs &a, int roles, hipStream_t s) {
-  const int grid = 1 + ((roles & BEGIN_Q) ? 4 * a.B : 0) + kBeginClearBlocks;
+  const int grid = 1 + ((roles & BEGIN_Q) ? 4 * a.B : 0) + kBeginClearBlocks +
+                   ((roles & BEGIN_REQ) && a.pages ? kPageBlocks : 0);
   hipLaunchKernelGGL(k_begin, dim3(grid), dim3(256), 0, s, a, roles);
   return hipGetLastError();
 }
@@ -335,6 +368,17 @@ hipError_t launch_kindex_pack(const uint8_t *rows, uint8_t *tiled, int64_t n_row
 
 constexpr int kChunks = kScoreTile / 64;  // 64-token chunks per work item
 
+// The page table through the constant address space: no kernel writes it, and
+// saying so lets the compiler read its wave-uniform entries with scalar loads.
+// Through a generic pointer, in the kernels that also store (the prefetch
+// installs), the entries became vector loads, and waiting for one -- it feeds the
+// next chunk's K addresses -- also waited for every K load issued before it (the
+// in-step scoring kernel took 132 us instead of 105).
+typedef const int32_t __attribute__((address_space(4))) const_i32;
+__device__ inline const const_i32 *page_table(const StepArgs &a) {
+  return (const const_i32 *)a.pages;
+}
+
 // Tiled-K groups (host id / 16, wave-uniform) of the four 16-token sub-tiles of
 // the chunk that starts at token s0 (a multiple of 64) of request b: from the page
 // table (PAGED, one page per group: scalar loads, issued a chunk before the K loads
@@ -349,7 +393,8 @@ __device__ inline void chunk_groups(const StepArgs &a, const ReqInfo &r, int b, 
   for (int u = 0; u < 4; ++u) {
     const int st = s0u + 16 * u;
     const int sg = st < r.ctx ? st : glast;
-    const int32_t g = PAGED ? a.pages[(int64_t)b * a.page_stride + (sg >> 4)] : (r.base + sg) >> 4;
+    const int32_t g =
+        PAGED ? page_table(a)[(int64_t)b * a.page_stride + (sg >> 4)] : (r.base + sg) >> 4;
     grp[u] = __builtin_amdgcn_readfirstlane(g);
   }
 }
@@ -524,7 +569,7 @@ __device__ inline void pf_pages(const StepArgs &a, int b, int pi, int tk, int (&
     gp[c] = 0;
     if (PAGED) {
       const int s = pi * kScoreTile + c * 64 + lane;
-      gp[c] = a.pages[(int64_t)b * a.page_stride + (((tk >> c) & 1) ? (s >> 4) : 0)];
+      gp[c] = page_table(a)[(int64_t)b * a.page_stride + (((tk >> c) & 1) ? (s >> 4) : 0)];
     }
   }
 }
