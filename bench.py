@@ -145,10 +145,12 @@ def stored_step_kernel(total_tok):
                       "bench.py --headline-only)"}
 
 
-def replay_median_ms(graph, n, warm=5):
+def replay_median_ms(graph, n, warm=40):
     """Median duration of n replays of `graph`, each timed with events on the current
-    stream after the previous one has finished, after `warm` untimed replays (the first
-    replays after idle or link-bound work measured 3-8% slower than the ones after them)."""
+    stream after the previous one has finished, after `warm` untimed replays: the GPU
+    reaches its sustained speed only after some tens of milliseconds of load (after 5
+    warm-up replays the scoring kernel still measured 1-4% slower than after 40, and
+    the first replays after idle or link-bound work 3-8% slower)."""
     import torch
     for _ in range(warm):
         graph.replay()
@@ -693,7 +695,7 @@ def main():
                                f"off): a graph of {nso} echo_indexer_prefetch calls less a "
                                f"graph of their {nso} prologues, each the median of {nrep} "
                                "replays timed one at a time with events on the replay stream, "
-                               "after 5 untimed replays",
+                               "after 40 untimed replays",
                      "bound": "hbm", "achieved": round(ks_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(ks_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "bytes_per_launch": idx_bytes,
