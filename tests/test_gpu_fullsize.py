@@ -91,3 +91,15 @@ def test_low_locality_full_size_and_lossless_ablation():
             assert np.array_equal(out["sel_tok"][b, :n], sel[b, :n]), (t, b)
         assert all(np.array_equal(x, y) for x, y in zip(rig.gathered(), rows)), t
     rig.close()
+
+
+@pytest.mark.timeout(900)
+def test_capacity_one_layer_full_size_paged():
+    # the same layer with a page table: every 16-id page of the 3.2M-token host pool
+    # moved to a random other page (K and latent rows move with it), so each request's
+    # tokens lie on pages scattered over the whole pool
+    _say("capacity, layer 30, page tables: 32 x U[80K,100K], EMA, 3 steps")
+    rig = H.Rig(get("capacity"), steps=3, layer=30, paged=True)
+    _run(rig, 3, H.MODE_EMA)
+    assert sum(int(out["n_pf"].sum()) for out, _ in rig.history[1:]) > 0
+    rig.close()
