@@ -57,10 +57,12 @@ __global__ __launch_bounds__(kSelThreads) void k_select_manage(StepArgs a) {
   }
   const int mb = blk - a.B, nblk = a.sc.atiles;
   if (mb >= nblk) {
-    // small batches until every selection is done: top-k is latency-bound and the
-    // host reads in flight slow its memory round trips (measured: the layer step
-    // 264-266 us with full batches throughout, 258 us with this)
-    if (st0 == 0) manage_copy(a, mb - nblk, &a.sc.misc[M_TOPK_DONE], a.B);
+    // small batches until every management workgroup has reached the recall: top-k
+    // and management are chains of memory round trips, and host reads in flight
+    // lengthen every one of them (measured: the layer step 264-266 us with full
+    // batches throughout, 258 us with small ones during top-k; small ones through
+    // management as well took the capacity decode step from 14.24 to 14.12 ms)
+    if (st0 == 0) manage_copy(a, mb - nblk, &a.sc.misc[M_BAR3], nblk);
     return;
   }
   if (st0 != 0) return;

@@ -281,6 +281,10 @@ __device__ static void manage_block(const StepArgs &a, int blk, int32_t st0, Man
     }
     __syncthreads();
     copy_rows<NT>(a, s_rh, s_rg, r1 - r0);
+  } else if (tid == 0) {
+    // no recall: count the arrival anyway, since the prefetch copy beside this
+    // launch keeps its batches small until the count reaches nblk
+    __hip_atomic_fetch_add(&a.sc.misc[M_BAR3], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if (ADVANCE) {
     __syncthreads();
