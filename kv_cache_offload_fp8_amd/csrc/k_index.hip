@@ -607,6 +607,21 @@ struct PendItem {
   uint64_t cand[kChunks];
 };
 
+// A queued item's candidate masks as lane 0 wrote them.  Lane 0 alone writes an
+// entry; the other lanes take its view through readfirstlane, since for them an
+// LDS read of lane 0's write with no barrier between is a data race, which the
+// compiler may resolve by reading before the write (a variant that installed an
+// item right after queueing it got wrong masks and missing installs that way).
+__device__ inline void pend_cand(const PendItem &e, uint64_t (&oc)[kChunks]) {
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const uint64_t v = e.cand[c];
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    oc[c] = ((uint64_t)hi << 32) | lo;
+  }
+}
+
 // Scores a wave holds in LDS before it writes them out (items of 256 tokens).
 constexpr int kDeferItems = 8;
 
@@ -708,8 +723,7 @@ __device__ static void score_job(const StepArgs &a, const ReqInfo &r, int b, int
   };
   auto install_oldest = [&]() {  // blocking
     uint64_t oc[kChunks];
-#pragma unroll
-    for (int c = 0; c < kChunks; ++c) oc[c] = pq[qh].cand[c];
+    pend_cand(pq[qh], oc);
     read_oldest();
     pf_install<PAGED>(a, r, b, o_i, oc, o_c, t, nfree);
     qh = qh + 1 == kPending ? 0 : qh + 1;
@@ -797,8 +811,7 @@ __device__ static void score_job(const StepArgs &a, const ReqInfo &r, int b, int
               lb_try_finish(a.sc.tstate, r.tile0 + o_i, r.tile0, o_c, sv, a.ws.status, E0)) {
             if (o_c > 0) {
               uint64_t oc[kChunks];
-#pragma unroll
-              for (int cc = 0; cc < kChunks; ++cc) oc[cc] = pq[qh].cand[cc];
+              pend_cand(pq[qh], oc);
               pf_plan(a, r, oc, E0, nfree, rk, tk, gi);
             }
             planned = true;
