@@ -680,7 +680,7 @@ __device__ static void score_job(const StepArgs &a, const ReqInfo &r, int b, int
       }
       if (r.use_guard) {
         const int64_t tau = r.tile0 + it;
-        const int n = wbuf->gcnt[j];
+        const int n = __builtin_amdgcn_readfirstlane(wbuf->gcnt[j]);  // lane 0 wrote it
         if (lane < kGuardSlots && lane < n) {
           a.sc.gcand_key[tau * kGuardSlots + lane] = wbuf->gkey[j * kGuardSlots + lane];
           a.sc.gcand_idx[tau * kGuardSlots + lane] = wbuf->gidx[j * kGuardSlots + lane];
