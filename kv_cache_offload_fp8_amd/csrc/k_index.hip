@@ -92,8 +92,7 @@ __device__ static bool ranges_overlap(const StepArgs &a) {
   return s_ovl != 0;
 }
 
-__device__ static void build_request_table(const StepArgs &a, int roles, int32_t st0,
-                                           bool overlap) {
+__device__ static void build_request_table(const StepArgs &a, int32_t st0, bool overlap) {
   // one wave: lane b handles request b.  Every input is read before the status
   // (st0, loaded by the caller) is looked at, so the reads take one round trip.
   const int l = threadIdx.x;
@@ -277,7 +276,7 @@ __global__ __launch_bounds__(256) void k_begin(StepArgs a, int roles) {
   if (blk == 0) {
     if (roles & BEGIN_REQ) {
       const bool overlap = !a.pages && a.B > 1 && ranges_overlap(a);
-      build_request_table(a, roles, st0, overlap);
+      build_request_table(a, st0, overlap);
     }
     if (st0 != 0) return;
     // small per-request arrays and counters
