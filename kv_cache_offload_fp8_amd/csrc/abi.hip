@@ -320,7 +320,10 @@ int prefill_args(const echo_dims_t *dims, const echo_layer_t *layer,
   p->pred = c->pred;
   p->qblocks = (c->queries + kPfQBlock - 1) / kPfQBlock;
   const int nch = (c->hist_len + 63) / 64;
-  int ts = (1024 + p->qblocks - 1) / p->qblocks;
+  // About one scoring workgroup per compute unit (a workgroup fills a compute unit's
+  // registers, so a grid of several rounds waits at every round for its slowest
+  // wave); token splits a multiple of the 8 XCDs.
+  int ts = (device_cus() + p->qblocks - 1) / p->qblocks;
   ts = (ts + 7) / 8 * 8;
   const int tmax = (nch + 7) / 8 * 8;
   p->tsplits = ts < 8 ? 8 : (ts > tmax ? tmax : ts);

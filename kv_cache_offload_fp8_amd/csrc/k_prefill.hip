@@ -15,10 +15,11 @@
 //   k_pf_stage    q split into fp8 hi/lo with a per-head power-of-two scale
 //   k_pf_score    scores [C][N] on the fp8 MFMA (the heads x tokens contraction
 //                 for every query; each wave keeps two queries' operands in
-//                 registers and streams 64-token K chunks; the grid is placed so
-//                 that the workgroups of one XCD share one token range through
-//                 its L2), and each query's histogram of the coarse buckets of
-//                 fp16(score - pred), counted in LDS as the scores are made
+//                 registers and streams 64-token K chunks; about one workgroup
+//                 per compute unit, placed so that the workgroups of one XCD
+//                 share one token range through its L2), and each query's
+//                 histogram of the coarse buckets of fp16(score - pred),
+//                 counted in LDS as the scores are made
 //   k_pf_coarse   per query: the boundary bucket from that histogram, and the
 //                 candidate flags above it (one pass over the row)
 //   k_pf_flags_*  the union of flags as an ascending token list
@@ -40,7 +41,10 @@ typedef int v8i_pf __attribute__((ext_vector_type(8)));
 typedef float v4f_pf __attribute__((ext_vector_type(4)));
 typedef int v4i_pf __attribute__((ext_vector_type(4)));
 
-constexpr int kPfCopyBlocks = 32;  // a small grid keeps about 256 KB of host reads in flight
+constexpr int kPfCopyBlocks = 32;
+// Word 3 of a raw buffer resource on gfx9: 32-bit data format (a zero format would
+// make every access out of range), no swizzle, no stride.
+constexpr int kRawBufWord3 = 0x00020000;  // a small grid keeps about 256 KB of host reads in flight
 
 // The status as one workgroup sees it: read once and shared, so that all of its
 // waves take the same branch before the block barriers that follow.
@@ -115,48 +119,23 @@ __global__ __launch_bounds__(256) void k_pf_stage(StepArgs a, PrefillArgs p) {
 // group of 16 (hb is a multiple of 16).  Tokens past the history read its last
 // group (their scores are dropped); lanes whose dims lie past D read the first 32
 // dims, which meet q's zero padding.
-__device__ inline void pf_load_k(const StepArgs &a, const PrefillArgs &p, int s0, int lane,
-                                 v8i_pf (&kb)[4]) {
+__device__ inline v8i_pf pf_load_k1(const StepArgs &a, const PrefillArgs &p, int s0, int u,
+                                    int lane) {
   const int lp = 32 * (lane >> 4) < a.D ? lane : (lane & 15);
   const int glast = (p.N - 1) & ~15;
   const uint32_t lo = (uint32_t)lp * 16u, hi = lo + 8u * (uint32_t)a.D;
-  const int s0u = __builtin_amdgcn_readfirstlane(s0);
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int st = s0u + 16 * u;
-    const int sg = st < p.N ? st : glast;
-    const uint8_t *g = a.kidx + ((int64_t)p.hb + sg) * a.D;
-    const v4i_pf x0 = *(const v4i_pf *)(g + lo);
-    const v4i_pf x1 = *(const v4i_pf *)(g + hi);
-    kb[u] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
-  }
+  const int st = __builtin_amdgcn_readfirstlane(s0) + 16 * u;
+  const int sg = st < p.N ? st : glast;
+  const uint8_t *g = a.kidx + ((int64_t)p.hb + sg) * a.D;
+  const v4i_pf x0 = *(const v4i_pf *)(g + lo);
+  const v4i_pf x1 = *(const v4i_pf *)(g + hi);
+  return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Lane l returns the score of token s0 + l for one query (four head groups, q_hi
-// and q_lo terms, ReLU as an integer max, the weighted sum over the lane's heads,
-// then over the four lane groups that share a token).
-__device__ inline float pf_score64(const v8i_pf (&kb)[4], const v8i_pf (&qa)[4][2],
-                                   const float (&wr)[4][4], int lane) {
-  float sc4[4];
+__device__ inline void pf_load_k(const StepArgs &a, const PrefillArgs &p, int s0, int lane,
+                                 v8i_pf (&kb)[4]) {
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    float v = 0.0f;
-#pragma unroll
-    for (int hg = 0; hg < 4; ++hg) {
-      v4f_pf acc = {0.0f, 0.0f, 0.0f, 0.0f};
-      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[hg][0], kb[u], acc, 0, 0, 0, 0,
-                                                             0, 0);
-      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[hg][1], kb[u], acc, 0, 0, 0, 0,
-                                                             0, 0);
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        v += wr[hg][rr] * __int_as_float(max(__float_as_int(acc[rr]), 0));
-    }
-    v = sum_lane_groups16(v);
-    sc4[u] = v;
-  }
-  const int sel = lane >> 4;
-  return sel == 0 ? sc4[0] : sel == 1 ? sc4[1] : sel == 2 ? sc4[2] : sc4[3];
+  for (int u = 0; u < 4; ++u) kb[u] = pf_load_k1(a, p, s0, u, lane);
 }
 
 // Bucket of a score shifted by the predicted k-th score: the difference in fp32,
@@ -179,7 +158,7 @@ __global__ __launch_bounds__(kPfWaves * kWave) void k_pf_score(StepArgs a, Prefi
   for (int i = threadIdx.x; i < kPfQBlock * 256; i += kPfWaves * kWave) (&s_hist[0][0])[i] = 0;
   __syncthreads();
   const bool dead = failed(p.status);
-  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int b = blockIdx.x, xcd = b & 7, jj = b >> 3;
   const int ts = xcd * (p.tsplits >> 3) + jj / p.qblocks, qb = jj % p.qblocks;
   const int q0 = qb * kPfQBlock + wave * kPfQ;
@@ -207,29 +186,83 @@ __global__ __launch_bounds__(kPfWaves * kWave) void k_pf_score(StepArgs a, Prefi
           wr[u][hg][rr] = p.wsc[(int64_t)qi * kHeadsPad + hg * 16 + (lane >> 4) * 4 + rr];
       }
     }
-    auto emit = [&](const v8i_pf (&kb)[4], int c) {
+    // Per chunk, lane l makes the score of token c*64 + l for each query: for each
+    // sub-tile, head group and query, the q_hi and q_lo MFMAs, then ReLU (an integer
+    // max on the float bits) and the weighted sum over the lane's four heads; the
+    // four lane groups that share a token are summed last.  Sub-tile by sub-tile,
+    // both queries' four head-group pairs run in sequence, and each pair's ReLU and
+    // weighted sum are issued around the next pair's two MFMAs, so that the vector
+    // work runs while the matrix core works.
+    // One K register set: sub-tile u of chunk c + 1 loads as soon as the last MFMA
+    // of chunk c that reads sub-tile u has issued (clamped to the split's last
+    // chunk: at most one extra chunk read per wave, from L2).  A single set keeps
+    // the wave near 210 registers, which leaves room on the compute unit for the
+    // copy kernel's waves beside a scoring workgroup.
+    // The scores go out through a raw buffer resource per query row: the hardware
+    // drops stores at offsets past the resource's range (tokens past the history,
+    // rows of missing queries, whose range is 0), so the chunk has no branch and
+    // the compiler can count the loads in flight across it.
+    v8i_pf kb[4];
+    pf_load_k(a, p, c0 * 64, lane, kb);
+    // Everything loaded so far is waited for here, so that the wait at the loop
+    // head only covers what the previous chunk issued.  The immediate is gfx9's
+    // s_waitcnt encoding of vmcnt(0) with the other counters left at their maxima.
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    const int sel = lane >> 4;
+    __amdgpu_buffer_rsrc_t srow[kPfQ];
+#pragma unroll
+    for (int u = 0; u < kPfQ; ++u)
+      srow[u] = __builtin_amdgcn_make_buffer_rsrc(p.scores + (int64_t)min(q0 + u, p.C - 1) * p.N,
+                                                  0, q0 + u < p.C ? p.N * 4 : 0, kRawBufWord3);
+    for (int c = c0; c < c1; ++c) {
+      const int cn = min(c + 1, c1 - 1);
+      float vs[kPfQ], vo[kPfQ];
+      v4f_pf prev = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int j = 0; j <= 16 * kPfQ; ++j) {
+        const bool mm = j < 16 * kPfQ, ep = j > 0;
+        const int u = j / (4 * kPfQ), q = (j >> 2) % kPfQ, hg = j & 3;
+        const int jp = j - 1, up = jp / (4 * kPfQ), qp = (jp >> 2) % kPfQ, hp = jp & 3;
+        v4f_pf cur = {0.0f, 0.0f, 0.0f, 0.0f};
+        float v = 0.0f;
+        if (ep && hp != 0) v = vs[qp];
+        if (mm)
+          cur = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[q][hg][0], kb[u], cur, 0, 0,
+                                                                 0, 0, 0, 0);
+        if (ep) {
+          v += wr[qp][hp][0] * __int_as_float(max(__float_as_int(prev[0]), 0));
+          v += wr[qp][hp][1] * __int_as_float(max(__float_as_int(prev[1]), 0));
+        }
+        if (mm)
+          cur = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[q][hg][1], kb[u], cur, 0, 0,
+                                                                 0, 0, 0, 0);
+        if (ep) {
+          v += wr[qp][hp][2] * __int_as_float(max(__float_as_int(prev[2]), 0));
+          v += wr[qp][hp][3] * __int_as_float(max(__float_as_int(prev[3]), 0));
+          vs[qp] = v;
+          if (hp == 3) {
+            const float t = sum_lane_groups16(v);
+            vo[qp] = (up == 0 || sel == up) ? t : vo[qp];
+          }
+        }
+        if (mm && j % (4 * kPfQ) == 4 * kPfQ - 1) kb[u] = pf_load_k1(a, p, cn * 64, u, lane);
+        // the order within the step: MFMA (q_hi), four vector instructions, MFMA
+        // (q_lo), the rest; nothing crosses into the next step
+        if (mm) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        prev = cur;
+      }
       const int s = c * 64 + lane;
 #pragma unroll
       for (int u = 0; u < kPfQ; ++u) {
-        const float v = pf_score64(kb, qa[u], wr[u], lane);
-        if (q0 + u < p.C && s < p.N) {
-          p.scores[(int64_t)(q0 + u) * p.N + s] = v;
-          atomicAdd(&s_hist[wave * kPfQ + u][pf_bucket(v, pr[u])], 1u);
-        }
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(vo[u]), srow[u], s * 4, 0, 0);
+        atomicAdd(&s_hist[wave * kPfQ + u][pf_bucket(vo[u], pr[u])],
+                  (q0 + u < p.C && s < p.N) ? 1u : 0u);
       }
-    };
-    // Two register sets: chunk c + 1 loads while c computes.  The loads are
-    // unconditional, clamped to the split's last chunk (at most two extra chunk
-    // reads per wave, from L2): a load under a branch would leave the compiler
-    // unable to count the loads in flight at the join, and it would wait for all
-    // of them there, once per pair of chunks.
-    v8i_pf k0[4], k1[4];
-    pf_load_k(a, p, c0 * 64, lane, k0);
-    for (int c = c0; c < c1; c += 2) {
-      pf_load_k(a, p, min(c + 1, c1 - 1) * 64, lane, k1);
-      emit(k0, c);
-      pf_load_k(a, p, min(c + 2, c1 - 1) * 64, lane, k0);
-      if (c + 1 < c1) emit(k1, c + 1);
     }
   }
   __syncthreads();
