@@ -279,7 +279,6 @@ __global__ __launch_bounds__(kSelThreads) void k_pf_coarse(StepArgs a, PrefillAr
   __shared__ int s_beta;
   if (block_failed(p.status)) return;
   const int i = blockIdx.x, tid = threadIdx.x;
-  const float *row = p.scores + (int64_t)i * p.N;
   const float pr = p.pred ? p.pred[i] : 0.0f;
   int beta = -1;
   if (p.N > a.K) {
@@ -294,11 +293,35 @@ __global__ __launch_bounds__(kSelThreads) void k_pf_coarse(StepArgs a, PrefillAr
     __syncthreads();
     beta = s_beta;
   }
+  // The row is read in 16-byte pieces of the score buffer (256-byte aligned, each
+  // region padded to whole 256-byte lines): piece j holds the buffer's floats
+  // 4j .. 4j+3, of which those outside the row are skipped.  Each thread loads
+  // four pieces before it flags any token (the byte-wide flag stores may alias the
+  // scores as far as the compiler knows), so four loads are in flight per thread.
+  constexpr int U = 4;
+  const int64_t f0 = (int64_t)i * p.N, f1 = f0 + p.N;
+  const int64_t j0 = f0 >> 2, j1 = (f1 + 3) >> 2;
+  const float4 *pc = reinterpret_cast<const float4 *>(p.scores);
   int cnt = 0;
-  for (int s = tid; s < p.N; s += kSelThreads) {
-    if (beta < 0 || pf_bucket(row[s], pr) > beta) {
-      p.cflag[s] = 1;
-      ++cnt;
+  for (int64_t jb = j0 + tid; jb < j1; jb += (int64_t)U * kSelThreads) {
+    float4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = jb + (int64_t)u * kSelThreads;
+      v[u] = pc[j < j1 ? j : j0];  // a piece past the row rereads the row's first
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = jb + (int64_t)u * kSelThreads;
+      const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int64_t f = 4 * j + k;
+        if (j < j1 && f >= f0 && f < f1 && (beta < 0 || pf_bucket(e[k], pr) > beta)) {
+          p.cflag[f - f0] = 1;
+          ++cnt;
+        }
+      }
     }
   }
   int tot;
