@@ -54,6 +54,20 @@ def test_prefill_64x128_ragged(use_pred):
     rig.close()
 
 
+@pytest.mark.parametrize("N,k,n_gpu,n_host", [(2999, 256, 4000, 4096), (1001, 64, 1500, 1024)])
+def test_prefill_rows_off_16_byte_boundaries(N, k, n_gpu, n_host):
+    # A history length that is not a multiple of 4: three score rows in four start
+    # inside a 16-byte piece of the score buffer, and the coarse pass reads whole
+    # pieces and must skip the neighbouring rows' floats.  19 queries leave a ragged
+    # query block (the scoring kernel's stores for the missing queries are dropped)
+    # and the last 64-token chunk is ragged too.
+    _say(f"prefill 64x128: N {N}, C 19, k {k} (rows off 16-byte boundaries)")
+    wl = get("prefill").scaled(rho=0.9)
+    rig = H.PrefillRig(wl, N=N, C=19, chunks=2, n_gpu=n_gpu, n_host=n_host, top_k=k)
+    _run(rig, 2)
+    rig.close()
+
+
 def test_prefill_4x32_small_heads():
     _say("prefill 4x32: N 1000, C 20, k 64")
     wl = get("tiny").scaled(rho=0.8)
