@@ -454,10 +454,10 @@ __global__ __launch_bounds__(kSelThreads) void k_pf_inst_write(StepArgs a, Prefi
 // all certain) and the k - n_qcand[i] best of the boundary bucket by (score desc,
 // token asc) -- the bucket of a rounded difference never decreases as the score
 // grows, so the order of the whole row is bucket by bucket.  The boundary
-// bucket's (key, token) composites are gathered in LDS (one atomic per wave) and
-// selected there; a bucket too large for LDS falls back to the radix select over
-// the whole row.  pred[i] is read before kth[i] is written (the caller may pass
-// this workspace's kth as pred).
+// bucket's (key, token) composites are gathered in LDS (one atomic per wave and
+// round of four 16-byte pieces per thread) and selected there; a bucket too large
+// for LDS falls back to the radix select over the whole row.  pred[i] is read
+// before kth[i] is written (the caller may pass this workspace's kth as pred).
 constexpr int kPfBoundaryCap = 6144;
 
 __global__ __launch_bounds__(kSelThreads) void k_pf_exact(StepArgs a, PrefillArgs p) {
@@ -472,22 +472,61 @@ __global__ __launch_bounds__(kSelThreads) void k_pf_exact(StepArgs a, PrefillArg
   const float pr = p.pred ? p.pred[i] : 0.0f;
   const int beta = p.beta[i];
   const int above = p.n_qcand[i];
+  // The row in 16-byte pieces of the score buffer, as the coarse pass reads it:
+  // piece j holds the buffer's floats 4j .. 4j+3, those outside the row skipped.
+  const int64_t f0 = (int64_t)i * p.N, f1 = f0 + p.N;
+  const int64_t j0 = f0 >> 2, j1 = (f1 + 3) >> 2;
+  const float4 *pc = reinterpret_cast<const float4 *>(p.scores);
   uint64_t P = ~0ull;
   int pos = 0;
   bool in_lds = false;
   if (beta >= 0) {
     if (tid == 0) s_n = 0;
     __syncthreads();
-    for (int s0 = 0; s0 < p.N; s0 += kSelThreads) {
-      const int s = s0 + tid;
-      const float v = s < p.N ? row[s] : 0.0f;
-      const bool m = s < p.N && pf_bucket(v, pr) == beta;
-      const uint64_t bal = __ballot(m);
+    // The boundary bucket's composites: four pieces per thread and round, every
+    // thread through every round (whole waves meet at the scan), one LDS atomic
+    // per wave and round.
+    constexpr int U = 4;
+    const int rounds = (int)((j1 - j0 + U * kSelThreads - 1) / (U * kSelThreads));
+    for (int rd = 0; rd < rounds; ++rd) {
+      const int64_t jb = j0 + (int64_t)rd * U * kSelThreads + tid;
+      float4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t j = jb + (int64_t)u * kSelThreads;
+        v[u] = pc[j < j1 ? j : j0];
+      }
+      uint32_t m = 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t j = jb + (int64_t)u * kSelThreads;
+        const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int64_t f = 4 * j + k;
+          const bool hit = j < j1 && f >= f0 && f < f1 && pf_bucket(e[k], pr) == beta;
+          m |= (hit ? 1u : 0u) << (4 * u + k);
+        }
+      }
+      const int cnt = __popc(m);
+      const int incl = wave_incl_scan(cnt);
+      const int wtot = __shfl(incl, kWave - 1);
       int b0 = 0;
-      if (lane == 0 && bal) b0 = atomicAdd(&s_n, __popcll(bal));
-      b0 = __shfl(b0, 0);
-      const int idx = b0 + __popcll(bal & lanemask_lt());
-      if (m && idx < kPfBoundaryCap) s_list[idx] = ((uint64_t)topk_key(v) << 32) | (uint32_t)s;
+      if (lane == 0 && wtot) b0 = atomicAdd(&s_n, wtot);
+      int idx = __shfl(b0, 0) + incl - cnt;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t j = jb + (int64_t)u * kSelThreads;
+        const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          if ((m >> (4 * u + k)) & 1u) {
+            if (idx < kPfBoundaryCap)
+              s_list[idx] = ((uint64_t)topk_key(e[k]) << 32) | (uint32_t)(4 * j + k - f0);
+            ++idx;
+          }
+        }
+      }
     }
     __syncthreads();
     const int n = s_n;
@@ -500,39 +539,42 @@ __global__ __launch_bounds__(kSelThreads) void k_pf_exact(StepArgs a, PrefillArg
           [=](int s) { return ((uint64_t)topk_key(row[s]) << 32) | (uint32_t)s; }, p.N, a.K, &P,
           &pos, s_sel_lds);
   }
+  // The selection in ascending token order, 1024 pieces per step (thread t takes
+  // piece t), one block scan per step.
   int32_t *out = p.sel + (int64_t)i * a.K;
   int written = 0;
   uint64_t worst = 0;  // the largest selected composite: the k-th in selection order
-  for (int base = 0; base < p.N; base += kPfSeg) {
+  for (int64_t jb0 = j0; jb0 < j1; jb0 += kSelThreads) {
+    const int64_t j = jb0 + tid;
+    const float4 v = pc[j < j1 ? j : j0];
+    const float e[4] = {v.x, v.y, v.z, v.w};
     uint32_t keys[4];
-    bool in[4];
-    int cnt = 0;
+    uint32_t m = 0;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int s = base + tid * 4 + v;
-      const float x = s < p.N ? row[s] : 0.0f;
-      keys[v] = topk_key(x);
-      bool sel = s < p.N;
+    for (int k = 0; k < 4; ++k) {
+      const int64_t f = 4 * j + k;
+      const int s = (int)(f - f0);
+      keys[k] = topk_key(e[k]);
+      bool sel = j < j1 && f >= f0 && f < f1;
       if (sel && beta >= 0) {
         if (in_lds) {
-          const int b = pf_bucket(x, pr);
-          sel = b > beta || (b == beta && composite_selected(keys[v], s, P, pos));
+          const int b = pf_bucket(e[k], pr);
+          sel = b > beta || (b == beta && composite_selected(keys[k], s, P, pos));
         } else {
-          sel = composite_selected(keys[v], s, P, pos);
+          sel = composite_selected(keys[k], s, P, pos);
         }
       }
-      in[v] = sel;
-      cnt += sel ? 1 : 0;
+      m |= (sel ? 1u : 0u) << k;
     }
     int tot;
-    int r = written + block_excl_scan<kSelThreads>(cnt, sh, &tot);
+    int r = written + block_excl_scan<kSelThreads>(__popc(m), sh, &tot);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      if (in[v]) {
-        const int s = base + tid * 4 + v;
+    for (int k = 0; k < 4; ++k) {
+      if ((m >> k) & 1u) {
+        const int s = (int)(4 * j + k - f0);
         out[r++] = s;
         p.uflag[s] = 1;
-        const uint64_t x = ((uint64_t)keys[v] << 32) | (uint32_t)s;
+        const uint64_t x = ((uint64_t)keys[k] << 32) | (uint32_t)s;
         worst = x > worst ? x : worst;
       }
     }
