@@ -68,6 +68,18 @@ def test_prefill_rows_off_16_byte_boundaries(N, k, n_gpu, n_host):
     rig.close()
 
 
+def test_prefill_single_query_chunks():
+    # C = 1: one query block, so the scoring grid takes as many token splits as the
+    # history allows and each workgroup has a single live wave (its second query and
+    # the other seven waves' queries are missing); the coarse and exact passes run one
+    # workgroup in all
+    _say("prefill 64x128: N 1500, C 1, k 128")
+    wl = get("prefill").scaled(rho=0.9)
+    rig = H.PrefillRig(wl, N=1500, C=1, chunks=3, n_gpu=2000, n_host=2048, top_k=128)
+    _run(rig, 3)
+    rig.close()
+
+
 def test_prefill_4x32_small_heads():
     _say("prefill 4x32: N 1000, C 20, k 64")
     wl = get("tiny").scaled(rho=0.8)
