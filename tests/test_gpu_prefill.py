@@ -80,6 +80,17 @@ def test_prefill_single_query_chunks():
     rig.close()
 
 
+def test_prefill_history_shorter_than_one_group():
+    # N = 10: one partial 16-token group and one partial 64-token chunk; every
+    # token split's range but the first is empty, and every token is selected
+    _say("prefill 64x128: N 10, C 3, k 64")
+    wl = get("prefill").scaled(rho=0.9)
+    rig = H.PrefillRig(wl, N=10, C=3, chunks=2, n_gpu=256, n_host=256, top_k=64)
+    o = _run(rig, 2)
+    assert (o["beta"] == -1).all() and o["uni"].size == 10
+    rig.close()
+
+
 def test_prefill_4x32_small_heads():
     _say("prefill 4x32: N 1000, C 20, k 64")
     wl = get("tiny").scaled(rho=0.8)
