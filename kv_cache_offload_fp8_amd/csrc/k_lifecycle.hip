@@ -55,7 +55,7 @@ __global__ __launch_bounds__(kReleaseThreads) void k_release_check(StepArgs a,
 
 __global__ __launch_bounds__(kReleaseThreads) void k_release_free(StepArgs a,
                                                                   const int32_t *mask) {
-  if (failed(a.ws.status)) return;  // an earlier error, or k_release_check's verdict
+  if (failed(a.ws.status)) return;  // an earlier error, or what k_release_check found
   const int tid = threadIdx.x;
   const int b = blockIdx.y;
   if (!mask[b]) return;
